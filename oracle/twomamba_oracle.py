@@ -1,0 +1,364 @@
+"""fp64 CPU oracle for the 2Mamba / 2Mamba-E sequence-mixing operator.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module; only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code, table or constant with the
+HIP library and imports nothing from it.
+
+Source: "2Mamba2Furious: Linear in Complexity, Competitive in Accuracy"
+(paperlayer summary of arXiv 2602.17363), cited below as [2M2F §n].  The
+pages describe the operator in prose only; where they leave a step open the
+plainest reading is taken and named here (the same list sits in the design
+notes):
+
+* decay: g_t = -softplus(z_t) with the exact softplus max(x,0)+log1p(exp(-|x|))
+  (softplus A-mask that drops the discretisation parameter, [2M2F §3, §4];
+  equal to the forgetting transformer's log-sigmoid up to the sign of its
+  argument, [2M2F §6]).
+* mask: L_ts = exp(sum_{r=s+1..t} g_r) for s <= t, so the diagonal L_tt = 1 is
+  kept (standard causal mask).
+* 2Mamba: weight w_ts = L_ts * (scale * q_t.k_s)^2 -- the square is taken of
+  the query-key product and the mask multiplies the squared score; the mask
+  itself is not squared [2M2F §5].  "Softmax normalisation" [2M2F §5] is read
+  as dividing by the sum of the same weights; o_t = 0 when that sum is 0.
+* 2Mamba-E: softmax over s <= t of scale * q_t.k_s + log L_ts, i.e. softmax
+  attention with the softplus A-mask as an additive log-bias [2M2F §6].
+* second-order state: the symmetric k (x) k (x) v tensor [2M2F §2] packed as
+  the row-major upper triangle p(i,j) = i*d - i*(i-1)/2 + (j-i), i <= j,
+  holding the unscaled products k_i*k_j; the off-diagonal weight 2 lives on
+  the query side.  A normaliser state n (same packing, sum of k (x) k) carries
+  the softmax-normalisation denominator.
+* an initial state enters as the state "before token 0" and is decayed by g_0
+  like any earlier token (the Mamba-2 recurrence h_t = a_t h_{t-1} + ...,
+  "Mamba-2 - State Space Duality" thread); a decode step consumes the decay
+  logit of its own token.
+
+Conv, time discretisation, gating and output norms are outside the operator:
+the kernels of [2M2F App. C] take Q, K, V and return post-attention outputs
+without pre- or post-processing.
+
+Every function works on fp64 numpy arrays with leading batch/head axes
+[B, H, ...] and treats each (b, h) independently.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "softplus", "decay_log", "num_pairs", "pair_index", "pair_list",
+    "phi_k", "phi_q", "fwd_quadratic", "fwd_quadratic_rows", "final_state_direct",
+    "fwd_recurrent_full", "fwd_recurrent_packed", "step",
+    "fwd_exp_quadratic", "fwd_exp_quadratic_rows", "fwd_exp_streaming",
+    "state_elements", "memory_crossover_tokens",
+]
+
+
+# ----------------------------------------------------------------------------
+# decay  [2M2F §3 softplus A-mask; §6 log-sigmoid connection]
+# ----------------------------------------------------------------------------
+
+def softplus(x):
+    """Exact softplus, log(1 + e^x), computed without overflow.
+
+    softplus(-inf) = 0 exactly; no large-argument linearisation threshold.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        out = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    return np.where(np.isneginf(x), 0.0, out)
+
+
+def decay_log(z):
+    """Per-token log decay g = -softplus(z) <= 0 (so every L_ts lies in (0, 1])."""
+    return -softplus(z)
+
+
+# ----------------------------------------------------------------------------
+# second-order features  [2M2F §2 higher-order state of about (dh^2, dh)]
+# ----------------------------------------------------------------------------
+
+def num_pairs(d: int) -> int:
+    """Number of distinct entries of a symmetric d x d tensor, d(d+1)/2."""
+    return d * (d + 1) // 2
+
+
+def pair_index(i: int, j: int, d: int) -> int:
+    """Packed position of the unordered pair (i, j), i <= j: row-major upper triangle."""
+    if not (0 <= i <= j < d):
+        raise ValueError("need 0 <= i <= j < d")
+    return i * d - i * (i - 1) // 2 + (j - i)
+
+
+def pair_list(d: int):
+    """Arrays (I, J) with (I[p], J[p]) the pair stored at packed position p."""
+    I = np.empty(num_pairs(d), dtype=np.int64)
+    J = np.empty(num_pairs(d), dtype=np.int64)
+    for i in range(d):
+        for j in range(i, d):
+            p = pair_index(i, j, d)
+            I[p], J[p] = i, j
+    return I, J
+
+
+def phi_k(k):
+    """Key-side features k_i k_j (i <= j), unscaled: [..., d] -> [..., D]."""
+    I, J = pair_list(k.shape[-1])
+    return k[..., I] * k[..., J]
+
+
+def phi_q(q):
+    """Query-side features c_ij q_i q_j with c = 2 off the diagonal, 1 on it.
+
+    With phi_k this gives phi_q(q) . phi_k(k) = (q . k)^2.
+    """
+    I, J = pair_list(q.shape[-1])
+    c = np.where(I == J, 1.0, 2.0)
+    return c * q[..., I] * q[..., J]
+
+
+# ----------------------------------------------------------------------------
+# form (A): quadratic masked form, built row by row
+# ----------------------------------------------------------------------------
+
+def _row_log_mask(g_row_upto_t):
+    """lambda_ts for s = 0..t from g_0..g_t, summed backward from the diagonal.
+
+    lambda_tt = 0; lambda_t,s-1 = lambda_ts + g_s.  No global cumulative sum.
+    """
+    t = g_row_upto_t.shape[-1] - 1
+    lam = np.zeros(g_row_upto_t.shape[:-1] + (t + 1,))
+    if t > 0:
+        # lambda_t,s = sum_{r=s+1}^{t} g_r  for s = 0..t-1
+        tail = g_row_upto_t[..., 1:][..., ::-1]          # g_t, g_{t-1}, ..., g_1
+        lam[..., :t] = np.cumsum(tail, axis=-1)[..., ::-1]
+    return lam
+
+
+def _sq_row(q_t, K, V, g_upto_t, scale, init_num=None, init_den=None, init_decay=None):
+    lam = _row_log_mask(g_upto_t)                          # [..., t+1]
+    score = scale * np.einsum("...d,...sd->...s", q_t, K)  # [..., t+1]
+    w = np.exp(lam) * score * score
+    num = np.einsum("...s,...sc->...c", w, V)
+    den = w.sum(axis=-1)
+    if init_num is not None:
+        num = num + init_decay[..., None] * init_num
+        den = den + init_decay * init_den
+    return num, den
+
+
+def _normalise(num, den, norm):
+    if not norm:
+        return num
+    safe = np.where(den == 0.0, 1.0, den)
+    return np.where(den[..., None] == 0.0, 0.0, num / safe[..., None])
+
+
+def _init_terms(q, scale, state_in, norm_in):
+    """phi_q(scale q_t) . S0 and phi_q(scale q_t) . n0 for every t."""
+    fq = phi_q(scale * q)                                  # [B,H,T,D]
+    num0 = np.einsum("bhtp,bhpc->bhtc", fq, state_in)
+    den0 = np.einsum("bhtp,bhp->bht", fq, norm_in)
+    return num0, den0
+
+
+def fwd_quadratic(q, k, v, z, scale=1.0, norm=True, state_in=None, norm_in=None):
+    """2Mamba output by the masked quadratic form, one query row at a time.
+
+    o_t = sum_{s<=t} L_ts (scale q_t.k_s)^2 v_s / sum_{s<=t} L_ts (scale q_t.k_s)^2,
+    plus the decayed initial-state term exp(g_0+...+g_t) phi_q(scale q_t).S0.
+    [2M2F §5: squared QK product, A-mask on the squared score, softmax normalisation]
+    """
+    g = decay_log(z)
+    B, H, T, _ = q.shape
+    out = np.zeros(v.shape)
+    has_init = state_in is not None
+    if has_init:
+        num0, den0 = _init_terms(q, scale, state_in, norm_in)
+    for t in range(T):
+        kw = {}
+        if has_init:
+            kw = dict(init_num=num0[:, :, t], init_den=den0[:, :, t],
+                      init_decay=np.exp(g[:, :, :t + 1].sum(axis=-1)))
+        num, den = _sq_row(q[:, :, t], k[:, :, :t + 1], v[:, :, :t + 1], g[:, :, :t + 1], scale, **kw)
+        out[:, :, t] = _normalise(num, den, norm)
+    return out
+
+
+def fwd_quadratic_rows(q, k, v, z, rows, scale=1.0, norm=True, state_in=None, norm_in=None):
+    """Form (A) evaluated only at the query positions ``rows`` -> [B, H, len(rows), dv]."""
+    g = decay_log(z)
+    res = []
+    for t in rows:
+        kw = {}
+        if state_in is not None:
+            fq = phi_q(scale * q[:, :, t])
+            kw = dict(init_num=np.einsum("bhp,bhpc->bhc", fq, state_in),
+                      init_den=np.einsum("bhp,bhp->bh", fq, norm_in),
+                      init_decay=np.exp(g[:, :, :t + 1].sum(axis=-1)))
+        num, den = _sq_row(q[:, :, t], k[:, :, :t + 1], v[:, :, :t + 1], g[:, :, :t + 1], scale, **kw)
+        res.append(_normalise(num, den, norm))
+    return np.stack(res, axis=2)
+
+
+def final_state_direct(k, v, z, state_in=None, norm_in=None):
+    """State after the last token, as a direct weighted sum over all tokens.
+
+    S_T = exp(g_0+...+g_{T-1}) S0 + sum_s exp(g_{s+1}+...+g_{T-1}) phi_k(k_s) v_s^T,
+    and the same for n with v replaced by 1.  Returns (S [B,H,D,dv], n [B,H,D]).
+    """
+    g = decay_log(z)
+    B, H, T, d = k.shape
+    # exponent for token s: sum_{r=s+1}^{T-1} g_r, summed backward from the end
+    tail = np.zeros((B, H, T))
+    tail[:, :, :T - 1] = np.cumsum(g[:, :, 1:][:, :, ::-1], axis=-1)[:, :, ::-1]
+    w = np.exp(tail)
+    fk = phi_k(k)                                            # [B,H,T,D]
+    S = np.einsum("bhtp,bht,bhtc->bhpc", fk, w, v)
+    n = np.einsum("bhtp,bht->bhp", fk, w)
+    if state_in is not None:
+        a = np.exp(g.sum(axis=-1))
+        S = S + a[..., None, None] * state_in
+        n = n + a[..., None] * norm_in
+    return S, n
+
+
+# ----------------------------------------------------------------------------
+# forms (B) and (C): token-by-token recurrence  [SSD duality, "Mamba-2 - State
+# Space Duality" thread: scalar-times-identity A makes the recurrence a causal
+# linear attention]
+# ----------------------------------------------------------------------------
+
+def fwd_recurrent_full(q, k, v, z, scale=1.0, norm=True):
+    """Form (B): recurrence over an explicit d^2 feature state vec(k k^T) v^T.
+
+    Uses no packing and no pair table; tiny inputs only.
+    """
+    g = decay_log(z)
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, d * d, dv))
+    n = np.zeros((B, H, d * d))
+    out = np.zeros(v.shape)
+    for t in range(T):
+        a = np.exp(g[:, :, t])
+        fk = np.einsum("bhi,bhj->bhij", k[:, :, t], k[:, :, t]).reshape(B, H, d * d)
+        qs = scale * q[:, :, t]
+        fq = np.einsum("bhi,bhj->bhij", qs, qs).reshape(B, H, d * d)
+        S = a[..., None, None] * S + fk[..., :, None] * v[:, :, t][..., None, :]
+        n = a[..., None] * n + fk
+        num = np.einsum("bhp,bhpc->bhc", fq, S)
+        den = np.einsum("bhp,bhp->bh", fq, n)
+        out[:, :, t] = _normalise(num, den, norm)
+    return out
+
+
+def step(q, k, v, z, state, norm_state, scale=1.0, norm=True):
+    """One decode step of the packed recurrence (form (C) for a single token).
+
+    S <- e^g S + phi_k(k) v^T ;  n <- e^g n + phi_k(k) ;  o = phi_q(scale q).S / phi_q(scale q).n
+    Inputs q,k [B,H,d], v [B,H,dv], z [B,H], state [B,H,D,dv], norm_state [B,H,D].
+    Returns (o, new_state, new_norm) without modifying the inputs.
+    """
+    a = np.exp(decay_log(z))
+    fk = phi_k(k)
+    S = a[..., None, None] * state + fk[..., :, None] * v[..., None, :]
+    n = a[..., None] * norm_state + fk
+    fq = phi_q(scale * q)
+    num = np.einsum("bhp,bhpc->bhc", fq, S)
+    den = np.einsum("bhp,bhp->bh", fq, n)
+    return _normalise(num, den, norm), S, n
+
+
+def fwd_recurrent_packed(q, k, v, z, scale=1.0, norm=True, state_in=None, norm_in=None):
+    """Form (C): the packed D-feature recurrence, token by token.
+
+    Returns (out, state_out, norm_out); the state is in the packed layout above.
+    """
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    D = num_pairs(d)
+    S = np.zeros((B, H, D, dv)) if state_in is None else np.array(state_in, dtype=np.float64)
+    n = np.zeros((B, H, D)) if norm_in is None else np.array(norm_in, dtype=np.float64)
+    out = np.zeros(v.shape)
+    for t in range(T):
+        out[:, :, t], S, n = step(q[:, :, t], k[:, :, t], v[:, :, t], z[:, :, t], S, n, scale, norm)
+    return out, S, n
+
+
+# ----------------------------------------------------------------------------
+# 2Mamba-E  [2M2F §6: exponentiated QK product = softmax attention with the
+# softplus A-mask]
+# ----------------------------------------------------------------------------
+
+def _exp_row(q_t, K, V, g_upto_t, scale):
+    lam = _row_log_mask(g_upto_t)
+    logit = scale * np.einsum("...d,...sd->...s", q_t, K) + lam
+    m = logit.max(axis=-1, keepdims=True)
+    p = np.exp(logit - m)
+    return np.einsum("...s,...sc->...c", p, V) / p.sum(axis=-1)[..., None]
+
+
+def fwd_exp_quadratic(q, k, v, z, scale=1.0):
+    """Form (E-A): masked softmax, max-subtracted, one query row at a time."""
+    g = decay_log(z)
+    T = q.shape[2]
+    out = np.zeros(v.shape)
+    for t in range(T):
+        out[:, :, t] = _exp_row(q[:, :, t], k[:, :, :t + 1], v[:, :, :t + 1], g[:, :, :t + 1], scale)
+    return out
+
+
+def fwd_exp_quadratic_rows(q, k, v, z, rows, scale=1.0):
+    g = decay_log(z)
+    return np.stack([_exp_row(q[:, :, t], k[:, :, :t + 1], v[:, :, :t + 1], g[:, :, :t + 1], scale)
+                     for t in rows], axis=2)
+
+
+def fwd_exp_streaming(q, k, v, z, scale=1.0):
+    """Form (E-B): decode-style evaluation over a growing key/value cache.
+
+    Each cached key carries a running log-decay bias; when token t arrives every
+    existing bias is decreased by softplus(z_t) and the new key enters with bias
+    0.  The query of token t then runs an online softmax (running max, running
+    sum, running weighted value) over the cache in arrival order.
+    """
+    g = decay_log(z)
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    out = np.zeros(v.shape)
+    bias = np.zeros((B, H, 0))
+    for t in range(T):
+        bias = np.concatenate([bias + g[:, :, t:t + 1], np.zeros((B, H, 1))], axis=-1)
+        m = np.full((B, H), -np.inf)
+        l = np.zeros((B, H))
+        acc = np.zeros((B, H, dv))
+        for s in range(t + 1):
+            x = scale * np.einsum("bhd,bhd->bh", q[:, :, t], k[:, :, s]) + bias[:, :, s]
+            m_new = np.maximum(m, x)
+            alpha = np.exp(m - m_new)
+            p = np.exp(x - m_new)
+            l = alpha * l + p
+            acc = alpha[..., None] * acc + p[..., None] * v[:, :, s]
+            m = m_new
+        out[:, :, t] = acc / l[..., None]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# memory accounting  [2M2F §2 KV cache of 2*N*dh per head; §5.1 crossover;
+# App. A window-1 cached q, k, v for the size-2 input convolution]
+# ----------------------------------------------------------------------------
+
+def state_elements(d: int, dv: int | None = None, conv_window: int = 2) -> int:
+    """Elements one head keeps between tokens: packed state, normaliser, conv cache."""
+    dv = d if dv is None else dv
+    D = num_pairs(d)
+    return D * dv + D + (conv_window - 1) * (2 * d + dv)
+
+
+def memory_crossover_tokens(d: int, dv: int | None = None, conv_window: int = 2) -> float:
+    """Sequence length above which the fixed state is smaller than a 2*N*dh KV cache."""
+    return state_elements(d, dv, conv_window) / (2.0 * d)
