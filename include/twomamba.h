@@ -1,0 +1,166 @@
+/*
+ * twomamba.h -- C ABI of the 2Mamba / 2Mamba-E sequence-mixing operator for
+ * AMD MI355X (gfx950).
+ *
+ * The operator is defined in "2Mamba2Furious: Linear in Complexity, Competitive
+ * in Accuracy" (paperlayer summary of arXiv 2602.17363), cited below as
+ * [2M2F §n].  It is the attention kernel of that work: it takes queries, keys
+ * and values and returns post-attention outputs, with no pre- or
+ * post-processing (no convolution, gate, residual or output norm) [2M2F App. C].
+ *
+ * Per (batch b, head h), with g_t = -softplus(z_t) and L_ts = exp(g_{s+1}+...+g_t)
+ * for s <= t (L_tt = 1):
+ *
+ *   2Mamba   (TWOMAMBA_SQ)  [2M2F §5]
+ *       w_ts = L_ts * (scale * q_t . k_s)^2
+ *       o_t  = sum_s w_ts v_s / sum_s w_ts          (o_t = 0 when the sum is 0)
+ *     The mask multiplies the squared score; it is not itself squared.
+ *   2Mamba-E (TWOMAMBA_EXP) [2M2F §6]
+ *       o_t  = softmax_{s<=t}( scale * q_t . k_s + log L_ts ) . v
+ *     i.e. softmax attention with the softplus A-mask as a log-bias.
+ *
+ * The second-order recurrent state of 2Mamba [2M2F §2, §5.1] is the symmetric
+ * tensor sum_s L k_s (x) k_s (x) v_s, stored PACKED: D = dk*(dk+1)/2 rows, row
+ * p(i,j) = i*dk - i*(i-1)/2 + (j-i) for 0 <= i <= j < dk (row-major upper
+ * triangle), each row holding dv fp32 values of the UNSCALED products
+ * k_i*k_j*v (the weight 2 of off-diagonal pairs is applied on the query side).
+ * The normaliser state has the same D rows and one value per row
+ * (sum_s L k_i k_j).  Layouts: state [B][H][D][dv], norm [B][H][D], fp32,
+ * C-contiguous.  An initial state is the state before token 0; it is decayed by
+ * g_0 like any earlier token.  A decode step consumes the decay logit of its
+ * own token.
+ *
+ * Conventions shared by every entry point:
+ *   - Every argument is checked on the host BEFORE any HIP call; an invalid
+ *     call returns a status and touches neither the device nor the buffers.
+ *   - Device pointers are caller-owned; the library allocates nothing and
+ *     keeps no pointer after the call returns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream).  A launch failure returns
+ *     TWOMAMBA_ERR_DEVICE; a fault inside a kernel surfaces at the caller's
+ *     next synchronisation.
+ *   - Outputs must not alias inputs, except that state_in == state_out and
+ *     norm_in == norm_out are allowed (exact alias: in-place resume).
+ *   - z may hold -inf (no decay for that token).  +inf and NaN in z, and
+ *     non-finite q, k, v, are undefined.
+ *   - Results are deterministic: identical inputs give bit-identical outputs
+ *     (no floating-point atomics).
+ */
+#ifndef TWOMAMBA_H
+#define TWOMAMBA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TWOMAMBA_ABI_VERSION 1
+
+typedef enum {
+    TWOMAMBA_OK = 0,
+    TWOMAMBA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    TWOMAMBA_ERR_SHAPE = 2,       /* negative size, or sizes that overflow size_t   */
+    TWOMAMBA_ERR_DTYPE = 3,       /* dtype or variant value not in its enum         */
+    TWOMAMBA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement    */
+    TWOMAMBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
+    TWOMAMBA_ERR_DEVICE = 6,      /* a HIP call failed (launch, attribute, device)  */
+    TWOMAMBA_ERR_ALIAS = 7        /* an output overlaps an input it may not alias   */
+} twomamba_status;
+
+typedef enum { TWOMAMBA_F32 = 0, TWOMAMBA_BF16 = 1 } twomamba_dtype;   /* dtype of q, k, v and out */
+
+typedef enum {
+    TWOMAMBA_SQ = 0,   /* 2Mamba: squared score, normalised by the sum of weights  [2M2F §5] */
+    TWOMAMBA_EXP = 1   /* 2Mamba-E: exponentiated score (softmax) with the A-mask   [2M2F §6] */
+} twomamba_variant;
+
+enum {
+    /* SQ only: return the numerator sum_s w_ts v_s instead of the normalised
+       output, for callers that normalise themselves (e.g. an RMSNorm as in the
+       Mamba-2 ablations, [2M2F §3]). */
+    TWOMAMBA_FLAG_NO_NORM = 1u,
+    /* Force the plain fp32 reference kernels instead of the MFMA kernels
+       (testing aid; same results within fp32 rounding). */
+    TWOMAMBA_FLAG_REFERENCE_KERNELS = 2u
+};
+
+typedef struct {
+    int B, H, T;        /* batch, heads, tokens; B, H, T >= 0 (0 = nothing to do)     */
+    int dk, dv;         /* head dims; supported: dk == dv, 16 or 64                   */
+    int chunk;          /* chunk length of the chunked form: 0 = library choice, or   *
+                         * 16, 32, 64 (reference kernels) / 64 (MFMA kernels, bf16,   *
+                         * d = 64).  The result does not depend on it beyond fp32     *
+                         * rounding.  Ignored by TWOMAMBA_EXP.                        */
+    float scale;        /* multiplies q . k before squaring / exponentiating          */
+    int variant;        /* twomamba_variant                                            */
+    int dtype;          /* twomamba_dtype                                              */
+    unsigned flags;     /* TWOMAMBA_FLAG_*                                             */
+} twomamba_fwd_desc;
+
+typedef struct {
+    int B, H;           /* batch, heads                                                */
+    int dk, dv;         /* head dims; supported: dk == dv, 16 or 64                   */
+    float scale;
+    int dtype;          /* dtype of q, k, v and out; the state is always fp32         */
+    unsigned flags;     /* TWOMAMBA_FLAG_NO_NORM                                       */
+} twomamba_step_desc;
+
+/* ABI version of the loaded library (TWOMAMBA_ABI_VERSION it was built with). */
+int twomamba_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char* twomamba_status_str(int status);
+
+/* Bytes of device workspace twomamba_fwd needs for *desc, written to *bytes.
+   Returns the same status twomamba_fwd would return for the descriptor alone. */
+int twomamba_fwd_workspace_size(const twomamba_fwd_desc* desc, size_t* bytes);
+
+/*
+ * Chunked/parallel forward of 2Mamba or 2Mamba-E over T tokens of every
+ * (b, h)  [2M2F §5, §6; chunked evaluation of the recurrence by the SSD
+ * duality, "Mamba-2 - State Space Duality" thread].
+ *
+ *   q, k      [B][H][T][dk]  dtype      device
+ *   v         [B][H][T][dv]  dtype      device
+ *   z         [B][H][T]      fp32       device   decay logits, g = -softplus(z)
+ *   state_in  [B][H][D][dv]  fp32       device   SQ only; NULL = zero state
+ *   norm_in   [B][H][D]      fp32       device   SQ only; NULL iff state_in NULL
+ *   out       [B][H][T][dv]  dtype      device   written (round to nearest even for bf16)
+ *   state_out [B][H][D][dv]  fp32       device   SQ only; NULL = not written
+ *   norm_out  [B][H][D]      fp32       device   SQ only; NULL iff state_out NULL
+ *   workspace                           device   >= twomamba_fwd_workspace_size bytes,
+ *                                                 256-byte aligned; contents undefined after
+ *
+ * TWOMAMBA_EXP takes no state pointers (it needs a KV cache, [2M2F §1, §6]):
+ * passing any returns TWOMAMBA_ERR_UNSUPPORTED.
+ */
+int twomamba_fwd(const twomamba_fwd_desc* desc,
+                 const void* q, const void* k, const void* v, const float* z,
+                 const float* state_in, const float* norm_in,
+                 void* out, float* state_out, float* norm_out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step of 2Mamba for every (b, h)  [2M2F §2 constant-size
+ * hidden state; App. A inference]:
+ *     S <- e^g S + phi(k) v^T,   n <- e^g n + phi(k),
+ *     o  = phi_q(scale q) . S / phi_q(scale q) . n      (numerator only with NO_NORM)
+ * with phi(k)_p(i,j) = k_i k_j and phi_q(q)_p(i,j) = (2 if i<j else 1) q_i q_j.
+ *
+ *   q, k   [B][H][dk]     dtype   device
+ *   v      [B][H][dv]     dtype   device
+ *   z      [B][H]         fp32    device
+ *   state  [B][H][D][dv]  fp32    device   read and updated in place
+ *   norm   [B][H][D]      fp32    device   read and updated in place
+ *   out    [B][H][dv]     dtype   device
+ */
+int twomamba_step(const twomamba_step_desc* desc,
+                  const void* q, const void* k, const void* v, const float* z,
+                  float* state, float* norm, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWOMAMBA_H */

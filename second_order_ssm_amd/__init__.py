@@ -1,0 +1,171 @@
+"""Python binding of libtwomamba.so, the MI355X 2Mamba / 2Mamba-E operator.
+
+Argument marshalling only: tensors are passed to the C ABI as raw device
+pointers together with torch's current HIP stream; every step of the
+computation runs in the library's HIP kernels.  PyTorch provides device memory
+and streams, nothing else.  If the library is not built, every entry point
+raises -- there is no fallback.
+
+    out, state, norm = fwd(q, k, v, z, variant="sq", want_state=True)
+    out = step(q, k, v, z, state, norm)          # state/norm updated in place
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "step", "library_path",
+           "TwoMambaError", "SQ", "EXP", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "num_pairs"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libtwomamba.so")
+
+SQ, EXP = 0, 1
+F32, BF16 = 0, 1
+FLAG_NO_NORM = 1
+FLAG_REFERENCE_KERNELS = 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+_VARIANT = {"sq": SQ, "exp": EXP}
+
+
+class TwoMambaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+        self.status = status
+
+
+class FwdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("T", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("scale", ctypes.c_float), ("variant", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("flags", ctypes.c_uint)]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int), ("dv", ctypes.c_int),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("flags", ctypes.c_uint)]
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load (once) and return the ctypes handle of libtwomamba.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path
+    if not os.path.exists(p):
+        raise RuntimeError(f"libtwomamba.so not built ({p}); run `python -m second_order_ssm_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp = ctypes.c_void_p
+    lib.twomamba_abi_version.restype = ctypes.c_int
+    lib.twomamba_status_str.restype = ctypes.c_char_p
+    lib.twomamba_status_str.argtypes = [ctypes.c_int]
+    lib.twomamba_fwd_workspace_size.restype = ctypes.c_int
+    lib.twomamba_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.twomamba_fwd.restype = ctypes.c_int
+    lib.twomamba_fwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+    lib.twomamba_step.restype = ctypes.c_int
+    lib.twomamba_step.argtypes = [ctypes.POINTER(StepDesc), vp, vp, vp, vp, vp, vp, vp, vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load().twomamba_abi_version()
+
+
+def status_str(status: int) -> str:
+    return load().twomamba_status_str(status).decode()
+
+
+def num_pairs(d: int) -> int:
+    return d * (d + 1) // 2
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_desc(B, H, T, dk, dv, *, variant="sq", dtype=torch.bfloat16, scale=1.0, chunk=0, flags=0) -> FwdDesc:
+    return FwdDesc(B, H, T, dk, dv, chunk, scale, _VARIANT[variant] if isinstance(variant, str) else variant,
+                   _DT[dtype] if isinstance(dtype, torch.dtype) else dtype, flags)
+
+
+def workspace_size(desc: FwdDesc) -> int:
+    n = ctypes.c_size_t(0)
+    s = load().twomamba_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_fwd_workspace_size")
+    return n.value
+
+
+def _check(t, shape, dtype, name):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, reference_kernels=False,
+        state_in=None, norm_in=None, want_state=False, out=None, state_out=None, norm_out=None, workspace=None):
+    """Chunked forward.  Returns out, or (out, state_out, norm_out) with want_state."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    flags = (FLAG_NO_NORM if no_norm else 0) | (FLAG_REFERENCE_KERNELS if reference_kernels else 0)
+    desc = make_desc(B, H, T, dk, dv, variant=variant, dtype=q.dtype, scale=scale, chunk=chunk, flags=flags)
+    _check(q, (B, H, T, dk), q.dtype, "q")
+    _check(k, (B, H, T, dk), q.dtype, "k")
+    _check(v, (B, H, T, dv), q.dtype, "v")
+    _check(z, (B, H, T), torch.float32, "z")
+    D = num_pairs(dk)
+    if state_in is not None:
+        _check(state_in, (B, H, D, dv), torch.float32, "state_in")
+        _check(norm_in, (B, H, D), torch.float32, "norm_in")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
+        norm_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    nbytes = workspace_size(desc)
+    if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    s = load().twomamba_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state_in), _ptr(norm_in),
+                            _ptr(out), _ptr(state_out), _ptr(norm_out), _ptr(workspace) if nbytes else None,
+                            ctypes.c_size_t(nbytes), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_fwd")
+    if want_state or state_out is not None:
+        return out, state_out, norm_out
+    return out
+
+
+def step(q, k, v, z, state, norm, *, scale=1.0, no_norm=False, out=None):
+    """One decode step; state [B,H,D,dv] and norm [B,H,D] (fp32) are updated in place."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(q, (B, H, dk), q.dtype, "q")
+    _check(k, (B, H, dk), q.dtype, "k")
+    _check(v, (B, H, dv), q.dtype, "v")
+    _check(z, (B, H), torch.float32, "z")
+    D = num_pairs(dk)
+    _check(state, (B, H, D, dv), torch.float32, "state")
+    _check(norm, (B, H, D), torch.float32, "norm")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    desc = StepDesc(B, H, dk, dv, scale, _DT[q.dtype], FLAG_NO_NORM if no_norm else 0)
+    s = load().twomamba_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state), _ptr(norm),
+                             _ptr(out), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_step")
+    return out

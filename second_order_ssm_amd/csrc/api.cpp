@@ -1,0 +1,217 @@
+// Host side of the 2Mamba C ABI: argument validation (before any HIP call),
+// path selection and status strings.  Kernels live in the .hip sources.
+#include <stdint.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "internal.h"
+
+using twm::FwdArgs;
+using twm::StepArgs;
+
+namespace {
+
+bool mul_ok(size_t a, size_t b, size_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+// product of non-negative ints into size_t, false on overflow
+bool prod(size_t* r, std::initializer_list<size_t> xs) {
+    size_t acc = 1;
+    for (size_t x : xs)
+        if (!mul_ok(acc, x, &acc)) return false;
+    *r = acc;
+    return true;
+}
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+bool overlaps(const Range& a, const Range& b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+Range rng(const void* p, size_t bytes) {
+    uintptr_t u = (uintptr_t)p;
+    return Range{u, p ? u + bytes : u};
+}
+
+bool supported_dims(int dk, int dv) { return dk == dv && (dk == 16 || dk == 64); }
+
+// Validates everything but pointers/workspace; fills the byte sizes.
+int check_desc(const twomamba_fwd_desc* d, size_t* qk_bytes, size_t* v_bytes, size_t* z_bytes,
+               size_t* st_bytes, size_t* nm_bytes) {
+    if (!d) return TWOMAMBA_ERR_NULL;
+    if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk <= 0 || d->dv <= 0) return TWOMAMBA_ERR_SHAPE;
+    if (d->variant != TWOMAMBA_SQ && d->variant != TWOMAMBA_EXP) return TWOMAMBA_ERR_DTYPE;
+    if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
+    if (d->flags & ~(unsigned)(TWOMAMBA_FLAG_NO_NORM | TWOMAMBA_FLAG_REFERENCE_KERNELS)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (d->variant == TWOMAMBA_EXP && (d->flags & TWOMAMBA_FLAG_NO_NORM)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (!supported_dims(d->dk, d->dv)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (!(d->scale == d->scale) || d->scale == __builtin_inff() || d->scale == -__builtin_inff())
+        return TWOMAMBA_ERR_SHAPE;
+    if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
+        return TWOMAMBA_ERR_UNSUPPORTED;
+    const size_t es = d->dtype == TWOMAMBA_BF16 ? 2 : 4;
+    const size_t B = d->B, H = d->H, T = d->T, D = twm::num_pairs(d->dk);
+    if (!prod(qk_bytes, {B, H, T, (size_t)d->dk, es}) || !prod(v_bytes, {B, H, T, (size_t)d->dv, es}) ||
+        !prod(z_bytes, {B, H, T, 4}) || !prod(st_bytes, {B, H, D, (size_t)d->dv, 4}) || !prod(nm_bytes, {B, H, D, 4}))
+        return TWOMAMBA_ERR_SHAPE;
+    // grid limits: (B*H) * chunks or query tiles must fit a 31-bit grid
+    size_t tiles = (T + 15) / 16, g;
+    if (!prod(&g, {B, H, tiles}) || g > 0x7fffffffu) return TWOMAMBA_ERR_SHAPE;
+    return TWOMAMBA_OK;
+}
+
+// Chooses the path and the effective chunk.  Returns a status.
+int plan(const twomamba_fwd_desc* d, FwdArgs* a) {
+    memset(a, 0, sizeof(*a));
+    a->B = d->B; a->H = d->H; a->T = d->T; a->dk = d->dk; a->dv = d->dv;
+    a->scale = d->scale; a->variant = d->variant; a->dtype = d->dtype; a->flags = d->flags;
+    a->chunk = d->chunk;
+    return TWOMAMBA_OK;
+}
+
+enum Path { REF, MFMA };
+
+int choose(FwdArgs* a, Path* path) {
+    const bool force_ref = (a->flags & TWOMAMBA_FLAG_REFERENCE_KERNELS) != 0;
+    if (a->variant == TWOMAMBA_EXP) {
+        a->chunk = 0;
+        *path = (!force_ref && twm::mfma_exp_supported(*a)) ? MFMA : REF;
+        return TWOMAMBA_OK;
+    }
+    if (!force_ref) {
+        FwdArgs t = *a;
+        if (t.chunk == 0) t.chunk = 64;
+        if (twm::mfma_sq_supported(t)) {
+            *a = t;
+            *path = MFMA;
+            return TWOMAMBA_OK;
+        }
+    }
+    if (a->chunk == 0) a->chunk = 64;
+    if (a->chunk > 64) return TWOMAMBA_ERR_UNSUPPORTED;   // reference kernels stage <= 64 tokens
+    *path = REF;
+    return TWOMAMBA_OK;
+}
+
+size_t workspace_for(const FwdArgs& a, Path path) {
+    if (a.variant == TWOMAMBA_EXP) return 0;
+    return path == MFMA ? twm::mfma_sq_workspace(a) : twm::ref_sq_workspace(a);
+}
+
+}  // namespace
+
+extern "C" {
+
+int twomamba_abi_version(void) { return TWOMAMBA_ABI_VERSION; }
+
+const char* twomamba_status_str(int s) {
+    switch (s) {
+        case TWOMAMBA_OK: return "ok";
+        case TWOMAMBA_ERR_NULL: return "required pointer is NULL";
+        case TWOMAMBA_ERR_SHAPE: return "invalid or overflowing shape/scale";
+        case TWOMAMBA_ERR_DTYPE: return "invalid dtype or variant";
+        case TWOMAMBA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TWOMAMBA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case TWOMAMBA_ERR_DEVICE: return "HIP launch or device error";
+        case TWOMAMBA_ERR_ALIAS: return "output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+int twomamba_fwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
+    if (!bytes) return TWOMAMBA_ERR_NULL;
+    *bytes = 0;
+    size_t a1, a2, a3, a4, a5;
+    int s = check_desc(d, &a1, &a2, &a3, &a4, &a5);
+    if (s != TWOMAMBA_OK) return s;
+    FwdArgs a;
+    plan(d, &a);
+    Path path;
+    s = choose(&a, &path);
+    if (s != TWOMAMBA_OK) return s;
+    *bytes = workspace_for(a, path);
+    return TWOMAMBA_OK;
+}
+
+int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                 const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    size_t qkb, vb, zb, sb, nb;
+    int s = check_desc(d, &qkb, &vb, &zb, &sb, &nb);
+    if (s != TWOMAMBA_OK) return s;
+    const bool any = qkb != 0;   // B*H*T > 0
+    const bool sq = d->variant == TWOMAMBA_SQ;
+    if (!sq && (state_in || norm_in || state_out || norm_out)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if ((state_in == nullptr) != (norm_in == nullptr)) return TWOMAMBA_ERR_NULL;
+    if ((state_out == nullptr) != (norm_out == nullptr)) return TWOMAMBA_ERR_NULL;
+    if (any && (!q || !k || !v || !z || !out)) return TWOMAMBA_ERR_NULL;
+
+    // aliasing: out and the state outputs may not touch any input; the state
+    // outputs may alias the state inputs only exactly (in-place resume).
+    const Range rq = rng(q, qkb), rk = rng(k, qkb), rv = rng(v, vb), rz = rng(z, zb);
+    const Range rsi = rng(state_in, sb), rni = rng(norm_in, nb), ro = rng(out, vb);
+    const Range rso = rng(state_out, sb), rno = rng(norm_out, nb);
+    for (const Range& in : {rq, rk, rv, rz, rsi, rni})
+        if (overlaps(ro, in)) return TWOMAMBA_ERR_ALIAS;
+    for (const Range& in : {rq, rk, rv, rz, ro})
+        if (overlaps(rso, in) || overlaps(rno, in)) return TWOMAMBA_ERR_ALIAS;
+    if (overlaps(rso, rno)) return TWOMAMBA_ERR_ALIAS;
+    if (overlaps(rso, rsi) && state_out != state_in) return TWOMAMBA_ERR_ALIAS;
+    if (overlaps(rno, rni) && norm_out != norm_in) return TWOMAMBA_ERR_ALIAS;
+    if (overlaps(rso, rni) || overlaps(rno, rsi)) return TWOMAMBA_ERR_ALIAS;
+
+    FwdArgs a;
+    plan(d, &a);
+    Path path;
+    s = choose(&a, &path);
+    if (s != TWOMAMBA_OK) return s;
+    const size_t need = workspace_for(a, path);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
+        const Range rw = rng(workspace, need);
+        for (const Range& o : {rq, rk, rv, rz, rsi, rni, ro, rso, rno})
+            if (overlaps(rw, o)) return TWOMAMBA_ERR_ALIAS;
+    }
+    a.q = q; a.k = k; a.v = v; a.z = z;
+    a.state_in = state_in; a.norm_in = norm_in;
+    a.out = out; a.state_out = state_out; a.norm_out = norm_out;
+    a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
+    if (a.variant == TWOMAMBA_EXP) return path == MFMA ? twm::mfma_exp_fwd(a) : twm::ref_exp_fwd(a);
+    return path == MFMA ? twm::mfma_sq_fwd(a) : twm::ref_sq_fwd(a);
+}
+
+int twomamba_step(const twomamba_step_desc* d, const void* q, const void* k, const void* v, const float* z,
+                  float* state, float* norm, void* out, void* stream) {
+    if (!d) return TWOMAMBA_ERR_NULL;
+    if (d->B < 0 || d->H < 0 || d->dk <= 0 || d->dv <= 0) return TWOMAMBA_ERR_SHAPE;
+    if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
+    if (d->flags & ~(unsigned)TWOMAMBA_FLAG_NO_NORM) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (!supported_dims(d->dk, d->dv)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (!(d->scale == d->scale) || d->scale == __builtin_inff() || d->scale == -__builtin_inff())
+        return TWOMAMBA_ERR_SHAPE;
+    const size_t es = d->dtype == TWOMAMBA_BF16 ? 2 : 4;
+    const size_t B = d->B, H = d->H, D = twm::num_pairs(d->dk);
+    size_t qkb, vb, zb, sb, nb;
+    if (!prod(&qkb, {B, H, (size_t)d->dk, es}) || !prod(&vb, {B, H, (size_t)d->dv, es}) || !prod(&zb, {B, H, 4}) ||
+        !prod(&sb, {B, H, D, (size_t)d->dv, 4}) || !prod(&nb, {B, H, D, 4}))
+        return TWOMAMBA_ERR_SHAPE;
+    if (B * H > 0x7fffffffu) return TWOMAMBA_ERR_SHAPE;
+    if (B * H == 0) return TWOMAMBA_OK;
+    if (!q || !k || !v || !z || !state || !norm || !out) return TWOMAMBA_ERR_NULL;
+    const Range rq = rng(q, qkb), rk = rng(k, qkb), rv = rng(v, vb), rz = rng(z, zb);
+    const Range rs = rng(state, sb), rn = rng(norm, nb), ro = rng(out, vb);
+    for (const Range& w : {rs, rn, ro})
+        for (const Range& in : {rq, rk, rv, rz})
+            if (overlaps(w, in)) return TWOMAMBA_ERR_ALIAS;
+    if (overlaps(rs, rn) || overlaps(rs, ro) || overlaps(rn, ro)) return TWOMAMBA_ERR_ALIAS;
+    StepArgs a;
+    a.B = d->B; a.H = d->H; a.dk = d->dk; a.dv = d->dv; a.scale = d->scale; a.dtype = d->dtype; a.flags = d->flags;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.state = state; a.norm = norm; a.out = out; a.stream = stream;
+    return twm::step_launch(a);
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal declarations shared by the host dispatcher and the HIP kernels of
+// the 2Mamba library.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/twomamba.h"
+
+namespace twm {
+
+// Everything the kernels need about one forward call, already validated.
+struct FwdArgs {
+    int B, H, T, dk, dv, chunk;
+    float scale;
+    int variant, dtype;
+    unsigned flags;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* z;
+    const float* state_in;
+    const float* norm_in;
+    void* out;
+    float* state_out;
+    float* norm_out;
+    void* ws;
+    size_t ws_bytes;
+    void* stream;
+};
+
+struct StepArgs {
+    int B, H, dk, dv;
+    float scale;
+    int dtype;
+    unsigned flags;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* z;
+    float* state;
+    float* norm;
+    void* out;
+    void* stream;
+};
+
+inline size_t num_pairs(int d) { return (size_t)d * (size_t)(d + 1) / 2; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- reference (plain fp32) kernels: any supported d, chunk 16/32/64 -------
+size_t ref_sq_workspace(const FwdArgs& a);
+int ref_sq_fwd(const FwdArgs& a);      // returns twomamba_status
+int ref_exp_fwd(const FwdArgs& a);
+
+// ---- MFMA kernels: bf16, dk = dv = 64 ---------------------------------------
+bool mfma_sq_supported(const FwdArgs& a);
+size_t mfma_sq_workspace(const FwdArgs& a);
+int mfma_sq_fwd(const FwdArgs& a);
+bool mfma_exp_supported(const FwdArgs& a);
+int mfma_exp_fwd(const FwdArgs& a);
+
+// ---- decode step -------------------------------------------------------------
+int step_launch(const StepArgs& a);
+
+}  // namespace twm

@@ -1,0 +1,150 @@
+// Recurrent decode step of 2Mamba ("2Mamba2Furious", §2 constant-size second-order
+// hidden state; App. A inference):
+//     S <- e^g S + phi(k) v^T,   n <- e^g n + phi(k),   o = phi_q(q).S / phi_q(q).n
+//
+// Bandwidth-bound: per head the packed fp32 state is D x dv (532 KB at d = 64) and
+// is read and written once.  One workgroup per (b, h) streams that head's rows
+// front to back; consecutive threads own consecutive 16-byte column slices of a
+// row, so every wave reads and writes whole contiguous rows (fully coalesced).
+// The readout sum over rows is reduced in a fixed order through LDS, so results
+// are bit-reproducible.
+#include "device_common.h"
+#include "internal.h"
+
+namespace twm {
+namespace {
+
+constexpr int kStepThreads = 256;
+
+template <int DK, int DV, typename In>
+__global__ void __launch_bounds__(kStepThreads)
+step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+            const float* __restrict__ z, float* __restrict__ state, float* __restrict__ norm,
+            In* __restrict__ out, float scale, int no_norm) {
+    constexpr int D = DK * (DK + 1) / 2;
+    constexpr int CG = DV / 4;                 // float4 column groups per row
+    constexpr int NR = kStepThreads / CG;      // rows processed per sweep
+    constexpr int UNR = 4;                     // rows in flight per thread
+
+    __shared__ float s_q[DK], s_k[DK], s_v[DV];
+    __shared__ float s_fk[D], s_fq[D];
+    __shared__ float4 s_part[NR][CG];
+    __shared__ float s_den[kStepThreads / 64];
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const size_t hoff = (size_t)bh;
+
+    if (tid < DK) {
+        s_q[tid] = IO<In>::ld(q, hoff * DK + tid) * scale;
+        s_k[tid] = IO<In>::ld(k, hoff * DK + tid);
+    }
+    if (tid < DV) s_v[tid] = IO<In>::ld(v, hoff * DV + tid);
+    const float a = expf(decay_log(z[hoff]));
+    __syncthreads();
+
+    // features of this token, one row i of the upper triangle per thread
+    if (tid < DK) {
+        const int i = tid;
+        int p = i * DK - (i * (i - 1)) / 2;
+        const float ki = s_k[i], qi = s_q[i];
+        for (int j = i; j < DK; ++j, ++p) {
+            s_fk[p] = ki * s_k[j];
+            s_fq[p] = (j == i ? 1.f : 2.f) * qi * s_q[j];
+        }
+    }
+    __syncthreads();
+
+    const int cg = tid % CG;
+    const int rs = tid / CG;
+    const float4 v4 = make_float4(s_v[4 * cg], s_v[4 * cg + 1], s_v[4 * cg + 2], s_v[4 * cg + 3]);
+    float4* S = reinterpret_cast<float4*>(state + hoff * (size_t)D * DV);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    int p = rs;
+    for (; p + (UNR - 1) * NR < D; p += UNR * NR) {
+        float4 x[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) x[u] = S[(size_t)(p + u * NR) * CG + cg];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int pr = p + u * NR;
+            const float fk = s_fk[pr], fq = s_fq[pr];
+            float4 y;
+            y.x = fmaf(a, x[u].x, fk * v4.x);
+            y.y = fmaf(a, x[u].y, fk * v4.y);
+            y.z = fmaf(a, x[u].z, fk * v4.z);
+            y.w = fmaf(a, x[u].w, fk * v4.w);
+            S[(size_t)pr * CG + cg] = y;
+            acc.x = fmaf(fq, y.x, acc.x);
+            acc.y = fmaf(fq, y.y, acc.y);
+            acc.z = fmaf(fq, y.z, acc.z);
+            acc.w = fmaf(fq, y.w, acc.w);
+        }
+    }
+    for (; p < D; p += NR) {
+        const float4 x = S[(size_t)p * CG + cg];
+        const float fk = s_fk[p], fq = s_fq[p];
+        float4 y;
+        y.x = fmaf(a, x.x, fk * v4.x);
+        y.y = fmaf(a, x.y, fk * v4.y);
+        y.z = fmaf(a, x.z, fk * v4.z);
+        y.w = fmaf(a, x.w, fk * v4.w);
+        S[(size_t)p * CG + cg] = y;
+        acc.x = fmaf(fq, y.x, acc.x);
+        acc.y = fmaf(fq, y.y, acc.y);
+        acc.z = fmaf(fq, y.z, acc.z);
+        acc.w = fmaf(fq, y.w, acc.w);
+    }
+    s_part[rs][cg] = acc;
+
+    // normaliser rows
+    float den = 0.f;
+    float* n = norm + hoff * (size_t)D;
+    for (int r = tid; r < D; r += kStepThreads) {
+        const float y = fmaf(a, n[r], s_fk[r]);
+        n[r] = y;
+        den = fmaf(s_fq[r], y, den);
+    }
+    // fixed-order wave reduction of den
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_down(den, off, 64);
+    if ((tid & 63) == 0) s_den[tid >> 6] = den;
+    __syncthreads();
+
+    if (tid < DV) {
+        const int c = tid;
+        float num = 0.f;
+        for (int r = 0; r < NR; ++r) {
+            const float4 t4 = s_part[r][c >> 2];
+            num += (c & 3) == 0 ? t4.x : (c & 3) == 1 ? t4.y : (c & 3) == 2 ? t4.z : t4.w;
+        }
+        float dsum = 0.f;
+        for (int w = 0; w < kStepThreads / 64; ++w) dsum += s_den[w];
+        float o;
+        if (no_norm) o = num;
+        else o = (dsum == 0.f) ? 0.f : num / dsum;
+        IO<In>::st(out, hoff * DV + c, o);
+    }
+}
+
+template <int DK, int DV, typename In>
+int launch(const StepArgs& a) {
+    const int nbh = a.B * a.H;
+    hipStream_t st = (hipStream_t)a.stream;
+    hipLaunchKernelGGL((step_kernel<DK, DV, In>), dim3(nbh), dim3(kStepThreads), 0, st,
+                       (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, a.state, a.norm, (In*)a.out,
+                       a.scale, (int)((a.flags & TWOMAMBA_FLAG_NO_NORM) != 0));
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+}  // namespace
+
+int step_launch(const StepArgs& a) {
+    if (a.B == 0 || a.H == 0) return TWOMAMBA_OK;
+    const bool bf = a.dtype == TWOMAMBA_BF16;
+    if (a.dk == 64) return bf ? launch<64, 64, bf16>(a) : launch<64, 64, float>(a);
+    if (a.dk == 16) return bf ? launch<16, 16, bf16>(a) : launch<16, 16, float>(a);
+    return TWOMAMBA_ERR_UNSUPPORTED;
+}
+
+}  // namespace twm

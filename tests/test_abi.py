@@ -1,0 +1,165 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid calls with the documented status before
+making any HIP call (fake non-NULL pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import second_order_ssm_amd as tmb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twomamba.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EDEV, EALIAS = range(8)
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tmb.library_path), reason="libtwomamba.so not built")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tmb.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(twomamba_\w+)\s*\(", src)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert {"twomamba_fwd", "twomamba_step", "twomamba_fwd_workspace_size", "twomamba_abi_version",
+            "twomamba_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.twomamba_abi_version() == 1
+    seen = set()
+    for s in range(8):
+        txt = lib.twomamba_status_str(s).decode()
+        assert txt and txt != "unknown status"
+        seen.add(txt)
+    assert len(seen) == 8
+    assert lib.twomamba_status_str(99).decode() == "unknown status"
+
+
+# fake, distinct, 256-aligned device addresses; validation never touches them
+BASE = 0x7F0000000000
+GAP = 1 << 34
+
+
+def fake(i):
+    return ctypes.c_void_p(BASE + i * GAP)
+
+
+def desc(B=2, H=3, T=100, d=64, variant=0, dtype=1, chunk=0, scale=1.0, flags=0):
+    return tmb.FwdDesc(B, H, T, d, d, chunk, scale, variant, dtype, flags)
+
+
+def call_fwd(lib, dsc, q=1, k=2, v=3, z=4, si=None, ni=None, out=5, so=None, no=None, ws=9, wsb=1 << 40):
+    p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
+    return lib.twomamba_fwd(ctypes.byref(dsc) if dsc is not None else None, p(q), p(k), p(v), p(z), p(si), p(ni),
+                            p(out), p(so), p(no), p(ws), ctypes.c_size_t(wsb), None)
+
+
+def ws_size(lib, dsc):
+    n = ctypes.c_size_t(12345)
+    s = lib.twomamba_fwd_workspace_size(ctypes.byref(dsc), ctypes.byref(n))
+    return s, n.value
+
+
+def test_workspace_size_reference_path(lib):
+    # reference kernels: per-chunk state + normaliser + chunk decay per head
+    d = desc(B=2, H=3, T=100, d=64, dtype=0, flags=tmb.FLAG_REFERENCE_KERNELS, chunk=64)
+    s, n = ws_size(lib, d)
+    assert s == OK
+    nbh, nc, D = 6, 2, 2080
+    a256 = lambda x: (x + 255) // 256 * 256
+    expect = a256(a256(a256(nbh * nc * D * 64 * 4) + nbh * nc * D * 4) + nbh * nc * 4)
+    assert n == expect
+    assert ws_size(lib, desc(variant=1, flags=tmb.FLAG_REFERENCE_KERNELS)) == (OK, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ESHAPE), (dict(T=-5), ESHAPE), (dict(d=0), ESHAPE),
+    (dict(dtype=7), EDTYPE), (dict(variant=3), EDTYPE),
+    (dict(d=32), EUNSUP), (dict(d=128), EUNSUP), (dict(chunk=48), EUNSUP), (dict(flags=1 << 7), EUNSUP),
+    (dict(variant=1, flags=1), EUNSUP), (dict(chunk=128, flags=2), EUNSUP), (dict(chunk=128, dtype=0), EUNSUP),
+    (dict(scale=float("nan")), ESHAPE), (dict(scale=float("inf")), ESHAPE),
+    (dict(B=1 << 30, H=1 << 30, T=1 << 30), ESHAPE),
+])
+def test_bad_descriptor(lib, kw, status):
+    d = desc(**kw)
+    assert ws_size(lib, d)[0] == status
+    assert call_fwd(lib, d) == status
+
+
+def test_null_arguments(lib):
+    assert call_fwd(lib, None) == ENULL
+    n = ctypes.c_size_t(0)
+    assert lib.twomamba_fwd_workspace_size(ctypes.byref(desc()), None) == ENULL
+    assert lib.twomamba_fwd_workspace_size(None, ctypes.byref(n)) == ENULL
+    for field in ("q", "k", "v", "z", "out"):
+        assert call_fwd(lib, desc(), **{field: None}) == ENULL
+    # state pointers come in pairs
+    assert call_fwd(lib, desc(), si=6, ni=None) == ENULL
+    assert call_fwd(lib, desc(), so=7, no=None) == ENULL
+
+
+def test_exp_rejects_state(lib):
+    assert call_fwd(lib, desc(variant=1), si=6, ni=7) == EUNSUP
+    assert call_fwd(lib, desc(variant=1), so=6, no=7) == EUNSUP
+
+
+def test_workspace_checks(lib):
+    d = desc(dtype=0, flags=tmb.FLAG_REFERENCE_KERNELS)
+    _, need = ws_size(lib, d)
+    assert need > 0
+    assert call_fwd(lib, d, ws=None) == EWS
+    assert call_fwd(lib, d, wsb=need - 1) == EWS
+    assert call_fwd(lib, d, ws=ctypes.c_void_p(BASE + 9 * GAP + 16)) == EWS     # not 256-aligned
+
+
+def test_alias_checks(lib):
+    d = desc(dtype=0, flags=tmb.FLAG_REFERENCE_KERNELS)
+    assert call_fwd(lib, d, out=1) == EALIAS                                  # out == q
+    assert call_fwd(lib, d, out=ctypes.c_void_p(BASE + 2 * GAP + 64)) == EALIAS  # out inside k
+    assert call_fwd(lib, d, ws=3) == EALIAS                                   # workspace == v
+    assert call_fwd(lib, d, si=6, ni=7, so=ctypes.c_void_p(BASE + 6 * GAP + 256), no=8) == EALIAS  # partial alias
+    assert call_fwd(lib, d, si=6, ni=7, so=7, no=8) == EALIAS                 # state_out over norm_in
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert call_fwd(lib, desc(B=0), q=None, k=None, v=None, z=None, out=None, ws=None, wsb=0) == OK
+
+
+def call_step(lib, dsc, q=1, k=2, v=3, z=4, s=5, n=6, out=7):
+    p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
+    return lib.twomamba_step(ctypes.byref(dsc) if dsc is not None else None, p(q), p(k), p(v), p(z), p(s), p(n),
+                             p(out), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ESHAPE), (dict(dk=32, dv=32), EUNSUP), (dict(dk=64, dv=16), EUNSUP), (dict(dtype=5), EDTYPE),
+    (dict(flags=2), EUNSUP), (dict(scale=float("nan")), ESHAPE),
+])
+def test_step_bad_descriptor(lib, kw, status):
+    a = dict(B=4, H=2, dk=64, dv=64, scale=1.0, dtype=1, flags=0)
+    a.update(kw)
+    assert call_step(lib, tmb.StepDesc(**a)) == status
+
+
+def test_step_null_and_alias(lib):
+    d = tmb.StepDesc(B=4, H=2, dk=64, dv=64, scale=1.0, dtype=1, flags=0)
+    assert call_step(lib, None) == ENULL
+    for f in ("q", "k", "v", "z", "s", "n", "out"):
+        assert call_step(lib, d, **{f: None}) == ENULL
+    assert call_step(lib, d, out=1) == EALIAS
+    assert call_step(lib, d, n=5) == EALIAS
+    assert call_step(lib, tmb.StepDesc(B=0, H=2, dk=64, dv=64, scale=1.0, dtype=1, flags=0),
+                     q=None, k=None, v=None, z=None, s=None, n=None, out=None) == OK

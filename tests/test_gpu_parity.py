@@ -1,0 +1,165 @@
+"""GPU parity of the HIP path against the fp64 oracle (small and ragged cases).
+
+Every case runs through the C ABI (via the ctypes binding) on cuda:0 and is
+compared element by element with the oracle on the same seeded inputs, using
+the per-head inf-norm relative error: <= 1e-4 for fp32 inputs, <= 2e-2 for bf16
+inputs with fp32 accumulation.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import second_order_ssm_amd as tmb
+import synth_inputs as SI
+from oracle import twomamba_oracle as O
+from gpu_util import TOL, announce, dev, host64, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_inputs(q, k, v, z):
+    return SI.to_f64(q), SI.to_f64(k), SI.to_f64(v), SI.to_f64(z)
+
+
+def run_sq(q, k, v, z, **kw):
+    res = tmb.fwd(*dev(q, k, v, z), variant="sq", **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+# ------------------------------------------------------------------ 2Mamba, reference kernels
+
+def test_config1_tiny_fp32():
+    announce("cfg1 SQ fp32 B=1 H=2 T=256 d=16 seed 0, reference kernels")
+    q, k, v, z = SI.draw(1, 2, 256, 16, seed=0, dtype="f32")
+    out, S, n = run_sq(q, k, v, z, chunk=64, reference_kernels=True, want_state=True)
+    qq, kk, vv, zz = oracle_inputs(q, k, v, z)
+    ref = O.fwd_quadratic(qq, kk, vv, zz)
+    ref_c, S_ref, n_ref = O.fwd_recurrent_packed(qq, kk, vv, zz)
+    assert relerr(ref_c, ref) < 1e-10          # the oracle's own forms agree first
+    assert relerr(host64(out), ref) < TOL["f32"]
+    assert relerr(host64(S), S_ref) < TOL["f32"]
+    assert relerr(host64(n), n_ref) < TOL["f32"]
+
+
+CASES = [
+    # (dtype, d, T, chunk, z_mean, z_neg_inf)
+    ("f32", 16, 100, 16, 0.0, False),
+    ("f32", 16, 65, 32, -6.0, False),
+    ("f32", 64, 100, 64, 0.0, False),
+    ("f32", 64, 130, 32, -8.0, False),
+    ("f32", 64, 63, 16, 0.0, True),
+    ("bf16", 64, 200, 64, -6.0, False),
+    ("bf16", 64, 1, 64, 0.0, False),
+    ("bf16", 16, 129, 64, -10.0, False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,T,chunk,zm,zinf", CASES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_sq_reference_kernels(dtype, d, T, chunk, zm, zinf, with_state):
+    announce(f"SQ ref {dtype} d={d} T={T} chunk={chunk} z_mean={zm} ninf={zinf} state={with_state}")
+    B, H = 2, 3
+    q, k, v, z = SI.draw(B, H, T, d, seed=T + d, dtype=dtype, z_mean=zm, z_neg_inf=zinf)
+    qq, kk, vv, zz = oracle_inputs(q, k, v, z)
+    kw = {}
+    if with_state:
+        # a carried state the oracle produces from an earlier stretch of tokens
+        q0, k0, v0, z0 = SI.draw(B, H, 40, d, seed=7, dtype="f32", z_mean=zm)
+        S0, n0 = O.final_state_direct(SI.to_f64(k0), SI.to_f64(v0), SI.to_f64(z0))
+        kw = dict(state_in=torch.from_numpy(S0.astype(np.float32)).cuda(),
+                  norm_in=torch.from_numpy(n0.astype(np.float32)).cuda())
+        S0, n0 = host64(kw["state_in"]), host64(kw["norm_in"])
+    out, S, n = run_sq(q, k, v, z, chunk=chunk, reference_kernels=True, want_state=True, **kw)
+    ref = O.fwd_quadratic(qq, kk, vv, zz, state_in=S0 if with_state else None, norm_in=n0 if with_state else None)
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz, state_in=S0 if with_state else None,
+                                        norm_in=n0 if with_state else None)
+    assert relerr(host64(out), ref) < TOL[dtype]
+    assert relerr(host64(S), S_ref) < 1e-4
+    assert relerr(host64(n), n_ref) < 1e-4
+
+
+def test_sq_no_norm_and_scale():
+    announce("SQ ref NO_NORM + scale, fp32 d=16")
+    q, k, v, z = SI.draw(1, 2, 90, 16, seed=3, dtype="f32", z_mean=-2.0)
+    qq, kk, vv, zz = oracle_inputs(q, k, v, z)
+    out = run_sq(q, k, v, z, chunk=32, reference_kernels=True, no_norm=True, scale=0.7)
+    assert relerr(host64(out), O.fwd_quadratic(qq, kk, vv, zz, scale=0.7, norm=False)) < TOL["f32"]
+
+
+def test_sq_empty_sequence_passes_state_through():
+    announce("SQ ref T=0 state passthrough")
+    d = 16
+    D = d * (d + 1) // 2
+    S0 = torch.randn(1, 2, D, d, device="cuda")
+    n0 = torch.rand(1, 2, D, device="cuda")
+    q = torch.empty(1, 2, 0, d, device="cuda")
+    z = torch.empty(1, 2, 0, device="cuda")
+    out, S, n = tmb.fwd(q, q, q, z, reference_kernels=True, state_in=S0, norm_in=n0, want_state=True)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and torch.equal(S, S0) and torch.equal(n, n0)
+
+
+# ------------------------------------------------------------------ 2Mamba-E, reference kernel
+
+@pytest.mark.parametrize("dtype,d,T,zm,zinf", [
+    ("f32", 16, 150, 0.0, False), ("f32", 64, 129, -6.0, False), ("f32", 64, 70, 0.0, True),
+    ("bf16", 64, 200, -8.0, False), ("bf16", 16, 1, 0.0, False),
+])
+def test_exp_reference_kernel(dtype, d, T, zm, zinf):
+    announce(f"EXP ref {dtype} d={d} T={T} z_mean={zm} ninf={zinf}")
+    q, k, v, z = SI.draw(2, 2, T, d, seed=11 + T, dtype=dtype, z_mean=zm, z_neg_inf=zinf)
+    out = tmb.fwd(*dev(q, k, v, z), variant="exp", scale=1.3, reference_kernels=True)
+    torch.cuda.synchronize()
+    ref = O.fwd_exp_quadratic(*oracle_inputs(q, k, v, z), scale=1.3)
+    assert relerr(host64(out), ref) < TOL[dtype]
+
+
+# ------------------------------------------------------------------ decode step
+
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 64), ("bf16", 64)])
+@pytest.mark.parametrize("no_norm", [False, True])
+def test_step_matches_oracle(dtype, d, no_norm):
+    announce(f"step {dtype} d={d} no_norm={no_norm}")
+    B, H = 3, 5
+    q0, k0, v0, z0 = SI.draw(B, H, 30, d, seed=5, dtype="f32", z_mean=-3.0)
+    S, n = O.final_state_direct(SI.to_f64(k0), SI.to_f64(v0), SI.to_f64(z0))
+    Sd = torch.from_numpy(S.astype(np.float32)).cuda()
+    nd = torch.from_numpy(n.astype(np.float32)).cuda()
+    S, n = host64(Sd), host64(nd)
+    q, k, v, z = SI.draw(B, H, 4, d, seed=6, dtype=dtype, z_mean=-1.0)
+    for t in range(4):
+        args = [x[:, :, t].contiguous() for x in (q, k, v)] + [z[:, :, t].contiguous()]
+        o = tmb.step(*dev(*args), Sd, nd, scale=0.9, no_norm=no_norm)
+        torch.cuda.synchronize()
+        ro, S, n = O.step(*[SI.to_f64(a) for a in args], S, n, scale=0.9, norm=not no_norm)
+        assert relerr(host64(o)[:, :, None], ro[:, :, None]) < TOL[dtype]
+        assert relerr(host64(Sd), S) < 1e-5
+        assert relerr(host64(nd), n) < 1e-5
+
+
+def test_forward_then_steps_equals_longer_forward():
+    announce("fwd(T0) -> state -> steps == fwd(T0+k), ref kernels fp32 d=64")
+    B, H, d, T0, K = 1, 2, 64, 70, 5
+    q, k, v, z = SI.draw(B, H, T0 + K, d, seed=21, dtype="f32", z_mean=-4.0)
+    full = run_sq(q, k, v, z, reference_kernels=True)
+    _, S, n = run_sq(q[:, :, :T0].contiguous(), k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(),
+                     z[:, :, :T0].contiguous(), reference_kernels=True, want_state=True)
+    for t in range(T0, T0 + K):
+        o = tmb.step(*dev(*[x[:, :, t].contiguous() for x in (q, k, v, z)]), S, n)
+        torch.cuda.synchronize()
+        assert relerr(host64(o)[:, :, None], host64(full)[:, :, t:t + 1]) < 1e-5
+
+
+def test_reference_kernels_are_deterministic():
+    announce("determinism ref SQ/EXP/step")
+    q, k, v, z = dev(*SI.draw(2, 2, 150, 64, seed=9, dtype="bf16", z_mean=-5.0))
+    a = tmb.fwd(q, k, v, z, reference_kernels=True, want_state=True)
+    b = tmb.fwd(q, k, v, z, reference_kernels=True, want_state=True)
+    e1 = tmb.fwd(q, k, v, z, variant="exp", reference_kernels=True)
+    e2 = tmb.fwd(q, k, v, z, variant="exp", reference_kernels=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert torch.equal(e1, e2)
