@@ -68,8 +68,8 @@ def test_sq_reference_kernels(dtype, d, T, chunk, zm, zinf, with_state):
         # a carried state the oracle produces from an earlier stretch of tokens
         q0, k0, v0, z0 = SI.draw(B, H, 40, d, seed=7, dtype="f32", z_mean=zm)
         S0, n0 = O.final_state_direct(SI.to_f64(k0), SI.to_f64(v0), SI.to_f64(z0))
-        kw = dict(state_in=torch.from_numpy(S0.astype(np.float32)).cuda(),
-                  norm_in=torch.from_numpy(n0.astype(np.float32)).cuda())
+        kw = dict(state_in=torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).cuda(),
+                  norm_in=torch.from_numpy(np.ascontiguousarray(n0, dtype=np.float32)).cuda())
         S0, n0 = host64(kw["state_in"]), host64(kw["norm_in"])
     out, S, n = run_sq(q, k, v, z, chunk=chunk, reference_kernels=True, want_state=True, **kw)
     ref = O.fwd_quadratic(qq, kk, vv, zz, state_in=S0 if with_state else None, norm_in=n0 if with_state else None)
@@ -125,8 +125,8 @@ def test_step_matches_oracle(dtype, d, no_norm):
     B, H = 3, 5
     q0, k0, v0, z0 = SI.draw(B, H, 30, d, seed=5, dtype="f32", z_mean=-3.0)
     S, n = O.final_state_direct(SI.to_f64(k0), SI.to_f64(v0), SI.to_f64(z0))
-    Sd = torch.from_numpy(S.astype(np.float32)).cuda()
-    nd = torch.from_numpy(n.astype(np.float32)).cuda()
+    Sd = torch.from_numpy(np.ascontiguousarray(S, dtype=np.float32)).cuda()
+    nd = torch.from_numpy(np.ascontiguousarray(n, dtype=np.float32)).cuda()
     S, n = host64(Sd), host64(nd)
     q, k, v, z = SI.draw(B, H, 4, d, seed=6, dtype=dtype, z_mean=-1.0)
     for t in range(4):
