@@ -1,0 +1,247 @@
+"""Benchmark of the 2Mamba operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs sq,exp,step] [--cpu-seconds S]
+
+A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
+chunk state, inter-chunk scan, readout, normalisation) over one batch of the
+long-context workload B=2, H=16, T=8192, d_k=d_v=64, bf16 inputs, seeded
+synthetic data.  ``value`` is its whole-job throughput in head-tokens/s with
+all inputs resident in HBM.  The same run also measures, each in its own timed
+loop, the 2Mamba-E forward on the same shape and the recurrent decode step
+(batch 64, 32 heads, fp32 packed state of 1.09 GB, 256 sequential steps after
+a T=2048 prefill); they are reported under ``legs``.
+
+The roofline entry is for the dominant kernel of the timed step: algorithmic
+work attributed to that kernel per launch divided by its average duration,
+measured with HIP events on the stream the kernel runs on (a second loop over
+the same inputs through twomamba_fwd_timed).  ``cpu_baseline`` times the fp64
+oracle (packed recurrent form) on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd tokens/s (B·H·T, d=64, bf16) + % MFMA peak; decode step HBM GB/s"
+PEAK_BF16_FLOPS = 2.5e15        # MI355X dense bf16/fp16 MFMA
+PEAK_FP32_VALU_FLOPS = 157.3e12 # MI355X fp32 vector
+PEAK_HBM = 8.0e12               # MI355X HBM3E bytes/s
+
+SQ_SHAPE = dict(B=2, H=16, T=8192, d=64, seed=3)
+EXP_SHAPE = dict(B=2, H=16, T=8192, d=64, seed=3)
+STEP_SHAPE = dict(B=64, H=32, d=64, prefill_T=2048, prefill_seed=4, steps=256)
+
+
+def sq_flops_per_head_token(d=64, dv=64, c0=64):
+    """Algorithmic 2Mamba work: two state contractions (update and readout,
+    2*D*dv each) plus the causal intra-chunk part at a fixed 64-token chunk."""
+    D = d * (d + 1) // 2
+    return 4 * D * dv + c0 * (d + dv)
+
+
+def exp_flops_per_head(T, d=64, dv=64):
+    """Causal softmax attention work: QK^T and PV over the lower triangle incl. diagonal."""
+    return T * (T + 1) * (d + dv)
+
+
+def step_bytes_per_head(d=64, dv=64):
+    """Decode step HBM bytes: read+write the fp32 state and normaliser, read q,k,z,v, write out (fp32)."""
+    D = d * (d + 1) // 2
+    return 2 * (D * dv + D) * 4 + (3 * d + 1) * 4 + dv * 4
+
+
+def kernel_work(name, leg_work):
+    """Algorithmic work a kernel is credited with per launch (see the design notes)."""
+    return leg_work
+
+
+def time_loop(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def dominant_kernel(fn_timed, calls):
+    """Average per-kernel durations over `calls` timed invocations; returns (name, ms, all)."""
+    acc = {}
+    for _ in range(calls):
+        kt = []
+        fn_timed(kt)
+        for name, ms in kt:
+            acc.setdefault(name, []).append(ms)
+    avg = {n: sum(v) / len(v) for n, v in acc.items()}
+    name = max(avg, key=avg.get)
+    return name, avg[name], avg
+
+
+def leg_sq(steps, warmup, variant="sq"):
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    shp = SQ_SHAPE if variant == "sq" else EXP_SHAPE
+    B, H, T, d = shp["B"], shp["H"], shp["T"], shp["d"]
+    q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=shp["seed"], dtype="bf16"))
+    out = torch.empty_like(v)
+    desc = tmb.make_desc(B, H, T, d, d, variant=variant, dtype=torch.bfloat16)
+    nws = tmb.workspace_size(desc)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    fn = lambda: tmb.fwd(q, k, v, z, variant=variant, out=out, workspace=ws)
+    ms = time_loop(fn, steps, warmup)
+    name, kms, allk = dominant_kernel(lambda kt: tmb.fwd(q, k, v, z, variant=variant, out=out, workspace=ws,
+                                                         kernel_times=kt), max(3, min(steps, 10)))
+    ht = B * H * T
+    if variant == "sq":
+        work = ht * sq_flops_per_head_token(d, d)
+    else:
+        work = B * H * exp_flops_per_head(T, d, d)
+    mfma = not name.startswith("ref_")
+    peak = PEAK_BF16_FLOPS if mfma else PEAK_FP32_VALU_FLOPS
+    achieved = kernel_work(name, work) / (kms * 1e-3)
+    return dict(
+        workload=f"{'2Mamba' if variant == 'sq' else '2Mamba-E'} fwd B={B} H={H} T={T} d={d} bf16",
+        ms=ms, head_tokens_per_s=ht / (ms * 1e-3), flops_per_call=work,
+        tflops=work / (ms * 1e-3) / 1e12, frac_peak_bf16=work / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        kernels_ms=allk,
+        roofline=dict(bound="mfma" if mfma else "alu", kernel=name, achieved=achieved / 1e12, peak=peak / 1e12,
+                      unit="TFLOP/s", frac=achieved / peak, traffic=None),
+    )
+
+
+def leg_step(warmup):
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    B, H, d, TP = STEP_SHAPE["B"], STEP_SHAPE["H"], STEP_SHAPE["d"], STEP_SHAPE["prefill_T"]
+    nsteps = STEP_SHAPE["steps"]
+    # prefill (setup, untimed): bf16 T=2048 forward, its final state is the decode state
+    q, k, v, z = (t.cuda() for t in SI.draw(B, H, TP, d, seed=STEP_SHAPE["prefill_seed"], dtype="bf16"))
+    _, S, n = tmb.fwd(q, k, v, z, want_state=True)
+    del q, k, v, z
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    # fresh per-step inputs drawn up front, resident in HBM
+    qs, ks, vs, zs = (t.cuda() for t in SI.draw(B, H, nsteps + warmup, d, seed=STEP_SHAPE["prefill_seed"] + 100,
+                                                 dtype="f32"))
+    steps_in = [tuple(x[:, :, i].contiguous() for x in (qs, ks, vs, zs)) for i in range(nsteps + warmup)]
+    out = torch.empty(B, H, d, device="cuda")
+    for i in range(warmup):
+        tmb.step(*steps_in[i], S, n, out=out)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(warmup, warmup + nsteps):
+        tmb.step(*steps_in[i], S, n, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / nsteps
+    byts = B * H * step_bytes_per_head(d, d)
+    bw = byts / (ms * 1e-3)
+    return dict(workload=f"decode step B={B} H={H} d={d} fp32 state, {nsteps} sequential steps",
+                ms=ms, bytes_per_step=byts,
+                roofline=dict(bound="hbm", kernel="step_kernel", achieved=bw / 1e9, peak=PEAK_HBM / 1e9,
+                              unit="GB/s", frac=bw / PEAK_HBM, traffic=None))
+
+
+def cpu_baseline(seconds):
+    """fp64 oracle (packed recurrent form) on head (0,0) of the 2Mamba workload, as many tokens as fit."""
+    import numpy as np
+
+    import synth_inputs as SI
+    from oracle import twomamba_oracle as O
+
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    shp = SQ_SHAPE
+    q, k, v, z = SI.draw(shp["B"], shp["H"], shp["T"], shp["d"], seed=shp["seed"], dtype="bf16")
+    q, k, v, z = (SI.to_f64(t)[:1, :1] for t in (q, k, v, z))
+    # calibrate on 32 tokens, then run a bounded sample
+    t0 = time.perf_counter()
+    O.fwd_recurrent_packed(q[:, :, :32], k[:, :, :32], v[:, :, :32], z[:, :, :32])
+    per_tok = (time.perf_counter() - t0) / 32
+    n = int(max(64, min(shp["T"], seconds / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    O.fwd_recurrent_packed(q[:, :, :n], k[:, :, :n], v[:, :, :n], z[:, :, :n])
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="head-tokens/s", cores=threads, kind="oracle",
+                sample=f"packed recurrent fp64 oracle, batch 0 head 0, first {n} of {shp['T']} tokens "
+                       f"of the B=2 H=16 T=8192 d=64 workload ({dt:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="sq,exp,step")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each head is independent, "
+              "so several GPUs would shard B*H with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    legs = args.legs.split(",")
+    res = {}
+    if "sq" in legs:
+        res["sq"] = leg_sq(args.steps, args.warmup, "sq")
+        print(f"[bench] sq leg done: {res['sq']['ms']:.3f} ms/step", file=sys.stderr, flush=True)
+    if "exp" in legs:
+        res["exp"] = leg_sq(max(3, args.steps // 4), 1, "exp")
+        print(f"[bench] exp leg done: {res['exp']['ms']:.3f} ms/call", file=sys.stderr, flush=True)
+    if "step" in legs:
+        res["step"] = leg_step(args.warmup)
+        print(f"[bench] step leg done: {res['step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    cpu = cpu_baseline(args.cpu_seconds) if args.cpu_seconds > 0 else None
+    head = res.get("sq") or next(iter(res.values()))
+    line = {
+        "metric": METRIC,
+        "value": head.get("head_tokens_per_s"),
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(d) q,k,v and N(0,1) decay logits)",
+        "config": {"workload": head["workload"], "B": SQ_SHAPE["B"], "H": SQ_SHAPE["H"], "T": SQ_SHAPE["T"],
+                   "d": SQ_SHAPE["d"], "chunk": 64},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "legs": res,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

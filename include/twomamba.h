@@ -142,6 +142,22 @@ int twomamba_fwd(const twomamba_fwd_desc* desc,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Profiling form of twomamba_fwd (same arguments and results).  Each kernel
+ * launch of the call is bracketed by a pair of HIP events; the call then WAITS
+ * for the stream and writes, for the first min(count, cap) launches, the
+ * duration in milliseconds to kernel_ms[i] and a static kernel name to
+ * kernel_names[i] (either array may be NULL).  *n_kernels receives the number
+ * of launches.  Meant for benchmarks: it creates and destroys HIP events, so
+ * it is not for use under graph capture.
+ */
+int twomamba_fwd_timed(const twomamba_fwd_desc* desc,
+                       const void* q, const void* k, const void* v, const float* z,
+                       const float* state_in, const float* norm_in,
+                       void* out, float* state_out, float* norm_out,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       float* kernel_ms, const char** kernel_names, int cap, int* n_kernels);
+
+/*
  * One recurrent decode step of 2Mamba for every (b, h)  [2M2F §2 constant-size
  * hidden state; App. A inference]:
  *     S <- e^g S + phi(k) v^T,   n <- e^g n + phi(k),

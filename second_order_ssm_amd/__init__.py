@@ -70,6 +70,10 @@ def load(path: str | None = None):
     lib.twomamba_fwd.restype = ctypes.c_int
     lib.twomamba_fwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    lib.twomamba_fwd_timed.restype = ctypes.c_int
+    lib.twomamba_fwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.twomamba_step.restype = ctypes.c_int
     lib.twomamba_step.argtypes = [ctypes.POINTER(StepDesc), vp, vp, vp, vp, vp, vp, vp, vp]
     if path is None:
@@ -118,8 +122,13 @@ def _check(t, shape, dtype, name):
 
 
 def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, reference_kernels=False,
-        state_in=None, norm_in=None, want_state=False, out=None, state_out=None, norm_out=None, workspace=None):
-    """Chunked forward.  Returns out, or (out, state_out, norm_out) with want_state."""
+        state_in=None, norm_in=None, want_state=False, out=None, state_out=None, norm_out=None, workspace=None,
+        kernel_times=None):
+    """Chunked forward.  Returns out, or (out, state_out, norm_out) with want_state.
+
+    With ``kernel_times`` (a list), the call goes through twomamba_fwd_timed:
+    it waits for completion and appends (kernel name, milliseconds) per launch.
+    """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     flags = (FLAG_NO_NORM if no_norm else 0) | (FLAG_REFERENCE_KERNELS if reference_kernels else 0)
@@ -140,9 +149,19 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
     nbytes = workspace_size(desc)
     if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    s = load().twomamba_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state_in), _ptr(norm_in),
-                            _ptr(out), _ptr(state_out), _ptr(norm_out), _ptr(workspace) if nbytes else None,
-                            ctypes.c_size_t(nbytes), _stream())
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state_in), _ptr(norm_in),
+            _ptr(out), _ptr(state_out), _ptr(norm_out), _ptr(workspace) if nbytes else None,
+            ctypes.c_size_t(nbytes), _stream())
+    if kernel_times is None:
+        s = load().twomamba_fwd(*args)
+    else:
+        cap = 8
+        ms = (ctypes.c_float * cap)()
+        names = (ctypes.c_char_p * cap)()
+        cnt = ctypes.c_int(0)
+        s = load().twomamba_fwd_timed(*args, ms, names, cap, ctypes.byref(cnt))
+        for i in range(min(cnt.value, cap)):
+            kernel_times.append((names[i].decode(), float(ms[i])))
     if s != 0:
         raise TwoMambaError(s, "twomamba_fwd")
     if want_state or state_out is not None:

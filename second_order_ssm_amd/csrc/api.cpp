@@ -137,9 +137,9 @@ int twomamba_fwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
     return TWOMAMBA_OK;
 }
 
-int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
-                 const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                    const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
+                    void* workspace, size_t workspace_bytes, void* stream, twm::KTimer* timer) {
     size_t qkb, vb, zb, sb, nb;
     int s = check_desc(d, &qkb, &vb, &zb, &sb, &nb);
     if (s != TWOMAMBA_OK) return s;
@@ -180,8 +180,31 @@ int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const
     a.state_in = state_in; a.norm_in = norm_in;
     a.out = out; a.state_out = state_out; a.norm_out = norm_out;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
+    a.timer = timer;
     if (a.variant == TWOMAMBA_EXP) return path == MFMA ? twm::mfma_exp_fwd(a) : twm::ref_exp_fwd(a);
     return path == MFMA ? twm::mfma_sq_fwd(a) : twm::ref_sq_fwd(a);
+}
+
+int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                 const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, workspace, workspace_bytes, stream,
+                    nullptr);
+}
+
+int twomamba_fwd_timed(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                       const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
+                       void* workspace, size_t workspace_bytes, void* stream, float* kernel_ms,
+                       const char** kernel_names, int cap, int* n_kernels) {
+    if (!n_kernels) return TWOMAMBA_ERR_NULL;
+    *n_kernels = 0;
+    twm::KTimer t;
+    memset(&t, 0, sizeof(t));
+    int s = fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, workspace, workspace_bytes, stream,
+                     &t);
+    const int c = twm::ktimer_collect(&t, kernel_ms, kernel_names, cap < 0 ? 0 : cap);
+    *n_kernels = t.n;
+    return s != TWOMAMBA_OK ? s : c;
 }
 
 int twomamba_step(const twomamba_step_desc* d, const void* q, const void* k, const void* v, const float* z,

@@ -96,9 +96,11 @@ template <int DK, int DV, typename In>
 int run(const FwdArgs& a) {
     const int nqt = (a.T + kQT - 1) / kQT;
     const int nbh = a.B * a.H;
+    ktimer_begin(a.timer, "ref_exp", a.stream);
     hipLaunchKernelGGL((ref_exp_kernel<DK, DV, In>), dim3(nbh * nqt), dim3(kQT * (DV / 8)), 0,
                        (hipStream_t)a.stream, (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, (In*)a.out,
                        a.T, nqt, a.scale);
+    ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 

@@ -9,6 +9,19 @@
 
 namespace twm {
 
+// Optional per-launch timing: when a KTimer is attached to a call, every
+// kernel launch is bracketed by a pair of HIP events (see twomamba_fwd_timed).
+struct KTimer {
+    static constexpr int kMax = 8;
+    void* ev[2 * kMax];
+    const char* names[kMax];
+    int n;
+    int error;
+};
+void ktimer_begin(KTimer* t, const char* name, void* stream);
+void ktimer_end(KTimer* t, void* stream);
+int ktimer_collect(KTimer* t, float* ms, const char** names, int cap);
+
 // Everything the kernels need about one forward call, already validated.
 struct FwdArgs {
     int B, H, T, dk, dv, chunk;
@@ -27,6 +40,7 @@ struct FwdArgs {
     void* ws;
     size_t ws_bytes;
     void* stream;
+    KTimer* timer;   // NULL unless called through twomamba_fwd_timed
 };
 
 struct StepArgs {

@@ -1,11 +1,767 @@
-// MFMA kernels of the 2Mamba chunked forward (bf16 inputs, d = 64).
+// MFMA kernels of the 2Mamba chunked forward for d_k = d_v = 64 and bf16 inputs,
+// "2Mamba2Furious", §5 (squared score, A-mask on the squared score, normalised
+// by the sum of weights) with the second-order state of §2.
+//
+// Design (one head = (b, h)):
+//  * The packed second-order state (2080 x 64 fp32) stays in MFMA accumulator
+//    registers for the whole sequence segment a workgroup walks.  It does not
+//    fit one CU (532 KB > 512 KB of VGPRs), so each head is split over two
+//    workgroups by value column (32 columns each); both form the same features.
+//  * Pair space.  The symmetric dim-pair matrix is cut into 4x4 blocks
+//    (ib <= jb): 120 off-diagonal blocks and 16 diagonal ones, 136 "tiles" of
+//    16 slots.  Slot r of tile (ib, jb) is the pair (4ib + r/4, 4jb + r%4).
+//    Each of the 8 waves owns 17 tiles (15 off-diagonal, 2 diagonal) x 2
+//    column tiles of 16x16 fp32 accumulators.  Diagonal tiles keep c * S in
+//    their accumulators, c = 2 above, 1 on and 0 below the dim diagonal, so
+//    that the query side needs no per-slot weight; off-diagonal tiles keep S
+//    and the query side reads 2 q_i from a pre-doubled copy.
+//  * Per 64-token chunk c (S_c = state before the chunk):
+//      readout   O = phi_q(Q) . S_c                      (MFMA, K = pair slots)
+//      intra     A = (Q K^T)^2 * exp(Gl_t - Gl_s), s <= t; A . V   (MFMA)
+//      norm      den via the d x d normaliser N: q^T N q  (MFMA)
+//      update    S_{c+1} = e^Gam S_c + phi(K)^T diag(w) V  (MFMA, K = tokens)
+//    The readout takes the accumulators themselves as its B operand: the rows
+//    4g..4g+3 a lane holds of two tiles are exactly the 8 K-slots that lane
+//    supplies, so the contraction over pair slots moves no data.
+//  * Operands are fp16.  Per chunk, q and k are scaled by powers of two to
+//    |x| < 1 (exact for bf16 inputs).  The accumulators carry a power-of-two
+//    "frame" (true value = acc * 2^lf) re-chosen every chunk so that a running
+//    bound on |acc| stays at 2^14; the frame change rides on the per-chunk decay
+//    multiply, the update's value operand is scaled to match, and the readout
+//    converts the accumulators to fp16 with a bare convert.
+//  * Long sequences are split into segments: a first kernel computes each
+//    segment's end state (update only), a scan kernel chains them, and the main
+//    kernel starts every segment from its carried state.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace twm {
+namespace {
 
-bool mfma_sq_supported(const FwdArgs&) { return false; }
-size_t mfma_sq_workspace(const FwdArgs&) { return 0; }
-int mfma_sq_fwd(const FwdArgs&) { return TWOMAMBA_ERR_UNSUPPORTED; }
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 64;          // head dim (keys and values)
+constexpr int kDV = 32;         // value columns per workgroup
+constexpr int kC = 64;          // chunk length
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTiles = 17;      // pair tiles per wave
+constexpr int kPairs = kD * (kD + 1) / 2;
+constexpr int kLS = 72;         // LDS row stride in halves (144 B)
+constexpr int kStateLane = kTiles * 2 * 4;            // fp32 state values per lane
+constexpr int kStateHalf = kWaves * 64 * kStateLane;  // per workgroup (one value half)
+constexpr int kNormWG = kD * kD;                      // full d x d normaliser
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTarget = 14.f;                       // log2 of the accumulator bound
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+
+// Wave w owns the block rows ib = w and ib = 15 - w of the upper block triangle
+// (16 - w and w + 1 blocks: 17 tiles).  Tile u: u = 0 and u = 16 are the two
+// diagonal blocks; 1 <= u <= 15 - w are (w, w + u), the rest (15 - w, u).
+__device__ __forceinline__ void tile_block(int w, int u, int& ib, int& jb) {
+    if (u == 0) {
+        ib = jb = w;
+    } else if (u == 16) {
+        ib = jb = 15 - w;
+    } else if (u <= 15 - w) {
+        ib = w;
+        jb = w + u;
+    } else {
+        ib = 15 - w;
+        jb = u;
+    }
+}
+
+__device__ __forceinline__ int pidx(int i, int j) { return i * kD - (i * (i - 1)) / 2 + (j - i); }
+
+// exponent e with x * 2^e in [0.5, 1) for x > 0; 0 for x == 0
+__device__ __forceinline__ int unit_exp(float x) {
+    if (!(x > 0.f)) return 0;
+    return -(ilogbf(x) + 1);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ float sum16(float x) {   // sum over the 16 lanes sharing lane>>4
+    for (int o = 8; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// log2(2^a + 2^b) for a or b possibly -inf
+__device__ __forceinline__ float log2_add(float a, float b) {
+    const float m = fmaxf(a, b);
+    if (m == -INFINITY) return -INFINITY;
+    return m + log2f(exp2f(a - m) + exp2f(b - m));
+}
+
+__device__ __forceinline__ void ld8_bf16(const bf16* p, float* o) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+struct Smem {
+    _Float16 Q[kC][kLS];        // q~ [t][d]
+    _Float16 K[kC][kLS];        // k~ [t][d]
+    _Float16 KT[kD + 1][kLS];   // k~^T [d][t]; row 64 is zero
+    _Float16 WKT[kD][kLS];      // normaliser update operand (w k)^T [d][t]
+    _Float16 WVT[kDV][kLS];     // state update operand (w v)^T [n][t]
+    _Float16 VT[kDV][kLS];      // intra operand v^T [n][t]
+    _Float16 A[kC][kLS];        // intra weights [t][s]
+    _Float16 NT[kD][kLS];       // normaliser, fp16, [j][i]
+    struct {
+        _Float16 Q2[kC][kLS];   // 2 q~, readout of off-diagonal tiles
+        float Op[kWaves][kC][kDV + 1];   // per-wave readout partials
+    } u;
+    float Oin[kC][kDV + 1];
+    float Dint[4][kC];
+    float Dinter[2][kC];
+    float Gl[kC];
+    float red[kWaves][4];
+    int wid[kWaves];
+    int zero;
+};
+
+template <bool kPhase1>
+__global__ void __launch_bounds__(kThreads, 1)
+sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+               const float* __restrict__ z, bf16* __restrict__ out,
+               const float* __restrict__ state_in, const float* __restrict__ norm_in,
+               float* __restrict__ state_out, float* __restrict__ norm_out,
+               float* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
+               int T, int nseg, int seg_chunks, float scale, int no_norm) {
+    __shared__ __attribute__((aligned(16))) Smem sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int kg = lane >> 4;
+
+    // block -> (head, segment, value half)
+    const int half = blockIdx.x & 1;
+    const int rest = blockIdx.x >> 1;
+    const int nseg_k = kPhase1 ? nseg - 1 : nseg;
+    const int seg = rest % nseg_k;
+    const int bh = rest / nseg_k;
+    const int nc_total = (T + kC - 1) / kC;
+    const int c_begin = seg * seg_chunks;
+    const int c_end = min(nc_total, c_begin + seg_chunks);
+    const size_t tok_base = (size_t)bh * T;
+    const int col0 = half * kDV;
+
+    // update A operand: slot row l16 -> (gq, bq); diagonal-tile weight of that slot
+    const int gq = l16 >> 2, bq4 = l16 & 3;
+    const _Float16 cslot = (_Float16)(bq4 < gq ? 0.f : (bq4 == gq ? 1.f : 2.f));
+    // accumulator row 4kg + b of a diagonal tile holds c(kg, b) * S
+    float cacc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cacc[b] = b < kg ? 0.f : (b == kg ? 1.f : 2.f);
+
+    // ---------------------------------------------------------------- state
+    f4 S[kTiles][2];
+    f4 Nacc[2];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) S[u][0] = S[u][1] = f4{0.f, 0.f, 0.f, 0.f};
+    Nacc[0] = Nacc[1] = f4{0.f, 0.f, 0.f, 0.f};
+    float lf = 0.f, lfn = 0.f;      // log2 frames: true value = acc * 2^lf
+    float Mb = 0.f, Mn = 0.f;       // bounds on |acc| (<= 2^14 once set)
+
+    const bool from_abi = (seg == 0) && state_in != nullptr;
+    const bool from_ws = seg > 0;
+    if (from_abi || from_ws) {
+        float mx = 0.f, mnx = 0.f;
+        const size_t wsi = (size_t)(bh * (nseg - 1) + seg - 1);
+        if (from_abi) {
+            const float* Sg = state_in + (size_t)bh * kPairs * kD;
+#pragma unroll
+            for (int u = 0; u < kTiles; ++u) {
+                int ib, jb;
+                tile_block(w, u, ib, jb);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int i = 4 * ib + kg, j = 4 * jb + b;
+                        float x = (i <= j) ? Sg[(size_t)pidx(i, j) * kD + col0 + 16 * ct + l16] : 0.f;
+                        if (u == 0 || u == 16) x *= cacc[b];
+                        S[u][ct][b] = x;
+                        mx = fmaxf(mx, fabsf(x));
+                    }
+            }
+        } else {
+            const float* Wg = ws_state + (wsi * 2 + half) * kStateHalf + (size_t)w * 64 * kStateLane;
+#pragma unroll
+            for (int u = 0; u < kTiles; ++u)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const float4 x = reinterpret_cast<const float4*>(Wg)[(u * 2 + ct) * 64 + lane];
+                    S[u][ct] = f4{x.x, x.y, x.z, x.w};
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+                }
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
+                const float val = from_abi ? norm_in[(size_t)bh * kPairs + pidx(min(i, j), max(i, j))]
+                                           : ws_norm[wsi * kNormWG + i * kD + j];
+                Nacc[x][b] = val;
+                mnx = fmaxf(mnx, fabsf(val));
+            }
+        }
+        mx = wave_max(mx);
+        mnx = wave_max(mnx);
+        if (lane == 0) {
+            sm.red[w][0] = mx;
+            sm.red[w][1] = mnx;
+        }
+        __syncthreads();
+        float a = 0.f, bb = 0.f;
+        for (int i = 0; i < kWaves; ++i) {
+            a = fmaxf(a, sm.red[i][0]);
+            bb = fmaxf(bb, sm.red[i][1]);
+        }
+        __syncthreads();
+        // normalise the frames so the bounds start at 2^14
+        if (a > 0.f) {
+            lf = ceilf(log2f(a) - kTarget);
+            const float f = exp2f(-lf);
+#pragma unroll
+            for (int u = 0; u < kTiles; ++u) {
+                S[u][0] *= f;
+                S[u][1] *= f;
+            }
+            Mb = a * f;
+        }
+        if (bb > 0.f) {
+            lfn = ceilf(log2f(bb) - kTarget);
+            const float f = exp2f(-lfn);
+            Nacc[0] *= f;
+            Nacc[1] *= f;
+            Mn = bb * f;
+        }
+    }
+
+    if (tid < kWaves) sm.wid[tid] = tid;
+    if (tid == 0) sm.zero = 0;
+    __syncthreads();
+
+    float gam_seg = 0.f;   // total log decay of the segment (phase 1)
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0 = c * kC;
+        const int Lc = min(kC, T - t0);
+        // Lane-derived indices are rebuilt from a value re-read from LDS every chunk
+        // (always 0), so address arithmetic stays inside the loop instead of being
+        // hoisted into (and spilled from) registers.
+        const int tidc = tid + sm.zero;
+        const int lane = tidc & 63;
+        const int l16 = lane & 15;
+        const int kg = lane >> 4;
+        const int gq = l16 >> 2, bq4 = l16 & 3;
+
+        // ------------------------------------------------ P1: load, decay, scales
+        float qv[8], kv[8], vv[8];
+        const int lt = tidc >> 3, ld8 = (tidc & 7) * 8;      // token, 8 dims
+        const bool tok_ok = lt < Lc;
+        const bf16* qc = q + (tok_base + t0) * kD;          // uniform chunk bases
+        const bf16* kc = k + (tok_base + t0) * kD;
+        const bf16* vcp = v + (tok_base + t0) * kD + col0;
+        if (tok_ok) {
+            ld8_bf16(qc + (lt * kD + ld8), qv);
+            ld8_bf16(kc + (lt * kD + ld8), kv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[i] = kv[i] = 0.f;
+        }
+        const int vt = tidc >> 2, vc = (tidc & 3) * 8;      // threads 0..255: token, 8 value columns
+        const bool v_ok = tidc < 256 && vt < Lc;
+        if (v_ok) ld8_bf16(vcp + (vt * kD + vc), vv);
+        else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vv[i] = 0.f;
+        }
+        float mq = 0.f, mk = 0.f, mv = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            qv[i] *= scale;
+            mq = fmaxf(mq, fabsf(qv[i]));
+            mk = fmaxf(mk, fabsf(kv[i]));
+            mv = fmaxf(mv, fabsf(vv[i]));
+        }
+        mq = wave_max(mq);
+        mk = wave_max(mk);
+        mv = wave_max(mv);
+        if (w == 0) {
+            // log decay of token `lane`, chunk-local inclusive prefix sum
+            const float g = (lane < Lc) ? decay_log(z[tok_base + t0 + lane]) : 0.f;
+            float s = g;
+            for (int o = 1; o < 64; o <<= 1) {
+                const float y = __shfl_up(s, o, 64);
+                if (lane >= o) s += y;
+            }
+            sm.Gl[lane] = s;
+        }
+        if (lane == 0) {
+            sm.red[w][0] = mq;
+            sm.red[w][1] = mk;
+            sm.red[w][2] = mv;
+        }
+        __syncthreads();
+
+        // The wave index re-read from LDS after a barrier: tile addresses derived from
+        // it are recomputed per chunk instead of being hoisted into registers.
+        const int wl = __builtin_amdgcn_readfirstlane(sm.wid[tid >> 6]);
+        float Mq = 0.f, Mk = 0.f, Mv = 0.f;
+        for (int i = 0; i < kWaves; ++i) {
+            Mq = fmaxf(Mq, sm.red[i][0]);
+            Mk = fmaxf(Mk, sm.red[i][1]);
+            Mv = fmaxf(Mv, sm.red[i][2]);
+        }
+        const float Gam = sm.Gl[kC - 1];
+        const float lg = Gam * kLog2e;
+        const int eq = max(-120, min(120, unit_exp(Mq)));
+        const int ek = max(-120, min(120, unit_exp(Mk)));
+        const int evi = max(-120, min(120, unit_exp(Mv) + 14));
+        const float mk1 = ldexpf(Mk, ek);   // max |k~| in [0.5, 1)
+        // new state frame: bound(e^Gam S_c + dS_c) normalised to 2^14
+        float lf_new, ratio_s, lfn_new, ratio_n;
+        {
+            const float lold = (Mb > 0.f) ? log2f(Mb) + lf + lg : -INFINITY;
+            const float lcon = (Mk > 0.f && Mv > 0.f) ? 7.f + 2.f * log2f(Mk) + log2f(Mv) : -INFINITY;
+            const float lt_ = log2_add(lold, lcon);
+            lf_new = (lt_ == -INFINITY) ? lf : ceilf(lt_ - kTarget);
+            lf_new = fmaxf(lf_new, lf + lg - 100.f);
+            ratio_s = exp2f(lf + lg - lf_new);
+            const float lnold = (Mn > 0.f) ? log2f(Mn) + lfn + lg : -INFINITY;
+            const float lncon = (Mk > 0.f) ? 6.f + 2.f * log2f(Mk) : -INFINITY;
+            const float ln_ = log2_add(lnold, lncon);
+            lfn_new = (ln_ == -INFINITY) ? lfn : ceilf(ln_ - kTarget);
+            lfn_new = fmaxf(lfn_new, lfn + lg - 100.f);
+            ratio_n = exp2f(lfn + lg - lfn_new);
+        }
+        // value-side operand scales: dS_acc = 2^-lf_new dS, dN_acc = 2^-lfn_new dN
+        const float sv = exp2f(-lf_new - 2.f * (float)ek);
+        const float swk = exp2f(-lfn_new - (float)ek);
+
+        // write the scaled fp16 operands
+        {
+            const float sq_ = ldexpf(1.f, eq), sk_ = ldexpf(1.f, ek);
+            const float wt = tok_ok ? exp2f((Gam - sm.Gl[lt]) * kLog2e) : 0.f;   // w_s = exp(Gam - Gl_s)
+            const float wk = wt * swk;
+            h8 q8, q28, k8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float qq = qv[i] * sq_;
+                q8[i] = (_Float16)qq;
+                q28[i] = (_Float16)(2.f * qq);
+                const float kt = kv[i] * sk_;
+                k8[i] = (_Float16)kt;
+                sm.KT[ld8 + i][lt] = (_Float16)kt;
+                sm.WKT[ld8 + i][lt] = (_Float16)(kv[i] * wk);
+            }
+            *reinterpret_cast<h8*>(&sm.Q[lt][ld8]) = q8;
+            *reinterpret_cast<h8*>(&sm.u.Q2[lt][ld8]) = q28;
+            *reinterpret_cast<h8*>(&sm.K[lt][ld8]) = k8;
+            if (tidc < 256) {
+                const float wv = (vt < Lc) ? exp2f((Gam - sm.Gl[vt]) * kLog2e) : 0.f;
+                const float svw = sv * wv, svi = ldexpf(1.f, evi);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    sm.WVT[vc + i][vt] = (_Float16)(vv[i] * svw);
+                    sm.VT[vc + i][vt] = (_Float16)(vv[i] * svi);
+                }
+            }
+        }
+        if (!kPhase1) {
+            // normaliser of S_c to fp16 (|N_acc| <= 2^14)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+                h4 t4;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) t4[b] = (_Float16)Nacc[x][b];
+                *reinterpret_cast<h4*>(&sm.NT[16 * njb + l16][16 * nib + 4 * kg]) = t4;
+            }
+        }
+        __syncthreads();
+
+        if (!kPhase1) {
+            // -------------------------------------------- P2: readout of S_c
+            f4 O[4][2];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) O[tb][0] = O[tb][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < 9; ++kp) {
+                const int ua = 2 * kp, ub = 2 * kp + 1;
+                int iba, jba, ibb = 0, jbb = 0;
+                tile_block(wl, ua, iba, jba);
+                if (ub < kTiles) tile_block(wl, ub, ibb, jbb);
+                h8 B0, B1;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    B0[b] = (_Float16)S[ua][0][b];
+                    B1[b] = (_Float16)S[ua][1][b];
+                    B0[4 + b] = (ub < kTiles) ? (_Float16)S[ub][0][b] : (_Float16)0.f;
+                    B1[4 + b] = (ub < kTiles) ? (_Float16)S[ub][1][b] : (_Float16)0.f;
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const int m = 16 * tb + l16;
+                    // off-diagonal tiles read 2 q~_i, diagonal tiles q~_i (their weight is in S)
+                    const _Float16 qa = (ua == 0 || ua == 16) ? sm.Q[m][4 * iba + kg] : sm.u.Q2[m][4 * iba + kg];
+                    const h4 qja = *reinterpret_cast<const h4*>(&sm.Q[m][4 * jba]);
+                    h8 A;
+                    A[0] = qa * qja[0]; A[1] = qa * qja[1]; A[2] = qa * qja[2]; A[3] = qa * qja[3];
+                    if (ub < kTiles) {
+                        const _Float16 qb = sm.u.Q2[m][4 * ibb + kg];   // odd tiles are off-diagonal
+                        const h4 qjb = *reinterpret_cast<const h4*>(&sm.Q[m][4 * jbb]);
+                        A[4] = qb * qjb[0]; A[5] = qb * qjb[1]; A[6] = qb * qjb[2]; A[7] = qb * qjb[3];
+                    } else {
+                        A[4] = A[5] = A[6] = A[7] = (_Float16)0.f;
+                    }
+                    O[tb][0] = mfma(A, B0, O[tb][0]);
+                    O[tb][1] = mfma(A, B1, O[tb][1]);
+                }
+            }
+            // this wave's partial readout (over its pair slots) to LDS
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) sm.u.Op[w][16 * tb + 4 * kg + b][16 * ct + l16] = O[tb][ct][b];
+
+            // -------------------------------------------- P3a: intra scores A = (QK^T)^2 * mask
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int tile = 2 * w + x, tt = tile >> 2, ts = tile & 3;
+                if (ts <= tt) {
+                    f4 X = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const h8 a = *reinterpret_cast<const h8*>(&sm.Q[16 * tt + l16][32 * kk + 8 * kg]);
+                        const h8 b = *reinterpret_cast<const h8*>(&sm.K[16 * ts + l16][32 * kk + 8 * kg]);
+                        X = mfma(a, b, X);
+                    }
+                    const int s = 16 * ts + l16;
+                    const float gls = sm.Gl[s];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int t = 16 * tt + 4 * kg + b;
+                        float a = 0.f;
+                        if (s <= t) a = X[b] * X[b] * exp2f((sm.Gl[t] - gls) * kLog2e);
+                        sm.A[t][s] = (_Float16)a;
+                        const float rs = sum16(a);
+                        if (l16 == 0) sm.Dint[ts][t] = rs;
+                    }
+                } else {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) sm.A[16 * tt + 4 * kg + b][16 * ts + l16] = (_Float16)0.f;
+                    if (l16 == 0) {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) sm.Dint[ts][16 * tt + 4 * kg + b] = 0.f;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        if (!kPhase1) {
+            // -------------------------------------------- P3b: intra A.V, den q^T N q
+            {
+                const int tb = w >> 1, ct = w & 1;
+                f4 Y = f4{0.f, 0.f, 0.f, 0.f};
+                const int nk = tb >= 2 ? 2 : 1;
+                for (int kk = 0; kk < nk; ++kk) {
+                    const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
+                    const h8 b = *reinterpret_cast<const h8*>(&sm.VT[16 * ct + l16][32 * kk + 8 * kg]);
+                    Y = mfma(a, b, Y);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) sm.Oin[16 * tb + 4 * kg + b][16 * ct + l16] = Y[b];
+            }
+            {
+                const int tb = w >> 1, jh = w & 1;
+                float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const int jt = 2 * jh + c2;
+                    f4 Y = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const h8 a = *reinterpret_cast<const h8*>(&sm.Q[16 * tb + l16][32 * kk + 8 * kg]);
+                        const h8 b = *reinterpret_cast<const h8*>(&sm.NT[16 * jt + l16][32 * kk + 8 * kg]);
+                        Y = mfma(a, b, Y);
+                    }
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        part[b] += (float)sm.Q[16 * tb + 4 * kg + b][16 * jt + l16] * Y[b];
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float sred = sum16(part[b]);
+                    if (l16 == 0) sm.Dinter[jh][16 * tb + 4 * kg + b] = sred;
+                }
+            }
+        }
+
+        // ------------------------------------------------ P4: update
+        {
+            h8 BV[2][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    BV[kk][ct] = *reinterpret_cast<const h8*>(&sm.WVT[16 * ct + l16][32 * kk + 8 * kg]);
+#pragma unroll
+            for (int u = 0; u < kTiles; ++u) {
+                S[u][0] *= ratio_s;
+                S[u][1] *= ratio_s;
+                int ib, jb;
+                tile_block(wl, u, ib, jb);
+                const int i = 4 * ib + gq;
+                const int j = 4 * jb + bq4;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const h8 ki = *reinterpret_cast<const h8*>(&sm.KT[i][32 * kk + 8 * kg]);
+                    const h8 kj = *reinterpret_cast<const h8*>(&sm.KT[j][32 * kk + 8 * kg]);
+                    h8 A = ki * kj;
+                    if (u == 0 || u == 16) A *= cslot;   // c * phi(k); zero on dead slots
+                    S[u][0] = mfma(A, BV[kk][0], S[u][0]);
+                    S[u][1] = mfma(A, BV[kk][1], S[u][1]);
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                Nacc[x] *= ratio_n;
+                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const h8 a = *reinterpret_cast<const h8*>(&sm.KT[16 * nib + l16][32 * kk + 8 * kg]);
+                    const h8 b = *reinterpret_cast<const h8*>(&sm.WKT[16 * njb + l16][32 * kk + 8 * kg]);
+                    Nacc[x] = mfma(a, b, Nacc[x]);
+                }
+            }
+        }
+
+        if (!kPhase1) {
+            __syncthreads();
+            // -------------------------------------------- P5: combine and write out
+            // o = (Oin 2^-evi + Osum r_num(t)) / (Dint + Dinter r_den(t)) after dropping the
+            // common factor 2^-(2eq+2ek) of numerator and denominator.
+            const int t = tidc >> 3, n0 = (tidc & 7) * 4;
+            if (t < Lc) {
+                const float glt = sm.Gl[t] * kLog2e;
+                const float r_num = exp2f(glt + lf + 2.f * (float)ek);
+                const float r_den = exp2f(glt + lfn + 2.f * (float)ek);
+                const float fin = ldexpf(1.f, -evi);
+                float den = (sm.Dint[0][t] + sm.Dint[1][t]) + (sm.Dint[2][t] + sm.Dint[3][t]);
+                den = fmaf(sm.Dinter[0][t] + sm.Dinter[1][t], r_den, den);
+                const float back = exp2f(-2.f * (float)eq - 2.f * (float)ek);
+                const size_t oo = (tok_base + t0 + t) * kD + col0 + n0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float osum = 0.f;
+#pragma unroll
+                    for (int ww = 0; ww < kWaves; ++ww) osum += sm.u.Op[ww][t][n0 + e];
+                    const float num = fmaf(sm.Oin[t][n0 + e], fin, osum * r_num);
+                    float o;
+                    if (no_norm) o = num * back;
+                    else o = (den == 0.f) ? 0.f : num / den;
+                    out[oo + e].bits = f32_to_bf16(o);
+                }
+            }
+        }
+        // advance the frames and bounds
+        // |dS_acc| <= 64 * 2 (diagonal weight) * |k~|^2 * |v| sv ; |dN_acc| <= 64 |k~| |k| swk
+        Mb = fmaf(Mb, ratio_s, 128.f * mk1 * mk1 * Mv * sv);
+        Mn = fmaf(Mn, ratio_n, 64.f * mk1 * Mk * swk);
+        lf = lf_new;
+        lfn = lfn_new;
+        gam_seg += Gam;
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    if (kPhase1) {
+        // true end state of this segment (from zero, or from state_in for segment 0),
+        // diagonal tiles still weighted by c
+        const float f = exp2f(lf), fn = exp2f(lfn);
+        const size_t wsi = (size_t)(bh * (nseg - 1) + seg);
+        float* Wg = ws_state + (wsi * 2 + half) * kStateHalf + (size_t)w * 64 * kStateLane;
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const f4 x = S[u][ct] * f;
+                reinterpret_cast<float4*>(Wg)[(u * 2 + ct) * 64 + lane] = make_float4(x[0], x[1], x[2], x[3]);
+            }
+        if (half == 0) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
+                    ws_norm[wsi * kNormWG + i * kD + j] = Nacc[x][b] * fn;
+                }
+            }
+            if (tid == 0) ws_gam[wsi] = gam_seg;
+        }
+    } else if (state_out != nullptr && seg == nseg - 1) {
+        const float f = exp2f(lf), fn = exp2f(lfn);
+        float* Sg = state_out + (size_t)bh * kPairs * kD;
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) {
+            int ib, jb;
+            tile_block(w, u, ib, jb);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = 4 * ib + kg, j = 4 * jb + b;
+                    if (i <= j) {
+                        float x = S[u][ct][b] * f;
+                        if (u == 0 || u == 16) x = (b == kg) ? x : 0.5f * x;
+                        Sg[(size_t)pidx(i, j) * kD + col0 + 16 * ct + l16] = x;
+                    }
+                }
+        }
+        if (half == 0) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
+                    if (i <= j) norm_out[(size_t)bh * kPairs + pidx(i, j)] = Nacc[x][b] * fn;
+                }
+            }
+        }
+    }
+}
+
+// Chains the segment end states: afterwards slot g holds the state entering
+// segment g + 1, S_{g+1} = exp(Gam_g) S_g + dS_g with S_1 = dS_0.
+__global__ void __launch_bounds__(256)
+sq_seg_scan(float* __restrict__ ws_state, float* __restrict__ ws_norm, const float* __restrict__ ws_gam,
+            int nseg, int per_head_state, int nblk_state, int nblk_norm) {
+    const int nb = nblk_state + nblk_norm;
+    const int bh = blockIdx.x / nb;
+    const int blk = blockIdx.x % nb;
+    const int ns1 = nseg - 1;
+    float* base;
+    size_t stride;
+    if (blk < nblk_state) {
+        const int e = blk * 256 + threadIdx.x;
+        if (e >= per_head_state) return;
+        base = ws_state + (size_t)bh * ns1 * per_head_state + e;
+        stride = per_head_state;
+    } else {
+        const int e = (blk - nblk_state) * 256 + threadIdx.x;
+        if (e >= kNormWG) return;
+        base = ws_norm + (size_t)bh * ns1 * kNormWG + e;
+        stride = kNormWG;
+    }
+    float run = base[0];
+    for (int g = 1; g < ns1; ++g) {
+        run = fmaf(expf(ws_gam[bh * ns1 + g]), run, base[g * stride]);
+        base[g * stride] = run;
+    }
+}
+
+struct Plan {
+    int nseg, seg_chunks;
+};
+
+Plan plan_for(const FwdArgs& a) {
+    const int nc = (a.T + kC - 1) / kC;
+    const long nbh = (long)a.B * a.H;
+    int want = (int)((256 + 2 * nbh - 1) / (2 * nbh));   // workgroups to fill 256 CUs
+    want = std::max(1, std::min(want, nc / 4));             // at least 4 chunks per segment
+    want = std::min(want, 64);
+    const int sc = (nc + want - 1) / want;
+    Plan p;
+    p.seg_chunks = sc;
+    p.nseg = (nc + sc - 1) / sc;
+    return p;
+}
+
+struct WsLayout {
+    size_t off_state, off_norm, off_gam, total;
+};
+
+WsLayout ws_layout(const FwdArgs& a, const Plan& p) {
+    const size_t nbh = (size_t)a.B * a.H;
+    const size_t ns1 = p.nseg > 1 ? (size_t)(p.nseg - 1) : 0;
+    WsLayout L;
+    L.off_state = 0;
+    L.off_norm = align256(nbh * ns1 * 2 * kStateHalf * sizeof(float));
+    L.off_gam = align256(L.off_norm + nbh * ns1 * kNormWG * sizeof(float));
+    L.total = ns1 ? align256(L.off_gam + nbh * ns1 * sizeof(float)) : 0;
+    return L;
+}
+
+int run(const FwdArgs& a) {
+    const Plan p = plan_for(a);
+    const WsLayout L = ws_layout(a, p);
+    char* ws = (char*)a.ws;
+    float* wsS = L.total ? (float*)(ws + L.off_state) : nullptr;
+    float* wsN = L.total ? (float*)(ws + L.off_norm) : nullptr;
+    float* wsG = L.total ? (float*)(ws + L.off_gam) : nullptr;
+    const int nbh = a.B * a.H;
+    hipStream_t st = (hipStream_t)a.stream;
+    const int no_norm = (a.flags & TWOMAMBA_FLAG_NO_NORM) != 0;
+    const bf16* q = (const bf16*)a.q;
+    const bf16* k = (const bf16*)a.k;
+    const bf16* v = (const bf16*)a.v;
+    if (p.nseg > 1) {
+        ktimer_begin(a.timer, "sq_mfma_segstate", a.stream);
+        hipLaunchKernelGGL(sq_mfma_kernel<true>, dim3(nbh * (p.nseg - 1) * 2), dim3(kThreads), 0, st, q, k, v, a.z,
+                           (bf16*)nullptr, a.state_in, a.norm_in, (float*)nullptr, (float*)nullptr, wsS, wsN, wsG,
+                           a.T, p.nseg, p.seg_chunks, a.scale, 0);
+        ktimer_end(a.timer, a.stream);
+        if (p.nseg > 2) {
+            const int per_head = 2 * kStateHalf;
+            const int nbs = (per_head + 255) / 256, nbn = (kNormWG + 255) / 256;
+            ktimer_begin(a.timer, "sq_seg_scan", a.stream);
+            hipLaunchKernelGGL(sq_seg_scan, dim3(nbh * (nbs + nbn)), dim3(256), 0, st, wsS, wsN, (const float*)wsG,
+                               p.nseg, per_head, nbs, nbn);
+            ktimer_end(a.timer, a.stream);
+        }
+    }
+    ktimer_begin(a.timer, "sq_mfma_main", a.stream);
+    hipLaunchKernelGGL(sq_mfma_kernel<false>, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z,
+                       (bf16*)a.out, a.state_in, a.norm_in, a.state_out, a.norm_out, wsS, wsN, wsG, a.T, p.nseg,
+                       p.seg_chunks, a.scale, no_norm);
+    ktimer_end(a.timer, a.stream);
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+}  // namespace
+
+bool mfma_sq_supported(const FwdArgs& a) {
+    return a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 && a.chunk == kC && a.T > 0 &&
+           (size_t)a.B * a.H > 0;
+}
+
+size_t mfma_sq_workspace(const FwdArgs& a) { return ws_layout(a, plan_for(a)).total; }
+
+int mfma_sq_fwd(const FwdArgs& a) { return run(a); }
 
 }  // namespace twm

@@ -220,14 +220,20 @@ int run(const FwdArgs& a) {
     float* wsG = (float*)(ws + L.off_G);
     hipStream_t st = (hipStream_t)a.stream;
     const int ptiles = (D + (256 / (DV / 8)) - 1) / (256 / (DV / 8));
+    ktimer_begin(a.timer, "ref_sq_delta", a.stream);
     hipLaunchKernelGGL((ref_sq_delta<DK, DV, In>), dim3(nbh * nc, ptiles), dim3(256), 0, st,
                        (const In*)a.k, (const In*)a.v, a.z, wsS, wsN, wsG, a.T, a.chunk, nc);
+    ktimer_end(a.timer, a.stream);
     const int etiles = (D * DV + D + 255) / 256;
+    ktimer_begin(a.timer, "ref_sq_scan", a.stream);
     hipLaunchKernelGGL((ref_sq_scan<DK, DV>), dim3(etiles * nbh), dim3(256), 0, st,
                        wsS, wsN, (const float*)wsG, a.state_in, a.norm_in, a.state_out, a.norm_out, nc, etiles);
+    ktimer_end(a.timer, a.stream);
+    ktimer_begin(a.timer, "ref_sq_out", a.stream);
     hipLaunchKernelGGL((ref_sq_out<DK, DV, In>), dim3(nbh * nc), dim3(a.chunk * (DV / 8)), 0, st,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, (const float*)wsS, (const float*)wsN,
                        (In*)a.out, a.T, a.chunk, nc, a.scale, (int)((a.flags & TWOMAMBA_FLAG_NO_NORM) != 0));
+    ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 

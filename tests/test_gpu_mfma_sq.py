@@ -1,0 +1,121 @@
+"""GPU parity of the MFMA 2Mamba forward (bf16 inputs, d = 64) against the fp64 oracle.
+
+Cases span several 64-token chunks with ragged tails, the multi-segment path
+(few heads and long sequences are split into segments chained by a scan), the
+weak-decay regimes where the carried state dominates, a carried initial state,
+the unnormalised numerator and the query scale.  Tolerance: per-head inf-norm
+relative error <= 2e-2 (bf16 inputs, fp32 accumulation), for outputs and for the
+final state and normaliser.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import second_order_ssm_amd as tmb
+import synth_inputs as SI
+from oracle import twomamba_oracle as O
+from gpu_util import TOL, announce, dev, host64, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def o64(*ts):
+    return tuple(SI.to_f64(t) for t in ts)
+
+
+def oracle_state(B, H, d, seed, z_mean):
+    _, k0, v0, z0 = SI.draw(B, H, 48, d, seed=seed, dtype="f32", z_mean=z_mean)
+    S0, n0 = O.final_state_direct(SI.to_f64(k0), SI.to_f64(v0), SI.to_f64(z0))
+    S0 = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).cuda()
+    n0 = torch.from_numpy(np.ascontiguousarray(n0, dtype=np.float32)).cuda()
+    return S0, n0
+
+
+CASES = [
+    # B, H, T, z_mean, z_neg_inf
+    (1, 2, 64, 0.0, False),
+    (2, 3, 200, 0.0, False),
+    (1, 2, 1000, -6.0, False),     # 4 segments, ragged tail
+    (1, 1, 1024, -10.0, False),    # 4 segments, slow decay: the carry matters
+    (2, 1, 333, 0.0, True),        # no decay at all
+    (1, 2, 1, 0.0, False),         # single token
+]
+
+
+@pytest.mark.parametrize("B,H,T,zm,zinf", CASES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_mfma_sq_matches_oracle(B, H, T, zm, zinf, with_state):
+    announce(f"MFMA SQ B={B} H={H} T={T} z_mean={zm} ninf={zinf} state={with_state}")
+    d = 64
+    q, k, v, z = SI.draw(B, H, T, d, seed=100 + T, dtype="bf16", z_mean=zm, z_neg_inf=zinf)
+    kw, S0, n0 = {}, None, None
+    if with_state:
+        S0d, n0d = oracle_state(B, H, d, seed=T, z_mean=zm)
+        kw = dict(state_in=S0d, norm_in=n0d)
+        S0, n0 = host64(S0d), host64(n0d)
+    out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True, **kw)
+    torch.cuda.synchronize()
+    qq, kk, vv, zz = o64(q, k, v, z)
+    ref = O.fwd_quadratic(qq, kk, vv, zz, state_in=S0, norm_in=n0)
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz, state_in=S0, norm_in=n0)
+    e_out, e_s, e_n = relerr(host64(out), ref), relerr(host64(S), S_ref), relerr(host64(n), n_ref)
+    print(f"  err out {e_out:.2e} state {e_s:.2e} norm {e_n:.2e}")
+    assert e_out < TOL["bf16"]
+    assert e_s < TOL["bf16"] and e_n < TOL["bf16"]
+
+
+def test_mfma_sq_no_norm_and_scale():
+    announce("MFMA SQ NO_NORM, scale 0.5")
+    q, k, v, z = SI.draw(1, 2, 300, 64, seed=5, dtype="bf16", z_mean=-4.0)
+    out = tmb.fwd(*dev(q, k, v, z), no_norm=True, scale=0.5)
+    torch.cuda.synchronize()
+    ref = O.fwd_quadratic(*o64(q, k, v, z), scale=0.5, norm=False)
+    assert relerr(host64(out), ref) < TOL["bf16"]
+
+
+def test_mfma_sq_large_magnitudes():
+    # inputs far from unit scale exercise the per-chunk power-of-two scaling
+    announce("MFMA SQ q*300, k/500, v*1e4")
+    q, k, v, z = SI.draw(1, 2, 260, 64, seed=6, dtype="f32", z_mean=-5.0)
+    q, k, v = (q * 300).bfloat16(), (k / 500).bfloat16(), (v * 1e4).bfloat16()
+    out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True)
+    torch.cuda.synchronize()
+    qq, kk, vv, zz = o64(q, k, v, z)
+    assert relerr(host64(out), O.fwd_quadratic(qq, kk, vv, zz)) < TOL["bf16"]
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz)
+    assert relerr(host64(S), S_ref) < TOL["bf16"] and relerr(host64(n), n_ref) < TOL["bf16"]
+
+
+def test_mfma_matches_reference_kernels():
+    # the two HIP paths agree with each other on a mid-size multi-segment case
+    announce("MFMA SQ vs reference kernels, B=2 H=2 T=2048")
+    q, k, v, z = dev(*SI.draw(2, 2, 2048, 64, seed=8, dtype="bf16", z_mean=-7.0))
+    a, Sa, na = tmb.fwd(q, k, v, z, want_state=True)
+    b, Sb, nb = tmb.fwd(q, k, v, z, want_state=True, reference_kernels=True)
+    torch.cuda.synchronize()
+    assert relerr(host64(a), host64(b)) < TOL["bf16"]
+    assert relerr(host64(Sa), host64(Sb)) < TOL["bf16"]
+
+
+def test_mfma_split_resume():
+    announce("MFMA SQ split/resume T=700 = 300 + 400")
+    q, k, v, z = dev(*SI.draw(1, 2, 700, 64, seed=9, dtype="bf16", z_mean=-8.0))
+    full, Sf, nf = tmb.fwd(q, k, v, z, want_state=True)
+    sl = lambda x, a, b: x[:, :, a:b].contiguous()
+    o1, S1, n1 = tmb.fwd(sl(q, 0, 300), sl(k, 0, 300), sl(v, 0, 300), sl(z, 0, 300), want_state=True)
+    o2, S2, n2 = tmb.fwd(sl(q, 300, 700), sl(k, 300, 700), sl(v, 300, 700), sl(z, 300, 700),
+                         state_in=S1, norm_in=n1, want_state=True)
+    torch.cuda.synchronize()
+    assert relerr(host64(torch.cat([o1, o2], 2)), host64(full)) < TOL["bf16"]
+    assert relerr(host64(S2), host64(Sf)) < TOL["bf16"]
+
+
+def test_mfma_deterministic():
+    announce("MFMA SQ bitwise determinism")
+    q, k, v, z = dev(*SI.draw(2, 2, 777, 64, seed=10, dtype="bf16", z_mean=-3.0))
+    a = tmb.fwd(q, k, v, z, want_state=True)
+    b = tmb.fwd(q, k, v, z, want_state=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
