@@ -178,8 +178,11 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     float lf = 0.f, lfn = 0.f;      // log2 frames: true value = acc * 2^lf
     float Mb = 0.f, Mn = 0.f;       // bounds on |acc| (<= 2^14 once set)
 
+    // Segment 0 starts from the caller's state (if any).  In the main kernel a later
+    // segment starts from the scanned carry; in the segment-state kernel it starts
+    // from zero (its own contribution only).
     const bool from_abi = (seg == 0) && state_in != nullptr;
-    const bool from_ws = seg > 0;
+    const bool from_ws = !kPhase1 && seg > 0;
     if (from_abi || from_ws) {
         float mx = 0.f, mnx = 0.f;
         const size_t wsi = (size_t)(bh * (nseg - 1) + seg - 1);
