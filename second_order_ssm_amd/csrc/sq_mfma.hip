@@ -33,6 +33,7 @@
 //    segment's end state (update only), a scan kernel chains them, and the main
 //    kernel starts every segment from its carried state.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -85,13 +86,30 @@ __device__ __forceinline__ int unit_exp(float x) {
     return -(ilogbf(x) + 1);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+// DPP lane permutes inside a 16-lane row: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_ror:4, row_ror:8.  Applied in turn they bring every lane of a row the value
+// of every other lane.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float sum16(float x) {   // sum over the 16 lanes sharing lane>>4
-    for (int o = 8; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    x += dpp<0xb1>(x);
+    x += dpp<0x4e>(x);
+    x += dpp<0x124>(x);
+    x += dpp<0x128>(x);
     return x;
+}
+__device__ __forceinline__ float wave_max(float x) {   // max over the wave, non-negative inputs
+    x = fmaxf(x, dpp<0xb1>(x));
+    x = fmaxf(x, dpp<0x4e>(x));
+    x = fmaxf(x, dpp<0x124>(x));
+    x = fmaxf(x, dpp<0x128>(x));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // log2(2^a + 2^b) for a or b possibly -inf
@@ -101,8 +119,8 @@ __device__ __forceinline__ float log2_add(float a, float b) {
     return m + log2f(exp2f(a - m) + exp2f(b - m));
 }
 
-__device__ __forceinline__ void ld8_bf16(const bf16* p, float* o) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+// 8 bf16 values (raw 16-byte load) to fp32
+__device__ __forceinline__ void unpack8(const uint4 u, float* o) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -112,6 +130,7 @@ __device__ __forceinline__ void ld8_bf16(const bf16* p, float* o) {
 }
 
 struct Smem {
+    _Float16 Q2[kC][kLS];       // 2 q~ [t][d], readout of off-diagonal tiles (must precede Q)
     _Float16 Q[kC][kLS];        // q~ [t][d]
     _Float16 K[kC][kLS];        // k~ [t][d]
     _Float16 KT[kD + 1][kLS];   // k~^T [d][t]; row 64 is zero
@@ -120,11 +139,8 @@ struct Smem {
     _Float16 VT[kDV][kLS];      // intra operand v^T [n][t]
     _Float16 A[kC][kLS];        // intra weights [t][s]
     _Float16 NT[kD][kLS];       // normaliser, fp16, [j][i]
-    struct {
-        _Float16 Q2[kC][kLS];   // 2 q~, readout of off-diagonal tiles
-        float Op[kWaves][kC][kDV + 1];   // per-wave readout partials
-    } u;
-    float Oin[kC][kDV + 1];
+    float Op[kWaves][kC][kDV + 4];   // per-wave readout partials (rows 16-byte aligned)
+    float Oin[kC][kDV + 4];
     float Dint[4][kC];
     float Dinter[2][kC];
     float Gl[kC];
@@ -265,6 +281,31 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 
     float gam_seg = 0.f;   // total log decay of the segment (phase 1)
 
+    // Raw inputs of one chunk, fetched a chunk ahead: thread tix holds 8 dims of
+    // token tix/8 of q and k, threads < 256 hold 8 value columns of token tix/4,
+    // lanes of wave 0 hold the decay logit of token tix.  Tokens past T read as 0.
+    uint4 rq, rk, rv;
+    float rz;
+    auto fetch = [&](int cc, int tix) {
+        const int tt0 = cc * kC;
+        const int L = min(kC, T - tt0);
+        const size_t base = (tok_base + tt0) * kD;
+        const int ltk = tix >> 3, ld = (tix & 7) * 8;
+        const int vtk = tix >> 2, vcc = (tix & 3) * 8;
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+        rq = z4;
+        rk = z4;
+        rv = z4;
+        rz = 0.f;
+        if (ltk < L) {
+            rq = *reinterpret_cast<const uint4*>(q + base + ltk * kD + ld);
+            rk = *reinterpret_cast<const uint4*>(k + base + ltk * kD + ld);
+        }
+        if (tix < 256 && vtk < L) rv = *reinterpret_cast<const uint4*>(v + base + vtk * kD + col0 + vcc);
+        if (tix < L) rz = z[tok_base + tt0 + tix];
+    };
+    if (c_begin < c_end) fetch(c_begin, tid);
+
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * kC;
         const int Lc = min(kC, T - t0);
@@ -278,26 +319,15 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         const int gq = l16 >> 2, bq4 = l16 & 3;
 
         // ------------------------------------------------ P1: load, decay, scales
+        // raw inputs of this chunk were fetched into registers during the previous
+        // chunk's update (or before the loop)
         float qv[8], kv[8], vv[8];
         const int lt = tidc >> 3, ld8 = (tidc & 7) * 8;      // token, 8 dims
         const bool tok_ok = lt < Lc;
-        const bf16* qc = q + (tok_base + t0) * kD;          // uniform chunk bases
-        const bf16* kc = k + (tok_base + t0) * kD;
-        const bf16* vcp = v + (tok_base + t0) * kD + col0;
-        if (tok_ok) {
-            ld8_bf16(qc + (lt * kD + ld8), qv);
-            ld8_bf16(kc + (lt * kD + ld8), kv);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qv[i] = kv[i] = 0.f;
-        }
         const int vt = tidc >> 2, vc = (tidc & 3) * 8;      // threads 0..255: token, 8 value columns
-        const bool v_ok = tidc < 256 && vt < Lc;
-        if (v_ok) ld8_bf16(vcp + (vt * kD + vc), vv);
-        else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vv[i] = 0.f;
-        }
+        unpack8(rq, qv);
+        unpack8(rk, kv);
+        unpack8(rv, vv);
         float mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -311,7 +341,7 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         mv = wave_max(mv);
         if (w == 0) {
             // log decay of token `lane`, chunk-local inclusive prefix sum
-            const float g = (lane < Lc) ? decay_log(z[tok_base + t0 + lane]) : 0.f;
+            const float g = (lane < Lc) ? decay_log(rz) : 0.f;
             float s = g;
             for (int o = 1; o < 64; o <<= 1) {
                 const float y = __shfl_up(s, o, 64);
@@ -378,7 +408,7 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 sm.WKT[ld8 + i][lt] = (_Float16)(kv[i] * wk);
             }
             *reinterpret_cast<h8*>(&sm.Q[lt][ld8]) = q8;
-            *reinterpret_cast<h8*>(&sm.u.Q2[lt][ld8]) = q28;
+            *reinterpret_cast<h8*>(&sm.Q2[lt][ld8]) = q28;
             *reinterpret_cast<h8*>(&sm.K[lt][ld8]) = k8;
             if (tidc < 256) {
                 const float wv = (vt < Lc) ? exp2f((Gam - sm.Gl[vt]) * kLog2e) : 0.f;
@@ -408,12 +438,43 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             f4 O[4][2];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) O[tb][0] = O[tb][1] = f4{0.f, 0.f, 0.f, 0.f};
+            // Byte addresses into Q2 (2 q~) and Q (q~), row m = 16 tb + l16: per-lane bases
+            // for the wave's two block rows, block column and token block as immediates.
+            // Diagonal tiles read q~_i from Q, which sits right after Q2.
+            const char* smq = reinterpret_cast<const char*>(&sm);
+            constexpr int kQ2Q = (int)(offsetof(Smem, Q) - offsetof(Smem, Q2));
+            const int rowq = 2 * kLS * l16;
+            const int qaA = (int)offsetof(Smem, Q2) + rowq + 8 * wl + 2 * kg;
+            const int qaB = (int)offsetof(Smem, Q2) + rowq + 8 * (15 - wl) + 2 * kg;
+            const int qjA = (int)offsetof(Smem, Q) + rowq + 8 * wl;
+            const int qjB = (int)offsetof(Smem, Q) + rowq;
+            const int qjD = (int)offsetof(Smem, Q) + rowq + 8 * (15 - wl);
 #pragma unroll
             for (int kp = 0; kp < 9; ++kp) {
                 const int ua = 2 * kp, ub = 2 * kp + 1;
-                int iba, jba, ibb = 0, jbb = 0;
-                tile_block(wl, ua, iba, jba);
-                if (ub < kTiles) tile_block(wl, ub, ibb, jbb);
+                int aqa, aja, aqb = 0, ajb = 0;
+                if (ua == 0) {
+                    aqa = qaA + kQ2Q;
+                    aja = qjA;
+                } else if (ua == 16) {
+                    aqa = qaB + kQ2Q;
+                    aja = qjD;
+                } else if (ua <= 15 - wl) {
+                    aqa = qaA;
+                    aja = qjA + 8 * ua;
+                } else {
+                    aqa = qaB;
+                    aja = qjB + 8 * ua;
+                }
+                if (ub < kTiles) {
+                    if (ub <= 15 - wl) {
+                        aqb = qaA;
+                        ajb = qjA + 8 * ub;
+                    } else {
+                        aqb = qaB;
+                        ajb = qjB + 8 * ub;
+                    }
+                }
                 h8 B0, B1;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -424,15 +485,14 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    const int m = 16 * tb + l16;
-                    // off-diagonal tiles read 2 q~_i, diagonal tiles q~_i (their weight is in S)
-                    const _Float16 qa = (ua == 0 || ua == 16) ? sm.Q[m][4 * iba + kg] : sm.u.Q2[m][4 * iba + kg];
-                    const h4 qja = *reinterpret_cast<const h4*>(&sm.Q[m][4 * jba]);
+                    const int ro = 32 * kLS * tb;   // 16 rows of Q per token block
+                    const _Float16 qa = *reinterpret_cast<const _Float16*>(smq + aqa + ro);
+                    const h4 qja = *reinterpret_cast<const h4*>(smq + aja + ro);
                     h8 A;
                     A[0] = qa * qja[0]; A[1] = qa * qja[1]; A[2] = qa * qja[2]; A[3] = qa * qja[3];
                     if (ub < kTiles) {
-                        const _Float16 qb = sm.u.Q2[m][4 * ibb + kg];   // odd tiles are off-diagonal
-                        const h4 qjb = *reinterpret_cast<const h4*>(&sm.Q[m][4 * jbb]);
+                        const _Float16 qb = *reinterpret_cast<const _Float16*>(smq + aqb + ro);
+                        const h4 qjb = *reinterpret_cast<const h4*>(smq + ajb + ro);
                         A[4] = qb * qjb[0]; A[5] = qb * qjb[1]; A[6] = qb * qjb[2]; A[7] = qb * qjb[3];
                     } else {
                         A[4] = A[5] = A[6] = A[7] = (_Float16)0.f;
@@ -447,7 +507,7 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) sm.u.Op[w][16 * tb + 4 * kg + b][16 * ct + l16] = O[tb][ct][b];
+                    for (int b = 0; b < 4; ++b) sm.Op[w][16 * tb + 4 * kg + b][16 * ct + l16] = O[tb][ct][b];
 
             // -------------------------------------------- P3a: intra scores A = (QK^T)^2 * mask
 #pragma unroll
@@ -524,6 +584,7 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         }
 
         // ------------------------------------------------ P4: update
+        if (c + 1 < c_end) fetch(c + 1, tidc);   // next chunk's inputs, consumed in its P1
         {
             h8 BV[2][2];
 #pragma unroll
@@ -531,27 +592,62 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct)
                     BV[kk][ct] = *reinterpret_cast<const h8*>(&sm.WVT[16 * ct + l16][32 * kk + 8 * kg]);
+            // Byte addresses into K^T: per-lane bases for the wave's two block rows;
+            // the block column enters as an immediate offset (4 rows of 144 B per block).
+            const char* smb = reinterpret_cast<const char*>(&sm);
+            const int kt0 = (int)offsetof(Smem, KT) + 16 * kg;
+            const int aiA = kt0 + (4 * wl + gq) * 2 * kLS, ajA = kt0 + (4 * wl + bq4) * 2 * kLS;
+            const int aiB = kt0 + (60 - 4 * wl + gq) * 2 * kLS, ajB = kt0 + bq4 * 2 * kLS;
+            const int ajD = kt0 + (60 - 4 * wl + bq4) * 2 * kLS;
+            // When the decayed carry is below 2^-40 of the new accumulator bound (it then
+            // cannot change any fp32 result), the first MFMA starts from zero instead of
+            // multiplying every accumulator by the decay.
+            const bool reset_s = ratio_s < 0x1p-40f;
+            auto update_tiles = [&](auto reset_tag) {
+                constexpr bool kReset = decltype(reset_tag)::value;
 #pragma unroll
             for (int u = 0; u < kTiles; ++u) {
-                S[u][0] *= ratio_s;
-                S[u][1] *= ratio_s;
-                int ib, jb;
-                tile_block(wl, u, ib, jb);
-                const int i = 4 * ib + gq;
-                const int j = 4 * jb + bq4;
+                if (!kReset) {
+                    S[u][0] *= ratio_s;
+                    S[u][1] *= ratio_s;
+                }
+                int ai, aj;
+                if (u == 0) {
+                    ai = aiA;
+                    aj = ajA;
+                } else if (u == 16) {
+                    ai = aiB;
+                    aj = ajD;
+                } else if (u <= 15 - wl) {
+                    ai = aiA;
+                    aj = ajA + u * 8 * kLS;
+                } else {
+                    ai = aiB;
+                    aj = ajB + u * 8 * kLS;
+                }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const h8 ki = *reinterpret_cast<const h8*>(&sm.KT[i][32 * kk + 8 * kg]);
-                    const h8 kj = *reinterpret_cast<const h8*>(&sm.KT[j][32 * kk + 8 * kg]);
+                    const h8 ki = *reinterpret_cast<const h8*>(smb + ai + 64 * kk);
+                    const h8 kj = *reinterpret_cast<const h8*>(smb + aj + 64 * kk);
                     h8 A = ki * kj;
                     if (u == 0 || u == 16) A *= cslot;   // c * phi(k); zero on dead slots
-                    S[u][0] = mfma(A, BV[kk][0], S[u][0]);
-                    S[u][1] = mfma(A, BV[kk][1], S[u][1]);
+                    if (kReset && kk == 0) {
+                        S[u][0] = mfma(A, BV[kk][0], f4{0.f, 0.f, 0.f, 0.f});
+                        S[u][1] = mfma(A, BV[kk][1], f4{0.f, 0.f, 0.f, 0.f});
+                    } else {
+                        S[u][0] = mfma(A, BV[kk][0], S[u][0]);
+                        S[u][1] = mfma(A, BV[kk][1], S[u][1]);
+                    }
                 }
             }
+            };
+            if (reset_s) update_tiles(std::true_type{});
+            else update_tiles(std::false_type{});
+            const bool reset_n = ratio_n < 0x1p-40f;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                Nacc[x] *= ratio_n;
+                if (reset_n) Nacc[x] = f4{0.f, 0.f, 0.f, 0.f};
+                else Nacc[x] *= ratio_n;
                 const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
@@ -576,18 +672,16 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 float den = (sm.Dint[0][t] + sm.Dint[1][t]) + (sm.Dint[2][t] + sm.Dint[3][t]);
                 den = fmaf(sm.Dinter[0][t] + sm.Dinter[1][t], r_den, den);
                 const float back = exp2f(-2.f * (float)eq - 2.f * (float)ek);
-                const size_t oo = (tok_base + t0 + t) * kD + col0 + n0;
+                const float mul = no_norm ? back : (den == 0.f ? 0.f : __builtin_amdgcn_rcpf(den));
+                f4 osum = *reinterpret_cast<const f4*>(&sm.Op[0][t][n0]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float osum = 0.f;
+                for (int ww = 1; ww < kWaves; ++ww) osum += *reinterpret_cast<const f4*>(&sm.Op[ww][t][n0]);
+                const f4 oin = *reinterpret_cast<const f4*>(&sm.Oin[t][n0]);
+                uint32_t ob[4];
 #pragma unroll
-                    for (int ww = 0; ww < kWaves; ++ww) osum += sm.u.Op[ww][t][n0 + e];
-                    const float num = fmaf(sm.Oin[t][n0 + e], fin, osum * r_num);
-                    float o;
-                    if (no_norm) o = num * back;
-                    else o = (den == 0.f) ? 0.f : num / den;
-                    out[oo + e].bits = f32_to_bf16(o);
-                }
+                for (int e = 0; e < 4; ++e) ob[e] = f32_to_bf16(fmaf(oin[e], fin, osum[e] * r_num) * mul);
+                *reinterpret_cast<uint2*>(out + (tok_base + t0 + t) * kD + col0 + n0) =
+                    make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
             }
         }
         // advance the frames and bounds
