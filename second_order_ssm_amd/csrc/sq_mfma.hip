@@ -4,34 +4,34 @@
 //
 // Design (one head = (b, h)):
 //  * The packed second-order state (2080 x 64 fp32) stays in MFMA accumulator
-//    registers for the whole sequence segment a workgroup walks.  It does not
+//    registers while a workgroup walks a segment of the sequence.  It does not
 //    fit one CU (532 KB > 512 KB of VGPRs), so each head is split over two
-//    workgroups by value column (32 columns each); both form the same features.
+//    workgroups by value column (32 columns each).
 //  * Pair space.  The symmetric dim-pair matrix is cut into 4x4 blocks
 //    (ib <= jb): 120 off-diagonal blocks and 16 diagonal ones, 136 "tiles" of
-//    16 slots.  Slot r of tile (ib, jb) is the pair (4ib + r/4, 4jb + r%4).
-//    Each of the 8 waves owns 17 tiles (15 off-diagonal, 2 diagonal) x 2
-//    column tiles of 16x16 fp32 accumulators.  Diagonal tiles keep c * S in
-//    their accumulators, c = 2 above, 1 on and 0 below the dim diagonal, so
-//    that the query side needs no per-slot weight; off-diagonal tiles keep S
-//    and the query side reads 2 q_i from a pre-doubled copy.
+//    16 slots; slot r of tile (ib, jb) is the pair (4ib + r/4, 4jb + r%4).
+//    Wave w owns the block rows ib = w and ib = 15 - w (17 tiles) x 2 column
+//    tiles of 16x16 fp32 accumulators.  Diagonal tiles hold c * S (c = 2 above,
+//    1 on, 0 below the dim diagonal) so the query side needs no per-slot weight;
+//    off-diagonal tiles hold S and the query side reads 2 q_i.
 //  * Per 64-token chunk c (S_c = state before the chunk):
-//      readout   O = phi_q(Q) . S_c                      (MFMA, K = pair slots)
-//      intra     A = (Q K^T)^2 * exp(Gl_t - Gl_s), s <= t; A . V   (MFMA)
-//      norm      den via the d x d normaliser N: q^T N q  (MFMA)
-//      update    S_{c+1} = e^Gam S_c + phi(K)^T diag(w) V  (MFMA, K = tokens)
-//    The readout takes the accumulators themselves as its B operand: the rows
-//    4g..4g+3 a lane holds of two tiles are exactly the 8 K-slots that lane
-//    supplies, so the contraction over pair slots moves no data.
-//  * Operands are fp16.  Per chunk, q and k are scaled by powers of two to
-//    |x| < 1 (exact for bf16 inputs).  The accumulators carry a power-of-two
-//    "frame" (true value = acc * 2^lf) re-chosen every chunk so that a running
-//    bound on |acc| stays at 2^14; the frame change rides on the per-chunk decay
-//    multiply, the update's value operand is scaled to match, and the readout
-//    converts the accumulators to fp16 with a bare convert.
-//  * Long sequences are split into segments: a first kernel computes each
-//    segment's end state (update only), a scan kernel chains them, and the main
-//    kernel starts every segment from its carried state.
+//      readout  O = phi_q(Q) . S_c           MFMA, K = pair slots; the state
+//               accumulators are themselves the B operand (a lane's rows
+//               4g..4g+3 of two tiles are exactly the K-slots it supplies)
+//      intra    A = (Q K^T)^2 * exp(Gl_t - Gl_s), s <= t; A . [V | 1]  (MFMA)
+//      den      q^T N q with the d x d normaliser N in accumulators  (MFMA)
+//      update   S_{c+1} = e^Gam S_c + phi(K)^T diag(w) V   MFMA, K = tokens
+//  * Operands are fp16: per chunk q and k are scaled by powers of two to
+//    |x| < 1 (exact for bf16 inputs).  The accumulators carry a "frame"
+//    (true value = acc * 2^lf) kept so that a running bound on |acc| stays at
+//    or below 2^14, which makes the readout's fp16 conversion a bare convert.
+//    The chunk decay is absorbed into the frame whenever the bound allows;
+//    otherwise the accumulators are rescaled, or restarted from zero when the
+//    decayed carry is below 2^-40 of the bound (it cannot change an fp32 sum).
+//  * Long sequences are split into segments.  A first kernel computes every
+//    segment's own end state as one backward pass (a plain accumulation with
+//    weights relative to the segment end); the main kernel starts segment g
+//    from the decayed sum of the earlier segments' end states.
 #include <algorithm>
 #include <type_traits>
 
@@ -53,6 +53,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 17;      // pair tiles per wave
 constexpr int kPairs = kD * (kD + 1) / 2;
 constexpr int kLS = 72;         // LDS row stride in halves (144 B)
+constexpr int kRow = 2 * kLS;   // ... in bytes
 constexpr int kStateLane = kTiles * 2 * 4;            // fp32 state values per lane
 constexpr int kStateHalf = kWaves * 64 * kStateLane;  // per workgroup (one value half)
 constexpr int kNormWG = kD * kD;                      // full d x d normaliser
@@ -60,10 +61,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTarget = 14.f;                       // log2 of the accumulator bound
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }   // no denormal fix-up
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Wave w owns the block rows ib = w and ib = 15 - w of the upper block triangle
-// (16 - w and w + 1 blocks: 17 tiles).  Tile u: u = 0 and u = 16 are the two
-// diagonal blocks; 1 <= u <= 15 - w are (w, w + u), the rest (15 - w, u).
+__device__ __forceinline__ int pidx(int i, int j) { return i * kD - (i * (i - 1)) / 2 + (j - i); }
+
+// Wave w owns block rows ib = w and ib = 15 - w.  Tile u: u = 0 and u = 16 are
+// the diagonal blocks (w, w) and (15-w, 15-w); 1 <= u <= 15 - w is (w, w + u);
+// otherwise (15 - w, u).
 __device__ __forceinline__ void tile_block(int w, int u, int& ib, int& jb) {
     if (u == 0) {
         ib = jb = w;
@@ -78,8 +83,6 @@ __device__ __forceinline__ void tile_block(int w, int u, int& ib, int& jb) {
     }
 }
 
-__device__ __forceinline__ int pidx(int i, int j) { return i * kD - (i * (i - 1)) / 2 + (j - i); }
-
 // exponent e with x * 2^e in [0.5, 1) for x > 0; 0 for x == 0
 __device__ __forceinline__ int unit_exp(float x) {
     if (!(x > 0.f)) return 0;
@@ -87,7 +90,7 @@ __device__ __forceinline__ int unit_exp(float x) {
 }
 
 // DPP lane permutes inside a 16-lane row: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
-// row_ror:4, row_ror:8.  Applied in turn they bring every lane of a row the value
+// row_ror:4, row_ror:8.  Applied in turn they give every lane of a row the value
 // of every other lane.
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -100,26 +103,27 @@ __device__ __forceinline__ float sum16(float x) {   // sum over the 16 lanes sha
     x += dpp<0x128>(x);
     return x;
 }
-__device__ __forceinline__ float wave_max(float x) {   // max over the wave, non-negative inputs
+__device__ __forceinline__ float rdl(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ float wave_max(float x) {   // max over the wave
     x = fmaxf(x, dpp<0xb1>(x));
     x = fmaxf(x, dpp<0x4e>(x));
     x = fmaxf(x, dpp<0x124>(x));
     x = fmaxf(x, dpp<0x128>(x));
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    return fmaxf(fmaxf(rdl(x, 0), rdl(x, 16)), fmaxf(rdl(x, 32), rdl(x, 48)));
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ float wave_scan(float s, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(s, o, 64);
+        if (lane >= o) s += y;
+    }
+    return s;
 }
 
-// log2(2^a + 2^b) for a or b possibly -inf
-__device__ __forceinline__ float log2_add(float a, float b) {
-    const float m = fmaxf(a, b);
-    if (m == -INFINITY) return -INFINITY;
-    return m + log2f(exp2f(a - m) + exp2f(b - m));
-}
-
-// 8 bf16 values (raw 16-byte load) to fp32
+// 8 bf16 values (one 16-byte load) to fp32
 __device__ __forceinline__ void unpack8(const uint4 u, float* o) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -129,205 +133,337 @@ __device__ __forceinline__ void unpack8(const uint4 u, float* o) {
     }
 }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// log2(2^a + 2^b) for a or b possibly -inf
+__device__ __forceinline__ float log2_add(float a, float b) {
+    const float m = fmaxf(a, b);
+    if (m == -INFINITY) return -INFINITY;
+    return m + flog2(fexp2(a - m) + fexp2(b - m));
+}
+
+// Raw inputs of one chunk, one token per lane: lane t of wave w holds dims
+// 8w..8w+7 of q and k of token t, waves 0..3 also value columns 8w..8w+7 of
+// this workgroup's half, every wave the decay logit.  Tokens past T read as 0.
+struct Raw {
+    uint4 q, k, v;
+    float z;
+};
+
+template <bool kWithQ>
+__device__ __forceinline__ void fetch(Raw& r, const bf16* q, const bf16* k, const bf16* v, const float* z,
+                                      size_t tok_base, int T, int t0, int lane, int w, int col0) {
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    r.q = r.k = r.v = z4;
+    r.z = 0.f;
+    if (t0 + lane < T) {
+        const size_t row = (tok_base + t0 + lane) * kD;
+        if (kWithQ) r.q = *reinterpret_cast<const uint4*>(q + row + 8 * w);
+        r.k = *reinterpret_cast<const uint4*>(k + row + 8 * w);
+        if (w < 4) r.v = *reinterpret_cast<const uint4*>(v + row + col0 + 8 * w);
+        r.z = z[tok_base + t0 + lane];
+    }
+}
+
 struct Smem {
-    _Float16 Q2[kC][kLS];       // 2 q~ [t][d], readout of off-diagonal tiles (must precede Q)
+    _Float16 Q2[kC][kLS];       // 2 q~ [t][d] (must directly precede Q)
     _Float16 Q[kC][kLS];        // q~ [t][d]
     _Float16 K[kC][kLS];        // k~ [t][d]
-    _Float16 KT[kD + 1][kLS];   // k~^T [d][t]; row 64 is zero
+    _Float16 KT[kD][kLS];       // k~^T [d][t]
     _Float16 WKT[kD][kLS];      // normaliser update operand (w k)^T [d][t]
     _Float16 WVT[kDV][kLS];     // state update operand (w v)^T [n][t]
-    _Float16 VT[kDV][kLS];      // intra operand v^T [n][t]
+    _Float16 VT[kDV + 16][kLS]; // intra operand [v | 1]^T [n][t]; rows 32..47 are ones
     _Float16 A[kC][kLS];        // intra weights [t][s]
-    _Float16 NT[kD][kLS];       // normaliser, fp16, [j][i]
-    float Op[kWaves][kC][kDV + 4];   // per-wave readout partials (rows 16-byte aligned)
-    float Oin[kC][kDV + 4];
-    float Dint[4][kC];
-    float Dinter[2][kC];
-    float Gl[kC];
-    float red[kWaves][4];
-    int wid[kWaves];
+    _Float16 NT[kD][kLS];       // normaliser (fp16) [j][i]
+    float Op[kWaves][kC][kDV + 4];   // per-wave readout partials
+    float Oin[kC][kDV + 4];     // intra numerator
+    float Dint[kC];             // intra denominator
+    float Dinter[2][kC];        // normaliser readout partials
+    float Gl[kC];               // chunk-local inclusive prefix of g
+    float red[2][kWaves][4];    // per-wave maxima, double-buffered by chunk parity
     int zero;
 };
 
-template <bool kPhase1>
+struct SmemSeg {
+    _Float16 KT[kD][kLS];
+    _Float16 WKT[kD][kLS];
+    _Float16 WVT[kDV][kLS];
+    float red[2][kWaves][4];
+    int zero;
+};
+
+// ---------------------------------------------------------------------------
+// update of the 17 x 2 state tiles and the 2 normaliser tiles of this wave from
+// the chunk's K^T / (w v)^T / (w k)^T in LDS.  kZero: start from zero.
+template <bool kZero, typename SM>
+__device__ __forceinline__ void update_tiles(f4 (&S)[kTiles][2], const SM& sm, int wl, int kg, int gq, int bq4,
+                                             _Float16 cslot, int l16) {
+    const char* smb = reinterpret_cast<const char*>(&sm);
+    h8 BV[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+            BV[kk][ct] = *reinterpret_cast<const h8*>(&sm.WVT[16 * ct + l16][32 * kk + 8 * kg]);
+    // K^T byte addresses: per-lane bases for the two block rows, block column as immediate
+    const int kt0 = (int)offsetof(SM, KT) + 16 * kg;
+    const int aiA = kt0 + (4 * wl + gq) * kRow, ajA = kt0 + (4 * wl + bq4) * kRow;
+    const int aiB = kt0 + (60 - 4 * wl + gq) * kRow, ajB = kt0 + bq4 * kRow;
+    const int ajD = kt0 + (60 - 4 * wl + bq4) * kRow;
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+        int ai, aj;
+        if (u == 0) {
+            ai = aiA;
+            aj = ajA;
+        } else if (u == 16) {
+            ai = aiB;
+            aj = ajD;
+        } else if (u <= 15 - wl) {
+            ai = aiA;
+            aj = ajA + u * 4 * kRow;
+        } else {
+            ai = aiB;
+            aj = ajB + u * 4 * kRow;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const h8 ki = *reinterpret_cast<const h8*>(smb + ai + 64 * kk);
+            const h8 kj = *reinterpret_cast<const h8*>(smb + aj + 64 * kk);
+            h8 A = ki * kj;
+            if (u == 0 || u == 16) A *= cslot;   // c * phi(k); zero on dead slots
+            if (kZero && kk == 0) {
+                S[u][0] = mfma(A, BV[0][0], f4{0.f, 0.f, 0.f, 0.f});
+                S[u][1] = mfma(A, BV[0][1], f4{0.f, 0.f, 0.f, 0.f});
+            } else {
+                S[u][0] = mfma(A, BV[kk][0], S[u][0]);
+                S[u][1] = mfma(A, BV[kk][1], S[u][1]);
+            }
+        }
+    }
+}
+
+template <typename SM>
+__device__ __forceinline__ void update_norm(f4 (&N)[2], const SM& sm, int w, int l16, int kg) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const h8 a = *reinterpret_cast<const h8*>(&sm.KT[16 * nib + l16][32 * kk + 8 * kg]);
+            const h8 b = *reinterpret_cast<const h8*>(&sm.WKT[16 * njb + l16][32 * kk + 8 * kg]);
+            N[x] = mfma(a, b, N[x]);
+        }
+    }
+}
+
+// Frame choice for one accumulator family.  In: current frame lf, bound Mb of
+// |acc| (<= 2^14), chunk log2 decay lg (<= 0), log2 of the bound of the chunk's
+// new contribution in true units lc.  Out: new frame, multiplier of the old
+// accumulators (1 = no multiply), zero-start flag, new bound.
+struct Frame {
+    float lf_new, ratio, mb_new;
+    bool mul, zero;
+};
+
+__device__ __forceinline__ Frame choose_frame(float lf, float Mb, float lg, float lc) {
+    Frame f;
+    // Absorb the decay into the frame (no multiply) while the accumulator bound
+    // stays within [2^10, 2^14]: large enough that the scaled operands keep fp16
+    // precision, small enough that the readout's fp16 conversion cannot overflow.
+    const float lf_d = lf + lg;
+    const float grow = (lc == -INFINITY) ? 0.f : fexp2(fminf(lc - lf_d, 64.f));
+    const float mb_d = Mb + grow;
+    if (mb_d <= 16384.f && mb_d >= 1024.f) {
+        f.lf_new = lf_d;
+        f.ratio = 1.f;
+        f.mul = false;
+        f.zero = false;
+        f.mb_new = mb_d;
+        return f;
+    }
+    const float lold = (Mb > 0.f) ? flog2(Mb) + lf + lg : -INFINITY;
+    const float lt = log2_add(lold, lc);
+    float ln = (lt == -INFINITY) ? lf : ceilf(lt - kTarget);
+    ln = fmaxf(ln, lf + lg - 100.f);
+    f.lf_new = ln;
+    f.ratio = fexp2(lf + lg - ln);
+    f.zero = f.ratio < 0x1p-40f;
+    f.mul = !f.zero;
+    const float add = (lc == -INFINITY) ? 0.f : fexp2(lc - ln);
+    f.mb_new = (f.zero ? 0.f : Mb * f.ratio) + add;
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// main kernel: one (head, segment, value half) per workgroup
 __global__ void __launch_bounds__(kThreads, 1)
-sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                const float* __restrict__ z, bf16* __restrict__ out,
                const float* __restrict__ state_in, const float* __restrict__ norm_in,
                float* __restrict__ state_out, float* __restrict__ norm_out,
-               float* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
-               int T, int nseg, int seg_chunks, float scale, int no_norm) {
+               const float* __restrict__ ws_state, const float* __restrict__ ws_norm,
+               const float* __restrict__ ws_gam, int T, int nseg, int seg_chunks, float scale, int no_norm) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15;
-    const int kg = lane >> 4;
 
-    // block -> (head, segment, value half)
     const int half = blockIdx.x & 1;
     const int rest = blockIdx.x >> 1;
-    const int nseg_k = kPhase1 ? nseg - 1 : nseg;
-    const int seg = rest % nseg_k;
-    const int bh = rest / nseg_k;
+    const int seg = rest % nseg;
+    const int bh = rest / nseg;
     const int nc_total = (T + kC - 1) / kC;
     const int c_begin = seg * seg_chunks;
     const int c_end = min(nc_total, c_begin + seg_chunks);
     const size_t tok_base = (size_t)bh * T;
     const int col0 = half * kDV;
 
-    // update A operand: slot row l16 -> (gq, bq); diagonal-tile weight of that slot
-    const int gq = l16 >> 2, bq4 = l16 & 3;
-    const _Float16 cslot = (_Float16)(bq4 < gq ? 0.f : (bq4 == gq ? 1.f : 2.f));
-    // accumulator row 4kg + b of a diagonal tile holds c(kg, b) * S
-    float cacc[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) cacc[b] = b < kg ? 0.f : (b == kg ? 1.f : 2.f);
-
-    // ---------------------------------------------------------------- state
     f4 S[kTiles][2];
-    f4 Nacc[2];
+    f4 N[2];
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) S[u][0] = S[u][1] = f4{0.f, 0.f, 0.f, 0.f};
-    Nacc[0] = Nacc[1] = f4{0.f, 0.f, 0.f, 0.f};
-    float lf = 0.f, lfn = 0.f;      // log2 frames: true value = acc * 2^lf
-    float Mb = 0.f, Mn = 0.f;       // bounds on |acc| (<= 2^14 once set)
+    N[0] = N[1] = f4{0.f, 0.f, 0.f, 0.f};
+    float lf = 0.f, lfn = 0.f;     // log2 frames: true value = acc * 2^lf
+    float Mb = 0.f, Mn = 0.f;      // bounds on |acc|
 
-    // Segment 0 starts from the caller's state (if any).  In the main kernel a later
-    // segment starts from the scanned carry; in the segment-state kernel it starts
-    // from zero (its own contribution only).
-    const bool from_abi = (seg == 0) && state_in != nullptr;
-    const bool from_ws = !kPhase1 && seg > 0;
-    if (from_abi || from_ws) {
-        float mx = 0.f, mnx = 0.f;
-        const size_t wsi = (size_t)(bh * (nseg - 1) + seg - 1);
-        if (from_abi) {
-            const float* Sg = state_in + (size_t)bh * kPairs * kD;
+    {
+        const int lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+        float cacc[4];
 #pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                int ib, jb;
-                tile_block(w, u, ib, jb);
+        for (int b = 0; b < 4; ++b) cacc[b] = b < kg ? 0.f : (b == kg ? 1.f : 2.f);
+        const bool from_abi = (seg == 0) && state_in != nullptr;
+        if (from_abi || seg > 0) {
+            float mx = 0.f, mnx = 0.f;
+            if (from_abi) {
+                const float* Sg = state_in + (size_t)bh * kPairs * kD;
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int u = 0; u < kTiles; ++u) {
+                    int ib, jb;
+                    tile_block(w, u, ib, jb);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const int i = 4 * ib + kg, j = 4 * jb + b;
+                            float x = (i <= j) ? Sg[(size_t)pidx(i, j) * kD + col0 + 16 * ct + l16] : 0.f;
+                            if (u == 0 || u == 16) x *= cacc[b];
+                            S[u][ct][b] = x;
+                            mx = fmaxf(mx, fabsf(x));
+                        }
+                }
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const int i = 4 * ib + kg, j = 4 * jb + b;
-                        float x = (i <= j) ? Sg[(size_t)pidx(i, j) * kD + col0 + 16 * ct + l16] : 0.f;
-                        if (u == 0 || u == 16) x *= cacc[b];
-                        S[u][ct][b] = x;
-                        mx = fmaxf(mx, fabsf(x));
+                        const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
+                        N[x][b] = norm_in[(size_t)bh * kPairs + pidx(min(i, j), max(i, j))];
+                        mnx = fmaxf(mnx, fabsf(N[x][b]));
                     }
-            }
-        } else {
-            const float* Wg = ws_state + (wsi * 2 + half) * kStateHalf + (size_t)w * 64 * kStateLane;
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const float4 x = reinterpret_cast<const float4*>(Wg)[(u * 2 + ct) * 64 + lane];
-                    S[u][ct] = f4{x.x, x.y, x.z, x.w};
-                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
                 }
-        }
+            } else {
+                // carry into segment seg: sum over earlier segments h of
+                // exp(Gam_{h+1} + ... + Gam_{seg-1}) * dS_h
+                const int ns1 = nseg - 1;
+                float lw = 0.f;   // log2 weight of slot h, built from the newest one down
+                for (int h = seg - 1; h >= 0; --h) {
+                    const float wgt = fexp2(lw);
+                    const float* Wg = ws_state + ((size_t)(bh * ns1 + h) * 2 + half) * kStateHalf +
+                                      (size_t)w * 64 * kStateLane;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+                    for (int u = 0; u < kTiles; ++u)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
-                const float val = from_abi ? norm_in[(size_t)bh * kPairs + pidx(min(i, j), max(i, j))]
-                                           : ws_norm[wsi * kNormWG + i * kD + j];
-                Nacc[x][b] = val;
-                mnx = fmaxf(mnx, fabsf(val));
+                        for (int ct = 0; ct < 2; ++ct) {
+                            const float4 x = reinterpret_cast<const float4*>(Wg)[(u * 2 + ct) * 64 + lane];
+                            S[u][ct] += wgt * f4{x.x, x.y, x.z, x.w};
+                        }
+                    const float* Ng = ws_norm + (size_t)(bh * ns1 + h) * kNormWG;
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            N[x][b] += wgt * Ng[(16 * nib + 4 * kg + b) * kD + 16 * njb + l16];
+                    }
+                    lw += ws_gam[bh * ns1 + h] * kLog2e;
+                }
+#pragma unroll
+                for (int u = 0; u < kTiles; ++u)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(S[u][ct][b]));
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) mnx = fmaxf(mnx, fabsf(N[x][b]));
             }
-        }
-        mx = wave_max(mx);
-        mnx = wave_max(mnx);
-        if (lane == 0) {
-            sm.red[w][0] = mx;
-            sm.red[w][1] = mnx;
-        }
-        __syncthreads();
-        float a = 0.f, bb = 0.f;
-        for (int i = 0; i < kWaves; ++i) {
-            a = fmaxf(a, sm.red[i][0]);
-            bb = fmaxf(bb, sm.red[i][1]);
-        }
-        __syncthreads();
-        // normalise the frames so the bounds start at 2^14
-        if (a > 0.f) {
-            lf = ceilf(log2f(a) - kTarget);
-            const float f = exp2f(-lf);
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                S[u][0] *= f;
-                S[u][1] *= f;
+            mx = wave_max(mx);
+            mnx = wave_max(mnx);
+            if (lane == 0) {
+                sm.red[0][w][0] = mx;
+                sm.red[0][w][1] = mnx;
             }
-            Mb = a * f;
-        }
-        if (bb > 0.f) {
-            lfn = ceilf(log2f(bb) - kTarget);
-            const float f = exp2f(-lfn);
-            Nacc[0] *= f;
-            Nacc[1] *= f;
-            Mn = bb * f;
+            __syncthreads();
+            float a = 0.f, bb = 0.f;
+            for (int i = 0; i < kWaves; ++i) {
+                a = fmaxf(a, sm.red[0][i][0]);
+                bb = fmaxf(bb, sm.red[0][i][1]);
+            }
+            __syncthreads();
+            if (a > 0.f) {   // normalise the frames so the bounds start at 2^14
+                lf = ceilf(log2f(a) - kTarget);
+                const float f = exp2f(-lf);
+#pragma unroll
+                for (int u = 0; u < kTiles; ++u) {
+                    S[u][0] *= f;
+                    S[u][1] *= f;
+                }
+                Mb = a * f;
+            }
+            if (bb > 0.f) {
+                lfn = ceilf(log2f(bb) - kTarget);
+                const float f = exp2f(-lfn);
+                N[0] *= f;
+                N[1] *= f;
+                Mn = bb * f;
+            }
         }
     }
 
-    if (tid < kWaves) sm.wid[tid] = tid;
+    // constant parts of LDS: ones rows of [V | 1]^T, the loop-opaque zero
+    for (int e = tid; e < 16 * kLS; e += kThreads) sm.VT[kDV + e / kLS][e % kLS] = (_Float16)1.f;
     if (tid == 0) sm.zero = 0;
+
+    Raw raw;
+    if (c_begin < c_end) fetch<true>(raw, q, k, v, z, tok_base, T, c_begin * kC, tid & 63, w, col0);
     __syncthreads();
-
-    float gam_seg = 0.f;   // total log decay of the segment (phase 1)
-
-    // Raw inputs of one chunk, fetched a chunk ahead: thread tix holds 8 dims of
-    // token tix/8 of q and k, threads < 256 hold 8 value columns of token tix/4,
-    // lanes of wave 0 hold the decay logit of token tix.  Tokens past T read as 0.
-    uint4 rq, rk, rv;
-    float rz;
-    auto fetch = [&](int cc, int tix) {
-        const int tt0 = cc * kC;
-        const int L = min(kC, T - tt0);
-        const size_t base = (tok_base + tt0) * kD;
-        const int ltk = tix >> 3, ld = (tix & 7) * 8;
-        const int vtk = tix >> 2, vcc = (tix & 3) * 8;
-        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-        rq = z4;
-        rk = z4;
-        rv = z4;
-        rz = 0.f;
-        if (ltk < L) {
-            rq = *reinterpret_cast<const uint4*>(q + base + ltk * kD + ld);
-            rk = *reinterpret_cast<const uint4*>(k + base + ltk * kD + ld);
-        }
-        if (tix < 256 && vtk < L) rv = *reinterpret_cast<const uint4*>(v + base + vtk * kD + col0 + vcc);
-        if (tix < L) rz = z[tok_base + tt0 + tix];
-    };
-    if (c_begin < c_end) fetch(c_begin, tid);
 
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * kC;
         const int Lc = min(kC, T - t0);
-        // Lane-derived indices are rebuilt from a value re-read from LDS every chunk
-        // (always 0), so address arithmetic stays inside the loop instead of being
-        // hoisted into (and spilled from) registers.
+        const int par = c & 1;
+        // Lane-derived indices rebuilt from a value re-read from LDS every chunk (always
+        // 0): address arithmetic then stays inside the loop instead of being hoisted
+        // into registers.
         const int tidc = tid + sm.zero;
         const int lane = tidc & 63;
         const int l16 = lane & 15;
         const int kg = lane >> 4;
         const int gq = l16 >> 2, bq4 = l16 & 3;
+        const int wl = __builtin_amdgcn_readfirstlane(tidc >> 6);
 
-        // ------------------------------------------------ P1: load, decay, scales
-        // raw inputs of this chunk were fetched into registers during the previous
-        // chunk's update (or before the loop)
+        // ------------------------------------------------ P1a: registers only
         float qv[8], kv[8], vv[8];
-        const int lt = tidc >> 3, ld8 = (tidc & 7) * 8;      // token, 8 dims
-        const bool tok_ok = lt < Lc;
-        const int vt = tidc >> 2, vc = (tidc & 3) * 8;      // threads 0..255: token, 8 value columns
-        unpack8(rq, qv);
-        unpack8(rk, kv);
-        unpack8(rv, vv);
+        unpack8(raw.q, qv);
+        unpack8(raw.k, kv);
+        unpack8(raw.v, vv);
+        const float g = (lane < Lc) ? decay_log(raw.z) : 0.f;
+        const float gl = wave_scan(g, lane);          // Gl of token `lane`
+        const float Gam = rdl(gl, 63);
         float mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -339,111 +475,77 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         mq = wave_max(mq);
         mk = wave_max(mk);
         mv = wave_max(mv);
-        if (w == 0) {
-            // log decay of token `lane`, chunk-local inclusive prefix sum
-            const float g = (lane < Lc) ? decay_log(rz) : 0.f;
-            float s = g;
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(s, o, 64);
-                if (lane >= o) s += y;
-            }
-            sm.Gl[lane] = s;
-        }
         if (lane == 0) {
-            sm.red[w][0] = mq;
-            sm.red[w][1] = mk;
-            sm.red[w][2] = mv;
+            sm.red[par][wl][0] = mq;
+            sm.red[par][wl][1] = mk;
+            sm.red[par][wl][2] = mv;
         }
-        __syncthreads();
+        __syncthreads();   // A
 
-        // The wave index re-read from LDS after a barrier: tile addresses derived from
-        // it are recomputed per chunk instead of being hoisted into registers.
-        const int wl = __builtin_amdgcn_readfirstlane(sm.wid[tid >> 6]);
+        // ------------------------------------------------ P1b: scales, frames, operands
         float Mq = 0.f, Mk = 0.f, Mv = 0.f;
+#pragma unroll
         for (int i = 0; i < kWaves; ++i) {
-            Mq = fmaxf(Mq, sm.red[i][0]);
-            Mk = fmaxf(Mk, sm.red[i][1]);
-            Mv = fmaxf(Mv, sm.red[i][2]);
+            Mq = fmaxf(Mq, sm.red[par][i][0]);
+            Mk = fmaxf(Mk, sm.red[par][i][1]);
+            if (i < 4) Mv = fmaxf(Mv, sm.red[par][i][2]);
         }
-        const float Gam = sm.Gl[kC - 1];
         const float lg = Gam * kLog2e;
         const int eq = max(-120, min(120, unit_exp(Mq)));
         const int ek = max(-120, min(120, unit_exp(Mk)));
         const int evi = max(-120, min(120, unit_exp(Mv) + 14));
-        const float mk1 = ldexpf(Mk, ek);   // max |k~| in [0.5, 1)
-        // new state frame: bound(e^Gam S_c + dS_c) normalised to 2^14
-        float lf_new, ratio_s, lfn_new, ratio_n;
+        const float lMk = (Mk > 0.f) ? flog2(Mk) : -INFINITY;
+        const float lcs = (Mk > 0.f && Mv > 0.f) ? 7.f + 2.f * lMk + flog2(Mv) : -INFINITY;
+        const float lcn = (Mk > 0.f) ? 6.f + 2.f * lMk : -INFINITY;
+        const Frame fs = choose_frame(lf, Mb, lg, lcs);
+        const Frame fn = choose_frame(lfn, Mn, lg, lcn);
         {
-            const float lold = (Mb > 0.f) ? log2f(Mb) + lf + lg : -INFINITY;
-            const float lcon = (Mk > 0.f && Mv > 0.f) ? 7.f + 2.f * log2f(Mk) + log2f(Mv) : -INFINITY;
-            const float lt_ = log2_add(lold, lcon);
-            lf_new = (lt_ == -INFINITY) ? lf : ceilf(lt_ - kTarget);
-            lf_new = fmaxf(lf_new, lf + lg - 100.f);
-            ratio_s = exp2f(lf + lg - lf_new);
-            const float lnold = (Mn > 0.f) ? log2f(Mn) + lfn + lg : -INFINITY;
-            const float lncon = (Mk > 0.f) ? 6.f + 2.f * log2f(Mk) : -INFINITY;
-            const float ln_ = log2_add(lnold, lncon);
-            lfn_new = (ln_ == -INFINITY) ? lfn : ceilf(ln_ - kTarget);
-            lfn_new = fmaxf(lfn_new, lfn + lg - 100.f);
-            ratio_n = exp2f(lfn + lg - lfn_new);
-        }
-        // value-side operand scales: dS_acc = 2^-lf_new dS, dN_acc = 2^-lfn_new dN
-        const float sv = exp2f(-lf_new - 2.f * (float)ek);
-        const float swk = exp2f(-lfn_new - (float)ek);
-
-        // write the scaled fp16 operands
-        {
-            const float sq_ = ldexpf(1.f, eq), sk_ = ldexpf(1.f, ek);
-            const float wt = tok_ok ? exp2f((Gam - sm.Gl[lt]) * kLog2e) : 0.f;   // w_s = exp(Gam - Gl_s)
-            const float wk = wt * swk;
+            const float sq = ldexpf(1.f, eq), sk = ldexpf(1.f, ek);
+            const float wt = (lane < Lc) ? fexp2((Gam - gl) * kLog2e) : 0.f;   // w_t = exp(Gam - Gl_t)
+            const float swk = wt * fexp2(-fn.lf_new - (float)ek);             // (w k) operand, dN_acc = 2^-lfn dN
+            const float swv = wt * fexp2(-fs.lf_new - 2.f * (float)ek);       // (w v) operand, dS_acc = 2^-lf dS
+            const float svi = ldexpf(1.f, evi);
             h8 q8, q28, k8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float qq = qv[i] * sq_;
+                const float qq = qv[i] * sq, kt = kv[i] * sk;
                 q8[i] = (_Float16)qq;
                 q28[i] = (_Float16)(2.f * qq);
-                const float kt = kv[i] * sk_;
                 k8[i] = (_Float16)kt;
-                sm.KT[ld8 + i][lt] = (_Float16)kt;
-                sm.WKT[ld8 + i][lt] = (_Float16)(kv[i] * wk);
+                sm.KT[8 * wl + i][lane] = (_Float16)kt;
+                sm.WKT[8 * wl + i][lane] = (_Float16)(kv[i] * swk);
             }
-            *reinterpret_cast<h8*>(&sm.Q[lt][ld8]) = q8;
-            *reinterpret_cast<h8*>(&sm.Q2[lt][ld8]) = q28;
-            *reinterpret_cast<h8*>(&sm.K[lt][ld8]) = k8;
-            if (tidc < 256) {
-                const float wv = (vt < Lc) ? exp2f((Gam - sm.Gl[vt]) * kLog2e) : 0.f;
-                const float svw = sv * wv, svi = ldexpf(1.f, evi);
+            *reinterpret_cast<h8*>(&sm.Q[lane][8 * wl]) = q8;
+            *reinterpret_cast<h8*>(&sm.Q2[lane][8 * wl]) = q28;
+            *reinterpret_cast<h8*>(&sm.K[lane][8 * wl]) = k8;
+            if (wl < 4) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    sm.WVT[vc + i][vt] = (_Float16)(vv[i] * svw);
-                    sm.VT[vc + i][vt] = (_Float16)(vv[i] * svi);
+                    sm.WVT[8 * wl + i][lane] = (_Float16)(vv[i] * swv);
+                    sm.VT[8 * wl + i][lane] = (_Float16)(vv[i] * svi);
                 }
             }
-        }
-        if (!kPhase1) {
-            // normaliser of S_c to fp16 (|N_acc| <= 2^14)
+            if (wl == 0) sm.Gl[lane] = gl;
+            // normaliser of S_c to fp16 (|N| <= 2^14)
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+                const int nt = 2 * wl + x, nib = nt >> 2, njb = nt & 3;
                 h4 t4;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) t4[b] = (_Float16)Nacc[x][b];
+                for (int b = 0; b < 4; ++b) t4[b] = (_Float16)N[x][b];
                 *reinterpret_cast<h4*>(&sm.NT[16 * njb + l16][16 * nib + 4 * kg]) = t4;
             }
         }
-        __syncthreads();
+        __syncthreads();   // B
 
-        if (!kPhase1) {
-            // -------------------------------------------- P2: readout of S_c
+        // ------------------------------------------------ P2: readout of S_c
+        {
             f4 O[4][2];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) O[tb][0] = O[tb][1] = f4{0.f, 0.f, 0.f, 0.f};
-            // Byte addresses into Q2 (2 q~) and Q (q~), row m = 16 tb + l16: per-lane bases
-            // for the wave's two block rows, block column and token block as immediates.
-            // Diagonal tiles read q~_i from Q, which sits right after Q2.
             const char* smq = reinterpret_cast<const char*>(&sm);
             constexpr int kQ2Q = (int)(offsetof(Smem, Q) - offsetof(Smem, Q2));
-            const int rowq = 2 * kLS * l16;
+            const int rowq = kRow * l16;
             const int qaA = (int)offsetof(Smem, Q2) + rowq + 8 * wl + 2 * kg;
             const int qaB = (int)offsetof(Smem, Q2) + rowq + 8 * (15 - wl) + 2 * kg;
             const int qjA = (int)offsetof(Smem, Q) + rowq + 8 * wl;
@@ -485,7 +587,7 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    const int ro = 32 * kLS * tb;   // 16 rows of Q per token block
+                    const int ro = 16 * kRow * tb;
                     const _Float16 qa = *reinterpret_cast<const _Float16*>(smq + aqa + ro);
                     const h4 qja = *reinterpret_cast<const h4*>(smq + aja + ro);
                     h8 A;
@@ -501,18 +603,20 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     O[tb][1] = mfma(A, B1, O[tb][1]);
                 }
             }
-            // this wave's partial readout (over its pair slots) to LDS
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) sm.Op[w][16 * tb + 4 * kg + b][16 * ct + l16] = O[tb][ct][b];
+                    for (int b = 0; b < 4; ++b) sm.Op[wl][16 * tb + 4 * kg + b][16 * ct + l16] = O[tb][ct][b];
+        }
 
-            // -------------------------------------------- P3a: intra scores A = (QK^T)^2 * mask
+        // ------------------------------------------------ P3a: intra scores, den readout
+        {
+            // 16 tiles (tt, ts) of the 64 x 64 score matrix, two per wave; upper ones are zero
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                const int tile = 2 * w + x, tt = tile >> 2, ts = tile & 3;
+                const int tile = 2 * wl + x, tt = tile >> 2, ts = tile & 3;
                 if (ts <= tt) {
                     f4 X = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -526,202 +630,126 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         const int t = 16 * tt + 4 * kg + b;
-                        float a = 0.f;
-                        if (s <= t) a = X[b] * X[b] * exp2f((sm.Gl[t] - gls) * kLog2e);
+                        const float a = (s <= t) ? X[b] * X[b] * fexp2((sm.Gl[t] - gls) * kLog2e) : 0.f;
                         sm.A[t][s] = (_Float16)a;
-                        const float rs = sum16(a);
-                        if (l16 == 0) sm.Dint[ts][t] = rs;
                     }
                 } else {
 #pragma unroll
                     for (int b = 0; b < 4; ++b) sm.A[16 * tt + 4 * kg + b][16 * ts + l16] = (_Float16)0.f;
-                    if (l16 == 0) {
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) sm.Dint[ts][16 * tt + 4 * kg + b] = 0.f;
-                    }
                 }
             }
-        }
-        __syncthreads();
-
-        if (!kPhase1) {
-            // -------------------------------------------- P3b: intra A.V, den q^T N q
-            {
-                const int tb = w >> 1, ct = w & 1;
+            // den readout: Y = Q N~, then sum_j Q[t][j] Y[t][j]
+            const int tb = wl >> 1, jh = wl & 1;
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int jt = 2 * jh + c2;
                 f4 Y = f4{0.f, 0.f, 0.f, 0.f};
-                const int nk = tb >= 2 ? 2 : 1;
-                for (int kk = 0; kk < nk; ++kk) {
-                    const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
-                    const h8 b = *reinterpret_cast<const h8*>(&sm.VT[16 * ct + l16][32 * kk + 8 * kg]);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const h8 a = *reinterpret_cast<const h8*>(&sm.Q[16 * tb + l16][32 * kk + 8 * kg]);
+                    const h8 b = *reinterpret_cast<const h8*>(&sm.NT[16 * jt + l16][32 * kk + 8 * kg]);
                     Y = mfma(a, b, Y);
                 }
 #pragma unroll
-                for (int b = 0; b < 4; ++b) sm.Oin[16 * tb + 4 * kg + b][16 * ct + l16] = Y[b];
+                for (int b = 0; b < 4; ++b) part[b] += (float)sm.Q[16 * tb + 4 * kg + b][16 * jt + l16] * Y[b];
             }
-            {
-                const int tb = w >> 1, jh = w & 1;
-                float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const int jt = 2 * jh + c2;
-                    f4 Y = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const h8 a = *reinterpret_cast<const h8*>(&sm.Q[16 * tb + l16][32 * kk + 8 * kg]);
-                        const h8 b = *reinterpret_cast<const h8*>(&sm.NT[16 * jt + l16][32 * kk + 8 * kg]);
-                        Y = mfma(a, b, Y);
-                    }
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        part[b] += (float)sm.Q[16 * tb + 4 * kg + b][16 * jt + l16] * Y[b];
+            for (int b = 0; b < 4; ++b) {
+                const float sred = sum16(part[b]);
+                if (l16 == 0) sm.Dinter[jh][16 * tb + 4 * kg + b] = sred;
+            }
+        }
+        __syncthreads();   // C
+
+        // ------------------------------------------------ P3b: intra [A.V | rowsum A]
+        {
+            const int tb = wl & 3;
+            const int nk = tb >= 2 ? 2 : 1;
+            if (wl < 4) {
+                f4 Y0 = f4{0.f, 0.f, 0.f, 0.f}, Y1 = Y0;
+                for (int kk = 0; kk < nk; ++kk) {
+                    const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
+                    const h8 b0 = *reinterpret_cast<const h8*>(&sm.VT[l16][32 * kk + 8 * kg]);
+                    const h8 b1 = *reinterpret_cast<const h8*>(&sm.VT[16 + l16][32 * kk + 8 * kg]);
+                    Y0 = mfma(a, b0, Y0);
+                    Y1 = mfma(a, b1, Y1);
                 }
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const float sred = sum16(part[b]);
-                    if (l16 == 0) sm.Dinter[jh][16 * tb + 4 * kg + b] = sred;
+                    sm.Oin[16 * tb + 4 * kg + b][l16] = Y0[b];
+                    sm.Oin[16 * tb + 4 * kg + b][16 + l16] = Y1[b];
+                }
+            } else {
+                f4 Y = f4{0.f, 0.f, 0.f, 0.f};
+                for (int kk = 0; kk < nk; ++kk) {
+                    const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
+                    const h8 b = *reinterpret_cast<const h8*>(&sm.VT[kDV + l16][32 * kk + 8 * kg]);
+                    Y = mfma(a, b, Y);
+                }
+                if (l16 == 0) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) sm.Dint[16 * tb + 4 * kg + b] = Y[b];
                 }
             }
         }
 
-        // ------------------------------------------------ P4: update
-        if (c + 1 < c_end) fetch(c + 1, tidc);   // next chunk's inputs, consumed in its P1
+        // ------------------------------------------------ P4: update (and next chunk's fetch)
+        if (c + 1 < c_end) fetch<true>(raw, q, k, v, z, tok_base, T, t0 + kC, lane, wl, col0);
         {
-            h8 BV[2][2];
+            const _Float16 cslot = (_Float16)(bq4 < gq ? 0.f : (bq4 == gq ? 1.f : 2.f));
+            if (fs.mul) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-                    BV[kk][ct] = *reinterpret_cast<const h8*>(&sm.WVT[16 * ct + l16][32 * kk + 8 * kg]);
-            // Byte addresses into K^T: per-lane bases for the wave's two block rows;
-            // the block column enters as an immediate offset (4 rows of 144 B per block).
-            const char* smb = reinterpret_cast<const char*>(&sm);
-            const int kt0 = (int)offsetof(Smem, KT) + 16 * kg;
-            const int aiA = kt0 + (4 * wl + gq) * 2 * kLS, ajA = kt0 + (4 * wl + bq4) * 2 * kLS;
-            const int aiB = kt0 + (60 - 4 * wl + gq) * 2 * kLS, ajB = kt0 + bq4 * 2 * kLS;
-            const int ajD = kt0 + (60 - 4 * wl + bq4) * 2 * kLS;
-            // When the decayed carry is below 2^-40 of the new accumulator bound (it then
-            // cannot change any fp32 result), the first MFMA starts from zero instead of
-            // multiplying every accumulator by the decay.
-            const bool reset_s = ratio_s < 0x1p-40f;
-            auto update_tiles = [&](auto reset_tag) {
-                constexpr bool kReset = decltype(reset_tag)::value;
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                if (!kReset) {
-                    S[u][0] *= ratio_s;
-                    S[u][1] *= ratio_s;
-                }
-                int ai, aj;
-                if (u == 0) {
-                    ai = aiA;
-                    aj = ajA;
-                } else if (u == 16) {
-                    ai = aiB;
-                    aj = ajD;
-                } else if (u <= 15 - wl) {
-                    ai = aiA;
-                    aj = ajA + u * 8 * kLS;
-                } else {
-                    ai = aiB;
-                    aj = ajB + u * 8 * kLS;
-                }
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const h8 ki = *reinterpret_cast<const h8*>(smb + ai + 64 * kk);
-                    const h8 kj = *reinterpret_cast<const h8*>(smb + aj + 64 * kk);
-                    h8 A = ki * kj;
-                    if (u == 0 || u == 16) A *= cslot;   // c * phi(k); zero on dead slots
-                    if (kReset && kk == 0) {
-                        S[u][0] = mfma(A, BV[kk][0], f4{0.f, 0.f, 0.f, 0.f});
-                        S[u][1] = mfma(A, BV[kk][1], f4{0.f, 0.f, 0.f, 0.f});
-                    } else {
-                        S[u][0] = mfma(A, BV[kk][0], S[u][0]);
-                        S[u][1] = mfma(A, BV[kk][1], S[u][1]);
-                    }
+                for (int u = 0; u < kTiles; ++u) {
+                    S[u][0] *= fs.ratio;
+                    S[u][1] *= fs.ratio;
                 }
             }
-            };
-            if (reset_s) update_tiles(std::true_type{});
-            else update_tiles(std::false_type{});
-            const bool reset_n = ratio_n < 0x1p-40f;
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                if (reset_n) Nacc[x] = f4{0.f, 0.f, 0.f, 0.f};
-                else Nacc[x] *= ratio_n;
-                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const h8 a = *reinterpret_cast<const h8*>(&sm.KT[16 * nib + l16][32 * kk + 8 * kg]);
-                    const h8 b = *reinterpret_cast<const h8*>(&sm.WKT[16 * njb + l16][32 * kk + 8 * kg]);
-                    Nacc[x] = mfma(a, b, Nacc[x]);
-                }
+            if (fs.zero) update_tiles<true>(S, sm, wl, kg, gq, bq4, cslot, l16);
+            else update_tiles<false>(S, sm, wl, kg, gq, bq4, cslot, l16);
+            if (fn.zero) N[0] = N[1] = f4{0.f, 0.f, 0.f, 0.f};
+            else if (fn.mul) {
+                N[0] *= fn.ratio;
+                N[1] *= fn.ratio;
             }
+            update_norm(N, sm, wl, l16, kg);
         }
+        __syncthreads();   // D
 
-        if (!kPhase1) {
-            __syncthreads();
-            // -------------------------------------------- P5: combine and write out
-            // o = (Oin 2^-evi + Osum r_num(t)) / (Dint + Dinter r_den(t)) after dropping the
-            // common factor 2^-(2eq+2ek) of numerator and denominator.
+        // ------------------------------------------------ P5: combine and write out
+        // o = (Oin 2^-evi + Osum r_num(t)) / (Dint + Dinter r_den(t)) after dropping the
+        // common factor 2^-(2eq+2ek) of numerator and denominator.
+        {
             const int t = tidc >> 3, n0 = (tidc & 7) * 4;
             if (t < Lc) {
                 const float glt = sm.Gl[t] * kLog2e;
-                const float r_num = exp2f(glt + lf + 2.f * (float)ek);
-                const float r_den = exp2f(glt + lfn + 2.f * (float)ek);
+                const float r_num = fexp2(glt + lf + 2.f * (float)ek);
+                const float r_den = fexp2(glt + lfn + 2.f * (float)ek);
                 const float fin = ldexpf(1.f, -evi);
-                float den = (sm.Dint[0][t] + sm.Dint[1][t]) + (sm.Dint[2][t] + sm.Dint[3][t]);
-                den = fmaf(sm.Dinter[0][t] + sm.Dinter[1][t], r_den, den);
-                const float back = exp2f(-2.f * (float)eq - 2.f * (float)ek);
+                const float den = fmaf(sm.Dinter[0][t] + sm.Dinter[1][t], r_den, sm.Dint[t]);
+                const float back = fexp2(-2.f * (float)eq - 2.f * (float)ek);
                 const float mul = no_norm ? back : (den == 0.f ? 0.f : __builtin_amdgcn_rcpf(den));
                 f4 osum = *reinterpret_cast<const f4*>(&sm.Op[0][t][n0]);
 #pragma unroll
                 for (int ww = 1; ww < kWaves; ++ww) osum += *reinterpret_cast<const f4*>(&sm.Op[ww][t][n0]);
                 const f4 oin = *reinterpret_cast<const f4*>(&sm.Oin[t][n0]);
-                uint32_t ob[4];
+                f4 o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ob[e] = f32_to_bf16(fmaf(oin[e], fin, osum[e] * r_num) * mul);
+                for (int e = 0; e < 4; ++e) o[e] = fmaf(oin[e], fin, osum[e] * r_num) * mul;
                 *reinterpret_cast<uint2*>(out + (tok_base + t0 + t) * kD + col0 + n0) =
-                    make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
         }
-        // advance the frames and bounds
-        // |dS_acc| <= 64 * 2 (diagonal weight) * |k~|^2 * |v| sv ; |dN_acc| <= 64 |k~| |k| swk
-        Mb = fmaf(Mb, ratio_s, 128.f * mk1 * mk1 * Mv * sv);
-        Mn = fmaf(Mn, ratio_n, 64.f * mk1 * Mk * swk);
-        lf = lf_new;
-        lfn = lfn_new;
-        gam_seg += Gam;
-        __syncthreads();
+        lf = fs.lf_new;
+        lfn = fn.lf_new;
+        Mb = fs.mb_new;
+        Mn = fn.mb_new;
     }
 
-    // ---------------------------------------------------------------- epilogue
-    if (kPhase1) {
-        // true end state of this segment (from zero, or from state_in for segment 0),
-        // diagonal tiles still weighted by c
-        const float f = exp2f(lf), fn = exp2f(lfn);
-        const size_t wsi = (size_t)(bh * (nseg - 1) + seg);
-        float* Wg = ws_state + (wsi * 2 + half) * kStateHalf + (size_t)w * 64 * kStateLane;
-#pragma unroll
-        for (int u = 0; u < kTiles; ++u)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const f4 x = S[u][ct] * f;
-                reinterpret_cast<float4*>(Wg)[(u * 2 + ct) * 64 + lane] = make_float4(x[0], x[1], x[2], x[3]);
-            }
-        if (half == 0) {
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
-                    ws_norm[wsi * kNormWG + i * kD + j] = Nacc[x][b] * fn;
-                }
-            }
-            if (tid == 0) ws_gam[wsi] = gam_seg;
-        }
-    } else if (state_out != nullptr && seg == nseg - 1) {
-        const float f = exp2f(lf), fn = exp2f(lfn);
+    // ---------------------------------------------------------------- state out
+    if (state_out != nullptr && seg == nseg - 1) {
+        const int lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+        const float f = exp2f(lf), fnn = exp2f(lfn);
         float* Sg = state_out + (size_t)bh * kPairs * kD;
 #pragma unroll
         for (int u = 0; u < kTiles; ++u) {
@@ -746,39 +774,176 @@ sq_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
-                    if (i <= j) norm_out[(size_t)bh * kPairs + pidx(i, j)] = Nacc[x][b] * fn;
+                    if (i <= j) norm_out[(size_t)bh * kPairs + pidx(i, j)] = N[x][b] * fnn;
                 }
             }
         }
     }
 }
 
-// Chains the segment end states: afterwards slot g holds the state entering
-// segment g + 1, S_{g+1} = exp(Gam_g) S_g + dS_g with S_1 = dS_0.
-__global__ void __launch_bounds__(256)
-sq_seg_scan(float* __restrict__ ws_state, float* __restrict__ ws_norm, const float* __restrict__ ws_gam,
-            int nseg, int per_head_state, int nblk_state, int nblk_norm) {
-    const int nb = nblk_state + nblk_norm;
-    const int bh = blockIdx.x / nb;
-    const int blk = blockIdx.x % nb;
+// ---------------------------------------------------------------------------
+// Segment end states: one (head, segment < last, value half) per workgroup.
+// dS_g = sum_{s in g} exp(g_{s+1} + ... + g_end) phi(k_s) v_s^T (plus the decayed
+// caller state for g = 0), accumulated from the segment end backwards so that
+// every weight is relative to the segment end and no accumulator is ever
+// rescaled except when a chunk's contribution would overflow the frame.
+__global__ void __launch_bounds__(kThreads, 1)
+sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
+                   const float* __restrict__ state_in, const float* __restrict__ norm_in,
+                   float* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
+                   int T, int nseg, int seg_chunks) {
+    __shared__ __attribute__((aligned(16))) SmemSeg sm;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = blockIdx.x & 1;
+    const int rest = blockIdx.x >> 1;
     const int ns1 = nseg - 1;
-    float* base;
-    size_t stride;
-    if (blk < nblk_state) {
-        const int e = blk * 256 + threadIdx.x;
-        if (e >= per_head_state) return;
-        base = ws_state + (size_t)bh * ns1 * per_head_state + e;
-        stride = per_head_state;
-    } else {
-        const int e = (blk - nblk_state) * 256 + threadIdx.x;
-        if (e >= kNormWG) return;
-        base = ws_norm + (size_t)bh * ns1 * kNormWG + e;
-        stride = kNormWG;
+    const int seg = rest % ns1;
+    const int bh = rest / ns1;
+    const int c_begin = seg * seg_chunks;
+    const int c_end = c_begin + seg_chunks;   // segments before the last are full
+    const size_t tok_base = (size_t)bh * T;
+    const int col0 = half * kDV;
+
+    f4 S[kTiles][2];
+    f4 N[2];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) S[u][0] = S[u][1] = f4{0.f, 0.f, 0.f, 0.f};
+    N[0] = N[1] = f4{0.f, 0.f, 0.f, 0.f};
+    float lf = 0.f, lfn = 0.f, Mb = 0.f, Mn = 0.f;
+    float lP = 0.f;   // log2 decay from the end of the current chunk to the segment end
+
+    if (tid == 0) sm.zero = 0;
+    Raw raw;
+    fetch<false>(raw, k, k, v, z, tok_base, T, (c_end - 1) * kC, tid & 63, w, col0);
+    __syncthreads();
+
+    for (int c = c_end - 1; c >= c_begin; --c) {
+        const int t0 = c * kC;
+        const int par = c & 1;
+        const int tidc = tid + sm.zero;
+        const int lane = tidc & 63;
+        const int l16 = lane & 15;
+        const int kg = lane >> 4;
+        const int gq = l16 >> 2, bq4 = l16 & 3;
+        const int wl = __builtin_amdgcn_readfirstlane(tidc >> 6);
+
+        float kv[8], vv[8];
+        unpack8(raw.k, kv);
+        unpack8(raw.v, vv);
+        const float g = decay_log(raw.z);
+        const float gl = wave_scan(g, lane);
+        const float Gam = rdl(gl, 63);
+        float mk = 0.f, mv = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mk = fmaxf(mk, fabsf(kv[i]));
+            mv = fmaxf(mv, fabsf(vv[i]));
+        }
+        mk = wave_max(mk);
+        mv = wave_max(mv);
+        if (lane == 0) {
+            sm.red[par][wl][0] = mk;
+            sm.red[par][wl][1] = mv;
+        }
+        __syncthreads();
+        float Mk = 0.f, Mv = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            Mk = fmaxf(Mk, sm.red[par][i][0]);
+            if (i < 4) Mv = fmaxf(Mv, sm.red[par][i][1]);
+        }
+        const int ek = max(-120, min(120, unit_exp(Mk)));
+        const float lMk = (Mk > 0.f) ? flog2(Mk) : -INFINITY;
+        // contributions of this chunk, relative to the segment end (decay lP folded in)
+        const float lcs = (Mk > 0.f && Mv > 0.f) ? 7.f + 2.f * lMk + flog2(Mv) + lP : -INFINITY;
+        const float lcn = (Mk > 0.f) ? 6.f + 2.f * lMk + lP : -INFINITY;
+        const Frame fs = choose_frame(lf, Mb, 0.f, lcs);
+        const Frame fn = choose_frame(lfn, Mn, 0.f, lcn);
+        {
+            const float sk = ldexpf(1.f, ek);
+            const float lw = (Gam - gl) * kLog2e + lP;   // log2 weight of token `lane`
+            const float swk = fexp2(lw - fn.lf_new - (float)ek);
+            const float swv = fexp2(lw - fs.lf_new - 2.f * (float)ek);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sm.KT[8 * wl + i][lane] = (_Float16)(kv[i] * sk);
+                sm.WKT[8 * wl + i][lane] = (_Float16)(kv[i] * swk);
+            }
+            if (wl < 4) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sm.WVT[8 * wl + i][lane] = (_Float16)(vv[i] * swv);
+            }
+        }
+        __syncthreads();
+        if (c - 1 >= c_begin) fetch<false>(raw, k, k, v, z, tok_base, T, t0 - kC, lane, wl, col0);
+        {
+            const _Float16 cslot = (_Float16)(bq4 < gq ? 0.f : (bq4 == gq ? 1.f : 2.f));
+            if (fs.mul) {
+#pragma unroll
+                for (int u = 0; u < kTiles; ++u) {
+                    S[u][0] *= fs.ratio;
+                    S[u][1] *= fs.ratio;
+                }
+            }
+            if (fs.zero) update_tiles<true>(S, sm, wl, kg, gq, bq4, cslot, l16);
+            else update_tiles<false>(S, sm, wl, kg, gq, bq4, cslot, l16);
+            if (fn.zero) N[0] = N[1] = f4{0.f, 0.f, 0.f, 0.f};
+            else if (fn.mul) {
+                N[0] *= fn.ratio;
+                N[1] *= fn.ratio;
+            }
+            update_norm(N, sm, wl, l16, kg);
+        }
+        lf = fs.lf_new;
+        lfn = fn.lf_new;
+        Mb = fs.mb_new;
+        Mn = fn.mb_new;
+        lP += Gam * kLog2e;
     }
-    float run = base[0];
-    for (int g = 1; g < ns1; ++g) {
-        run = fmaf(expf(ws_gam[bh * ns1 + g]), run, base[g * stride]);
-        base[g * stride] = run;
+
+    // true end state (diagonal tiles weighted by c), plus the decayed caller state
+    const int lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+    const float f = exp2f(lf), fnn = exp2f(lfn), fin = exp2f(lP);
+    const bool add_in = seg == 0 && state_in != nullptr;
+    float cacc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cacc[b] = b < kg ? 0.f : (b == kg ? 1.f : 2.f);
+    const size_t wsi = (size_t)(bh * ns1 + seg);
+    float* Wg = ws_state + (wsi * 2 + half) * kStateHalf + (size_t)w * 64 * kStateLane;
+    const float* Sg = state_in ? state_in + (size_t)bh * kPairs * kD : nullptr;
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+        int ib, jb;
+        tile_block(w, u, ib, jb);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f4 x = S[u][ct] * f;
+            if (add_in) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = 4 * ib + kg, j = 4 * jb + b;
+                    float s0 = (i <= j) ? Sg[(size_t)pidx(i, j) * kD + col0 + 16 * ct + l16] : 0.f;
+                    if (u == 0 || u == 16) s0 *= cacc[b];
+                    x[b] = fmaf(fin, s0, x[b]);
+                }
+            }
+            reinterpret_cast<float4*>(Wg)[(u * 2 + ct) * 64 + lane] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    }
+    if (half == 0) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
+                float val = N[x][b] * fnn;
+                if (add_in) val = fmaf(fin, norm_in[(size_t)bh * kPairs + pidx(min(i, j), max(i, j))], val);
+                ws_norm[wsi * kNormWG + i * kD + j] = val;
+            }
+        }
+        if (tid == 0) ws_gam[wsi] = lP / kLog2e;
     }
 }
 
@@ -828,24 +993,15 @@ int run(const FwdArgs& a) {
     const bf16* k = (const bf16*)a.k;
     const bf16* v = (const bf16*)a.v;
     if (p.nseg > 1) {
-        ktimer_begin(a.timer, "sq_mfma_segstate", a.stream);
-        hipLaunchKernelGGL(sq_mfma_kernel<true>, dim3(nbh * (p.nseg - 1) * 2), dim3(kThreads), 0, st, q, k, v, a.z,
-                           (bf16*)nullptr, a.state_in, a.norm_in, (float*)nullptr, (float*)nullptr, wsS, wsN, wsG,
-                           a.T, p.nseg, p.seg_chunks, a.scale, 0);
+        ktimer_begin(a.timer, "sq_segstate", a.stream);
+        hipLaunchKernelGGL(sq_segstate_kernel, dim3(nbh * (p.nseg - 1) * 2), dim3(kThreads), 0, st, k, v, a.z,
+                           a.state_in, a.norm_in, wsS, wsN, wsG, a.T, p.nseg, p.seg_chunks);
         ktimer_end(a.timer, a.stream);
-        if (p.nseg > 2) {
-            const int per_head = 2 * kStateHalf;
-            const int nbs = (per_head + 255) / 256, nbn = (kNormWG + 255) / 256;
-            ktimer_begin(a.timer, "sq_seg_scan", a.stream);
-            hipLaunchKernelGGL(sq_seg_scan, dim3(nbh * (nbs + nbn)), dim3(256), 0, st, wsS, wsN, (const float*)wsG,
-                               p.nseg, per_head, nbs, nbn);
-            ktimer_end(a.timer, a.stream);
-        }
     }
     ktimer_begin(a.timer, "sq_mfma_main", a.stream);
-    hipLaunchKernelGGL(sq_mfma_kernel<false>, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z,
-                       (bf16*)a.out, a.state_in, a.norm_in, a.state_out, a.norm_out, wsS, wsN, wsG, a.T, p.nseg,
-                       p.seg_chunks, a.scale, no_norm);
+    hipLaunchKernelGGL(sq_main_kernel, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z, (bf16*)a.out,
+                       a.state_in, a.norm_in, a.state_out, a.norm_out, (const float*)wsS, (const float*)wsN,
+                       (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
