@@ -113,15 +113,33 @@ __device__ __forceinline__ float wave_max(float x) {   // max over the wave
     x = fmaxf(x, dpp<0x128>(x));
     return fmaxf(fmaxf(rdl(x, 0), rdl(x, 16)), fmaxf(rdl(x, 32), rdl(x, 48)));
 }
-// inclusive prefix sum over the 64 lanes
-__device__ __forceinline__ float wave_scan(float s, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(s, o, 64);
-        if (lane >= o) s += y;
-    }
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_m(float x) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, kRowMask, 0xf, true));
+}
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each 16-lane
+// row, then the total of row 0 (row 2) is added to row 1 (row 3) and the total of
+// rows 0-1 to rows 2-3.
+__device__ __forceinline__ float wave_scan(float s) {
+    s += dpp_m<0x111, 0xf>(s);
+    s += dpp_m<0x112, 0xf>(s);
+    s += dpp_m<0x114, 0xf>(s);
+    s += dpp_m<0x118, 0xf>(s);
+    s += dpp_m<0x142, 0xa>(s);
+    s += dpp_m<0x143, 0xc>(s);
     return s;
 }
+// g = -softplus(z) from the hardware exp2/log2: for exp(-|z|) below 2^-24 the
+// log1p term is dropped (an absolute error below 2^-24 in g).
+__device__ __forceinline__ float decay_log_fast(float z) {
+    const float y = fexp2(-fabsf(z) * kLog2e);
+    return -(fmaxf(z, 0.f) + flog2(1.f + y) * 0.6931471805599453f);
+}
+__device__ __forceinline__ float uni(float x) {   // wave-uniform value into a scalar register
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // 8 bf16 values (one 16-byte load) to fp32
 __device__ __forceinline__ void unpack8(const uint4 u, float* o) {
@@ -297,6 +315,15 @@ __device__ __forceinline__ Frame choose_frame(float lf, float Mb, float lg, floa
     return f;
 }
 
+__device__ __forceinline__ Frame uni_frame(Frame f) {
+    f.lf_new = uni(f.lf_new);
+    f.ratio = uni(f.ratio);
+    f.mb_new = uni(f.mb_new);
+    f.mul = uni((int)f.mul) != 0;
+    f.zero = uni((int)f.zero) != 0;
+    return f;
+}
+
 // ---------------------------------------------------------------------------
 // main kernel: one (head, segment, value half) per workgroup
 __global__ void __launch_bounds__(kThreads, 1)
@@ -461,8 +488,8 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         unpack8(raw.q, qv);
         unpack8(raw.k, kv);
         unpack8(raw.v, vv);
-        const float g = (lane < Lc) ? decay_log(raw.z) : 0.f;
-        const float gl = wave_scan(g, lane);          // Gl of token `lane`
+        const float g = (lane < Lc) ? decay_log_fast(raw.z) : 0.f;
+        const float gl = wave_scan(g);                // Gl of token `lane`
         const float Gam = rdl(gl, 63);
         float mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll
@@ -490,10 +517,13 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             Mk = fmaxf(Mk, sm.red[par][i][1]);
             if (i < 4) Mv = fmaxf(Mv, sm.red[par][i][2]);
         }
+        Mq = uni(Mq);
+        Mk = uni(Mk);
+        Mv = uni(Mv);
         const float lg = Gam * kLog2e;
-        const int eq = max(-120, min(120, unit_exp(Mq)));
-        const int ek = max(-120, min(120, unit_exp(Mk)));
-        const int evi = max(-120, min(120, unit_exp(Mv) + 14));
+        const int eq = uni(max(-120, min(120, unit_exp(Mq))));
+        const int ek = uni(max(-120, min(120, unit_exp(Mk))));
+        const int evi = uni(max(-120, min(120, unit_exp(Mv) + 14)));
         const float lMk = (Mk > 0.f) ? flog2(Mk) : -INFINITY;
         const float lcs = (Mk > 0.f && Mv > 0.f) ? 7.f + 2.f * lMk + flog2(Mv) : -INFINITY;
         const float lcn = (Mk > 0.f) ? 6.f + 2.f * lMk : -INFINITY;
@@ -585,17 +615,27 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     B0[4 + b] = (ub < kTiles) ? (_Float16)S[ub][0][b] : (_Float16)0.f;
                     B1[4 + b] = (ub < kTiles) ? (_Float16)S[ub][1][b] : (_Float16)0.f;
                 }
+                // all LDS reads of this tile pair first, so one wait covers them
+                _Float16 qa[4], qb[4];
+                h4 qja[4], qjb[4];
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     const int ro = 16 * kRow * tb;
-                    const _Float16 qa = *reinterpret_cast<const _Float16*>(smq + aqa + ro);
-                    const h4 qja = *reinterpret_cast<const h4*>(smq + aja + ro);
-                    h8 A;
-                    A[0] = qa * qja[0]; A[1] = qa * qja[1]; A[2] = qa * qja[2]; A[3] = qa * qja[3];
+                    qa[tb] = *reinterpret_cast<const _Float16*>(smq + aqa + ro);
+                    qja[tb] = *reinterpret_cast<const h4*>(smq + aja + ro);
                     if (ub < kTiles) {
-                        const _Float16 qb = *reinterpret_cast<const _Float16*>(smq + aqb + ro);
-                        const h4 qjb = *reinterpret_cast<const h4*>(smq + ajb + ro);
-                        A[4] = qb * qjb[0]; A[5] = qb * qjb[1]; A[6] = qb * qjb[2]; A[7] = qb * qjb[3];
+                        qb[tb] = *reinterpret_cast<const _Float16*>(smq + aqb + ro);
+                        qjb[tb] = *reinterpret_cast<const h4*>(smq + ajb + ro);
+                    }
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    h8 A;
+                    A[0] = qa[tb] * qja[tb][0]; A[1] = qa[tb] * qja[tb][1];
+                    A[2] = qa[tb] * qja[tb][2]; A[3] = qa[tb] * qja[tb][3];
+                    if (ub < kTiles) {
+                        A[4] = qb[tb] * qjb[tb][0]; A[5] = qb[tb] * qjb[tb][1];
+                        A[6] = qb[tb] * qjb[tb][2]; A[7] = qb[tb] * qjb[tb][3];
                     } else {
                         A[4] = A[5] = A[6] = A[7] = (_Float16)0.f;
                     }
@@ -831,8 +871,8 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
         float kv[8], vv[8];
         unpack8(raw.k, kv);
         unpack8(raw.v, vv);
-        const float g = decay_log(raw.z);
-        const float gl = wave_scan(g, lane);
+        const float g = decay_log_fast(raw.z);
+        const float gl = wave_scan(g);
         const float Gam = rdl(gl, 63);
         float mk = 0.f, mv = 0.f;
 #pragma unroll
