@@ -1,10 +1,351 @@
-// MFMA kernel of the 2Mamba-E forward (bf16 inputs, d = 64).
+// MFMA kernel of the 2Mamba-E forward for d_k = d_v = 64 and bf16 inputs
+// ("2Mamba2Furious", §6: the query-key product is exponentiated, i.e. causal
+// softmax attention whose logits carry the softplus A-mask as an additive
+// log-decay, lambda_ts = sum over r = s+1..t of g_r, g = -softplus(z)).
+//
+// Design (one workgroup = 4 waves = 256 queries of one head; one wave = 64
+// queries as two 32-query column blocks):
+//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMAs: a
+//    lane then holds one query and 16 keys, so the per-query max and sum need
+//    one exchange between the two lane halves only.  The probabilities P^T
+//    leave the accumulators as the B operand of O^T = V^T P^T directly (the key
+//    order a lane holds is matched by the order in which V^T is staged), and the
+//    per-query rescale of O^T is one multiplier per lane.
+//  * Decay bias.  For the queries of a wave with last token E, the bias of key
+//    s is -c_s with c_s = sum over r = s+1..E of softplus(z_r); the true bias
+//    -sum_{r=s+1..t} differs from it by c_t, a per-query constant that the
+//    softmax cancels, and c_t spans at most 64 tokens so no precision is lost.
+//    The bias enters as the accumulator's initial value (in units of the score
+//    before scaling), so the softmax needs one fma and one exp2 per score.
+//  * Key tiles of 64 are staged in LDS (K row-major, V transposed), double
+//    buffered, and visited from the diagonal backwards, so the running max is
+//    set by the most recent keys and is moved (rescaling O) only when a score
+//    exceeds it by more than 2^8.
+//  * Query tiles are dispatched longest first for load balance.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace twm {
+namespace {
 
-bool mfma_exp_supported(const FwdArgs&) { return false; }
-int mfma_exp_fwd(const FwdArgs&) { return TWOMAMBA_ERR_UNSUPPORTED; }
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 64;               // head dim (keys and values)
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQW = 64;              // queries per wave
+constexpr int kQT = kWaves * kQW;    // queries per workgroup
+constexpr int kKT = 64;              // keys per LDS tile
+constexpr int kLS = 72;              // LDS row stride in bf16 (144 B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;         // log2 headroom before the running max moves
+
+__device__ __forceinline__ f16v mfma(b8 a, b8 b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Lanes l and l + 32 hold the same query.  v_permlane32_swap with both operands
+// x leaves the lower-half values of x in the first result and the upper-half
+// values in the second, in every lane, so both halves combine them in the same
+// order.
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_m(float x) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, kRowMask, 0xf, true));
+}
+// inclusive prefix sum over the 64 lanes (row shifts 1, 2, 4, 8, then the row
+// totals are broadcast into the following rows)
+__device__ __forceinline__ float wave_scan(float s) {
+    s += dpp_m<0x111, 0xf>(s);
+    s += dpp_m<0x112, 0xf>(s);
+    s += dpp_m<0x114, 0xf>(s);
+    s += dpp_m<0x118, 0xf>(s);
+    s += dpp_m<0x142, 0xa>(s);
+    s += dpp_m<0x143, 0xc>(s);
+    return s;
+}
+// softplus(z) from the hardware exp2/log2 (log1p term dropped below 2^-24)
+__device__ __forceinline__ float softplus_fast(float z) {
+    const float y = fexp2(-fabsf(z) * kLog2e);
+    return fmaxf(z, 0.f) + flog2(1.f + y) * 0.6931471805599453f;
+}
+
+__device__ __forceinline__ b8 as_b8(uint4 u) { return __builtin_bit_cast(b8, u); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
+}
+
+struct ESmem {
+    uint16_t K[2][kKT][kLS];          // [key][dim]
+    uint16_t VT[2][kD][kLS];          // [value column][key], keys permuted inside groups of 16
+    float bias[2][kWaves][kKT];       // per wave: -c_s / scale
+};
+
+// Position of key s (inside a 64-key tile) in a V^T row: inside each group of
+// 16 keys, s = 8h + 4g + b goes to 8g + 4h + b, so that lane half g reads the
+// keys 4g..4g+3 and 8+4g..8+4g+3 that its accumulator rows hold as one 16-byte
+// vector.
+__device__ __forceinline__ int vt_pos(int s) { return (s & ~15) | ((s & 4) << 1) | ((s & 8) >> 1) | (s & 3); }
+
+// Per-head buffer resource: loads past `bytes` return zero, which pads the
+// ragged last tile without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ float ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Global -> register staging of one key tile.
+struct Stage {
+    uint4 k0, k1;   // K rows tid/8 and tid/8 + 32, dims 8*(tid%8)..+7
+    uint2 v[4];     // V rows 4*(tid%16)+i, columns 4*(tid/16)..+3
+    float z;        // decay logit of key lane
+};
+
+__device__ __forceinline__ void stage_load(Stage& st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           __amdgpu_buffer_rsrc_t rz, int s0, int tid, int lane) {
+    const uint32_t r0 = tid >> 3, c8 = (tid & 7) * 8;
+    st.k0 = ld16(rk, ((s0 + r0) * kD + c8) * 2);
+    st.k1 = ld16(rk, ((s0 + r0 + 32) * kD + c8) * 2);
+    const uint32_t kg = tid & 15, cg = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.v[i] = ld8(rv, ((s0 + 4 * kg + i) * kD + 4 * cg) * 2);
+    st.z = ld4f(rz, (s0 + lane) * 4);
+}
+
+// Register -> LDS for K and V^T; each wave then writes its own bias row of the
+// tile (when the tile is not past its queries).  M is the wave's running sum
+// of softplus over the keys after this tile up to E.
+__device__ __forceinline__ void stage_store(const Stage& st, ESmem& sm, int buf, int tid, int lane, int w, int s0,
+                                            int E, bool wave_needs, float& M, float inv_scale) {
+    const int r0 = tid >> 3, c8 = (tid & 7) * 8;
+    *reinterpret_cast<uint4*>(&sm.K[buf][r0][c8]) = st.k0;
+    *reinterpret_cast<uint4*>(&sm.K[buf][r0 + 32][c8]) = st.k1;
+    const int kg = tid & 15, cg = tid >> 4;
+    const int p = vt_pos(4 * kg);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        // column c of rows 4kg..4kg+3: low halves for even c, high halves for odd c
+        uint32_t e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wd = (c < 2) ? st.v[i].x : st.v[i].y;
+            e[i] = (c & 1) ? (wd >> 16) : (wd & 0xffffu);
+        }
+        *reinterpret_cast<uint2*>(&sm.VT[buf][4 * cg + c][p]) = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+    }
+    if (wave_needs) {
+        const float a = (s0 + lane <= E) ? softplus_fast(st.z) : 0.f;
+        const float incl = wave_scan(a);
+        const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+        sm.bias[buf][w][lane] = -((total - incl) + M) * inv_scale;
+        M += total;
+    }
+}
+
+// One 32-key block of scores for one 32-query block: softmax statistics update
+// (running max m, partial sum l over this lane half's keys, rescale of O) and
+// the probabilities as two bf16 B operands.
+__device__ __forceinline__ void softmax_block(f16v S, float& m, float& l, f16v (&O)[2], b8 (&P)[2], float scl,
+                                              float lazy) {
+    float mx = S[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[i]);
+    mx = half_max(mx);
+    if (__any(mx > m + lazy)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = fexp2((m - mn) * scl);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            O[0][i] *= alpha;
+            O[1][i] *= alpha;
+        }
+        m = mn;
+    }
+    const float nm = -m * scl;
+    float p[16];
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        p[i] = fexp2(fmaf(S[i], scl, nm));
+        ls += p[i];
+    }
+    l += ls;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint4 w = make_uint4(pack2(p[8 * u], p[8 * u + 1]), pack2(p[8 * u + 2], p[8 * u + 3]),
+                                   pack2(p[8 * u + 4], p[8 * u + 5]), pack2(p[8 * u + 6], p[8 * u + 7]));
+        P[u] = as_b8(w);
+    }
+}
+
+__global__ void __launch_bounds__(kThreads, 2)
+exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                const float* __restrict__ z, uint16_t* __restrict__ out, int T, int nqt, int nbh, float scale) {
+    __shared__ ESmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lo = lane & 31, g = lane >> 5;
+    const int qt = nqt - 1 - (int)(blockIdx.x / nbh);   // longest query tiles first
+    const int bh = blockIdx.x % nbh;
+    const size_t base = (size_t)bh * T;
+    const int t0 = qt * kQT;
+    const int E = min(T, t0 + kQT) - 1;
+    const int jE = E / kKT;
+    const int tw = t0 + w * kQW;                       // first query of this wave
+    const bool wact = tw < T;
+    const int Ew = min(T - 1, tw + kQW - 1);
+    const int jdiag = tw / kKT;
+    const uint32_t hb = (uint32_t)T * kD * 2;
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + base * kD, hb), rk = head_rsrc(k + base * kD, hb),
+                                 rv = head_rsrc(v + base * kD, hb), rz = head_rsrc(z + base, (uint32_t)T * 4);
+    const float scl = scale * kLog2e;
+    const float inv_scale = 1.f / scale;
+    const float lazy = kLazy / scl;
+
+    // queries as B operands: lane (lo, g) holds query tw + 32 qb + lo, dims 16 ks + 8 g .. + 7
+    b8 Qop[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int t = tw + 32 * qb + lo;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            Qop[qb][ks] = as_b8(ld16(rq, (uint32_t)(t * kD + 16 * ks + 8 * g) * 2));
+        }
+    }
+
+    f16v O[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[qb][0][i] = O[qb][1][i] = 0.f;
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    float M = 0.f;
+
+    Stage st;
+    stage_load(st, rk, rv, rz, jE * kKT, tid, lane);
+    stage_store(st, sm, 0, tid, lane, w, jE * kKT, Ew, wact && jE <= jdiag, M, inv_scale);
+    __syncthreads();
+
+    for (int j = jE, it = 0; j >= 0; --j, ++it) {
+        const int buf = it & 1;
+        if (j > 0) stage_load(st, rk, rv, rz, (j - 1) * kKT, tid, lane);
+        if (wact && j <= jdiag) {
+            const bool diag = j == jdiag;
+            const float* bias = sm.bias[buf][w];
+#pragma unroll
+            for (int kb = 1; kb >= 0; --kb) {
+                b8 Kop[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    Kop[ks] = as_b8(*reinterpret_cast<const uint4*>(&sm.K[buf][32 * kb + lo][16 * ks + 8 * g]));
+                f16v C;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const float4 c4 = *reinterpret_cast<const float4*>(&bias[32 * kb + 8 * a + 4 * g]);
+                    C[4 * a] = c4.x;
+                    C[4 * a + 1] = c4.y;
+                    C[4 * a + 2] = c4.z;
+                    C[4 * a + 3] = c4.w;
+                }
+                b8 P[2][2];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    if (diag && kb > qb) continue;
+                    f16v S = C;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) S = mfma(Kop[ks], Qop[qb][ks], S);
+                    if (diag && kb == qb) {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                if (8 * a + 4 * g + b > lo) S[4 * a + b] = -INFINITY;
+                    }
+                    softmax_block(S, m[qb], l[qb], O[qb], P[qb], scl, lazy);
+                }
+                b8 Vop[2][2];
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        Vop[mb][u] = as_b8(
+                            *reinterpret_cast<const uint4*>(&sm.VT[buf][32 * mb + lo][32 * kb + 16 * u + 8 * g]));
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    if (diag && kb > qb) continue;
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) O[qb][mb] = mfma(Vop[mb][u], P[qb][u], O[qb][mb]);
+                }
+            }
+        }
+        if (j > 0)
+            stage_store(st, sm, buf ^ 1, tid, lane, w, (j - 1) * kKT, Ew, wact && j - 1 <= jdiag, M, inv_scale);
+        __syncthreads();
+    }
+
+    if (!wact) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int t = tw + 32 * qb + lo;
+        const float lt = half_sum(l[qb]);
+        const float inv = 1.f / lt;
+        if (t >= T) continue;
+        uint16_t* o = out + (base + t) * kD;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int c = 32 * mb + 8 * a + 4 * g;
+                const uint2 wv = make_uint2(pack2(O[qb][mb][4 * a] * inv, O[qb][mb][4 * a + 1] * inv),
+                                            pack2(O[qb][mb][4 * a + 2] * inv, O[qb][mb][4 * a + 3] * inv));
+                *reinterpret_cast<uint2*>(o + c) = wv;
+            }
+    }
+}
+
+}  // namespace
+
+bool mfma_exp_supported(const FwdArgs& a) {
+    // the bias enters the accumulator divided by the scale: positive, not tiny
+    return a.dtype == TWOMAMBA_BF16 && a.dk == kD && a.dv == kD && a.scale > 1e-20f && a.T > 0 &&
+           (size_t)a.B * a.H > 0;
+}
+
+int mfma_exp_fwd(const FwdArgs& a) {
+    const int nbh = a.B * a.H;
+    const int nqt = (a.T + kQT - 1) / kQT;
+    ktimer_begin(a.timer, "exp_mfma", a.stream);
+    hipLaunchKernelGGL(exp_mfma_kernel, dim3((unsigned)nbh * nqt), dim3(kThreads), 0, (hipStream_t)a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.z, (uint16_t*)a.out, a.T,
+                       nqt, nbh, a.scale);
+    ktimer_end(a.timer, a.stream);
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
 
 }  // namespace twm
