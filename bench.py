@@ -59,8 +59,42 @@ def step_bytes_per_head(d=64, dv=64):
 
 
 def kernel_work(name, leg_work):
-    """Algorithmic work a kernel is credited with per launch (see the design notes)."""
+    """Algorithmic work credited to the dominant kernel per launch: the whole
+    leg's work, since each forward kernel executes every algorithmic step of its
+    variant itself (the segment-state pre-pass of the 2Mamba forward is extra
+    work on top)."""
     return leg_work
+
+
+KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "step_kernel": "step.hip"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def source_digest(kernel):
+    import hashlib
+
+    src = KERNEL_SOURCES.get(kernel)
+    if src is None:
+        return None
+    with open(os.path.join(ROOT, "second_order_ssm_amd", "csrc", src), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    counter summary (already scaled by the copy-kernel calibration), or None when
+    there is none or the kernel's source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = source_digest(kernel)
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if not line.startswith("kernel="):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split())
+            if kv.get("kernel") == kernel and kv.get("src_sha256") == want:
+                return float(kv["traffic_bytes"])
+    return None
 
 
 def time_loop(fn, steps, warmup):
@@ -123,7 +157,7 @@ def leg_sq(steps, warmup, variant="sq"):
         tflops=work / (ms * 1e-3) / 1e12, frac_peak_bf16=work / (ms * 1e-3) / PEAK_BF16_FLOPS,
         kernels_ms=allk,
         roofline=dict(bound="mfma" if mfma else "alu", kernel=name, achieved=achieved / 1e12, peak=peak / 1e12,
-                      unit="TFLOP/s", frac=achieved / peak, traffic=None),
+                      unit="TFLOP/s", frac=achieved / peak, traffic=measured_traffic(name)),
     )
 
 
@@ -162,44 +196,55 @@ def leg_step(warmup):
     return dict(workload=f"decode step B={B} H={H} d={d} fp32 state, {nsteps} sequential steps",
                 ms=ms, bytes_per_step=byts,
                 roofline=dict(bound="hbm", kernel="step_kernel", achieved=bw / 1e9, peak=PEAK_HBM / 1e9,
-                              unit="GB/s", frac=bw / PEAK_HBM, traffic=None))
+                              unit="GB/s", frac=bw / PEAK_HBM, traffic=measured_traffic("step_kernel")))
 
 
 def cpu_baseline(seconds):
-    """fp64 oracle (packed recurrent form) on head (0,0) of the 2Mamba workload, as many tokens as fit."""
-    import numpy as np
-
+    """fp64 oracle (packed recurrent form, all 32 heads of the 2Mamba workload at
+    once) over the first n tokens, n sized to about `seconds` of CPU work."""
     import synth_inputs as SI
     from oracle import twomamba_oracle as O
 
-    try:
-        import threadpoolctl
-        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    # the oracle is numpy elementwise work, which runs on one thread
+    cores = 1
     shp = SQ_SHAPE
     q, k, v, z = SI.draw(shp["B"], shp["H"], shp["T"], shp["d"], seed=shp["seed"], dtype="bf16")
-    q, k, v, z = (SI.to_f64(t)[:1, :1] for t in (q, k, v, z))
-    # calibrate on 32 tokens, then run a bounded sample
+    q, k, v, z = (SI.to_f64(t) for t in (q, k, v, z))
+    B, H = shp["B"], shp["H"]
     t0 = time.perf_counter()
-    O.fwd_recurrent_packed(q[:, :, :32], k[:, :, :32], v[:, :, :32], z[:, :, :32])
-    per_tok = (time.perf_counter() - t0) / 32
-    n = int(max(64, min(shp["T"], seconds / max(per_tok, 1e-9))))
+    O.fwd_recurrent_packed(q[:, :, :8], k[:, :, :8], v[:, :, :8], z[:, :, :8])
+    per_tok = (time.perf_counter() - t0) / 8
+    n = int(max(16, min(shp["T"], seconds / max(per_tok, 1e-9))))
     t0 = time.perf_counter()
     O.fwd_recurrent_packed(q[:, :, :n], k[:, :, :n], v[:, :, :n], z[:, :, :n])
     dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="head-tokens/s", cores=threads, kind="oracle",
-                sample=f"packed recurrent fp64 oracle, batch 0 head 0, first {n} of {shp['T']} tokens "
-                       f"of the B=2 H=16 T=8192 d=64 workload ({dt:.1f} s)")
+    return dict(value=B * H * n / dt, unit="head-tokens/s", cores=cores, kind="oracle",
+                sample=f"packed recurrent fp64 oracle (form C), all {B}x{H} heads of the B=2 H=16 T=8192 d=64 "
+                       f"workload, first {n} of {shp['T']} tokens ({dt:.1f} s, numpy elementwise, 1 thread)")
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, run under rocprofv3 --pmc to
+    calibrate FETCH_SIZE / WRITE_SIZE (each dispatch moves nbytes each way)."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="sq,exp,step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each head is independent, "
@@ -208,13 +253,16 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     legs = args.legs.split(",")
     res = {}
     if "sq" in legs:
         res["sq"] = leg_sq(args.steps, args.warmup, "sq")
         print(f"[bench] sq leg done: {res['sq']['ms']:.3f} ms/step", file=sys.stderr, flush=True)
     if "exp" in legs:
-        res["exp"] = leg_sq(max(3, args.steps // 4), 1, "exp")
+        res["exp"] = leg_sq(args.steps, args.warmup, "exp")
         print(f"[bench] exp leg done: {res['exp']['ms']:.3f} ms/call", file=sys.stderr, flush=True)
     if "step" in legs:
         res["step"] = leg_step(args.warmup)
