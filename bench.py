@@ -223,6 +223,29 @@ def cpu_baseline(seconds):
                        f"workload, first {n} of {shp['T']} tokens ({dt:.1f} s, numpy elementwise, 1 thread)")
 
 
+def achievable_peaks():
+    """Measured ceilings on this GPU: a plain 1 GiB device copy (bytes read +
+    written per second) and a large bf16 library GEMM (8192^3, hipBLASLt via
+    torch.matmul).  Context for the roofline fractions, which stay against the
+    published peaks."""
+    import torch
+
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_loop(lambda: dst.copy_(src), 20, 3)
+    copy_bw = 2 * src.numel() * 4 / (ms * 1e-3)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    ms = time_loop(lambda: torch.matmul(a, b), 20, 3)
+    gemm = 2 * n ** 3 / (ms * 1e-3)
+    del a, b
+    torch.cuda.empty_cache()
+    return dict(copy_GBps=copy_bw / 1e9, copy_frac_of_peak=copy_bw / PEAK_HBM,
+                bf16_gemm_TFLOPs=gemm / 1e12, bf16_gemm_frac_of_peak=gemm / PEAK_BF16_FLOPS)
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size, run under rocprofv3 --pmc to
     calibrate FETCH_SIZE / WRITE_SIZE (each dispatch moves nbytes each way)."""
@@ -243,6 +266,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="sq,exp,step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the copy / GEMM ceiling measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -267,6 +292,14 @@ def main():
     if "step" in legs:
         res["step"] = leg_step(args.warmup)
         print(f"[bench] step leg done: {res['step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    peaks = achievable_peaks() if args.peaks else None
+    if peaks:
+        for leg in res.values():
+            rf = leg["roofline"]
+            if rf["unit"] == "GB/s":
+                rf["frac_of_measured_copy"] = rf["achieved"] / peaks["copy_GBps"]
+            elif rf["bound"] == "mfma":
+                rf["frac_of_measured_gemm"] = rf["achieved"] / peaks["bf16_gemm_TFLOPs"]
     cpu = cpu_baseline(args.cpu_seconds) if args.cpu_seconds > 0 else None
     head = res.get("sq") or next(iter(res.values()))
     line = {
@@ -287,6 +320,7 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "legs": res,
+        "measured_peaks": peaks,
     }
     print(json.dumps(line))
 

@@ -87,12 +87,17 @@ __device__ __forceinline__ float softplus_fast(float z) {
 }
 
 __device__ __forceinline__ b8 as_b8(uint4 u) { return __builtin_bit_cast(b8, u); }
+// sum of the two bf16 halves of w added to c (exact products, fp32 sum)
+__device__ __forceinline__ float dot2_ones(uint32_t w, float c) {
+    const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), one, c, false);
+}
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     const f2 f = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
 }
 
-struct ESmem {
+struct __attribute__((aligned(16))) ESmem {
     uint16_t K[2][kKT][kLS];          // [key][dim]
     uint16_t VT[2][kD][kLS];          // [value column][key], keys permuted inside groups of 16
     float bias[2][kWaves][kKT];       // per wave: -c_s / scale
@@ -167,47 +172,118 @@ __device__ __forceinline__ void stage_store(const Stage& st, ESmem& sm, int buf,
     }
 }
 
-// One 32-key block of scores for one 32-query block: softmax statistics update
-// (running max m, partial sum l over this lane half's keys, rescale of O) and
-// the probabilities as two bf16 B operands.
+// Probabilities of one 32-key x 32-query score block as two bf16 B operands;
+// the row sum is taken over the rounded values the PV product uses.
+__device__ __forceinline__ void probs(const f16v& S, float nm, float scl, float& l, b8 (&P)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = fexp2(fmaf(S[8 * u + 2 * e], scl, nm));
+            const float p1 = fexp2(fmaf(S[8 * u + 2 * e + 1], scl, nm));
+            wd[e] = pack2(p0, p1);
+            l = dot2_ones(wd[e], l);
+        }
+        P[u] = as_b8(make_uint4(wd[0], wd[1], wd[2], wd[3]));
+    }
+}
+
+__device__ __forceinline__ void rescale(float mx, float& m, float& l, f16v (&O)[2], float scl) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = fexp2((m - mn) * scl);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        O[0][i] *= alpha;
+        O[1][i] *= alpha;
+    }
+    m = mn;
+}
+
+// One 32-key block of scores for one 32-query block (diagonal tiles): softmax
+// statistics update (running max m, partial sum l over this lane half's keys,
+// rescale of O) and the probabilities as two bf16 B operands.
 __device__ __forceinline__ void softmax_block(f16v S, float& m, float& l, f16v (&O)[2], b8 (&P)[2], float scl,
                                               float lazy) {
     float mx = S[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[i]);
     mx = half_max(mx);
-    if (__any(mx > m + lazy)) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = fexp2((m - mn) * scl);
-        l *= alpha;
+    if (__any(mx > m + lazy)) rescale(mx, m, l, O, scl);
+    probs(S, -m * scl, scl, l, P);
+}
+
+// A 64-key tile wholly before this wave's queries: the four score blocks
+// first, one max / rescale decision for the tile, then probabilities and the
+// PV products, so that MFMA and VALU work share large basic blocks.
+__device__ __forceinline__ void tile_full(const ESmem& sm, int buf, int w, int lo, int g, const b8 (&Qop)[2][4],
+                                          f16v (&O)[2][2], float (&m)[2], float (&l)[2], float scl, float lazy) {
+    const float* bias = sm.bias[buf][w];
+    f16v S[2][2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            O[0][i] *= alpha;
-            O[1][i] *= alpha;
+    for (int kb = 0; kb < 2; ++kb) {
+        b8 Kop[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            Kop[ks] = as_b8(*reinterpret_cast<const uint4*>(&sm.K[buf][32 * kb + lo][16 * ks + 8 * g]));
+        f16v C;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const float4 c4 = *reinterpret_cast<const float4*>(&bias[32 * kb + 8 * a + 4 * g]);
+            C[4 * a] = c4.x;
+            C[4 * a + 1] = c4.y;
+            C[4 * a + 2] = c4.z;
+            C[4 * a + 3] = c4.w;
         }
-        m = mn;
-    }
-    const float nm = -m * scl;
-    float p[16];
-    float ls = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        p[i] = fexp2(fmaf(S[i], scl, nm));
-        ls += p[i];
-    }
-    l += ls;
+        for (int qb = 0; qb < 2; ++qb) {
+            S[kb][qb] = mfma(Kop[0], Qop[qb][0], C);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const uint4 w = make_uint4(pack2(p[8 * u], p[8 * u + 1]), pack2(p[8 * u + 2], p[8 * u + 3]),
-                                   pack2(p[8 * u + 4], p[8 * u + 5]), pack2(p[8 * u + 6], p[8 * u + 7]));
-        P[u] = as_b8(w);
+            for (int ks = 1; ks < 4; ++ks) S[kb][qb] = mfma(Kop[ks], Qop[qb][ks], S[kb][qb]);
+        }
+    }
+    float mx[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float x = fmaxf(S[0][qb][0], S[1][qb][0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, fmaxf(S[0][qb][i], S[1][qb][i]));
+        mx[qb] = half_max(x);
+    }
+    if (__any(mx[0] > m[0] + lazy || mx[1] > m[1] + lazy)) {
+        rescale(mx[0], m[0], l[0], O[0], scl);
+        rescale(mx[1], m[1], l[1], O[1], scl);
+    }
+    b8 P[2][2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float nm = -m[qb] * scl;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) probs(S[kb][qb], nm, scl, l[qb], P[kb][qb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        b8 Vop[2][2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                Vop[mb][u] =
+                    as_b8(*reinterpret_cast<const uint4*>(&sm.VT[buf][32 * mb + lo][32 * kb + 16 * u + 8 * g]));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) O[qb][mb] = mfma(Vop[mb][u], P[kb][qb][u], O[qb][mb]);
     }
 }
 
 __global__ void __launch_bounds__(kThreads, 2)
 exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                 const float* __restrict__ z, uint16_t* __restrict__ out, int T, int nqt, int nbh, float scale) {
-    __shared__ ESmem sm;
+    __shared__ __attribute__((aligned(16))) ESmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lo = lane & 31, g = lane >> 5;
     const int qt = nqt - 1 - (int)(blockIdx.x / nbh);   // longest query tiles first
     const int bh = blockIdx.x % nbh;
@@ -253,8 +329,10 @@ exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     for (int j = jE, it = 0; j >= 0; --j, ++it) {
         const int buf = it & 1;
         if (j > 0) stage_load(st, rk, rv, rz, (j - 1) * kKT, tid, lane);
-        if (wact && j <= jdiag) {
-            const bool diag = j == jdiag;
+        if (wact && j < jdiag) {
+            tile_full(sm, buf, w, lo, g, Qop, O, m, l, scl, lazy);
+        } else if (wact && j == jdiag) {
+            constexpr bool diag = true;
             const float* bias = sm.bias[buf][w];
 #pragma unroll
             for (int kb = 1; kb >= 0; --kb) {
