@@ -6,9 +6,11 @@
 // is read and written once.  One workgroup per (b, h) streams that head's rows
 // front to back; consecutive threads own consecutive 16-byte column slices of a
 // row, so every wave reads and writes whole contiguous rows (fully coalesced).
-// The state is touched once per step, so its loads and stores are non-temporal;
-// 512 threads with 6 rows in flight each was the fastest shape measured (about
-// 5.9 TB/s at B = 64, H = 32, against 5.1 TB/s for a plain device copy).
+// The state is touched once per step, so the main sweep's loads and stores are
+// non-temporal; 512 threads with 6 rows in flight each was the fastest shape
+// measured (about 5.9 TB/s at B = 64, H = 32, against 5.1 TB/s for a plain
+// device copy).  The short tail sweep uses ordinary loads and stores: making
+// it non-temporal as well measured 8 % slower.
 // The readout sum over rows is reduced in a fixed order through LDS, so results
 // are bit-reproducible.
 #include "device_common.h"
@@ -103,14 +105,14 @@ step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __rest
         }
     }
     for (; p < D; p += NR) {
-        const float4 x = ld_nt(&S[(size_t)p * CG + cg]);
+        const float4 x = S[(size_t)p * CG + cg];
         const float fk = s_fk[p], fq = s_fq[p];
         float4 y;
         y.x = fmaf(a, x.x, fk * v4.x);
         y.y = fmaf(a, x.y, fk * v4.y);
         y.z = fmaf(a, x.z, fk * v4.z);
         y.w = fmaf(a, x.w, fk * v4.w);
-        st_nt(&S[(size_t)p * CG + cg], y);
+        S[(size_t)p * CG + cg] = y;
         acc.x = fmaf(fq, y.x, acc.x);
         acc.y = fmaf(fq, y.y, acc.y);
         acc.z = fmaf(fq, y.z, acc.z);
