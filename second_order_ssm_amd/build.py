@@ -28,6 +28,13 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
+# Per-source extra device flags.  The 2Mamba-E kernel's row maxima are plain
+# fmaxf chains over MFMA results; without NaN semantics the compiler emits
+# v_max3 directly instead of canonicalising every operand first (NaN inputs
+# are undefined for the operator).
+FILE_FLAGS = {"exp_mfma.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
@@ -36,7 +43,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ, src + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, *DEVICE, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", path, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-x", "c++", "-c", path, "-o", obj]
     if verbose:

@@ -17,10 +17,11 @@
 //    softmax cancels, and c_t spans at most 64 tokens so no precision is lost.
 //    The bias enters as the accumulator's initial value (in units of the score
 //    before scaling), so the softmax needs one fma and one exp2 per score.
-//  * Key tiles of 64 are staged in LDS (K row-major, V transposed), double
-//    buffered, and visited from the diagonal backwards, so the running max is
-//    set by the most recent keys and is moved (rescaling O) only when a score
-//    exceeds it by more than 2^8.
+//  * Key tiles of 64 travel by buffer-to-LDS transfers into a ring of three
+//    slots, two tiles ahead of their use; K and V stay row-major (swizzled) and
+//    the V^T operand comes from transposing LDS reads.  Tiles are visited from
+//    the diagonal backwards, so the running max is set by the most recent keys
+//    and is moved (rescaling O) only when a score exceeds it by more than 2^8.
 //  * Query tiles are dispatched longest first for load balance.
 #include <algorithm>
 
@@ -97,17 +98,31 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
 }
 
-struct __attribute__((aligned(16))) ESmem {
-    uint16_t K[2][kKT][kLS];          // [key][dim]
-    uint16_t VT[2][kD][kLS];          // [value column][key], keys permuted inside groups of 16
-    float bias[2][kWaves][kKT];       // per wave: -c_s / scale
+constexpr int kNST = 3;             // key tiles in flight (LDS ring)
+
+// K and V tiles are stored row-major, 128 bytes per key row, with the 16-byte
+// chunks of each row XOR-swizzled (see k_off, v_off) against bank conflicts.
+// The tiles are written by buffer-to-LDS transfers two tiles ahead of use.
+struct __attribute__((aligned(16))) Slot {
+    uint16_t K[kKT * kD];
+    uint16_t V[kKT * kD];
+    float Z[kWaves][kKT];         // decay logits of the tile, one copy per wave
+    float B[kWaves][kKT];         // per wave: -c_s / scale, computed from Z
 };
 
-// Position of key s (inside a 64-key tile) in a V^T row: inside each group of
-// 16 keys, s = 8h + 4g + b goes to 8g + 4h + b, so that lane half g reads the
-// keys 4g..4g+3 and 8+4g..8+4g+3 that its accumulator rows hold as one 16-byte
-// vector.
-__device__ __forceinline__ int vt_pos(int s) { return (s & ~15) | ((s & 4) << 1) | ((s & 8) >> 1) | (s & 3); }
+// K: chunk c of key row r sits at position c ^ fk(r), fk using only r mod 32,
+// so that the two 32-row halves share per-lane offsets; eight consecutive rows
+// (and the same-parity rows of sixteen) fall on distinct positions.
+__device__ __forceinline__ int fk(int row) { return ((row & 31) ^ ((row & 31) >> 3)) & 7; }
+__device__ __forceinline__ int k_off(int row, int c) { return row * 128 + ((c ^ fk(row)) << 4); }
+// V: only the two low chunk bits are swizzled, by r mod 4, which keeps the
+// transposing reads' addresses a per-lane constant plus immediates.
+__device__ __forceinline__ int v_pos(int row, int c) { return (c & 4) | ((c & 3) ^ (row & 3)); }
+__device__ __forceinline__ int v_off(int row, int c) { return row * 128 + (v_pos(row, c) << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
 
 // Per-head buffer resource: loads past `bytes` return zero, which pads the
 // ragged last tile without branches.
@@ -117,59 +132,77 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* p, uint3
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-__device__ __forceinline__ float ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
 
-// Global -> register staging of one key tile.
-struct Stage {
-    uint4 k0, k1;   // K rows tid/8 and tid/8 + 32, dims 8*(tid%8)..+7
-    uint2 v[4];     // V rows 4*(tid%16)+i, columns 4*(tid/16)..+3
-    float z;        // decay logit of key lane
-};
-
-__device__ __forceinline__ void stage_load(Stage& st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                           __amdgpu_buffer_rsrc_t rz, int s0, int tid, int lane) {
-    const uint32_t r0 = tid >> 3, c8 = (tid & 7) * 8;
-    st.k0 = ld16(rk, ((s0 + r0) * kD + c8) * 2);
-    st.k1 = ld16(rk, ((s0 + r0 + 32) * kD + c8) * 2);
-    const uint32_t kg = tid & 15, cg = tid >> 4;
+// Start the transfers of key tile s0 into ring slot st: wave w fills key rows
+// 16w..16w+15 of K and V (two 1 KB transfers each; lane l of a transfer lands
+// at byte 16 l, so it fetches the chunk the swizzle places there) and its own
+// copy of the 64 decay logits.  Five transfers per lane per tile.
+__device__ __forceinline__ void issue_tile(Slot& sl, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           __amdgpu_buffer_rsrc_t rz, int s0, int w, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = ld8(rv, ((s0 + 4 * kg + i) * kD + 4 * cg) * 2);
-    st.z = ld4f(rz, (s0 + lane) * 4);
-}
-
-// Register -> LDS for K and V^T; each wave then writes its own bias row of the
-// tile (when the tile is not past its queries).  M is the wave's running sum
-// of softplus over the keys after this tile up to E.
-__device__ __forceinline__ void stage_store(const Stage& st, ESmem& sm, int buf, int tid, int lane, int w, int s0,
-                                            int E, bool wave_needs, float& M, float inv_scale) {
-    const int r0 = tid >> 3, c8 = (tid & 7) * 8;
-    *reinterpret_cast<uint4*>(&sm.K[buf][r0][c8]) = st.k0;
-    *reinterpret_cast<uint4*>(&sm.K[buf][r0 + 32][c8]) = st.k1;
-    const int kg = tid & 15, cg = tid >> 4;
-    const int p = vt_pos(4 * kg);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        // column c of rows 4kg..4kg+3: low halves for even c, high halves for odd c
-        uint32_t e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t wd = (c < 2) ? st.v[i].x : st.v[i].y;
-            e[i] = (c & 1) ? (wd >> 16) : (wd & 0xffffu);
-        }
-        *reinterpret_cast<uint2*>(&sm.VT[buf][4 * cg + c][p]) = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+    for (int n = 0; n < 2; ++n) {
+        const int r = 16 * w + 8 * n + (lane >> 3);
+        const int p = lane & 7;                       // position this lane fills
+        const int ck = p ^ fk(r);                     // logical chunk stored there (the maps are involutions)
+        const int cv = v_pos(r, p);
+        char* kd = reinterpret_cast<char*>(sl.K) + (16 * w + 8 * n) * 128;
+        char* vd = reinterpret_cast<char*>(sl.V) + (16 * w + 8 * n) * 128;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)kd, 16, (uint32_t)((s0 + r) * kD + 8 * ck) * 2, 0, 0,
+                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)vd, 16, (uint32_t)((s0 + r) * kD + 8 * cv) * 2, 0, 0,
+                                                 0);
     }
-    if (wave_needs) {
-        const float a = (s0 + lane <= E) ? softplus_fast(st.z) : 0.f;
-        const float incl = wave_scan(a);
-        const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
-        sm.bias[buf][w][lane] = -((total - incl) + M) * inv_scale;
-        M += total;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)sl.Z[w], 4, (uint32_t)(s0 + lane) * 4, 0, 0, 0);
+}
+
+// A operand of S^T = K Q^T: key row 32 kb + lo, dims 16 ks + 8 g .. + 7
+__device__ __forceinline__ b8 k_operand(const Slot& sl, int kb, int ks, int lo, int g) {
+    const char* t = reinterpret_cast<const char*>(sl.K);
+    return as_b8(*reinterpret_cast<const uint4*>(t + k_off(32 * kb + lo, 2 * ks + g)));
+}
+
+// A operand of O^T = V^T P^T for value columns 32 mb .. + 31 and the key
+// group 32 kb + 16 u: lane (c, g) needs V[key][c] for keys 4g..4g+3 and
+// 8+4g..8+4g+3 of the group.  Two transposing reads: inside a 16-lane group,
+// lane 4j + r addresses 4 columns c0 + 4r .. + 3 of key row base + j, and lane
+// l then receives column c0 + l of the four rows base .. base + 3.
+__device__ __forceinline__ b8 vt_operand(const Slot& sl, int kb, int mb, int u, int lane) {
+    const int G = lane >> 4, m16 = lane & 15, j = m16 >> 2, r = m16 & 3;
+    const int g = G >> 1, half = G & 1;
+    const int col = 32 * mb + 16 * half + 4 * r;
+    const int row = 32 * kb + 16 * u + 4 * g + j;
+    const char* t = reinterpret_cast<const char*>(sl.V);
+    const int sub = (col & 7) * 2;
+    const s4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(t + v_off(row, col >> 3) + sub));
+    const s4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(t + v_off(row + 8, col >> 3) + sub));
+    const uint2 a = __builtin_bit_cast(uint2, x0), b = __builtin_bit_cast(uint2, x1);
+    return as_b8(make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// The wave's decay bias for the tile: with a_s = softplus(z_s) for keys up to
+// E (0 after it), bias_s = -(sum of a over s+1 .. tile end + M) / scale, where
+// M is the sum over the later tiles already visited.
+__device__ __forceinline__ void tile_bias(Slot& sl, int w, int lane, int s0, int E, float& M,
+                                          float inv_scale) {
+    const float a = (s0 + lane <= E) ? softplus_fast(sl.Z[w][lane]) : 0.f;
+    const float incl = wave_scan(a);
+    const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+    sl.B[w][lane] = -((total - incl) + M) * inv_scale;
+    M += total;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the row is written before the wave reads it back
+}
+
+__device__ __forceinline__ f16v bias_init(const Slot& sl, int w, int kb, int g) {
+    f16v C;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&sl.B[w][32 * kb + 8 * a + 4 * g]);
+        C[4 * a] = c4.x;
+        C[4 * a + 1] = c4.y;
+        C[4 * a + 2] = c4.z;
+        C[4 * a + 3] = c4.w;
     }
+    return C;
 }
 
 // Probabilities of one 32-key x 32-query score block as two bf16 B operands;
@@ -214,76 +247,134 @@ __device__ __forceinline__ void softmax_block(f16v S, float& m, float& l, f16v (
     probs(S, -m * scl, scl, l, P);
 }
 
-// A 64-key tile wholly before this wave's queries: the four score blocks
-// first, one max / rescale decision for the tile, then probabilities and the
-// PV products, so that MFMA and VALU work share large basic blocks.
-__device__ __forceinline__ void tile_full(const ESmem& sm, int buf, int w, int lo, int g, const b8 (&Qop)[2][4],
+// A 64-key tile wholly before this wave's queries, in two 32-key halves (the
+// later keys first): per half, the two query blocks' score MFMAs, one
+// max / rescale decision, then probabilities and the PV products.
+__device__ __forceinline__ void tile_full(const Slot& sl, int w, int lane, const b8 (&Qop)[2][4],
                                           f16v (&O)[2][2], float (&m)[2], float (&l)[2], float scl, float lazy) {
-    const float* bias = sm.bias[buf][w];
-    f16v S[2][2];
+    const int lo = lane & 31, g = lane >> 5;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        b8 Kop[4];
+    for (int kb = 1; kb >= 0; --kb) {
+        f16v S[2];
+        {
+            b8 Kop[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            Kop[ks] = as_b8(*reinterpret_cast<const uint4*>(&sm.K[buf][32 * kb + lo][16 * ks + 8 * g]));
-        f16v C;
+            for (int ks = 0; ks < 4; ++ks) Kop[ks] = k_operand(sl, kb, ks, lo, g);
+            const f16v C = bias_init(sl, w, kb, g);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const float4 c4 = *reinterpret_cast<const float4*>(&bias[32 * kb + 8 * a + 4 * g]);
-            C[4 * a] = c4.x;
-            C[4 * a + 1] = c4.y;
-            C[4 * a + 2] = c4.z;
-            C[4 * a + 3] = c4.w;
+            for (int qb = 0; qb < 2; ++qb) {
+                S[qb] = mfma(Kop[0], Qop[qb][0], C);
+#pragma unroll
+                for (int ks = 1; ks < 4; ++ks) S[qb] = mfma(Kop[ks], Qop[qb][ks], S[qb]);
+            }
         }
+        float mx[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            S[kb][qb] = mfma(Kop[0], Qop[qb][0], C);
+            float x = S[qb][0];
 #pragma unroll
-            for (int ks = 1; ks < 4; ++ks) S[kb][qb] = mfma(Kop[ks], Qop[qb][ks], S[kb][qb]);
+            for (int i = 1; i < 16; ++i) x = fmaxf(x, S[qb][i]);
+            mx[qb] = half_max(x);
         }
-    }
-    float mx[2];
+        if (__any(mx[0] > m[0] + lazy || mx[1] > m[1] + lazy)) {
+            rescale(mx[0], m[0], l[0], O[0], scl);
+            rescale(mx[1], m[1], l[1], O[1], scl);
+        }
+        b8 P[2][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float x = fmaxf(S[0][qb][0], S[1][qb][0]);
-#pragma unroll
-        for (int i = 1; i < 16; ++i) x = fmaxf(x, fmaxf(S[0][qb][i], S[1][qb][i]));
-        mx[qb] = half_max(x);
-    }
-    if (__any(mx[0] > m[0] + lazy || mx[1] > m[1] + lazy)) {
-        rescale(mx[0], m[0], l[0], O[0], scl);
-        rescale(mx[1], m[1], l[1], O[1], scl);
-    }
-    b8 P[2][2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float nm = -m[qb] * scl;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) probs(S[kb][qb], nm, scl, l[qb], P[kb][qb]);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int qb = 0; qb < 2; ++qb) probs(S[qb], -m[qb] * scl, scl, l[qb], P[qb]);
         b8 Vop[2][2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                Vop[mb][u] =
-                    as_b8(*reinterpret_cast<const uint4*>(&sm.VT[buf][32 * mb + lo][32 * kb + 16 * u + 8 * g]));
+            for (int u = 0; u < 2; ++u) Vop[mb][u] = vt_operand(sl, kb, mb, u, lane);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) O[qb][mb] = mfma(Vop[mb][u], P[kb][qb][u], O[qb][mb]);
+                for (int u = 0; u < 2; ++u) O[qb][mb] = mfma(Vop[mb][u], P[qb][u], O[qb][mb]);
+    }
+}
+
+// The diagonal tile of a wave: per 32-key block, causal mask inside the
+// blocks on the diagonal, blocks above it skipped.
+__device__ __forceinline__ void tile_diag(const Slot& sl, int w, int lane, const b8 (&Qop)[2][4],
+                                          f16v (&O)[2][2], float (&m)[2], float (&l)[2], float scl, float lazy) {
+    const int lo = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int kb = 1; kb >= 0; --kb) {
+        b8 Kop[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) Kop[ks] = k_operand(sl, kb, ks, lo, g);
+        const f16v C = bias_init(sl, w, kb, g);
+        b8 P[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            if (kb > qb) continue;
+            f16v S = C;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) S = mfma(Kop[ks], Qop[qb][ks], S);
+            if (kb == qb) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        if (8 * a + 4 * g + b > lo) S[4 * a + b] = -INFINITY;
+            }
+            softmax_block(S, m[qb], l[qb], O[qb], P[qb], scl, lazy);
+        }
+        b8 Vop[2][2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) Vop[mb][u] = vt_operand(sl, kb, mb, u, lane);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            if (kb > qb) continue;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) O[qb][mb] = mfma(Vop[mb][u], P[qb][u], O[qb][mb]);
+        }
+    }
+}
+
+struct WaveState {
+    f16v O[2][2];
+    float m[2], l[2], M;
+};
+
+// One key tile j from slot `cur` while the transfers of tile j - 2 go into
+// slot `nxt` (the slot tile j + 1 used).  The slots are distinct shared
+// arrays, so the compiler can tell the reads of `cur` from the transfers in
+// flight into the other two and needs no wait for them.
+__device__ __forceinline__ void tile_step(Slot* __restrict__ curp, Slot* __restrict__ nxtp, int j, int w, int lane, int jdiag, int Ew,
+                                          bool wact, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          __amdgpu_buffer_rsrc_t rz, const b8 (&Qop)[2][4], WaveState& ws, float scl,
+                                          float lazy, float inv_scale) {
+    Slot& cur = *curp;
+    Slot& nxt = *nxtp;
+    // this wave's transfers of tile j have landed (those of tile j - 1 may not)
+    if (j >= 1) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+    // every wave's transfers of tile j are visible and every wave is done with
+    // tile j + 1, whose slot is refilled next
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j >= 2) issue_tile(nxt, rk, rv, rz, (j - 2) * kKT, w, lane);
+    if (wact && j <= jdiag) {
+        tile_bias(cur, w, lane, j * kKT, Ew, ws.M, inv_scale);
+        if (j < jdiag) tile_full(cur, w, lane, Qop, ws.O, ws.m, ws.l, scl, lazy);
+        else tile_diag(cur, w, lane, Qop, ws.O, ws.m, ws.l, scl, lazy);
     }
 }
 
 __global__ void __launch_bounds__(kThreads, 2)
 exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                 const float* __restrict__ z, uint16_t* __restrict__ out, int T, int nqt, int nbh, float scale) {
-    __shared__ __attribute__((aligned(16))) ESmem sm;
+    __shared__ Slot slot0, slot1, slot2;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lo = lane & 31, g = lane >> 5;
     const int qt = nqt - 1 - (int)(blockIdx.x / nbh);   // longest query tiles first
     const int bh = blockIdx.x % nbh;
@@ -313,85 +404,38 @@ exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
         }
     }
 
-    f16v O[2][2];
+    WaveState ws;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) O[qb][0][i] = O[qb][1][i] = 0.f;
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-    float M = 0.f;
+        for (int i = 0; i < 16; ++i) ws.O[qb][0][i] = ws.O[qb][1][i] = 0.f;
+        ws.m[qb] = -INFINITY;
+        ws.l[qb] = 0.f;
+    }
+    ws.M = 0.f;
 
-    Stage st;
-    stage_load(st, rk, rv, rz, jE * kKT, tid, lane);
-    stage_store(st, sm, 0, tid, lane, w, jE * kKT, Ew, wact && jE <= jdiag, M, inv_scale);
-    __syncthreads();
-
-    for (int j = jE, it = 0; j >= 0; --j, ++it) {
-        const int buf = it & 1;
-        if (j > 0) stage_load(st, rk, rv, rz, (j - 1) * kKT, tid, lane);
-        if (wact && j < jdiag) {
-            tile_full(sm, buf, w, lo, g, Qop, O, m, l, scl, lazy);
-        } else if (wact && j == jdiag) {
-            constexpr bool diag = true;
-            const float* bias = sm.bias[buf][w];
-#pragma unroll
-            for (int kb = 1; kb >= 0; --kb) {
-                b8 Kop[4];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    Kop[ks] = as_b8(*reinterpret_cast<const uint4*>(&sm.K[buf][32 * kb + lo][16 * ks + 8 * g]));
-                f16v C;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float4 c4 = *reinterpret_cast<const float4*>(&bias[32 * kb + 8 * a + 4 * g]);
-                    C[4 * a] = c4.x;
-                    C[4 * a + 1] = c4.y;
-                    C[4 * a + 2] = c4.z;
-                    C[4 * a + 3] = c4.w;
-                }
-                b8 P[2][2];
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    if (diag && kb > qb) continue;
-                    f16v S = C;
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) S = mfma(Kop[ks], Qop[qb][ks], S);
-                    if (diag && kb == qb) {
-#pragma unroll
-                        for (int a = 0; a < 4; ++a)
-#pragma unroll
-                            for (int b = 0; b < 4; ++b)
-                                if (8 * a + 4 * g + b > lo) S[4 * a + b] = -INFINITY;
-                    }
-                    softmax_block(S, m[qb], l[qb], O[qb], P[qb], scl, lazy);
-                }
-                b8 Vop[2][2];
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        Vop[mb][u] = as_b8(
-                            *reinterpret_cast<const uint4*>(&sm.VT[buf][32 * mb + lo][32 * kb + 16 * u + 8 * g]));
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    if (diag && kb > qb) continue;
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) O[qb][mb] = mfma(Vop[mb][u], P[qb][u], O[qb][mb]);
-                }
-            }
-        }
-        if (j > 0)
-            stage_store(st, sm, buf ^ 1, tid, lane, w, (j - 1) * kKT, Ew, wact && j - 1 <= jdiag, M, inv_scale);
-        __syncthreads();
+    // Ring of three key-tile slots, two tiles in flight ahead of the one in
+    // use: tile j lives in slot (jE - j) mod 3.
+    issue_tile(slot0, rk, rv, rz, jE * kKT, w, lane);
+    if (jE >= 1) {
+        issue_tile(slot1, rk, rv, rz, (jE - 1) * kKT, w, lane);
+        __builtin_amdgcn_s_waitcnt(0x0F7A);   // vmcnt(10): the query operands have landed
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+    }
+    for (int j = jE; j >= 0; j -= 3) {
+        tile_step(&slot0, &slot2, j, w, lane, jdiag, Ew, wact, rk, rv, rz, Qop, ws, scl, lazy, inv_scale);
+        if (j - 1 < 0) break;
+        tile_step(&slot1, &slot0, j - 1, w, lane, jdiag, Ew, wact, rk, rv, rz, Qop, ws, scl, lazy, inv_scale);
+        if (j - 2 < 0) break;
+        tile_step(&slot2, &slot1, j - 2, w, lane, jdiag, Ew, wact, rk, rv, rz, Qop, ws, scl, lazy, inv_scale);
     }
 
     if (!wact) return;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const int t = tw + 32 * qb + lo;
-        const float lt = half_sum(l[qb]);
+        const float lt = half_sum(ws.l[qb]);
         const float inv = 1.f / lt;
         if (t >= T) continue;
         uint16_t* o = out + (base + t) * kD;
@@ -400,8 +444,8 @@ exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int c = 32 * mb + 8 * a + 4 * g;
-                const uint2 wv = make_uint2(pack2(O[qb][mb][4 * a] * inv, O[qb][mb][4 * a + 1] * inv),
-                                            pack2(O[qb][mb][4 * a + 2] * inv, O[qb][mb][4 * a + 3] * inv));
+                const uint2 wv = make_uint2(pack2(ws.O[qb][mb][4 * a] * inv, ws.O[qb][mb][4 * a + 1] * inv),
+                                            pack2(ws.O[qb][mb][4 * a + 2] * inv, ws.O[qb][mb][4 * a + 3] * inv));
                 *reinterpret_cast<uint2*>(o + c) = wv;
             }
     }
