@@ -400,13 +400,25 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     const float wgt = fexp2(lw);
                     const float* Wg = ws_state + ((size_t)(bh * ns1 + h) * 2 + half) * kStateHalf +
                                       (size_t)w * 64 * kStateLane;
+                    // in batches of 12 loads, all in flight before any is used
 #pragma unroll
-                    for (int u = 0; u < kTiles; ++u)
+                    for (int u0 = 0; u0 < kTiles; u0 += 6) {
+                        float4 xs[6][2];
 #pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) {
-                            const float4 x = reinterpret_cast<const float4*>(Wg)[(u * 2 + ct) * 64 + lane];
-                            S[u][ct] += wgt * f4{x.x, x.y, x.z, x.w};
-                        }
+                        for (int du = 0; du < 6; ++du)
+#pragma unroll
+                            for (int ct = 0; ct < 2; ++ct)
+                                if (u0 + du < kTiles)
+                                    xs[du][ct] = reinterpret_cast<const float4*>(Wg)[((u0 + du) * 2 + ct) * 64 + lane];
+#pragma unroll
+                        for (int du = 0; du < 6; ++du)
+#pragma unroll
+                            for (int ct = 0; ct < 2; ++ct)
+                                if (u0 + du < kTiles) {
+                                    const float4 x = xs[du][ct];
+                                    S[u0 + du][ct] += wgt * f4{x.x, x.y, x.z, x.w};
+                                }
+                    }
                     const float* Ng = ws_norm + (size_t)(bh * ns1 + h) * kNormWG;
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
