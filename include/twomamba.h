@@ -175,6 +175,65 @@ int twomamba_step(const twomamba_step_desc* desc,
                   const void* q, const void* k, const void* v, const float* z,
                   float* state, float* norm, void* out, void* stream);
 
+/*
+ * 2Mamba-E decoding over a key/value cache  [2M2F §6: 2Mamba-E is softmax
+ * attention with the softplus A-mask, so inference keeps every past key and
+ * value; §1-§2: the KV cache grows with the sequence].
+ *
+ * The cache of every (b, h) holds, for each past token s, its key, its value
+ * and G_s = softplus(z_0) + ... + softplus(z_s) in fp64.  At token t the decay
+ * log-bias of key s <= t is G_s - G_t (= sum of g over s+1..t), so the output
+ * is  o_t = softmax_{s<=t}(scale q_t . k_s + G_s - G_t) . v.
+ *
+ *   k_cache [B][H][max_len][dk]  dtype   device
+ *   v_cache [B][H][max_len][dv]  dtype   device
+ *   g_cache [B][H][max_len]      fp64    device
+ */
+typedef struct {
+    int B, H;           /* batch, heads                                                */
+    int dk, dv;         /* head dims; supported: dk == dv, 16 or 64                   */
+    int max_len;        /* token capacity of the caches                                */
+    int pos;            /* twomamba_exp_step: index of the new token (tokens 0..pos-1  *
+                         * are cached).  twomamba_exp_cache_fill: number of tokens T   */
+    float scale;        /* multiplies q . k                                            */
+    int dtype;          /* dtype of q, k, v, out and of the K/V caches                 */
+    unsigned flags;     /* must be 0                                                   */
+} twomamba_exp_cache_desc;
+
+/*
+ * Fill positions 0..T-1 (T = desc->pos) of the caches from a prompt: keys and
+ * values copied, G_s the running sum of softplus(z) (fp64, in token order).
+ *
+ *   k [B][H][T][dk], v [B][H][T][dv]  dtype   device
+ *   z [B][H][T]                       fp32    device
+ * T <= max_len; T = 0 does nothing.
+ */
+int twomamba_exp_cache_fill(const twomamba_exp_cache_desc* desc,
+                            const void* k, const void* v, const float* z,
+                            void* k_cache, void* v_cache, double* g_cache, void* stream);
+
+/* Bytes of device workspace twomamba_exp_step needs for *desc, written to *bytes. */
+int twomamba_exp_step_workspace_size(const twomamba_exp_cache_desc* desc, size_t* bytes);
+
+/*
+ * One 2Mamba-E decode step at position pos = desc->pos for every (b, h): the
+ * new key and value are appended at row pos of the caches (with
+ * G_pos = G_{pos-1} + softplus(z), G_{-1} = 0) and the new query attends over
+ * rows 0..pos.  pos < max_len.
+ *
+ *   q, k   [B][H][dk]     dtype   device
+ *   v      [B][H][dv]     dtype   device
+ *   z      [B][H]         fp32    device
+ *   out    [B][H][dv]     dtype   device
+ *   workspace                     device   >= twomamba_exp_step_workspace_size bytes,
+ *                                          256-byte aligned; contents undefined after
+ * The caches are read for rows 0..pos-1 and written at row pos only.
+ */
+int twomamba_exp_step(const twomamba_exp_cache_desc* desc,
+                      const void* q, const void* k, const void* v, const float* z,
+                      void* k_cache, void* v_cache, double* g_cache,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

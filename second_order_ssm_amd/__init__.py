@@ -18,6 +18,7 @@ import os
 import torch
 
 __all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "step", "library_path",
+           "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step",
            "TwoMambaError", "SQ", "EXP", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "num_pairs"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +43,12 @@ class FwdDesc(ctypes.Structure):
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
                 ("scale", ctypes.c_float), ("variant", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("flags", ctypes.c_uint)]
+
+
+class ExpCacheDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int), ("dv", ctypes.c_int),
+                ("max_len", ctypes.c_int), ("pos", ctypes.c_int), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int), ("flags", ctypes.c_uint)]
 
 
 class StepDesc(ctypes.Structure):
@@ -76,6 +83,13 @@ def load(path: str | None = None):
                                        ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.twomamba_step.restype = ctypes.c_int
     lib.twomamba_step.argtypes = [ctypes.POINTER(StepDesc), vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.twomamba_exp_cache_fill.restype = ctypes.c_int
+    lib.twomamba_exp_cache_fill.argtypes = [ctypes.POINTER(ExpCacheDesc), vp, vp, vp, vp, vp, vp, vp]
+    lib.twomamba_exp_step_workspace_size.restype = ctypes.c_int
+    lib.twomamba_exp_step_workspace_size.argtypes = [ctypes.POINTER(ExpCacheDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.twomamba_exp_step.restype = ctypes.c_int
+    lib.twomamba_exp_step.argtypes = [ctypes.POINTER(ExpCacheDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
     if path is None:
         _lib = lib
     return lib
@@ -187,4 +201,74 @@ def step(q, k, v, z, state, norm, *, scale=1.0, no_norm=False, out=None):
                              _ptr(out), _stream())
     if s != 0:
         raise TwoMambaError(s, "twomamba_step")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 2Mamba-E decoding over a key/value cache
+
+def exp_cache(B, H, d, max_len, dtype=torch.bfloat16, device="cuda"):
+    """Empty caches: k [B,H,max_len,d], v [B,H,max_len,d] (dtype), g [B,H,max_len] (fp64)."""
+    kc = torch.empty((B, H, max_len, d), dtype=dtype, device=device)
+    vc = torch.empty((B, H, max_len, d), dtype=dtype, device=device)
+    gc = torch.empty((B, H, max_len), dtype=torch.float64, device=device)
+    return kc, vc, gc
+
+
+def _cache_desc(B, H, dk, dv, max_len, pos, scale, dtype):
+    return ExpCacheDesc(B, H, dk, dv, max_len, pos, scale, _DT[dtype], 0)
+
+
+def exp_cache_fill(k, v, z, k_cache, v_cache, g_cache):
+    """Write a prompt k, v [B,H,T,d], z [B,H,T] into cache positions 0..T-1."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    L = k_cache.shape[2]
+    _check(k, (B, H, T, dk), k.dtype, "k")
+    _check(v, (B, H, T, dv), k.dtype, "v")
+    _check(z, (B, H, T), torch.float32, "z")
+    _check(k_cache, (B, H, L, dk), k.dtype, "k_cache")
+    _check(v_cache, (B, H, L, dv), k.dtype, "v_cache")
+    _check(g_cache, (B, H, L), torch.float64, "g_cache")
+    desc = _cache_desc(B, H, dk, dv, L, T, 1.0, k.dtype)
+    s = load().twomamba_exp_cache_fill(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(z), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(g_cache), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_exp_cache_fill")
+
+
+def exp_step_workspace_size(B, H, d, max_len, pos, dtype=torch.bfloat16) -> int:
+    desc = _cache_desc(B, H, d, d, max_len, pos, 1.0, dtype)
+    n = ctypes.c_size_t(0)
+    s = load().twomamba_exp_step_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_exp_step_workspace_size")
+    return n.value
+
+
+def exp_step(q, k, v, z, k_cache, v_cache, g_cache, pos, *, scale=1.0, out=None, workspace=None):
+    """2Mamba-E decode at position `pos` (caches hold tokens 0..pos-1; row pos is appended)."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    L = k_cache.shape[2]
+    _check(q, (B, H, dk), q.dtype, "q")
+    _check(k, (B, H, dk), q.dtype, "k")
+    _check(v, (B, H, dv), q.dtype, "v")
+    _check(z, (B, H), torch.float32, "z")
+    _check(k_cache, (B, H, L, dk), q.dtype, "k_cache")
+    _check(v_cache, (B, H, L, dv), q.dtype, "v_cache")
+    _check(g_cache, (B, H, L), torch.float64, "g_cache")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    desc = _cache_desc(B, H, dk, dv, L, pos, scale, q.dtype)
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        s = load().twomamba_exp_step_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+        if s != 0:
+            raise TwoMambaError(s, "twomamba_exp_step_workspace_size")
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    s = load().twomamba_exp_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(g_cache), _ptr(out), _ptr(workspace), workspace.numel(), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_exp_step")
     return out

@@ -237,4 +237,88 @@ int twomamba_step(const twomamba_step_desc* d, const void* q, const void* k, con
     return twm::step_launch(a);
 }
 
+// ---------------------------------------------------------------------------
+// 2Mamba-E key/value cache
+static int check_cache(const twomamba_exp_cache_desc* d, bool fill, size_t* kb, size_t* vb, size_t* zb,
+                       size_t* kcb, size_t* vcb, size_t* gcb) {
+    if (!d) return TWOMAMBA_ERR_NULL;
+    if (d->B < 0 || d->H < 0 || d->dk <= 0 || d->dv <= 0 || d->max_len < 0 || d->pos < 0) return TWOMAMBA_ERR_SHAPE;
+    if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
+    if (d->flags != 0u) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (!supported_dims(d->dk, d->dv)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (!(d->scale == d->scale) || d->scale == __builtin_inff() || d->scale == -__builtin_inff())
+        return TWOMAMBA_ERR_SHAPE;
+    if (fill ? d->pos > d->max_len : d->pos >= d->max_len) return TWOMAMBA_ERR_SHAPE;
+    const size_t es = d->dtype == TWOMAMBA_BF16 ? 2 : 4;
+    const size_t B = d->B, H = d->H, L = d->max_len, T = fill ? (size_t)d->pos : 1;
+    if (!prod(kb, {B, H, T, (size_t)d->dk, es}) || !prod(vb, {B, H, T, (size_t)d->dv, es}) ||
+        !prod(zb, {B, H, T, 4}) || !prod(kcb, {B, H, L, (size_t)d->dk, es}) ||
+        !prod(vcb, {B, H, L, (size_t)d->dv, es}) || !prod(gcb, {B, H, L, 8}))
+        return TWOMAMBA_ERR_SHAPE;
+    // grid: (B*H) * splits of 512 keys must fit a 31-bit grid
+    size_t g;
+    if (!prod(&g, {B, H, ((size_t)d->pos + 512) / 512}) || g > 0x7fffffffu) return TWOMAMBA_ERR_SHAPE;
+    return TWOMAMBA_OK;
+}
+
+static twm::ExpCacheArgs cache_args(const twomamba_exp_cache_desc* d) {
+    twm::ExpCacheArgs a;
+    memset(&a, 0, sizeof(a));
+    a.B = d->B; a.H = d->H; a.dk = d->dk; a.dv = d->dv; a.max_len = d->max_len; a.pos = d->pos;
+    a.scale = d->scale; a.dtype = d->dtype;
+    return a;
+}
+
+int twomamba_exp_cache_fill(const twomamba_exp_cache_desc* d, const void* k, const void* v, const float* z,
+                            void* k_cache, void* v_cache, double* g_cache, void* stream) {
+    size_t kb, vb, zb, kcb, vcb, gcb;
+    int s = check_cache(d, true, &kb, &vb, &zb, &kcb, &vcb, &gcb);
+    if (s != TWOMAMBA_OK) return s;
+    if ((size_t)d->B * d->H == 0 || d->pos == 0) return TWOMAMBA_OK;
+    if (!k || !v || !z || !k_cache || !v_cache || !g_cache) return TWOMAMBA_ERR_NULL;
+    const Range rk = rng(k, kb), rv = rng(v, vb), rz = rng(z, zb);
+    const Range rkc = rng(k_cache, kcb), rvc = rng(v_cache, vcb), rgc = rng(g_cache, gcb);
+    for (const Range& w : {rkc, rvc, rgc})
+        for (const Range& in : {rk, rv, rz})
+            if (overlaps(w, in)) return TWOMAMBA_ERR_ALIAS;
+    if (overlaps(rkc, rvc) || overlaps(rkc, rgc) || overlaps(rvc, rgc)) return TWOMAMBA_ERR_ALIAS;
+    twm::ExpCacheArgs a = cache_args(d);
+    a.k = k; a.v = v; a.z = z; a.k_cache = k_cache; a.v_cache = v_cache; a.g_cache = g_cache; a.stream = stream;
+    return twm::exp_cache_fill_launch(a);
+}
+
+int twomamba_exp_step_workspace_size(const twomamba_exp_cache_desc* d, size_t* bytes) {
+    if (!bytes) return TWOMAMBA_ERR_NULL;
+    size_t kb, vb, zb, kcb, vcb, gcb;
+    int s = check_cache(d, false, &kb, &vb, &zb, &kcb, &vcb, &gcb);
+    if (s != TWOMAMBA_OK) return s;
+    *bytes = twm::exp_step_workspace(cache_args(d));
+    return TWOMAMBA_OK;
+}
+
+int twomamba_exp_step(const twomamba_exp_cache_desc* d, const void* q, const void* k, const void* v,
+                      const float* z, void* k_cache, void* v_cache, double* g_cache, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    size_t kb, vb, zb, kcb, vcb, gcb;
+    int s = check_cache(d, false, &kb, &vb, &zb, &kcb, &vcb, &gcb);
+    if (s != TWOMAMBA_OK) return s;
+    if ((size_t)d->B * d->H == 0) return TWOMAMBA_OK;
+    if (!q || !k || !v || !z || !k_cache || !v_cache || !g_cache || !out) return TWOMAMBA_ERR_NULL;
+    twm::ExpCacheArgs a = cache_args(d);
+    const size_t need = twm::exp_step_workspace(a);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
+    const Range rq = rng(q, kb), rk = rng(k, kb), rv = rng(v, vb), rz = rng(z, zb), ro = rng(out, vb);
+    const Range rkc = rng(k_cache, kcb), rvc = rng(v_cache, vcb), rgc = rng(g_cache, gcb), rws = rng(workspace, need);
+    for (const Range& w : {rkc, rvc, rgc, ro, rws})
+        for (const Range& in : {rq, rk, rv, rz})
+            if (overlaps(w, in)) return TWOMAMBA_ERR_ALIAS;
+    const Range outs[] = {rkc, rvc, rgc, ro, rws};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i], outs[j])) return TWOMAMBA_ERR_ALIAS;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.k_cache = k_cache; a.v_cache = v_cache; a.g_cache = g_cache; a.out = out;
+    a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
+    return twm::exp_step_launch(a);
+}
+
 }  // extern "C"

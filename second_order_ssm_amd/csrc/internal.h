@@ -77,4 +77,22 @@ int mfma_exp_fwd(const FwdArgs& a);
 // ---- decode step -------------------------------------------------------------
 int step_launch(const StepArgs& a);
 
+// 2Mamba-E decoding over a key/value cache (exp_step.hip)
+struct ExpCacheArgs {
+    int B, H, dk, dv, max_len, pos;
+    float scale;
+    int dtype;
+    const void *q, *k, *v;
+    const float* z;
+    void *k_cache, *v_cache;
+    double* g_cache;
+    void* out;
+    void* ws;
+    size_t ws_bytes;
+    void* stream;
+};
+size_t exp_step_workspace(const ExpCacheArgs& a);
+int exp_step_launch(const ExpCacheArgs& a);
+int exp_cache_fill_launch(const ExpCacheArgs& a);
+
 }  // namespace twm

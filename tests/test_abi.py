@@ -163,3 +163,59 @@ def test_step_null_and_alias(lib):
     assert call_step(lib, d, n=5) == EALIAS
     assert call_step(lib, tmb.StepDesc(B=0, H=2, dk=64, dv=64, scale=1.0, dtype=1, flags=0),
                      q=None, k=None, v=None, z=None, s=None, n=None, out=None) == OK
+
+
+# ---------------------------------------------------------------------------
+# 2Mamba-E key/value cache entry points
+
+def cdesc(B=2, H=3, d=64, max_len=100, pos=10, dtype=1, scale=1.0, flags=0):
+    return tmb.ExpCacheDesc(B, H, d, d, max_len, pos, scale, dtype, flags)
+
+
+def exp_step_call(lib, d, ws_bytes=1 << 20, **ptrs):
+    p = {n: fake(i) for i, n in enumerate(["q", "k", "v", "z", "kc", "vc", "gc", "out", "ws"])}
+    p.update(ptrs)
+    return lib.twomamba_exp_step(ctypes.byref(d), p["q"], p["k"], p["v"], p["z"], p["kc"], p["vc"], p["gc"],
+                                 p["out"], p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=100), ESHAPE),            # pos must be < max_len
+    (dict(pos=-1), ESHAPE),
+    (dict(max_len=-1), ESHAPE),
+    (dict(dtype=5), EDTYPE),
+    (dict(flags=1), EUNSUP),
+    (dict(d=32), EUNSUP),
+    (dict(scale=float("nan")), ESHAPE),
+])
+def test_exp_step_bad_descriptor(lib, kw, status):
+    assert exp_step_call(lib, cdesc(**kw)) == status
+
+
+def test_exp_step_workspace_and_pointers(lib):
+    n = ctypes.c_size_t(0)
+    d = cdesc(B=2, H=16, max_len=8192, pos=8191)
+    assert lib.twomamba_exp_step_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert n.value == 32 * 16 * 66 * 4          # 16 splits of 512 keys, (dv + 2) floats each
+    assert exp_step_call(lib, d, ws_bytes=n.value - 1) == EWS
+    assert exp_step_call(lib, d, ws=None) == EWS
+    assert exp_step_call(lib, d, ws=ctypes.c_void_p(BASE + 8 * GAP + 16)) == EWS   # misaligned
+    assert exp_step_call(lib, d, q=None) == ENULL
+    assert exp_step_call(lib, d, gc=None) == ENULL
+    assert exp_step_call(lib, d, out=fake(0)) == EALIAS     # out over q
+    assert exp_step_call(lib, d, vc=fake(4)) == EALIAS      # v cache over k cache
+    assert lib.twomamba_exp_step_workspace_size(ctypes.byref(d), None) == ENULL
+    empty = cdesc(B=0)
+    assert exp_step_call(lib, empty, q=None, ws=None) == OK
+
+
+def test_exp_cache_fill_validation(lib):
+    def call(d, **ptrs):
+        p = {n: fake(i) for i, n in enumerate(["k", "v", "z", "kc", "vc", "gc"])}
+        p.update(ptrs)
+        return lib.twomamba_exp_cache_fill(ctypes.byref(d), p["k"], p["v"], p["z"], p["kc"], p["vc"], p["gc"], None)
+    assert call(cdesc(pos=101)) == ESHAPE        # T > max_len
+    assert call(cdesc(pos=10, flags=2)) == EUNSUP
+    assert call(cdesc(pos=10), z=None) == ENULL
+    assert call(cdesc(pos=10), kc=fake(1)) == EALIAS
+    assert call(cdesc(pos=0), k=None) == OK      # nothing to fill
