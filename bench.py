@@ -1,6 +1,6 @@
 """Benchmark of the 2Mamba operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs sq,exp,step] [--cpu-seconds S]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs sq,exp,step,exp_step] [--cpu-seconds S]
 
 A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
 chunk state, inter-chunk scan, readout, normalisation) over one batch of the
@@ -9,7 +9,9 @@ synthetic data.  ``value`` is its whole-job throughput in head-tokens/s with
 all inputs resident in HBM.  The same run also measures, each in its own timed
 loop, the 2Mamba-E forward on the same shape and the recurrent decode step
 (batch 64, 32 heads, fp32 packed state of 1.09 GB, 256 sequential steps after
-a T=2048 prefill); they are reported under ``legs``.
+a T=2048 prefill) and the 2Mamba-E decode over a bf16 key/value cache (batch
+64, 32 heads, 256 sequential steps after a 2048-token prompt); they are
+reported under ``legs``.
 
 The roofline entry is for the dominant kernel of the timed step: algorithmic
 work attributed to that kernel per launch divided by its average duration,
@@ -38,6 +40,7 @@ PEAK_HBM = 8.0e12               # MI355X HBM3E bytes/s
 SQ_SHAPE = dict(B=2, H=16, T=8192, d=64, seed=3)
 EXP_SHAPE = dict(B=2, H=16, T=8192, d=64, seed=3)
 STEP_SHAPE = dict(B=64, H=32, d=64, prefill_T=2048, prefill_seed=4, steps=256)
+EXP_STEP_SHAPE = dict(B=64, H=32, d=64, prompt_T=2048, seed=4, steps=256)
 
 
 def sq_flops_per_head_token(d=64, dv=64, c0=64):
@@ -58,6 +61,14 @@ def step_bytes_per_head(d=64, dv=64):
     return 2 * (D * dv + D) * 4 + (3 * d + 1) * 4 + dv * 4
 
 
+def exp_step_bytes_per_head(pos, d=64, dv=64, esize=2):
+    """2Mamba-E decode step at position `pos`: read the pos cached key/value rows
+    and their fp64 running decay sums, append row pos, read q, k, v (input dtype)
+    and z (fp32), write the output row."""
+    row = (d + dv) * esize + 8
+    return pos * row + row + (2 * d + dv) * esize + 4 + dv * esize
+
+
 def kernel_work(name, leg_work):
     """Algorithmic work credited to the dominant kernel per launch: the whole
     leg's work, since each forward kernel executes every algorithmic step of its
@@ -66,7 +77,8 @@ def kernel_work(name, leg_work):
     return leg_work
 
 
-KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "step_kernel": "step.hip"}
+KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "step_kernel": "step.hip",
+                  "exp_decode_partial": "exp_step.hip", "exp_decode_combine": "exp_step.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -95,6 +107,12 @@ def measured_traffic(kernel):
             if kv.get("kernel") == kernel and kv.get("src_sha256") == want:
                 return float(kv["traffic_bytes"])
     return None
+
+
+def traffic_sum(*kernels):
+    """Summed counter traffic of kernels that together make one step, or None if any is missing."""
+    t = [measured_traffic(k) for k in kernels]
+    return None if any(x is None for x in t) else sum(t)
 
 
 def time_loop(fn, steps, warmup):
@@ -199,6 +217,50 @@ def leg_step(warmup):
                               unit="GB/s", frac=bw / PEAK_HBM, traffic=measured_traffic("step_kernel")))
 
 
+def leg_exp_step(warmup):
+    """2Mamba-E decode over a key/value cache: a bf16 prompt of 2048 tokens goes
+    into the caches (untimed), `warmup` untimed steps, then 256 timed sequential
+    steps, each attending over every cached position (split over 512-key blocks,
+    then one combine launch)."""
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    shp = EXP_STEP_SHAPE
+    B, H, d, T0, nsteps = shp["B"], shp["H"], shp["d"], shp["prompt_T"], shp["steps"]
+    L = T0 + warmup + nsteps
+    kc, vc, gc = tmb.exp_cache(B, H, d, L, dtype=torch.bfloat16)
+    _, k, v, z = SI.draw(B, H, T0, d, seed=shp["seed"], dtype="bf16")
+    k, v, z = k.cuda(), v.cuda(), z.cuda()
+    tmb.exp_cache_fill(k, v, z, kc, vc, gc)
+    del k, v, z
+    torch.cuda.synchronize()
+    qs, ks, vs, zs = (t.cuda() for t in SI.draw(B, H, warmup + nsteps, d, seed=shp["seed"] + 100, dtype="bf16"))
+    steps_in = [tuple(x[:, :, i].contiguous() for x in (qs, ks, vs, zs)) for i in range(warmup + nsteps)]
+    out = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(tmb.exp_step_workspace_size(B, H, d, L, L - 1), dtype=torch.uint8, device="cuda")
+    for i in range(warmup):
+        tmb.exp_step(*steps_in[i], kc, vc, gc, T0 + i, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(warmup, warmup + nsteps):
+        tmb.exp_step(*steps_in[i], kc, vc, gc, T0 + i, out=out, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / nsteps
+    byts = B * H * sum(exp_step_bytes_per_head(T0 + i, d, d) for i in range(warmup, warmup + nsteps)) / nsteps
+    bw = byts / (ms * 1e-3)
+    return dict(workload=f"2Mamba-E decode B={B} H={H} d={d} bf16 key/value cache, positions "
+                         f"{T0 + warmup}..{T0 + warmup + nsteps - 1}",
+                ms=ms, bytes_per_step=byts,
+                roofline=dict(bound="hbm", kernel="exp_decode_partial+exp_decode_combine", achieved=bw / 1e9,
+                              peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM,
+                              traffic=traffic_sum("exp_decode_partial", "exp_decode_combine")))
+
+
 def cpu_baseline(seconds):
     """fp64 oracle (packed recurrent form, all 32 heads of the 2Mamba workload at
     once) over the first n tokens, n sized to about `seconds` of CPU work."""
@@ -264,7 +326,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sq,exp,step")
+    ap.add_argument("--legs", default="sq,exp,step,exp_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the copy / GEMM ceiling measurements")
@@ -292,6 +354,9 @@ def main():
     if "step" in legs:
         res["step"] = leg_step(args.warmup)
         print(f"[bench] step leg done: {res['step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    if "exp_step" in legs:
+        res["exp_step"] = leg_exp_step(args.warmup)
+        print(f"[bench] exp_step leg done: {res['exp_step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)
     peaks = achievable_peaks() if args.peaks else None
     if peaks:
         for leg in res.values():
