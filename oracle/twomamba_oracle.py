@@ -53,6 +53,7 @@ __all__ = [
     "fwd_recurrent_full", "fwd_recurrent_packed", "step",
     "fwd_exp_quadratic", "fwd_exp_quadratic_rows", "fwd_exp_streaming",
     "state_elements", "memory_crossover_tokens",
+    "sigmoid", "bwd_quadratic", "bwd_exp_quadratic",
 ]
 
 
@@ -362,3 +363,93 @@ def state_elements(d: int, dv: int | None = None, conv_window: int = 2) -> int:
 def memory_crossover_tokens(d: int, dv: int | None = None, conv_window: int = 2) -> float:
     """Sequence length above which the fixed state is smaller than a 2*N*dh KV cache."""
     return state_elements(d, dv, conv_window) / (2.0 * d)
+
+
+# ----------------------------------------------------------------------------
+# gradients  [2M2F App. C: each attention kernel is differentiated with Q, K, V
+# as its inputs and the post-attention outputs as its outputs; C.1: the A-mask
+# gradient is a sum of the masked matrix over the key axis and the query axis]
+#
+# Both functions return the gradients of  sum_t dout_t . o_t  with respect to
+# q, k, v and the decay logits z, row by row over the quadratic form (A) or
+# (E-A).  The A-mask enters through lambda_ts = g_{s+1} + ... + g_t, so an
+# entry (t, s) of dL/dlambda reaches every g_r with s < r <= t; g = -softplus(z)
+# gives dz = -sigmoid(z) dg.
+# ----------------------------------------------------------------------------
+
+def sigmoid(x):
+    """Logistic function 1 / (1 + e^-x) without overflow; sigmoid(-inf) = 0."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def _add_mask_grad(dg, dlam, t):
+    """dg_r += sum_{s<r} dlam_s for r = 1..t (dlam over s = 0..t of row t)."""
+    if t > 0:
+        dg[..., 1:t + 1] += np.cumsum(dlam[..., :t], axis=-1)
+
+
+def bwd_quadratic(q, k, v, z, dout, scale=1.0, norm=True):
+    """Gradients (dq, dk, dv, dz) of the 2Mamba output, form (A), no initial state.
+
+    Row t: a_s = scale q_t.k_s, w_s = L_ts a_s^2, num = sum w_s v_s,
+    den = sum w_s, o_t = num / den.  With dnum = dout_t / den and
+    dden = -dout_t.o_t / den:  dL/dw_s = dnum.v_s + dden, dv_s += w_s dnum,
+    dL/da_s = dL/dw_s * 2 L_ts a_s, dq_t += scale sum_s dL/da_s k_s,
+    dk_s += scale dL/da_s q_t and dL/dlambda_ts = dL/dw_s * w_s.  A row whose
+    den is 0 has o_t = 0 by definition and passes no gradient.  Without
+    normalisation o_t = num, dnum = dout_t and dden = 0.
+    """
+    g = decay_log(z)
+    T = q.shape[2]
+    dq, dk, dv, dg = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape), np.zeros(z.shape)
+    for t in range(T):
+        K, V = k[:, :, :t + 1], v[:, :, :t + 1]
+        L = np.exp(_row_log_mask(g[:, :, :t + 1]))
+        a = scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], K)
+        w = L * a * a
+        do = dout[:, :, t]
+        if norm:
+            den = w.sum(axis=-1)
+            rden = np.where(den > 0, 1.0 / np.where(den > 0, den, 1.0), 0.0)
+            o = np.einsum("bhs,bhsc->bhc", w, V) * rden[..., None]
+            dnum = do * rden[..., None]
+            dden = -(do * o).sum(axis=-1) * rden
+        else:
+            dnum = do
+            dden = np.zeros(w.shape[:-1])
+        dw = np.einsum("bhsc,bhc->bhs", V, dnum) + dden[..., None]
+        dv[:, :, :t + 1] += w[..., None] * dnum[:, :, None, :]
+        da = dw * L * 2.0 * a
+        dq[:, :, t] += scale * np.einsum("bhs,bhsd->bhd", da, K)
+        dk[:, :, :t + 1] += scale * da[..., None] * q[:, :, t][:, :, None, :]
+        _add_mask_grad(dg, dw * w, t)
+    return dq, dk, dv, -sigmoid(z) * dg
+
+
+def bwd_exp_quadratic(q, k, v, z, dout, scale=1.0):
+    """Gradients (dq, dk, dv, dz) of the 2Mamba-E output, form (E-A).
+
+    Row t: p = softmax_s(scale q_t.k_s + lambda_ts), o_t = sum p_s v_s.
+    dp_s = dout_t.v_s, dL/dlogit_s = p_s (dp_s - dout_t.o_t), dv_s += p_s dout_t,
+    dq_t += scale sum_s dL/dlogit_s k_s, dk_s += scale dL/dlogit_s q_t, and
+    dL/dlambda_ts = dL/dlogit_s.
+    """
+    g = decay_log(z)
+    T = q.shape[2]
+    dq, dk, dv, dg = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape), np.zeros(z.shape)
+    for t in range(T):
+        K, V = k[:, :, :t + 1], v[:, :, :t + 1]
+        logit = scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], K) + _row_log_mask(g[:, :, :t + 1])
+        p = np.exp(logit - logit.max(axis=-1, keepdims=True))
+        p /= p.sum(axis=-1, keepdims=True)
+        do = dout[:, :, t]
+        o = np.einsum("bhs,bhsc->bhc", p, V)
+        dp = np.einsum("bhsc,bhc->bhs", V, do)
+        dl = p * (dp - (do * o).sum(axis=-1)[..., None])
+        dv[:, :, :t + 1] += p[..., None] * do[:, :, None, :]
+        dq[:, :, t] += scale * np.einsum("bhs,bhsd->bhd", dl, K)
+        dk[:, :, :t + 1] += scale * dl[..., None] * q[:, :, t][:, :, None, :]
+        _add_mask_grad(dg, dl, t)
+    return dq, dk, dv, -sigmoid(z) * dg
