@@ -234,6 +234,40 @@ int twomamba_exp_step(const twomamba_exp_cache_desc* desc,
                       void* k_cache, void* v_cache, double* g_cache,
                       void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Backward pass of twomamba_fwd  [2M2F App. C: the gradients of each attention
+ * kernel, with Q, K, V as inputs and the post-attention outputs as outputs;
+ * C.1: the A-mask gradient is built from sums of the masked matrix along the
+ * key axis and along the query axis].
+ *
+ * Given dout = dL/dout for out = twomamba_fwd(q, k, v, z) (no initial state),
+ * writes dq, dk, dv (= dL/dq, dL/dk, dL/dv) and dz = dL/dz, the decay logits'
+ * gradient (g = -softplus(z), so dz = -sigmoid(z) dL/dg).  The same descriptor
+ * as the forward: variant, dtype, scale and TWOMAMBA_FLAG_NO_NORM (2Mamba only)
+ * select the operator; desc->chunk is ignored (0 or a forward chunk size).  A
+ * 2Mamba row whose weight sum is 0 has o_t = 0 and passes no gradient.
+ *
+ *   q, k      [B][H][T][dk]  dtype   device
+ *   v         [B][H][T][dv]  dtype   device
+ *   z         [B][H][T]      fp32    device
+ *   out       [B][H][T][dv]  dtype   device   the forward's output for these inputs
+ *                                             (only dout_t . out_t is used)
+ *   dout      [B][H][T][dv]  dtype   device
+ *   dq, dk    [B][H][T][dk]  dtype   device   written
+ *   dv        [B][H][T][dv]  dtype   device   written
+ *   dz        [B][H][T]      fp32    device   written
+ *   workspace                        device   >= twomamba_bwd_workspace_size bytes,
+ *                                             256-byte aligned; contents undefined after
+ * No output may overlap an input, another output or the workspace.
+ */
+int twomamba_bwd_workspace_size(const twomamba_fwd_desc* desc, size_t* bytes);
+
+int twomamba_bwd(const twomamba_fwd_desc* desc,
+                 const void* q, const void* k, const void* v, const float* z,
+                 const void* out, const void* dout,
+                 void* dq, void* dk, void* dv, float* dz,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

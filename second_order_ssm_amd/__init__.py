@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "step", "library_path",
-           "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step",
+           "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd",
            "TwoMambaError", "SQ", "EXP", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "num_pairs"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -90,9 +90,22 @@ def load(path: str | None = None):
     lib.twomamba_exp_step.restype = ctypes.c_int
     lib.twomamba_exp_step.argtypes = [ctypes.POINTER(ExpCacheDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
+    lib.twomamba_bwd_workspace_size.restype = ctypes.c_int
+    lib.twomamba_bwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.twomamba_bwd.restype = ctypes.c_int
+    lib.twomamba_bwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
     if path is None:
         _lib = lib
     return lib
+
+
+def bwd_workspace_size(desc: FwdDesc) -> int:
+    n = ctypes.c_size_t(0)
+    s = load().twomamba_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_bwd_workspace_size")
+    return n.value
 
 
 def abi_version() -> int:
@@ -272,3 +285,38 @@ def exp_step(q, k, v, z, k_cache, v_cache, g_cache, pos, *, scale=1.0, out=None,
     if s != 0:
         raise TwoMambaError(s, "twomamba_exp_step")
     return out
+
+
+def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, reference_kernels=False,
+        grads=None, workspace=None):
+    """Backward of fwd (no initial state): returns (dq, dk, dv, dz).
+
+    ``out`` is the forward output for the same inputs; ``grads`` may supply the
+    four output tensors.
+    """
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    flags = (FLAG_NO_NORM if no_norm else 0) | (FLAG_REFERENCE_KERNELS if reference_kernels else 0)
+    desc = make_desc(B, H, T, dk, dv, variant=variant, dtype=q.dtype, scale=scale, flags=flags)
+    _check(q, (B, H, T, dk), q.dtype, "q")
+    _check(k, (B, H, T, dk), q.dtype, "k")
+    _check(v, (B, H, T, dv), q.dtype, "v")
+    _check(z, (B, H, T), torch.float32, "z")
+    _check(out, (B, H, T, dv), q.dtype, "out")
+    _check(dout, (B, H, T, dv), q.dtype, "dout")
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z))
+    gq, gk, gv, gz = grads
+    _check(gq, (B, H, T, dk), q.dtype, "dq")
+    _check(gk, (B, H, T, dk), q.dtype, "dk")
+    _check(gv, (B, H, T, dv), q.dtype, "dv")
+    _check(gz, (B, H, T), torch.float32, "dz")
+    nbytes = bwd_workspace_size(desc)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    s = load().twomamba_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(out), _ptr(dout),
+                            _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gz), _ptr(workspace), ctypes.c_size_t(nbytes),
+                            _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_bwd")
+    return gq, gk, gv, gz

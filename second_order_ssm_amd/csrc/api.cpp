@@ -321,4 +321,60 @@ int twomamba_exp_step(const twomamba_exp_cache_desc* d, const void* q, const voi
     return twm::exp_step_launch(a);
 }
 
+// ---------------------------------------------------------------------------
+// backward
+static int check_bwd(const twomamba_fwd_desc* d, size_t* qkb, size_t* vb, size_t* zb) {
+    size_t sb, nb;
+    int s = check_desc(d, qkb, vb, zb, &sb, &nb);
+    if (s != TWOMAMBA_OK) return s;
+    size_t g;
+    if (!prod(&g, {(size_t)d->B, (size_t)d->H, ((size_t)d->T + 63) / 64}) || g > 0x7fffffffu)
+        return TWOMAMBA_ERR_SHAPE;
+    if ((size_t)d->B * d->H > 0x7fffffffu) return TWOMAMBA_ERR_SHAPE;
+    return TWOMAMBA_OK;
+}
+
+static twm::BwdArgs bwd_args(const twomamba_fwd_desc* d) {
+    twm::BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.B = d->B; a.H = d->H; a.T = d->T; a.dk = d->dk; a.dv = d->dv;
+    a.scale = d->scale; a.variant = d->variant; a.dtype = d->dtype; a.flags = d->flags;
+    return a;
+}
+
+int twomamba_bwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
+    if (!bytes) return TWOMAMBA_ERR_NULL;
+    *bytes = 0;
+    size_t qkb, vb, zb;
+    int s = check_bwd(d, &qkb, &vb, &zb);
+    if (s != TWOMAMBA_OK) return s;
+    *bytes = twm::bwd_workspace(bwd_args(d));
+    return TWOMAMBA_OK;
+}
+
+int twomamba_bwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                 const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    size_t qkb, vb, zb;
+    int s = check_bwd(d, &qkb, &vb, &zb);
+    if (s != TWOMAMBA_OK) return s;
+    if (qkb == 0) return TWOMAMBA_OK;
+    if (!q || !k || !v || !z || !out || !dout || !dq || !dk || !dv || !dz) return TWOMAMBA_ERR_NULL;
+    twm::BwdArgs a = bwd_args(d);
+    const size_t need = twm::bwd_workspace(a);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
+    const Range ins[] = {rng(q, qkb), rng(k, qkb), rng(v, vb), rng(z, zb), rng(out, vb), rng(dout, vb)};
+    const Range outs[] = {rng(dq, qkb), rng(dk, qkb), rng(dv, vb), rng(dz, zb), rng(workspace, need)};
+    for (const Range& o : outs)
+        for (const Range& in : ins)
+            if (overlaps(o, in)) return TWOMAMBA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i], outs[j])) return TWOMAMBA_ERR_ALIAS;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.out = out; a.dout = dout;
+    a.gq = dq; a.gk = dk; a.gv = dv; a.gz = dz;
+    a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
+    return twm::ref_bwd(a);
+}
+
 }  // extern "C"

@@ -1,0 +1,372 @@
+// Reference (plain fp32 VALU) kernels of the 2Mamba / 2Mamba-E backward pass
+// ("2Mamba2Furious", App. C: gradients of the attention kernels with Q, K, V as
+// inputs and the post-attention outputs as outputs; C.1: the A-mask gradient
+// sums the masked matrix along the key axis and along the query axis).
+//
+// Per head, with G_t = softplus(z_0) + ... + softplus(z_t) (fp64), the log-mask
+// of a pair s <= t is lambda_ts = G_s - G_t.  For a pair, x = scale q_t.k_s and
+// dP = dout_t.v_s; with the row statistics of the query (1/den_t or the
+// log-sum-exp) and D_t = dout_t.o_t:
+//   2Mamba:   w = e^lambda x^2, P = w / den_t, dw = (dP - D_t) / den_t,
+//             dS = 2 e^lambda x dw (the derivative by q_t.k_s / scale), M = dw w
+//             (without normalisation: 1/den_t = 1 and D_t = 0);
+//   2Mamba-E: P = exp(x + lambda - lse_t), dS = P (dP - D_t), M = dS.
+// Then dv_s = sum_t P dout_t, dq_t = scale sum_s dS k_s, dk_s = scale sum_t dS q_t,
+// and M (the gradient by lambda_ts) reaches g_r for s < r <= t:
+//   dg_r = sum_{t >= r, s < r} M_ts = sum_{r' < r} (colsum_r' - rowsum_r'),
+// rowsum_t = sum_{s<t} M_ts, colsum_s = sum_{t>s} M_ts; dz = -sigmoid(z) dg.
+//
+//  * bwd_prep_kernel: G and D_t (one workgroup per head).
+//  * bwd_ref_q_kernel: one thread per query; a pass over the keys for the row
+//    statistic, a second one for dq and rowsum.
+//  * bwd_ref_kv_kernel: two threads per key (half of the dims each); a pass
+//    over the queries t >= s for dk, dv and colsum.
+//  * bwd_dz_kernel: the scan of colsum - rowsum and dz (one workgroup per head).
+#include "device_common.h"
+#include "internal.h"
+
+namespace twm {
+namespace {
+
+constexpr int kTile = 64;
+
+__device__ __forceinline__ double softplus_d(float zf) {
+    const double z = zf;
+    return fmax(z, 0.0) + log1p(exp(-fabs(z)));
+}
+
+__device__ __forceinline__ float sigmoid_f(float x) {
+    const float e = expf(-fabsf(x));
+    return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+
+// G (running fp64 softplus sums) and D_t = dout_t . out_t (0 without normalisation)
+template <int DV, typename In>
+__global__ void __launch_bounds__(256)
+bwd_prep_kernel(const float* __restrict__ z, const In* __restrict__ out, const In* __restrict__ dout,
+                double* __restrict__ G, float* __restrict__ Dt, int T, int use_d) {
+    __shared__ double s_tot[256];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const size_t base = (size_t)bh * T;
+    const int run = (T + 255) / 256;
+    const int t0 = min(T, tid * run), t1 = min(T, t0 + run);
+    double acc = 0.0;
+    for (int t = t0; t < t1; ++t) acc += softplus_d(z[base + t]);
+    s_tot[tid] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double r = 0.0;
+        for (int i = 0; i < 256; ++i) {
+            const double x = s_tot[i];
+            s_tot[i] = r;
+            r += x;
+        }
+    }
+    __syncthreads();
+    double g = s_tot[tid];
+    for (int t = t0; t < t1; ++t) {
+        g += softplus_d(z[base + t]);
+        G[base + t] = g;
+    }
+    for (int t = tid; t < T; t += 256) {
+        float d = 0.f;
+        if (use_d)
+            for (int c = 0; c < DV; ++c) d = fmaf(IO<In>::ld(dout, (base + t) * DV + c), IO<In>::ld(out, (base + t) * DV + c), d);
+        Dt[base + t] = d;
+    }
+}
+
+// one thread per query row
+template <int D, typename In, bool kExp>
+__global__ void __launch_bounds__(kTile)
+bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+                 const In* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
+                 float* __restrict__ stat, float* __restrict__ rowsum, In* __restrict__ dq, int T, int nqt,
+                 float scale, int norm) {
+    __shared__ float s_k[kTile][D], s_v[kTile][D];
+    __shared__ double s_g[kTile];
+    const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+    const int tid = threadIdx.x;
+    const size_t base = (size_t)bh * T;
+    const int t = qt * kTile + tid;
+    const bool active = t < T;
+    float qv[D], dov[D], dqv[D];
+    double Gt = 0.0;
+    float Dq = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        qv[i] = active ? IO<In>::ld(q, (base + t) * D + i) : 0.f;
+        dov[i] = active ? IO<In>::ld(dout, (base + t) * D + i) : 0.f;
+        dqv[i] = 0.f;
+    }
+    if (active) {
+        Gt = G[base + t];
+        Dq = Dt[base + t];
+    }
+
+    auto stage = [&](int kt) {
+        const int s0 = kt * kTile, Lk = min(kTile, T - s0);
+        __syncthreads();
+        for (int e = tid; e < Lk * D; e += kTile) {
+            s_k[e / D][e % D] = IO<In>::ld(k, (base + s0) * D + e);
+            s_v[e / D][e % D] = IO<In>::ld(v, (base + s0) * D + e);
+        }
+        if (tid < Lk) s_g[tid] = G[base + s0 + tid];
+        __syncthreads();
+        return Lk;
+    };
+
+    // pass 1: row statistic
+    float den = 0.f, m = -INFINITY, l = 0.f;
+    for (int kt = 0; kt <= qt; ++kt) {
+        const int Lk = stage(kt);
+        const int s0 = kt * kTile;
+        if (!active) continue;
+        for (int sl = 0; sl < Lk && s0 + sl <= t; ++sl) {
+            float x = 0.f;
+#pragma unroll
+            for (int i = 0; i < D; ++i) x = fmaf(qv[i], s_k[sl][i], x);
+            x *= scale;
+            const float lam = (float)(s_g[sl] - Gt);
+            if (kExp) {
+                const float y = x + lam;
+                const float mn = fmaxf(m, y);
+                l = l * expf(m - mn) + expf(y - mn);
+                m = mn;
+            } else {
+                den = fmaf(expf(lam) * x, x, den);
+            }
+        }
+    }
+    float st;
+    if (kExp) st = m + logf(l);
+    else st = norm ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
+
+    // pass 2: dq and rowsum
+    float rs = 0.f;
+    for (int kt = 0; kt <= qt; ++kt) {
+        const int Lk = stage(kt);
+        const int s0 = kt * kTile;
+        if (!active) continue;
+        for (int sl = 0; sl < Lk && s0 + sl <= t; ++sl) {
+            float x = 0.f, dp = 0.f;
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                x = fmaf(qv[i], s_k[sl][i], x);
+                dp = fmaf(dov[i], s_v[sl][i], dp);
+            }
+            x *= scale;
+            const float lam = (float)(s_g[sl] - Gt);
+            float ds, Mv;
+            if (kExp) {
+                const float p = expf(x + lam - st);
+                ds = p * (dp - Dq);
+                Mv = ds;
+            } else {
+                const float L = expf(lam);
+                const float dw = (dp - Dq) * st;
+                ds = 2.f * L * x * dw;
+                Mv = dw * L * x * x;
+            }
+            if (s0 + sl < t) rs += Mv;
+            const float c = scale * ds;
+#pragma unroll
+            for (int i = 0; i < D; ++i) dqv[i] = fmaf(c, s_k[sl][i], dqv[i]);
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) IO<In>::st(dq, (base + t) * D + i, dqv[i]);
+        stat[base + t] = st;
+        rowsum[base + t] = rs;
+    }
+}
+
+// two threads per key: thread 2j+h holds dims [h D/2, (h+1) D/2) of key j
+template <int D, typename In, bool kExp>
+__global__ void __launch_bounds__(2 * kTile)
+bwd_ref_kv_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+                  const In* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
+                  const float* __restrict__ stat, float* __restrict__ colsum, In* __restrict__ dk,
+                  In* __restrict__ dv, int T, int nkt, float scale) {
+    constexpr int DH = D / 2;
+    __shared__ float s_q[kTile][D], s_do[kTile][D];
+    __shared__ float s_st[kTile], s_D[kTile];
+    __shared__ double s_g[kTile];
+    const int bh = blockIdx.x / nkt, kt = blockIdx.x % nkt;
+    const int tid = threadIdx.x, j = tid >> 1, h = tid & 1;
+    const size_t base = (size_t)bh * T;
+    const int s = kt * kTile + j;
+    const bool active = s < T;
+    float kv[DH], vv[DH], dkv[DH], dvv[DH];
+#pragma unroll
+    for (int i = 0; i < DH; ++i) {
+        kv[i] = active ? IO<In>::ld(k, (base + s) * D + h * DH + i) : 0.f;
+        vv[i] = active ? IO<In>::ld(v, (base + s) * D + h * DH + i) : 0.f;
+        dkv[i] = dvv[i] = 0.f;
+    }
+    const double Gs = active ? G[base + s] : 0.0;
+    float cs = 0.f;
+    const int nqt = (T + kTile - 1) / kTile;
+    for (int qt = kt; qt < nqt; ++qt) {
+        const int t0 = qt * kTile, Lq = min(kTile, T - t0);
+        __syncthreads();
+        for (int e = tid; e < Lq * D; e += 2 * kTile) {
+            s_q[e / D][e % D] = IO<In>::ld(q, (base + t0) * D + e);
+            s_do[e / D][e % D] = IO<In>::ld(dout, (base + t0) * D + e);
+        }
+        if (tid < Lq) {
+            s_st[tid] = stat[base + t0 + tid];
+            s_D[tid] = Dt[base + t0 + tid];
+            s_g[tid] = G[base + t0 + tid];
+        }
+        __syncthreads();
+        if (!active) continue;
+        for (int tl = 0; tl < Lq; ++tl) {
+            if (t0 + tl < s) continue;   // the same for both threads of a key
+            float xh = 0.f, dph = 0.f;
+#pragma unroll
+            for (int i = 0; i < DH; ++i) {
+                xh = fmaf(s_q[tl][h * DH + i], kv[i], xh);
+                dph = fmaf(s_do[tl][h * DH + i], vv[i], dph);
+            }
+            const float x = scale * (xh + __shfl_xor(xh, 1));
+            const float dp = dph + __shfl_xor(dph, 1);
+            const float lam = (float)(Gs - s_g[tl]);
+            float p, ds, Mv;
+            if (kExp) {
+                p = expf(x + lam - s_st[tl]);
+                ds = p * (dp - s_D[tl]);
+                Mv = ds;
+            } else {
+                const float L = expf(lam);
+                const float w = L * x * x;
+                p = w * s_st[tl];
+                const float dw = (dp - s_D[tl]) * s_st[tl];
+                ds = 2.f * L * x * dw;
+                Mv = dw * w;
+            }
+            if (t0 + tl > s) cs += Mv;
+            const float c = scale * ds;
+#pragma unroll
+            for (int i = 0; i < DH; ++i) {
+                dvv[i] = fmaf(p, s_do[tl][h * DH + i], dvv[i]);
+                dkv[i] = fmaf(c, s_q[tl][h * DH + i], dkv[i]);
+            }
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < DH; ++i) {
+            IO<In>::st(dk, (base + s) * D + h * DH + i, dkv[i]);
+            IO<In>::st(dv, (base + s) * D + h * DH + i, dvv[i]);
+        }
+        if (h == 0) colsum[base + s] = cs;
+    }
+}
+
+}  // namespace
+
+// dz from the row and column sums: exclusive fp64 prefix of colsum - rowsum
+__global__ void __launch_bounds__(256)
+bwd_dz_kernel(const float* __restrict__ z, const float* __restrict__ rowsum, const float* __restrict__ colsum,
+              float* __restrict__ dz, int T) {
+    __shared__ double s_tot[256];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const size_t base = (size_t)bh * T;
+    const int run = (T + 255) / 256;
+    const int t0 = min(T, tid * run), t1 = min(T, t0 + run);
+    double acc = 0.0;
+    for (int t = t0; t < t1; ++t) acc += (double)colsum[base + t] - (double)rowsum[base + t];
+    s_tot[tid] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double r = 0.0;
+        for (int i = 0; i < 256; ++i) {
+            const double x = s_tot[i];
+            s_tot[i] = r;
+            r += x;
+        }
+    }
+    __syncthreads();
+    double c = s_tot[tid];
+    for (int t = t0; t < t1; ++t) {
+        dz[base + t] = -sigmoid_f(z[base + t]) * (float)c;
+        c += (double)colsum[base + t] - (double)rowsum[base + t];
+    }
+}
+
+size_t bwd_workspace(const BwdArgs& a) {
+    const size_t n = (size_t)a.B * a.H * a.T;
+    return align256(n * sizeof(double)) + 4 * align256(n * sizeof(float));
+}
+
+BwdScratch bwd_scratch(const BwdArgs& a) {
+    const size_t n = (size_t)a.B * a.H * a.T;
+    char* p = (char*)a.ws;
+    BwdScratch s;
+    s.G = (double*)p;
+    p += align256(n * sizeof(double));
+    s.stat = (float*)p;
+    p += align256(n * sizeof(float));
+    s.Dt = (float*)p;
+    p += align256(n * sizeof(float));
+    s.rowsum = (float*)p;
+    p += align256(n * sizeof(float));
+    s.colsum = (float*)p;
+    return s;
+}
+
+template <int D, typename In>
+static int launch_prep(const BwdArgs& a, const BwdScratch& s) {
+    hipStream_t st = (hipStream_t)a.stream;
+    const int use_d = (a.variant == TWOMAMBA_EXP) || !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    hipLaunchKernelGGL((bwd_prep_kernel<D, In>), dim3(a.B * a.H), dim3(256), 0, st, a.z, (const In*)a.out,
+                       (const In*)a.dout, s.G, s.Dt, a.T, use_d);
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s) {
+    const bool bf = a.dtype == TWOMAMBA_BF16;
+    if (a.dv == 64) return bf ? launch_prep<64, bf16>(a, s) : launch_prep<64, float>(a, s);
+    return bf ? launch_prep<16, bf16>(a, s) : launch_prep<16, float>(a, s);
+}
+
+int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s) {
+    hipLaunchKernelGGL(bwd_dz_kernel, dim3(a.B * a.H), dim3(256), 0, (hipStream_t)a.stream, a.z, s.rowsum,
+                       s.colsum, a.gz, a.T);
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+template <int D, typename In, bool kExp>
+static int launch_ref(const BwdArgs& a, const BwdScratch& s) {
+    hipStream_t st = (hipStream_t)a.stream;
+    const int nt = (a.T + kTile - 1) / kTile;
+    const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    hipLaunchKernelGGL((bwd_ref_q_kernel<D, In, kExp>), dim3(a.B * a.H * nt), dim3(kTile), 0, st, (const In*)a.q,
+                       (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, s.stat, s.rowsum, (In*)a.gq, a.T,
+                       nt, a.scale, norm);
+    hipLaunchKernelGGL((bwd_ref_kv_kernel<D, In, kExp>), dim3(a.B * a.H * nt), dim3(2 * kTile), 0, st,
+                       (const In*)a.q, (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, s.stat,
+                       s.colsum, (In*)a.gk, (In*)a.gv, a.T, nt, a.scale);
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+int ref_bwd(const BwdArgs& a) {
+    if ((size_t)a.B * a.H * a.T == 0) return TWOMAMBA_OK;
+    const BwdScratch s = bwd_scratch(a);
+    int r = bwd_prep_launch(a, s);
+    if (r != TWOMAMBA_OK) return r;
+    const bool bf = a.dtype == TWOMAMBA_BF16, ex = a.variant == TWOMAMBA_EXP;
+    if (a.dk == 64) {
+        if (bf) r = ex ? launch_ref<64, bf16, true>(a, s) : launch_ref<64, bf16, false>(a, s);
+        else r = ex ? launch_ref<64, float, true>(a, s) : launch_ref<64, float, false>(a, s);
+    } else {
+        if (bf) r = ex ? launch_ref<16, bf16, true>(a, s) : launch_ref<16, bf16, false>(a, s);
+        else r = ex ? launch_ref<16, float, true>(a, s) : launch_ref<16, float, false>(a, s);
+    }
+    if (r != TWOMAMBA_OK) return r;
+    return bwd_dz_launch(a, s);
+}
+
+}  // namespace twm

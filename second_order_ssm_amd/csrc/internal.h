@@ -95,4 +95,33 @@ size_t exp_step_workspace(const ExpCacheArgs& a);
 int exp_step_launch(const ExpCacheArgs& a);
 int exp_cache_fill_launch(const ExpCacheArgs& a);
 
+// backward pass (bwd_ref.hip, bwd_mfma.hip)
+struct BwdArgs {
+    int B, H, T, dk, dv;
+    float scale;
+    int variant, dtype;
+    unsigned flags;
+    const void *q, *k, *v;
+    const float* z;
+    const void *out, *dout;
+    void *gq, *gk, *gv;   // dL/dq, dL/dk, dL/dv
+    float* gz;            // dL/dz
+    void* ws;
+    size_t ws_bytes;
+    void* stream;
+};
+// per-token scratch carved from the workspace
+struct BwdScratch {
+    double* G;       // running fp64 softplus sums
+    float* stat;     // 1/den (2Mamba) or log-sum-exp (2Mamba-E) of each query row
+    float* Dt;       // dout_t . out_t
+    float* rowsum;   // sum_{s<t} dL/dlambda_ts
+    float* colsum;   // sum_{t>s} dL/dlambda_ts
+};
+size_t bwd_workspace(const BwdArgs& a);
+BwdScratch bwd_scratch(const BwdArgs& a);
+int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s);
+int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s);
+int ref_bwd(const BwdArgs& a);
+
 }  // namespace twm

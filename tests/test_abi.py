@@ -219,3 +219,52 @@ def test_exp_cache_fill_validation(lib):
     assert call(cdesc(pos=10), z=None) == ENULL
     assert call(cdesc(pos=10), kc=fake(1)) == EALIAS
     assert call(cdesc(pos=0), k=None) == OK      # nothing to fill
+
+
+# ---------------------------------------------------------------- backward
+def call_bwd(lib, dsc, q=1, k=2, v=3, z=4, out=5, dout=6, dq=10, dk=11, dv=12, dz=13, ws=14, wsb=1 << 40):
+    p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
+    return lib.twomamba_bwd(ctypes.byref(dsc) if dsc is not None else None, p(q), p(k), p(v), p(z), p(out),
+                            p(dout), p(dq), p(dk), p(dv), p(dz), p(ws), ctypes.c_size_t(wsb), None)
+
+
+def bwd_ws(lib, dsc):
+    n = ctypes.c_size_t(12345)
+    s = lib.twomamba_bwd_workspace_size(ctypes.byref(dsc), ctypes.byref(n))
+    return s, n.value
+
+
+def test_bwd_workspace_size(lib):
+    # per token: fp64 decay prefix + four fp32 rows (statistic, dout.out, row and column sums)
+    a256 = lambda x: (x + 255) // 256 * 256
+    n = 2 * 3 * 100
+    assert bwd_ws(lib, desc(B=2, H=3, T=100)) == (OK, a256(8 * n) + 4 * a256(4 * n))
+    assert bwd_ws(lib, desc(B=0)) == (OK, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ESHAPE), (dict(dtype=7), EDTYPE), (dict(variant=3), EDTYPE), (dict(d=32), EUNSUP),
+    (dict(variant=1, flags=1), EUNSUP), (dict(flags=1 << 7), EUNSUP), (dict(scale=float("nan")), ESHAPE),
+    (dict(B=1 << 30, H=1 << 30, T=1 << 30), ESHAPE),
+])
+def test_bwd_bad_descriptor(lib, kw, status):
+    d = desc(**kw)
+    assert bwd_ws(lib, d)[0] == status
+    assert call_bwd(lib, d) == status
+
+
+def test_bwd_pointer_checks(lib):
+    d = desc()
+    _, need = bwd_ws(lib, d)
+    assert call_bwd(lib, None) == ENULL
+    for field in ("q", "k", "v", "z", "out", "dout", "dq", "dk", "dv", "dz"):
+        assert call_bwd(lib, d, **{field: None}) == ENULL
+    assert call_bwd(lib, d, ws=None) == EWS
+    assert call_bwd(lib, d, wsb=need - 1) == EWS
+    assert call_bwd(lib, d, ws=ctypes.c_void_p(BASE + 14 * GAP + 16)) == EWS
+    assert call_bwd(lib, d, dq=1) == EALIAS                                  # dq == q
+    assert call_bwd(lib, d, dv=ctypes.c_void_p(BASE + 6 * GAP + 64)) == EALIAS  # dv inside dout
+    assert call_bwd(lib, d, dk=10) == EALIAS                                 # dk == dq
+    assert call_bwd(lib, d, ws=13) == EALIAS                                 # workspace == dz
+    assert call_bwd(lib, desc(B=0), q=None, k=None, v=None, z=None, out=None, dout=None, dq=None, dk=None,
+                    dv=None, dz=None, ws=None, wsb=0) == OK
