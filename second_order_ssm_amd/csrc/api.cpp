@@ -374,7 +374,7 @@ int twomamba_bwd(const twomamba_fwd_desc* d, const void* q, const void* k, const
     a.q = q; a.k = k; a.v = v; a.z = z; a.out = out; a.dout = dout;
     a.gq = dq; a.gk = dk; a.gv = dv; a.gz = dz;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
-    return twm::ref_bwd(a);
+    return twm::mfma_bwd_supported(a) ? twm::mfma_bwd(a) : twm::ref_bwd(a);
 }
 
 }  // extern "C"

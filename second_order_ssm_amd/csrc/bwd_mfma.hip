@@ -1,0 +1,515 @@
+// MFMA kernels of the 2Mamba / 2Mamba-E backward pass for bf16 inputs and
+// d_k = d_v = 64 ("2Mamba2Furious", App. C: gradients of the attention kernels
+// with Q, K, V as inputs; C.1: the A-mask gradient from sums of the masked
+// matrix along the key axis and along the query axis).
+//
+// The arithmetic per pair (t, s), s <= t, with x = q_t.k_s (bf16 products,
+// fp32 sums), lambda2 = log2(e) (G_s - G_t) and dP = dout_t.v_s:
+//   2Mamba:   u = 2^lambda2 x, P = scale^2 u x / den_t, dw = (dP - D_t) / den_t,
+//             dS' = u dw;  dq_t = 2 scale^2 sum_s dS' k_s, dk_s = 2 scale^2
+//             sum_t dS' q_t, dL/dlambda_ts = scale^2 x dS'   (den_t = scale^2
+//             sum_s 2^lambda2 x^2; without normalisation 1/den_t = 1, D_t = 0);
+//   2Mamba-E: P = 2^(log2(e) scale x + lambda2 - lse2_t), dS = P (dP - D_t);
+//             dq_t = scale sum_s dS k_s, dk_s = scale sum_t dS q_t,
+//             dL/dlambda_ts = dS;
+// and dv_s = sum_t P dout_t.  D_t = dout_t.o_t comes from the preparation
+// kernel together with the fp64 running sums G.
+//
+// Both kernels use 16x16x32 bf16 MFMAs.  A lane of a 16x16 accumulator holds
+// four consecutive rows 4g..4g+3 (g = lane / 16) of one column (lane mod 16).
+//  * bwd_q_kernel (64 queries per workgroup, 16 per wave, one query per lane
+//    column): scores transposed, S^T = K Q^T and dP^T = V dout^T, over key
+//    tiles of 64 from the first to the diagonal.  A first sweep gives the row
+//    statistic (1/den_t or the log-sum-exp), a second one dq, through
+//    dq^T = K^T dS^T, and the row sums of dL/dlambda.
+//  * bwd_kv_kernel (64 keys per workgroup, 16 per wave, one key per lane
+//    column): S = Q K^T and dP = dout V^T over query tiles of 64 from the
+//    diagonal to the end; dv^T = dout^T P and dk^T = Q^T dS, and the column
+//    sums of dL/dlambda.
+// The probability / gradient accumulators leave the MFMA already in the B
+// operand layout of the next product: two vertically adjacent 16x16 tiles give
+// a lane the eight K-slots {4g..4g+3, 16+4g..16+4g+3}; the transposed A
+// operands (K^T, Q^T, dout^T) are read in that order with gfx950's
+// transposing LDS read.  Tiles are staged through LDS row-major (144-byte
+// rows), double-buffered, with the next tile's global loads in flight during
+// the current tile's MFMAs.
+#include "device_common.h"
+#include "internal.h"
+
+namespace twm {
+namespace {
+
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+constexpr int kD = 64;
+constexpr int kW = 4;                  // waves per workgroup
+constexpr int kThreads = 64 * kW;
+constexpr int kBlk = 64;               // queries or keys per workgroup
+constexpr int kTile = 64;              // keys or queries per loop step
+constexpr int kLS = 72;                // LDS row stride in bf16 (144 B)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f4 mfma(b8 a, b8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ b8 as_b8(uint4 u) { return __builtin_bit_cast(b8, u); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+// two 16x16 accumulators (rows 4g..4g+3 and 16+4g..16+4g+3) as one B operand
+__device__ __forceinline__ b8 to_b(const float (&x)[8]) {
+    return as_b8(make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])));
+}
+__device__ __forceinline__ float xor_sum(float x) {   // over the four lane groups g
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+struct Tile {
+    uint16_t X[kTile][kLS];
+};
+
+// A operand of a row-major tile: row r, dims 8g + 32 kk .. + 7
+__device__ __forceinline__ b8 row_op(const Tile& t, int r, int g, int kk) {
+    return as_b8(*reinterpret_cast<const uint4*>(&t.X[r][8 * g + 32 * kk]));
+}
+// A operand of the transposed tile X^T (dims 16 dt .. 16 dt + 15 as rows) for
+// the K-slots {16 tt + 4g + 0..3, 16 tt + 16 + 4g + 0..3}: inside a 16-lane
+// group, lane 4j + r addresses columns 16 dt + 4r .. + 3 of row base + j and
+// receives column 16 dt + (lane mod 16) of rows base .. base + 3.
+__device__ __forceinline__ b8 tr_op(const Tile& t, int dt, int tt, int lane) {
+    const int g = lane >> 4, m = lane & 15, j = m >> 2, r = m & 3;
+    const int row = 16 * tt + 4 * g + j, col = 16 * dt + 4 * r;
+    const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)&t.X[row][col]);
+    const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)&t.X[row + 16][col]);
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return as_b8(make_uint4(ua.x, ua.y, ub.x, ub.y));
+}
+
+// Global -> registers for one 64-row tile (two 16-byte chunks per thread),
+// rows past `rows` read as zero; registers -> LDS.
+struct Stage {
+    uint4 c[2];
+};
+__device__ __forceinline__ void fetch(Stage& s, const bf16* src, int rows, int tid) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int e = tid + n * kThreads, r = e >> 3, c = e & 7;
+        s.c[n] = r < rows ? *reinterpret_cast<const uint4*>(src + (size_t)r * kD + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+__device__ __forceinline__ void store(const Stage& s, Tile& t, int tid) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int e = tid + n * kThreads, r = e >> 3, c = e & 7;
+        *reinterpret_cast<uint4*>(&t.X[r][8 * c]) = s.c[n];
+    }
+}
+
+// registers of one lane's own row (query or key): B operand, dims 8g + 32 kk
+__device__ __forceinline__ b8 own_op(const bf16* row, int g, int kk) {
+    return as_b8(*reinterpret_cast<const uint4*>(row + 8 * g + 32 * kk));
+}
+
+// ---------------------------------------------------------------------------
+// query-major: row statistic, dq, row sums
+struct QSmem {
+    Tile K[2], V[2];
+    float A[2][kTile];      // log2(e) (G_s - G_ref) per key of the tile
+};
+
+template <bool kExp>
+__global__ void __launch_bounds__(kThreads)
+bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+             const bf16* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
+             float* __restrict__ stat, float* __restrict__ rowsum, bf16* __restrict__ dq, int T, int nqb,
+             float scale, int norm) {
+    __shared__ __attribute__((aligned(16))) QSmem sm;
+    const int bh = blockIdx.x / nqb;
+    const int qb = nqb - 1 - blockIdx.x % nqb;     // longest rows first
+    const int q0 = qb * kBlk;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const size_t base = (size_t)bh * T;
+    const int t = q0 + 16 * w + col;               // this lane's query
+    const bool tv = t < T;
+    const int tc = tv ? t : T - 1;
+    const double gref = G[base + q0];
+    const float b2 = (float)(G[base + tc] - gref) * kLog2e;
+    const float Dq = tv ? Dt[base + t] : 0.f;
+    const b8 Qb[2] = {own_op(q + (base + tc) * kD, g, 0), own_op(q + (base + tc) * kD, g, 1)};
+    const b8 Ob[2] = {own_op(dout + (base + tc) * kD, g, 0), own_op(dout + (base + tc) * kD, g, 1)};
+    const float sl2 = scale * kLog2e;
+
+    auto stage_a = [&](int buf, int s0) {
+        if (tid < kTile) {
+            const int s = s0 + tid;
+            sm.A[buf][tid] = s < T ? (float)(G[base + s] - gref) * kLog2e : -INFINITY;
+        }
+    };
+
+    // scores of a 64-key tile: S^T[s][t] for the 4 key tiles (st) of 16
+    auto scores = [&](const Tile& K, f4 (&S)[4]) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            f4 c = {0.f, 0.f, 0.f, 0.f};
+            c = mfma(row_op(K, 16 * st + col, g, 0), Qb[0], c);
+            c = mfma(row_op(K, 16 * st + col, g, 1), Qb[1], c);
+            S[st] = c;
+        }
+    };
+
+    const int nkt = qb + 1;
+    Stage sk, sv;
+    // ---------------------------------------------------------- sweep 1: statistic
+    float den = 0.f, m = -INFINITY, l = 0.f;
+    fetch(sk, k + base * kD, min(kTile, T), tid);
+    store(sk, sm.K[0], tid);
+    stage_a(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int cur = kt & 1, s0 = kt * kTile;
+        if (kt + 1 < nkt) fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
+        f4 S[4];
+        scores(sm.K[cur], S);
+        const bool diag = kt == qb;
+        if (kExp) {
+            float y[16];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[cur][16 * st + 4 * g]);
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float yy = fmaf(S[st][i], sl2, av[i] - b2);
+                    if (diag && s0 + 16 * st + 4 * g + i > t) yy = -INFINITY;
+                    y[4 * st + i] = yy;
+                    mx = fmaxf(mx, yy);
+                }
+            }
+            if (mx > m) {
+                l *= fexp2(m - mx);
+                m = mx;
+            }
+            const float mref = (m == -INFINITY) ? 0.f : m;   // a lane group may see only masked keys so far
+#pragma unroll
+            for (int i = 0; i < 16; ++i) l += fexp2(y[i] - mref);
+        } else {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[cur][16 * st + 4 * g]);
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float L = fexp2(av[i] - b2);
+                    if (diag && s0 + 16 * st + 4 * g + i > t) L = 0.f;
+                    den = fmaf(L * S[st][i], S[st][i], den);
+                }
+            }
+        }
+        if (kt + 1 < nkt) {
+            store(sk, sm.K[cur ^ 1], tid);
+            stage_a(cur ^ 1, s0 + kTile);
+        }
+        __syncthreads();
+    }
+    float st_v, cq;   // row statistic; cq: 2^-lse2 offset (EXP) or -D / den (2Mamba)
+    if (kExp) {
+        // combine the four lane groups' (m, l)
+        float M = fmaxf(m, __shfl_xor(m, 16));
+        M = fmaxf(M, __shfl_xor(M, 32));
+        const float lsc = (m == -INFINITY) ? 0.f : l * fexp2(m - M);
+        const float L = xor_sum(lsc);
+        st_v = M + flog2(L);
+        cq = b2 + st_v;
+    } else {
+        const float dn = xor_sum(den) * scale * scale;
+        st_v = norm ? (dn > 0.f ? 1.f / dn : 0.f) : 1.f;
+        cq = -Dq * st_v;
+    }
+
+    // ---------------------------------------------------------- sweep 2: dq, row sums
+    f4 dQ[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dQ[dt] = f4{0.f, 0.f, 0.f, 0.f};
+    float rs = 0.f;
+    fetch(sk, k + base * kD, min(kTile, T), tid);
+    fetch(sv, v + base * kD, min(kTile, T), tid);
+    store(sk, sm.K[0], tid);
+    store(sv, sm.V[0], tid);
+    stage_a(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int cur = kt & 1, s0 = kt * kTile;
+        if (kt + 1 < nkt) {
+            fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
+            fetch(sv, v + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
+        }
+        const Tile& K = sm.K[cur];
+        const Tile& V = sm.V[cur];
+        f4 S[4], P[4];
+        scores(K, S);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            f4 c = {0.f, 0.f, 0.f, 0.f};
+            c = mfma(row_op(V, 16 * st + col, g, 0), Ob[0], c);
+            c = mfma(row_op(V, 16 * st + col, g, 1), Ob[1], c);
+            P[st] = c;   // dP^T
+        }
+        const bool diag = kt == qb;
+        float ds[16];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[cur][16 * st + 4 * g]);
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = s0 + 16 * st + 4 * g + i;
+                const bool ok = !diag || s <= t;
+                const float x = S[st][i];
+                float d, Mv;
+                if (kExp) {
+                    const float p = fexp2(fmaf(x, sl2, av[i] - cq));
+                    d = p * (P[st][i] - Dq);
+                    Mv = d;
+                } else {
+                    const float u = fexp2(av[i] - b2) * x;
+                    const float dw = fmaf(P[st][i], st_v, cq);
+                    d = u * dw;
+                    Mv = x * d;
+                }
+                d = ok ? d : 0.f;
+                if (s < t) rs += Mv;
+                ds[4 * st + i] = d;
+            }
+        }
+        // dq^T[d][t] += K^T[d][s] dS^T[s][t] over the two 32-key halves
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float x8[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x8[i] = ds[4 * (2 * h) + i];
+                x8[4 + i] = ds[4 * (2 * h + 1) + i];
+            }
+            const b8 B = to_b(x8);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) dQ[dt] = mfma(tr_op(K, dt, 2 * h, lane), B, dQ[dt]);
+        }
+        if (kt + 1 < nkt) {
+            store(sk, sm.K[cur ^ 1], tid);
+            store(sv, sm.V[cur ^ 1], tid);
+            stage_a(cur ^ 1, s0 + kTile);
+        }
+        __syncthreads();
+    }
+    rs = xor_sum(rs);
+    if (tv) {
+        const float f = kExp ? scale : 2.f * scale * scale;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            uint2 o;
+            o.x = pack2(dQ[dt][0] * f, dQ[dt][1] * f);
+            o.y = pack2(dQ[dt][2] * f, dQ[dt][3] * f);
+            *reinterpret_cast<uint2*>(dq + (base + t) * kD + 16 * dt + 4 * g) = o;
+        }
+        if (g == 0) {
+            stat[base + t] = st_v;
+            rowsum[base + t] = kExp ? rs : rs * scale * scale;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// key-major: dk, dv, column sums
+struct KVSmem {
+    Tile Q[2], O[2];
+    float B[2][kTile];      // log2(e) (G_t - G_ref) per query of the tile (+ lse2 for 2Mamba-E)
+    float R[2][kTile];      // 2Mamba: 1/den_t; 2Mamba-E: unused
+    float C[2][kTile];      // 2Mamba: -D_t/den_t; 2Mamba-E: D_t
+};
+
+template <bool kExp>
+__global__ void __launch_bounds__(kThreads)
+bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+              const bf16* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
+              const float* __restrict__ stat, float* __restrict__ colsum, bf16* __restrict__ dk,
+              bf16* __restrict__ dv, int T, int nkb, float scale) {
+    __shared__ __attribute__((aligned(16))) KVSmem sm;
+    const int bh = blockIdx.x / nkb;
+    const int kb = blockIdx.x % nkb;               // earliest keys (longest columns) first
+    const int k0 = kb * kBlk;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const size_t base = (size_t)bh * T;
+    const int s = k0 + 16 * w + col;               // this lane's key
+    const bool sv_ok = s < T;
+    const int sc = sv_ok ? s : T - 1;
+    const double gref = G[base + k0];
+    const float a2 = sv_ok ? (float)(G[base + sc] - gref) * kLog2e : -INFINITY;
+    const b8 Kb[2] = {own_op(k + (base + sc) * kD, g, 0), own_op(k + (base + sc) * kD, g, 1)};
+    const b8 Vb[2] = {own_op(v + (base + sc) * kD, g, 0), own_op(v + (base + sc) * kD, g, 1)};
+    const float sl2 = scale * kLog2e;
+
+    auto stage_rows = [&](int buf, int t0) {
+        if (tid < kTile) {
+            const int t = t0 + tid;
+            float b = INFINITY, r = 0.f, c = 0.f;
+            if (t < T) {
+                b = (float)(G[base + t] - gref) * kLog2e;
+                const float st = stat[base + t], d = Dt[base + t];
+                if (kExp) {
+                    b += st;
+                    c = d;
+                } else {
+                    r = st;
+                    c = -d * st;
+                }
+            }
+            sm.B[buf][tid] = b;
+            sm.R[buf][tid] = r;
+            sm.C[buf][tid] = c;
+        }
+    };
+
+    f4 dK[4], dV[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dK[dt] = dV[dt] = f4{0.f, 0.f, 0.f, 0.f};
+    float cs = 0.f;
+    const int nqt = (T - k0 + kTile - 1) / kTile;
+    Stage sq, so;
+    fetch(sq, q + (base + k0) * kD, min(kTile, T - k0), tid);
+    fetch(so, dout + (base + k0) * kD, min(kTile, T - k0), tid);
+    store(sq, sm.Q[0], tid);
+    store(so, sm.O[0], tid);
+    stage_rows(0, k0);
+    __syncthreads();
+    for (int it = 0; it < nqt; ++it) {
+        const int cur = it & 1, t0 = k0 + it * kTile;
+        if (it + 1 < nqt) {
+            fetch(sq, q + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
+            fetch(so, dout + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
+        }
+        const Tile& Q = sm.Q[cur];
+        const Tile& O = sm.O[cur];
+        f4 S[4], DP[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f4 c = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
+            c = mfma(row_op(Q, 16 * tt + col, g, 0), Kb[0], c);
+            c = mfma(row_op(Q, 16 * tt + col, g, 1), Kb[1], c);
+            e = mfma(row_op(O, 16 * tt + col, g, 0), Vb[0], e);
+            e = mfma(row_op(O, 16 * tt + col, g, 1), Vb[1], e);
+            S[tt] = c;
+            DP[tt] = e;
+        }
+        const bool diag = it == 0;
+        float p[16], ds[16];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const float4 b4 = *reinterpret_cast<const float4*>(&sm.B[cur][16 * tt + 4 * g]);
+            const float4 r4 = *reinterpret_cast<const float4*>(&sm.R[cur][16 * tt + 4 * g]);
+            const float4 c4 = *reinterpret_cast<const float4*>(&sm.C[cur][16 * tt + 4 * g]);
+            const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 16 * tt + 4 * g + i;
+                const bool ok = !diag || t >= s;
+                const float x = S[tt][i];
+                float pp, d, Mv;
+                if (kExp) {
+                    pp = fexp2(fmaf(x, sl2, a2 - bv[i]));
+                    d = pp * (DP[tt][i] - cv[i]);
+                    Mv = d;
+                } else {
+                    const float u = fexp2(a2 - bv[i]) * x;
+                    pp = u * x * rv[i];
+                    const float dw = fmaf(DP[tt][i], rv[i], cv[i]);
+                    d = u * dw;
+                    Mv = x * d;
+                }
+                pp = ok ? pp : 0.f;
+                d = ok ? d : 0.f;
+                if (t > s) cs += Mv;
+                p[4 * tt + i] = pp;
+                ds[4 * tt + i] = d;
+            }
+        }
+        // dv^T[c][s] += dout^T[c][t] P[t][s];  dk^T[d][s] += Q^T[d][t] dS[t][s]
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float xp[8], xd[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xp[i] = p[8 * h + i];
+                xp[4 + i] = p[8 * h + 4 + i];
+                xd[i] = ds[8 * h + i];
+                xd[4 + i] = ds[8 * h + 4 + i];
+            }
+            const b8 BP = to_b(xp), BD = to_b(xd);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                dV[dt] = mfma(tr_op(O, dt, 2 * h, lane), BP, dV[dt]);
+                dK[dt] = mfma(tr_op(Q, dt, 2 * h, lane), BD, dK[dt]);
+            }
+        }
+        if (it + 1 < nqt) {
+            store(sq, sm.Q[cur ^ 1], tid);
+            store(so, sm.O[cur ^ 1], tid);
+            stage_rows(cur ^ 1, t0 + kTile);
+        }
+        __syncthreads();
+    }
+    cs = xor_sum(cs);
+    if (sv_ok) {
+        const float fk = kExp ? scale : 2.f * scale * scale;
+        const float fv = kExp ? 1.f : scale * scale;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            uint2 a, b;
+            a.x = pack2(dK[dt][0] * fk, dK[dt][1] * fk);
+            a.y = pack2(dK[dt][2] * fk, dK[dt][3] * fk);
+            b.x = pack2(dV[dt][0] * fv, dV[dt][1] * fv);
+            b.y = pack2(dV[dt][2] * fv, dV[dt][3] * fv);
+            *reinterpret_cast<uint2*>(dk + (base + s) * kD + 16 * dt + 4 * g) = a;
+            *reinterpret_cast<uint2*>(dv + (base + s) * kD + 16 * dt + 4 * g) = b;
+        }
+        if (g == 0) colsum[base + s] = kExp ? cs : cs * scale * scale;
+    }
+}
+
+template <bool kExp>
+int launch(const BwdArgs& a, const BwdScratch& s) {
+    hipStream_t st = (hipStream_t)a.stream;
+    const int nb = (a.T + kBlk - 1) / kBlk;
+    const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    hipLaunchKernelGGL((bwd_q_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, s.G, s.Dt, s.stat, s.rowsum,
+                       (bf16*)a.gq, a.T, nb, a.scale, norm);
+    hipLaunchKernelGGL((bwd_kv_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, s.G, s.Dt, s.stat, s.colsum,
+                       (bf16*)a.gk, (bf16*)a.gv, a.T, nb, a.scale);
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+}  // namespace
+
+bool mfma_bwd_supported(const BwdArgs& a) {
+    return a.dtype == TWOMAMBA_BF16 && a.dk == kD && a.dv == kD && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
+}
+
+int mfma_bwd(const BwdArgs& a) {
+    if ((size_t)a.B * a.H * a.T == 0) return TWOMAMBA_OK;
+    const BwdScratch s = bwd_scratch(a);
+    int r = bwd_prep_launch(a, s);
+    if (r != TWOMAMBA_OK) return r;
+    r = a.variant == TWOMAMBA_EXP ? launch<true>(a, s) : launch<false>(a, s);
+    if (r != TWOMAMBA_OK) return r;
+    return bwd_dz_launch(a, s);
+}
+
+}  // namespace twm

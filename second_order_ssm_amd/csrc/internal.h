@@ -123,5 +123,7 @@ BwdScratch bwd_scratch(const BwdArgs& a);
 int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s);
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s);
 int ref_bwd(const BwdArgs& a);
+bool mfma_bwd_supported(const BwdArgs& a);
+int mfma_bwd(const BwdArgs& a);
 
 }  // namespace twm

@@ -64,6 +64,10 @@ CASES = [
     ("exp", "f32", 1, 2, 150, 16, 0.0, 1.0, False),
     ("exp", "bf16", 2, 2, 200, 64, -3.0, 1.0, False),
     ("exp", "f32", 1, 1, 65, 64, -8.0, 0.5, False),
+    ("sq", "bf16", 1, 2, 1000, 64, -3.0, 1.0, False),
+    ("exp", "bf16", 1, 2, 1000, 64, -1.0, 0.7, False),
+    ("sq", "bf16", 1, 1, 64, 64, -12.0, 1.0, False),
+    ("exp", "bf16", 1, 1, 63, 64, 0.0, 1.0, False),
 ]
 
 
