@@ -1,6 +1,7 @@
 """Benchmark of the 2Mamba operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs sq,exp,step,exp_step] [--cpu-seconds S]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs sq,exp,step,exp_step,bwd,exp_bwd]
+                    [--cpu-seconds S]
 
 A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
 chunk state, inter-chunk scan, readout, normalisation) over one batch of the
@@ -10,8 +11,9 @@ all inputs resident in HBM.  The same run also measures, each in its own timed
 loop, the 2Mamba-E forward on the same shape and the recurrent decode step
 (batch 64, 32 heads, fp32 packed state of 1.09 GB, 256 sequential steps after
 a T=2048 prefill) and the 2Mamba-E decode over a bf16 key/value cache (batch
-64, 32 heads, 256 sequential steps after a 2048-token prompt); they are
-reported under ``legs``.
+64, 32 heads, 256 sequential steps after a 2048-token prompt), and the
+backward pass of both variants on the forward's workload; they are reported
+under ``legs``.
 
 The roofline entry is for the dominant kernel of the timed step: algorithmic
 work attributed to that kernel per launch divided by its average duration,
@@ -69,6 +71,25 @@ def exp_step_bytes_per_head(pos, d=64, dv=64, esize=2):
     return pos * row + row + (2 * d + dv) * esize + 4 + dv * esize
 
 
+def bwd_flops_per_head(T, d=64, dv=64):
+    """Algorithmic backward work over the causal pairs T(T+1)/2: recompute the
+    score (2d), dP = dout.v (2dv), dv (2dv), dk (2d), dq (2d)."""
+    return T * (T + 1) // 2 * 2 * (3 * d + 2 * dv)
+
+
+def bwd_kernel_work(name, T, d=64, dv=64):
+    """Share of the backward work credited to one kernel per head: the
+    key-major kernel does the score, dP, dv and dk products, the query-major one
+    dq (its score / dP recomputation and the row-statistic sweep are counted as
+    overhead, not work)."""
+    pairs = T * (T + 1) // 2
+    if name == "bwd_kv":
+        return pairs * 2 * (2 * d + 2 * dv)
+    if name == "bwd_q":
+        return pairs * 2 * d
+    return 0
+
+
 def kernel_work(name, leg_work):
     """Algorithmic work credited to the dominant kernel per launch: the whole
     leg's work, since each forward kernel executes every algorithmic step of its
@@ -78,7 +99,8 @@ def kernel_work(name, leg_work):
 
 
 KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "step_kernel": "step.hip",
-                  "exp_decode_partial": "exp_step.hip", "exp_decode_combine": "exp_step.hip"}
+                  "exp_decode_partial": "exp_step.hip", "exp_decode_combine": "exp_step.hip",
+                  "bwd_q": "bwd_mfma.hip", "bwd_kv": "bwd_mfma.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -176,6 +198,41 @@ def leg_sq(steps, warmup, variant="sq"):
         kernels_ms=allk,
         roofline=dict(bound="mfma" if mfma else "alu", kernel=name, achieved=achieved / 1e12, peak=peak / 1e12,
                       unit="TFLOP/s", frac=achieved / peak, traffic=measured_traffic(name)),
+    )
+
+
+def leg_bwd(steps, warmup, variant="sq"):
+    """Backward (dq, dk, dv, dz) of the forward on the same workload, with a
+    seeded N(0,1) output gradient; the forward output is computed once, untimed."""
+    import numpy as np
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    shp = SQ_SHAPE
+    B, H, T, d = shp["B"], shp["H"], shp["T"], shp["d"]
+    q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=shp["seed"], dtype="bf16"))
+    dout = torch.from_numpy(np.random.default_rng(shp["seed"] + 500).standard_normal((B, H, T, d))).to(
+        torch.bfloat16).cuda()
+    out = tmb.fwd(q, k, v, z, variant=variant)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z))
+    desc = tmb.make_desc(B, H, T, d, d, variant=variant, dtype=torch.bfloat16)
+    ws = torch.empty(tmb.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    fn = lambda: tmb.bwd(q, k, v, z, out, dout, variant=variant, grads=grads, workspace=ws)
+    ms = time_loop(fn, steps, warmup)
+    name, kms, allk = dominant_kernel(lambda kt: tmb.bwd(q, k, v, z, out, dout, variant=variant, grads=grads,
+                                                         workspace=ws, kernel_times=kt), max(3, min(steps, 10)))
+    work = B * H * bwd_flops_per_head(T, d, d)
+    kwork = B * H * bwd_kernel_work(name, T, d, d)
+    achieved = kwork / (kms * 1e-3)
+    return dict(
+        workload=f"{'2Mamba' if variant == 'sq' else '2Mamba-E'} bwd B={B} H={H} T={T} d={d} bf16",
+        ms=ms, head_tokens_per_s=B * H * T / (ms * 1e-3), flops_per_call=work,
+        tflops=work / (ms * 1e-3) / 1e12, frac_peak_bf16=work / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        kernels_ms=allk,
+        roofline=dict(bound="mfma", kernel=name, achieved=achieved / 1e12, peak=PEAK_BF16_FLOPS / 1e12,
+                      unit="TFLOP/s", frac=achieved / PEAK_BF16_FLOPS, traffic=measured_traffic(name)),
     )
 
 
@@ -326,7 +383,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sq,exp,step,exp_step")
+    ap.add_argument("--legs", default="sq,exp,step,exp_step,bwd,exp_bwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the copy / GEMM ceiling measurements")
@@ -354,6 +411,12 @@ def main():
     if "step" in legs:
         res["step"] = leg_step(args.warmup)
         print(f"[bench] step leg done: {res['step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    if "bwd" in legs:
+        res["bwd"] = leg_bwd(args.steps, args.warmup, "sq")
+        print(f"[bench] bwd leg done: {res['bwd']['ms']:.3f} ms/call", file=sys.stderr, flush=True)
+    if "exp_bwd" in legs:
+        res["exp_bwd"] = leg_bwd(args.steps, args.warmup, "exp")
+        print(f"[bench] exp_bwd leg done: {res['exp_bwd']['ms']:.3f} ms/call", file=sys.stderr, flush=True)
     if "exp_step" in legs:
         res["exp_step"] = leg_exp_step(args.warmup)
         print(f"[bench] exp_step leg done: {res['exp_step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)

@@ -268,6 +268,15 @@ int twomamba_bwd(const twomamba_fwd_desc* desc,
                  void* dq, void* dk, void* dv, float* dz,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Profiling form of twomamba_bwd, with the per-launch timings of
+   twomamba_fwd_timed (the call waits for the stream). */
+int twomamba_bwd_timed(const twomamba_fwd_desc* desc,
+                       const void* q, const void* k, const void* v, const float* z,
+                       const void* out, const void* dout,
+                       void* dq, void* dk, void* dv, float* dz,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       float* kernel_ms, const char** kernel_names, int cap, int* n_kernels);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,10 @@ def load(path: str | None = None):
     lib.twomamba_bwd.restype = ctypes.c_int
     lib.twomamba_bwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    lib.twomamba_bwd_timed.restype = ctypes.c_int
+    lib.twomamba_bwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     if path is None:
         _lib = lib
     return lib
@@ -288,11 +292,12 @@ def exp_step(q, k, v, z, k_cache, v_cache, g_cache, pos, *, scale=1.0, out=None,
 
 
 def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, reference_kernels=False,
-        grads=None, workspace=None):
+        grads=None, workspace=None, kernel_times=None):
     """Backward of fwd (no initial state): returns (dq, dk, dv, dz).
 
     ``out`` is the forward output for the same inputs; ``grads`` may supply the
-    four output tensors.
+    four output tensors.  With ``kernel_times`` (a list) the call goes through
+    twomamba_bwd_timed and appends (kernel name, milliseconds) per launch.
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -314,9 +319,18 @@ def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, refere
     nbytes = bwd_workspace_size(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    s = load().twomamba_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(out), _ptr(dout),
-                            _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gz), _ptr(workspace), ctypes.c_size_t(nbytes),
-                            _stream())
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(out), _ptr(dout), _ptr(gq), _ptr(gk),
+            _ptr(gv), _ptr(gz), _ptr(workspace), ctypes.c_size_t(nbytes), _stream())
+    if kernel_times is None:
+        s = load().twomamba_bwd(*args)
+    else:
+        cap = 8
+        ms = (ctypes.c_float * cap)()
+        names = (ctypes.c_char_p * cap)()
+        cnt = ctypes.c_int(0)
+        s = load().twomamba_bwd_timed(*args, ms, names, cap, ctypes.byref(cnt))
+        for i in range(min(cnt.value, cap)):
+            kernel_times.append((names[i].decode(), float(ms[i])))
     if s != 0:
         raise TwoMambaError(s, "twomamba_bwd")
     return gq, gk, gv, gz

@@ -352,9 +352,9 @@ int twomamba_bwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
     return TWOMAMBA_OK;
 }
 
-int twomamba_bwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
-                 const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                    const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
+                    size_t workspace_bytes, void* stream, twm::KTimer* timer) {
     size_t qkb, vb, zb;
     int s = check_bwd(d, &qkb, &vb, &zb);
     if (s != TWOMAMBA_OK) return s;
@@ -373,8 +373,28 @@ int twomamba_bwd(const twomamba_fwd_desc* d, const void* q, const void* k, const
             if (overlaps(outs[i], outs[j])) return TWOMAMBA_ERR_ALIAS;
     a.q = q; a.k = k; a.v = v; a.z = z; a.out = out; a.dout = dout;
     a.gq = dq; a.gk = dk; a.gv = dv; a.gz = dz;
-    a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
+    a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream; a.timer = timer;
     return twm::mfma_bwd_supported(a) ? twm::mfma_bwd(a) : twm::ref_bwd(a);
+}
+
+int twomamba_bwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                 const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    return bwd_impl(d, q, k, v, z, out, dout, dq, dk, dv, dz, workspace, workspace_bytes, stream, nullptr);
+}
+
+int twomamba_bwd_timed(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                       const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
+                       size_t workspace_bytes, void* stream, float* kernel_ms, const char** kernel_names, int cap,
+                       int* n_kernels) {
+    if (!n_kernels) return TWOMAMBA_ERR_NULL;
+    *n_kernels = 0;
+    twm::KTimer t;
+    memset(&t, 0, sizeof(t));
+    int s = bwd_impl(d, q, k, v, z, out, dout, dq, dk, dv, dz, workspace, workspace_bytes, stream, &t);
+    const int c = twm::ktimer_collect(&t, kernel_ms, kernel_names, cap < 0 ? 0 : cap);
+    *n_kernels = t.n;
+    return s != TWOMAMBA_OK ? s : c;
 }
 
 }  // extern "C"

@@ -487,12 +487,16 @@ int launch(const BwdArgs& a, const BwdScratch& s) {
     hipStream_t st = (hipStream_t)a.stream;
     const int nb = (a.T + kBlk - 1) / kBlk;
     const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    ktimer_begin(a.timer, "bwd_q", a.stream);
     hipLaunchKernelGGL((bwd_q_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, s.G, s.Dt, s.stat, s.rowsum,
                        (bf16*)a.gq, a.T, nb, a.scale, norm);
+    ktimer_end(a.timer, a.stream);
+    ktimer_begin(a.timer, "bwd_kv", a.stream);
     hipLaunchKernelGGL((bwd_kv_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, s.G, s.Dt, s.stat, s.colsum,
                        (bf16*)a.gk, (bf16*)a.gv, a.T, nb, a.scale);
+    ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 

@@ -321,8 +321,10 @@ template <int D, typename In>
 static int launch_prep(const BwdArgs& a, const BwdScratch& s) {
     hipStream_t st = (hipStream_t)a.stream;
     const int use_d = (a.variant == TWOMAMBA_EXP) || !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    ktimer_begin(a.timer, "bwd_prep", a.stream);
     hipLaunchKernelGGL((bwd_prep_kernel<D, In>), dim3(a.B * a.H), dim3(256), 0, st, a.z, (const In*)a.out,
                        (const In*)a.dout, s.G, s.Dt, a.T, use_d);
+    ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
@@ -333,8 +335,10 @@ int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s) {
 }
 
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s) {
+    ktimer_begin(a.timer, "bwd_dz", a.stream);
     hipLaunchKernelGGL(bwd_dz_kernel, dim3(a.B * a.H), dim3(256), 0, (hipStream_t)a.stream, a.z, s.rowsum,
                        s.colsum, a.gz, a.T);
+    ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
@@ -343,12 +347,16 @@ static int launch_ref(const BwdArgs& a, const BwdScratch& s) {
     hipStream_t st = (hipStream_t)a.stream;
     const int nt = (a.T + kTile - 1) / kTile;
     const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    ktimer_begin(a.timer, "ref_bwd_q", a.stream);
     hipLaunchKernelGGL((bwd_ref_q_kernel<D, In, kExp>), dim3(a.B * a.H * nt), dim3(kTile), 0, st, (const In*)a.q,
                        (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, s.stat, s.rowsum, (In*)a.gq, a.T,
                        nt, a.scale, norm);
+    ktimer_end(a.timer, a.stream);
+    ktimer_begin(a.timer, "ref_bwd_kv", a.stream);
     hipLaunchKernelGGL((bwd_ref_kv_kernel<D, In, kExp>), dim3(a.B * a.H * nt), dim3(2 * kTile), 0, st,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, s.stat,
                        s.colsum, (In*)a.gk, (In*)a.gv, a.T, nt, a.scale);
+    ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 

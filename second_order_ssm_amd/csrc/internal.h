@@ -109,6 +109,7 @@ struct BwdArgs {
     void* ws;
     size_t ws_bytes;
     void* stream;
+    KTimer* timer;   // NULL unless called through twomamba_bwd_timed
 };
 // per-token scratch carved from the workspace
 struct BwdScratch {
