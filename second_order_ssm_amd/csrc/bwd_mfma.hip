@@ -33,6 +33,8 @@
 // transposing LDS read.  Tiles are staged through LDS row-major (144-byte
 // rows), double-buffered, with the next tile's global loads in flight during
 // the current tile's MFMAs.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -50,14 +52,19 @@ constexpr int kThreads = 64 * kW;
 constexpr int kBlk = 64;               // queries or keys per workgroup
 constexpr int kTile = 64;              // keys or queries per loop step
 constexpr int kLS = 72;                // LDS row stride in bf16 (144 B)
+constexpr int kMinBlocks = 3;          // workgroups per CU the register budget is sized for
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ f4 mfma(b8 a, b8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ b8 as_b8(uint4 u) { return __builtin_bit_cast(b8, u); }
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+// two fp32 -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    const f2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
 }
 // two 16x16 accumulators (rows 4g..4g+3 and 16+4g..16+4g+3) as one B operand
 __device__ __forceinline__ b8 to_b(const float (&x)[8]) {
@@ -116,18 +123,29 @@ __device__ __forceinline__ b8 own_op(const bf16* row, int g, int kk) {
 }
 
 // ---------------------------------------------------------------------------
-// query-major: row statistic, dq, row sums
+// query-major: D_t, row statistic, dq, row sums
 struct QSmem {
     Tile K[2], V[2];
     float A[2][kTile];      // log2(e) (G_s - G_ref) per key of the tile
 };
 
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {   // 8 bf16 x 8 bf16, fp32 sum
+    const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+    float r = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r = fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), r);
+        r = fmaf(__uint_as_float(x[i] & 0xffff0000u), __uint_as_float(y[i] & 0xffff0000u), r);
+    }
+    return r;
+}
+
 template <bool kExp>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, kMinBlocks)
 bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-             const bf16* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
-             float* __restrict__ stat, float* __restrict__ rowsum, bf16* __restrict__ dq, int T, int nqb,
-             float scale, int norm) {
+             const bf16* __restrict__ out, const bf16* __restrict__ dout, const double* __restrict__ G,
+             float* __restrict__ Dt, float* __restrict__ stat, float* __restrict__ rowsum, bf16* __restrict__ dq,
+             int T, int nqb, float scale, int norm, int use_d) {
     __shared__ __attribute__((aligned(16))) QSmem sm;
     const int bh = blockIdx.x / nqb;
     const int qb = nqb - 1 - blockIdx.x % nqb;     // longest rows first
@@ -139,9 +157,20 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     const int tc = tv ? t : T - 1;
     const double gref = G[base + q0];
     const float b2 = (float)(G[base + tc] - gref) * kLog2e;
-    const float Dq = tv ? Dt[base + t] : 0.f;
-    const b8 Qb[2] = {own_op(q + (base + tc) * kD, g, 0), own_op(q + (base + tc) * kD, g, 1)};
-    const b8 Ob[2] = {own_op(dout + (base + tc) * kD, g, 0), own_op(dout + (base + tc) * kD, g, 1)};
+    const bf16* qrow = q + (base + tc) * kD;
+    const bf16* orow = dout + (base + tc) * kD;
+    const b8 Qb[2] = {own_op(qrow, g, 0), own_op(qrow, g, 1)};
+    const b8 Ob[2] = {own_op(orow, g, 0), own_op(orow, g, 1)};
+    // D_t = dout_t . out_t from the 16 dims each lane group holds
+    float Dq = 0.f;
+    if (use_d) {
+        const bf16* yrow = out + (base + tc) * kD;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            Dq += dot8(*reinterpret_cast<const uint4*>(orow + 8 * g + 32 * kk),
+                       *reinterpret_cast<const uint4*>(yrow + 8 * g + 32 * kk));
+        Dq = xor_sum(Dq);
+    }
     const float sl2 = scale * kLog2e;
 
     auto stage_a = [&](int buf, int s0) {
@@ -150,19 +179,18 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             sm.A[buf][tid] = s < T ? (float)(G[base + s] - gref) * kLog2e : -INFINITY;
         }
     };
-
-    // scores of a 64-key tile: S^T[s][t] for the 4 key tiles (st) of 16
-    auto scores = [&](const Tile& K, f4 (&S)[4]) {
+    // S^T[s][t] for the key tiles st = 2h, 2h+1 of 16
+    auto scores = [&](const Tile& K, int h, f4 (&S)[2]) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int u = 0; u < 2; ++u) {
+            const int r = 16 * (2 * h + u) + col;
             f4 c = {0.f, 0.f, 0.f, 0.f};
-            c = mfma(row_op(K, 16 * st + col, g, 0), Qb[0], c);
-            c = mfma(row_op(K, 16 * st + col, g, 1), Qb[1], c);
-            S[st] = c;
+            c = mfma(row_op(K, r, g, 0), Qb[0], c);
+            c = mfma(row_op(K, r, g, 1), Qb[1], c);
+            S[u] = c;
         }
     };
 
-    const int nkt = qb + 1;
     Stage sk, sv;
     // ---------------------------------------------------------- sweep 1: statistic
     float den = 0.f, m = -INFINITY, l = 0.f;
@@ -170,54 +198,57 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     store(sk, sm.K[0], tid);
     stage_a(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
+    auto sweep1 = [&](int kt, auto diag_tag) {
+        constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = kt & 1, s0 = kt * kTile;
-        if (kt + 1 < nkt) fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
-        f4 S[4];
-        scores(sm.K[cur], S);
-        const bool diag = kt == qb;
-        if (kExp) {
-            float y[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f4 S[2];
+            scores(sm.K[cur], h, S);
+            float y[8];
             float mx = -INFINITY;
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int u = 0; u < 2; ++u) {
+                const int st = 2 * h + u;
                 const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[cur][16 * st + 4 * g]);
                 const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float yy = fmaf(S[st][i], sl2, av[i] - b2);
-                    if (diag && s0 + 16 * st + 4 * g + i > t) yy = -INFINITY;
-                    y[4 * st + i] = yy;
-                    mx = fmaxf(mx, yy);
+                    const bool masked = kDiag && s0 + 16 * st + 4 * g + i > t;
+                    if (kExp) {
+                        float yy = fmaf(S[u][i], sl2, av[i] - b2);
+                        yy = masked ? -INFINITY : yy;
+                        y[4 * u + i] = yy;
+                        mx = fmaxf(mx, yy);
+                    } else {
+                        float L = fexp2(av[i] - b2);
+                        L = masked ? 0.f : L;
+                        den = fmaf(L * S[u][i], S[u][i], den);
+                    }
                 }
             }
-            if (mx > m) {
-                l *= fexp2(m - mx);
-                m = mx;
-            }
-            const float mref = (m == -INFINITY) ? 0.f : m;   // a lane group may see only masked keys so far
-#pragma unroll
-            for (int i = 0; i < 16; ++i) l += fexp2(y[i] - mref);
-        } else {
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[cur][16 * st + 4 * g]);
-                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float L = fexp2(av[i] - b2);
-                    if (diag && s0 + 16 * st + 4 * g + i > t) L = 0.f;
-                    den = fmaf(L * S[st][i], S[st][i], den);
+            if (kExp) {
+                if (mx > m) {
+                    l *= fexp2(m - mx);
+                    m = mx;
                 }
+                const float mref = (m == -INFINITY) ? 0.f : m;   // a lane group may see only masked keys so far
+#pragma unroll
+                for (int i = 0; i < 8; ++i) l += fexp2(y[i] - mref);
             }
         }
-        if (kt + 1 < nkt) {
-            store(sk, sm.K[cur ^ 1], tid);
-            stage_a(cur ^ 1, s0 + kTile);
-        }
+    };
+    for (int kt = 0; kt < qb; ++kt) {   // key tiles wholly before the queries
+        const int cur = kt & 1, s0 = kt * kTile;
+        fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
+        sweep1(kt, std::false_type{});
+        store(sk, sm.K[cur ^ 1], tid);
+        stage_a(cur ^ 1, s0 + kTile);
         __syncthreads();
     }
-    float st_v, cq;   // row statistic; cq: 2^-lse2 offset (EXP) or -D / den (2Mamba)
+    sweep1(qb, std::true_type{});
+    __syncthreads();
+    float st_v, cq;   // row statistic; cq: b2 + lse2 (2Mamba-E) or -D / den (2Mamba)
     if (kExp) {
         // combine the four lane groups' (m, l)
         float M = fmaxf(m, __shfl_xor(m, 16));
@@ -243,70 +274,70 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     store(sv, sm.V[0], tid);
     stage_a(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
+    auto sweep2 = [&](int kt, auto diag_tag) {
+        constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = kt & 1, s0 = kt * kTile;
-        if (kt + 1 < nkt) {
-            fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
-            fetch(sv, v + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
-        }
         const Tile& K = sm.K[cur];
         const Tile& V = sm.V[cur];
-        f4 S[4], P[4];
-        scores(K, S);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            f4 c = {0.f, 0.f, 0.f, 0.f};
-            c = mfma(row_op(V, 16 * st + col, g, 0), Ob[0], c);
-            c = mfma(row_op(V, 16 * st + col, g, 1), Ob[1], c);
-            P[st] = c;   // dP^T
-        }
-        const bool diag = kt == qb;
-        float ds[16];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[cur][16 * st + 4 * g]);
-            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = s0 + 16 * st + 4 * g + i;
-                const bool ok = !diag || s <= t;
-                const float x = S[st][i];
-                float d, Mv;
-                if (kExp) {
-                    const float p = fexp2(fmaf(x, sl2, av[i] - cq));
-                    d = p * (P[st][i] - Dq);
-                    Mv = d;
-                } else {
-                    const float u = fexp2(av[i] - b2) * x;
-                    const float dw = fmaf(P[st][i], st_v, cq);
-                    d = u * dw;
-                    Mv = x * d;
-                }
-                d = ok ? d : 0.f;
-                if (s < t) rs += Mv;
-                ds[4 * st + i] = d;
-            }
-        }
-        // dq^T[d][t] += K^T[d][s] dS^T[s][t] over the two 32-key halves
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            float x8[8];
+            f4 S[2], P[2];
+            scores(K, h, S);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x8[i] = ds[4 * (2 * h) + i];
-                x8[4 + i] = ds[4 * (2 * h + 1) + i];
+            for (int u = 0; u < 2; ++u) {
+                const int r = 16 * (2 * h + u) + col;
+                f4 c = {0.f, 0.f, 0.f, 0.f};
+                c = mfma(row_op(V, r, g, 0), Ob[0], c);
+                c = mfma(row_op(V, r, g, 1), Ob[1], c);
+                P[u] = c;   // dP^T
             }
-            const b8 B = to_b(x8);
+            float ds[8];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int st = 2 * h + u;
+                const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[cur][16 * st + 4 * g]);
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = s0 + 16 * st + 4 * g + i;
+                    const float x = S[u][i];
+                    float d, Mv;
+                    if (kExp) {
+                        const float p = fexp2(fmaf(x, sl2, av[i] - cq));
+                        d = p * (P[u][i] - Dq);
+                        Mv = d;
+                    } else {
+                        const float uu = fexp2(av[i] - b2) * x;
+                        const float dw = fmaf(P[u][i], st_v, cq);
+                        d = uu * dw;
+                        Mv = x * d;
+                    }
+                    if (kDiag) {
+                        if (s < t) rs += Mv;
+                        d = s <= t ? d : 0.f;
+                    } else {
+                        rs += Mv;
+                    }
+                    ds[4 * u + i] = d;
+                }
+            }
+            // dq^T[d][t] += K^T[d][s] dS^T[s][t] over this 32-key half
+            const b8 B = to_b(ds);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) dQ[dt] = mfma(tr_op(K, dt, 2 * h, lane), B, dQ[dt]);
         }
-        if (kt + 1 < nkt) {
-            store(sk, sm.K[cur ^ 1], tid);
-            store(sv, sm.V[cur ^ 1], tid);
-            stage_a(cur ^ 1, s0 + kTile);
-        }
+    };
+    for (int kt = 0; kt < qb; ++kt) {
+        const int cur = kt & 1, s0 = kt * kTile;
+        fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
+        fetch(sv, v + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
+        sweep2(kt, std::false_type{});
+        store(sk, sm.K[cur ^ 1], tid);
+        store(sv, sm.V[cur ^ 1], tid);
+        stage_a(cur ^ 1, s0 + kTile);
         __syncthreads();
     }
+    sweep2(qb, std::true_type{});
     rs = xor_sum(rs);
     if (tv) {
         const float f = kExp ? scale : 2.f * scale * scale;
@@ -319,6 +350,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
         if (g == 0) {
             stat[base + t] = st_v;
+            Dt[base + t] = Dq;
             rowsum[base + t] = kExp ? rs : rs * scale * scale;
         }
     }
@@ -334,7 +366,7 @@ struct KVSmem {
 };
 
 template <bool kExp>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, kMinBlocks)
 bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const bf16* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
               const float* __restrict__ stat, float* __restrict__ colsum, bf16* __restrict__ dk,
@@ -387,83 +419,88 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     store(so, sm.O[0], tid);
     stage_rows(0, k0);
     __syncthreads();
-    for (int it = 0; it < nqt; ++it) {
+    auto tile = [&](int it, auto diag_tag) {
+        constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = it & 1, t0 = k0 + it * kTile;
-        if (it + 1 < nqt) {
-            fetch(sq, q + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
-            fetch(so, dout + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
-        }
         const Tile& Q = sm.Q[cur];
         const Tile& O = sm.O[cur];
-        f4 S[4], DP[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f4 c = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
-            c = mfma(row_op(Q, 16 * tt + col, g, 0), Kb[0], c);
-            c = mfma(row_op(Q, 16 * tt + col, g, 1), Kb[1], c);
-            e = mfma(row_op(O, 16 * tt + col, g, 0), Vb[0], e);
-            e = mfma(row_op(O, 16 * tt + col, g, 1), Vb[1], e);
-            S[tt] = c;
-            DP[tt] = e;
-        }
-        const bool diag = it == 0;
-        float p[16], ds[16];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const float4 b4 = *reinterpret_cast<const float4*>(&sm.B[cur][16 * tt + 4 * g]);
-            const float4 r4 = *reinterpret_cast<const float4*>(&sm.R[cur][16 * tt + 4 * g]);
-            const float4 c4 = *reinterpret_cast<const float4*>(&sm.C[cur][16 * tt + 4 * g]);
-            const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
-            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 16 * tt + 4 * g + i;
-                const bool ok = !diag || t >= s;
-                const float x = S[tt][i];
-                float pp, d, Mv;
-                if (kExp) {
-                    pp = fexp2(fmaf(x, sl2, a2 - bv[i]));
-                    d = pp * (DP[tt][i] - cv[i]);
-                    Mv = d;
-                } else {
-                    const float u = fexp2(a2 - bv[i]) * x;
-                    pp = u * x * rv[i];
-                    const float dw = fmaf(DP[tt][i], rv[i], cv[i]);
-                    d = u * dw;
-                    Mv = x * d;
-                }
-                pp = ok ? pp : 0.f;
-                d = ok ? d : 0.f;
-                if (t > s) cs += Mv;
-                p[4 * tt + i] = pp;
-                ds[4 * tt + i] = d;
-            }
-        }
-        // dv^T[c][s] += dout^T[c][t] P[t][s];  dk^T[d][s] += Q^T[d][t] dS[t][s]
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            float xp[8], xd[8];
+            f4 S[2], DP[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xp[i] = p[8 * h + i];
-                xp[4 + i] = p[8 * h + 4 + i];
-                xd[i] = ds[8 * h + i];
-                xd[4 + i] = ds[8 * h + 4 + i];
+            for (int u = 0; u < 2; ++u) {
+                const int r = 16 * (2 * h + u) + col;
+                f4 c = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
+                c = mfma(row_op(Q, r, g, 0), Kb[0], c);
+                c = mfma(row_op(Q, r, g, 1), Kb[1], c);
+                e = mfma(row_op(O, r, g, 0), Vb[0], e);
+                e = mfma(row_op(O, r, g, 1), Vb[1], e);
+                S[u] = c;
+                DP[u] = e;
             }
-            const b8 BP = to_b(xp), BD = to_b(xd);
+            float p[8], ds[8];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tt = 2 * h + u;
+                const float4 b4 = *reinterpret_cast<const float4*>(&sm.B[cur][16 * tt + 4 * g]);
+                const float4 c4 = *reinterpret_cast<const float4*>(&sm.C[cur][16 * tt + 4 * g]);
+                float4 r4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (!kExp) r4 = *reinterpret_cast<const float4*>(&sm.R[cur][16 * tt + 4 * g]);
+                const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+                const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = t0 + 16 * tt + 4 * g + i;
+                    const float x = S[u][i];
+                    float pp, d, Mv;
+                    if (kExp) {
+                        pp = fexp2(fmaf(x, sl2, a2 - bv[i]));
+                        d = pp * (DP[u][i] - cv[i]);
+                        Mv = d;
+                    } else {
+                        const float uu = fexp2(a2 - bv[i]) * x;
+                        pp = uu * x * rv[i];
+                        const float dw = fmaf(DP[u][i], rv[i], cv[i]);
+                        d = uu * dw;
+                        Mv = x * d;
+                    }
+                    if (kDiag) {
+                        if (t > s) cs += Mv;
+                        pp = t >= s ? pp : 0.f;
+                        d = t >= s ? d : 0.f;
+                    } else {
+                        cs += Mv;
+                    }
+                    p[4 * u + i] = pp;
+                    ds[4 * u + i] = d;
+                }
+            }
+            // dv^T[c][s] += dout^T[c][t] P[t][s];  dk^T[d][s] += Q^T[d][t] dS[t][s]
+            const b8 BP = to_b(p), BD = to_b(ds);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 dV[dt] = mfma(tr_op(O, dt, 2 * h, lane), BP, dV[dt]);
                 dK[dt] = mfma(tr_op(Q, dt, 2 * h, lane), BD, dK[dt]);
             }
         }
-        if (it + 1 < nqt) {
+    };
+    auto step = [&](int it, auto diag_tag) {
+        const int cur = it & 1, t0 = k0 + it * kTile;
+        const bool more = it + 1 < nqt;
+        if (more) {
+            fetch(sq, q + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
+            fetch(so, dout + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
+        }
+        tile(it, diag_tag);
+        if (more) {
             store(sq, sm.Q[cur ^ 1], tid);
             store(so, sm.O[cur ^ 1], tid);
             stage_rows(cur ^ 1, t0 + kTile);
         }
         __syncthreads();
-    }
+    };
+    step(0, std::true_type{});   // the diagonal tile
+    for (int it = 1; it < nqt; ++it) step(it, std::false_type{});
     cs = xor_sum(cs);
     if (sv_ok) {
         const float fk = kExp ? scale : 2.f * scale * scale;
@@ -487,10 +524,11 @@ int launch(const BwdArgs& a, const BwdScratch& s) {
     hipStream_t st = (hipStream_t)a.stream;
     const int nb = (a.T + kBlk - 1) / kBlk;
     const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    const int use_d = kExp || norm;
     ktimer_begin(a.timer, "bwd_q", a.stream);
     hipLaunchKernelGGL((bwd_q_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, s.G, s.Dt, s.stat, s.rowsum,
-                       (bf16*)a.gq, a.T, nb, a.scale, norm);
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.out, (const bf16*)a.dout, s.G, s.Dt,
+                       s.stat, s.rowsum, (bf16*)a.gq, a.T, nb, a.scale, norm, use_d);
     ktimer_end(a.timer, a.stream);
     ktimer_begin(a.timer, "bwd_kv", a.stream);
     hipLaunchKernelGGL((bwd_kv_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
@@ -509,7 +547,7 @@ bool mfma_bwd_supported(const BwdArgs& a) {
 int mfma_bwd(const BwdArgs& a) {
     if ((size_t)a.B * a.H * a.T == 0) return TWOMAMBA_OK;
     const BwdScratch s = bwd_scratch(a);
-    int r = bwd_prep_launch(a, s);
+    int r = bwd_prep_launch(a, s, false);   // G only: D_t comes from the query-major kernel
     if (r != TWOMAMBA_OK) return r;
     r = a.variant == TWOMAMBA_EXP ? launch<true>(a, s) : launch<false>(a, s);
     if (r != TWOMAMBA_OK) return r;

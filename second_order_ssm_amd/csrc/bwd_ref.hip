@@ -16,7 +16,8 @@
 //   dg_r = sum_{t >= r, s < r} M_ts = sum_{r' < r} (colsum_r' - rowsum_r'),
 // rowsum_t = sum_{s<t} M_ts, colsum_s = sum_{t>s} M_ts; dz = -sigmoid(z) dg.
 //
-//  * bwd_prep_kernel: G and D_t (one workgroup per head).
+//  * bwd_prep_kernel: G and D_t (one workgroup per head; the MFMA path takes
+//    only G from it and forms D_t in its query-major kernel).
 //  * bwd_ref_q_kernel: one thread per query; a pass over the keys for the row
 //    statistic, a second one for dq and rowsum.
 //  * bwd_ref_kv_kernel: two threads per key (half of the dims each); a pass
@@ -40,40 +41,57 @@ __device__ __forceinline__ float sigmoid_f(float x) {
     return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
 }
 
-// G (running fp64 softplus sums) and D_t = dout_t . out_t (0 without normalisation)
+// G (running fp64 softplus sums) and, when use_d, D_t = dout_t . out_t
+// (0 without normalisation).  One workgroup of kPrep threads per head.
+constexpr int kPrep = 1024;
 template <int DV, typename In>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kPrep)
 bwd_prep_kernel(const float* __restrict__ z, const In* __restrict__ out, const In* __restrict__ dout,
-                double* __restrict__ G, float* __restrict__ Dt, int T, int use_d) {
-    __shared__ double s_tot[256];
+                double* __restrict__ G, float* __restrict__ Dt, int T, int use_d, int write_d) {
+    __shared__ double s_tot[kPrep];
     const int bh = blockIdx.x, tid = threadIdx.x;
     const size_t base = (size_t)bh * T;
-    const int run = (T + 255) / 256;
+    const int run = (T + kPrep - 1) / kPrep;
     const int t0 = min(T, tid * run), t1 = min(T, t0 + run);
     double acc = 0.0;
     for (int t = t0; t < t1; ++t) acc += softplus_d(z[base + t]);
     s_tot[tid] = acc;
     __syncthreads();
-    if (tid == 0) {
+    // exclusive scan of the kPrep run totals: within each wave by its first
+    // lane, then over the wave totals
+    __shared__ double s_wave[kPrep / 64];
+    if ((tid & 63) == 0) {
         double r = 0.0;
-        for (int i = 0; i < 256; ++i) {
+        for (int i = tid; i < tid + 64; ++i) {
             const double x = s_tot[i];
             s_tot[i] = r;
             r += x;
         }
+        s_wave[tid >> 6] = r;
     }
     __syncthreads();
-    double g = s_tot[tid];
+    if (tid == 0) {
+        double r = 0.0;
+        for (int i = 0; i < kPrep / 64; ++i) {
+            const double x = s_wave[i];
+            s_wave[i] = r;
+            r += x;
+        }
+    }
+    __syncthreads();
+    double g = s_tot[tid] + s_wave[tid >> 6];
     for (int t = t0; t < t1; ++t) {
         g += softplus_d(z[base + t]);
         G[base + t] = g;
     }
-    for (int t = tid; t < T; t += 256) {
-        float d = 0.f;
-        if (use_d)
-            for (int c = 0; c < DV; ++c) d = fmaf(IO<In>::ld(dout, (base + t) * DV + c), IO<In>::ld(out, (base + t) * DV + c), d);
-        Dt[base + t] = d;
-    }
+    if (write_d)
+        for (int t = tid; t < T; t += kPrep) {
+            float d = 0.f;
+            if (use_d)
+                for (int c = 0; c < DV; ++c)
+                    d = fmaf(IO<In>::ld(dout, (base + t) * DV + c), IO<In>::ld(out, (base + t) * DV + c), d);
+            Dt[base + t] = d;
+        }
 }
 
 // one thread per query row
@@ -318,20 +336,20 @@ BwdScratch bwd_scratch(const BwdArgs& a) {
 }
 
 template <int D, typename In>
-static int launch_prep(const BwdArgs& a, const BwdScratch& s) {
+static int launch_prep(const BwdArgs& a, const BwdScratch& s, bool with_d) {
     hipStream_t st = (hipStream_t)a.stream;
     const int use_d = (a.variant == TWOMAMBA_EXP) || !(a.flags & TWOMAMBA_FLAG_NO_NORM);
     ktimer_begin(a.timer, "bwd_prep", a.stream);
-    hipLaunchKernelGGL((bwd_prep_kernel<D, In>), dim3(a.B * a.H), dim3(256), 0, st, a.z, (const In*)a.out,
-                       (const In*)a.dout, s.G, s.Dt, a.T, use_d);
+    hipLaunchKernelGGL((bwd_prep_kernel<D, In>), dim3(a.B * a.H), dim3(kPrep), 0, st, a.z, (const In*)a.out,
+                       (const In*)a.dout, s.G, s.Dt, a.T, use_d, (int)with_d);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
-int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s) {
+int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s, bool with_d) {
     const bool bf = a.dtype == TWOMAMBA_BF16;
-    if (a.dv == 64) return bf ? launch_prep<64, bf16>(a, s) : launch_prep<64, float>(a, s);
-    return bf ? launch_prep<16, bf16>(a, s) : launch_prep<16, float>(a, s);
+    if (a.dv == 64) return bf ? launch_prep<64, bf16>(a, s, with_d) : launch_prep<64, float>(a, s, with_d);
+    return bf ? launch_prep<16, bf16>(a, s, with_d) : launch_prep<16, float>(a, s, with_d);
 }
 
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s) {
@@ -363,7 +381,7 @@ static int launch_ref(const BwdArgs& a, const BwdScratch& s) {
 int ref_bwd(const BwdArgs& a) {
     if ((size_t)a.B * a.H * a.T == 0) return TWOMAMBA_OK;
     const BwdScratch s = bwd_scratch(a);
-    int r = bwd_prep_launch(a, s);
+    int r = bwd_prep_launch(a, s, true);
     if (r != TWOMAMBA_OK) return r;
     const bool bf = a.dtype == TWOMAMBA_BF16, ex = a.variant == TWOMAMBA_EXP;
     if (a.dk == 64) {

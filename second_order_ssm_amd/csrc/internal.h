@@ -121,7 +121,7 @@ struct BwdScratch {
 };
 size_t bwd_workspace(const BwdArgs& a);
 BwdScratch bwd_scratch(const BwdArgs& a);
-int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s);
+int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s, bool with_d);
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s);
 int ref_bwd(const BwdArgs& a);
 bool mfma_bwd_supported(const BwdArgs& a);
