@@ -53,7 +53,7 @@ __all__ = [
     "fwd_recurrent_full", "fwd_recurrent_packed", "step",
     "fwd_exp_quadratic", "fwd_exp_quadratic_rows", "fwd_exp_streaming",
     "state_elements", "memory_crossover_tokens",
-    "sigmoid", "bwd_quadratic", "bwd_exp_quadratic",
+    "sigmoid", "bwd_quadratic", "bwd_exp_quadratic", "conv2", "step_conv",
 ]
 
 
@@ -453,3 +453,45 @@ def bwd_exp_quadratic(q, k, v, z, dout, scale=1.0):
         dk[:, :, :t + 1] += scale * dl[..., None] * q[:, :, t][:, :, None, :]
         _add_mask_grad(dg, dl, t)
     return dq, dk, dv, -sigmoid(z) * dg
+
+
+# ----------------------------------------------------------------------------
+# size-2 input convolution  [2M2F §3: a convolution of kernel size 2 over the
+# sequence, no activation; §4: kept in Mamba-2S; App. A: decoding caches the
+# window - 1 = 1 previous query, key and value]
+#
+# Reading: a causal depthwise convolution of each channel of q, k and v
+# separately, y_t = w1 * x_t + w0 * x_{t-1} + b, with x_{-1} the cached raw
+# row of the token before the sequence (zeros when there is none).
+# ----------------------------------------------------------------------------
+
+def conv2(x, w, b=None, prev=None):
+    """Causal kernel-2 convolution along the token axis, channel by channel.
+
+    x [B, H, T, d]; w [H, d, 2] with tap 0 on x_{t-1} and tap 1 on x_t;
+    b [H, d] or None; prev [B, H, d] (the raw row before token 0) or None.
+    """
+    B, H, T, d = x.shape
+    y = np.zeros(x.shape)
+    for t in range(T):
+        before = x[:, :, t - 1] if t > 0 else (np.zeros((B, H, d)) if prev is None else prev)
+        y[:, :, t] = w[None, :, :, 1] * x[:, :, t] + w[None, :, :, 0] * before
+        if b is not None:
+            y[:, :, t] += b[None]
+    return y
+
+
+def step_conv(q, k, v, z, w, b, conv_state, state, norm_state, scale=1.0, norm=True):
+    """One decode step with the input convolution in front of the recurrence.
+
+    w [3, H, d, 2] and b [3, H, d] (or None) hold the q, k, v convolutions;
+    conv_state [B, H, 3, d] holds the raw q, k, v of the previous token.
+    Returns (out, state, norm, new conv_state = the raw q, k, v of this token).
+    """
+    xs = (q, k, v)
+    ys = []
+    for i in range(3):
+        bi = None if b is None else b[i]
+        ys.append(conv2(xs[i][:, :, None], w[i], bi, conv_state[:, :, i])[:, :, 0])
+    out, S, n = step(ys[0], ys[1], ys[2], z, state, norm_state, scale=scale, norm=norm)
+    return out, S, n, np.stack([q, k, v], axis=2)
