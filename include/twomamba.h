@@ -235,6 +235,54 @@ int twomamba_exp_step(const twomamba_exp_cache_desc* desc,
                       void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Size-2 causal input convolution  [2M2F §3: a convolution of kernel size 2
+ * along the sequence, without activation, in front of the attention kernel;
+ * §4: kept in Mamba-2S; App. A: decoding then caches the raw query, key and
+ * value of the one previous token].
+ *
+ * Each channel c of q, k and v (x below) is convolved separately:
+ *     y_t[c] = w[c][1] * x_t[c] + w[c][0] * x_{t-1}[c] + b[c],
+ * with x_{-1} the cached raw row of the token before the sequence (zeros when
+ * none is given).  The outputs feed twomamba_fwd (or the reference forward)
+ * in place of q, k, v; twomamba_step_conv does the same inside a decode step.
+ */
+typedef struct {
+    int B, H, T;        /* batch, heads, tokens                                         */
+    int d;              /* head dim of q, k and v (equal); supported: 16, 64            */
+    int dtype;          /* dtype of q, k, v, the outputs and the cache                  */
+    unsigned flags;     /* must be 0                                                    */
+} twomamba_conv_desc;
+
+/*
+ *   q, k, v        [B][H][T][d]   dtype   device
+ *   weight         [3][H][d][2]   fp32    device   q, k, v in that order; tap 0 multiplies
+ *                                                  x_{t-1}, tap 1 multiplies x_t
+ *   bias           [3][H][d]      fp32    device   or NULL (no bias)
+ *   conv_state_in  [B][H][3][d]   dtype   device   raw q, k, v rows of the token before
+ *                                                  t = 0, or NULL (zeros)
+ *   q_out, k_out, v_out  [B][H][T][d]  dtype  device   written (round to nearest even for bf16)
+ *   conv_state_out [B][H][3][d]   dtype   device   the raw rows of token T-1 (conv_state_in
+ *                                                  when T = 0), or NULL (not written)
+ * Outputs must not overlap inputs or each other.
+ */
+int twomamba_conv2(const twomamba_conv_desc* desc,
+                   const void* q, const void* k, const void* v,
+                   const float* weight, const float* bias, const void* conv_state_in,
+                   void* q_out, void* k_out, void* v_out, void* conv_state_out, void* stream);
+
+/*
+ * twomamba_step with the size-2 input convolution in front: q, k, v are this
+ * token's raw rows; each is convolved with the cached raw row of the previous
+ * token (conv_state, [B][H][3][d] in the input dtype, read and then replaced
+ * by this token's raw rows), then the step runs on the results.  weight and
+ * bias as for twomamba_conv2 (bias may be NULL); dk == dv.
+ */
+int twomamba_step_conv(const twomamba_step_desc* desc,
+                       const void* q, const void* k, const void* v, const float* z,
+                       const float* weight, const float* bias, void* conv_state,
+                       float* state, float* norm, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Backward pass of twomamba_fwd  [2M2F App. C: the gradients of each attention
  * kernel, with Q, K, V as inputs and the post-attention outputs as outputs;
  * C.1: the A-mask gradient is built from sums of the masked matrix along the

@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "step", "library_path",
-           "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd",
+           "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd", "conv2", "step_conv",
            "TwoMambaError", "SQ", "EXP", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "num_pairs"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +48,11 @@ class FwdDesc(ctypes.Structure):
 class ExpCacheDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int), ("dv", ctypes.c_int),
                 ("max_len", ctypes.c_int), ("pos", ctypes.c_int), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int), ("flags", ctypes.c_uint)]
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("T", ctypes.c_int), ("d", ctypes.c_int),
                 ("dtype", ctypes.c_int), ("flags", ctypes.c_uint)]
 
 
@@ -99,6 +104,10 @@ def load(path: str | None = None):
     lib.twomamba_bwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
                                        ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.twomamba_conv2.restype = ctypes.c_int
+    lib.twomamba_conv2.argtypes = [ctypes.POINTER(ConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.twomamba_step_conv.restype = ctypes.c_int
+    lib.twomamba_step_conv.argtypes = [ctypes.POINTER(StepDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -334,3 +343,51 @@ def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, refere
     if s != 0:
         raise TwoMambaError(s, "twomamba_bwd")
     return gq, gk, gv, gz
+
+
+def conv2(q, k, v, weight, bias=None, state_in=None, *, outs=None, want_state=False, state_out=None):
+    """Size-2 causal input convolution of q, k, v.  Returns (q', k', v') or,
+    with ``want_state``, (q', k', v', conv_state_out)."""
+    B, H, T, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, (B, H, T, d), q.dtype, n)
+    _check(weight, (3, H, d, 2), torch.float32, "weight")
+    if bias is not None:
+        _check(bias, (3, H, d), torch.float32, "bias")
+    if state_in is not None:
+        _check(state_in, (B, H, 3, d), q.dtype, "state_in")
+    if outs is None:
+        outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, 3, d), dtype=q.dtype, device=q.device)
+    desc = ConvDesc(B, H, T, d, _DT[q.dtype], 0)
+    s = load().twomamba_conv2(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(weight), _ptr(bias),
+                              _ptr(state_in), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(state_out),
+                              _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_conv2")
+    return (*outs, state_out) if (want_state or state_out is not None) else tuple(outs)
+
+
+def step_conv(q, k, v, z, weight, bias, conv_state, state, norm, *, scale=1.0, no_norm=False, out=None):
+    """Decode step with the size-2 input convolution; conv_state, state and
+    norm are updated in place."""
+    B, H, d = q.shape
+    _check(k, (B, H, d), q.dtype, "k")
+    _check(v, (B, H, d), q.dtype, "v")
+    _check(z, (B, H), torch.float32, "z")
+    _check(weight, (3, H, d, 2), torch.float32, "weight")
+    if bias is not None:
+        _check(bias, (3, H, d), torch.float32, "bias")
+    _check(conv_state, (B, H, 3, d), q.dtype, "conv_state")
+    D = num_pairs(d)
+    _check(state, (B, H, D, d), torch.float32, "state")
+    _check(norm, (B, H, D), torch.float32, "norm")
+    if out is None:
+        out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
+    desc = StepDesc(B, H, d, d, scale, _DT[q.dtype], FLAG_NO_NORM if no_norm else 0)
+    s = load().twomamba_step_conv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(weight),
+                                  _ptr(bias), _ptr(conv_state), _ptr(state), _ptr(norm), _ptr(out), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_step_conv")
+    return out

@@ -207,8 +207,9 @@ int twomamba_fwd_timed(const twomamba_fwd_desc* d, const void* q, const void* k,
     return s != TWOMAMBA_OK ? s : c;
 }
 
-int twomamba_step(const twomamba_step_desc* d, const void* q, const void* k, const void* v, const float* z,
-                  float* state, float* norm, void* out, void* stream) {
+static int step_impl(const twomamba_step_desc* d, const void* q, const void* k, const void* v, const float* z,
+                     const float* conv_w, const float* conv_b, void* conv_state, float* state, float* norm,
+                     void* out, void* stream) {
     if (!d) return TWOMAMBA_ERR_NULL;
     if (d->B < 0 || d->H < 0 || d->dk <= 0 || d->dv <= 0) return TWOMAMBA_ERR_SHAPE;
     if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
@@ -231,10 +232,72 @@ int twomamba_step(const twomamba_step_desc* d, const void* q, const void* k, con
         for (const Range& in : {rq, rk, rv, rz})
             if (overlaps(w, in)) return TWOMAMBA_ERR_ALIAS;
     if (overlaps(rs, rn) || overlaps(rs, ro) || overlaps(rn, ro)) return TWOMAMBA_ERR_ALIAS;
+    if (conv_w) {
+        size_t cb, wb, bb;
+        if (!prod(&cb, {B, H, 3, (size_t)d->dk, es}) || !prod(&wb, {3, H, (size_t)d->dk, 2, 4}) ||
+            !prod(&bb, {3, H, (size_t)d->dk, 4}))
+            return TWOMAMBA_ERR_SHAPE;
+        const Range rc = rng(conv_state, cb), rw = rng(conv_w, wb), rb = rng(conv_b, bb);
+        for (const Range& x : {rq, rk, rv, rz, rs, rn, ro, rw, rb})
+            if (overlaps(rc, x)) return TWOMAMBA_ERR_ALIAS;
+        for (const Range& w : {rs, rn, ro})
+            if (overlaps(w, rw) || overlaps(w, rb)) return TWOMAMBA_ERR_ALIAS;
+    }
     StepArgs a;
+    memset(&a, 0, sizeof(a));
     a.B = d->B; a.H = d->H; a.dk = d->dk; a.dv = d->dv; a.scale = d->scale; a.dtype = d->dtype; a.flags = d->flags;
     a.q = q; a.k = k; a.v = v; a.z = z; a.state = state; a.norm = norm; a.out = out; a.stream = stream;
+    a.conv_w = conv_w; a.conv_b = conv_b; a.conv_state = conv_state;
     return twm::step_launch(a);
+}
+
+int twomamba_step(const twomamba_step_desc* d, const void* q, const void* k, const void* v, const float* z,
+                  float* state, float* norm, void* out, void* stream) {
+    return step_impl(d, q, k, v, z, nullptr, nullptr, nullptr, state, norm, out, stream);
+}
+
+int twomamba_step_conv(const twomamba_step_desc* d, const void* q, const void* k, const void* v, const float* z,
+                       const float* conv_w, const float* conv_b, void* conv_state, float* state, float* norm,
+                       void* out, void* stream) {
+    if (!d) return TWOMAMBA_ERR_NULL;
+    if ((size_t)(d->B < 0 ? 0 : d->B) * (size_t)(d->H < 0 ? 0 : d->H) > 0 && (!conv_w || !conv_state))
+        return TWOMAMBA_ERR_NULL;
+    if (d->dk != d->dv) return TWOMAMBA_ERR_UNSUPPORTED;
+    return step_impl(d, q, k, v, z, conv_w, conv_b, conv_state, state, norm, out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// size-2 input convolution
+int twomamba_conv2(const twomamba_conv_desc* d, const void* q, const void* k, const void* v, const float* weight,
+                   const float* bias, const void* conv_state_in, void* q_out, void* k_out, void* v_out,
+                   void* conv_state_out, void* stream) {
+    if (!d) return TWOMAMBA_ERR_NULL;
+    if (d->B < 0 || d->H < 0 || d->T < 0 || d->d <= 0) return TWOMAMBA_ERR_SHAPE;
+    if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
+    if (d->flags != 0u) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (d->d != 16 && d->d != 64) return TWOMAMBA_ERR_UNSUPPORTED;
+    const size_t es = d->dtype == TWOMAMBA_BF16 ? 2 : 4;
+    const size_t B = d->B, H = d->H, T = d->T, D = d->d;
+    size_t xb, cb, wb, bb, g;
+    if (!prod(&xb, {B, H, T, D, es}) || !prod(&cb, {B, H, 3, D, es}) || !prod(&wb, {3, H, D, 2, 4}) ||
+        !prod(&bb, {3, H, D, 4}) || !prod(&g, {B, H, T, 3, D / 8}) || (g + 255) / 256 > 0x7fffffffu)
+        return TWOMAMBA_ERR_SHAPE;
+    if (B * H == 0) return TWOMAMBA_OK;
+    if (T > 0 && (!q || !k || !v || !weight || !q_out || !k_out || !v_out)) return TWOMAMBA_ERR_NULL;
+    const Range ins[] = {rng(q, xb), rng(k, xb), rng(v, xb), rng(weight, wb), rng(bias, bb), rng(conv_state_in, cb)};
+    const Range outs[] = {rng(q_out, xb), rng(k_out, xb), rng(v_out, xb), rng(conv_state_out, cb)};
+    for (const Range& o : outs)
+        for (const Range& in : ins)
+            if (overlaps(o, in)) return TWOMAMBA_ERR_ALIAS;
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return TWOMAMBA_ERR_ALIAS;
+    twm::ConvArgs a;
+    memset(&a, 0, sizeof(a));
+    a.B = d->B; a.H = d->H; a.T = d->T; a.d = d->d; a.dtype = d->dtype;
+    a.q = q; a.k = k; a.v = v; a.w = weight; a.b = bias; a.prev = conv_state_in;
+    a.qo = q_out; a.ko = k_out; a.vo = v_out; a.prev_out = conv_state_out; a.stream = stream;
+    return twm::conv2_launch(a);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,131 @@
+// Size-2 causal input convolution in front of the operator ("2Mamba2Furious",
+// §3: a convolution of kernel size 2 along the sequence, without activation;
+// §4: part of Mamba-2S; App. A: decoding caches the one previous query, key and
+// value it needs).  Each channel of q, k and v is convolved separately:
+//     y_t = w1 * x_t + w0 * x_{t-1} + b,   x_{-1} = the cached raw row (or 0).
+//
+// HBM-bound: one thread per (head, token, tensor, 8 channels) loads 2 x 16
+// bytes (bf16) of input and stores 16 bytes; the weights of its 8 channels
+// come through the caches.
+#include "device_common.h"
+#include "internal.h"
+
+namespace twm {
+namespace {
+
+template <typename In> struct Vec8;
+template <> struct Vec8<bf16> {
+    static __device__ __forceinline__ void ld(const bf16* p, float* o) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void st(bf16* p, const float* x) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    static __device__ __forceinline__ void copy(bf16* d, const bf16* s) {
+        *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+    }
+};
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void ld(const float* p, float* o) {
+        const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+    static __device__ __forceinline__ void st(float* p, const float* x) {
+        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    }
+    static __device__ __forceinline__ void copy(float* d, const float* s) {
+        *reinterpret_cast<float4*>(d) = *reinterpret_cast<const float4*>(s);
+        *reinterpret_cast<float4*>(d + 4) = *reinterpret_cast<const float4*>(s + 4);
+    }
+};
+
+template <int D, typename In>
+__global__ void __launch_bounds__(256)
+conv2_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+             const float* __restrict__ w, const float* __restrict__ b, const In* __restrict__ prev,
+             In* __restrict__ qo, In* __restrict__ ko, In* __restrict__ vo, In* __restrict__ prev_out, int H, int T,
+             size_t n) {
+    constexpr int CG = D / 8;
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= n) return;
+    const int cg = (int)(id % CG);
+    size_t r = id / CG;
+    const int which = (int)(r % 3);
+    r /= 3;
+    const int t = (int)(r % T);
+    const size_t bh = r / T;
+    const int h = (int)(bh % H);
+    const In* x = which == 0 ? q : which == 1 ? k : v;
+    In* y = which == 0 ? qo : which == 1 ? ko : vo;
+    const size_t row = (bh * T + t) * D + 8 * cg;
+    float cur[8], bef[8];
+    Vec8<In>::ld(x + row, cur);
+    if (t > 0) {
+        Vec8<In>::ld(x + row - D, bef);
+    } else if (prev) {
+        Vec8<In>::ld(prev + (bh * 3 + which) * D + 8 * cg, bef);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bef[i] = 0.f;
+    }
+    const float* wp = w + ((size_t)(which * H + h) * D + 8 * cg) * 2;
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float2 wi = *reinterpret_cast<const float2*>(wp + 2 * i);
+        o[i] = fmaf(wi.y, cur[i], wi.x * bef[i]);
+        if (b) o[i] += b[(size_t)(which * H + h) * D + 8 * cg + i];
+    }
+    Vec8<In>::st(y + row, o);
+    if (prev_out && t == T - 1) Vec8<In>::copy(prev_out + (bh * 3 + which) * D + 8 * cg, x + row);
+}
+
+// T = 0: the cached row passes through (zeros without one)
+template <int D, typename In>
+__global__ void __launch_bounds__(256)
+conv2_pass_kernel(const In* __restrict__ prev, In* __restrict__ prev_out, size_t n) {
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= n) return;
+    IO<In>::st(prev_out, id, prev ? IO<In>::ld(prev, id) : 0.f);
+}
+
+template <int D, typename In>
+int launch(const ConvArgs& a) {
+    hipStream_t st = (hipStream_t)a.stream;
+    if (a.T == 0) {
+        if (!a.prev_out) return TWOMAMBA_OK;
+        const size_t n = (size_t)a.B * a.H * 3 * D;
+        hipLaunchKernelGGL((conv2_pass_kernel<D, In>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           (const In*)a.prev, (In*)a.prev_out, n);
+    } else {
+        const size_t n = (size_t)a.B * a.H * a.T * 3 * (D / 8);
+        hipLaunchKernelGGL((conv2_kernel<D, In>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           (const In*)a.q, (const In*)a.k, (const In*)a.v, a.w, a.b, (const In*)a.prev, (In*)a.qo,
+                           (In*)a.ko, (In*)a.vo, (In*)a.prev_out, a.H, a.T, n);
+    }
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+}  // namespace
+
+int conv2_launch(const ConvArgs& a) {
+    if ((size_t)a.B * a.H == 0) return TWOMAMBA_OK;
+    const bool bf = a.dtype == TWOMAMBA_BF16;
+    if (a.d == 64) return bf ? launch<64, bf16>(a) : launch<64, float>(a);
+    if (a.d == 16) return bf ? launch<16, bf16>(a) : launch<16, float>(a);
+    return TWOMAMBA_ERR_UNSUPPORTED;
+}
+
+}  // namespace twm

@@ -56,7 +56,26 @@ struct StepArgs {
     float* norm;
     void* out;
     void* stream;
+    // optional size-2 input convolution (twomamba_step_conv): weights
+    // [3][H][d][2], bias [3][H][d] or NULL, cache [B][H][3][d] (input dtype)
+    const float* conv_w;
+    const float* conv_b;
+    void* conv_state;
 };
+
+// size-2 input convolution (conv.hip)
+struct ConvArgs {
+    int B, H, T, d;
+    int dtype;
+    const void *q, *k, *v;
+    const float* w;
+    const float* b;
+    const void* prev;
+    void *qo, *ko, *vo;
+    void* prev_out;
+    void* stream;
+};
+int conv2_launch(const ConvArgs& a);
 
 inline size_t num_pairs(int d) { return (size_t)d * (size_t)(d + 1) / 2; }
 

@@ -12,7 +12,9 @@
 // device copy).  The short tail sweep uses ordinary loads and stores: making
 // it non-temporal as well measured 8 % slower.
 // The readout sum over rows is reduced in a fixed order through LDS, so results
-// are bit-reproducible.
+// are bit-reproducible.  With an input convolution attached (twomamba_step_conv,
+// App. A: one cached previous query, key and value) the three input rows are
+// convolved with the cached ones on the way into LDS.
 #include "device_common.h"
 #include "internal.h"
 
@@ -35,7 +37,8 @@ template <int DK, int DV, typename In>
 __global__ void __launch_bounds__(kStepThreads)
 step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
             const float* __restrict__ z, float* __restrict__ state, float* __restrict__ norm,
-            In* __restrict__ out, float scale, int no_norm) {
+            In* __restrict__ out, float scale, int no_norm, const float* __restrict__ cw,
+            const float* __restrict__ cb, In* __restrict__ cst, int H) {
     constexpr int D = DK * (DK + 1) / 2;
     constexpr int CG = DV / 4;                 // float4 column groups per row
     constexpr int NR = kStepThreads / CG;      // rows processed per sweep
@@ -57,11 +60,23 @@ step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __rest
     const int tid = threadIdx.x;
     const size_t hoff = (size_t)bh;
 
-    if (tid < DK) {
-        s_q[tid] = IO<In>::ld(q, hoff * DK + tid) * scale;
-        s_k[tid] = IO<In>::ld(k, hoff * DK + tid);
+    // inputs, through the size-2 convolution when one is attached: the cached
+    // raw row of the previous token is read and replaced by this token's
+    if (tid < 3 * DK) {
+        const int which = tid / DK, c = tid % DK;
+        const In* src = which == 0 ? q : which == 1 ? k : v;
+        float x = IO<In>::ld(src, hoff * DK + c);
+        if (cw) {
+            const size_t wi = (size_t)(which * H + bh % H) * DK + c;
+            In* cs = cst + (hoff * 3 + which) * DK;
+            const float before = IO<In>::ld(cs, c);
+            IO<In>::st(cs, c, x);
+            x = fmaf(cw[2 * wi + 1], x, cw[2 * wi] * before) + (cb ? cb[wi] : 0.f);
+        }
+        if (which == 0) s_q[c] = x * scale;
+        else if (which == 1) s_k[c] = x;
+        else s_v[c] = x;
     }
-    if (tid < DV) s_v[tid] = IO<In>::ld(v, hoff * DV + tid);
     const float a = expf(decay_log(z[hoff]));
     __syncthreads();
 
@@ -156,7 +171,8 @@ int launch(const StepArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     hipLaunchKernelGGL((step_kernel<DK, DV, In>), dim3(nbh), dim3(kStepThreads), 0, st,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, a.state, a.norm, (In*)a.out,
-                       a.scale, (int)((a.flags & TWOMAMBA_FLAG_NO_NORM) != 0));
+                       a.scale, (int)((a.flags & TWOMAMBA_FLAG_NO_NORM) != 0), a.conv_w, a.conv_b,
+                       (In*)a.conv_state, a.H);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 

@@ -268,3 +268,46 @@ def test_bwd_pointer_checks(lib):
     assert call_bwd(lib, d, ws=13) == EALIAS                                 # workspace == dz
     assert call_bwd(lib, desc(B=0), q=None, k=None, v=None, z=None, out=None, dout=None, dq=None, dk=None,
                     dv=None, dz=None, ws=None, wsb=0) == OK
+
+
+# ---------------------------------------------------------------- input convolution
+def call_conv(lib, dsc, q=1, k=2, v=3, w=4, b=None, si=None, qo=6, ko=7, vo=8, so=None):
+    p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
+    return lib.twomamba_conv2(ctypes.byref(dsc) if dsc is not None else None, p(q), p(k), p(v), p(w), p(b), p(si),
+                              p(qo), p(ko), p(vo), p(so), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ESHAPE), (dict(d=32), EUNSUP), (dict(dtype=5), EDTYPE), (dict(flags=1), EUNSUP),
+    (dict(B=1 << 30, H=1 << 30, T=1 << 30), ESHAPE),
+])
+def test_conv_bad_descriptor(lib, kw, status):
+    a = dict(B=2, H=3, T=50, d=64, dtype=1, flags=0)
+    a.update(kw)
+    assert call_conv(lib, tmb.ConvDesc(**a)) == status
+
+
+def test_conv_pointer_checks(lib):
+    dsc = tmb.ConvDesc(2, 3, 50, 64, 1, 0)
+    assert call_conv(lib, None) == ENULL
+    for field in ("q", "k", "v", "w", "qo", "ko", "vo"):
+        assert call_conv(lib, dsc, **{field: None}) == ENULL
+    assert call_conv(lib, dsc, qo=1) == EALIAS                  # q_out == q
+    assert call_conv(lib, dsc, ko=6) == EALIAS                  # k_out == q_out
+    assert call_conv(lib, dsc, so=4) == EALIAS                  # state out == weight
+    assert call_conv(lib, tmb.ConvDesc(0, 3, 50, 64, 1, 0), q=None, k=None, v=None, w=None, qo=None, ko=None,
+                     vo=None) == OK
+
+
+def test_step_conv_checks(lib):
+    d = tmb.StepDesc(2, 3, 64, 64, 1.0, 1, 0)
+    p = lambda x: None if x is None else fake(x)
+
+    def call(w=10, cs=11, b=None, state=6, d_=d):
+        return lib.twomamba_step_conv(ctypes.byref(d_), p(1), p(2), p(3), p(4), p(w), p(b), p(cs), p(state),
+                                      p(7), p(8), None)
+    assert call(w=None) == ENULL
+    assert call(cs=None) == ENULL
+    assert call(cs=6) == EALIAS                                 # cache over the state
+    assert call(cs=1) == EALIAS                                 # cache over q
+    assert call(d_=tmb.StepDesc(2, 3, 64, 16, 1.0, 1, 0)) == EUNSUP
