@@ -54,6 +54,7 @@ __all__ = [
     "fwd_exp_quadratic", "fwd_exp_quadratic_rows", "fwd_exp_streaming",
     "state_elements", "memory_crossover_tokens",
     "sigmoid", "bwd_quadratic", "bwd_exp_quadratic", "conv2", "step_conv",
+    "fwd_linear_quadratic", "fwd_linear_recurrent", "step_linear", "bwd_linear_quadratic",
 ]
 
 
@@ -495,3 +496,70 @@ def step_conv(q, k, v, z, w, b, conv_state, state, norm_state, scale=1.0, norm=T
         ys.append(conv2(xs[i][:, :, None], w[i], bi, conv_state[:, :, i])[:, :, 0])
     out, S, n = step(ys[0], ys[1], ys[2], z, state, norm_state, scale=scale, norm=norm)
     return out, S, n, np.stack([q, k, v], axis=2)
+
+
+# ----------------------------------------------------------------------------
+# first-order variant (Mamba-2S)  [2M2F §2: first-order linear attention keeps a
+# (dh, dh) state; §3-§4: the Mamba-2S base is output-norm linear attention with
+# the softplus A-mask -- the norm sits outside the attention kernel, so the
+# kernel returns the unnormalised sum]
+#
+#   o_t = sum_{s<=t} L_ts (scale q_t.k_s) v_s,   state S = sum_s L k_s v_s^T.
+# ----------------------------------------------------------------------------
+
+def fwd_linear_quadratic(q, k, v, z, scale=1.0, state_in=None):
+    """First-order output by the masked quadratic form, one query row at a time,
+    plus the decayed initial-state term exp(g_0+...+g_t) scale q_t.S0."""
+    g = decay_log(z)
+    T = q.shape[2]
+    out = np.zeros(v.shape)
+    for t in range(T):
+        L = np.exp(_row_log_mask(g[:, :, :t + 1]))
+        w = L * scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], k[:, :, :t + 1])
+        out[:, :, t] = np.einsum("bhs,bhsc->bhc", w, v[:, :, :t + 1])
+        if state_in is not None:
+            out[:, :, t] += np.exp(g[:, :, :t + 1].sum(axis=-1))[..., None] * scale * np.einsum(
+                "bhd,bhdc->bhc", q[:, :, t], state_in)
+    return out
+
+
+def step_linear(q, k, v, z, state, scale=1.0):
+    """One first-order decode step: S <- e^g S + k v^T, o = scale q.S."""
+    a = np.exp(decay_log(z))
+    S = a[..., None, None] * state + k[..., :, None] * v[..., None, :]
+    return scale * np.einsum("bhd,bhdc->bhc", q, S), S
+
+
+def fwd_linear_recurrent(q, k, v, z, scale=1.0, state_in=None):
+    """First-order recurrence token by token; returns (out, final state [B,H,dk,dv])."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if state_in is None else state_in.copy()
+    out = np.zeros(v.shape)
+    for t in range(T):
+        out[:, :, t], S = step_linear(q[:, :, t], k[:, :, t], v[:, :, t], z[:, :, t], S, scale)
+    return out, S
+
+
+def bwd_linear_quadratic(q, k, v, z, dout, scale=1.0):
+    """Gradients (dq, dk, dv, dz) of the first-order output (no initial state).
+
+    Row t: w_s = L_ts scale q_t.k_s, o_t = sum w_s v_s; dL/dw_s = dout_t.v_s,
+    dv_s += w_s dout_t, dq_t += scale sum_s dL/dw_s L_ts k_s,
+    dk_s += scale dL/dw_s L_ts q_t, dL/dlambda_ts = dL/dw_s w_s.
+    """
+    g = decay_log(z)
+    T = q.shape[2]
+    dq, dk, dv, dg = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape), np.zeros(z.shape)
+    for t in range(T):
+        K, V = k[:, :, :t + 1], v[:, :, :t + 1]
+        L = np.exp(_row_log_mask(g[:, :, :t + 1]))
+        w = L * scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], K)
+        do = dout[:, :, t]
+        dw = np.einsum("bhsc,bhc->bhs", V, do)
+        dv[:, :, :t + 1] += w[..., None] * do[:, :, None, :]
+        da = dw * L * scale
+        dq[:, :, t] += np.einsum("bhs,bhsd->bhd", da, K)
+        dk[:, :, :t + 1] += da[..., None] * q[:, :, t][:, :, None, :]
+        _add_mask_grad(dg, dw * w, t)
+    return dq, dk, dv, -sigmoid(z) * dg
