@@ -72,7 +72,11 @@ typedef enum { TWOMAMBA_F32 = 0, TWOMAMBA_BF16 = 1 } twomamba_dtype;   /* dtype 
 
 typedef enum {
     TWOMAMBA_SQ = 0,   /* 2Mamba: squared score, normalised by the sum of weights  [2M2F §5] */
-    TWOMAMBA_EXP = 1   /* 2Mamba-E: exponentiated score (softmax) with the A-mask   [2M2F §6] */
+    TWOMAMBA_EXP = 1,  /* 2Mamba-E: exponentiated score (softmax) with the A-mask   [2M2F §6] */
+    TWOMAMBA_LIN = 2   /* first order (Mamba-2S): o_t = sum_s L_ts (scale q_t.k_s) v_s, not
+                          normalised (the output norm sits outside the kernel); the state
+                          is the dk x dv matrix sum_s L k_s v_s^T, [B][H][dk][dv] fp32, with
+                          no normaliser  [2M2F §2, §3-§4] */
 } twomamba_variant;
 
 enum {
@@ -82,7 +86,11 @@ enum {
     TWOMAMBA_FLAG_NO_NORM = 1u,
     /* Force the plain fp32 reference kernels instead of the MFMA kernels
        (testing aid; same results within fp32 rounding). */
-    TWOMAMBA_FLAG_REFERENCE_KERNELS = 2u
+    TWOMAMBA_FLAG_REFERENCE_KERNELS = 2u,
+    /* twomamba_step / twomamba_step_conv: the first-order (TWOMAMBA_LIN) step,
+       S <- e^g S + k v^T, o = scale q.S, on a [B][H][dk][dv] state; norm must
+       be NULL. */
+    TWOMAMBA_FLAG_FIRST_ORDER = 4u
 };
 
 typedef struct {
@@ -103,7 +111,7 @@ typedef struct {
     int dk, dv;         /* head dims; supported: dk == dv, 16 or 64                   */
     float scale;
     int dtype;          /* dtype of q, k, v and out; the state is always fp32         */
-    unsigned flags;     /* TWOMAMBA_FLAG_NO_NORM                                       */
+    unsigned flags;     /* TWOMAMBA_FLAG_NO_NORM, TWOMAMBA_FLAG_FIRST_ORDER            */
 } twomamba_step_desc;
 
 /* ABI version of the loaded library (TWOMAMBA_ABI_VERSION it was built with). */
@@ -133,7 +141,10 @@ int twomamba_fwd_workspace_size(const twomamba_fwd_desc* desc, size_t* bytes);
  *                                                 256-byte aligned; contents undefined after
  *
  * TWOMAMBA_EXP takes no state pointers (it needs a KV cache, [2M2F §1, §6]):
- * passing any returns TWOMAMBA_ERR_UNSUPPORTED.
+ * passing any returns TWOMAMBA_ERR_UNSUPPORTED.  TWOMAMBA_LIN takes
+ * state_in / state_out of [B][H][dk][dv] (each optional on its own) and no
+ * normaliser (norm_in and norm_out must be NULL); TWOMAMBA_FLAG_NO_NORM does
+ * not change it.
  */
 int twomamba_fwd(const twomamba_fwd_desc* desc,
                  const void* q, const void* k, const void* v, const float* z,

@@ -19,17 +19,19 @@ import torch
 
 __all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "step", "library_path",
            "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd", "conv2", "step_conv",
-           "TwoMambaError", "SQ", "EXP", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "num_pairs"]
+           "TwoMambaError", "SQ", "EXP", "LIN", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "FLAG_FIRST_ORDER",
+           "num_pairs"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libtwomamba.so")
 
-SQ, EXP = 0, 1
+SQ, EXP, LIN = 0, 1, 2
 F32, BF16 = 0, 1
 FLAG_NO_NORM = 1
 FLAG_REFERENCE_KERNELS = 2
+FLAG_FIRST_ORDER = 4
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
-_VARIANT = {"sq": SQ, "exp": EXP}
+_VARIANT = {"sq": SQ, "exp": EXP, "lin": LIN}
 
 
 class TwoMambaError(RuntimeError):
@@ -177,15 +179,18 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
     _check(k, (B, H, T, dk), q.dtype, "k")
     _check(v, (B, H, T, dv), q.dtype, "v")
     _check(z, (B, H, T), torch.float32, "z")
-    D = num_pairs(dk)
+    lin = desc.variant == LIN     # first order: dk x dv state, no normaliser
+    D = dk if lin else num_pairs(dk)
     if state_in is not None:
         _check(state_in, (B, H, D, dv), torch.float32, "state_in")
-        _check(norm_in, (B, H, D), torch.float32, "norm_in")
+        if not lin:
+            _check(norm_in, (B, H, D), torch.float32, "norm_in")
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if want_state and state_out is None:
         state_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
-        norm_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+        if not lin:
+            norm_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     nbytes = workspace_size(desc)
     if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -209,20 +214,23 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
     return out
 
 
-def step(q, k, v, z, state, norm, *, scale=1.0, no_norm=False, out=None):
-    """One decode step; state [B,H,D,dv] and norm [B,H,D] (fp32) are updated in place."""
+def step(q, k, v, z, state, norm, *, scale=1.0, no_norm=False, first_order=False, out=None):
+    """One decode step; state [B,H,D,dv] and norm [B,H,D] (fp32) are updated in
+    place.  first_order: the Mamba-2S step on a [B,H,dk,dv] state, norm None."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     _check(q, (B, H, dk), q.dtype, "q")
     _check(k, (B, H, dk), q.dtype, "k")
     _check(v, (B, H, dv), q.dtype, "v")
     _check(z, (B, H), torch.float32, "z")
-    D = num_pairs(dk)
+    D = dk if first_order else num_pairs(dk)
     _check(state, (B, H, D, dv), torch.float32, "state")
-    _check(norm, (B, H, D), torch.float32, "norm")
+    if not first_order:
+        _check(norm, (B, H, D), torch.float32, "norm")
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
-    desc = StepDesc(B, H, dk, dv, scale, _DT[q.dtype], FLAG_NO_NORM if no_norm else 0)
+    flags = (FLAG_NO_NORM if no_norm else 0) | (FLAG_FIRST_ORDER if first_order else 0)
+    desc = StepDesc(B, H, dk, dv, scale, _DT[q.dtype], flags)
     s = load().twomamba_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state), _ptr(norm),
                              _ptr(out), _stream())
     if s != 0:
@@ -369,9 +377,10 @@ def conv2(q, k, v, weight, bias=None, state_in=None, *, outs=None, want_state=Fa
     return (*outs, state_out) if (want_state or state_out is not None) else tuple(outs)
 
 
-def step_conv(q, k, v, z, weight, bias, conv_state, state, norm, *, scale=1.0, no_norm=False, out=None):
+def step_conv(q, k, v, z, weight, bias, conv_state, state, norm, *, scale=1.0, no_norm=False, first_order=False,
+              out=None):
     """Decode step with the size-2 input convolution; conv_state, state and
-    norm are updated in place."""
+    norm are updated in place (first_order: [B,H,d,d] state, norm None)."""
     B, H, d = q.shape
     _check(k, (B, H, d), q.dtype, "k")
     _check(v, (B, H, d), q.dtype, "v")
@@ -380,12 +389,14 @@ def step_conv(q, k, v, z, weight, bias, conv_state, state, norm, *, scale=1.0, n
     if bias is not None:
         _check(bias, (3, H, d), torch.float32, "bias")
     _check(conv_state, (B, H, 3, d), q.dtype, "conv_state")
-    D = num_pairs(d)
+    D = d if first_order else num_pairs(d)
     _check(state, (B, H, D, d), torch.float32, "state")
-    _check(norm, (B, H, D), torch.float32, "norm")
+    if not first_order:
+        _check(norm, (B, H, D), torch.float32, "norm")
     if out is None:
         out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
-    desc = StepDesc(B, H, d, d, scale, _DT[q.dtype], FLAG_NO_NORM if no_norm else 0)
+    flags = (FLAG_NO_NORM if no_norm else 0) | (FLAG_FIRST_ORDER if first_order else 0)
+    desc = StepDesc(B, H, d, d, scale, _DT[q.dtype], flags)
     s = load().twomamba_step_conv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(weight),
                                   _ptr(bias), _ptr(conv_state), _ptr(state), _ptr(norm), _ptr(out), _stream())
     if s != 0:

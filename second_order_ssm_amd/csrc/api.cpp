@@ -44,7 +44,8 @@ int check_desc(const twomamba_fwd_desc* d, size_t* qk_bytes, size_t* v_bytes, si
                size_t* st_bytes, size_t* nm_bytes) {
     if (!d) return TWOMAMBA_ERR_NULL;
     if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk <= 0 || d->dv <= 0) return TWOMAMBA_ERR_SHAPE;
-    if (d->variant != TWOMAMBA_SQ && d->variant != TWOMAMBA_EXP) return TWOMAMBA_ERR_DTYPE;
+    if (d->variant != TWOMAMBA_SQ && d->variant != TWOMAMBA_EXP && d->variant != TWOMAMBA_LIN)
+        return TWOMAMBA_ERR_DTYPE;
     if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
     if (d->flags & ~(unsigned)(TWOMAMBA_FLAG_NO_NORM | TWOMAMBA_FLAG_REFERENCE_KERNELS)) return TWOMAMBA_ERR_UNSUPPORTED;
     if (d->variant == TWOMAMBA_EXP && (d->flags & TWOMAMBA_FLAG_NO_NORM)) return TWOMAMBA_ERR_UNSUPPORTED;
@@ -54,7 +55,8 @@ int check_desc(const twomamba_fwd_desc* d, size_t* qk_bytes, size_t* v_bytes, si
     if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
         return TWOMAMBA_ERR_UNSUPPORTED;
     const size_t es = d->dtype == TWOMAMBA_BF16 ? 2 : 4;
-    const size_t B = d->B, H = d->H, T = d->T, D = twm::num_pairs(d->dk);
+    const size_t B = d->B, H = d->H, T = d->T;
+    const size_t D = d->variant == TWOMAMBA_LIN ? (size_t)d->dk : twm::num_pairs(d->dk);
     if (!prod(qk_bytes, {B, H, T, (size_t)d->dk, es}) || !prod(v_bytes, {B, H, T, (size_t)d->dv, es}) ||
         !prod(z_bytes, {B, H, T, 4}) || !prod(st_bytes, {B, H, D, (size_t)d->dv, 4}) || !prod(nm_bytes, {B, H, D, 4}))
         return TWOMAMBA_ERR_SHAPE;
@@ -73,10 +75,15 @@ int plan(const twomamba_fwd_desc* d, FwdArgs* a) {
     return TWOMAMBA_OK;
 }
 
-enum Path { REF, MFMA };
+enum Path { REF, MFMA, LINP };
 
 int choose(FwdArgs* a, Path* path) {
     const bool force_ref = (a->flags & TWOMAMBA_FLAG_REFERENCE_KERNELS) != 0;
+    if (a->variant == TWOMAMBA_LIN) {
+        a->chunk = 64;
+        *path = LINP;
+        return TWOMAMBA_OK;
+    }
     if (a->variant == TWOMAMBA_EXP) {
         a->chunk = 0;
         *path = (!force_ref && twm::mfma_exp_supported(*a)) ? MFMA : REF;
@@ -99,6 +106,7 @@ int choose(FwdArgs* a, Path* path) {
 
 size_t workspace_for(const FwdArgs& a, Path path) {
     if (a.variant == TWOMAMBA_EXP) return 0;
+    if (path == LINP) return twm::lin_workspace(a);
     return path == MFMA ? twm::mfma_sq_workspace(a) : twm::ref_sq_workspace(a);
 }
 
@@ -144,10 +152,11 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     int s = check_desc(d, &qkb, &vb, &zb, &sb, &nb);
     if (s != TWOMAMBA_OK) return s;
     const bool any = qkb != 0;   // B*H*T > 0
-    const bool sq = d->variant == TWOMAMBA_SQ;
-    if (!sq && (state_in || norm_in || state_out || norm_out)) return TWOMAMBA_ERR_UNSUPPORTED;
-    if ((state_in == nullptr) != (norm_in == nullptr)) return TWOMAMBA_ERR_NULL;
-    if ((state_out == nullptr) != (norm_out == nullptr)) return TWOMAMBA_ERR_NULL;
+    const bool sq = d->variant == TWOMAMBA_SQ, lin = d->variant == TWOMAMBA_LIN;
+    if (!sq && !lin && (state_in || norm_in || state_out || norm_out)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (lin && (norm_in || norm_out)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (sq && (state_in == nullptr) != (norm_in == nullptr)) return TWOMAMBA_ERR_NULL;
+    if (sq && (state_out == nullptr) != (norm_out == nullptr)) return TWOMAMBA_ERR_NULL;
     if (any && (!q || !k || !v || !z || !out)) return TWOMAMBA_ERR_NULL;
 
     // aliasing: out and the state outputs may not touch any input; the state
@@ -181,6 +190,7 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     a.out = out; a.state_out = state_out; a.norm_out = norm_out;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
     a.timer = timer;
+    if (path == LINP) return twm::lin_fwd(a);
     if (a.variant == TWOMAMBA_EXP) return path == MFMA ? twm::mfma_exp_fwd(a) : twm::ref_exp_fwd(a);
     return path == MFMA ? twm::mfma_sq_fwd(a) : twm::ref_sq_fwd(a);
 }
@@ -213,19 +223,21 @@ static int step_impl(const twomamba_step_desc* d, const void* q, const void* k, 
     if (!d) return TWOMAMBA_ERR_NULL;
     if (d->B < 0 || d->H < 0 || d->dk <= 0 || d->dv <= 0) return TWOMAMBA_ERR_SHAPE;
     if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
-    if (d->flags & ~(unsigned)TWOMAMBA_FLAG_NO_NORM) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (d->flags & ~(unsigned)(TWOMAMBA_FLAG_NO_NORM | TWOMAMBA_FLAG_FIRST_ORDER)) return TWOMAMBA_ERR_UNSUPPORTED;
     if (!supported_dims(d->dk, d->dv)) return TWOMAMBA_ERR_UNSUPPORTED;
     if (!(d->scale == d->scale) || d->scale == __builtin_inff() || d->scale == -__builtin_inff())
         return TWOMAMBA_ERR_SHAPE;
+    const bool first = (d->flags & TWOMAMBA_FLAG_FIRST_ORDER) != 0;
     const size_t es = d->dtype == TWOMAMBA_BF16 ? 2 : 4;
-    const size_t B = d->B, H = d->H, D = twm::num_pairs(d->dk);
+    const size_t B = d->B, H = d->H, D = first ? (size_t)d->dk : twm::num_pairs(d->dk);
     size_t qkb, vb, zb, sb, nb;
     if (!prod(&qkb, {B, H, (size_t)d->dk, es}) || !prod(&vb, {B, H, (size_t)d->dv, es}) || !prod(&zb, {B, H, 4}) ||
         !prod(&sb, {B, H, D, (size_t)d->dv, 4}) || !prod(&nb, {B, H, D, 4}))
         return TWOMAMBA_ERR_SHAPE;
     if (B * H > 0x7fffffffu) return TWOMAMBA_ERR_SHAPE;
     if (B * H == 0) return TWOMAMBA_OK;
-    if (!q || !k || !v || !z || !state || !norm || !out) return TWOMAMBA_ERR_NULL;
+    if (first && norm) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !z || !state || (!first && !norm) || !out) return TWOMAMBA_ERR_NULL;
     const Range rq = rng(q, qkb), rk = rng(k, qkb), rv = rng(v, vb), rz = rng(z, zb);
     const Range rs = rng(state, sb), rn = rng(norm, nb), ro = rng(out, vb);
     for (const Range& w : {rs, rn, ro})
@@ -280,7 +292,8 @@ int twomamba_conv2(const twomamba_conv_desc* d, const void* q, const void* k, co
     const size_t B = d->B, H = d->H, T = d->T, D = d->d;
     size_t xb, cb, wb, bb, g;
     if (!prod(&xb, {B, H, T, D, es}) || !prod(&cb, {B, H, 3, D, es}) || !prod(&wb, {3, H, D, 2, 4}) ||
-        !prod(&bb, {3, H, D, 4}) || !prod(&g, {B, H, T, 3, D / 8}) || (g + 255) / 256 > 0x7fffffffu)
+        !prod(&bb, {3, H, D, 4}) || T * (D / 8) + 255 > 0x7fffffffu ||
+        !prod(&g, {B, H, (T * (D / 8) + 255) / 256}) || g > 0x7fffffffu)
         return TWOMAMBA_ERR_SHAPE;
     if (B * H == 0) return TWOMAMBA_OK;
     if (T > 0 && (!q || !k || !v || !weight || !q_out || !k_out || !v_out)) return TWOMAMBA_ERR_NULL;

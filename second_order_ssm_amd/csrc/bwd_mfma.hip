@@ -12,6 +12,9 @@
 //   2Mamba-E: P = 2^(log2(e) scale x + lambda2 - lse2_t), dS = P (dP - D_t);
 //             dq_t = scale sum_s dS k_s, dk_s = scale sum_t dS q_t,
 //             dL/dlambda_ts = dS;
+//   first order: P = scale 2^lambda2 x, dS = 2^lambda2 dP; dq_t = scale
+//             sum_s dS k_s, dk_s = scale sum_t dS q_t, dL/dlambda_ts = scale x dS
+//             (no row statistic, so the first sweep is skipped);
 // and dv_s = sum_t P dout_t.  D_t = dout_t.o_t comes from the preparation
 // kernel together with the fp64 running sums G.
 //
@@ -54,6 +57,7 @@ constexpr int kTile = 64;              // keys or queries per loop step
 constexpr int kLS = 72;                // LDS row stride in bf16 (144 B)
 constexpr int kMinBlocks = 3;          // workgroups per CU the register budget is sized for
 constexpr float kLog2e = 1.4426950408889634f;
+enum { kSq = 0, kExpV = 1, kLin = 2 };   // second order, exponentiated, first order
 
 __device__ __forceinline__ f4 mfma(b8 a, b8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -70,6 +74,22 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ b8 to_b(const float (&x)[8]) {
     return as_b8(make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])));
 }
+// Workgroups are dealt to the 8 XCDs round-robin by index, block i to XCD
+// i mod 8.  When the head count is a multiple of 8 the (head, block) pair of
+// index i is chosen so that every block of a head runs on one XCD, where that
+// head's tiles then stay in one L2: XCD x takes heads x, x + 8, ... in turn.
+constexpr int kXcd = 8;
+__device__ __forceinline__ void xcd_map(int i, int nb, bool by_xcd, int& bh, int& blk) {
+    if (by_xcd) {
+        const int x = i % kXcd, j = i / kXcd;
+        bh = x + kXcd * (j / nb);
+        blk = j % nb;
+    } else {
+        bh = i / nb;
+        blk = i % nb;
+    }
+}
+
 __device__ __forceinline__ float xor_sum(float x) {   // over the four lane groups g
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
@@ -140,15 +160,16 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b) {   // 8 bf16 x 8 bf16, 
     return r;
 }
 
-template <bool kExp>
+template <int kVar>
 __global__ void __launch_bounds__(kThreads, kMinBlocks)
 bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const bf16* __restrict__ out, const bf16* __restrict__ dout, const double* __restrict__ G,
              float* __restrict__ Dt, float* __restrict__ stat, float* __restrict__ rowsum, bf16* __restrict__ dq,
-             int T, int nqb, float scale, int norm, int use_d) {
+             int T, int nqb, float scale, int norm, int use_d, int by_xcd) {
     __shared__ __attribute__((aligned(16))) QSmem sm;
-    const int bh = blockIdx.x / nqb;
-    const int qb = nqb - 1 - blockIdx.x % nqb;     // longest rows first
+    int bh, blk;
+    xcd_map(blockIdx.x, nqb, by_xcd, bh, blk);
+    const int qb = nqb - 1 - blk;                  // longest rows first
     const int q0 = qb * kBlk;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
     const size_t base = (size_t)bh * T;
@@ -215,7 +236,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool masked = kDiag && s0 + 16 * st + 4 * g + i > t;
-                    if (kExp) {
+                    if (kVar == kExpV) {
                         float yy = fmaf(S[u][i], sl2, av[i] - b2);
                         yy = masked ? -INFINITY : yy;
                         y[4 * u + i] = yy;
@@ -227,7 +248,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                     }
                 }
             }
-            if (kExp) {
+            if (kVar == kExpV) {
                 if (mx > m) {
                     l *= fexp2(m - mx);
                     m = mx;
@@ -238,18 +259,23 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             }
         }
     };
-    for (int kt = 0; kt < qb; ++kt) {   // key tiles wholly before the queries
-        const int cur = kt & 1, s0 = kt * kTile;
-        fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
-        sweep1(kt, std::false_type{});
-        store(sk, sm.K[cur ^ 1], tid);
-        stage_a(cur ^ 1, s0 + kTile);
+    if (kVar != kLin) {   // the first order has no row statistic
+        for (int kt = 0; kt < qb; ++kt) {   // key tiles wholly before the queries
+            const int cur = kt & 1, s0 = kt * kTile;
+            fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
+            sweep1(kt, std::false_type{});
+            store(sk, sm.K[cur ^ 1], tid);
+            stage_a(cur ^ 1, s0 + kTile);
+            __syncthreads();
+        }
+        sweep1(qb, std::true_type{});
         __syncthreads();
     }
-    sweep1(qb, std::true_type{});
-    __syncthreads();
     float st_v, cq;   // row statistic; cq: b2 + lse2 (2Mamba-E) or -D / den (2Mamba)
-    if (kExp) {
+    if (kVar == kLin) {
+        st_v = 1.f;
+        cq = 0.f;
+    } else if (kVar == kExpV) {
         // combine the four lane groups' (m, l)
         float M = fmaxf(m, __shfl_xor(m, 16));
         M = fmaxf(M, __shfl_xor(M, 32));
@@ -302,14 +328,17 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                     const int s = s0 + 16 * st + 4 * g + i;
                     const float x = S[u][i];
                     float d, Mv;
-                    if (kExp) {
+                    if (kVar == kExpV) {
                         const float p = fexp2(fmaf(x, sl2, av[i] - cq));
                         d = p * (P[u][i] - Dq);
                         Mv = d;
-                    } else {
+                    } else if (kVar == kSq) {
                         const float uu = fexp2(av[i] - b2) * x;
                         const float dw = fmaf(P[u][i], st_v, cq);
                         d = uu * dw;
+                        Mv = x * d;
+                    } else {
+                        d = fexp2(av[i] - b2) * P[u][i];
                         Mv = x * d;
                     }
                     if (kDiag) {
@@ -340,7 +369,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     sweep2(qb, std::true_type{});
     rs = xor_sum(rs);
     if (tv) {
-        const float f = kExp ? scale : 2.f * scale * scale;
+        const float f = kVar == kSq ? 2.f * scale * scale : scale;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             uint2 o;
@@ -351,7 +380,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         if (g == 0) {
             stat[base + t] = st_v;
             Dt[base + t] = Dq;
-            rowsum[base + t] = kExp ? rs : rs * scale * scale;
+            rowsum[base + t] = kVar == kExpV ? rs : kVar == kSq ? rs * scale * scale : rs * scale;
         }
     }
 }
@@ -365,15 +394,15 @@ struct KVSmem {
     float C[2][kTile];      // 2Mamba: -D_t/den_t; 2Mamba-E: D_t
 };
 
-template <bool kExp>
+template <int kVar>
 __global__ void __launch_bounds__(kThreads, kMinBlocks)
 bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const bf16* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
               const float* __restrict__ stat, float* __restrict__ colsum, bf16* __restrict__ dk,
-              bf16* __restrict__ dv, int T, int nkb, float scale) {
+              bf16* __restrict__ dv, int T, int nkb, float scale, int by_xcd) {
     __shared__ __attribute__((aligned(16))) KVSmem sm;
-    const int bh = blockIdx.x / nkb;
-    const int kb = blockIdx.x % nkb;               // earliest keys (longest columns) first
+    int bh, kb;
+    xcd_map(blockIdx.x, nkb, by_xcd, bh, kb);     // earliest keys (longest columns) first
     const int k0 = kb * kBlk;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
     const size_t base = (size_t)bh * T;
@@ -393,7 +422,8 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             if (t < T) {
                 b = (float)(G[base + t] - gref) * kLog2e;
                 const float st = stat[base + t], d = Dt[base + t];
-                if (kExp) {
+                if (kVar == kLin) {
+                } else if (kVar == kExpV) {
                     b += st;
                     c = d;
                 } else {
@@ -445,7 +475,7 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
                 const float4 b4 = *reinterpret_cast<const float4*>(&sm.B[cur][16 * tt + 4 * g]);
                 const float4 c4 = *reinterpret_cast<const float4*>(&sm.C[cur][16 * tt + 4 * g]);
                 float4 r4 = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (!kExp) r4 = *reinterpret_cast<const float4*>(&sm.R[cur][16 * tt + 4 * g]);
+                if (kVar == kSq) r4 = *reinterpret_cast<const float4*>(&sm.R[cur][16 * tt + 4 * g]);
                 const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
                 const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
@@ -453,15 +483,20 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
                     const int t = t0 + 16 * tt + 4 * g + i;
                     const float x = S[u][i];
                     float pp, d, Mv;
-                    if (kExp) {
+                    if (kVar == kExpV) {
                         pp = fexp2(fmaf(x, sl2, a2 - bv[i]));
                         d = pp * (DP[u][i] - cv[i]);
                         Mv = d;
-                    } else {
+                    } else if (kVar == kSq) {
                         const float uu = fexp2(a2 - bv[i]) * x;
                         pp = uu * x * rv[i];
                         const float dw = fmaf(DP[u][i], rv[i], cv[i]);
                         d = uu * dw;
+                        Mv = x * d;
+                    } else {
+                        const float L = fexp2(a2 - bv[i]);
+                        pp = L * x;
+                        d = L * DP[u][i];
                         Mv = x * d;
                     }
                     if (kDiag) {
@@ -503,8 +538,8 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     for (int it = 1; it < nqt; ++it) step(it, std::false_type{});
     cs = xor_sum(cs);
     if (sv_ok) {
-        const float fk = kExp ? scale : 2.f * scale * scale;
-        const float fv = kExp ? 1.f : scale * scale;
+        const float fk = kVar == kSq ? 2.f * scale * scale : scale;
+        const float fv = kVar == kSq ? scale * scale : kVar == kLin ? scale : 1.f;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             uint2 a, b;
@@ -515,25 +550,26 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             *reinterpret_cast<uint2*>(dk + (base + s) * kD + 16 * dt + 4 * g) = a;
             *reinterpret_cast<uint2*>(dv + (base + s) * kD + 16 * dt + 4 * g) = b;
         }
-        if (g == 0) colsum[base + s] = kExp ? cs : cs * scale * scale;
+        if (g == 0) colsum[base + s] = kVar == kExpV ? cs : kVar == kSq ? cs * scale * scale : cs * scale;
     }
 }
 
-template <bool kExp>
+template <int kVar>
 int launch(const BwdArgs& a, const BwdScratch& s) {
     hipStream_t st = (hipStream_t)a.stream;
     const int nb = (a.T + kBlk - 1) / kBlk;
     const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
-    const int use_d = kExp || norm;
+    const int use_d = kVar == kExpV || (kVar == kSq && norm);
+    const int by_xcd = (a.B * a.H) % kXcd == 0;
     ktimer_begin(a.timer, "bwd_q", a.stream);
-    hipLaunchKernelGGL((bwd_q_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
+    hipLaunchKernelGGL((bwd_q_kernel<kVar>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.out, (const bf16*)a.dout, s.G, s.Dt,
-                       s.stat, s.rowsum, (bf16*)a.gq, a.T, nb, a.scale, norm, use_d);
+                       s.stat, s.rowsum, (bf16*)a.gq, a.T, nb, a.scale, norm, use_d, by_xcd);
     ktimer_end(a.timer, a.stream);
     ktimer_begin(a.timer, "bwd_kv", a.stream);
-    hipLaunchKernelGGL((bwd_kv_kernel<kExp>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
+    hipLaunchKernelGGL((bwd_kv_kernel<kVar>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, s.G, s.Dt, s.stat, s.colsum,
-                       (bf16*)a.gk, (bf16*)a.gv, a.T, nb, a.scale);
+                       (bf16*)a.gk, (bf16*)a.gv, a.T, nb, a.scale, by_xcd);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
@@ -549,7 +585,8 @@ int mfma_bwd(const BwdArgs& a) {
     const BwdScratch s = bwd_scratch(a);
     int r = bwd_prep_launch(a, s, false);   // G only: D_t comes from the query-major kernel
     if (r != TWOMAMBA_OK) return r;
-    r = a.variant == TWOMAMBA_EXP ? launch<true>(a, s) : launch<false>(a, s);
+    r = a.variant == TWOMAMBA_EXP ? launch<kExpV>(a, s) : a.variant == TWOMAMBA_LIN ? launch<kLin>(a, s)
+                                                                                    : launch<kSq>(a, s);
     if (r != TWOMAMBA_OK) return r;
     return bwd_dz_launch(a, s);
 }

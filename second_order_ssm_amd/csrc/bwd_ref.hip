@@ -10,7 +10,8 @@
 //   2Mamba:   w = e^lambda x^2, P = w / den_t, dw = (dP - D_t) / den_t,
 //             dS = 2 e^lambda x dw (the derivative by q_t.k_s / scale), M = dw w
 //             (without normalisation: 1/den_t = 1 and D_t = 0);
-//   2Mamba-E: P = exp(x + lambda - lse_t), dS = P (dP - D_t), M = dS.
+//   2Mamba-E: P = exp(x + lambda - lse_t), dS = P (dP - D_t), M = dS;
+//   first order: P = e^lambda x, dS = e^lambda dP, M = dP P (no row statistic).
 // Then dv_s = sum_t P dout_t, dq_t = scale sum_s dS k_s, dk_s = scale sum_t dS q_t,
 // and M (the gradient by lambda_ts) reaches g_r for s < r <= t:
 //   dg_r = sum_{t >= r, s < r} M_ts = sum_{r' < r} (colsum_r' - rowsum_r'),
@@ -23,6 +24,8 @@
 //  * bwd_ref_kv_kernel: two threads per key (half of the dims each); a pass
 //    over the queries t >= s for dk, dv and colsum.
 //  * bwd_dz_kernel: the scan of colsum - rowsum and dz (one workgroup per head).
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -30,6 +33,7 @@ namespace twm {
 namespace {
 
 constexpr int kTile = 64;
+enum { kSq = 0, kExpV = 1, kLin = 2 };   // second order, exponentiated, first order
 
 __device__ __forceinline__ double softplus_d(float zf) {
     const double z = zf;
@@ -95,7 +99,7 @@ bwd_prep_kernel(const float* __restrict__ z, const In* __restrict__ out, const I
 }
 
 // one thread per query row
-template <int D, typename In, bool kExp>
+template <int D, typename In, int kVar>
 __global__ void __launch_bounds__(kTile)
 bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
                  const In* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
@@ -134,9 +138,9 @@ bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* _
         return Lk;
     };
 
-    // pass 1: row statistic
+    // pass 1: row statistic (none for the first order)
     float den = 0.f, m = -INFINITY, l = 0.f;
-    for (int kt = 0; kt <= qt; ++kt) {
+    for (int kt = 0; kt <= (kVar == kLin ? -1 : qt); ++kt) {
         const int Lk = stage(kt);
         const int s0 = kt * kTile;
         if (!active) continue;
@@ -146,19 +150,20 @@ bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* _
             for (int i = 0; i < D; ++i) x = fmaf(qv[i], s_k[sl][i], x);
             x *= scale;
             const float lam = (float)(s_g[sl] - Gt);
-            if (kExp) {
+            if (kVar == kExpV) {
                 const float y = x + lam;
                 const float mn = fmaxf(m, y);
                 l = l * expf(m - mn) + expf(y - mn);
                 m = mn;
-            } else {
+            } else if (kVar == kSq) {
                 den = fmaf(expf(lam) * x, x, den);
             }
         }
     }
     float st;
-    if (kExp) st = m + logf(l);
-    else st = norm ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
+    if (kVar == kExpV) st = m + logf(l);
+    else if (kVar == kSq) st = norm ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
+    else st = 1.f;
 
     // pass 2: dq and rowsum
     float rs = 0.f;
@@ -176,15 +181,19 @@ bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* _
             x *= scale;
             const float lam = (float)(s_g[sl] - Gt);
             float ds, Mv;
-            if (kExp) {
+            if (kVar == kExpV) {
                 const float p = expf(x + lam - st);
                 ds = p * (dp - Dq);
                 Mv = ds;
-            } else {
+            } else if (kVar == kSq) {
                 const float L = expf(lam);
                 const float dw = (dp - Dq) * st;
                 ds = 2.f * L * x * dw;
                 Mv = dw * L * x * x;
+            } else {
+                const float L = expf(lam);
+                ds = L * dp;
+                Mv = dp * L * x;
             }
             if (s0 + sl < t) rs += Mv;
             const float c = scale * ds;
@@ -201,7 +210,7 @@ bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* _
 }
 
 // two threads per key: thread 2j+h holds dims [h D/2, (h+1) D/2) of key j
-template <int D, typename In, bool kExp>
+template <int D, typename In, int kVar>
 __global__ void __launch_bounds__(2 * kTile)
 bwd_ref_kv_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
                   const In* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
@@ -252,17 +261,22 @@ bwd_ref_kv_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* 
             const float dp = dph + __shfl_xor(dph, 1);
             const float lam = (float)(Gs - s_g[tl]);
             float p, ds, Mv;
-            if (kExp) {
+            if (kVar == kExpV) {
                 p = expf(x + lam - s_st[tl]);
                 ds = p * (dp - s_D[tl]);
                 Mv = ds;
-            } else {
+            } else if (kVar == kSq) {
                 const float L = expf(lam);
                 const float w = L * x * x;
                 p = w * s_st[tl];
                 const float dw = (dp - s_D[tl]) * s_st[tl];
                 ds = 2.f * L * x * dw;
                 Mv = dw * w;
+            } else {
+                const float L = expf(lam);
+                p = L * x;
+                ds = L * dp;
+                Mv = dp * p;
             }
             if (t0 + tl > s) cs += Mv;
             const float c = scale * ds;
@@ -338,7 +352,8 @@ BwdScratch bwd_scratch(const BwdArgs& a) {
 template <int D, typename In>
 static int launch_prep(const BwdArgs& a, const BwdScratch& s, bool with_d) {
     hipStream_t st = (hipStream_t)a.stream;
-    const int use_d = (a.variant == TWOMAMBA_EXP) || !(a.flags & TWOMAMBA_FLAG_NO_NORM);
+    const int use_d = (a.variant == TWOMAMBA_EXP) ||
+                      (a.variant == TWOMAMBA_SQ && !(a.flags & TWOMAMBA_FLAG_NO_NORM));
     ktimer_begin(a.timer, "bwd_prep", a.stream);
     hipLaunchKernelGGL((bwd_prep_kernel<D, In>), dim3(a.B * a.H), dim3(kPrep), 0, st, a.z, (const In*)a.out,
                        (const In*)a.dout, s.G, s.Dt, a.T, use_d, (int)with_d);
@@ -360,18 +375,18 @@ int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s) {
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
-template <int D, typename In, bool kExp>
+template <int D, typename In, int kVar>
 static int launch_ref(const BwdArgs& a, const BwdScratch& s) {
     hipStream_t st = (hipStream_t)a.stream;
     const int nt = (a.T + kTile - 1) / kTile;
     const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
     ktimer_begin(a.timer, "ref_bwd_q", a.stream);
-    hipLaunchKernelGGL((bwd_ref_q_kernel<D, In, kExp>), dim3(a.B * a.H * nt), dim3(kTile), 0, st, (const In*)a.q,
+    hipLaunchKernelGGL((bwd_ref_q_kernel<D, In, kVar>), dim3(a.B * a.H * nt), dim3(kTile), 0, st, (const In*)a.q,
                        (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, s.stat, s.rowsum, (In*)a.gq, a.T,
                        nt, a.scale, norm);
     ktimer_end(a.timer, a.stream);
     ktimer_begin(a.timer, "ref_bwd_kv", a.stream);
-    hipLaunchKernelGGL((bwd_ref_kv_kernel<D, In, kExp>), dim3(a.B * a.H * nt), dim3(2 * kTile), 0, st,
+    hipLaunchKernelGGL((bwd_ref_kv_kernel<D, In, kVar>), dim3(a.B * a.H * nt), dim3(2 * kTile), 0, st,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, s.stat,
                        s.colsum, (In*)a.gk, (In*)a.gv, a.T, nt, a.scale);
     ktimer_end(a.timer, a.stream);
@@ -383,14 +398,16 @@ int ref_bwd(const BwdArgs& a) {
     const BwdScratch s = bwd_scratch(a);
     int r = bwd_prep_launch(a, s, true);
     if (r != TWOMAMBA_OK) return r;
-    const bool bf = a.dtype == TWOMAMBA_BF16, ex = a.variant == TWOMAMBA_EXP;
-    if (a.dk == 64) {
-        if (bf) r = ex ? launch_ref<64, bf16, true>(a, s) : launch_ref<64, bf16, false>(a, s);
-        else r = ex ? launch_ref<64, float, true>(a, s) : launch_ref<64, float, false>(a, s);
-    } else {
-        if (bf) r = ex ? launch_ref<16, bf16, true>(a, s) : launch_ref<16, bf16, false>(a, s);
-        else r = ex ? launch_ref<16, float, true>(a, s) : launch_ref<16, float, false>(a, s);
-    }
+    const bool bf = a.dtype == TWOMAMBA_BF16;
+    const int var = a.variant == TWOMAMBA_EXP ? kExpV : a.variant == TWOMAMBA_LIN ? kLin : kSq;
+    auto pick = [&](auto d_tag, auto in_tag) {
+        constexpr int DD = decltype(d_tag)::value;
+        using In = decltype(in_tag);
+        return var == kExpV ? launch_ref<DD, In, kExpV>(a, s)
+                            : var == kLin ? launch_ref<DD, In, kLin>(a, s) : launch_ref<DD, In, kSq>(a, s);
+    };
+    if (a.dk == 64) r = bf ? pick(std::integral_constant<int, 64>{}, bf16{}) : pick(std::integral_constant<int, 64>{}, 0.f);
+    else r = bf ? pick(std::integral_constant<int, 16>{}, bf16{}) : pick(std::integral_constant<int, 16>{}, 0.f);
     if (r != TWOMAMBA_OK) return r;
     return bwd_dz_launch(a, s);
 }

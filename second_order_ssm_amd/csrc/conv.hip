@@ -5,8 +5,9 @@
 //     y_t = w1 * x_t + w0 * x_{t-1} + b,   x_{-1} = the cached raw row (or 0).
 //
 // HBM-bound: one thread per (head, token, tensor, 8 channels) loads 2 x 16
-// bytes (bf16) of input and stores 16 bytes; the weights of its 8 channels
-// come through the caches.
+// bytes (bf16) of input (the earlier row mostly from L2) and stores 16 bytes;
+// the weights of its 8 channels come through the caches.  Index arithmetic is
+// 32-bit within a head.
 #include "device_common.h"
 #include "internal.h"
 
@@ -51,45 +52,42 @@ template <> struct Vec8<float> {
     }
 };
 
+// grid: x = (head, 256-slot tile of the head's T x D/8 chunks), y = tensor
 template <int D, typename In>
 __global__ void __launch_bounds__(256)
 conv2_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
              const float* __restrict__ w, const float* __restrict__ b, const In* __restrict__ prev,
              In* __restrict__ qo, In* __restrict__ ko, In* __restrict__ vo, In* __restrict__ prev_out, int H, int T,
-             size_t n) {
+             int tiles) {
     constexpr int CG = D / 8;
-    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (id >= n) return;
-    const int cg = (int)(id % CG);
-    size_t r = id / CG;
-    const int which = (int)(r % 3);
-    r /= 3;
-    const int t = (int)(r % T);
-    const size_t bh = r / T;
-    const int h = (int)(bh % H);
+    const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles, which = blockIdx.y;
+    const int idx = tile * 256 + threadIdx.x;
+    if (idx >= T * CG) return;
+    const int t = idx / CG, cg = idx % CG;
+    const int h = bh % H;
     const In* x = which == 0 ? q : which == 1 ? k : v;
     In* y = which == 0 ? qo : which == 1 ? ko : vo;
-    const size_t row = (bh * T + t) * D + 8 * cg;
+    const size_t row = ((size_t)bh * T + t) * D + 8 * cg;
     float cur[8], bef[8];
     Vec8<In>::ld(x + row, cur);
     if (t > 0) {
         Vec8<In>::ld(x + row - D, bef);
     } else if (prev) {
-        Vec8<In>::ld(prev + (bh * 3 + which) * D + 8 * cg, bef);
+        Vec8<In>::ld(prev + ((size_t)bh * 3 + which) * D + 8 * cg, bef);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) bef[i] = 0.f;
     }
-    const float* wp = w + ((size_t)(which * H + h) * D + 8 * cg) * 2;
+    const size_t wo = (size_t)(which * H + h) * D + 8 * cg;
     float o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float2 wi = *reinterpret_cast<const float2*>(wp + 2 * i);
+        const float2 wi = *reinterpret_cast<const float2*>(w + 2 * (wo + i));
         o[i] = fmaf(wi.y, cur[i], wi.x * bef[i]);
-        if (b) o[i] += b[(size_t)(which * H + h) * D + 8 * cg + i];
+        if (b) o[i] += b[wo + i];
     }
     Vec8<In>::st(y + row, o);
-    if (prev_out && t == T - 1) Vec8<In>::copy(prev_out + (bh * 3 + which) * D + 8 * cg, x + row);
+    if (prev_out && t == T - 1) Vec8<In>::copy(prev_out + ((size_t)bh * 3 + which) * D + 8 * cg, x + row);
 }
 
 // T = 0: the cached row passes through (zeros without one)
@@ -110,10 +108,10 @@ int launch(const ConvArgs& a) {
         hipLaunchKernelGGL((conv2_pass_kernel<D, In>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                            (const In*)a.prev, (In*)a.prev_out, n);
     } else {
-        const size_t n = (size_t)a.B * a.H * a.T * 3 * (D / 8);
-        hipLaunchKernelGGL((conv2_kernel<D, In>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+        const int tiles = (a.T * (D / 8) + 255) / 256;
+        hipLaunchKernelGGL((conv2_kernel<D, In>), dim3((unsigned)(a.B * a.H * tiles), 3), dim3(256), 0, st,
                            (const In*)a.q, (const In*)a.k, (const In*)a.v, a.w, a.b, (const In*)a.prev, (In*)a.qo,
-                           (In*)a.ko, (In*)a.vo, (In*)a.prev_out, a.H, a.T, n);
+                           (In*)a.ko, (In*)a.vo, (In*)a.prev_out, a.H, a.T, tiles);
     }
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

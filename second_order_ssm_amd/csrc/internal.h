@@ -93,6 +93,10 @@ int mfma_sq_fwd(const FwdArgs& a);
 bool mfma_exp_supported(const FwdArgs& a);
 int mfma_exp_fwd(const FwdArgs& a);
 
+// ---- first-order variant (lin.hip) -----------------------------------------
+size_t lin_workspace(const FwdArgs& a);
+int lin_fwd(const FwdArgs& a);
+
 // ---- decode step -------------------------------------------------------------
 int step_launch(const StepArgs& a);
 

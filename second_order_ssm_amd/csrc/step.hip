@@ -33,13 +33,16 @@ __device__ __forceinline__ void st_nt(float4* p, float4 y) {
     __builtin_nontemporal_store(t, reinterpret_cast<vf4*>(p));
 }
 
-template <int DK, int DV, typename In>
+// kOrder 2: the packed second-order state and its normaliser; kOrder 1: the
+// first-order (Mamba-2S) state S <- e^g S + k v^T, o = scale q.S, D = dk rows,
+// no normaliser ("2Mamba2Furious", §2 and §3-§4).
+template <int DK, int DV, typename In, int kOrder>
 __global__ void __launch_bounds__(kStepThreads)
 step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
             const float* __restrict__ z, float* __restrict__ state, float* __restrict__ norm,
             In* __restrict__ out, float scale, int no_norm, const float* __restrict__ cw,
             const float* __restrict__ cb, In* __restrict__ cst, int H) {
-    constexpr int D = DK * (DK + 1) / 2;
+    constexpr int D = kOrder == 2 ? DK * (DK + 1) / 2 : DK;
     constexpr int CG = DV / 4;                 // float4 column groups per row
     constexpr int NR = kStepThreads / CG;      // rows processed per sweep
     constexpr int UNR = 6;                     // rows in flight per thread
@@ -83,11 +86,16 @@ step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __rest
     // features of this token, one row i of the upper triangle per thread
     if (tid < DK) {
         const int i = tid;
-        int p = i * DK - (i * (i - 1)) / 2;
-        const float ki = s_k[i], qi = s_q[i];
-        for (int j = i; j < DK; ++j, ++p) {
-            s_fk[p] = ki * s_k[j];
-            s_fq[p] = (j == i ? 1.f : 2.f) * qi * s_q[j];
+        if (kOrder == 2) {
+            int p = i * DK - (i * (i - 1)) / 2;
+            const float ki = s_k[i], qi = s_q[i];
+            for (int j = i; j < DK; ++j, ++p) {
+                s_fk[p] = ki * s_k[j];
+                s_fq[p] = (j == i ? 1.f : 2.f) * qi * s_q[j];
+            }
+        } else {
+            s_fk[i] = s_k[i];
+            s_fq[i] = s_q[i];
         }
     }
     __syncthreads();
@@ -136,11 +144,13 @@ step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __rest
 
     // normaliser rows
     float den = 0.f;
-    float* n = norm + hoff * (size_t)D;
-    for (int r = tid; r < D; r += kStepThreads) {
-        const float y = fmaf(a, n[r], s_fk[r]);
-        n[r] = y;
-        den = fmaf(s_fq[r], y, den);
+    if (kOrder == 2) {
+        float* n = norm + hoff * (size_t)D;
+        for (int r = tid; r < D; r += kStepThreads) {
+            const float y = fmaf(a, n[r], s_fk[r]);
+            n[r] = y;
+            den = fmaf(s_fq[r], y, den);
+        }
     }
     // fixed-order wave reduction of den
     for (int off = 32; off > 0; off >>= 1) den += __shfl_down(den, off, 64);
@@ -159,7 +169,7 @@ step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __rest
         float dsum = 0.f;
         for (int w = 0; w < kStepThreads / 64; ++w) dsum += s_den[w];
         float o;
-        if (no_norm) o = num;
+        if (no_norm || kOrder == 1) o = num;
         else o = (dsum == 0.f) ? 0.f : num / dsum;
         IO<In>::st(out, hoff * DV + c, o);
     }
@@ -169,7 +179,9 @@ template <int DK, int DV, typename In>
 int launch(const StepArgs& a) {
     const int nbh = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
-    hipLaunchKernelGGL((step_kernel<DK, DV, In>), dim3(nbh), dim3(kStepThreads), 0, st,
+    const bool first = (a.flags & TWOMAMBA_FLAG_FIRST_ORDER) != 0;
+    auto kern = first ? step_kernel<DK, DV, In, 1> : step_kernel<DK, DV, In, 2>;
+    hipLaunchKernelGGL(kern, dim3(nbh), dim3(kStepThreads), 0, st,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, a.state, a.norm, (In*)a.out,
                        a.scale, (int)((a.flags & TWOMAMBA_FLAG_NO_NORM) != 0), a.conv_w, a.conv_b,
                        (In*)a.conv_state, a.H);

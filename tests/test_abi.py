@@ -311,3 +311,23 @@ def test_step_conv_checks(lib):
     assert call(cs=6) == EALIAS                                 # cache over the state
     assert call(cs=1) == EALIAS                                 # cache over q
     assert call(d_=tmb.StepDesc(2, 3, 64, 16, 1.0, 1, 0)) == EUNSUP
+
+
+# ---------------------------------------------------------------- first order
+def test_first_order_forward_validation(lib):
+    d = desc(variant=2)
+    a256 = lambda x: (x + 255) // 256 * 256
+    s, n = ws_size(lib, d)
+    assert s == OK and n == a256(a256(6 * 2 * 64 * 64 * 4) + 6 * 2 * 4)      # per-chunk d x d states + decays
+    assert call_fwd(lib, d, si=6, ni=7) == EUNSUP                           # no normaliser
+    assert call_fwd(lib, d, so=6, no=7) == EUNSUP
+    assert call_fwd(lib, desc(variant=2, flags=1), out=1) == EALIAS         # NO_NORM accepted, checks still run
+
+
+def test_first_order_step_validation(lib):
+    p = lambda x: None if x is None else fake(x)
+    d = tmb.StepDesc(2, 3, 64, 64, 1.0, 1, tmb.FLAG_FIRST_ORDER)
+    call = lambda norm: lib.twomamba_step(ctypes.byref(d), p(1), p(2), p(3), p(4), p(5), p(norm), p(7), None)
+    assert call(6) == EUNSUP                                                # first order takes no normaliser
+    bad = tmb.StepDesc(2, 3, 64, 64, 1.0, 1, 8)
+    assert lib.twomamba_step(ctypes.byref(bad), p(1), p(2), p(3), p(4), p(5), p(6), p(7), None) == EUNSUP

@@ -68,6 +68,9 @@ CASES = [
     ("exp", "bf16", 1, 2, 1000, 64, -1.0, 0.7, False),
     ("sq", "bf16", 1, 1, 64, 64, -12.0, 1.0, False),
     ("exp", "bf16", 1, 1, 63, 64, 0.0, 1.0, False),
+    # head counts that are multiples of 8 take the XCD-grouped block order
+    ("sq", "bf16", 2, 4, 300, 64, -2.0, 1.0, False),
+    ("exp", "bf16", 1, 8, 257, 64, -1.0, 1.0, False),
 ]
 
 
