@@ -1,6 +1,7 @@
 """Benchmark of the 2Mamba operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs sq,exp,step,exp_step,bwd,exp_bwd]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--legs sq,exp,step,exp_step,bwd,exp_bwd,conv,lin,lin_step]
                     [--cpu-seconds S]
 
 A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
@@ -12,8 +13,9 @@ loop, the 2Mamba-E forward on the same shape and the recurrent decode step
 (batch 64, 32 heads, fp32 packed state of 1.09 GB, 256 sequential steps after
 a T=2048 prefill) and the 2Mamba-E decode over a bf16 key/value cache (batch
 64, 32 heads, 256 sequential steps after a 2048-token prompt), and the
-backward pass of both variants on the forward's workload; they are reported
-under ``legs``.
+backward pass of both variants, the size-2 input convolution and the
+first-order (Mamba-2S) forward on the forward's workload, and the first-order
+decode step; they are reported under ``legs``.
 
 The roofline entry is for the dominant kernel of the timed step: algorithmic
 work attributed to that kernel per launch divided by its average duration,
@@ -100,7 +102,8 @@ def kernel_work(name, leg_work):
 
 KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "step_kernel": "step.hip",
                   "exp_decode_partial": "exp_step.hip", "exp_decode_combine": "exp_step.hip",
-                  "bwd_q": "bwd_mfma.hip", "bwd_kv": "bwd_mfma.hip"}
+                  "bwd_q": "bwd_mfma.hip", "bwd_kv": "bwd_mfma.hip", "exp_bwd_q": "bwd_mfma.hip",
+                  "exp_bwd_kv": "bwd_mfma.hip", "conv2_kernel": "conv.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -237,9 +240,97 @@ def leg_bwd(steps, warmup, variant="sq"):
                             if bwd_kernel_work(n, T, d, d)},
         roofline=dict(bound="mfma", kernel="+".join(allk), achieved=achieved / 1e12, peak=PEAK_BF16_FLOPS / 1e12,
                       unit="TFLOP/s", frac=achieved / PEAK_BF16_FLOPS,
-                      traffic=traffic_sum(*[n for n in allk if n in KERNEL_SOURCES]) if all(
-                          n in KERNEL_SOURCES for n in allk) else None),
+                      # counter traffic of the two MFMA kernels (the decay scan and dz kernels are small)
+                      traffic=traffic_sum(*[("" if variant == "sq" else "exp_") + n for n in ("bwd_q", "bwd_kv")])),
     )
+
+
+def leg_conv(steps, warmup):
+    """Size-2 input convolution of q, k and v on the forward's workload (bf16,
+    with bias and a cached row): HBM-bound, three tensors read and written."""
+    import numpy as np
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    shp = SQ_SHAPE
+    B, H, T, d = shp["B"], shp["H"], shp["T"], shp["d"]
+    q, k, v, _ = (t.cuda() for t in SI.draw(B, H, T, d, seed=shp["seed"], dtype="bf16"))
+    r = np.random.default_rng(shp["seed"] + 900)
+    w = torch.from_numpy(r.normal(0.0, 0.7, size=(3, H, d, 2)).astype(np.float32)).cuda()
+    b = torch.from_numpy(r.normal(0.0, 0.1, size=(3, H, d)).astype(np.float32)).cuda()
+    prev = torch.zeros(B, H, 3, d, dtype=torch.bfloat16, device="cuda")
+    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    st = torch.empty_like(prev)
+    ms = time_loop(lambda: tmb.conv2(q, k, v, w, b, prev, outs=outs, state_out=st), steps, warmup)
+    byts = 2 * 3 * B * H * T * d * 2 + 2 * B * H * 3 * d * 2 + w.numel() * 4 + b.numel() * 4
+    bw = byts / (ms * 1e-3)
+    return dict(workload=f"size-2 input convolution of q, k, v B={B} H={H} T={T} d={d} bf16", ms=ms,
+                bytes_per_call=byts,
+                roofline=dict(bound="hbm", kernel="conv2_kernel", achieved=bw / 1e9, peak=PEAK_HBM / 1e9,
+                              unit="GB/s", frac=bw / PEAK_HBM, traffic=measured_traffic("conv2_kernel")))
+
+
+def leg_lin(steps, warmup):
+    """First-order (Mamba-2S) chunked forward on the forward's workload.  Its
+    work is small (4 d dv flops per head-token), so the roofline is HBM: q, k,
+    v and out in bf16, z in fp32 (516 bytes per head-token)."""
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    shp = SQ_SHAPE
+    B, H, T, d = shp["B"], shp["H"], shp["T"], shp["d"]
+    q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=shp["seed"], dtype="bf16"))
+    out = torch.empty_like(v)
+    desc = tmb.make_desc(B, H, T, d, d, variant="lin", dtype=torch.bfloat16)
+    ws = torch.empty(max(tmb.workspace_size(desc), 1), dtype=torch.uint8, device="cuda")
+    ms = time_loop(lambda: tmb.fwd(q, k, v, z, variant="lin", out=out, workspace=ws), steps, warmup)
+    _, _, allk = dominant_kernel(lambda kt: tmb.fwd(q, k, v, z, variant="lin", out=out, workspace=ws,
+                                                    kernel_times=kt), max(3, min(steps, 10)))
+    ht = B * H * T
+    byts = ht * (3 * d * 2 + 4 + d * 2)
+    ktot = sum(allk.values())
+    bw = byts / (ktot * 1e-3)
+    return dict(workload=f"first-order (Mamba-2S) fwd B={B} H={H} T={T} d={d} bf16", ms=ms,
+                head_tokens_per_s=ht / (ms * 1e-3), bytes_per_call=byts, kernels_ms=allk,
+                roofline=dict(bound="hbm", kernel="+".join(allk), achieved=bw / 1e9, peak=PEAK_HBM / 1e9,
+                              unit="GB/s", frac=bw / PEAK_HBM, traffic=None))
+
+
+def leg_lin_step(warmup):
+    """First-order decode step at batch 64, 32 heads: the dk x dv fp32 state is
+    read and written once per step."""
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    B, H, d, nsteps = STEP_SHAPE["B"], STEP_SHAPE["H"], STEP_SHAPE["d"], STEP_SHAPE["steps"]
+    S = torch.zeros(B, H, d, d, device="cuda")
+    qs, ks, vs, zs = (t.cuda() for t in SI.draw(B, H, nsteps + warmup, d, seed=STEP_SHAPE["prefill_seed"] + 200,
+                                                 dtype="f32"))
+    steps_in = [tuple(x[:, :, i].contiguous() for x in (qs, ks, vs, zs)) for i in range(nsteps + warmup)]
+    out = torch.empty(B, H, d, device="cuda")
+    for i in range(warmup):
+        tmb.step(*steps_in[i], S, None, first_order=True, out=out)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(warmup, warmup + nsteps):
+        tmb.step(*steps_in[i], S, None, first_order=True, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / nsteps
+    byts = B * H * (2 * d * d * 4 + (3 * d + 1) * 4 + d * 4)
+    bw = byts / (ms * 1e-3)
+    return dict(workload=f"first-order decode step B={B} H={H} d={d} fp32 state, {nsteps} sequential steps",
+                ms=ms, bytes_per_step=byts,
+                roofline=dict(bound="hbm", kernel="step_kernel (first order)", achieved=bw / 1e9,
+                              peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM, traffic=None))
 
 
 def leg_step(warmup):
@@ -389,7 +480,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sq,exp,step,exp_step,bwd,exp_bwd")
+    ap.add_argument("--legs", default="sq,exp,step,exp_step,bwd,exp_bwd,conv,lin,lin_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the copy / GEMM ceiling measurements")
@@ -423,6 +514,15 @@ def main():
     if "exp_bwd" in legs:
         res["exp_bwd"] = leg_bwd(args.steps, args.warmup, "exp")
         print(f"[bench] exp_bwd leg done: {res['exp_bwd']['ms']:.3f} ms/call", file=sys.stderr, flush=True)
+    if "conv" in legs:
+        res["conv"] = leg_conv(args.steps, args.warmup)
+        print(f"[bench] conv leg done: {res['conv']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
+    if "lin" in legs:
+        res["lin"] = leg_lin(args.steps, args.warmup)
+        print(f"[bench] lin leg done: {res['lin']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
+    if "lin_step" in legs:
+        res["lin_step"] = leg_lin_step(args.warmup)
+        print(f"[bench] lin_step leg done: {res['lin_step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)
     if "exp_step" in legs:
         res["exp_step"] = leg_exp_step(args.warmup)
         print(f"[bench] exp_step leg done: {res['exp_step']['ms']:.4f} ms/step", file=sys.stderr, flush=True)

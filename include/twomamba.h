@@ -267,8 +267,10 @@ typedef struct {
 /*
  *   q, k, v        [B][H][T][d]   dtype   device
  *   weight         [3][H][d][2]   fp32    device   q, k, v in that order; tap 0 multiplies
- *                                                  x_{t-1}, tap 1 multiplies x_t
- *   bias           [3][H][d]      fp32    device   or NULL (no bias)
+ *                                                  x_{t-1}, tap 1 multiplies x_t; 16-byte aligned
+ *   bias           [3][H][d]      fp32    device   or NULL (no bias); 16-byte aligned
+ *                                                  (a misaligned weight or bias returns
+ *                                                  TWOMAMBA_ERR_UNSUPPORTED)
  *   conv_state_in  [B][H][3][d]   dtype   device   raw q, k, v rows of the token before
  *                                                  t = 0, or NULL (zeros)
  *   q_out, k_out, v_out  [B][H][T][d]  dtype  device   written (round to nearest even for bf16)

@@ -297,6 +297,7 @@ int twomamba_conv2(const twomamba_conv_desc* d, const void* q, const void* k, co
         return TWOMAMBA_ERR_SHAPE;
     if (B * H == 0) return TWOMAMBA_OK;
     if (T > 0 && (!q || !k || !v || !weight || !q_out || !k_out || !v_out)) return TWOMAMBA_ERR_NULL;
+    if (((uintptr_t)weight & 15u) || ((uintptr_t)bias & 15u)) return TWOMAMBA_ERR_UNSUPPORTED;
     const Range ins[] = {rng(q, xb), rng(k, xb), rng(v, xb), rng(weight, wb), rng(bias, bb), rng(conv_state_in, cb)};
     const Range outs[] = {rng(q_out, xb), rng(k_out, xb), rng(v_out, xb), rng(conv_state_out, cb)};
     for (const Range& o : outs)

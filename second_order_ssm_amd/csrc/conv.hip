@@ -52,7 +52,10 @@ template <> struct Vec8<float> {
     }
 };
 
-// grid: x = (head, 256-slot tile of the head's T x D/8 chunks), y = tensor
+// grid: x = (head, tile of 256 threads), y = tensor.  Thread (token group of
+// kTok, 8 channels): its weights and bias are loaded once, each input row once
+// (the row before the group as well), kTok rows are written.
+constexpr int kTok = 4;
 template <int D, typename In>
 __global__ void __launch_bounds__(256)
 conv2_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
@@ -62,32 +65,56 @@ conv2_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __res
     constexpr int CG = D / 8;
     const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles, which = blockIdx.y;
     const int idx = tile * 256 + threadIdx.x;
-    if (idx >= T * CG) return;
-    const int t = idx / CG, cg = idx % CG;
+    const int ngroups = (T + kTok - 1) / kTok;
+    if (idx >= ngroups * CG) return;
+    const int tg = idx / CG, cg = idx % CG;
+    const int t0 = tg * kTok;
     const int h = bh % H;
     const In* x = which == 0 ? q : which == 1 ? k : v;
     In* y = which == 0 ? qo : which == 1 ? ko : vo;
-    const size_t row = ((size_t)bh * T + t) * D + 8 * cg;
-    float cur[8], bef[8];
-    Vec8<In>::ld(x + row, cur);
-    if (t > 0) {
-        Vec8<In>::ld(x + row - D, bef);
+    const size_t wo = (size_t)(which * H + h) * D + 8 * cg;
+    float w0[8], w1[8], bb[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 wv = *reinterpret_cast<const float4*>(w + 2 * wo + 4 * i);   // taps of channels 2i, 2i+1
+        w0[2 * i] = wv.x;
+        w1[2 * i] = wv.y;
+        w0[2 * i + 1] = wv.z;
+        w1[2 * i + 1] = wv.w;
+    }
+    if (b) {
+        const float4 b0 = *reinterpret_cast<const float4*>(b + wo), b1 = *reinterpret_cast<const float4*>(b + wo + 4);
+        bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
+        bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bb[i] = 0.f;
+    }
+    const size_t row0 = ((size_t)bh * T + t0) * D + 8 * cg;
+    float bef[8];
+    if (t0 > 0) {
+        Vec8<In>::ld(x + row0 - D, bef);
     } else if (prev) {
         Vec8<In>::ld(prev + ((size_t)bh * 3 + which) * D + 8 * cg, bef);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) bef[i] = 0.f;
     }
-    const size_t wo = (size_t)(which * H + h) * D + 8 * cg;
-    float o[8];
+    const int nt = min(kTok, T - t0);
+    float cur[kTok][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float2 wi = *reinterpret_cast<const float2*>(w + 2 * (wo + i));
-        o[i] = fmaf(wi.y, cur[i], wi.x * bef[i]);
-        if (b) o[i] += b[wo + i];
+    for (int j = 0; j < kTok; ++j)
+        if (j < nt) Vec8<In>::ld(x + row0 + (size_t)j * D, cur[j]);
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+        if (j >= nt) break;
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = fmaf(w1[i], cur[j][i], fmaf(w0[i], j == 0 ? bef[i] : cur[j - 1][i], bb[i]));
+        Vec8<In>::st(y + row0 + (size_t)j * D, o);
     }
-    Vec8<In>::st(y + row, o);
-    if (prev_out && t == T - 1) Vec8<In>::copy(prev_out + ((size_t)bh * 3 + which) * D + 8 * cg, x + row);
+    if (prev_out && t0 + nt == T)
+        Vec8<In>::copy(prev_out + ((size_t)bh * 3 + which) * D + 8 * cg, x + row0 + (size_t)(nt - 1) * D);
 }
 
 // T = 0: the cached row passes through (zeros without one)
@@ -108,7 +135,7 @@ int launch(const ConvArgs& a) {
         hipLaunchKernelGGL((conv2_pass_kernel<D, In>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                            (const In*)a.prev, (In*)a.prev_out, n);
     } else {
-        const int tiles = (a.T * (D / 8) + 255) / 256;
+        const int tiles = ((a.T + kTok - 1) / kTok * (D / 8) + 255) / 256;
         hipLaunchKernelGGL((conv2_kernel<D, In>), dim3((unsigned)(a.B * a.H * tiles), 3), dim3(256), 0, st,
                            (const In*)a.q, (const In*)a.k, (const In*)a.v, a.w, a.b, (const In*)a.prev, (In*)a.qo,
                            (In*)a.ko, (In*)a.vo, (In*)a.prev_out, a.H, a.T, tiles);

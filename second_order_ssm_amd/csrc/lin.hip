@@ -90,13 +90,18 @@ lin_scan(float* __restrict__ wsS, const float* __restrict__ wsG, const float* st
     if (state_out) state_out[(size_t)bh * DK * DV + e] = run;
 }
 
-// one workgroup per (head, chunk); thread (token, column group of 8)
+// one workgroup per (head, chunk).  The chunk's masked score matrix
+// A[t][s] = exp(Gl_t - Gl_s) (scale q_t.k_s), s <= t, is formed once in LDS
+// (each entry by one thread), then thread (token, column group of 8) forms
+// o_t = A[t] V + exp(Gl_t) (scale q_t) S_c.
 template <int DK, int DV, typename In>
 __global__ void __launch_bounds__(kLinChunk * DV / 8)
 lin_out(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ z,
         const float* __restrict__ wsS, In* __restrict__ out, int T, int nc, float scale) {
     constexpr int NT = kLinChunk * DV / 8;
-    __shared__ float s_q[kLinChunk][DK], s_k[kLinChunk][DK], s_v[kLinChunk][DV], s_S[DK][DV], s_gl[kLinChunk];
+    constexpr int KS = DK + 1;   // padded rows: thread (t, s) pairs read distinct banks
+    __shared__ float s_q[kLinChunk][KS], s_k[kLinChunk][KS], s_v[kLinChunk][DV], s_S[DK][DV];
+    __shared__ float s_A[kLinChunk][kLinChunk + 1], s_gl[kLinChunk];
     const int bh = blockIdx.x / nc, c = blockIdx.x % nc;
     const int t0 = c * kLinChunk, Lc = min(kLinChunk, T - t0);
     const int tid = threadIdx.x;
@@ -116,16 +121,24 @@ lin_out(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict
         }
     }
     __syncthreads();
+    for (int e = tid; e < kLinChunk * kLinChunk; e += NT) {
+        const int t = e / kLinChunk, sk = e % kLinChunk;
+        float a = 0.f;
+        if (sk <= t && t < Lc) {
+#pragma unroll 8
+            for (int i = 0; i < DK; ++i) a = fmaf(s_q[t][i], s_k[sk][i], a);
+            a *= expf(s_gl[t] - s_gl[sk]);
+        }
+        s_A[t][sk] = a;
+    }
+    __syncthreads();
     const int tl = tid / (DV / 8), cg = tid % (DV / 8);
     if (tl >= Lc) return;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s = 0; s <= tl; ++s) {
-        float x = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < DK; ++i) x = fmaf(s_q[tl][i], s_k[s][i], x);
-        const float w = expf(s_gl[tl] - s_gl[s]) * x;
+    for (int sk = 0; sk <= tl; ++sk) {
+        const float a = s_A[tl][sk];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = fmaf(w, s_v[s][8 * cg + u], o[u]);
+        for (int u = 0; u < 8; ++u) o[u] = fmaf(a, s_v[sk][8 * cg + u], o[u]);
     }
     float r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int i = 0; i < DK; ++i) {

@@ -295,6 +295,7 @@ def test_conv_pointer_checks(lib):
     assert call_conv(lib, dsc, qo=1) == EALIAS                  # q_out == q
     assert call_conv(lib, dsc, ko=6) == EALIAS                  # k_out == q_out
     assert call_conv(lib, dsc, so=4) == EALIAS                  # state out == weight
+    assert call_conv(lib, dsc, w=ctypes.c_void_p(BASE + 4 * GAP + 8)) == EUNSUP   # weight not 16-byte aligned
     assert call_conv(lib, tmb.ConvDesc(0, 3, 50, 64, 1, 0), q=None, k=None, v=None, w=None, qo=None, ko=None,
                      vo=None) == OK
 
