@@ -54,7 +54,7 @@ __all__ = [
     "fwd_exp_quadratic", "fwd_exp_quadratic_rows", "fwd_exp_streaming",
     "state_elements", "memory_crossover_tokens",
     "sigmoid", "bwd_quadratic", "bwd_exp_quadratic", "conv2", "step_conv",
-    "fwd_linear_quadratic", "fwd_linear_recurrent", "step_linear", "bwd_linear_quadratic",
+    "fwd_linear_quadratic", "fwd_linear_recurrent", "step_linear", "bwd_linear_quadratic", "bwd_blocked",
 ]
 
 
@@ -562,4 +562,67 @@ def bwd_linear_quadratic(q, k, v, z, dout, scale=1.0):
         dq[:, :, t] += np.einsum("bhs,bhsd->bhd", da, K)
         dk[:, :, :t + 1] += da[..., None] * q[:, :, t][:, :, None, :]
         _add_mask_grad(dg, dw * w, t)
+    return dq, dk, dv, -sigmoid(z) * dg
+
+
+def bwd_blocked(q, k, v, z, dout, variant="sq", scale=1.0, norm=True, block=512):
+    """The same gradients as bwd_quadratic / bwd_exp_quadratic /
+    bwd_linear_quadratic, written with whole score matrices for long sequences:
+    query rows are taken `block` at a time against every key.  lambda_ts comes
+    from the running sum G_t = g_0 + ... + g_t (fp64) as G_t - G_s.  Returns
+    (dq, dk, dv, dz) for inputs [B, H, T, d] (one (b, h) at a time).
+    """
+    g = decay_log(z)
+    B, H, T, _ = q.shape
+    dq, dk, dv, dg = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape), np.zeros(z.shape)
+    for b in range(B):
+        for h in range(H):
+            Q, K, V, DO = q[b, h], k[b, h], v[b, h], dout[b, h]
+            G = np.cumsum(g[b, h])
+            rows = np.zeros(T)      # strict row sums of dL/dlambda
+            cols = np.zeros(T)      # strict column sums
+            for r0 in range(0, T, block):
+                r1 = min(T, r0 + block)
+                t = np.arange(r0, r1)[:, None]
+                s_ = np.arange(T)[None, :]
+                causal = s_ <= t
+                lam = np.where(causal, G[r0:r1, None] - G[None, :], -np.inf)
+                x = scale * (Q[r0:r1] @ K.T)
+                if variant == "exp":
+                    logit = np.where(causal, x + lam, -np.inf)
+                    P = np.exp(logit - logit.max(axis=1, keepdims=True))
+                    P /= P.sum(axis=1, keepdims=True)
+                    o = P @ V
+                    dP = DO[r0:r1] @ V.T
+                    dS = P * (dP - (DO[r0:r1] * o).sum(axis=1, keepdims=True))
+                    dx, M, W = dS, dS, P
+                else:
+                    L = np.where(causal, np.exp(np.where(causal, lam, 0.0)), 0.0)
+                    if variant == "sq":
+                        w = L * x * x
+                        den = w.sum(axis=1, keepdims=True)
+                        if norm:
+                            rden = np.where(den > 0, 1.0 / np.where(den > 0, den, 1.0), 0.0)
+                            o = (w @ V) * rden
+                            dw = (DO[r0:r1] @ V.T - (DO[r0:r1] * o).sum(axis=1, keepdims=True)) * rden
+                            W = w * rden
+                        else:
+                            dw = DO[r0:r1] @ V.T
+                            W = w
+                        dx = dw * L * 2.0 * x
+                    else:   # first order
+                        w = L * x
+                        dw = DO[r0:r1] @ V.T
+                        W = w
+                        dx = dw * L
+                    M = dw * w
+                dv[b, h] += W.T @ DO[r0:r1]
+                dq[b, h, r0:r1] += scale * (dx @ K)
+                dk[b, h] += scale * (dx.T @ Q[r0:r1])
+                strict = s_ < t
+                Ms = np.where(strict, M, 0.0)
+                rows[r0:r1] += Ms.sum(axis=1)
+                cols += Ms.sum(axis=0)
+            # dg_r = sum over r' < r of (cols - rows)
+            dg[b, h] = np.concatenate([[0.0], np.cumsum(cols - rows)[:-1]])
     return dq, dk, dv, -sigmoid(z) * dg

@@ -114,3 +114,22 @@ def test_bwd_deterministic():
     b, _ = run_bwd("exp", "bf16", 1, 2, 300, 64, -2.0, 1.0)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("variant", ["sq", "exp", "lin"])
+def test_bwd_full_size_two_heads(variant):
+    # the benchmark workload 2 x 16 x 8192 bf16, in the launch configuration the
+    # benchmark times; two whole heads against the oracle's whole-matrix form
+    B, H, T, d = 2, 16, 8192, 64
+    announce(f"bwd {variant} full size {B}x{H}x{T}")
+    q, k, v, z = SI.draw(B, H, T, d, seed=3, dtype="bf16")
+    do = _dout(B, H, T, d, "bf16", 3)
+    qd, kd, vd, zd, dod = dev(q, k, v, z, do)
+    out = tmb.fwd(qd, kd, vd, zd, variant=variant)
+    g = tmb.bwd(qd, kd, vd, zd, out, dod, variant=variant)
+    torch.cuda.synchronize()
+    got = [host64(x) for x in g]
+    for b, h in [(0, 0), (1, 15)]:
+        sl = lambda t: SI.to_f64(t[b:b + 1, h:h + 1])
+        ref = O.bwd_blocked(sl(q), sl(k), sl(v), sl(z), sl(do), variant=variant)
+        check([x[b:b + 1, h:h + 1] for x in got], ref, TOL["bf16"], f"{variant} head ({b},{h})")

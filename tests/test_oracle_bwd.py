@@ -197,3 +197,19 @@ def test_planted_gradient_mistake_is_caught(monkeypatch, name, attr, patch, pins
     for pin in pins:
         with pytest.raises(AssertionError):
             pin()
+
+
+@pytest.mark.parametrize("variant,norm", [("sq", True), ("sq", False), ("exp", True), ("lin", True)])
+def test_blocked_gradients_equal_the_row_loop(variant, norm):
+    # the whole-matrix form used for long sequences, against the row loop,
+    # with blocks that split the rows unevenly
+    q, k, v, z, do = _inputs(11, B=2, H=2, T=37, d=5, dv=4, z_mean=-1.5)
+    if variant == "sq":
+        ref = O.bwd_quadratic(q, k, v, z, do, scale=0.8, norm=norm)
+    elif variant == "exp":
+        ref = O.bwd_exp_quadratic(q, k, v, z, do, scale=0.8)
+    else:
+        ref = O.bwd_linear_quadratic(q, k, v, z, do, scale=0.8)
+    got = O.bwd_blocked(q, k, v, z, do, variant=variant, scale=0.8, norm=norm, block=10)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-10)
