@@ -15,9 +15,12 @@
 // Gl is the chunk-local inclusive prefix of g = -softplus(z); every exponent is
 // a sum of g over a stretch inside one chunk.  The first-order work is small
 // (4 dk dv flops per head-token plus the chunk-local part), so the path is bound
-// by the traffic of q, k, v, out and the per-chunk states.  bf16 at d = 64 runs
-// 16x16x32 MFMA versions of the delta and output kernels (per-chunk states then
-// stored transposed, [dv][dk]); everything else runs the fp32 VALU kernels.
+// by the traffic of q, k, v, out and the per-chunk states.  That three-pass form
+// serves fp32 and d = 16; bf16 at d = 64 runs a segmented single pass on
+// 16x16x32 MFMAs instead (see below), which reads k and v twice and q once and
+// keeps the states of whole segments, not of chunks.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 #include "mfma_tiles.h"
@@ -113,151 +116,6 @@ lin_scan(float* __restrict__ wsS, const float* __restrict__ wsG, const float* st
     if (state_out) state_out[(size_t)bh * DK * DV + ea] = run;
 }
 
-// ---------------------------------------------------------------------------
-// MFMA kernels for bf16 inputs at d = 64 (one workgroup of 4 waves per chunk)
-using namespace tiles;
-
-// dS_c^T[c][d] = sum_t (w V)^T[c][t] K[t][d], w_t = exp(Gam_c - Gl_t): both
-// operands come from transposing reads of the row-major tiles; wave w forms the
-// value rows 16w .. 16w + 15.
-__global__ void __launch_bounds__(kThreads)
-lin_delta_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
-               float* __restrict__ wsS, float* __restrict__ wsG, int T, int nc) {
-    __shared__ __attribute__((aligned(16))) Tile sK, sV;
-    __shared__ float s_w[kTile];
-    const int bh = blockIdx.x / nc, c = blockIdx.x % nc;
-    const int t0 = c * kTile, Lc = min(kTile, T - t0);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
-    const size_t tok0 = (size_t)bh * T + t0;
-    Stage st;
-    fetch(st, k + tok0 * kD, Lc, tid);
-    store(st, sK, tid);
-    if (w == 0) {   // w_t from the chunk-local suffix sums of g (a wave-wide scan)
-        const float gv = lane < Lc ? decay_log(z[tok0 + lane]) : 0.f;
-        float incl = gv;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
-        const float total = __shfl(incl, 63);
-        s_w[lane] = expf(total - incl);
-        if (lane == 0) wsG[(size_t)bh * nc + c] = total;
-    }
-    fetch(st, v + tok0 * kD, Lc, tid);
-    __syncthreads();
-    // V rows scaled by w_t on the way into LDS
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int e = tid + n * kThreads, r = e >> 3, cc = e & 7;
-        const uint32_t x[4] = {st.c[n].x, st.c[n].y, st.c[n].z, st.c[n].w};
-        const float ww = s_w[r];
-        uint32_t y[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            y[i] = pack2(__uint_as_float(x[i] << 16) * ww, __uint_as_float(x[i] & 0xffff0000u) * ww);
-        *reinterpret_cast<uint4*>(&sV.X[r][8 * cc]) = make_uint4(y[0], y[1], y[2], y[3]);
-    }
-    __syncthreads();
-    f4 acc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const b8 A = tr_op(sV, w, 2 * h, lane);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(A, tr_op(sK, dt, 2 * h, lane), acc[dt]);
-    }
-    float* dst = wsS + ((size_t)bh * nc + c) * kD * kD;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * w + 4 * g + i) * kD + 16 * dt + col] = acc[dt][i];
-}
-
-// o_t = sum_{s<=t in c} exp(Gl_t - Gl_s) (scale q_t.k_s) v_s + exp(Gl_t) scale q_t.S_c.
-// Wave w owns queries 16w .. 16w + 15, one per lane column: S^T = K Q^T, the
-// masked weights P^T as the B operand of O^T = V^T P^T, and the carried state
-// as the A operand of O^T += S_c^T Q^T (S_c rounded to bf16 for the product).
-__global__ void __launch_bounds__(kThreads)
-lin_out_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-             const float* __restrict__ z, const float* __restrict__ wsS, bf16* __restrict__ out, int T, int nc,
-             float scale) {
-    __shared__ __attribute__((aligned(16))) Tile sK, sV;
-    __shared__ float s_gl[kTile];
-    const int bh = blockIdx.x / nc, c = blockIdx.x % nc;
-    const int t0 = c * kTile, Lc = min(kTile, T - t0);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
-    const size_t tok0 = (size_t)bh * T + t0;
-    const int tl = 16 * w + col;                   // this lane's query within the chunk
-    const bool tv = tl < Lc;
-    const bf16* qrow = q + (tok0 + (tv ? tl : 0)) * kD;
-    const b8 Qb[2] = {own_op(qrow, g, 0), own_op(qrow, g, 1)};
-    Stage sk, sv;
-    fetch(sk, k + tok0 * kD, Lc, tid);
-    fetch(sv, v + tok0 * kD, Lc, tid);
-    if (w == 0) {
-        const float gv = lane < Lc ? decay_log(z[tok0 + lane]) : 0.f;
-        float incl = gv;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
-        s_gl[lane] = incl * kLog2e;
-    }
-    store(sk, sK, tid);
-    store(sv, sV, tid);
-    // carried state S_c^T rows as A operands (fp32 -> bf16), loaded while LDS fills
-    const float* Sc = wsS + ((size_t)bh * nc + c) * kD * kD;
-    b8 SA[4][2];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float* r = Sc + (16 * ct + col) * kD + 8 * g + 32 * kk;
-            const float4 a = *reinterpret_cast<const float4*>(r), b = *reinterpret_cast<const float4*>(r + 4);
-            SA[ct][kk] = as_b8(make_uint4(pack2(a.x, a.y), pack2(a.z, a.w), pack2(b.x, b.y), pack2(b.z, b.w)));
-        }
-    __syncthreads();
-    const float glt = s_gl[tv ? tl : 0];
-    f4 O[4], OI[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        O[ct] = f4{0.f, 0.f, 0.f, 0.f};
-        OI[ct] = mfma(SA[ct][1], Qb[1], mfma(SA[ct][0], Qb[0], f4{0.f, 0.f, 0.f, 0.f}));
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float p[8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int st = 2 * h + u, r = 16 * st + col;
-            f4 S = mfma(row_op(sK, r, g, 0), Qb[0], f4{0.f, 0.f, 0.f, 0.f});
-            S = mfma(row_op(sK, r, g, 1), Qb[1], S);
-            const float4 g4 = *reinterpret_cast<const float4*>(&s_gl[16 * st + 4 * g]);
-            const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sl = 16 * st + 4 * g + i;
-                p[4 * u + i] = sl <= tl ? scale * fexp2(glt - gs[i]) * S[i] : 0.f;
-            }
-        }
-        const b8 B = to_b(p);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) O[ct] = mfma(tr_op(sV, ct, 2 * h, lane), B, O[ct]);
-    }
-    if (!tv) return;
-    const float dec = scale * fexp2(glt);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        uint2 o;
-        o.x = pack2(fmaf(dec, OI[ct][0], O[ct][0]), fmaf(dec, OI[ct][1], O[ct][1]));
-        o.y = pack2(fmaf(dec, OI[ct][2], O[ct][2]), fmaf(dec, OI[ct][3], O[ct][3]));
-        *reinterpret_cast<uint2*>(out + (tok0 + tl) * kD + 16 * ct + 4 * g) = o;
-    }
-}
-
 // one workgroup per (head, chunk).  The chunk's masked score matrix
 // A[t][s] = exp(Gl_t - Gl_s) (scale q_t.k_s), s <= t, is formed once in LDS
 // (each entry by one thread), then thread (token, column group of 8) forms
@@ -348,25 +206,244 @@ int run(const FwdArgs& a) {
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
-int run_mfma(const FwdArgs& a) {
-    const LinLayout L = lin_layout(a);
+// ---------------------------------------------------------------------------
+// MFMA kernels for bf16 inputs at d = 64
+using namespace tiles;
+
+// ---------------------------------------------------------------------------
+// Segmented single pass (bf16, d = 64): the sequence of a head is cut into
+// segments of whole chunks.  lin_seg_mfma forms every segment's own end state
+// (weights relative to the segment end), lin_scan over segments turns them into
+// the carry entering each segment (and the final state), and lin_main_mfma walks
+// a segment's chunks with the state in MFMA accumulators: per chunk the
+// intra-chunk scores, the readout of the carried state and the state update.
+// HBM traffic is then q, k, v, out plus one k, v read and small per-segment states.
+
+// B operand of Q for the K-slot order of tr_op: dims {16 dtt + 4g .. +3, 16 dtt + 16 + 4g .. +3} of row t
+__device__ __forceinline__ b8 q_tr_order(const Tile& t, int row, int dtt, int g) {
+    const uint2 a = *reinterpret_cast<const uint2*>(&t.X[row][16 * dtt + 4 * g]);
+    const uint2 b = *reinterpret_cast<const uint2*>(&t.X[row][16 * dtt + 16 + 4 * g]);
+    return as_b8(make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// chunk-local inclusive prefix of g (log2 units) over the 64 lanes of one wave
+__device__ __forceinline__ float chunk_prefix(const float* z, int lane, int Lc) {
+    float incl = lane < Lc ? decay_log(z[lane]) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    return incl * kLog2e;
+}
+
+// V rows scaled by w_t = 2^(s_w[t]) into a tile
+__device__ __forceinline__ void store_scaled(const Stage& st, Tile& t, const float* s_w, int tid) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int e = tid + n * kThreads, r = e >> 3, cc = e & 7;
+        const uint32_t x[4] = {st.c[n].x, st.c[n].y, st.c[n].z, st.c[n].w};
+        const float ww = fexp2(s_w[r]);
+        uint32_t y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            y[i] = pack2(__uint_as_float(x[i] << 16) * ww, __uint_as_float(x[i] & 0xffff0000u) * ww);
+        *reinterpret_cast<uint4*>(&t.X[r][8 * cc]) = make_uint4(y[0], y[1], y[2], y[3]);
+    }
+}
+
+// segment end states S_g^T[c][d] (transposed), weights relative to the segment end
+__global__ void __launch_bounds__(kThreads)
+lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
+             float* __restrict__ wsS, float* __restrict__ wsG, int T, int nseg, int seg_chunks) {
+    __shared__ __attribute__((aligned(16))) Tile sK, sV;
+    __shared__ float s_w[kTile];
+    const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int nc = (T + kTile - 1) / kTile;
+    const int c0 = seg * seg_chunks, c1 = min(nc, c0 + seg_chunks);
+    const size_t base = (size_t)bh * T;
+    f4 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+    float later = 0.f;   // log2 decay from the end of the current chunk to the segment end
+    Stage sk, sv;
+    {
+        const int t0 = (c1 - 1) * kTile;
+        fetch(sk, k + (base + t0) * kD, min(kTile, T - t0), tid);
+        fetch(sv, v + (base + t0) * kD, min(kTile, T - t0), tid);
+    }
+    for (int c = c1 - 1; c >= c0; --c) {   // from the segment end backwards
+        const int t0 = c * kTile, Lc = min(kTile, T - t0);
+        if (w == 0) {
+            const float incl = chunk_prefix(z + base + t0, lane, Lc);
+            const float total = __shfl(incl, 63);
+            s_w[lane] = total - incl + later;      // log2 w_t relative to the segment end
+            later += total;   // kept by wave 0, which also writes the segment's decay
+        }
+        __syncthreads();
+        store(sk, sK, tid);
+        store_scaled(sv, sV, s_w, tid);
+        __syncthreads();
+        if (c > c0) {
+            const int tn = t0 - kTile;
+            fetch(sk, k + (base + tn) * kD, kTile, tid);
+            fetch(sv, v + (base + tn) * kD, kTile, tid);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const b8 A = tr_op(sV, w, 2 * h, lane);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(A, tr_op(sK, dt, 2 * h, lane), acc[dt]);
+        }
+        __syncthreads();
+    }
+    float* dst = wsS + ((size_t)bh * nseg + seg) * kD * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * w + 4 * g + i) * kD + 16 * dt + col] = acc[dt][i];
+    if (tid == 0) wsG[(size_t)bh * nseg + seg] = later / kLog2e;
+}
+
+// one segment of one head: carried state in accumulators (wave w: value rows
+// 16w..16w+15 of S^T), per chunk intra-chunk scores + readout + update
+__global__ void __launch_bounds__(kThreads)
+lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+              const float* __restrict__ z, const float* __restrict__ carry, bf16* __restrict__ out, int T, int nseg,
+              int seg_chunks, float scale) {
+    __shared__ __attribute__((aligned(16))) Tile sQ, sK, sV, sW, sS;
+    __shared__ float s_gl[kTile], s_w[kTile];
+    const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int nc = (T + kTile - 1) / kTile;
+    const int c0 = seg * seg_chunks, c1 = min(nc, c0 + seg_chunks);
+    const size_t base = (size_t)bh * T;
+    // carry S^T[c][d] into the accumulator layout: rows 16w + 4g + i, column 16 dt + col
+    f4 S[4];
+    {
+        const float* src = carry + ((size_t)bh * nseg + seg) * kD * kD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[dt][i] = src[(16 * w + 4 * g + i) * kD + 16 * dt + col];
+    }
+    Stage sq, sk, sv;
+    {
+        const int t0 = c0 * kTile, Lc = min(kTile, T - t0);
+        fetch(sq, q + (base + t0) * kD, Lc, tid);
+        fetch(sk, k + (base + t0) * kD, Lc, tid);
+        fetch(sv, v + (base + t0) * kD, Lc, tid);
+    }
+    for (int c = c0; c < c1; ++c) {
+        const int t0 = c * kTile, Lc = min(kTile, T - t0);
+        if (w == 0) {
+            const float incl = chunk_prefix(z + base + t0, lane, Lc);
+            const float total = __shfl(incl, 63);
+            s_gl[lane] = incl;
+            s_w[lane] = total - incl;              // log2 of w_t = exp(Gam - Gl_t)
+        }
+        // the state before this chunk, bf16, as S[d][c] rows (4 consecutive c per lane)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            uint2 o;
+            o.x = pack2(S[dt][0], S[dt][1]);
+            o.y = pack2(S[dt][2], S[dt][3]);
+            *reinterpret_cast<uint2*>(&sS.X[16 * dt + col][16 * w + 4 * g]) = o;
+        }
+        store(sq, sQ, tid);
+        store(sk, sK, tid);
+        __syncthreads();
+        store_scaled(sv, sW, s_w, tid);
+        store(sv, sV, tid);
+        __syncthreads();
+        if (c + 1 < c1) {
+            const int tn = t0 + kTile, Ln = min(kTile, T - tn);
+            fetch(sq, q + (base + tn) * kD, Ln, tid);
+            fetch(sk, k + (base + tn) * kD, Ln, tid);
+            fetch(sv, v + (base + tn) * kD, Ln, tid);
+        }
+        // this wave's queries 16w .. 16w + 15, one per lane column
+        const int tl = 16 * w + col;
+        const float glt = s_gl[tl];
+        const b8 Qb[2] = {row_op(sQ, tl, g, 0), row_op(sQ, tl, g, 1)};
+        f4 O[4], OI[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            O[ct] = f4{0.f, 0.f, 0.f, 0.f};
+            OI[ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dtt = 0; dtt < 2; ++dtt)
+                OI[ct] = mfma(tr_op(sS, ct, 2 * dtt, lane), q_tr_order(sQ, tl, 2 * dtt, g), OI[ct]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float p[8];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int st = 2 * h + u, r = 16 * st + col;
+                f4 X = mfma(row_op(sK, r, g, 0), Qb[0], f4{0.f, 0.f, 0.f, 0.f});
+                X = mfma(row_op(sK, r, g, 1), Qb[1], X);
+                const float4 g4 = *reinterpret_cast<const float4*>(&s_gl[16 * st + 4 * g]);
+                const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int sl = 16 * st + 4 * g + i;
+                    p[4 * u + i] = sl <= tl ? scale * fexp2(glt - gs[i]) * X[i] : 0.f;
+                }
+            }
+            const b8 B = to_b(p);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) O[ct] = mfma(tr_op(sV, ct, 2 * h, lane), B, O[ct]);
+        }
+        if (tl < Lc) {
+            const float dec = scale * fexp2(glt);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                uint2 o;
+                o.x = pack2(fmaf(dec, OI[ct][0], O[ct][0]), fmaf(dec, OI[ct][1], O[ct][1]));
+                o.y = pack2(fmaf(dec, OI[ct][2], O[ct][2]), fmaf(dec, OI[ct][3], O[ct][3]));
+                *reinterpret_cast<uint2*>(out + (base + t0 + tl) * kD + 16 * ct + 4 * g) = o;
+            }
+        }
+        // update: S^T = exp(Gam) S^T + (w V)^T K
+        const float eg = fexp2(s_gl[63]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) S[dt] *= eg;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const b8 A = tr_op(sW, w, 2 * h, lane);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) S[dt] = mfma(A, tr_op(sK, dt, 2 * h, lane), S[dt]);
+        }
+        __syncthreads();
+    }
+}
+
+int run_fused(const FwdArgs& a) {
     const int nc = (a.T + kTile - 1) / kTile;
     const int nbh = a.B * a.H;
+    // segments: about two workgroups per CU, at least two chunks each
+    int want = std::max(1, (512 + nbh - 1) / nbh);
+    want = std::min(want, std::max(1, nc / 2));
+    const int sc = (nc + want - 1) / want;
+    const int nseg = (nc + sc - 1) / sc;
+    const LinLayout L = lin_layout(a);   // per-chunk slots; nseg <= nc of them are used
     float* wsS = (float*)((char*)a.ws + L.off_S);
     float* wsG = (float*)((char*)a.ws + L.off_G);
     hipStream_t st = (hipStream_t)a.stream;
-    ktimer_begin(a.timer, "lin_delta", a.stream);
-    hipLaunchKernelGGL(lin_delta_mfma, dim3(nbh * nc), dim3(kThreads), 0, st, (const bf16*)a.k, (const bf16*)a.v,
-                       a.z, wsS, wsG, a.T, nc);
+    ktimer_begin(a.timer, "lin_seg", a.stream);
+    hipLaunchKernelGGL(lin_seg_mfma, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k, (const bf16*)a.v, a.z,
+                       wsS, wsG, a.T, nseg, sc);
     ktimer_end(a.timer, a.stream);
     const int etiles = (kD * kD + 255) / 256;
     ktimer_begin(a.timer, "lin_scan", a.stream);
     hipLaunchKernelGGL((lin_scan<kD, kD, true>), dim3(nbh * etiles), dim3(256), 0, st, wsS, (const float*)wsG,
-                       a.state_in, a.state_out, nc, etiles);
+                       a.state_in, a.state_out, nseg, etiles);
     ktimer_end(a.timer, a.stream);
-    ktimer_begin(a.timer, "lin_out", a.stream);
-    hipLaunchKernelGGL(lin_out_mfma, dim3(nbh * nc), dim3(kThreads), 0, st, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, a.z, (const float*)wsS, (bf16*)a.out, a.T, nc, a.scale);
+    ktimer_begin(a.timer, "lin_main", a.stream);
+    hipLaunchKernelGGL(lin_main_mfma, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, a.z, (const float*)wsS, (bf16*)a.out, a.T, nseg, sc, a.scale);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
@@ -390,7 +467,7 @@ int lin_fwd(const FwdArgs& a) {
         return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
     }
     const bool bf = a.dtype == TWOMAMBA_BF16;
-    if (bf && a.dk == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS)) return run_mfma(a);
+    if (bf && a.dk == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS)) return run_fused(a);
     if (a.dk == 64) return bf ? run<64, 64, bf16>(a) : run<64, 64, float>(a);
     if (a.dk == 16) return bf ? run<16, 16, bf16>(a) : run<16, 16, float>(a);
     return TWOMAMBA_ERR_UNSUPPORTED;
