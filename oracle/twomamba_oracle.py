@@ -55,6 +55,7 @@ __all__ = [
     "state_elements", "memory_crossover_tokens",
     "sigmoid", "bwd_quadratic", "bwd_exp_quadratic", "conv2", "step_conv",
     "fwd_linear_quadratic", "fwd_linear_recurrent", "step_linear", "bwd_linear_quadratic", "bwd_blocked",
+    "row_weight_sums", "row_logsumexp",
 ]
 
 
@@ -626,3 +627,36 @@ def bwd_blocked(q, k, v, z, dout, variant="sq", scale=1.0, norm=True, block=512)
             # dg_r = sum over r' < r of (cols - rows)
             dg[b, h] = np.concatenate([[0.0], np.cumsum(cols - rows)[:-1]])
     return dq, dk, dv, -sigmoid(z) * dg
+
+
+# ----------------------------------------------------------------------------
+# per-row statistics a training forward hands to its backward: the 2Mamba
+# weight sum (the normaliser of [2M2F §5]) and the 2Mamba-E log-sum-exp
+# ----------------------------------------------------------------------------
+
+def row_weight_sums(q, k, z, scale=1.0, state_in_norm=None):
+    """den_t = sum_{s<=t} L_ts (scale q_t.k_s)^2, plus exp(g_0+...+g_t)
+    phi_q(scale q_t).n0 for an initial normaliser n0 -> [B, H, T]."""
+    g = decay_log(z)
+    T = q.shape[2]
+    den = np.zeros(q.shape[:3])
+    for t in range(T):
+        L = np.exp(_row_log_mask(g[:, :, :t + 1]))
+        a = scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], k[:, :, :t + 1])
+        den[:, :, t] = (L * a * a).sum(axis=-1)
+        if state_in_norm is not None:
+            den[:, :, t] += np.exp(g[:, :, :t + 1].sum(axis=-1)) * np.einsum(
+                "bhp,bhp->bh", phi_q(scale * q[:, :, t]), state_in_norm)
+    return den
+
+
+def row_logsumexp(q, k, z, scale=1.0):
+    """lse_t = log sum_{s<=t} exp(scale q_t.k_s + lambda_ts) (natural log) -> [B, H, T]."""
+    g = decay_log(z)
+    T = q.shape[2]
+    lse = np.zeros(q.shape[:3])
+    for t in range(T):
+        logit = scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], k[:, :, :t + 1]) + _row_log_mask(g[:, :, :t + 1])
+        m = logit.max(axis=-1)
+        lse[:, :, t] = m + np.log(np.exp(logit - m[..., None]).sum(axis=-1))
+    return lse

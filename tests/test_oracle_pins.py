@@ -350,3 +350,27 @@ def test_model_shapes_fixture_consistent():
         s = json.load(f)
     for m in ("small_300M", "medium_700M"):
         assert s[m]["hidden"] == s[m]["heads"] * s[m]["head_dim"]
+
+
+# ---------------------------------------------------------------- row statistics
+def test_row_weight_sums_relate_the_two_normalisations():
+    # o_t (normalised) * den_t = o_t without normalisation, row by row
+    r = np.random.default_rng(61)
+    q, k, v = (r.normal(size=(2, 2, 19, 4)) for _ in range(3))
+    z = r.normal(-1.0, 1.0, size=(2, 2, 19))
+    n0 = np.abs(r.normal(size=(2, 2, 10)))
+    S0 = r.normal(size=(2, 2, 10, 4))
+    den = O.row_weight_sums(q, k, z, scale=0.7, state_in_norm=n0)
+    o = O.fwd_quadratic(q, k, v, z, scale=0.7, state_in=S0, norm_in=n0)
+    num = O.fwd_quadratic(q, k, v, z, scale=0.7, norm=False, state_in=S0, norm_in=n0)
+    np.testing.assert_allclose(o * den[..., None], num, rtol=1e-10, atol=1e-12)
+
+
+def test_row_logsumexp_matches_torch_without_decay():
+    r = np.random.default_rng(62)
+    q, k = (r.normal(size=(2, 3, 17, 5)) for _ in range(2))
+    z = np.full((2, 3, 17), -np.inf)
+    s = 0.8 * np.matmul(q, np.swapaxes(k, -1, -2))
+    s = np.where(np.tril(np.ones((17, 17), dtype=bool)), s, -np.inf)
+    ref = torch.logsumexp(torch.tensor(s), dim=-1).numpy()
+    np.testing.assert_allclose(O.row_logsumexp(q, k, z, scale=0.8), ref, rtol=1e-12, atol=1e-12)
