@@ -206,7 +206,8 @@ def leg_sq(steps, warmup, variant="sq"):
 
 def leg_bwd(steps, warmup, variant="sq"):
     """Backward (dq, dk, dv, dz) of the forward on the same workload, with a
-    seeded N(0,1) output gradient; the forward output is computed once, untimed."""
+    seeded N(0,1) output gradient; the forward output and its per-row
+    statistics (as a training step keeps them) are computed once, untimed."""
     import numpy as np
     import torch
 
@@ -218,14 +219,15 @@ def leg_bwd(steps, warmup, variant="sq"):
     q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=shp["seed"], dtype="bf16"))
     dout = torch.from_numpy(np.random.default_rng(shp["seed"] + 500).standard_normal((B, H, T, d))).to(
         torch.bfloat16).cuda()
-    out = tmb.fwd(q, k, v, z, variant=variant)
+    out, stat = tmb.fwd(q, k, v, z, variant=variant, want_stats=True)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z))
     desc = tmb.make_desc(B, H, T, d, d, variant=variant, dtype=torch.bfloat16)
     ws = torch.empty(tmb.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
-    fn = lambda: tmb.bwd(q, k, v, z, out, dout, variant=variant, grads=grads, workspace=ws)
+    fn = lambda: tmb.bwd(q, k, v, z, out, dout, variant=variant, grads=grads, workspace=ws, row_stat=stat)
     ms = time_loop(fn, steps, warmup)
     name, kms, allk = dominant_kernel(lambda kt: tmb.bwd(q, k, v, z, out, dout, variant=variant, grads=grads,
-                                                         workspace=ws, kernel_times=kt), max(3, min(steps, 10)))
+                                                         workspace=ws, row_stat=stat, kernel_times=kt),
+                                      max(3, min(steps, 10)))
     work = B * H * bwd_flops_per_head(T, d, d)
     # the work splits over two MFMA kernels (and two small ones); the roofline
     # entry covers all of them: the op's work over the summed kernel durations

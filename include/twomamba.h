@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define TWOMAMBA_ABI_VERSION 1
+#define TWOMAMBA_ABI_VERSION 2
 
 typedef enum {
     TWOMAMBA_OK = 0,
@@ -167,6 +167,28 @@ int twomamba_fwd_timed(const twomamba_fwd_desc* desc,
                        void* out, float* state_out, float* norm_out,
                        void* workspace, size_t workspace_bytes, void* stream,
                        float* kernel_ms, const char** kernel_names, int cap, int* n_kernels);
+
+/*
+ * twomamba_fwd that also writes each row's normalising statistic, the quantity
+ * the backward otherwise recomputes with a pass over all earlier keys
+ * [2M2F App. C: the gradient of a normalised kernel needs the row's
+ * normaliser; storing it from the forward is the usual flash-attention
+ * practice]:
+ *
+ *   row_stat  [B][H][T]  fp32  device  written, required (non-NULL) when B H T > 0
+ *     TWOMAMBA_SQ:  den_t = sum_{s<=t} L_ts (scale q_t.k_s)^2 plus the initial
+ *                   normaliser's term e^(g_0+..+g_t) phi_q(scale q_t).n0 when
+ *                   norm_in is given (also written with TWOMAMBA_FLAG_NO_NORM);
+ *     TWOMAMBA_EXP: lse_t = ln sum_{s<=t} exp(scale q_t.k_s + lambda_ts);
+ *     TWOMAMBA_LIN: none; returns TWOMAMBA_ERR_UNSUPPORTED.
+ * row_stat may not overlap any other argument.  The other arguments, results
+ * and errors are those of twomamba_fwd.
+ */
+int twomamba_fwd_stats(const twomamba_fwd_desc* desc,
+                       const void* q, const void* k, const void* v, const float* z,
+                       const float* state_in, const float* norm_in,
+                       void* out, float* state_out, float* norm_out, float* row_stat,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step of 2Mamba for every (b, h)  [2M2F §2 constant-size
@@ -314,6 +336,11 @@ int twomamba_step_conv(const twomamba_step_desc* desc,
  *   out       [B][H][T][dv]  dtype   device   the forward's output for these inputs
  *                                             (only dout_t . out_t is used)
  *   dout      [B][H][T][dv]  dtype   device
+ *   row_stat  [B][H][T]      fp32    device   the row statistics twomamba_fwd_stats wrote for
+ *                                             these inputs (no initial state), or NULL: then
+ *                                             the backward recomputes them (one more pass over
+ *                                             the keys).  Ignored by TWOMAMBA_LIN and, being
+ *                                             unused there, by TWOMAMBA_SQ with NO_NORM.
  *   dq, dk    [B][H][T][dk]  dtype   device   written
  *   dv        [B][H][T][dv]  dtype   device   written
  *   dz        [B][H][T]      fp32    device   written
@@ -325,7 +352,7 @@ int twomamba_bwd_workspace_size(const twomamba_fwd_desc* desc, size_t* bytes);
 
 int twomamba_bwd(const twomamba_fwd_desc* desc,
                  const void* q, const void* k, const void* v, const float* z,
-                 const void* out, const void* dout,
+                 const void* out, const void* dout, const float* row_stat,
                  void* dq, void* dk, void* dv, float* dz,
                  void* workspace, size_t workspace_bytes, void* stream);
 
@@ -333,7 +360,7 @@ int twomamba_bwd(const twomamba_fwd_desc* desc,
    twomamba_fwd_timed (the call waits for the stream). */
 int twomamba_bwd_timed(const twomamba_fwd_desc* desc,
                        const void* q, const void* k, const void* v, const float* z,
-                       const void* out, const void* dout,
+                       const void* out, const void* dout, const float* row_stat,
                        void* dq, void* dk, void* dv, float* dz,
                        void* workspace, size_t workspace_bytes, void* stream,
                        float* kernel_ms, const char** kernel_names, int cap, int* n_kernels);

@@ -634,29 +634,31 @@ def bwd_blocked(q, k, v, z, dout, variant="sq", scale=1.0, norm=True, block=512)
 # weight sum (the normaliser of [2M2F §5]) and the 2Mamba-E log-sum-exp
 # ----------------------------------------------------------------------------
 
-def row_weight_sums(q, k, z, scale=1.0, state_in_norm=None):
+def row_weight_sums(q, k, z, scale=1.0, state_in_norm=None, rows=None):
     """den_t = sum_{s<=t} L_ts (scale q_t.k_s)^2, plus exp(g_0+...+g_t)
-    phi_q(scale q_t).n0 for an initial normaliser n0 -> [B, H, T]."""
+    phi_q(scale q_t).n0 for an initial normaliser n0 -> [B, H, T] (or
+    [B, H, len(rows)] for the listed rows t only)."""
     g = decay_log(z)
-    T = q.shape[2]
-    den = np.zeros(q.shape[:3])
-    for t in range(T):
+    rows = range(q.shape[2]) if rows is None else rows
+    den = np.zeros(q.shape[:2] + (len(rows),))
+    for i, t in enumerate(rows):
         L = np.exp(_row_log_mask(g[:, :, :t + 1]))
         a = scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], k[:, :, :t + 1])
-        den[:, :, t] = (L * a * a).sum(axis=-1)
+        den[:, :, i] = (L * a * a).sum(axis=-1)
         if state_in_norm is not None:
-            den[:, :, t] += np.exp(g[:, :, :t + 1].sum(axis=-1)) * np.einsum(
+            den[:, :, i] += np.exp(g[:, :, :t + 1].sum(axis=-1)) * np.einsum(
                 "bhp,bhp->bh", phi_q(scale * q[:, :, t]), state_in_norm)
     return den
 
 
-def row_logsumexp(q, k, z, scale=1.0):
-    """lse_t = log sum_{s<=t} exp(scale q_t.k_s + lambda_ts) (natural log) -> [B, H, T]."""
+def row_logsumexp(q, k, z, scale=1.0, rows=None):
+    """lse_t = log sum_{s<=t} exp(scale q_t.k_s + lambda_ts) (natural log) -> [B, H, T]
+    (or [B, H, len(rows)] for the listed rows t only)."""
     g = decay_log(z)
-    T = q.shape[2]
-    lse = np.zeros(q.shape[:3])
-    for t in range(T):
+    rows = range(q.shape[2]) if rows is None else rows
+    lse = np.zeros(q.shape[:2] + (len(rows),))
+    for i, t in enumerate(rows):
         logit = scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], k[:, :, :t + 1]) + _row_log_mask(g[:, :, :t + 1])
         m = logit.max(axis=-1)
-        lse[:, :, t] = m + np.log(np.exp(logit - m[..., None]).sum(axis=-1))
+        lse[:, :, i] = m + np.log(np.exp(logit - m[..., None]).sum(axis=-1))
     return lse

@@ -84,6 +84,9 @@ def load(path: str | None = None):
     lib.twomamba_fwd.restype = ctypes.c_int
     lib.twomamba_fwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    lib.twomamba_fwd_stats.restype = ctypes.c_int
+    lib.twomamba_fwd_stats.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
     lib.twomamba_fwd_timed.restype = ctypes.c_int
     lib.twomamba_fwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
@@ -100,10 +103,10 @@ def load(path: str | None = None):
     lib.twomamba_bwd_workspace_size.restype = ctypes.c_int
     lib.twomamba_bwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(ctypes.c_size_t)]
     lib.twomamba_bwd.restype = ctypes.c_int
-    lib.twomamba_bwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+    lib.twomamba_bwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
     lib.twomamba_bwd_timed.restype = ctypes.c_int
-    lib.twomamba_bwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+    lib.twomamba_bwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
                                        ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.twomamba_conv2.restype = ctypes.c_int
@@ -165,9 +168,13 @@ def _check(t, shape, dtype, name):
 
 def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, reference_kernels=False,
         state_in=None, norm_in=None, want_state=False, out=None, state_out=None, norm_out=None, workspace=None,
-        kernel_times=None):
+        kernel_times=None, want_stats=False, row_stat=None):
     """Chunked forward.  Returns out, or (out, state_out, norm_out) with want_state.
 
+    With ``want_stats`` (or a ``row_stat`` tensor [B, H, T] fp32 to fill) the
+    call goes through twomamba_fwd_stats and the per-row statistic (the 2Mamba
+    weight sum, the 2Mamba-E log-sum-exp) is appended to what is returned:
+    (out, row_stat) or (out, state_out, norm_out, row_stat); bwd takes it.
     With ``kernel_times`` (a list), the call goes through twomamba_fwd_timed:
     it waits for completion and appends (kernel name, milliseconds) per launch.
     """
@@ -191,13 +198,23 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
         state_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
         if not lin:
             norm_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    stats = want_stats or row_stat is not None
+    if stats:
+        if kernel_times is not None:
+            raise ValueError("kernel_times is not available with row statistics")
+        if row_stat is None:
+            row_stat = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+        _check(row_stat, (B, H, T), torch.float32, "row_stat")
     nbytes = workspace_size(desc)
     if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state_in), _ptr(norm_in),
-            _ptr(out), _ptr(state_out), _ptr(norm_out), _ptr(workspace) if nbytes else None,
-            ctypes.c_size_t(nbytes), _stream())
-    if kernel_times is None:
+    head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state_in), _ptr(norm_in),
+            _ptr(out), _ptr(state_out), _ptr(norm_out))
+    tail = (_ptr(workspace) if nbytes else None, ctypes.c_size_t(nbytes), _stream())
+    args = head + tail
+    if stats:
+        s = load().twomamba_fwd_stats(*head, _ptr(row_stat), *tail)
+    elif kernel_times is None:
         s = load().twomamba_fwd(*args)
     else:
         cap = 8
@@ -208,10 +225,11 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
         for i in range(min(cnt.value, cap)):
             kernel_times.append((names[i].decode(), float(ms[i])))
     if s != 0:
-        raise TwoMambaError(s, "twomamba_fwd")
-    if want_state or state_out is not None:
-        return out, state_out, norm_out
-    return out
+        raise TwoMambaError(s, "twomamba_fwd_stats" if stats else "twomamba_fwd")
+    res = (out, state_out, norm_out) if want_state or state_out is not None else (out,)
+    if stats:
+        res += (row_stat,)
+    return res if len(res) > 1 else out
 
 
 def step(q, k, v, z, state, norm, *, scale=1.0, no_norm=False, first_order=False, out=None):
@@ -309,11 +327,12 @@ def exp_step(q, k, v, z, k_cache, v_cache, g_cache, pos, *, scale=1.0, out=None,
 
 
 def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, reference_kernels=False,
-        grads=None, workspace=None, kernel_times=None):
+        grads=None, workspace=None, kernel_times=None, row_stat=None):
     """Backward of fwd (no initial state): returns (dq, dk, dv, dz).
 
-    ``out`` is the forward output for the same inputs; ``grads`` may supply the
-    four output tensors.  With ``kernel_times`` (a list) the call goes through
+    ``out`` is the forward output for the same inputs; ``row_stat`` the
+    forward's row statistics (fwd(..., want_stats=True)), or None to have the
+    backward recompute them; ``grads`` may supply the four output tensors.  With ``kernel_times`` (a list) the call goes through
     twomamba_bwd_timed and appends (kernel name, milliseconds) per launch.
     """
     B, H, T, dk = q.shape
@@ -326,6 +345,8 @@ def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, refere
     _check(z, (B, H, T), torch.float32, "z")
     _check(out, (B, H, T, dv), q.dtype, "out")
     _check(dout, (B, H, T, dv), q.dtype, "dout")
+    if row_stat is not None:
+        _check(row_stat, (B, H, T), torch.float32, "row_stat")
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z))
     gq, gk, gv, gz = grads
@@ -336,8 +357,8 @@ def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, refere
     nbytes = bwd_workspace_size(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(out), _ptr(dout), _ptr(gq), _ptr(gk),
-            _ptr(gv), _ptr(gz), _ptr(workspace), ctypes.c_size_t(nbytes), _stream())
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(out), _ptr(dout), _ptr(row_stat),
+            _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gz), _ptr(workspace), ctypes.c_size_t(nbytes), _stream())
     if kernel_times is None:
         s = load().twomamba_bwd(*args)
     else:

@@ -147,14 +147,14 @@ int twomamba_fwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
 
 static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
                     const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
-                    void* workspace, size_t workspace_bytes, void* stream, twm::KTimer* timer) {
+                    float* row_stat, void* workspace, size_t workspace_bytes, void* stream, twm::KTimer* timer) {
     size_t qkb, vb, zb, sb, nb;
     int s = check_desc(d, &qkb, &vb, &zb, &sb, &nb);
     if (s != TWOMAMBA_OK) return s;
     const bool any = qkb != 0;   // B*H*T > 0
     const bool sq = d->variant == TWOMAMBA_SQ, lin = d->variant == TWOMAMBA_LIN;
     if (!sq && !lin && (state_in || norm_in || state_out || norm_out)) return TWOMAMBA_ERR_UNSUPPORTED;
-    if (lin && (norm_in || norm_out)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (lin && (norm_in || norm_out || row_stat)) return TWOMAMBA_ERR_UNSUPPORTED;
     if (sq && (state_in == nullptr) != (norm_in == nullptr)) return TWOMAMBA_ERR_NULL;
     if (sq && (state_out == nullptr) != (norm_out == nullptr)) return TWOMAMBA_ERR_NULL;
     if (any && (!q || !k || !v || !z || !out)) return TWOMAMBA_ERR_NULL;
@@ -172,6 +172,9 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     if (overlaps(rso, rsi) && state_out != state_in) return TWOMAMBA_ERR_ALIAS;
     if (overlaps(rno, rni) && norm_out != norm_in) return TWOMAMBA_ERR_ALIAS;
     if (overlaps(rso, rni) || overlaps(rno, rsi)) return TWOMAMBA_ERR_ALIAS;
+    const Range rst = rng(row_stat, zb);   // [B][H][T] fp32, the size of z
+    for (const Range& x : {rq, rk, rv, rz, rsi, rni, ro, rso, rno})
+        if (overlaps(rst, x)) return TWOMAMBA_ERR_ALIAS;
 
     FwdArgs a;
     plan(d, &a);
@@ -182,7 +185,7 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     if (need > 0) {
         if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
         const Range rw = rng(workspace, need);
-        for (const Range& o : {rq, rk, rv, rz, rsi, rni, ro, rso, rno})
+        for (const Range& o : {rq, rk, rv, rz, rsi, rni, ro, rso, rno, rst})
             if (overlaps(rw, o)) return TWOMAMBA_ERR_ALIAS;
     }
     a.q = q; a.k = k; a.v = v; a.z = z;
@@ -190,6 +193,7 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     a.out = out; a.state_out = state_out; a.norm_out = norm_out;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
     a.timer = timer;
+    a.row_stat = row_stat;
     if (path == LINP) return twm::lin_fwd(a);
     if (a.variant == TWOMAMBA_EXP) return path == MFMA ? twm::mfma_exp_fwd(a) : twm::ref_exp_fwd(a);
     return path == MFMA ? twm::mfma_sq_fwd(a) : twm::ref_sq_fwd(a);
@@ -198,8 +202,19 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
 int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
                  const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
                  void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, workspace, workspace_bytes, stream,
-                    nullptr);
+    return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, nullptr, workspace, workspace_bytes,
+                    stream, nullptr);
+}
+
+int twomamba_fwd_stats(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                       const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
+                       float* row_stat, void* workspace, size_t workspace_bytes, void* stream) {
+    size_t qkb, vb, zb, sb, nb;
+    int s = check_desc(d, &qkb, &vb, &zb, &sb, &nb);
+    if (s != TWOMAMBA_OK) return s;
+    if (qkb != 0 && !row_stat) return TWOMAMBA_ERR_NULL;
+    return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, row_stat, workspace, workspace_bytes,
+                    stream, nullptr);
 }
 
 int twomamba_fwd_timed(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
@@ -210,8 +225,8 @@ int twomamba_fwd_timed(const twomamba_fwd_desc* d, const void* q, const void* k,
     *n_kernels = 0;
     twm::KTimer t;
     memset(&t, 0, sizeof(t));
-    int s = fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, workspace, workspace_bytes, stream,
-                     &t);
+    int s = fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, nullptr, workspace, workspace_bytes,
+                     stream, &t);
     const int c = twm::ktimer_collect(&t, kernel_ms, kernel_names, cap < 0 ? 0 : cap);
     *n_kernels = t.n;
     return s != TWOMAMBA_OK ? s : c;
@@ -430,8 +445,8 @@ int twomamba_bwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
 }
 
 static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
-                    const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
-                    size_t workspace_bytes, void* stream, twm::KTimer* timer) {
+                    const void* out, const void* dout, const float* row_stat, void* dq, void* dk, void* dv, float* dz,
+                    void* workspace, size_t workspace_bytes, void* stream, twm::KTimer* timer) {
     size_t qkb, vb, zb;
     int s = check_bwd(d, &qkb, &vb, &zb);
     if (s != TWOMAMBA_OK) return s;
@@ -440,7 +455,8 @@ static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     twm::BwdArgs a = bwd_args(d);
     const size_t need = twm::bwd_workspace(a);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
-    const Range ins[] = {rng(q, qkb), rng(k, qkb), rng(v, vb), rng(z, zb), rng(out, vb), rng(dout, vb)};
+    const Range ins[] = {rng(q, qkb), rng(k, qkb), rng(v, vb), rng(z, zb), rng(out, vb), rng(dout, vb),
+                         rng(row_stat, zb)};
     const Range outs[] = {rng(dq, qkb), rng(dk, qkb), rng(dv, vb), rng(dz, zb), rng(workspace, need)};
     for (const Range& o : outs)
         for (const Range& in : ins)
@@ -449,26 +465,27 @@ static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
         for (int j = i + 1; j < 5; ++j)
             if (overlaps(outs[i], outs[j])) return TWOMAMBA_ERR_ALIAS;
     a.q = q; a.k = k; a.v = v; a.z = z; a.out = out; a.dout = dout;
+    a.row_stat = d->variant == TWOMAMBA_LIN ? nullptr : row_stat;   // the first order has none
     a.gq = dq; a.gk = dk; a.gv = dv; a.gz = dz;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream; a.timer = timer;
     return twm::mfma_bwd_supported(a) ? twm::mfma_bwd(a) : twm::ref_bwd(a);
 }
 
 int twomamba_bwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
-                 const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
-                 size_t workspace_bytes, void* stream) {
-    return bwd_impl(d, q, k, v, z, out, dout, dq, dk, dv, dz, workspace, workspace_bytes, stream, nullptr);
+                 const void* out, const void* dout, const float* row_stat, void* dq, void* dk, void* dv, float* dz,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(d, q, k, v, z, out, dout, row_stat, dq, dk, dv, dz, workspace, workspace_bytes, stream, nullptr);
 }
 
 int twomamba_bwd_timed(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
-                       const void* out, const void* dout, void* dq, void* dk, void* dv, float* dz, void* workspace,
-                       size_t workspace_bytes, void* stream, float* kernel_ms, const char** kernel_names, int cap,
-                       int* n_kernels) {
+                       const void* out, const void* dout, const float* row_stat, void* dq, void* dk, void* dv,
+                       float* dz, void* workspace, size_t workspace_bytes, void* stream, float* kernel_ms,
+                       const char** kernel_names, int cap, int* n_kernels) {
     if (!n_kernels) return TWOMAMBA_ERR_NULL;
     *n_kernels = 0;
     twm::KTimer t;
     memset(&t, 0, sizeof(t));
-    int s = bwd_impl(d, q, k, v, z, out, dout, dq, dk, dv, dz, workspace, workspace_bytes, stream, &t);
+    int s = bwd_impl(d, q, k, v, z, out, dout, row_stat, dq, dk, dv, dz, workspace, workspace_bytes, stream, &t);
     const int c = twm::ktimer_collect(&t, kernel_ms, kernel_names, cap < 0 ? 0 : cap);
     *n_kernels = t.n;
     return s != TWOMAMBA_OK ? s : c;

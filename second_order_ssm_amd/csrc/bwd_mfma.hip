@@ -73,8 +73,9 @@ template <int kVar>
 __global__ void __launch_bounds__(kThreads, kMinBlocks)
 bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const bf16* __restrict__ out, const bf16* __restrict__ dout, const double* __restrict__ G,
-             float* __restrict__ Dt, float* __restrict__ stat, float* __restrict__ rowsum, bf16* __restrict__ dq,
-             int T, int nqb, float scale, int norm, int use_d, int by_xcd) {
+             const float* __restrict__ fstat, float* __restrict__ Dt, float* __restrict__ stat,
+             float* __restrict__ rowsum, bf16* __restrict__ dq, int T, int nqb, float scale, int norm, int use_d,
+             int by_xcd) {
     __shared__ __attribute__((aligned(16))) QSmem sm;
     int bh, blk;
     xcd_map(blockIdx.x, nqb, by_xcd, bh, blk);
@@ -123,11 +124,10 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 
     Stage sk, sv;
     // ---------------------------------------------------------- sweep 1: statistic
+    // (none for the first order; not needed without normalisation or when the
+    // forward handed it over)
+    const bool need_sweep1 = kVar != kLin && !fstat && !(kVar == kSq && !norm);
     float den = 0.f, m = -INFINITY, l = 0.f;
-    fetch(sk, k + base * kD, min(kTile, T), tid);
-    store(sk, sm.K[0], tid);
-    stage_a(0, 0);
-    __syncthreads();
     auto sweep1 = [&](int kt, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = kt & 1, s0 = kt * kTile;
@@ -168,7 +168,11 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             }
         }
     };
-    if (kVar != kLin) {   // the first order has no row statistic
+    if (need_sweep1) {
+        fetch(sk, k + base * kD, min(kTile, T), tid);
+        store(sk, sm.K[0], tid);
+        stage_a(0, 0);
+        __syncthreads();
         for (int kt = 0; kt < qb; ++kt) {   // key tiles wholly before the queries
             const int cur = kt & 1, s0 = kt * kTile;
             fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
@@ -181,19 +185,23 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         __syncthreads();
     }
     float st_v, cq;   // row statistic; cq: b2 + lse2 (2Mamba-E) or -D / den (2Mamba)
+    const float given = fstat ? fstat[base + tc] : 0.f;   // lse_t (natural log) or den_t from the forward
     if (kVar == kLin) {
         st_v = 1.f;
         cq = 0.f;
     } else if (kVar == kExpV) {
-        // combine the four lane groups' (m, l)
-        float M = fmaxf(m, __shfl_xor(m, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float lsc = (m == -INFINITY) ? 0.f : l * fexp2(m - M);
-        const float L = xor_sum(lsc);
-        st_v = M + flog2(L);
+        if (fstat) {
+            st_v = given * kLog2e;
+        } else {   // combine the four lane groups' (m, l)
+            float M = fmaxf(m, __shfl_xor(m, 16));
+            M = fmaxf(M, __shfl_xor(M, 32));
+            const float lsc = (m == -INFINITY) ? 0.f : l * fexp2(m - M);
+            const float L = xor_sum(lsc);
+            st_v = M + flog2(L);
+        }
         cq = b2 + st_v;
     } else {
-        const float dn = xor_sum(den) * scale * scale;
+        const float dn = fstat ? given : xor_sum(den) * scale * scale;
         st_v = norm ? (dn > 0.f ? 1.f / dn : 0.f) : 1.f;
         cq = -Dq * st_v;
     }
@@ -472,8 +480,8 @@ int launch(const BwdArgs& a, const BwdScratch& s) {
     const int by_xcd = (a.B * a.H) % kXcd == 0;
     ktimer_begin(a.timer, "bwd_q", a.stream);
     hipLaunchKernelGGL((bwd_q_kernel<kVar>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.out, (const bf16*)a.dout, s.G, s.Dt,
-                       s.stat, s.rowsum, (bf16*)a.gq, a.T, nb, a.scale, norm, use_d, by_xcd);
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.out, (const bf16*)a.dout, s.G, a.row_stat,
+                       s.Dt, s.stat, s.rowsum, (bf16*)a.gq, a.T, nb, a.scale, norm, use_d, by_xcd);
     ktimer_end(a.timer, a.stream);
     ktimer_begin(a.timer, "bwd_kv", a.stream);
     hipLaunchKernelGGL((bwd_kv_kernel<kVar>), dim3(a.B * a.H * nb), dim3(kThreads), 0, st, (const bf16*)a.q,

@@ -103,8 +103,8 @@ template <int D, typename In, int kVar>
 __global__ void __launch_bounds__(kTile)
 bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
                  const In* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
-                 float* __restrict__ stat, float* __restrict__ rowsum, In* __restrict__ dq, int T, int nqt,
-                 float scale, int norm) {
+                 const float* __restrict__ fstat, float* __restrict__ stat, float* __restrict__ rowsum,
+                 In* __restrict__ dq, int T, int nqt, float scale, int norm) {
     __shared__ float s_k[kTile][D], s_v[kTile][D];
     __shared__ double s_g[kTile];
     const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
@@ -138,9 +138,11 @@ bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* _
         return Lk;
     };
 
-    // pass 1: row statistic (none for the first order)
+    // pass 1: row statistic (none for the first order; not needed without
+    // normalisation or when the forward handed it over)
     float den = 0.f, m = -INFINITY, l = 0.f;
-    for (int kt = 0; kt <= (kVar == kLin ? -1 : qt); ++kt) {
+    const bool sweep = kVar != kLin && !fstat && !(kVar == kSq && !norm);
+    for (int kt = 0; kt <= (sweep ? qt : -1); ++kt) {
         const int Lk = stage(kt);
         const int s0 = kt * kTile;
         if (!active) continue;
@@ -160,10 +162,16 @@ bwd_ref_q_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* _
             }
         }
     }
+    const float given = fstat && active ? fstat[base + t] : 0.f;   // lse_t or den_t from the forward
     float st;
-    if (kVar == kExpV) st = m + logf(l);
-    else if (kVar == kSq) st = norm ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
-    else st = 1.f;
+    if (kVar == kExpV) {
+        st = fstat ? given : m + logf(l);
+    } else if (kVar == kSq) {
+        if (fstat) den = given;
+        st = norm ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
+    } else {
+        st = 1.f;
+    }
 
     // pass 2: dq and rowsum
     float rs = 0.f;
@@ -382,8 +390,8 @@ static int launch_ref(const BwdArgs& a, const BwdScratch& s) {
     const int norm = !(a.flags & TWOMAMBA_FLAG_NO_NORM);
     ktimer_begin(a.timer, "ref_bwd_q", a.stream);
     hipLaunchKernelGGL((bwd_ref_q_kernel<D, In, kVar>), dim3(a.B * a.H * nt), dim3(kTile), 0, st, (const In*)a.q,
-                       (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, s.stat, s.rowsum, (In*)a.gq, a.T,
-                       nt, a.scale, norm);
+                       (const In*)a.k, (const In*)a.v, (const In*)a.dout, s.G, s.Dt, a.row_stat, s.stat, s.rowsum,
+                       (In*)a.gq, a.T, nt, a.scale, norm);
     ktimer_end(a.timer, a.stream);
     ktimer_begin(a.timer, "ref_bwd_kv", a.stream);
     hipLaunchKernelGGL((bwd_ref_kv_kernel<D, In, kVar>), dim3(a.B * a.H * nt), dim3(2 * kTile), 0, st,

@@ -373,7 +373,8 @@ __device__ __forceinline__ void tile_step(Slot* __restrict__ curp, Slot* __restr
 
 __global__ void __launch_bounds__(kThreads, 2)
 exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                const float* __restrict__ z, uint16_t* __restrict__ out, int T, int nqt, int nbh, float scale) {
+                const float* __restrict__ z, uint16_t* __restrict__ out, int T, int nqt, int nbh, float scale,
+                float* __restrict__ row_stat) {
     __shared__ Slot slot0, slot1, slot2;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lo = lane & 31, g = lane >> 5;
     const int qt = nqt - 1 - (int)(blockIdx.x / nbh);   // longest query tiles first
@@ -432,12 +433,23 @@ exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     }
 
     if (!wact) return;
+    // log-sum-exp of the true logits: the accumulator held scale^-1 (scale q.k - c_s)
+    // with c_s the softplus sum from s+1 to the wave end Ew, so add back c_t
+    float csuf = 0.f;
+    if (row_stat) {
+        const float sp = (tw + lane <= Ew) ? softplus_fast(z[base + tw + lane]) : 0.f;
+        const float incl = wave_scan(sp);
+        csuf = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63)) - incl;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const int t = tw + 32 * qb + lo;
         const float lt = half_sum(ws.l[qb]);
         const float inv = 1.f / lt;
+        const float ct = __shfl(csuf, 32 * qb + lo);
         if (t >= T) continue;
+        if (row_stat && g == 0)   // log2 of the sum, converted to the natural log
+            row_stat[base + t] = scale * ws.m[qb] + __builtin_amdgcn_logf(lt) * 0.6931471805599453f + ct;
         uint16_t* o = out + (base + t) * kD;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -465,7 +477,7 @@ int mfma_exp_fwd(const FwdArgs& a) {
     ktimer_begin(a.timer, "exp_mfma", a.stream);
     hipLaunchKernelGGL(exp_mfma_kernel, dim3((unsigned)nbh * nqt), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.z, (uint16_t*)a.out, a.T,
-                       nqt, nbh, a.scale);
+                       nqt, nbh, a.scale, a.row_stat);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

@@ -22,7 +22,8 @@ constexpr int kKT = 64;   // keys per LDS tile
 template <int DK, int DV, typename In>
 __global__ void __launch_bounds__(512)
 ref_exp_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
-               const float* __restrict__ z, In* __restrict__ out, int T, int nqt, float scale) {
+               const float* __restrict__ z, In* __restrict__ out, int T, int nqt, float scale,
+               float* __restrict__ row_stat) {
     constexpr int CGN = DV / 8;
     __shared__ float s_q[kQT][DK];
     __shared__ float s_k[kKT][DK], s_v[kKT][DV];
@@ -87,6 +88,7 @@ ref_exp_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __r
         if (kt != qt) M += s_tot;
     }
     if (!active) return;
+    if (row_stat && cg == 0) row_stat[base + t0 + tl] = m + logf(l);   // logits carry their true bias
     const float inv = 1.f / l;
 #pragma unroll
     for (int u = 0; u < 8; ++u) IO<In>::st(out, (base + t0 + tl) * DV + cg * 8 + u, acc[u] * inv);
@@ -99,7 +101,7 @@ int run(const FwdArgs& a) {
     ktimer_begin(a.timer, "ref_exp", a.stream);
     hipLaunchKernelGGL((ref_exp_kernel<DK, DV, In>), dim3(nbh * nqt), dim3(kQT * (DV / 8)), 0,
                        (hipStream_t)a.stream, (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, (In*)a.out,
-                       a.T, nqt, a.scale);
+                       a.T, nqt, a.scale, a.row_stat);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

@@ -40,7 +40,8 @@ struct FwdArgs {
     void* ws;
     size_t ws_bytes;
     void* stream;
-    KTimer* timer;   // NULL unless called through twomamba_fwd_timed
+    KTimer* timer;     // NULL unless called through twomamba_fwd_timed
+    float* row_stat;   // NULL, or [B][H][T]: weight sum (2Mamba) / log-sum-exp (2Mamba-E) per query
 };
 
 struct StepArgs {
@@ -127,6 +128,7 @@ struct BwdArgs {
     const void *q, *k, *v;
     const float* z;
     const void *out, *dout;
+    const float* row_stat;   // the forward's per-row statistic, or NULL (recomputed)
     void *gq, *gk, *gv;   // dL/dq, dL/dk, dL/dv
     float* gz;            // dL/dz
     void* ws;

@@ -332,7 +332,8 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                const float* __restrict__ state_in, const float* __restrict__ norm_in,
                float* __restrict__ state_out, float* __restrict__ norm_out,
                const float* __restrict__ ws_state, const float* __restrict__ ws_norm,
-               const float* __restrict__ ws_gam, int T, int nseg, int seg_chunks, float scale, int no_norm) {
+               const float* __restrict__ ws_gam, int T, int nseg, int seg_chunks, float scale, int no_norm,
+               float* __restrict__ row_stat) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
     const int tid = threadIdx.x;
@@ -790,6 +791,8 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 for (int e = 0; e < 4; ++e) o[e] = fmaf(oin[e], fin, osum[e] * r_num) * mul;
                 *reinterpret_cast<uint2*>(out + (tok_base + t0 + t) * kD + col0 + n0) =
                     make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                // the weight sum in true units (the common factor dropped above put back)
+                if (row_stat && half == 0 && n0 == 0) row_stat[tok_base + t0 + t] = den * back;
             }
         }
         lf = fs.lf_new;
@@ -1053,7 +1056,7 @@ int run(const FwdArgs& a) {
     ktimer_begin(a.timer, "sq_mfma_main", a.stream);
     hipLaunchKernelGGL(sq_main_kernel, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z, (bf16*)a.out,
                        a.state_in, a.norm_in, a.state_out, a.norm_out, (const float*)wsS, (const float*)wsN,
-                       (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm);
+                       (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm, a.row_stat);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

@@ -116,7 +116,7 @@ template <int DK, int DV, typename In>
 __global__ void __launch_bounds__(512)
 ref_sq_out(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
            const float* __restrict__ z, const float* __restrict__ wsS, const float* __restrict__ wsN,
-           In* __restrict__ out, int T, int C, int nc, float scale, int no_norm) {
+           In* __restrict__ out, int T, int C, int nc, float scale, int no_norm, float* __restrict__ row_stat) {
     constexpr int D = DK * (DK + 1) / 2;
     constexpr int CGN = DV / 8;
     constexpr int PTILE = 32;
@@ -194,6 +194,7 @@ ref_sq_out(const In* __restrict__ q, const In* __restrict__ k, const In* __restr
     if (!active) return;
     const float dt = expf(s_gl[tl]);
     den = fmaf(dt, iden, den);
+    if (row_stat && cg == 0) row_stat[tok0 + tl] = den;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const float nu = fmaf(dt, inum[u], num[u]);
@@ -232,7 +233,8 @@ int run(const FwdArgs& a) {
     ktimer_begin(a.timer, "ref_sq_out", a.stream);
     hipLaunchKernelGGL((ref_sq_out<DK, DV, In>), dim3(nbh * nc), dim3(a.chunk * (DV / 8)), 0, st,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, (const float*)wsS, (const float*)wsN,
-                       (In*)a.out, a.T, a.chunk, nc, a.scale, (int)((a.flags & TWOMAMBA_FLAG_NO_NORM) != 0));
+                       (In*)a.out, a.T, a.chunk, nc, a.scale, (int)((a.flags & TWOMAMBA_FLAG_NO_NORM) != 0),
+                       a.row_stat);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

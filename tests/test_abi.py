@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.twomamba_abi_version() == 1
+    assert lib.twomamba_abi_version() == 2
     seen = set()
     for s in range(8):
         txt = lib.twomamba_status_str(s).decode()
@@ -222,10 +222,11 @@ def test_exp_cache_fill_validation(lib):
 
 
 # ---------------------------------------------------------------- backward
-def call_bwd(lib, dsc, q=1, k=2, v=3, z=4, out=5, dout=6, dq=10, dk=11, dv=12, dz=13, ws=14, wsb=1 << 40):
+def call_bwd(lib, dsc, q=1, k=2, v=3, z=4, out=5, dout=6, rs=None, dq=10, dk=11, dv=12, dz=13, ws=14,
+             wsb=1 << 40):
     p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
     return lib.twomamba_bwd(ctypes.byref(dsc) if dsc is not None else None, p(q), p(k), p(v), p(z), p(out),
-                            p(dout), p(dq), p(dk), p(dv), p(dz), p(ws), ctypes.c_size_t(wsb), None)
+                            p(dout), p(rs), p(dq), p(dk), p(dv), p(dz), p(ws), ctypes.c_size_t(wsb), None)
 
 
 def bwd_ws(lib, dsc):
@@ -266,8 +267,34 @@ def test_bwd_pointer_checks(lib):
     assert call_bwd(lib, d, dv=ctypes.c_void_p(BASE + 6 * GAP + 64)) == EALIAS  # dv inside dout
     assert call_bwd(lib, d, dk=10) == EALIAS                                 # dk == dq
     assert call_bwd(lib, d, ws=13) == EALIAS                                 # workspace == dz
+    assert call_bwd(lib, d, rs=13) == EALIAS                                 # row statistics == dz
+    assert call_bwd(lib, d, rs=ctypes.c_void_p(BASE + 14 * GAP + 256)) == EALIAS   # inside the workspace
     assert call_bwd(lib, desc(B=0), q=None, k=None, v=None, z=None, out=None, dout=None, dq=None, dk=None,
                     dv=None, dz=None, ws=None, wsb=0) == OK
+
+
+# ---------------------------------------------------------------- forward with row statistics
+def call_fwd_stats(lib, dsc, rs=7, si=None, ni=None, so=None, no=None, ws=9, wsb=1 << 40):
+    p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
+    return lib.twomamba_fwd_stats(ctypes.byref(dsc), p(1), p(2), p(3), p(4), p(si), p(ni), p(5), p(so), p(no), p(rs),
+                                  p(ws), ctypes.c_size_t(wsb), None)
+
+
+def test_fwd_stats_pointer_checks(lib):
+    # the validation of the plain forward plus the statistics buffer: required,
+    # [B][H][T] fp32 disjoint from everything else, none for the first order
+    # (no call here gets past validation: nothing is launched)
+    d = desc(T=1000)                      # needs a workspace
+    n = 2 * 3 * 1000
+    assert call_fwd_stats(lib, d, rs=None) == ENULL
+    assert call_fwd_stats(lib, d, rs=4) == EALIAS                                        # == z
+    assert call_fwd_stats(lib, d, rs=ctypes.c_void_p(BASE + 4 * GAP + 4 * (n - 1))) == EALIAS   # last float of z
+    assert call_fwd_stats(lib, d, rs=ctypes.c_void_p(BASE + 4 * GAP + 4 * n), ws=None) == EWS   # just past z: taken
+    assert call_fwd_stats(lib, d, rs=9) == EALIAS                                        # == workspace
+    assert call_fwd_stats(lib, d, rs=5) == EALIAS                                        # == out
+    assert call_fwd_stats(lib, desc(variant=1), rs=2) == EALIAS                          # 2Mamba-E: == k
+    assert call_fwd_stats(lib, desc(variant=2)) == EUNSUP                                # first order: none
+    assert call_fwd_stats(lib, desc(B=0), rs=None, ws=None, wsb=0) == OK
 
 
 # ---------------------------------------------------------------- input convolution

@@ -374,3 +374,14 @@ def test_row_logsumexp_matches_torch_without_decay():
     s = np.where(np.tril(np.ones((17, 17), dtype=bool)), s, -np.inf)
     ref = torch.logsumexp(torch.tensor(s), dim=-1).numpy()
     np.testing.assert_allclose(O.row_logsumexp(q, k, z, scale=0.8), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_row_statistics_on_a_row_subset_are_those_rows():
+    r = np.random.default_rng(63)
+    q, k = (r.normal(size=(1, 2, 23, 4)) for _ in range(2))
+    z = r.normal(-1.0, 1.0, size=(1, 2, 23))
+    rows = [0, 5, 22]
+    np.testing.assert_array_equal(O.row_weight_sums(q, k, z, scale=0.9, rows=rows),
+                                  O.row_weight_sums(q, k, z, scale=0.9)[:, :, rows])
+    np.testing.assert_array_equal(O.row_logsumexp(q, k, z, scale=0.9, rows=rows),
+                                  O.row_logsumexp(q, k, z, scale=0.9)[:, :, rows])
