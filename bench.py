@@ -1,7 +1,8 @@
 """Benchmark of the 2Mamba operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--legs sq,exp,step,exp_step,bwd,exp_bwd,conv,lin,lin_step]
+                    [--legs sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,lin,
+                            lin_step]
                     [--cpu-seconds S]
 
 A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
@@ -9,7 +10,8 @@ chunk state, inter-chunk scan, readout, normalisation) over one batch of the
 long-context workload B=2, H=16, T=8192, d_k=d_v=64, bf16 inputs, seeded
 synthetic data.  ``value`` is its whole-job throughput in head-tokens/s with
 all inputs resident in HBM.  The same run also measures, each in its own timed
-loop, the 2Mamba-E forward on the same shape and the recurrent decode step
+loop, the 2Mamba forward at B=4 H=16 T=2048 and at B=1 H=16 T=32768, the
+2Mamba-E forward on the headline shape and the recurrent decode step
 (batch 64, 32 heads, fp32 packed state of 1.09 GB, 256 sequential steps after
 a T=2048 prefill) and the 2Mamba-E decode over a bf16 key/value cache (batch
 64, 32 heads, 256 sequential steps after a 2048-token prompt), and the
@@ -43,6 +45,9 @@ PEAK_HBM = 8.0e12               # MI355X HBM3E bytes/s
 
 SQ_SHAPE = dict(B=2, H=16, T=8192, d=64, seed=3)
 EXP_SHAPE = dict(B=2, H=16, T=8192, d=64, seed=3)
+# the other two 2Mamba workloads of the pages' shapes, reported beside the headline
+SQ_SHAPES_EXTRA = {"sq_4x16x2048": dict(B=4, H=16, T=2048, d=64, seed=1),
+                   "sq_1x16x32768": dict(B=1, H=16, T=32768, d=64, seed=2)}
 STEP_SHAPE = dict(B=64, H=32, d=64, prefill_T=2048, prefill_seed=4, steps=256)
 EXP_STEP_SHAPE = dict(B=64, H=32, d=64, prompt_T=2048, seed=4, steps=256)
 
@@ -103,7 +108,8 @@ def kernel_work(name, leg_work):
 KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "step_kernel": "step.hip",
                   "exp_decode_partial": "exp_step.hip", "exp_decode_combine": "exp_step.hip",
                   "bwd_q": "bwd_mfma.hip", "bwd_kv": "bwd_mfma.hip", "exp_bwd_q": "bwd_mfma.hip",
-                  "exp_bwd_kv": "bwd_mfma.hip", "conv2_kernel": "conv.hip"}
+                  "exp_bwd_kv": "bwd_mfma.hip", "conv2_kernel": "conv.hip", "lin_seg": "lin.hip",
+                  "lin_scan": "lin.hip", "lin_main": "lin.hip", "step_kernel_first_order": "step.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -169,13 +175,13 @@ def dominant_kernel(fn_timed, calls):
     return name, avg[name], avg
 
 
-def leg_sq(steps, warmup, variant="sq"):
+def leg_sq(steps, warmup, variant="sq", shape=None):
     import torch
 
     import second_order_ssm_amd as tmb
     import synth_inputs as SI
 
-    shp = SQ_SHAPE if variant == "sq" else EXP_SHAPE
+    shp = shape or (SQ_SHAPE if variant == "sq" else EXP_SHAPE)
     B, H, T, d = shp["B"], shp["H"], shp["T"], shp["d"]
     q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=shp["seed"], dtype="bf16"))
     out = torch.empty_like(v)
@@ -200,7 +206,9 @@ def leg_sq(steps, warmup, variant="sq"):
         tflops=work / (ms * 1e-3) / 1e12, frac_peak_bf16=work / (ms * 1e-3) / PEAK_BF16_FLOPS,
         kernels_ms=allk,
         roofline=dict(bound="mfma" if mfma else "alu", kernel=name, achieved=achieved / 1e12, peak=peak / 1e12,
-                      unit="TFLOP/s", frac=achieved / peak, traffic=measured_traffic(name)),
+                      unit="TFLOP/s", frac=achieved / peak,
+                      # the counter summary covers the headline shape only
+                      traffic=measured_traffic(name) if shape is None else None),
     )
 
 
@@ -299,7 +307,7 @@ def leg_lin(steps, warmup):
     return dict(workload=f"first-order (Mamba-2S) fwd B={B} H={H} T={T} d={d} bf16", ms=ms,
                 head_tokens_per_s=ht / (ms * 1e-3), bytes_per_call=byts, kernels_ms=allk,
                 roofline=dict(bound="hbm", kernel="+".join(allk), achieved=bw / 1e9, peak=PEAK_HBM / 1e9,
-                              unit="GB/s", frac=bw / PEAK_HBM, traffic=None))
+                              unit="GB/s", frac=bw / PEAK_HBM, traffic=traffic_sum(*allk)))
 
 
 def leg_lin_step(warmup):
@@ -332,7 +340,8 @@ def leg_lin_step(warmup):
     return dict(workload=f"first-order decode step B={B} H={H} d={d} fp32 state, {nsteps} sequential steps",
                 ms=ms, bytes_per_step=byts,
                 roofline=dict(bound="hbm", kernel="step_kernel (first order)", achieved=bw / 1e9,
-                              peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM, traffic=None))
+                              peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM,
+                              traffic=measured_traffic("step_kernel_first_order")))
 
 
 def leg_step(warmup):
@@ -461,7 +470,36 @@ def achievable_peaks():
     del a, b
     torch.cuda.empty_cache()
     return dict(copy_GBps=copy_bw / 1e9, copy_frac_of_peak=copy_bw / PEAK_HBM,
-                bf16_gemm_TFLOPs=gemm / 1e12, bf16_gemm_frac_of_peak=gemm / PEAK_BF16_FLOPS)
+                bf16_gemm_TFLOPs=gemm / 1e12, bf16_gemm_frac_of_peak=gemm / PEAK_BF16_FLOPS,
+                device=device_facts())
+
+
+def device_facts():
+    """What the device reports about itself: the published peaks assume 256
+    compute units at 2.4 GHz and 288 GB of HBM."""
+    import subprocess
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    facts = dict(name=p.name, arch=getattr(p, "gcnArchName", None), compute_units=p.multi_processor_count,
+                 hbm_GB=round(p.total_memory / 1e9, 1))
+    facts["max_clock_MHz"] = None
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        # one block per agent; the GPU agent's block names gfx950 (CPU agents report their own clocks)
+        for block in txt.split("*******"):
+            if "gfx950" not in block:
+                continue
+            for line in block.splitlines():
+                if "Max Clock Freq" in line:
+                    facts["max_clock_MHz"] = int(line.split(":")[1].split()[0])
+                if "Compute Unit:" in line:
+                    facts["rocminfo_compute_units"] = int(line.split(":")[1].split()[0])
+            break
+    except (OSError, subprocess.SubprocessError, ValueError, IndexError):
+        pass
+    return facts
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -482,7 +520,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sq,exp,step,exp_step,bwd,exp_bwd,conv,lin,lin_step")
+    ap.add_argument("--legs", default="sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,lin,"
+                                      "lin_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the copy / GEMM ceiling measurements")
@@ -504,6 +543,10 @@ def main():
     if "sq" in legs:
         res["sq"] = leg_sq(args.steps, args.warmup, "sq")
         print(f"[bench] sq leg done: {res['sq']['ms']:.3f} ms/step", file=sys.stderr, flush=True)
+    for name, shp in SQ_SHAPES_EXTRA.items():
+        if name in legs:
+            res[name] = leg_sq(args.steps, args.warmup, "sq", shp)
+            print(f"[bench] {name} leg done: {res[name]['ms']:.3f} ms/call", file=sys.stderr, flush=True)
     if "exp" in legs:
         res["exp"] = leg_sq(args.steps, args.warmup, "exp")
         print(f"[bench] exp leg done: {res['exp']['ms']:.3f} ms/call", file=sys.stderr, flush=True)
