@@ -29,10 +29,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 
 
 # Per-source extra device flags.  The 2Mamba-E kernel's row maxima are plain
-# fmaxf chains over MFMA results; without NaN semantics the compiler emits
-# v_max3 directly instead of canonicalising every operand first (NaN inputs
-# are undefined for the operator).
-FILE_FLAGS = {"exp_mfma.hip": ["-fno-honor-nans"]}
+# fmaxf chains over MFMA results, and the 2Mamba kernels' lane maxima of |q|,
+# |k|, |v|; without NaN semantics the compiler emits v_max3 directly instead of
+# canonicalising every operand first (NaN inputs are undefined for the operator).
+FILE_FLAGS = {"exp_mfma.hip": ["-fno-honor-nans"], "sq_mfma.hip": ["-fno-honor-nans"]}
 
 
 def sources():
