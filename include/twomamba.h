@@ -62,7 +62,7 @@ typedef enum {
     TWOMAMBA_ERR_NULL = 1,        /* a required pointer is NULL                     */
     TWOMAMBA_ERR_SHAPE = 2,       /* negative size, or sizes that overflow size_t   */
     TWOMAMBA_ERR_DTYPE = 3,       /* dtype or variant value not in its enum         */
-    TWOMAMBA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement    */
+    TWOMAMBA_ERR_UNSUPPORTED = 4, /* valid request the library does not implement   */
     TWOMAMBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
     TWOMAMBA_ERR_DEVICE = 6,      /* a HIP call failed (launch, attribute, device)  */
     TWOMAMBA_ERR_ALIAS = 7        /* an output overlaps an input it may not alias   */
