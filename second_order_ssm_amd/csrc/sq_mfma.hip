@@ -652,16 +652,17 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     } else {
                         A[4] = A[5] = A[6] = A[7] = (_Float16)0.f;
                     }
-                    O[tb][0] = mfma(A, B0, O[tb][0]);
-                    O[tb][1] = mfma(A, B1, O[tb][1]);
+                    // transposed product O^T = S^T phi_q^T: a lane ends with four consecutive
+                    // value columns of one token (one 16-byte LDS write below)
+                    O[tb][0] = mfma(B0, A, O[tb][0]);
+                    O[tb][1] = mfma(B1, A, O[tb][1]);
                 }
             }
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) sm.Op[wl][16 * tb + 4 * kg + b][16 * ct + l16] = O[tb][ct][b];
+                    *reinterpret_cast<f4*>(&sm.Op[wl][16 * tb + l16][16 * ct + 4 * kg]) = O[tb][ct];
         }
 
         // ------------------------------------------------ P3a: intra scores, den readout
@@ -670,25 +671,29 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int tile = 2 * wl + x, tt = tile >> 2, ts = tile & 3;
+                // transposed scores X^T = K Q^T: a lane holds keys 4kg..4kg+3 of one query,
+                // i.e. four consecutive entries of its row of A (one 8-byte LDS write)
+                const int t = 16 * tt + l16;
                 if (ts <= tt) {
                     f4 X = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        const h8 a = *reinterpret_cast<const h8*>(&sm.Q[16 * tt + l16][32 * kk + 8 * kg]);
+                        const h8 a = *reinterpret_cast<const h8*>(&sm.Q[t][32 * kk + 8 * kg]);
                         const h8 b = *reinterpret_cast<const h8*>(&sm.K[16 * ts + l16][32 * kk + 8 * kg]);
-                        X = mfma(a, b, X);
+                        X = mfma(b, a, X);
                     }
-                    const int s = 16 * ts + l16;
-                    const float gls = sm.Gl[s];
+                    const float glt = sm.Gl[t];
+                    const f4 gls = *reinterpret_cast<const f4*>(&sm.Gl[16 * ts + 4 * kg]);
+                    h4 av;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const int t = 16 * tt + 4 * kg + b;
-                        const float a = (s <= t) ? X[b] * X[b] * fexp2((sm.Gl[t] - gls) * kLog2e) : 0.f;
-                        sm.A[t][s] = (_Float16)a;
+                        const int s = 16 * ts + 4 * kg + b;
+                        const float a = (s <= t) ? X[b] * X[b] * fexp2((glt - gls[b]) * kLog2e) : 0.f;
+                        av[b] = (_Float16)a;
                     }
+                    *reinterpret_cast<h4*>(&sm.A[t][16 * ts + 4 * kg]) = av;
                 } else {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) sm.A[16 * tt + 4 * kg + b][16 * ts + l16] = (_Float16)0.f;
+                    *reinterpret_cast<h4*>(&sm.A[t][16 * ts + 4 * kg]) = h4{0, 0, 0, 0};
                 }
             }
             // den readout: Y = Q N~, then sum_j Q[t][j] Y[t][j]
@@ -719,31 +724,27 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         {
             const int tb = wl & 3;
             const int nk = tb >= 2 ? 2 : 1;
+            // transposed products (V^T A^T): a lane ends with four consecutive value columns of
+            // one query
             if (wl < 4) {
                 f4 Y0 = f4{0.f, 0.f, 0.f, 0.f}, Y1 = Y0;
                 for (int kk = 0; kk < nk; ++kk) {
                     const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
                     const h8 b0 = *reinterpret_cast<const h8*>(&sm.VT[l16][32 * kk + 8 * kg]);
                     const h8 b1 = *reinterpret_cast<const h8*>(&sm.VT[16 + l16][32 * kk + 8 * kg]);
-                    Y0 = mfma(a, b0, Y0);
-                    Y1 = mfma(a, b1, Y1);
+                    Y0 = mfma(b0, a, Y0);
+                    Y1 = mfma(b1, a, Y1);
                 }
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    sm.Oin[16 * tb + 4 * kg + b][l16] = Y0[b];
-                    sm.Oin[16 * tb + 4 * kg + b][16 + l16] = Y1[b];
-                }
+                *reinterpret_cast<f4*>(&sm.Oin[16 * tb + l16][4 * kg]) = Y0;
+                *reinterpret_cast<f4*>(&sm.Oin[16 * tb + l16][16 + 4 * kg]) = Y1;
             } else {
                 f4 Y = f4{0.f, 0.f, 0.f, 0.f};
                 for (int kk = 0; kk < nk; ++kk) {
                     const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
                     const h8 b = *reinterpret_cast<const h8*>(&sm.VT[kDV + l16][32 * kk + 8 * kg]);
-                    Y = mfma(a, b, Y);
+                    Y = mfma(b, a, Y);
                 }
-                if (l16 == 0) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) sm.Dint[16 * tb + 4 * kg + b] = Y[b];
-                }
+                if (kg == 0) sm.Dint[16 * tb + l16] = Y[0];   // every row of the ones block is the row sum
             }
         }
 
