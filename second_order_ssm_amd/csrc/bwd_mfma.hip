@@ -103,11 +103,20 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         Dq = xor_sum(Dq);
     }
     const float sl2 = scale * kLog2e;
+    // Off the diagonal tile every key precedes every query of the block, so the
+    // decay 2^(a_s - b_t) splits into a key factor 2^a_s and a query factor
+    // 2^-b_t, each in (0, 1] (G rises along the sequence and the reference is the
+    // block's first query): one multiply per pair instead of an exp2.  The
+    // diagonal tile keeps the exact exponent.  2Mamba-E folds the decay into its
+    // softmax exponent and always takes the log form.
+    constexpr bool kSplit = kVar != kExpV;
+    const float eb = kSplit ? fexp2(-b2) : 0.f;
 
-    auto stage_a = [&](int buf, int s0) {
+    auto stage_a = [&](int buf, int s0, bool split) {
         if (tid < kTile) {
             const int s = s0 + tid;
-            sm.A[buf][tid] = s < T ? (float)(G[base + s] - gref) * kLog2e : -INFINITY;
+            const float a = s < T ? (float)(G[base + s] - gref) * kLog2e : -INFINITY;
+            sm.A[buf][tid] = (kSplit && split) ? fexp2(a) : a;   // 2^a, or a
         }
     };
     // S^T[s][t] for the key tiles st = 2h, 2h+1 of 16
@@ -151,7 +160,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                         y[4 * u + i] = yy;
                         mx = fmaxf(mx, yy);
                     } else {
-                        float L = fexp2(av[i] - b2);
+                        float L = kDiag ? fexp2(av[i] - b2) : av[i] * eb;
                         L = masked ? 0.f : L;
                         den = fmaf(L * S[u][i], S[u][i], den);
                     }
@@ -171,14 +180,14 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     if (need_sweep1) {
         fetch(sk, k + base * kD, min(kTile, T), tid);
         store(sk, sm.K[0], tid);
-        stage_a(0, 0);
+        stage_a(0, 0, 0 < qb);
         __syncthreads();
         for (int kt = 0; kt < qb; ++kt) {   // key tiles wholly before the queries
             const int cur = kt & 1, s0 = kt * kTile;
             fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
             sweep1(kt, std::false_type{});
             store(sk, sm.K[cur ^ 1], tid);
-            stage_a(cur ^ 1, s0 + kTile);
+            stage_a(cur ^ 1, s0 + kTile, kt + 1 < qb);
             __syncthreads();
         }
         sweep1(qb, std::true_type{});
@@ -215,7 +224,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     fetch(sv, v + base * kD, min(kTile, T), tid);
     store(sk, sm.K[0], tid);
     store(sv, sm.V[0], tid);
-    stage_a(0, 0);
+    stage_a(0, 0, 0 < qb);
     __syncthreads();
     auto sweep2 = [&](int kt, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
@@ -250,12 +259,12 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                         d = p * (P[u][i] - Dq);
                         Mv = d;
                     } else if (kVar == kSq) {
-                        const float uu = fexp2(av[i] - b2) * x;
+                        const float uu = (kDiag ? fexp2(av[i] - b2) : av[i] * eb) * x;
                         const float dw = fmaf(P[u][i], st_v, cq);
                         d = uu * dw;
                         Mv = x * d;
                     } else {
-                        d = fexp2(av[i] - b2) * P[u][i];
+                        d = (kDiag ? fexp2(av[i] - b2) : av[i] * eb) * P[u][i];
                         Mv = x * d;
                     }
                     if (kDiag) {
@@ -280,7 +289,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         sweep2(kt, std::false_type{});
         store(sk, sm.K[cur ^ 1], tid);
         store(sv, sm.V[cur ^ 1], tid);
-        stage_a(cur ^ 1, s0 + kTile);
+        stage_a(cur ^ 1, s0 + kTile, kt + 1 < qb);
         __syncthreads();
     }
     sweep2(qb, std::true_type{});
@@ -328,16 +337,23 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     const int sc = sv_ok ? s : T - 1;
     const double gref = G[base + k0];
     const float a2 = sv_ok ? (float)(G[base + sc] - gref) * kLog2e : -INFINITY;
+    // Off the diagonal tile every query follows every key of the block, so the
+    // decay splits into a key factor and a query factor, each in (0, 1], taken
+    // against the block's last key (see the query-major kernel).
+    constexpr bool kSplit = kVar != kExpV;
+    const double gend = G[base + min(k0 + kBlk - 1, T - 1)];
+    const float ea = (kSplit && sv_ok) ? fexp2((float)(G[base + sc] - gend) * kLog2e) : 0.f;
     const b8 Kb[2] = {own_op(k + (base + sc) * kD, g, 0), own_op(k + (base + sc) * kD, g, 1)};
     const b8 Vb[2] = {own_op(v + (base + sc) * kD, g, 0), own_op(v + (base + sc) * kD, g, 1)};
     const float sl2 = scale * kLog2e;
 
-    auto stage_rows = [&](int buf, int t0) {
+    auto stage_rows = [&](int buf, int t0, bool split) {
         if (tid < kTile) {
             const int t = t0 + tid;
-            float b = INFINITY, r = 0.f, c = 0.f;
+            const bool lin = kSplit && split;   // B holds 2^-b (query factor) instead of b
+            float b = lin ? 0.f : INFINITY, r = 0.f, c = 0.f;
             if (t < T) {
-                b = (float)(G[base + t] - gref) * kLog2e;
+                b = lin ? fexp2(-(float)(G[base + t] - gend) * kLog2e) : (float)(G[base + t] - gref) * kLog2e;
                 const float st = stat[base + t], d = Dt[base + t];
                 if (kVar == kLin) {
                 } else if (kVar == kExpV) {
@@ -364,7 +380,7 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     fetch(so, dout + (base + k0) * kD, min(kTile, T - k0), tid);
     store(sq, sm.Q[0], tid);
     store(so, sm.O[0], tid);
-    stage_rows(0, k0);
+    stage_rows(0, k0, false);   // the diagonal tile
     __syncthreads();
     auto tile = [&](int it, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
@@ -405,13 +421,13 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
                         d = pp * (DP[u][i] - cv[i]);
                         Mv = d;
                     } else if (kVar == kSq) {
-                        const float uu = fexp2(a2 - bv[i]) * x;
+                        const float uu = (kDiag ? fexp2(a2 - bv[i]) : ea * bv[i]) * x;
                         pp = uu * x * rv[i];
                         const float dw = fmaf(DP[u][i], rv[i], cv[i]);
                         d = uu * dw;
                         Mv = x * d;
                     } else {
-                        const float L = fexp2(a2 - bv[i]);
+                        const float L = kDiag ? fexp2(a2 - bv[i]) : ea * bv[i];
                         pp = L * x;
                         d = L * DP[u][i];
                         Mv = x * d;
@@ -447,7 +463,7 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         if (more) {
             store(sq, sm.Q[cur ^ 1], tid);
             store(so, sm.O[cur ^ 1], tid);
-            stage_rows(cur ^ 1, t0 + kTile);
+            stage_rows(cur ^ 1, t0 + kTile, true);
         }
         __syncthreads();
     };
