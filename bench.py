@@ -335,10 +335,24 @@ def leg_lin_step(warmup):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / nsteps
+    # the same steps captured once as a HIP graph and replayed: a 16 us step
+    # otherwise pays a launch gap each time
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(warmup, warmup + nsteps):
+            tmb.step(*steps_in[i], S, None, first_order=True, out=out)
+    graph.replay()
+    torch.cuda.synchronize()
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms_graph = a.elapsed_time(b) / nsteps
     byts = B * H * (2 * d * d * 4 + (3 * d + 1) * 4 + d * 4)
     bw = byts / (ms * 1e-3)
     return dict(workload=f"first-order decode step B={B} H={H} d={d} fp32 state, {nsteps} sequential steps",
-                ms=ms, bytes_per_step=byts,
+                ms=ms, bytes_per_step=byts, ms_graph_replay=ms_graph,
+                GBps_graph_replay=byts / (ms_graph * 1e-3) / 1e9,
                 roofline=dict(bound="hbm", kernel="step_kernel (first order)", achieved=bw / 1e9,
                               peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM,
                               traffic=measured_traffic("step_kernel_first_order")))
