@@ -359,3 +359,21 @@ def test_first_order_step_validation(lib):
     assert call(6) == EUNSUP                                                # first order takes no normaliser
     bad = tmb.StepDesc(2, 3, 64, 64, 1.0, 1, 8)
     assert lib.twomamba_step(ctypes.byref(bad), p(1), p(2), p(3), p(4), p(5), p(6), p(7), None) == EUNSUP
+
+
+# ---------------------------------------------------------------- no fallback
+def test_missing_library_fails_loudly(tmp_path):
+    # the binding has no CPU or oracle fallback: without the library it raises
+    with pytest.raises(RuntimeError):
+        tmb.load(str(tmp_path / "libtwomamba.so"))
+
+
+def test_product_package_never_touches_the_oracle():
+    # the oracle is test infrastructure: nothing under the package imports or
+    # names it
+    pkg = os.path.dirname(tmb.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                src = open(os.path.join(root, f), encoding="utf-8").read()
+                assert "oracle" not in src, f"{f} refers to the oracle"
