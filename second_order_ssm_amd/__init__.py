@@ -20,7 +20,7 @@ import torch
 __all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "step", "library_path",
            "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd", "conv2", "step_conv",
            "TwoMambaError", "SQ", "EXP", "LIN", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "FLAG_FIRST_ORDER",
-           "num_pairs"]
+           "num_pairs", "twomamba"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libtwomamba.so")
@@ -423,3 +423,35 @@ def step_conv(q, k, v, z, weight, bias, conv_state, state, norm, *, scale=1.0, n
     if s != 0:
         raise TwoMambaError(s, "twomamba_step_conv")
     return out
+
+
+# ---------------------------------------------------------------------------
+# autograd: the forward keeps its row statistics for the backward
+
+class _TwoMambaFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, z, variant, scale, no_norm):
+        q, k, v, z = (t.contiguous() for t in (q, k, v, z))
+        if variant == "lin":
+            out = fwd(q, k, v, z, variant=variant, scale=scale, no_norm=no_norm)
+            stat = None
+        else:
+            out, stat = fwd(q, k, v, z, variant=variant, scale=scale, no_norm=no_norm, want_stats=True)
+        ctx.save_for_backward(q, k, v, z, out, stat)
+        ctx.opts = (variant, scale, no_norm)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, z, out, stat = ctx.saved_tensors
+        variant, scale, no_norm = ctx.opts
+        dq, dk, dv, dz = bwd(q, k, v, z, out, dout.contiguous(), variant=variant, scale=scale, no_norm=no_norm,
+                             row_stat=stat)
+        return dq, dk, dv, dz, None, None, None
+
+
+def twomamba(q, k, v, z, *, variant="sq", scale=1.0, no_norm=False):
+    """Differentiable operator: out = fwd(q, k, v, z); the backward runs
+    twomamba_bwd with the forward's row statistics.  q, k, v [B,H,T,d] (bf16 or
+    fp32, d = 16 or 64), z [B,H,T] fp32, no initial state."""
+    return _TwoMambaFn.apply(q, k, v, z, variant, scale, no_norm)
