@@ -199,7 +199,7 @@ struct Smem {
     float Oin[kC][kDV + 4];     // intra numerator
     float Dint[kC];             // intra denominator
     float Dinter[2][kC];        // normaliser readout partials
-    float Gl[kC];               // chunk-local inclusive prefix of g
+    float Gl[2][kC];            // chunk-local inclusive prefix of g, by chunk parity
     float red[2][kWaves][4];    // per-wave maxima, double-buffered by chunk parity
     int zero;
 };
@@ -479,7 +479,35 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     if (tid == 0) sm.zero = 0;
 
     Raw raw;
-    if (c_begin < c_end) fetch<true>(raw, q, k, v, z, tok_base, T, c_begin * kC, tid & 63, w, col0);
+    // Per-wave maxima of |scale q|, |k|, |v| over the chunk rows in `raw`, published in
+    // red[c & 1]: the next barrier (the one that ends the previous chunk) makes them
+    // visible to the scale and frame choice, so the chunk needs no barrier of its own
+    // for them.
+    auto publish_max = [&](int c_pub, int lane_, int wl_) {
+        float qv[8], kv[8], vv[8];
+        unpack8(raw.q, qv);
+        unpack8(raw.k, kv);
+        unpack8(raw.v, vv);
+        float mq = 0.f, mk = 0.f, mv = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mq = fmaxf(mq, fabsf(qv[i] * scale));
+            mk = fmaxf(mk, fabsf(kv[i]));
+            mv = fmaxf(mv, fabsf(vv[i]));
+        }
+        mq = wave_max(mq);
+        mk = wave_max(mk);
+        mv = wave_max(mv);
+        if (lane_ == 0) {
+            sm.red[c_pub & 1][wl_][0] = mq;
+            sm.red[c_pub & 1][wl_][1] = mk;
+            sm.red[c_pub & 1][wl_][2] = mv;
+        }
+    };
+    if (c_begin < c_end) {
+        fetch<true>(raw, q, k, v, z, tok_base, T, c_begin * kC, tid & 63, w, col0);
+        publish_max(c_begin, tid & 63, w);
+    }
     __syncthreads();
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -496,31 +524,17 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         const int gq = l16 >> 2, bq4 = l16 & 3;
         const int wl = __builtin_amdgcn_readfirstlane(tidc >> 6);
 
-        // ------------------------------------------------ P1a: registers only
+        // ------------------------------------------------ P1a: registers only (the chunk's
+        // maxima were published before the barrier that ended the previous chunk)
         float qv[8], kv[8], vv[8];
         unpack8(raw.q, qv);
         unpack8(raw.k, kv);
         unpack8(raw.v, vv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] *= scale;
         const float g = (lane < Lc) ? decay_log_fast(raw.z) : 0.f;
         const float gl = wave_scan(g);                // Gl of token `lane`
         const float Gam = rdl(gl, 63);
-        float mq = 0.f, mk = 0.f, mv = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            qv[i] *= scale;
-            mq = fmaxf(mq, fabsf(qv[i]));
-            mk = fmaxf(mk, fabsf(kv[i]));
-            mv = fmaxf(mv, fabsf(vv[i]));
-        }
-        mq = wave_max(mq);
-        mk = wave_max(mk);
-        mv = wave_max(mv);
-        if (lane == 0) {
-            sm.red[par][wl][0] = mq;
-            sm.red[par][wl][1] = mk;
-            sm.red[par][wl][2] = mv;
-        }
-        __syncthreads();   // A
 
         // ------------------------------------------------ P1b: scales, frames, operands
         float Mq = 0.f, Mk = 0.f, Mv = 0.f;
@@ -568,7 +582,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     sm.VT[8 * wl + i][lane] = (_Float16)(vv[i] * svi);
                 }
             }
-            if (wl == 0) sm.Gl[lane] = gl;
+            if (wl == 0) sm.Gl[par][lane] = gl;
             // normaliser of S_c to fp16 (|N| <= 2^14)
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
@@ -682,8 +696,8 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                         const h8 b = *reinterpret_cast<const h8*>(&sm.K[16 * ts + l16][32 * kk + 8 * kg]);
                         X = mfma(b, a, X);
                     }
-                    const float glt = sm.Gl[t];
-                    const f4 gls = *reinterpret_cast<const f4*>(&sm.Gl[16 * ts + 4 * kg]);
+                    const float glt = sm.Gl[par][t];
+                    const f4 gls = *reinterpret_cast<const f4*>(&sm.Gl[par][16 * ts + 4 * kg]);
                     h4 av;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
@@ -768,6 +782,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             }
             update_norm(N, sm, wl, l16, kg);
         }
+        if (c + 1 < c_end) publish_max(c + 1, lane, wl);   // rows fetched above
         __syncthreads();   // D
 
         // ------------------------------------------------ P5: combine and write out
@@ -776,7 +791,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         {
             const int t = tidc >> 3, n0 = (tidc & 7) * 4;
             if (t < Lc) {
-                const float glt = sm.Gl[t] * kLog2e;
+                const float glt = sm.Gl[par][t] * kLog2e;
                 const float r_num = fexp2(glt + lf + 2.f * (float)ek);
                 const float r_den = fexp2(glt + lfn + 2.f * (float)ek);
                 const float fin = ldexpf(1.f, -evi);
