@@ -596,6 +596,10 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         __syncthreads();   // B
 
         // ------------------------------------------------ P2: readout of S_c
+        // Waves 4..7 share a SIMD with waves 0..3 and are the younger of each pair; left
+        // to age order they finish the readout last and then run alone.  Raising their
+        // issue priority for the readout evens the pair out.
+        if (wl >= 4) __builtin_amdgcn_s_setprio(2);
         {
             f4 O[4][2];
 #pragma unroll
@@ -679,6 +683,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     *reinterpret_cast<f4*>(&sm.Op[wl][16 * tb + l16][16 * ct + 4 * kg]) = O[tb][ct];
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // ------------------------------------------------ P3a: intra scores, den readout
         {
             // 16 tiles (tt, ts) of the 64 x 64 score matrix, two per wave; upper ones are zero
