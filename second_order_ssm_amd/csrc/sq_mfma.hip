@@ -86,7 +86,7 @@ __device__ __forceinline__ void tile_block(int w, int u, int& ib, int& jb) {
 // exponent e with x * 2^e in [0.5, 1) for x > 0; 0 for x == 0
 __device__ __forceinline__ int unit_exp(float x) {
     if (!(x > 0.f)) return 0;
-    return -(ilogbf(x) + 1);
+    return -__builtin_amdgcn_frexp_expf(x);   // x = m 2^e, m in [0.5, 1)
 }
 
 // DPP lane permutes inside a 16-lane row: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
@@ -567,12 +567,12 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             for (int i = 0; i < 8; ++i) {
                 const float qq = qv[i] * sq, kt = kv[i] * sk;
                 q8[i] = (_Float16)qq;
-                q28[i] = (_Float16)(2.f * qq);
                 k8[i] = (_Float16)kt;
                 sm.KT[8 * wl + i][lane] = (_Float16)kt;
                 sm.WKT[8 * wl + i][lane] = (_Float16)(kv[i] * swk);
             }
             *reinterpret_cast<h8*>(&sm.Q[lane][8 * wl]) = q8;
+            q28 = q8 + q8;   // exact doubling in fp16 (|q8| < 1)
             *reinterpret_cast<h8*>(&sm.Q2[lane][8 * wl]) = q28;
             *reinterpret_cast<h8*>(&sm.K[lane][8 * wl]) = k8;
             if (wl < 4) {
