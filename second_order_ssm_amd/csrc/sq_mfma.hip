@@ -15,9 +15,10 @@
 //    1 on, 0 below the dim diagonal) so the query side needs no per-slot weight;
 //    off-diagonal tiles hold S and the query side reads 2 q_i.
 //  * Per 64-token chunk c (S_c = state before the chunk):
-//      readout  O = phi_q(Q) . S_c           MFMA, K = pair slots; the state
-//               accumulators are themselves the B operand (a lane's rows
-//               4g..4g+3 of two tiles are exactly the K-slots it supplies)
+//      readout  O = phi_q(Q) . S_c           MFMA, K = pair slots, computed as
+//               O^T = S_c^T phi_q(Q)^T: the state accumulators are themselves
+//               the A operand (a lane's rows 4g..4g+3 of two tiles are exactly
+//               the K-slots it supplies)
 //      intra    A = (Q K^T)^2 * exp(Gl_t - Gl_s), s <= t; A . [V | 1]  (MFMA)
 //      den      q^T N q with the d x d normaliser N in accumulators  (MFMA)
 //      update   S_{c+1} = e^Gam S_c + phi(K)^T diag(w) V   MFMA, K = tokens
