@@ -119,3 +119,30 @@ def test_mfma_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("B,H,T,with_state", [
+    (1, 1, 16384, False),      # 64 segments of 4 chunks: the carries go through the segment scan
+    (1, 2, 6000 - 37, True),   # 19 segments, ragged last chunk, caller state folded into the first
+])
+def test_mfma_sq_many_segments(B, H, T, with_state):
+    # few heads and a long sequence split into many segments, with slow decay so
+    # that every carry matters; sampled rows against the oracle, and the final state
+    announce(f"MFMA SQ many segments B={B} H={H} T={T} state={with_state}")
+    d = 64
+    q, k, v, z = SI.draw(B, H, T, d, seed=110, dtype="bf16", z_mean=-10.0)
+    kw, S0, n0 = {}, None, None
+    if with_state:
+        S0d, n0d = oracle_state(B, H, d, seed=111, z_mean=-10.0)
+        kw = dict(state_in=S0d, norm_in=n0d)
+        S0, n0 = host64(S0d), host64(n0d)
+    out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True, **kw)
+    torch.cuda.synchronize()
+    qq, kk, vv, zz = o64(q, k, v, z)
+    rows = sorted({0, 1, 255, 256, 257, 1023, 1024, T // 3, T // 2, T - 300, T - 65, T - 64, T - 1})
+    ref = O.fwd_quadratic_rows(qq, kk, vv, zz, rows, state_in=S0, norm_in=n0)
+    e = relerr(host64(out)[:, :, rows], ref)
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz, state_in=S0, norm_in=n0)
+    es, en = relerr(host64(S), S_ref), relerr(host64(n), n_ref)
+    print(f"  rows err {e:.2e} state {es:.2e} norm {en:.2e}")
+    assert e < TOL["bf16"] and es < TOL["bf16"] and en < TOL["bf16"]
