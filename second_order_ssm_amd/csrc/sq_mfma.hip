@@ -31,8 +31,11 @@
 //    decayed carry is below 2^-40 of the bound (it cannot change an fp32 sum).
 //  * Long sequences are split into segments.  A first kernel computes every
 //    segment's own end state as one backward pass (a plain accumulation with
-//    weights relative to the segment end); the main kernel starts segment g
-//    from the decayed sum of the earlier segments' end states.
+//    weights relative to the segment end) and stores it as fp16 with one
+//    power-of-two scale per slot (2^-11 relative rounding, below that of the
+//    bf16 inputs); the main kernel starts segment g from the decayed sum of the
+//    earlier segments' end states, or, for heads with many segments, from one
+//    slot that a scan kernel has turned into the whole carry.
 #include <algorithm>
 #include <type_traits>
 
@@ -332,9 +335,9 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                const float* __restrict__ z, bf16* __restrict__ out,
                const float* __restrict__ state_in, const float* __restrict__ norm_in,
                float* __restrict__ state_out, float* __restrict__ norm_out,
-               const float* __restrict__ ws_state, const float* __restrict__ ws_norm,
+               const _Float16* __restrict__ ws_state, const float* __restrict__ ws_norm,
                const float* __restrict__ ws_gam, int T, int nseg, int seg_chunks, float scale, int no_norm,
-               float* __restrict__ row_stat, int scanned) {
+               float* __restrict__ row_stat, int scanned, const int* __restrict__ ws_exp) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
     const int tid = threadIdx.x;
@@ -401,28 +404,30 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 // (scanned: slot seg-1 already holds the whole carry, see sq_carry_scan)
                 const int h_end = scanned ? seg - 1 : 0;
                 for (int h = seg - 1; h >= h_end; --h) {
-                    const float wgt = fexp2(lw);
-                    const float* Wg = ws_state + ((size_t)(bh * ns1 + h) * 2 + half) * kStateHalf +
-                                      (size_t)w * 64 * kStateLane;
-                    // in batches of 12 loads, all in flight before any is used
+                    const size_t slot = (size_t)(bh * ns1 + h) * 2 + half;
+                    // fp16 slot with its own power-of-two scale, in two batches of loads,
+                    // each all in flight before any is used
+                    const float wgh = fexp2(lw - (float)ws_exp[slot]);
+                    const uint2* Wh = reinterpret_cast<const uint2*>(ws_state + slot * kStateHalf) +
+                                      (size_t)w * 64 * kTiles * 2;
 #pragma unroll
-                    for (int u0 = 0; u0 < kTiles; u0 += 6) {
-                        float4 xs[6][2];
+                    for (int u0 = 0; u0 < kTiles; u0 += 9) {
+                        uint2 xs[9][2];
 #pragma unroll
-                        for (int du = 0; du < 6; ++du)
+                        for (int du = 0; du < 9; ++du)
 #pragma unroll
                             for (int ct = 0; ct < 2; ++ct)
-                                if (u0 + du < kTiles)
-                                    xs[du][ct] = reinterpret_cast<const float4*>(Wg)[((u0 + du) * 2 + ct) * 64 + lane];
+                                if (u0 + du < kTiles) xs[du][ct] = Wh[((u0 + du) * 2 + ct) * 64 + lane];
 #pragma unroll
-                        for (int du = 0; du < 6; ++du)
+                        for (int du = 0; du < 9; ++du)
 #pragma unroll
                             for (int ct = 0; ct < 2; ++ct)
                                 if (u0 + du < kTiles) {
-                                    const float4 x = xs[du][ct];
-                                    S[u0 + du][ct] += wgt * f4{x.x, x.y, x.z, x.w};
+                                    const h4 hv = __builtin_bit_cast(h4, xs[du][ct]);
+                                    S[u0 + du][ct] += wgh * f4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
                                 }
                     }
+                    const float wgt = fexp2(lw);   // the normaliser slots are fp32
                     const float* Ng = ws_norm + (size_t)(bh * ns1 + h) * kNormWG;
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
@@ -869,8 +874,8 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 __global__ void __launch_bounds__(kThreads, 1)
 sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
                    const float* __restrict__ state_in, const float* __restrict__ norm_in,
-                   float* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
-                   int T, int nseg, int seg_chunks) {
+                   _Float16* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
+                   int* __restrict__ ws_exp, int T, int nseg, int seg_chunks) {
     __shared__ __attribute__((aligned(16))) SmemSeg sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -989,8 +994,8 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
 #pragma unroll
     for (int b = 0; b < 4; ++b) cacc[b] = b < kg ? 0.f : (b == kg ? 1.f : 2.f);
     const size_t wsi = (size_t)(bh * ns1 + seg);
-    float* Wg = ws_state + (wsi * 2 + half) * kStateHalf + (size_t)w * 64 * kStateLane;
     const float* Sg = state_in ? state_in + (size_t)bh * kPairs * kD : nullptr;
+    float mx = 0.f;
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) {
         int ib, jb;
@@ -1007,9 +1012,32 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
                     x[b] = fmaf(fin, s0, x[b]);
                 }
             }
-            reinterpret_cast<float4*>(Wg)[(u * 2 + ct) * 64 + lane] = make_float4(x[0], x[1], x[2], x[3]);
+            S[u][ct] = x;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(x[b]));
         }
     }
+    // fp16 slot: values scaled by 2^e so that the largest stays below 2^14 (the
+    // precision the readout's fp16 state operand has anyway); half the bytes for
+    // the main kernel to read back
+    mx = wave_max(mx);
+    if (lane == 0) sm.red[0][w][0] = mx;
+    __syncthreads();
+    float M = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, sm.red[0][i][0]);
+    const int e = uni(max(-120, min(120, unit_exp(M) + 14)));
+    const float sc = ldexpf(1.f, e);
+    uint2* Wh = reinterpret_cast<uint2*>(ws_state + (wsi * 2 + half) * kStateHalf) + (size_t)w * 64 * kTiles * 2;
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const f4 x = S[u][ct] * sc;
+            const h4 hv = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+            Wh[(u * 2 + ct) * 64 + lane] = __builtin_bit_cast(uint2, hv);
+        }
+    if (tid == 0) ws_exp[wsi * 2 + half] = e;
     if (half == 0) {
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -1032,30 +1060,69 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
 //     C_{h+1} = exp(Gam_h) C_h + dS_h,   C_1 = dS_0,
 // so that each main-kernel workgroup reads one slot instead of summing all
 // earlier ones (which costs a quadratic number of state reads).  One thread per
-// four consecutive floats of a head's slots (both value halves, then the
-// normaliser), sequential over the segments.
-constexpr int kScanElems = 2 * kStateHalf + kNormWG;   // floats per (head, slot)
+// four consecutive entries of a head's slots (both fp16 value halves, then the
+// fp32 normaliser), sequential over the segments, the running carry in fp32.
+// A state slot is stored as fp16 times 2^e with |entry| 2^e < 2^14; the carry's
+// exponent comes from a bound every thread of the slot computes alike,
+//     |C_{h+1}| <= 2^14 B_{h+1},   B_{h+1} = exp(Gam_h) B_h + 2^-e_h,
+// and is written to its own array (the segment pass's exponents stay as read).
+constexpr int kScanState = 2 * kStateHalf / 4;   // threads per head on the fp16 state
+constexpr int kScanElems = kScanState + kNormWG / 4;
 
 __global__ void __launch_bounds__(256)
-sq_carry_scan(float* __restrict__ ws_state, float* __restrict__ ws_norm, const float* __restrict__ ws_gam, int ns1,
-              int etiles) {
+sq_carry_scan(_Float16* __restrict__ ws_state, float* __restrict__ ws_norm, const float* __restrict__ ws_gam,
+              const int* __restrict__ ws_exp, int* __restrict__ ws_exps, int ns1, int etiles) {
     const int bh = blockIdx.x / etiles;
-    const int e = ((blockIdx.x % etiles) * 256 + threadIdx.x) * 4;
+    const int e = (blockIdx.x % etiles) * 256 + threadIdx.x;
     if (e >= kScanElems) return;
-    float* p0;
-    size_t stride;
-    if (e < 2 * kStateHalf) {
-        const int half = e / kStateHalf, off = e % kStateHalf;
-        p0 = ws_state + ((size_t)bh * ns1 * 2 + half) * kStateHalf + off;
-        stride = (size_t)2 * kStateHalf;
-    } else {
-        p0 = ws_norm + (size_t)bh * ns1 * kNormWG + (e - 2 * kStateHalf);
-        stride = kNormWG;
-    }
     const float* gam = ws_gam + (size_t)bh * ns1;
-    float4 c = *reinterpret_cast<const float4*>(p0);   // C_1 = dS_0
-    // the chain is serial in h: load eight slots ahead of it
-    constexpr int U = 8;
+    constexpr int U = 8;   // the chain is serial in h: loads run this many slots ahead
+    if (e < kScanState) {
+        const int half = (4 * e) / kStateHalf, off = (4 * e) % kStateHalf;
+        uint2* p0 = reinterpret_cast<uint2*>(ws_state + ((size_t)bh * ns1 * 2 + half) * kStateHalf + off);
+        const size_t stride = (size_t)2 * kStateHalf / 4;   // uint2 per slot (two value halves)
+        const int* ex = ws_exp + (size_t)bh * ns1 * 2 + half;
+        int* exs = ws_exps + (size_t)bh * ns1 * 2 + half;
+        const bool head = off == 0;   // one thread per half writes the exponents
+        const auto unpack = [](uint2 u, float sc) {
+            const h4 hv = __builtin_bit_cast(h4, u);
+            return f4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]} * sc;
+        };
+        int e0 = ex[0];
+        f4 c = unpack(p0[0], ldexpf(1.f, -e0));   // C_1 = dS_0, stored as it is
+        float bnd = ldexpf(1.f, -e0);
+        if (head) exs[0] = e0;
+        const auto step = [&](int h, uint2 x, int eh, float g) {
+            const float a = fexp2(g * kLog2e);
+            const float sc = ldexpf(1.f, -eh);
+            c = a * c + unpack(x, sc);
+            bnd = fmaf(a, bnd, sc);
+            const int en = max(-120, min(120, unit_exp(bnd)));
+            const f4 y = c * ldexpf(1.f, en);
+            const h4 hv = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+            p0[h * stride] = __builtin_bit_cast(uint2, hv);
+            if (head) exs[(size_t)h * 2] = en;
+        };
+        int h = 1;
+        for (; h + U <= ns1; h += U) {
+            uint2 x[U];
+            int eh[U];
+            float g[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                x[u] = p0[(h + u) * stride];
+                eh[u] = ex[(size_t)(h + u) * 2];
+                g[u] = gam[h + u];   // segment h's own decay carries C_h across it
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) step(h + u, x[u], eh[u], g[u]);
+        }
+        for (; h < ns1; ++h) step(h, p0[h * stride], ex[(size_t)h * 2], gam[h]);
+        return;
+    }
+    float* p0 = ws_norm + (size_t)bh * ns1 * kNormWG + 4 * (e - kScanState);
+    const size_t stride = kNormWG;
+    float4 c = *reinterpret_cast<const float4*>(p0);
     int h = 1;
     for (; h + U <= ns1; h += U) {
         float4 x[U];
@@ -1063,7 +1130,7 @@ sq_carry_scan(float* __restrict__ ws_state, float* __restrict__ ws_norm, const f
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             x[u] = *reinterpret_cast<const float4*>(p0 + (h + u) * stride);
-            g[u] = gam[h + u];   // segment h's own decay carries C_h across it
+            g[u] = gam[h + u];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1104,7 +1171,7 @@ Plan plan_for(const FwdArgs& a) {
 }
 
 struct WsLayout {
-    size_t off_state, off_norm, off_gam, total;
+    size_t off_state, off_norm, off_gam, off_exp, off_exps, total;
 };
 
 WsLayout ws_layout(const FwdArgs& a, const Plan& p) {
@@ -1112,9 +1179,11 @@ WsLayout ws_layout(const FwdArgs& a, const Plan& p) {
     const size_t ns1 = p.nseg > 1 ? (size_t)(p.nseg - 1) : 0;
     WsLayout L;
     L.off_state = 0;
-    L.off_norm = align256(nbh * ns1 * 2 * kStateHalf * sizeof(float));
+    L.off_norm = align256(nbh * ns1 * 2 * kStateHalf * sizeof(_Float16));
     L.off_gam = align256(L.off_norm + nbh * ns1 * kNormWG * sizeof(float));
-    L.total = ns1 ? align256(L.off_gam + nbh * ns1 * sizeof(float)) : 0;
+    L.off_exp = align256(L.off_gam + nbh * ns1 * sizeof(float));   // fp16 slots' scale exponents
+    L.off_exps = align256(L.off_exp + nbh * ns1 * 2 * sizeof(int));   // the scanned carries' exponents
+    L.total = ns1 ? align256(L.off_exps + nbh * ns1 * 2 * sizeof(int)) : 0;
     return L;
 }
 
@@ -1122,9 +1191,13 @@ int run(const FwdArgs& a) {
     const Plan p = plan_for(a);
     const WsLayout L = ws_layout(a, p);
     char* ws = (char*)a.ws;
-    float* wsS = L.total ? (float*)(ws + L.off_state) : nullptr;
+    _Float16* wsS = L.total ? (_Float16*)(ws + L.off_state) : nullptr;
     float* wsN = L.total ? (float*)(ws + L.off_norm) : nullptr;
     float* wsG = L.total ? (float*)(ws + L.off_gam) : nullptr;
+    int* wsE = L.total ? (int*)(ws + L.off_exp) : nullptr;
+    int* wsEs = L.total ? (int*)(ws + L.off_exps) : nullptr;
+    // carries: scanned in place for many segments, else summed by each main workgroup
+    const int scanned = p.nseg >= kScanFrom;
     const int nbh = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
     const int no_norm = (a.flags & TWOMAMBA_FLAG_NO_NORM) != 0;
@@ -1134,21 +1207,21 @@ int run(const FwdArgs& a) {
     if (p.nseg > 1) {
         ktimer_begin(a.timer, "sq_segstate", a.stream);
         hipLaunchKernelGGL(sq_segstate_kernel, dim3(nbh * (p.nseg - 1) * 2), dim3(kThreads), 0, st, k, v, a.z,
-                           a.state_in, a.norm_in, wsS, wsN, wsG, a.T, p.nseg, p.seg_chunks);
+                           a.state_in, a.norm_in, wsS, wsN, wsG, wsE, a.T, p.nseg, p.seg_chunks);
         ktimer_end(a.timer, a.stream);
     }
-    const int scanned = p.nseg >= kScanFrom;
     if (scanned) {
-        const int etiles = (kScanElems / 4 + 255) / 256;
+        const int etiles = (kScanElems + 255) / 256;
         ktimer_begin(a.timer, "sq_carry_scan", a.stream);
         hipLaunchKernelGGL(sq_carry_scan, dim3(nbh * etiles), dim3(256), 0, st, wsS, wsN, (const float*)wsG,
-                           p.nseg - 1, etiles);
+                           (const int*)wsE, wsEs, p.nseg - 1, etiles);
         ktimer_end(a.timer, a.stream);
     }
     ktimer_begin(a.timer, "sq_mfma_main", a.stream);
     hipLaunchKernelGGL(sq_main_kernel, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z, (bf16*)a.out,
-                       a.state_in, a.norm_in, a.state_out, a.norm_out, (const float*)wsS, (const float*)wsN,
-                       (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm, a.row_stat, scanned);
+                       a.state_in, a.norm_in, a.state_out, a.norm_out, (const _Float16*)wsS, (const float*)wsN,
+                       (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm, a.row_stat, scanned,
+                       (const int*)(scanned ? wsEs : wsE));
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
