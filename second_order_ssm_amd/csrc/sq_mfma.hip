@@ -499,11 +499,12 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         float mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            mq = fmaxf(mq, fabsf(qv[i] * scale));
+            mq = fmaxf(mq, fabsf(qv[i]));
             mk = fmaxf(mk, fabsf(kv[i]));
             mv = fmaxf(mv, fabsf(vv[i]));
         }
-        mq = wave_max(mq);
+        // max |q scale| = |scale| max |q| (rounding is monotone)
+        mq = wave_max(mq) * fabsf(scale);
         mk = wave_max(mk);
         mv = wave_max(mv);
         if (lane_ == 0) {
@@ -538,8 +539,6 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         unpack8(raw.q, qv);
         unpack8(raw.k, kv);
         unpack8(raw.v, vv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[i] *= scale;
         const float g = (lane < Lc) ? decay_log_fast(raw.z) : 0.f;
         const float gl = wave_scan(g);                // Gl of token `lane`
         const float Gam = rdl(gl, 63);
@@ -565,7 +564,9 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         const Frame fs = choose_frame(lf, Mb, lg, lcs);
         const Frame fn = choose_frame(lfn, Mn, lg, lcn);
         {
-            const float sq = ldexpf(1.f, eq), sk = ldexpf(1.f, ek);
+            // q scale 2^eq in one factor: the power of two is exact, so this rounds as
+            // (q scale) 2^eq does
+            const float sq = scale * ldexpf(1.f, eq), sk = ldexpf(1.f, ek);
             const float wt = (lane < Lc) ? fexp2((Gam - gl) * kLog2e) : 0.f;   // w_t = exp(Gam - Gl_t)
             const float swk = wt * fexp2(-fn.lf_new - (float)ek);             // (w k) operand, dN_acc = 2^-lfn dN
             const float swv = wt * fexp2(-fs.lf_new - 2.f * (float)ek);       // (w v) operand, dS_acc = 2^-lf dS
