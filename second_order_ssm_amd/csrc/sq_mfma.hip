@@ -60,6 +60,7 @@ constexpr int kLS = 72;         // LDS row stride in halves (144 B)
 constexpr int kRow = 2 * kLS;   // ... in bytes
 constexpr int kStateLane = kTiles * 2 * 4;            // fp32 state values per lane
 constexpr int kStateHalf = kWaves * 64 * kStateLane;  // per workgroup (one value half)
+static_assert(kStateHalf % 4 == 0, "fp16 slots are addressed in groups of four");
 constexpr int kNormWG = kD * kD;                      // full d x d normaliser
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTarget = 14.f;                       // log2 of the accumulator bound
@@ -335,7 +336,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                const float* __restrict__ z, bf16* __restrict__ out,
                const float* __restrict__ state_in, const float* __restrict__ norm_in,
                float* __restrict__ state_out, float* __restrict__ norm_out,
-               const _Float16* __restrict__ ws_state, const float* __restrict__ ws_norm,
+               const uint2* __restrict__ ws_state, const float* __restrict__ ws_norm,
                const float* __restrict__ ws_gam, int T, int nseg, int seg_chunks, float scale, int no_norm,
                float* __restrict__ row_stat, int scanned, const int* __restrict__ ws_exp) {
     __shared__ __attribute__((aligned(16))) Smem sm;
@@ -408,8 +409,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     // fp16 slot with its own power-of-two scale, in two batches of loads,
                     // each all in flight before any is used
                     const float wgh = fexp2(lw - (float)ws_exp[slot]);
-                    const uint2* Wh = reinterpret_cast<const uint2*>(ws_state + slot * kStateHalf) +
-                                      (size_t)w * 64 * kTiles * 2;
+                    const uint2* Wh = ws_state + slot * (kStateHalf / 4) + (size_t)w * 64 * kTiles * 2;
 #pragma unroll
                     for (int u0 = 0; u0 < kTiles; u0 += 9) {
                         uint2 xs[9][2];
@@ -875,7 +875,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 __global__ void __launch_bounds__(kThreads, 1)
 sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
                    const float* __restrict__ state_in, const float* __restrict__ norm_in,
-                   _Float16* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
+                   uint2* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
                    int* __restrict__ ws_exp, int T, int nseg, int seg_chunks) {
     __shared__ __attribute__((aligned(16))) SmemSeg sm;
     const int tid = threadIdx.x;
@@ -1029,7 +1029,7 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
     for (int i = 0; i < kWaves; ++i) M = fmaxf(M, sm.red[0][i][0]);
     const int e = uni(max(-120, min(120, unit_exp(M) + 14)));
     const float sc = ldexpf(1.f, e);
-    uint2* Wh = reinterpret_cast<uint2*>(ws_state + (wsi * 2 + half) * kStateHalf) + (size_t)w * 64 * kTiles * 2;
+    uint2* Wh = ws_state + (wsi * 2 + half) * (kStateHalf / 4) + (size_t)w * 64 * kTiles * 2;
 #pragma unroll
     for (int u = 0; u < kTiles; ++u)
 #pragma unroll
@@ -1071,7 +1071,7 @@ constexpr int kScanState = 2 * kStateHalf / 4;   // threads per head on the fp16
 constexpr int kScanElems = kScanState + kNormWG / 4;
 
 __global__ void __launch_bounds__(256)
-sq_carry_scan(_Float16* __restrict__ ws_state, float* __restrict__ ws_norm, const float* __restrict__ ws_gam,
+sq_carry_scan(uint2* __restrict__ ws_state, float* __restrict__ ws_norm, const float* __restrict__ ws_gam,
               const int* __restrict__ ws_exp, int* __restrict__ ws_exps, int ns1, int etiles) {
     const int bh = blockIdx.x / etiles;
     const int e = (blockIdx.x % etiles) * 256 + threadIdx.x;
@@ -1080,7 +1080,7 @@ sq_carry_scan(_Float16* __restrict__ ws_state, float* __restrict__ ws_norm, cons
     constexpr int U = 8;   // the chain is serial in h: loads run this many slots ahead
     if (e < kScanState) {
         const int half = (4 * e) / kStateHalf, off = (4 * e) % kStateHalf;
-        uint2* p0 = reinterpret_cast<uint2*>(ws_state + ((size_t)bh * ns1 * 2 + half) * kStateHalf + off);
+        uint2* p0 = ws_state + ((size_t)bh * ns1 * 2 + half) * (kStateHalf / 4) + off / 4;
         const size_t stride = (size_t)2 * kStateHalf / 4;   // uint2 per slot (two value halves)
         const int* ex = ws_exp + (size_t)bh * ns1 * 2 + half;
         int* exs = ws_exps + (size_t)bh * ns1 * 2 + half;
@@ -1192,7 +1192,7 @@ int run(const FwdArgs& a) {
     const Plan p = plan_for(a);
     const WsLayout L = ws_layout(a, p);
     char* ws = (char*)a.ws;
-    _Float16* wsS = L.total ? (_Float16*)(ws + L.off_state) : nullptr;
+    uint2* wsS = L.total ? (uint2*)(ws + L.off_state) : nullptr;   // fp16 x 4
     float* wsN = L.total ? (float*)(ws + L.off_norm) : nullptr;
     float* wsG = L.total ? (float*)(ws + L.off_gam) : nullptr;
     int* wsE = L.total ? (int*)(ws + L.off_exp) : nullptr;
@@ -1220,7 +1220,7 @@ int run(const FwdArgs& a) {
     }
     ktimer_begin(a.timer, "sq_mfma_main", a.stream);
     hipLaunchKernelGGL(sq_main_kernel, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z, (bf16*)a.out,
-                       a.state_in, a.norm_in, a.state_out, a.norm_out, (const _Float16*)wsS, (const float*)wsN,
+                       a.state_in, a.norm_in, a.state_out, a.norm_out, (const uint2*)wsS, (const float*)wsN,
                        (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm, a.row_stat, scanned,
                        (const int*)(scanned ? wsEs : wsE));
     ktimer_end(a.timer, a.stream);
