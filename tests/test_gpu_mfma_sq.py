@@ -146,3 +146,40 @@ def test_mfma_sq_many_segments(B, H, T, with_state):
     es, en = relerr(host64(S), S_ref), relerr(host64(n), n_ref)
     print(f"  rows err {e:.2e} state {es:.2e} norm {en:.2e}")
     assert e < TOL["bf16"] and es < TOL["bf16"] and en < TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,H,T", [
+    (1, 1, 4096),   # 16 segments: carries through the segment scan
+    (1, 4, 2048),   # 8 segments: carries summed in the main kernel's prologue
+])
+@pytest.mark.parametrize("mode", ["blocks", "huge", "tiny"])
+def test_mfma_sq_carry_magnitudes(B, H, T, mode):
+    # The segment end states are stored as fp16 with one power-of-two scale per
+    # slot.  Values far from unit scale, and slots whose magnitudes differ by up
+    # to 2^60 from one segment to the next, must come through the slots and the
+    # scan without overflow or loss.  Slow decay, so that every carry matters.
+    announce(f"MFMA SQ carry magnitudes B={B} H={H} T={T} mode={mode}")
+    d = 64
+    q, k, v, z = SI.draw(B, H, T, d, seed=120, dtype="f32", z_mean=-10.0)
+    if mode == "blocks":
+        # v scaled by 2^u per 256-token block, u in [-30, 30]
+        u = np.random.default_rng(121).integers(-30, 31, size=(T + 255) // 256)
+        f = torch.from_numpy(np.repeat(2.0 ** u, 256)[:T].astype(np.float32))
+        v = v * f[None, None, :, None]
+    elif mode == "huge":
+        v = v * 1e20
+    else:
+        k, v = k * 1e-6, v * 1e-20
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True)
+    torch.cuda.synchronize()
+    qq, kk, vv, zz = o64(q, k, v, z)
+    rows = sorted({0, 255, 256, 511, 1023, 1024, T // 2 + 7, T - 257, T - 1})
+    ref = O.fwd_quadratic_rows(qq, kk, vv, zz, rows)
+    got = host64(out)[:, :, rows]
+    assert np.isfinite(got).all()
+    e = relerr(got, ref)
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz)
+    es, en = relerr(host64(S), S_ref), relerr(host64(n), n_ref)
+    print(f"  rows err {e:.2e} state {es:.2e} norm {en:.2e}")
+    assert e < TOL["bf16"] and es < TOL["bf16"] and en < TOL["bf16"]
