@@ -1027,7 +1027,9 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
     float M = 0.f;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) M = fmaxf(M, sm.red[0][i][0]);
-    const int e = uni(max(-120, min(120, unit_exp(M) + 14)));
+    // an all-zero slot takes the largest exponent, so that it adds next to nothing
+    // to the bound the carry scan keeps
+    const int e = uni(M > 0.f ? max(-120, min(120, unit_exp(M) + 14)) : 120);
     const float sc = ldexpf(1.f, e);
     uint2* Wh = ws_state + (wsi * 2 + half) * (kStateHalf / 4) + (size_t)w * 64 * kTiles * 2;
 #pragma unroll

@@ -152,7 +152,7 @@ def test_mfma_sq_many_segments(B, H, T, with_state):
     (1, 1, 4096),   # 16 segments: carries through the segment scan
     (1, 4, 2048),   # 8 segments: carries summed in the main kernel's prologue
 ])
-@pytest.mark.parametrize("mode", ["blocks", "huge", "tiny"])
+@pytest.mark.parametrize("mode", ["blocks", "huge", "tiny", "zero_then_tiny"])
 def test_mfma_sq_carry_magnitudes(B, H, T, mode):
     # The segment end states are stored as fp16 with one power-of-two scale per
     # slot.  Values far from unit scale, and slots whose magnitudes differ by up
@@ -168,8 +168,14 @@ def test_mfma_sq_carry_magnitudes(B, H, T, mode):
         v = v * f[None, None, :, None]
     elif mode == "huge":
         v = v * 1e20
-    else:
+    elif mode == "tiny":
         k, v = k * 1e-6, v * 1e-20
+    else:
+        # a quarter of the sequence with k = 0 (all-zero segment states), the rest
+        # tiny: the zero slots must not swamp the scaling of the tiny carries
+        k = k.clone()
+        k[:, :, : T // 4] = 0
+        v = v * 1e-20
     q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
     out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True)
     torch.cuda.synchronize()
