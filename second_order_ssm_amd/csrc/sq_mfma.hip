@@ -23,7 +23,11 @@
 //      den      q^T N q with the d x d normaliser N in accumulators  (MFMA)
 //      update   S_{c+1} = e^Gam S_c + phi(K)^T diag(w) V   MFMA, K = tokens
 //  * Operands are fp16: per chunk q and k are scaled by powers of two to
-//    |x| < 1 (exact for bf16 inputs).  The accumulators carry a "frame"
+//    |x| < 1 (exact for bf16 inputs).  The intra weights and [V | 1] are bf16
+//    instead: a row whose weights are all tiny (its first token, or very strong
+//    decay with q nearly orthogonal to k) would underflow fp16 and lose its
+//    denominator, while bf16 keeps fp32's exponent range; the weights' rounding
+//    enters numerator and denominator alike.  The accumulators carry a "frame"
 //    (true value = acc * 2^lf) kept so that a running bound on |acc| stays at
 //    or below 2^14, which makes the readout's fp16 conversion a bare convert.
 //    The chunk decay is absorbed into the frame whenever the bound allows;
@@ -47,6 +51,8 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bh8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bh4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 64;          // head dim (keys and values)
@@ -66,6 +72,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTarget = 14.f;                       // log2 of the accumulator bound
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ f4 mfma(bh8 a, bh8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }   // no denormal fix-up
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -197,8 +206,8 @@ struct Smem {
     _Float16 KT[kD][kLS];       // k~^T [d][t]
     _Float16 WKT[kD][kLS];      // normaliser update operand (w k)^T [d][t]
     _Float16 WVT[kDV][kLS];     // state update operand (w v)^T [n][t]
-    _Float16 VT[kDV + 16][kLS]; // intra operand [v | 1]^T [n][t]; rows 32..47 are ones
-    _Float16 A[kC][kLS];        // intra weights [t][s]
+    __bf16 VT[kDV + 16][kLS];   // intra operand [v | 1]^T [n][t]; rows 32..47 are ones
+    __bf16 A[kC][kLS];          // intra weights [t][s]; bf16 for fp32's exponent range
     _Float16 NT[kD][kLS];       // normaliser (fp16) [j][i]
     float Op[kWaves][kC][kDV + 4];   // per-wave readout partials
     float Oin[kC][kDV + 4];     // intra numerator
@@ -483,7 +492,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     }
 
     // constant parts of LDS: ones rows of [V | 1]^T, the loop-opaque zero
-    for (int e = tid; e < 16 * kLS; e += kThreads) sm.VT[kDV + e / kLS][e % kLS] = (_Float16)1.f;
+    for (int e = tid; e < 16 * kLS; e += kThreads) sm.VT[kDV + e / kLS][e % kLS] = (__bf16)1.f;
     if (tid == 0) sm.zero = 0;
 
     Raw raw;
@@ -588,7 +597,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     sm.WVT[8 * wl + i][lane] = (_Float16)(vv[i] * swv);
-                    sm.VT[8 * wl + i][lane] = (_Float16)(vv[i] * svi);
+                    sm.VT[8 * wl + i][lane] = (__bf16)(vv[i] * svi);   // exact
                 }
             }
             if (wl == 0) sm.Gl[par][lane] = gl;
@@ -712,16 +721,16 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     }
                     const float glt = sm.Gl[par][t];
                     const f4 gls = *reinterpret_cast<const f4*>(&sm.Gl[par][16 * ts + 4 * kg]);
-                    h4 av;
+                    bh4 av;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         const int s = 16 * ts + 4 * kg + b;
                         const float a = (s <= t) ? X[b] * X[b] * fexp2((glt - gls[b]) * kLog2e) : 0.f;
-                        av[b] = (_Float16)a;
+                        av[b] = (__bf16)a;
                     }
-                    *reinterpret_cast<h4*>(&sm.A[t][16 * ts + 4 * kg]) = av;
+                    *reinterpret_cast<bh4*>(&sm.A[t][16 * ts + 4 * kg]) = av;
                 } else {
-                    *reinterpret_cast<h4*>(&sm.A[t][16 * ts + 4 * kg]) = h4{0, 0, 0, 0};
+                    *reinterpret_cast<bh4*>(&sm.A[t][16 * ts + 4 * kg]) = bh4{0, 0, 0, 0};
                 }
             }
             // den readout: Y = Q N~, then sum_j Q[t][j] Y[t][j]
@@ -757,9 +766,9 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             if (wl < 4) {
                 f4 Y0 = f4{0.f, 0.f, 0.f, 0.f}, Y1 = Y0;
                 for (int kk = 0; kk < nk; ++kk) {
-                    const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
-                    const h8 b0 = *reinterpret_cast<const h8*>(&sm.VT[l16][32 * kk + 8 * kg]);
-                    const h8 b1 = *reinterpret_cast<const h8*>(&sm.VT[16 + l16][32 * kk + 8 * kg]);
+                    const bh8 a = *reinterpret_cast<const bh8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
+                    const bh8 b0 = *reinterpret_cast<const bh8*>(&sm.VT[l16][32 * kk + 8 * kg]);
+                    const bh8 b1 = *reinterpret_cast<const bh8*>(&sm.VT[16 + l16][32 * kk + 8 * kg]);
                     Y0 = mfma(b0, a, Y0);
                     Y1 = mfma(b1, a, Y1);
                 }
@@ -768,8 +777,8 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             } else {
                 f4 Y = f4{0.f, 0.f, 0.f, 0.f};
                 for (int kk = 0; kk < nk; ++kk) {
-                    const h8 a = *reinterpret_cast<const h8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
-                    const h8 b = *reinterpret_cast<const h8*>(&sm.VT[kDV + l16][32 * kk + 8 * kg]);
+                    const bh8 a = *reinterpret_cast<const bh8*>(&sm.A[16 * tb + l16][32 * kk + 8 * kg]);
+                    const bh8 b = *reinterpret_cast<const bh8*>(&sm.VT[kDV + l16][32 * kk + 8 * kg]);
                     Y = mfma(b, a, Y);
                 }
                 if (kg == 0) sm.Dint[16 * tb + l16] = Y[0];   // every row of the ones block is the row sum

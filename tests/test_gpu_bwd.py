@@ -71,6 +71,12 @@ CASES = [
     # head counts that are multiples of 8 take the XCD-grouped block order
     ("sq", "bf16", 2, 4, 300, 64, -2.0, 1.0, False),
     ("exp", "bf16", 1, 8, 257, 64, -1.0, 1.0, False),
+    # strong decay (a bias near -4, for 2Mamba-E -2, per token): only the nearest
+    # pairs count.  Stronger decay leaves each output nearly its own value: dq and
+    # dk then shrink to the size of the bf16 rounding of the forward output that
+    # the backward is given, and the comparison measures that rounding.
+    ("sq", "bf16", 1, 2, 300, 64, 4.0, 1.0, False),
+    ("exp", "bf16", 1, 2, 300, 64, 2.0, 1.0, False),
 ]
 
 

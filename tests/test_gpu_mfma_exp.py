@@ -104,3 +104,16 @@ def test_mfma_exp_full_size_sampled_rows(zm):
         e = relerr(out[b:b + 1, h:h + 1, rows], ref)
         print(f"  head ({b},{h}) err {e:.2e}")
         assert e < TOL["bf16"]
+
+
+def test_mfma_exp_decay_resets():
+    # no decay except a near-total reset (bias about -50) every 97 tokens
+    announce("MFMA EXP decay resets B=1 H=2 T=1000")
+    q, k, v, z = SI.draw(1, 2, 1000, 64, seed=230, dtype="bf16")
+    z = torch.full_like(z, float("-inf"))
+    z[:, :, ::97] = 50.0
+    out = tmb.fwd(*dev(q, k, v, z), variant="exp")
+    torch.cuda.synchronize()
+    e = relerr(host64(out), O.fwd_exp_quadratic(*o64(q, k, v, z)))
+    print(f"  err out {e:.2e}")
+    assert e < TOL["bf16"]

@@ -40,6 +40,7 @@ CASES = [
     (1, 1, 1024, -10.0, False),    # 4 segments, slow decay: the carry matters
     (2, 1, 333, 0.0, True),        # no decay at all
     (1, 2, 1, 0.0, False),         # single token
+    (1, 2, 1000, 20.0, False),     # very strong decay: the carry vanishes every chunk
 ]
 
 
@@ -185,6 +186,26 @@ def test_mfma_sq_carry_magnitudes(B, H, T, mode):
     got = host64(out)[:, :, rows]
     assert np.isfinite(got).all()
     e = relerr(got, ref)
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz)
+    es, en = relerr(host64(S), S_ref), relerr(host64(n), n_ref)
+    print(f"  rows err {e:.2e} state {es:.2e} norm {en:.2e}")
+    assert e < TOL["bf16"] and es < TOL["bf16"] and en < TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 2, 1000), (1, 1, 4096)])
+def test_mfma_sq_decay_resets(B, H, T):
+    # no decay at all except a near-total reset (g about -50) every 97 tokens:
+    # the accumulators restart inside chunks, segments and across the scan
+    announce(f"MFMA SQ decay resets B={B} H={H} T={T}")
+    q, k, v, z = SI.draw(B, H, T, 64, seed=130, dtype="bf16")
+    z = torch.full_like(z, float("-inf"))
+    z[:, :, ::97] = 50.0
+    out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True)
+    torch.cuda.synchronize()
+    qq, kk, vv, zz = o64(q, k, v, z)
+    rows = sorted({0, 1, 96, 97, 98, 500, T // 2, T - 98, T - 97, T - 2, T - 1})
+    ref = O.fwd_quadratic_rows(qq, kk, vv, zz, rows)
+    e = relerr(host64(out)[:, :, rows], ref)
     S_ref, n_ref = O.final_state_direct(kk, vv, zz)
     es, en = relerr(host64(S), S_ref), relerr(host64(n), n_ref)
     print(f"  rows err {e:.2e} state {es:.2e} norm {en:.2e}")
