@@ -214,7 +214,9 @@ struct Smem {
     float Dint[kC];             // intra denominator
     float Dinter[2][kC];        // normaliser readout partials
     float Gl[2][kC];            // chunk-local inclusive prefix of g, by chunk parity
-    float red[2][kWaves][4];    // per-wave maxima, double-buffered by chunk parity
+    float qrow[kC][kWaves];     // per token, each wave's max |q scale| over its 8 dims
+    float red[2][kWaves][4];    // per-wave maxima of |k| [1], |v| [2], by chunk parity
+    int erow[2][kC];            // per-token query exponent, by chunk parity
     int zero;
 };
 
@@ -496,10 +498,10 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     if (tid == 0) sm.zero = 0;
 
     Raw raw;
-    // Per-wave maxima of |scale q|, |k|, |v| over the chunk rows in `raw`, published in
-    // red[c & 1]: the next barrier (the one that ends the previous chunk) makes them
-    // visible to the scale and frame choice, so the chunk needs no barrier of its own
-    // for them.
+    // Per-wave maxima of |k|, |v| over the chunk rows in `raw` and of |scale q| per
+    // token, published in red[c & 1] and qrow: the next barrier (the one that ends
+    // the previous chunk) makes them visible to the scale and frame choice, so the
+    // chunk needs no barrier of its own for them.
     auto publish_max = [&](int c_pub, int lane_, int wl_) {
         float qv[8], kv[8], vv[8];
         unpack8(raw.q, qv);
@@ -513,11 +515,10 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             mv = fmaxf(mv, fabsf(vv[i]));
         }
         // max |q scale| = |scale| max |q| (rounding is monotone)
-        mq = wave_max(mq) * fabsf(scale);
+        sm.qrow[lane_][wl_] = mq * fabsf(scale);
         mk = wave_max(mk);
         mv = wave_max(mv);
         if (lane_ == 0) {
-            sm.red[c_pub & 1][wl_][0] = mq;
             sm.red[c_pub & 1][wl_][1] = mk;
             sm.red[c_pub & 1][wl_][2] = mv;
         }
@@ -553,18 +554,24 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         const float Gam = rdl(gl, 63);
 
         // ------------------------------------------------ P1b: scales, frames, operands
-        float Mq = 0.f, Mk = 0.f, Mv = 0.f;
+        float Mk = 0.f, Mv = 0.f;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) {
-            Mq = fmaxf(Mq, sm.red[par][i][0]);
             Mk = fmaxf(Mk, sm.red[par][i][1]);
             if (i < 4) Mv = fmaxf(Mv, sm.red[par][i][2]);
         }
-        Mq = uni(Mq);
+        // Per-token query scale: a row's weights, intra and inter, numerator and
+        // denominator, all scale with the square of its query, so o_t does not depend
+        // on it, and a query far smaller than the chunk's largest keeps its products
+        // q_i q_j out of the fp16 subnormals.
+        const f4 qm0 = *reinterpret_cast<const f4*>(&sm.qrow[lane][0]);
+        const f4 qm1 = *reinterpret_cast<const f4*>(&sm.qrow[lane][4]);
+        const float Mq = fmaxf(fmaxf(fmaxf(qm0[0], qm0[1]), fmaxf(qm0[2], qm0[3])),
+                               fmaxf(fmaxf(qm1[0], qm1[1]), fmaxf(qm1[2], qm1[3])));
         Mk = uni(Mk);
         Mv = uni(Mv);
         const float lg = Gam * kLog2e;
-        const int eq = uni(max(-120, min(120, unit_exp(Mq))));
+        const int eq = max(-120, min(120, unit_exp(Mq)));   // per lane (token)
         const int ek = uni(max(-120, min(120, unit_exp(Mk))));
         const int evi = uni(max(-120, min(120, unit_exp(Mv) + 14)));
         const float lMk = (Mk > 0.f) ? flog2(Mk) : -INFINITY;
@@ -576,6 +583,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             // q scale 2^eq in one factor: the power of two is exact, so this rounds as
             // (q scale) 2^eq does
             const float sq = scale * ldexpf(1.f, eq), sk = ldexpf(1.f, ek);
+            if (wl == 0) sm.erow[par][lane] = eq;
             const float wt = (lane < Lc) ? fexp2((Gam - gl) * kLog2e) : 0.f;   // w_t = exp(Gam - Gl_t)
             const float swk = wt * fexp2(-fn.lf_new - (float)ek);             // (w k) operand, dN_acc = 2^-lfn dN
             const float swv = wt * fexp2(-fs.lf_new - 2.f * (float)ek);       // (w v) operand, dS_acc = 2^-lf dS
@@ -810,7 +818,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 
         // ------------------------------------------------ P5: combine and write out
         // o = (Oin 2^-evi + Osum r_num(t)) / (Dint + Dinter r_den(t)) after dropping the
-        // common factor 2^-(2eq+2ek) of numerator and denominator.
+        // common factor 2^-(2eq_t+2ek) of numerator and denominator.
         {
             const int t = tidc >> 3, n0 = (tidc & 7) * 4;
             if (t < Lc) {
@@ -819,7 +827,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 const float r_den = fexp2(glt + lfn + 2.f * (float)ek);
                 const float fin = ldexpf(1.f, -evi);
                 const float den = fmaf(sm.Dinter[0][t] + sm.Dinter[1][t], r_den, sm.Dint[t]);
-                const float back = fexp2(-2.f * (float)eq - 2.f * (float)ek);
+                const float back = fexp2(-2.f * (float)sm.erow[par][t] - 2.f * (float)ek);
                 const float mul = no_norm ? back : (den == 0.f ? 0.f : __builtin_amdgcn_rcpf(den));
                 f4 osum = *reinterpret_cast<const f4*>(&sm.Op[0][t][n0]);
 #pragma unroll

@@ -210,3 +210,28 @@ def test_mfma_sq_decay_resets(B, H, T):
     es, en = relerr(host64(S), S_ref), relerr(host64(n), n_ref)
     print(f"  rows err {e:.2e} state {es:.2e} norm {en:.2e}")
     assert e < TOL["bf16"] and es < TOL["bf16"] and en < TOL["bf16"]
+
+
+@pytest.mark.parametrize("no_norm", [False, True])
+def test_mfma_sq_small_query_rows(no_norm):
+    # Every 7th query is 1000x smaller than the rest, with weak decay, so that the
+    # carried state dominates.  A normalised output does not depend on its query's
+    # size, so those rows must be as accurate as the others (their products q_i q_j
+    # would sit in the fp16 subnormals under a chunk-wide query scale); without
+    # normalisation, and for the row statistic, they are compared on their own scale.
+    announce(f"MFMA SQ small query rows no_norm={no_norm}")
+    B, H, T = 1, 2, 1000
+    q, k, v, z = SI.draw(B, H, T, 64, seed=140, dtype="f32", z_mean=-10.0)
+    q = q.clone()
+    q[:, :, ::7] *= 1e-3
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    out, st = tmb.fwd(*dev(q, k, v, z), no_norm=no_norm, want_stats=True)
+    torch.cuda.synchronize()
+    qq, kk, vv, zz = o64(q, k, v, z)
+    rows = list(range(0, T, 7))
+    ref = O.fwd_quadratic_rows(qq, kk, vv, zz, rows, norm=not no_norm)
+    e = relerr(host64(out)[:, :, rows], ref)
+    den_ref = O.row_weight_sums(qq, kk, zz, rows=rows)
+    es = relerr(host64(st)[:, :, rows], den_ref)
+    print(f"  small rows err {e:.2e} statistic {es:.2e}")
+    assert e < TOL["bf16"] and es < TOL["bf16"]
