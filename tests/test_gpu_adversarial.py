@@ -133,3 +133,21 @@ def test_backward(variant, mode):
     print("  " + " ".join(f"{nm} {e:.2e}" for nm, e in errs.items()))
     for nm, e in errs.items():
         assert e < TOL["bf16"], f"{nm} {e:.3e}"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 64), ("f32", 16)])
+def test_sq_forward(mode, dtype, d):
+    # bf16, d = 64 takes the MFMA kernels; fp32 takes the reference kernels
+    announce(f"adversarial 2Mamba forward {mode} {dtype} d={d}")
+    q, k, v, z = adversarial(1, 2, 700, d, mode, seed=306, dtype=dtype)
+    out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True)
+    torch.cuda.synchronize()
+    qq, kk, vv = f64(q, k, v)
+    zz = SI.to_f64(z)
+    rows = list(range(0, 700, 7)) if mode == "small_q" else list(range(700))
+    ref = O.fwd_quadratic_rows(qq, kk, vv, zz, rows)
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz)
+    e, es, en = relerr(host64(out)[:, :, rows], ref), relerr(host64(S), S_ref), relerr(host64(n), n_ref)
+    print(f"  err {e:.2e} state {es:.2e} norm {en:.2e}")
+    assert e < TOL[dtype] and es < TOL[dtype] and en < TOL[dtype]
