@@ -151,3 +151,39 @@ def test_sq_forward(mode, dtype, d):
     e, es, en = relerr(host64(out)[:, :, rows], ref), relerr(host64(S), S_ref), relerr(host64(n), n_ref)
     print(f"  err {e:.2e} state {es:.2e} norm {en:.2e}")
     assert e < TOL[dtype] and es < TOL[dtype] and en < TOL[dtype]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_first_order_prompt_then_steps(mode):
+    announce(f"adversarial first-order prompt + steps {mode}")
+    B, H, d, T0, N = 1, 2, 64, 300, 6
+    q, k, v, z = adversarial(B, H, T0 + N, d, mode, seed=307)
+    qd, kd, vd, zd = dev(q, k, v, z)
+    _, S, _ = tmb.fwd(qd[:, :, :T0].contiguous(), kd[:, :, :T0].contiguous(), vd[:, :, :T0].contiguous(),
+                      zd[:, :, :T0].contiguous(), variant="lin", want_state=True)
+    outs = [tmb.step(*[x[:, :, t].contiguous() for x in (qd, kd, vd, zd)], S, None, first_order=True)
+            for t in range(T0, T0 + N)]
+    torch.cuda.synchronize()
+    got = np.stack([host64(o) for o in outs], axis=2)
+    qq, kk, vv = f64(q, k, v)
+    ref = O.fwd_linear_quadratic(qq, kk, vv, SI.to_f64(z))[:, :, T0:]
+    e = relerr(got, ref)
+    print(f"  err {e:.2e}")
+    assert e < TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["small_q", "huge_v", "tiny_k", "resets_decay"])
+def test_first_order_backward(mode):
+    announce(f"adversarial first-order backward {mode}")
+    B, H, T, d = 1, 2, 300, 64
+    q, k, v, z = adversarial(B, H, T, d, mode, seed=308)
+    do = torch.from_numpy(np.random.default_rng(309).standard_normal((B, H, T, d))).to(torch.bfloat16)
+    qd, kd, vd, zd, dod = dev(q, k, v, z, do)
+    out = tmb.fwd(qd, kd, vd, zd, variant="lin")
+    g = tmb.bwd(qd, kd, vd, zd, out, dod, variant="lin")
+    torch.cuda.synchronize()
+    ref = O.bwd_linear_quadratic(*f64(q, k, v), SI.to_f64(z), SI.to_f64(do))
+    errs = {nm: relerr(host64(a), r) for nm, a, r in zip(("dq", "dk", "dv", "dz"), g, ref)}
+    print("  " + " ".join(f"{nm} {e:.2e}" for nm, e in errs.items()))
+    for nm, e in errs.items():
+        assert e < TOL["bf16"], f"{nm} {e:.3e}"
