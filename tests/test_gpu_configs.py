@@ -135,3 +135,21 @@ def test_chunk_size_invariance(dtype, d, T):
         m = host64(tmb.fwd(qd, kd, vd, zd))
         torch.cuda.synchronize()
         assert relerr(m, outs[64]) < tol
+
+
+@pytest.mark.parametrize("variant", ["sq", "exp"])
+def test_very_long_single_head(variant):
+    # one head of 2^18 tokens: 64 segments of 64 chunks for 2Mamba (carries
+    # through the segment scan), 1024 query tiles for 2Mamba-E; very weak decay so
+    # that the whole prefix counts.  Sampled rows against the oracle.
+    B, H, T = 1, 1, 1 << 18
+    announce(f"{variant} bf16 single head T={T}")
+    q, k, v, z = SI.draw(B, H, T, 64, seed=3, dtype="bf16", z_mean=-12.0)
+    out = tmb.fwd(*dev(q, k, v, z), variant=variant)
+    torch.cuda.synchronize()
+    rows = sorted(set(rows_for(T) + [4095, 4096, 65535, 65536, 131071, 200000]))
+    qq, kk, vv, zz = (SI.to_f64(t) for t in (q, k, v, z))
+    ref = (O.fwd_quadratic_rows if variant == "sq" else O.fwd_exp_quadratic_rows)(qq, kk, vv, zz, rows)
+    e = relerr(host64(out)[:, :, rows], ref)
+    print(f"  rows err {e:.2e}")
+    assert e < TOL["bf16"]
