@@ -355,8 +355,21 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const int half = blockIdx.x & 1;
-    const int rest = blockIdx.x >> 1;
+    // Both value halves of one (head, segment) go to the same XCD (blocks b and
+    // b + 8 are dispatched to one), so the second half's reads of the rows both
+    // halves use can hit the L2 that the first filled; a last group of fewer than 8 items
+    // keeps the plain order.
+    int half, rest;
+    {
+        const int b = blockIdx.x, nitems = (int)(gridDim.x >> 1), grp = b >> 4;
+        if ((grp + 1) * 8 <= nitems) {
+            rest = grp * 8 + (b & 7);
+            half = (b >> 3) & 1;
+        } else {
+            rest = b >> 1;
+            half = b & 1;
+        }
+    }
     const int seg = rest % nseg;
     const int bh = rest / nseg;
     const int nc_total = (T + kC - 1) / kC;
@@ -897,8 +910,21 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
     __shared__ __attribute__((aligned(16))) SmemSeg sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = blockIdx.x & 1;
-    const int rest = blockIdx.x >> 1;
+    // Both value halves of one (head, segment) go to the same XCD (blocks b and
+    // b + 8 are dispatched to one), so the second half's reads of the rows both
+    // halves use can hit the L2 that the first filled; a last group of fewer than 8 items
+    // keeps the plain order.
+    int half, rest;
+    {
+        const int b = blockIdx.x, nitems = (int)(gridDim.x >> 1), grp = b >> 4;
+        if ((grp + 1) * 8 <= nitems) {
+            rest = grp * 8 + (b & 7);
+            half = (b >> 3) & 1;
+        } else {
+            rest = b >> 1;
+            half = b & 1;
+        }
+    }
     const int ns1 = nseg - 1;
     const int seg = rest % ns1;
     const int bh = rest / ns1;
