@@ -355,23 +355,25 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // Both value halves of one (head, segment) go to the same XCD (blocks b and
-    // b + 8 are dispatched to one), so the second half's reads of the rows both
-    // halves use can hit the L2 that the first filled; a last group of fewer than 8 items
-    // keeps the plain order.
-    int half, rest;
+    // All workgroups of one head (both value halves, every segment) go to the same
+    // XCD (blocks b, b + 8, b + 16, ... are dispatched to one): the two halves read
+    // the same q, k and z rows, and later segments read the same carry slots, so
+    // most of those reads hit the L2 that the first reader filled.  A last group of
+    // fewer than 8 heads keeps the plain order.
+    int half, seg, bh;
     {
-        const int b = blockIdx.x, nitems = (int)(gridDim.x >> 1), grp = b >> 4;
-        if ((grp + 1) * 8 <= nitems) {
-            rest = grp * 8 + (b & 7);
-            half = (b >> 3) & 1;
+        const int b = blockIdx.x, per = 2 * nseg, nbh_ = (int)gridDim.x / per, grp = b / (8 * per);
+        if ((grp + 1) * 8 <= nbh_) {
+            const int within = b - grp * 8 * per, j = within >> 3;
+            bh = grp * 8 + (within & 7);
+            half = j & 1;
+            seg = j >> 1;
         } else {
-            rest = b >> 1;
             half = b & 1;
+            seg = (b >> 1) % nseg;
+            bh = (b >> 1) / nseg;
         }
     }
-    const int seg = rest % nseg;
-    const int bh = rest / nseg;
     const int nc_total = (T + kC - 1) / kC;
     const int c_begin = seg * seg_chunks;
     const int c_end = min(nc_total, c_begin + seg_chunks);
