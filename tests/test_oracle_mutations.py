@@ -98,3 +98,33 @@ def test_initial_state_without_decay_is_caught(monkeypatch):
     monkeypatch.setattr(O, "fwd_quadratic", patched)
     with pytest.raises(AssertionError):
         P.test_split_and_resume(6)
+
+
+_orig_lse = O.row_logsumexp
+
+
+def _lse_without_decay(q, k, z, scale=1.0, rows=None):
+    return _orig_lse(q, k, np.full(z.shape, -np.inf), scale, rows)
+
+
+def _lse_decay_sign_flipped(q, k, z, scale=1.0, rows=None):
+    # lambda_ts entering with the wrong sign, e^{-lambda}: the mask of logits -z'
+    # with softplus(z') = -softplus(z) is not available, so build it from the rows
+    g = O.decay_log(z)
+    rows_ = range(q.shape[2]) if rows is None else rows
+    out = np.zeros(q.shape[:2] + (len(rows_),))
+    for i, t in enumerate(rows_):
+        logit = scale * np.einsum("bhd,bhsd->bhs", q[:, :, t], k[:, :, :t + 1]) - O._row_log_mask(g[:, :, :t + 1])
+        out[:, :, i] = np.log(np.exp(logit).sum(axis=-1))
+    return out
+
+
+@pytest.mark.parametrize("fn", [_lse_without_decay, _lse_decay_sign_flipped], ids=["lse decay dropped",
+                                                                                   "lse decay sign"])
+def test_planted_mistake_in_row_logsumexp_is_caught(monkeypatch, fn):
+    monkeypatch.setattr(O, "row_logsumexp", fn)
+    for pin in (P.test_row_logsumexp_zero_scores_geometric_closed_form,
+                P.test_row_logsumexp_zero_scores_follow_the_one_token_recursion,
+                P.test_row_logsumexp_decay_gradient_is_softmax_mass_before_the_token):
+        with pytest.raises(AssertionError):
+            pin()

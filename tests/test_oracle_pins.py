@@ -385,3 +385,78 @@ def test_row_statistics_on_a_row_subset_are_those_rows():
                                   O.row_weight_sums(q, k, z, scale=0.9)[:, :, rows])
     np.testing.assert_array_equal(O.row_logsumexp(q, k, z, scale=0.9, rows=rows),
                                   O.row_logsumexp(q, k, z, scale=0.9)[:, :, rows])
+
+
+def test_row_logsumexp_zero_scores_geometric_closed_form():
+    # With zero scores only the A-mask is left [2M2F §6]: for a constant decay logit c
+    # every row is a geometric series, lse_t = log sum_{m=0..t} e^{m g} with
+    # g = -softplus(c).  A dropped mask gives log(t+1), a mask of the wrong sign a
+    # growing series, a mask that includes the query's own token a shift by g.
+    T = 40
+    t = np.arange(T)
+    for c in (-3.0, -1.0, 0.0, 0.7, 2.5):
+        g = -math.log1p(math.exp(c))
+        q = np.zeros((1, 1, T, 3))
+        k = np.random.default_rng(64).normal(size=(1, 1, T, 3))
+        z = np.full((1, 1, T), c)
+        ref = np.log(-np.expm1((t + 1) * g) / -math.expm1(g))
+        np.testing.assert_allclose(O.row_logsumexp(q, k, z)[0, 0], ref, rtol=1e-13, atol=1e-13)
+    # no decay at all: t + 1 equal terms
+    z = np.full((1, 1, T), -np.inf)
+    np.testing.assert_allclose(O.row_logsumexp(np.zeros((1, 1, T, 3)), k, z)[0, 0], np.log(t + 1.0), rtol=1e-14)
+
+
+def test_row_logsumexp_zero_scores_follow_the_one_token_recursion():
+    # Zero scores with a varying decay: the row sum of token t is e^{g_t} times the row
+    # sum of token t-1 plus the diagonal's 1, so lse_t = log(1 + e^{g_t + lse_{t-1}}).
+    r = np.random.default_rng(65)
+    z = r.normal(-1.0, 1.0, size=(2, 2, 31))
+    g = -np.logaddexp(0.0, z)
+    ref = np.zeros_like(z)
+    for t in range(1, 31):
+        ref[..., t] = np.logaddexp(0.0, g[..., t] + ref[..., t - 1])
+    got = O.row_logsumexp(np.zeros((2, 2, 31, 4)), r.normal(size=(2, 2, 31, 4)), z)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def _lse_fd_inputs():
+    r = np.random.default_rng(66)
+    q, k = (r.normal(size=(1, 2, 13, 3)) for _ in range(2))
+    z = r.normal(-1.0, 1.0, size=(1, 2, 13))
+    return q, k, z
+
+
+def test_row_logsumexp_decay_gradient_is_softmax_mass_before_the_token():
+    # d lse_t / d g_r is the softmax mass on keys s < r <= t (those whose mask sums g_r),
+    # and dg_r/dz_r = -sigmoid(z_r).  The 2Mamba-E forward with values 1(s < r) returns
+    # exactly that mass, so a central difference of lse in z_r must match
+    # -sigmoid(z_r) * o_t.  The forward is pinned on its own (causal SDPA without decay,
+    # the zero-score closed form with decay, the streaming form).
+    q, k, z = _lse_fd_inputs()
+    T = q.shape[2]
+    h = 1e-6
+    for r_ in (1, 5, 12):
+        v = (np.arange(T) < r_).astype(float)[None, None, :, None] * np.ones((1, 2, T, 1))
+        o = O.fwd_exp_quadratic(q, k, v, z, scale=0.9)[..., 0]
+        zp, zm = z.copy(), z.copy()
+        zp[..., r_] += h
+        zm[..., r_] -= h
+        fd = (O.row_logsumexp(q, k, zp, scale=0.9) - O.row_logsumexp(q, k, zm, scale=0.9)) / (2 * h)
+        ref = -O.sigmoid(z[..., r_])[..., None] * o
+        ref[..., :r_] = 0.0     # rows before r do not contain g_r
+        np.testing.assert_allclose(fd, ref, rtol=1e-6, atol=1e-8)
+        assert np.abs(ref[..., r_:]).max() > 1e-3
+
+
+def test_row_logsumexp_query_gradient_is_softmax_mean_key():
+    # d lse_t / d q_t = scale * sum_s p_ts k_s: the 2Mamba-E forward with the keys as values
+    q, k, z = _lse_fd_inputs()
+    o = O.fwd_exp_quadratic(q, k, k, z, scale=0.9)
+    h = 1e-6
+    for t in (0, 4, 12):
+        for i in range(3):
+            qp, qm = q.copy(), q.copy()
+            qp[:, :, t, i] += h
+            qm[:, :, t, i] -= h
+            fd = (O.row_logsumexp(qp, k, z, scale=0.9, rows=[t]) - O.row_logsumexp(qm, k, z, scale=0.9, rows=[t]))
+            np.testing.assert_allclose(fd[..., 0] / (2 * h), 0.9 * o[:, :, t, i], rtol=1e-6, atol=1e-8)
