@@ -150,6 +150,30 @@ __device__ __forceinline__ float decay_log_fast(float z) {
     const float y = fexp2(-fabsf(z) * kLog2e);
     return -(fmaxf(z, 0.f) + flog2(1.f + y) * 0.6931471805599453f);
 }
+// unit_exp of the largest |k| over this lane's 8 dims, 127 when all are 0 (no constraint)
+__device__ __forceinline__ int8_t lane_kexp(const float* kv) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(kv[i]));
+    return (int8_t)(m > 0.f ? max(-120, min(120, unit_exp(m))) : 127);
+}
+// Per-token key exponent of the state update's operands.  A key 2^-delta times the
+// chunk's largest would, at the chunk's scale, give pair products near 2^-2delta: fp16
+// subnormals with few bits left.  Half of delta goes onto the key (the phi(K)
+// operand) and the other half stays on the weighted value and key operands, whose
+// scale is 2^-e per key factor, so that both stay normal for delta up to about 20.
+// The products, and with them the accumulators, do not change.
+__device__ __forceinline__ int token_kexp(const int8_t (&row)[kWaves], int ek) {
+    const uint2 u = *reinterpret_cast<const uint2*>(row);
+    int m = 127;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = min(m, (int)(int8_t)((u.x >> (8 * i)) & 0xffu));
+        m = min(m, (int)(int8_t)((u.y >> (8 * i)) & 0xffu));
+    }
+    return m == 127 ? ek : ek + ((max(m, ek) - ek) >> 1);
+}
+
 __device__ __forceinline__ float uni(float x) {   // wave-uniform value into a scalar register
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
@@ -215,6 +239,7 @@ struct Smem {
     float Dinter[2][kC];        // normaliser readout partials
     float Gl[2][kC];            // chunk-local inclusive prefix of g, by chunk parity
     float qrow[kC][kWaves];     // per token, each wave's max |q scale| over its 8 dims
+    alignas(8) int8_t kexp[kC][kWaves];   // per token, unit_exp of each wave's max |k| over its 8 dims (127: all 0)
     float red[2][kWaves][4];    // per-wave maxima of |k| [1], |v| [2], by chunk parity
     int erow[2][kC];            // per-token query exponent, by chunk parity
     int zero;
@@ -224,6 +249,7 @@ struct SmemSeg {
     _Float16 KT[kD][kLS];
     _Float16 WKT[kD][kLS];
     _Float16 WVT[kDV][kLS];
+    alignas(8) int8_t kexp[kC][kWaves];
     float red[2][kWaves][4];
     int zero;
 };
@@ -531,6 +557,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         }
         // max |q scale| = |scale| max |q| (rounding is monotone)
         sm.qrow[lane_][wl_] = mq * fabsf(scale);
+        sm.kexp[lane_][wl_] = lane_kexp(kv);
         mk = wave_max(mk);
         mv = wave_max(mv);
         if (lane_ == 0) {
@@ -599,9 +626,11 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             // (q scale) 2^eq does
             const float sq = scale * ldexpf(1.f, eq), sk = ldexpf(1.f, ek);
             if (wl == 0) sm.erow[par][lane] = eq;
+            const int et = token_kexp(sm.kexp[lane], ek);                      // the update's key exponent
+            const float skt = ldexpf(1.f, et);
             const float wt = (lane < Lc) ? fexp2((Gam - gl) * kLog2e) : 0.f;   // w_t = exp(Gam - Gl_t)
-            const float swk = wt * fexp2(-fn.lf_new - (float)ek);             // (w k) operand, dN_acc = 2^-lfn dN
-            const float swv = wt * fexp2(-fs.lf_new - 2.f * (float)ek);       // (w v) operand, dS_acc = 2^-lf dS
+            const float swk = wt * fexp2(-fn.lf_new - (float)et);             // (w k) operand, dN_acc = 2^-lfn dN
+            const float swv = wt * fexp2(-fs.lf_new - 2.f * (float)et);       // (w v) operand, dS_acc = 2^-lf dS
             const float svi = ldexpf(1.f, evi);
             h8 q8, q28, k8;
 #pragma unroll
@@ -609,7 +638,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 const float qq = qv[i] * sq, kt = kv[i] * sk;
                 q8[i] = (_Float16)qq;
                 k8[i] = (_Float16)kt;
-                sm.KT[8 * wl + i][lane] = (_Float16)kt;
+                sm.KT[8 * wl + i][lane] = (_Float16)(kv[i] * skt);
                 sm.WKT[8 * wl + i][lane] = (_Float16)(kv[i] * swk);
             }
             *reinterpret_cast<h8*>(&sm.Q[lane][8 * wl]) = q8;
@@ -970,6 +999,7 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
             mk = fmaxf(mk, fabsf(kv[i]));
             mv = fmaxf(mv, fabsf(vv[i]));
         }
+        sm.kexp[lane][wl] = lane_kexp(kv);
         mk = wave_max(mk);
         mv = wave_max(mv);
         if (lane == 0) {
@@ -991,10 +1021,11 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
         const Frame fs = choose_frame(lf, Mb, 0.f, lcs);
         const Frame fn = choose_frame(lfn, Mn, 0.f, lcn);
         {
-            const float sk = ldexpf(1.f, ek);
+            const int et = token_kexp(sm.kexp[lane], ek);
+            const float sk = ldexpf(1.f, et);
             const float lw = (Gam - gl) * kLog2e + lP;   // log2 weight of token `lane`
-            const float swk = fexp2(lw - fn.lf_new - (float)ek);
-            const float swv = fexp2(lw - fs.lf_new - 2.f * (float)ek);
+            const float swk = fexp2(lw - fn.lf_new - (float)et);
+            const float swv = fexp2(lw - fs.lf_new - 2.f * (float)et);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 sm.KT[8 * wl + i][lane] = (_Float16)(kv[i] * sk);
@@ -1218,8 +1249,15 @@ Plan plan_for(const FwdArgs& a) {
     return p;
 }
 
+// Workspace: the segment slots (when a head has more than one segment), then a
+// staging copy of the caller's initial state for in-place resume.  With one
+// segment only the normaliser needs staging: both value halves of a head read
+// all of norm_in while half 0 writes norm_out; each half reads and writes only
+// its own state columns, in the same threads.  With several segments the
+// segment-0 workgroups read state_in and norm_in while the last segment's write
+// state_out and norm_out, so both are staged.
 struct WsLayout {
-    size_t off_state, off_norm, off_gam, off_exp, off_exps, total;
+    size_t off_state, off_norm, off_gam, off_exp, off_exps, off_stage_s, off_stage_n, total;
 };
 
 WsLayout ws_layout(const FwdArgs& a, const Plan& p) {
@@ -1231,7 +1269,10 @@ WsLayout ws_layout(const FwdArgs& a, const Plan& p) {
     L.off_gam = align256(L.off_norm + nbh * ns1 * kNormWG * sizeof(float));
     L.off_exp = align256(L.off_gam + nbh * ns1 * sizeof(float));   // fp16 slots' scale exponents
     L.off_exps = align256(L.off_exp + nbh * ns1 * 2 * sizeof(int));   // the scanned carries' exponents
-    L.total = ns1 ? align256(L.off_exps + nbh * ns1 * 2 * sizeof(int)) : 0;
+    L.off_stage_s = ns1 ? align256(L.off_exps + nbh * ns1 * 2 * sizeof(int)) : 0;
+    const size_t stage_s = ns1 ? nbh * kPairs * kD * sizeof(float) : 0;
+    L.off_stage_n = align256(L.off_stage_s + stage_s);
+    L.total = align256(L.off_stage_n + nbh * kPairs * sizeof(float));
     return L;
 }
 
@@ -1239,11 +1280,12 @@ int run(const FwdArgs& a) {
     const Plan p = plan_for(a);
     const WsLayout L = ws_layout(a, p);
     char* ws = (char*)a.ws;
-    uint2* wsS = L.total ? (uint2*)(ws + L.off_state) : nullptr;   // fp16 x 4
-    float* wsN = L.total ? (float*)(ws + L.off_norm) : nullptr;
-    float* wsG = L.total ? (float*)(ws + L.off_gam) : nullptr;
-    int* wsE = L.total ? (int*)(ws + L.off_exp) : nullptr;
-    int* wsEs = L.total ? (int*)(ws + L.off_exps) : nullptr;
+    const bool slots = p.nseg > 1;
+    uint2* wsS = slots ? (uint2*)(ws + L.off_state) : nullptr;   // fp16 x 4
+    float* wsN = slots ? (float*)(ws + L.off_norm) : nullptr;
+    float* wsG = slots ? (float*)(ws + L.off_gam) : nullptr;
+    int* wsE = slots ? (int*)(ws + L.off_exp) : nullptr;
+    int* wsEs = slots ? (int*)(ws + L.off_exps) : nullptr;
     // carries: scanned in place for many segments, else summed by each main workgroup
     const int scanned = p.nseg >= kScanFrom;
     const int nbh = a.B * a.H;
@@ -1252,10 +1294,27 @@ int run(const FwdArgs& a) {
     const bf16* q = (const bf16*)a.q;
     const bf16* k = (const bf16*)a.k;
     const bf16* v = (const bf16*)a.v;
+    // in-place resume: read the caller's initial state from a staged copy (see WsLayout)
+    const float* state_in = a.state_in;
+    const float* norm_in = a.norm_in;
+    if (a.state_in != nullptr && (a.state_in == a.state_out || a.norm_in == a.norm_out)) {
+        const size_t nbh_ = (size_t)a.B * a.H;
+        float* sn = (float*)(ws + L.off_stage_n);
+        if (hipMemcpyAsync(sn, a.norm_in, nbh_ * kPairs * sizeof(float), hipMemcpyDeviceToDevice, st) != hipSuccess)
+            return TWOMAMBA_ERR_DEVICE;
+        norm_in = sn;
+        if (p.nseg > 1) {
+            float* ss = (float*)(ws + L.off_stage_s);
+            if (hipMemcpyAsync(ss, a.state_in, nbh_ * kPairs * kD * sizeof(float), hipMemcpyDeviceToDevice, st) !=
+                hipSuccess)
+                return TWOMAMBA_ERR_DEVICE;
+            state_in = ss;
+        }
+    }
     if (p.nseg > 1) {
         ktimer_begin(a.timer, "sq_segstate", a.stream);
         hipLaunchKernelGGL(sq_segstate_kernel, dim3(nbh * (p.nseg - 1) * 2), dim3(kThreads), 0, st, k, v, a.z,
-                           a.state_in, a.norm_in, wsS, wsN, wsG, wsE, a.T, p.nseg, p.seg_chunks);
+                           state_in, norm_in, wsS, wsN, wsG, wsE, a.T, p.nseg, p.seg_chunks);
         ktimer_end(a.timer, a.stream);
     }
     if (scanned) {
@@ -1267,7 +1326,7 @@ int run(const FwdArgs& a) {
     }
     ktimer_begin(a.timer, "sq_mfma_main", a.stream);
     hipLaunchKernelGGL(sq_main_kernel, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z, (bf16*)a.out,
-                       a.state_in, a.norm_in, a.state_out, a.norm_out, (const uint2*)wsS, (const float*)wsN,
+                       state_in, norm_in, a.state_out, a.norm_out, (const uint2*)wsS, (const float*)wsN,
                        (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm, a.row_stat, scanned,
                        (const int*)(scanned ? wsEs : wsE));
     ktimer_end(a.timer, a.stream);

@@ -20,16 +20,32 @@ from gpu_util import TOL, announce, dev, host64, relerr
 
 pytestmark = pytest.mark.gpu
 
-MODES = ["small_q", "huge_v", "tiny_k", "strong_decay", "resets"]
+MODES = ["small_q", "small_k", "small_k_strong", "small_k_aligned", "huge_v", "tiny_k", "strong_decay", "resets"]
+Z_MEAN = {"strong_decay": 20.0, "small_k_strong": 20.0, "small_q": -10.0, "small_k": -10.0, "small_k_aligned": -10.0}
 
 
 def adversarial(B, H, T, d, mode, seed, dtype="bf16"):
-    """Seeded inputs of one adversarial kind, cast to dtype (z stays fp32)."""
-    zm = 20.0 if mode == "strong_decay" else (-10.0 if mode == "small_q" else -2.0)
+    """Seeded inputs of one adversarial kind, cast to dtype (z stays fp32).
+
+    small_k*: every 7th key 1000x smaller than the rest.  In small_k_aligned the
+    other keys live in the first half of the dims and the small keys and every
+    query in the second half, so each query scores only the small keys and every
+    output is made of their (weakly decayed, carried) contributions alone."""
+    zm = Z_MEAN.get(mode, -2.0)
     q, k, v, z = SI.draw(B, H, T, d, seed=seed, dtype="f32", z_mean=zm)
     q, k, v = q.clone(), k.clone(), v.clone()
     if mode == "small_q":
         q[:, :, ::7] *= 1e-3
+    elif mode in ("small_k", "small_k_strong"):
+        k[:, :, ::7] *= 1e-3
+    elif mode == "small_k_aligned":
+        h = d // 2
+        small = torch.zeros(T, dtype=torch.bool)
+        small[::7] = True
+        k[:, :, small] *= 1e-3
+        k[:, :, small, :h] = 0.0
+        k[:, :, ~small, h:] = 0.0
+        q[..., :h] = 0.0
     elif mode == "huge_v":
         v *= 1e20
     elif mode == "tiny_k":
@@ -116,7 +132,7 @@ def test_first_order_forward(mode):
 # them, every dz is zero or the sigmoid of 50 times a vanishing dL/dg, so the
 # reference dz is ~1e-22 and only the rounding of the running sums is compared.
 @pytest.mark.parametrize("variant", ["sq", "exp"])
-@pytest.mark.parametrize("mode", ["small_q", "huge_v", "tiny_k", "resets_decay"])
+@pytest.mark.parametrize("mode", ["small_q", "small_k", "small_k_aligned", "huge_v", "tiny_k", "resets_decay"])
 def test_backward(variant, mode):
     announce(f"adversarial backward {variant} {mode}")
     B, H, T, d = 1, 2, 300, 64
@@ -146,11 +162,20 @@ def test_sq_forward(mode, dtype, d):
     qq, kk, vv = f64(q, k, v)
     zz = SI.to_f64(z)
     rows = list(range(0, 700, 7)) if mode == "small_q" else list(range(700))
+    if mode == "small_k_aligned":
+        rows = list(range(350, 700))   # made of carried small-key state, measured on their own scale
     ref = O.fwd_quadratic_rows(qq, kk, vv, zz, rows)
     S_ref, n_ref = O.final_state_direct(kk, vv, zz)
     e, es, en = relerr(host64(out)[:, :, rows], ref), relerr(host64(S), S_ref), relerr(host64(n), n_ref)
     print(f"  err {e:.2e} state {es:.2e} norm {en:.2e}")
     assert e < TOL[dtype] and es < TOL[dtype] and en < TOL[dtype]
+    if mode == "small_k_aligned":
+        # the state's block of small-key pairs (both dims in the second half), on its own scale
+        I, J = O.pair_list(d)
+        blk = (I >= d // 2) & (J >= d // 2)
+        eb = relerr(host64(S)[:, :, blk], S_ref[:, :, blk])
+        print(f"  small-key pair block of the state: err {eb:.2e}")
+        assert eb < TOL[dtype]
 
 
 @pytest.mark.parametrize("mode", MODES)
