@@ -235,3 +235,24 @@ def test_mfma_sq_small_query_rows(no_norm):
     es = relerr(host64(st)[:, :, rows], den_ref)
     print(f"  small rows err {e:.2e} statistic {es:.2e}")
     assert e < TOL["bf16"] and es < TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [300, 1000])   # one segment per head; four segments per head
+def test_mfma_sq_in_place_resume(T):
+    # state_out == state_in and norm_out == norm_in (exact alias, in-place resume): the
+    # result must equal the call with separate output buffers, bit for bit, and the oracle.
+    announce(f"MFMA SQ in-place resume B=1 H=2 T={T}")
+    q, k, v, z = SI.draw(1, 2, T, 64, seed=11 + T, dtype="bf16", z_mean=-8.0)
+    S0d, n0d = oracle_state(1, 2, 64, seed=12, z_mean=-8.0)
+    qd, kd, vd, zd = dev(q, k, v, z)
+    o_sep, S_sep, n_sep = tmb.fwd(qd, kd, vd, zd, state_in=S0d, norm_in=n0d, want_state=True)
+    S, n = S0d.clone(), n0d.clone()
+    o_alias, S_a, n_a = tmb.fwd(qd, kd, vd, zd, state_in=S, norm_in=n, state_out=S, norm_out=n, want_state=True)
+    torch.cuda.synchronize()
+    assert S_a.data_ptr() == S.data_ptr() and n_a.data_ptr() == n.data_ptr()
+    assert torch.equal(o_alias, o_sep) and torch.equal(S, S_sep) and torch.equal(n, n_sep)
+    qq, kk, vv, zz = o64(q, k, v, z)
+    S0, n0 = host64(S0d), host64(n0d)
+    assert relerr(host64(o_alias), O.fwd_quadratic(qq, kk, vv, zz, state_in=S0, norm_in=n0)) < TOL["bf16"]
+    S_ref, n_ref = O.final_state_direct(kk, vv, zz, state_in=S0, norm_in=n0)
+    assert relerr(host64(S), S_ref) < TOL["bf16"] and relerr(host64(n), n_ref) < TOL["bf16"]
