@@ -61,6 +61,32 @@ def test_sq_4x16x2048(zm):
         assert es < TOL["bf16"] and en < TOL["bf16"]
 
 
+@pytest.mark.parametrize("zm", [0.0, -8.0])
+def test_sq_bench_shape_2x16x8192(zm):
+    # The workload the benchmark times (B=2 H=16 T=8192, seed 3): four segments of
+    # 2048 tokens per head, carries summed in each workgroup's prologue.  Rows at the
+    # chunk and segment boundaries and the last token, on every head; the final state
+    # and normaliser on two heads.
+    B, H, T = 2, 16, 8192
+    announce(f"2Mamba bf16 bench shape {B}x{H}x{T} z_mean={zm}")
+    q, k, v, z = SI.draw(B, H, T, 64, seed=3, dtype="bf16", z_mean=zm)
+    out, S, n = tmb.fwd(*dev(q, k, v, z), want_state=True)
+    torch.cuda.synchronize()
+    out = host64(out)
+    rows = [0, 63, 64, 2047, 2048, 4095, 4096, 6143, 6144, 8191]
+    qq, kk, vv, zz = (SI.to_f64(t) for t in (q, k, v, z))
+    ref = O.fwd_quadratic_rows(qq, kk, vv, zz, rows)
+    e = relerr(out[:, :, rows], ref)
+    print(f"  rows err {e:.2e}")
+    assert e < TOL["bf16"]
+    for b, h in [(0, 5), (1, 15)]:
+        S_ref, n_ref = O.final_state_direct(head(k, b, h), head(v, b, h), head(z, b, h))
+        es = relerr(host64(S)[b:b + 1, h:h + 1], S_ref)
+        en = relerr(host64(n)[b:b + 1, h:h + 1], n_ref)
+        print(f"  head ({b},{h}) state err {es:.2e} norm err {en:.2e}")
+        assert es < TOL["bf16"] and en < TOL["bf16"]
+
+
 @pytest.mark.parametrize("zm", [-10.0, 0.0])
 def test_sq_long_1x16x32768(zm):
     B, H, T = 1, 16, 32768
