@@ -24,8 +24,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include")]
 # Packed-fp32 VALU ops are switched off for all device code.
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 # Per-source extra device flags.  The 2Mamba-E kernel's row maxima are plain

@@ -471,9 +471,12 @@ exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 }  // namespace
 
 bool mfma_exp_supported(const FwdArgs& a) {
-    // the bias enters the accumulator divided by the scale: positive, not tiny
+    // The bias enters the accumulator divided by the scale: positive, not tiny.  A
+    // head's rows are addressed through a buffer resource with 32-bit byte offsets
+    // formed in int arithmetic (row * 64 * 2 bytes): heads of 2^24 tokens or more run
+    // on the reference kernel instead.
     return a.dtype == TWOMAMBA_BF16 && a.dk == kD && a.dv == kD && a.scale > 1e-20f && a.T > 0 &&
-           (size_t)a.B * a.H > 0;
+           (size_t)a.T * kD * 2 < ((size_t)1 << 31) && (size_t)a.B * a.H > 0;
 }
 
 int mfma_exp_fwd(const FwdArgs& a) {
