@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define TWOMAMBA_ABI_VERSION 2
+#define TWOMAMBA_ABI_VERSION 3
 
 typedef enum {
     TWOMAMBA_OK = 0,
@@ -65,7 +65,9 @@ typedef enum {
     TWOMAMBA_ERR_UNSUPPORTED = 4, /* valid request the library does not implement   */
     TWOMAMBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
     TWOMAMBA_ERR_DEVICE = 6,      /* a HIP call failed (launch, attribute, device)  */
-    TWOMAMBA_ERR_ALIAS = 7        /* an output overlaps an input it may not alias   */
+    TWOMAMBA_ERR_ALIAS = 7,       /* an output overlaps an input it may not alias   */
+    TWOMAMBA_ERR_SCRATCH = 8      /* twomamba_fwd_noalloc: the call needs more than *
+                                   * TWOMAMBA_NOALLOC_SCRATCH_BYTES of workspace     */
 } twomamba_status;
 
 typedef enum { TWOMAMBA_F32 = 0, TWOMAMBA_BF16 = 1 } twomamba_dtype;   /* dtype of q, k, v and out */
@@ -167,6 +169,27 @@ int twomamba_fwd_timed(const twomamba_fwd_desc* desc,
                        void* out, float* state_out, float* norm_out,
                        void* workspace, size_t workspace_bytes, void* stream,
                        float* kernel_ms, const char** kernel_names, int cap, int* n_kernels);
+
+/*
+ * twomamba_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as twomamba_fwd, without the workspace: the
+ * workspace twomamba_fwd_workspace_size reports comes from a buffer the library
+ * owns, a static device array of TWOMAMBA_NOALLOC_SCRATCH_BYTES on each GPU,
+ * held until the process ends.  A call whose workspace would exceed it returns
+ * TWOMAMBA_ERR_SCRATCH before any HIP call (use twomamba_fwd with a workspace
+ * of your own).  The call allocates nothing and leaves nothing behind that a
+ * later call depends on.  `stream` must belong to the current device (else
+ * TWOMAMBA_ERR_DEVICE).  All calls on one GPU share its buffer: calls that may
+ * overlap on one GPU (other streams, other host threads) race on it and must
+ * be serialised by the caller.
+ */
+#define TWOMAMBA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int twomamba_fwd_noalloc(const twomamba_fwd_desc* desc,
+                         const void* q, const void* k, const void* v, const float* z,
+                         const float* state_in, const float* norm_in,
+                         void* out, float* state_out, float* norm_out, void* stream);
 
 /*
  * twomamba_fwd that also writes each row's normalising statistic, the quantity

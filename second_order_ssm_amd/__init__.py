@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "step", "library_path",
+__all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "fwd_noalloc", "step", "library_path",
            "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd", "conv2", "step_conv",
            "TwoMambaError", "SQ", "EXP", "LIN", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "FLAG_FIRST_ORDER",
            "num_pairs", "twomamba"]
@@ -109,6 +109,8 @@ def load(path: str | None = None):
     lib.twomamba_bwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
                                        ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.twomamba_fwd_noalloc.restype = ctypes.c_int
+    lib.twomamba_fwd_noalloc.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.twomamba_conv2.restype = ctypes.c_int
     lib.twomamba_conv2.argtypes = [ctypes.POINTER(ConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.twomamba_step_conv.restype = ctypes.c_int
@@ -168,7 +170,7 @@ def _check(t, shape, dtype, name):
 
 def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, reference_kernels=False,
         state_in=None, norm_in=None, want_state=False, out=None, state_out=None, norm_out=None, workspace=None,
-        kernel_times=None, want_stats=False, row_stat=None):
+        kernel_times=None, want_stats=False, row_stat=None, noalloc=False):
     """Chunked forward.  Returns out, or (out, state_out, norm_out) with want_state.
 
     With ``want_stats`` (or a ``row_stat`` tensor [B, H, T] fp32 to fill) the
@@ -205,11 +207,18 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
         if row_stat is None:
             row_stat = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
         _check(row_stat, (B, H, T), torch.float32, "row_stat")
+    head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state_in), _ptr(norm_in),
+            _ptr(out), _ptr(state_out), _ptr(norm_out))
+    if noalloc:
+        if stats or kernel_times is not None or workspace is not None:
+            raise ValueError("noalloc takes no workspace, row statistics or kernel timings")
+        s = load().twomamba_fwd_noalloc(*head, _stream())
+        if s != 0:
+            raise TwoMambaError(s, "twomamba_fwd_noalloc")
+        return (out, state_out, norm_out) if want_state or state_out is not None else out
     nbytes = workspace_size(desc)
     if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(state_in), _ptr(norm_in),
-            _ptr(out), _ptr(state_out), _ptr(norm_out))
     tail = (_ptr(workspace) if nbytes else None, ctypes.c_size_t(nbytes), _stream())
     args = head + tail
     if stats:
@@ -230,6 +239,12 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
     if stats:
         res += (row_stat,)
     return res if len(res) > 1 else out
+
+
+def fwd_noalloc(q, k, v, z, **kw):
+    """fwd through twomamba_fwd_noalloc: the library's static scratch instead of a
+    workspace (output and state tensors are still allocated here unless passed)."""
+    return fwd(q, k, v, z, noalloc=True, **kw)
 
 
 def step(q, k, v, z, state, norm, *, scale=1.0, no_norm=False, first_order=False, out=None):

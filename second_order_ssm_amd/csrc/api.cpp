@@ -126,6 +126,7 @@ const char* twomamba_status_str(int s) {
         case TWOMAMBA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case TWOMAMBA_ERR_DEVICE: return "HIP launch or device error";
         case TWOMAMBA_ERR_ALIAS: return "output overlaps an input";
+        case TWOMAMBA_ERR_SCRATCH: return "workspace larger than the library's static scratch";
         default: return "unknown status";
     }
 }
@@ -145,9 +146,12 @@ int twomamba_fwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
     return TWOMAMBA_OK;
 }
 
+// With `noalloc`, the workspace arguments are ignored and the call runs on the
+// library's static scratch (twomamba_fwd_noalloc).
 static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
                     const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
-                    float* row_stat, void* workspace, size_t workspace_bytes, void* stream, twm::KTimer* timer) {
+                    float* row_stat, void* workspace, size_t workspace_bytes, void* stream, twm::KTimer* timer,
+                    bool noalloc = false) {
     size_t qkb, vb, zb, sb, nb;
     int s = check_desc(d, &qkb, &vb, &zb, &sb, &nb);
     if (s != TWOMAMBA_OK) return s;
@@ -182,7 +186,17 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     s = choose(&a, &path);
     if (s != TWOMAMBA_OK) return s;
     const size_t need = workspace_for(a, path);
-    if (need > 0) {
+    if (noalloc) {
+        // every check above has passed; the scratch lookup is the call's first HIP call
+        if (need > (size_t)TWOMAMBA_NOALLOC_SCRATCH_BYTES) return TWOMAMBA_ERR_SCRATCH;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            const int st = twm::noalloc_scratch(stream, &workspace);
+            if (st != TWOMAMBA_OK) return st;
+            workspace_bytes = TWOMAMBA_NOALLOC_SCRATCH_BYTES;
+        }
+    } else if (need > 0) {
         if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
         const Range rw = rng(workspace, need);
         for (const Range& o : {rq, rk, rv, rz, rsi, rni, ro, rso, rno, rst})
@@ -204,6 +218,13 @@ int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const
                  void* workspace, size_t workspace_bytes, void* stream) {
     return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, nullptr, workspace, workspace_bytes,
                     stream, nullptr);
+}
+
+int twomamba_fwd_noalloc(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                         const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
+                         void* stream) {
+    return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, nullptr, nullptr, 0, stream, nullptr,
+                    true);
 }
 
 int twomamba_fwd_stats(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,

@@ -98,6 +98,11 @@ int mfma_exp_fwd(const FwdArgs& a);
 size_t lin_workspace(const FwdArgs& a);
 int lin_fwd(const FwdArgs& a);
 
+// ---- library-owned workspace of twomamba_fwd_noalloc (noalloc.hip) ----------
+// Device address of the current device's static scratch array (looked up once per
+// device); `stream` must belong to the current device.  Returns a status.
+int noalloc_scratch(void* stream, void** ptr);
+
 // ---- decode step -------------------------------------------------------------
 int step_launch(const StepArgs& a);
 

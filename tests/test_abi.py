@@ -13,7 +13,7 @@ import second_order_ssm_amd as tmb
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "twomamba.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EDEV, EALIAS = range(8)
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EDEV, EALIAS, ESCRATCH = range(9)
 
 pytestmark = pytest.mark.skipif(not os.path.exists(tmb.library_path), reason="libtwomamba.so not built")
 
@@ -38,13 +38,13 @@ def test_header_symbols_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.twomamba_abi_version() == 2
+    assert lib.twomamba_abi_version() == 3
     seen = set()
-    for s in range(8):
+    for s in range(9):
         txt = lib.twomamba_status_str(s).decode()
         assert txt and txt != "unknown status"
         seen.add(txt)
-    assert len(seen) == 8
+    assert len(seen) == 9
     assert lib.twomamba_status_str(99).decode() == "unknown status"
 
 
@@ -377,3 +377,24 @@ def test_product_package_never_touches_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 src = open(os.path.join(root, f), encoding="utf-8").read()
                 assert "oracle" not in src, f"{f} refers to the oracle"
+
+
+def call_fwd_noalloc(lib, dsc, q=1, k=2, v=3, z=4, si=None, ni=None, out=5, so=None, no=None):
+    p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
+    return lib.twomamba_fwd_noalloc(ctypes.byref(dsc) if dsc is not None else None, p(q), p(k), p(v), p(z), p(si),
+                                    p(ni), p(out), p(so), p(no), None)
+
+
+def test_fwd_noalloc_validation_before_any_hip_call(lib):
+    # the checks of twomamba_fwd, then the static scratch's limit (64 MiB), all
+    # before the scratch lookup (the call's first HIP call): nothing here is launched
+    assert call_fwd_noalloc(lib, None) == ENULL
+    assert call_fwd_noalloc(lib, desc(T=100), q=None) == ENULL
+    assert call_fwd_noalloc(lib, desc(T=100), out=1) == EALIAS
+    assert call_fwd_noalloc(lib, desc(T=100, d=48)) == EUNSUP
+    # fp32 reference kernels keep one state per chunk: 2 heads x 64 chunks x 532 KB > 64 MiB
+    big = desc(B=1, H=2, T=4096, d=64, dtype=0)
+    s, need = ws_size(lib, big)
+    assert s == OK and need > (64 << 20)
+    assert call_fwd_noalloc(lib, big) == ESCRATCH
+    assert lib.twomamba_status_str(ESCRATCH).decode() == "workspace larger than the library's static scratch"
