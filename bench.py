@@ -440,42 +440,98 @@ def leg_exp_step(warmup):
                               traffic=traffic_sum("exp_decode_partial", "exp_decode_combine")))
 
 
-def cpu_baseline(seconds):
-    """fp64 oracle (packed recurrent form, all 32 heads of the 2Mamba workload at
-    once) over the first n tokens, n sized to about `seconds` of CPU work."""
-    import synth_inputs as SI
+_ORACLE_INPUTS = None   # (q, k, v, z) fp64 [B*H, T, ...], set before the pool forks
+
+
+def _oracle_heads(args):
+    """Worker of the CPU baseline: form (C) over the first n tokens of a subset of heads."""
     from oracle import twomamba_oracle as O
 
-    # the oracle is numpy elementwise work, which runs on one thread
-    cores = 1
+    heads, n = args
+    sel = lambda x: x[heads][None, :, :n]
+    q, k, v, z = _ORACLE_INPUTS
+    t0 = time.perf_counter()
+    O.fwd_recurrent_packed(sel(q), sel(k), sel(v), sel(z))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_worker(seconds):
+    """fp64 oracle (packed recurrent form, form C) on the host cores: the 32 heads of
+    the 2Mamba workload split over a process pool (heads are independent), over
+    the first n tokens, n sized to about `seconds` of wall time.  Runs in a child
+    process that never touches the GPU; prints one JSON object."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import platform
+
+    global _ORACLE_INPUTS
+    import synth_inputs as SI
+
     shp = SQ_SHAPE
+    nh = shp["B"] * shp["H"]
     q, k, v, z = SI.draw(shp["B"], shp["H"], shp["T"], shp["d"], seed=shp["seed"], dtype="bf16")
-    q, k, v, z = (SI.to_f64(t) for t in (q, k, v, z))
-    B, H = shp["B"], shp["H"]
-    t0 = time.perf_counter()
-    O.fwd_recurrent_packed(q[:, :, :8], k[:, :, :8], v[:, :, :8], z[:, :, :8])
-    per_tok = (time.perf_counter() - t0) / 8
-    n = int(max(16, min(shp["T"], seconds / max(per_tok, 1e-9))))
-    t0 = time.perf_counter()
-    O.fwd_recurrent_packed(q[:, :, :n], k[:, :, :n], v[:, :, :n], z[:, :, :n])
-    dt = time.perf_counter() - t0
-    return dict(value=B * H * n / dt, unit="head-tokens/s", cores=cores, kind="oracle",
-                sample=f"packed recurrent fp64 oracle (form C), all {B}x{H} heads of the B=2 H=16 T=8192 d=64 "
-                       f"workload, first {n} of {shp['T']} tokens ({dt:.1f} s, numpy elementwise, 1 thread)")
+    _ORACLE_INPUTS = tuple(SI.to_f64(t).reshape((nh,) + tuple(t.shape[2:])) for t in (q, k, v, z))
+    procs = max(1, min(os.cpu_count() or 1, 16, nh))
+    groups = [list(range(i, nh, procs)) for i in range(procs)]
+    ctx = mp.get_context("fork")
+    with cf.ProcessPoolExecutor(procs, mp_context=ctx) as ex:
+        # calibration: 16 tokens of every group at once, then the sized run
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_heads, [(g, 16) for g in groups]))
+        per_tok = (time.perf_counter() - t0) / 16
+        n = int(max(32, min(shp["T"], seconds / max(per_tok, 1e-9))))
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_heads, [(g, n) for g in groups]))
+        dt = time.perf_counter() - t0
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    print(json.dumps(dict(value=nh * n / dt, unit="head-tokens/s", cores=procs, kind="oracle",
+                          sample=f"packed recurrent fp64 oracle (form C), all {shp['B']}x{shp['H']} heads of the "
+                                 f"B=2 H=16 T=8192 d=64 workload over {procs} processes (heads split between "
+                                 f"them, one thread each), first {n} of {shp['T']} tokens, {dt:.1f} s wall; "
+                                 f"host {cpu}, {os.cpu_count()} logical CPUs")))
+
+
+def cpu_baseline(seconds):
+    """The CPU baseline, run in a child process (it never touches the GPU)."""
+    import subprocess
+
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", str(seconds)],
+                       capture_output=True, text=True, env=env, timeout=max(120.0, 8 * seconds))
+    if r.returncode != 0:
+        print(f"[bench] cpu baseline failed: {r.stderr[-500:]}", file=sys.stderr)
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def achievable_peaks():
-    """Measured ceilings on this GPU: a plain 1 GiB device copy (bytes read +
-    written per second) and a large bf16 library GEMM (8192^3, hipBLASLt via
-    torch.matmul).  Context for the roofline fractions, which stay against the
-    published peaks."""
+    """Measured ceilings on this GPU, with the library's own microbenchmark kernels:
+    a 1 GiB streaming device copy (bytes read + written per second) and a loop of
+    independent 16x16x32 f16 MFMAs on register operands; beside them a large bf16
+    library GEMM (8192^3, hipBLASLt via torch.matmul).  Context for the roofline
+    fractions, which stay against the published peaks."""
     import torch
+
+    import second_order_ssm_amd as tmb
 
     src = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    ms = time_loop(lambda: dst.copy_(src), 20, 3)
+    ms = time_loop(lambda: tmb.ceiling_copy(src, dst), 20, 3)
     copy_bw = 2 * src.numel() * 4 / (ms * 1e-3)
+    assert torch.equal(dst[:: 1 << 20], src[:: 1 << 20])
     del src, dst
+    wgs, iters = 256 * 8, 1000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros((wgs, 2), dtype=torch.int64, device="cuda")
+    ms = time_loop(lambda: tmb.ceiling_mfma(wgs, iters, sink, clocks), 10, 2)
+    mfma = wgs * 4 * iters * 8 * 16384 / (ms * 1e-3)
+    ck = clocks.cpu().double()
+    mhz = float((ck[:, 0] / ck[:, 1].clamp(min=1)).median()) * 100.0
     n = 8192
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
     b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
@@ -484,6 +540,8 @@ def achievable_peaks():
     del a, b
     torch.cuda.empty_cache()
     return dict(copy_GBps=copy_bw / 1e9, copy_frac_of_peak=copy_bw / PEAK_HBM,
+                mfma_loop_TFLOPs=mfma / 1e12, mfma_loop_frac_of_peak=mfma / PEAK_BF16_FLOPS,
+                mfma_loop_clock_MHz=mhz,
                 bf16_gemm_TFLOPs=gemm / 1e12, bf16_gemm_frac_of_peak=gemm / PEAK_BF16_FLOPS,
                 device=device_facts())
 
@@ -517,14 +575,17 @@ def device_facts():
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
-    """A plain device-to-device copy of known size, run under rocprofv3 --pmc to
-    calibrate FETCH_SIZE / WRITE_SIZE (each dispatch moves nbytes each way)."""
+    """The library's streaming copy kernel on a buffer of known size, run under
+    rocprofv3 --pmc to calibrate FETCH_SIZE / WRITE_SIZE (each dispatch moves
+    nbytes each way)."""
     import torch
+
+    import second_order_ssm_amd as tmb
 
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(reps):
-        dst.copy_(src)
+        tmb.ceiling_copy(src, dst)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
@@ -541,7 +602,11 @@ def main():
                     help="skip the copy / GEMM ceiling measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--cpu-baseline-worker", type=float, default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_worker is not None:
+        cpu_baseline_worker(args.cpu_baseline_worker)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each head is independent, "
               "so several GPUs would shard B*H with no exchange; see the design notes).", file=sys.stderr)
@@ -592,7 +657,7 @@ def main():
             if rf["unit"] == "GB/s":
                 rf["frac_of_measured_copy"] = rf["achieved"] / peaks["copy_GBps"]
             elif rf["bound"] == "mfma":
-                rf["frac_of_measured_gemm"] = rf["achieved"] / peaks["bf16_gemm_TFLOPs"]
+                rf["frac_of_measured_mfma"] = rf["achieved"] / peaks["mfma_loop_TFLOPs"]
     cpu = cpu_baseline(args.cpu_seconds) if args.cpu_seconds > 0 else None
     head = res.get("sq") or next(iter(res.values()))
     line = {

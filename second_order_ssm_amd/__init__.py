@@ -20,10 +20,11 @@ import torch
 __all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "fwd_noalloc", "step", "library_path",
            "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd", "conv2", "step_conv",
            "TwoMambaError", "SQ", "EXP", "LIN", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "FLAG_FIRST_ORDER",
-           "num_pairs", "twomamba"]
+           "num_pairs", "twomamba", "ceiling_copy", "ceiling_mfma"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_PKG, "libtwomamba.so")
+# TWOMAMBA_LIBRARY names another build of the same library (e.g. the host-sanitized one)
+library_path = os.environ.get("TWOMAMBA_LIBRARY") or os.path.join(_PKG, "libtwomamba.so")
 
 SQ, EXP, LIN = 0, 1, 2
 F32, BF16 = 0, 1
@@ -111,6 +112,10 @@ def load(path: str | None = None):
                                        ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.twomamba_fwd_noalloc.restype = ctypes.c_int
     lib.twomamba_fwd_noalloc.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.twomamba_ceiling_copy.restype = ctypes.c_int
+    lib.twomamba_ceiling_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    lib.twomamba_ceiling_mfma.restype = ctypes.c_int
+    lib.twomamba_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.twomamba_conv2.restype = ctypes.c_int
     lib.twomamba_conv2.argtypes = [ctypes.POINTER(ConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.twomamba_step_conv.restype = ctypes.c_int
@@ -239,6 +244,29 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
     if stats:
         res += (row_stat,)
     return res if len(res) > 1 else out
+
+
+def ceiling_copy(src, dst):
+    """Streaming device copy of src into dst (measurement aid, twomamba_ceiling_copy)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst sizes differ")
+    s = load().twomamba_ceiling_copy(_ptr(src), _ptr(dst), ctypes.c_size_t(n), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_ceiling_copy")
+
+
+def ceiling_mfma(workgroups, iters, sink, clocks=None):
+    """MFMA-loop microbenchmark (measurement aid, twomamba_ceiling_mfma); sink is a
+    float32 device tensor of workgroups * 256 elements, clocks None or an int64
+    device tensor [workgroups, 2] (shader cycles, 100 MHz ticks)."""
+    if sink.dtype != torch.float32 or sink.numel() < workgroups * 256 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 tensor of workgroups * 256 elements")
+    if clocks is not None and (clocks.dtype != torch.int64 or clocks.numel() < 2 * workgroups):
+        raise ValueError("clocks must be an int64 tensor of workgroups x 2 elements")
+    s = load().twomamba_ceiling_mfma(int(workgroups), int(iters), _ptr(sink), _ptr(clocks), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_ceiling_mfma")
 
 
 def fwd_noalloc(q, k, v, z, **kw):

@@ -24,15 +24,20 @@ def lib():
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(twomamba_\w+)\s*\(", src)))
+    """Every function declared by a header under include/."""
+    names = set()
+    inc = os.path.dirname(HEADER)
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(twomamba_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert {"twomamba_fwd", "twomamba_step", "twomamba_fwd_workspace_size", "twomamba_abi_version",
-            "twomamba_status_str"} <= set(names)
+            "twomamba_status_str", "twomamba_fwd_noalloc", "twomamba_ceiling_copy", "twomamba_ceiling_mfma"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -398,3 +403,14 @@ def test_fwd_noalloc_validation_before_any_hip_call(lib):
     assert s == OK and need > (64 << 20)
     assert call_fwd_noalloc(lib, big) == ESCRATCH
     assert lib.twomamba_status_str(ESCRATCH).decode() == "workspace larger than the library's static scratch"
+
+
+def test_ceiling_kernels_validate_before_any_hip_call(lib):
+    vp = ctypes.c_void_p
+    assert lib.twomamba_ceiling_copy(None, fake(1), ctypes.c_size_t(64), None) == ENULL
+    assert lib.twomamba_ceiling_copy(fake(0), fake(1), ctypes.c_size_t(65), None) == EUNSUP     # not 16-byte sized
+    assert lib.twomamba_ceiling_copy(vp(BASE + 8), fake(1), ctypes.c_size_t(64), None) == EUNSUP  # misaligned
+    assert lib.twomamba_ceiling_copy(fake(0), vp(BASE + 32), ctypes.c_size_t(64), None) == EALIAS  # overlap
+    assert lib.twomamba_ceiling_copy(fake(0), fake(1), ctypes.c_size_t(0), None) == OK           # nothing to do
+    assert lib.twomamba_ceiling_mfma(0, 10, fake(0), None, None) == ESHAPE
+    assert lib.twomamba_ceiling_mfma(4, 10, None, None, None) == ENULL
