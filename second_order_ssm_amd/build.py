@@ -71,5 +71,37 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+SANITIZED_LIB = os.path.join(OBJ, "libtwomamba_hostsan.so")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI
+    (argument validation, path choice, workspace layout: csrc/api.cpp), compiled
+    by g++ and linked with the library's unchanged HIP objects.  Device code is
+    not instrumented.  Load it with gcc's libasan preloaded (see
+    tests/test_abi_sanitized.py); returns its path."""
+    if not all(os.path.exists(os.path.join(OBJ, f + ".o")) for f in sources()):
+        build(verbose)
+    gxx = shutil.which("g++") or "g++"
+    api_o = os.path.join(OBJ, "api_hostsan.o")
+    cmd = [gxx, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-std=c++17", "-fPIC",
+           "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, "api.cpp"), "-o", api_o]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized compile failed\n{r.stdout}\n{r.stderr}")
+    objs = [os.path.join(OBJ, f + ".o") for f in sources() if f != "api.cpp"]
+    tmp = SANITIZED_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, *objs, "-o", tmp, "-lasan", "-lubsan"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
