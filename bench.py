@@ -512,7 +512,8 @@ def cpu_baseline(seconds):
 def achievable_peaks():
     """Measured ceilings on this GPU, with the library's own microbenchmark kernels:
     a 1 GiB streaming device copy (bytes read + written per second) and a loop of
-    independent 16x16x32 f16 MFMAs on register operands; beside them a large bf16
+    16 independent chains of 16x16x32 f16 MFMAs per wave on register operands,
+    with the shader clock it ran at; beside them a large bf16
     library GEMM (8192^3, hipBLASLt via torch.matmul).  Context for the roofline
     fractions, which stay against the published peaks."""
     import torch
@@ -525,11 +526,11 @@ def achievable_peaks():
     copy_bw = 2 * src.numel() * 4 / (ms * 1e-3)
     assert torch.equal(dst[:: 1 << 20], src[:: 1 << 20])
     del src, dst
-    wgs, iters = 256 * 8, 1000
+    wgs, iters = 256 * 8, 500
     sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
     clocks = torch.zeros((wgs, 2), dtype=torch.int64, device="cuda")
     ms = time_loop(lambda: tmb.ceiling_mfma(wgs, iters, sink, clocks), 10, 2)
-    mfma = wgs * 4 * iters * 8 * 16384 / (ms * 1e-3)
+    mfma = wgs * 4 * iters * 16 * 16384 / (ms * 1e-3)
     ck = clocks.cpu().double()
     mhz = float((ck[:, 0] / ck[:, 1].clamp(min=1)).median()) * 100.0
     n = 8192

@@ -20,8 +20,9 @@ extern "C" {
    TWOMAMBA_ERR_ALIAS otherwise).  HBM traffic is 2 x bytes. */
 int twomamba_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream);
 
-/* `workgroups` workgroups of four waves, each wave issuing iters x 8 independent
-   v_mfma_f32_16x16x32_f16 (16384 FLOP each) on register operands; one float per
+/* `workgroups` workgroups of four waves, each wave issuing iters x 16
+   v_mfma_f32_16x16x32_f16 (16384 FLOP each) on register operands, in 16
+   independent accumulation chains; one float per
    thread is written to sink[workgroups * 256] (device, caller-owned).  clocks
    (device, [workgroups][2], or NULL) receives per workgroup the shader-clock
    cycles (s_memtime) and the 100 MHz real-time ticks (s_memrealtime) of its

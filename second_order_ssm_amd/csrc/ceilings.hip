@@ -9,9 +9,12 @@
 //    grid sizes (1K-16K workgroups), vectors per thread (4, 8, 16) and
 //    temporal/non-temporal access on MI355X (about 6.0 TB/s at 1 GiB).
 //  * ceiling_mfma: a loop of independent 16x16x32 f16 MFMAs on register
-//    operands, eight accumulator chains per wave, four waves per workgroup;
-//    no memory traffic except one store per lane at the end (so the work
-//    cannot be removed).  Executed work: waves x iters x 8 x 16384 FLOP.  The
+//    operands, sixteen accumulator chains per wave with operands of their own,
+//    four waves per workgroup; no memory traffic except one store per lane at
+//    the end (so the work cannot be removed).  Executed work: waves x iters x
+//    16 x 16384 FLOP.  On MI355X the unit's rate needs about 32 independent
+//    accumulations in flight per SIMD (8 chains per wave reach about 60 % of it,
+//    4 about 30 %).  The
 //    first wave of each workgroup also records the shader-clock cycles and the
 //    100 MHz real-time ticks its loop took, which give the clock the MFMA
 //    units actually ran at.
@@ -49,23 +52,28 @@ __global__ void __launch_bounds__(256) copy_kernel(const u4* __restrict__ src, u
 __global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float seed, float* __restrict__ sink,
                                                         unsigned long long* __restrict__ clocks) {
     const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    // 16 chains, each with operands of its own: dependent MFMAs are 16 apart, and no
+    // two chains compute the same values (which a compiler could merge)
+    constexpr int kChains = 16;
     const float x = seed + 1e-3f * (float)(threadIdx.x & 63);
-    h8 a, b;
+    h8 a[kChains], b[kChains];
+    f4 acc[kChains];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a[e] = (_Float16)(x + 0.01f * e);
-        b[e] = (_Float16)(x - 0.02f * e);
+    for (int c = 0; c < kChains; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[c][e] = (_Float16)(x + 0.01f * e + 0.125f * c);
+            b[c][e] = (_Float16)(x - 0.02f * e - 0.0625f * c);
+        }
+        acc[c] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    f4 acc[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+        for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c], b[c], acc[c], 0, 0, 0);
     }
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
     if (clocks != nullptr && threadIdx.x == 0) {
         const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
