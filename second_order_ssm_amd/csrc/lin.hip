@@ -21,6 +21,7 @@
 // keeps the states of whole segments, not of chunks.
 #include <algorithm>
 
+#include "conv_common.h"
 #include "device_common.h"
 #include "internal.h"
 #include "mfma_tiles.h"
@@ -237,6 +238,63 @@ __device__ __forceinline__ float chunk_prefix(const float* z, int lane, int Lc) 
     return incl * kLog2e;
 }
 
+// Input convolution on the staged rows (twomamba_fwd_conv): the raw rows of a
+// chunk and the raw rows one token earlier (the cached row, or zeros, before
+// t = 0), convolved just before the tile is written to LDS, with the same
+// arithmetic as the standalone pass.  Weights and bias of the three tensors sit
+// in LDS as ConvLds: [tensor][w0 | w1 | b][channel].
+struct ConvLds {
+    float x[3][3][kD];
+};
+
+__device__ __forceinline__ void conv_lds_fill(ConvLds& c, const float* w, const float* b, int h, int H, int tid) {
+    for (int e = tid; e < 3 * kD; e += kThreads) {
+        const int tensor = e / kD, ch = e % kD;
+        const size_t o = (size_t)(tensor * H + h) * kD + ch;
+        c.x[tensor][0][ch] = w[2 * o];
+        c.x[tensor][1][ch] = w[2 * o + 1];
+        c.x[tensor][2][ch] = b ? b[o] : 0.f;
+    }
+}
+
+__device__ __forceinline__ Conv8 conv_lds_get(const ConvLds& c, int tensor, int ch0) {
+    Conv8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        r.w0[i] = c.x[tensor][0][ch0 + i];
+        r.w1[i] = c.x[tensor][1][ch0 + i];
+        r.b[i] = c.x[tensor][2][ch0 + i];
+    }
+    return r;
+}
+
+// rows t0 - 1 .. t0 + rows - 2 of a head's tensor in the Stage layout (the row before
+// each staged row); `prev` is the cached raw row of token -1 (NULL = zeros)
+__device__ __forceinline__ void fetch_before(Stage& s, const bf16* head, const bf16* prev, int t0, int rows,
+                                             int tid) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int e = tid + n * kThreads, r = e >> 3, c = e & 7, t = t0 + r - 1;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (r < rows) {
+            if (t >= 0) x = *reinterpret_cast<const uint4*>(head + (size_t)t * kD + 8 * c);
+            else if (prev) x = *reinterpret_cast<const uint4*>(prev + 8 * c);
+        }
+        s.c[n] = x;
+    }
+}
+
+// rows past the chunk's last token stay zero (a bias would otherwise make them count)
+__device__ __forceinline__ void conv_stage(Stage& s, const Stage& before, const ConvLds& c, int tensor, int rows,
+                                           int tid) {
+    const Conv8 w = conv_lds_get(c, tensor, 8 * (tid & 7));   // a thread's channel group is the same for n = 0, 1
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int r = (tid + n * kThreads) >> 3;
+        s.c[n] = r < rows ? conv8_bf16(w, s.c[n], before.c[n]) : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 // V rows scaled by w_t = 2^(s_w[t]) into a tile
 __device__ __forceinline__ void store_scaled(const Stage& st, Tile& t, const float* s_w, int tid) {
 #pragma unroll
@@ -253,25 +311,36 @@ __device__ __forceinline__ void store_scaled(const Stage& st, Tile& t, const flo
 }
 
 // segment end states S_g^T[c][d] (transposed), weights relative to the segment end
+template <bool kConv>
 __global__ void __launch_bounds__(kThreads)
 lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
-             float* __restrict__ wsS, float* __restrict__ wsG, int T, int nseg, int seg_chunks) {
+             float* __restrict__ wsS, float* __restrict__ wsG, int T, int nseg, int seg_chunks,
+             const float* __restrict__ cw, const float* __restrict__ cb, const bf16* __restrict__ cprev, int H) {
     __shared__ __attribute__((aligned(16))) Tile sK, sV;
     __shared__ float s_w[kTile];
+    __shared__ ConvLds s_conv;
     const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
     const int nc = (T + kTile - 1) / kTile;
     const int c0 = seg * seg_chunks, c1 = min(nc, c0 + seg_chunks);
     const size_t base = (size_t)bh * T;
+    constexpr bool conv = kConv;
+    const bf16* kprev = cprev ? cprev + ((size_t)bh * 3 + 1) * kD : nullptr;
+    const bf16* vprev = cprev ? cprev + ((size_t)bh * 3 + 2) * kD : nullptr;
+    if (conv) conv_lds_fill(s_conv, cw, cb, bh % H, H, tid);
     f4 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
     float later = 0.f;   // log2 decay from the end of the current chunk to the segment end
-    Stage sk, sv;
+    Stage sk, sv, bk, bv;
     {
         const int t0 = (c1 - 1) * kTile;
         fetch(sk, k + (base + t0) * kD, min(kTile, T - t0), tid);
         fetch(sv, v + (base + t0) * kD, min(kTile, T - t0), tid);
+        if (conv) {
+            fetch_before(bk, k + base * kD, kprev, t0, min(kTile, T - t0), tid);
+            fetch_before(bv, v + base * kD, vprev, t0, min(kTile, T - t0), tid);
+        }
     }
     for (int c = c1 - 1; c >= c0; --c) {   // from the segment end backwards
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
@@ -282,6 +351,10 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
             later += total;   // kept by wave 0, which also writes the segment's decay
         }
         __syncthreads();
+        if (conv) {
+            conv_stage(sk, bk, s_conv, 1, Lc, tid);
+            conv_stage(sv, bv, s_conv, 2, Lc, tid);
+        }
         store(sk, sK, tid);
         store_scaled(sv, sV, s_w, tid);
         __syncthreads();
@@ -289,6 +362,10 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
             const int tn = t0 - kTile;
             fetch(sk, k + (base + tn) * kD, kTile, tid);
             fetch(sv, v + (base + tn) * kD, kTile, tid);
+            if (conv) {
+                fetch_before(bk, k + base * kD, kprev, tn, kTile, tid);
+                fetch_before(bv, v + base * kD, vprev, tn, kTile, tid);
+            }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -308,17 +385,28 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
 
 // one segment of one head: carried state in accumulators (wave w: value rows
 // 16w..16w+15 of S^T), per chunk intra-chunk scores + readout + update
+template <bool kConv>
 __global__ void __launch_bounds__(kThreads)
 lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const float* __restrict__ z, const float* __restrict__ carry, bf16* __restrict__ out, int T, int nseg,
-              int seg_chunks, float scale) {
-    __shared__ __attribute__((aligned(16))) Tile sQ, sK, sV, sW, sS;
+              int seg_chunks, float scale, const float* __restrict__ cw, const float* __restrict__ cb,
+              const bf16* __restrict__ cprev, int H) {
+    __shared__ __attribute__((aligned(16))) Tile sQ, sK, sV, sW, sS, sSlo;
     __shared__ float s_gl[kTile], s_w[kTile];
+    __shared__ ConvLds s_conv;
     const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
     const int nc = (T + kTile - 1) / kTile;
     const int c0 = seg * seg_chunks, c1 = min(nc, c0 + seg_chunks);
     const size_t base = (size_t)bh * T;
+    constexpr bool conv = kConv;
+    const bf16* qprev = cprev ? cprev + ((size_t)bh * 3 + 0) * kD : nullptr;
+    const bf16* kprev = cprev ? cprev + ((size_t)bh * 3 + 1) * kD : nullptr;
+    const bf16* vprev = cprev ? cprev + ((size_t)bh * 3 + 2) * kD : nullptr;
+    if (conv) {
+        conv_lds_fill(s_conv, cw, cb, bh % H, H, tid);
+        __syncthreads();
+    }
     // carry S^T[c][d] into the accumulator layout: rows 16w + 4g + i, column 16 dt + col
     f4 S[4];
     {
@@ -328,12 +416,17 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[dt][i] = src[(16 * w + 4 * g + i) * kD + 16 * dt + col];
     }
-    Stage sq, sk, sv;
+    Stage sq, sk, sv, bq, bk, bv;
     {
         const int t0 = c0 * kTile, Lc = min(kTile, T - t0);
         fetch(sq, q + (base + t0) * kD, Lc, tid);
         fetch(sk, k + (base + t0) * kD, Lc, tid);
         fetch(sv, v + (base + t0) * kD, Lc, tid);
+        if (conv) {
+            fetch_before(bq, q + base * kD, qprev, t0, Lc, tid);
+            fetch_before(bk, k + base * kD, kprev, t0, Lc, tid);
+            fetch_before(bv, v + base * kD, vprev, t0, Lc, tid);
+        }
     }
     for (int c = c0; c < c1; ++c) {
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
@@ -343,13 +436,24 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             s_gl[lane] = incl;
             s_w[lane] = total - incl;              // log2 of w_t = exp(Gam - Gl_t)
         }
-        // the state before this chunk, bf16, as S[d][c] rows (4 consecutive c per lane)
+        // the state before this chunk as S[d][c] rows (4 consecutive c per lane), split into
+        // a bf16 high part and the bf16 rounding of what it leaves: 16 significant bits.  A
+        // state with a large common component (inputs with a bias, slow decay) read through
+        // one bf16 copy loses the small differences the output is made of.
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-            uint2 o;
+            uint2 o, r;
             o.x = pack2(S[dt][0], S[dt][1]);
             o.y = pack2(S[dt][2], S[dt][3]);
+            r.x = pack2(S[dt][0] - __uint_as_float(o.x << 16), S[dt][1] - __uint_as_float(o.x & 0xffff0000u));
+            r.y = pack2(S[dt][2] - __uint_as_float(o.y << 16), S[dt][3] - __uint_as_float(o.y & 0xffff0000u));
             *reinterpret_cast<uint2*>(&sS.X[16 * dt + col][16 * w + 4 * g]) = o;
+            *reinterpret_cast<uint2*>(&sSlo.X[16 * dt + col][16 * w + 4 * g]) = r;
+        }
+        if (conv) {
+            conv_stage(sq, bq, s_conv, 0, Lc, tid);
+            conv_stage(sk, bk, s_conv, 1, Lc, tid);
+            conv_stage(sv, bv, s_conv, 2, Lc, tid);
         }
         store(sq, sQ, tid);
         store(sk, sK, tid);
@@ -362,6 +466,11 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             fetch(sq, q + (base + tn) * kD, Ln, tid);
             fetch(sk, k + (base + tn) * kD, Ln, tid);
             fetch(sv, v + (base + tn) * kD, Ln, tid);
+            if (conv) {
+                fetch_before(bq, q + base * kD, qprev, tn, Ln, tid);
+                fetch_before(bk, k + base * kD, kprev, tn, Ln, tid);
+                fetch_before(bv, v + base * kD, vprev, tn, Ln, tid);
+            }
         }
         // this wave's queries 16w .. 16w + 15, one per lane column
         const int tl = 16 * w + col;
@@ -373,8 +482,11 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             O[ct] = f4{0.f, 0.f, 0.f, 0.f};
             OI[ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dtt = 0; dtt < 2; ++dtt)
-                OI[ct] = mfma(tr_op(sS, ct, 2 * dtt, lane), q_tr_order(sQ, tl, 2 * dtt, g), OI[ct]);
+            for (int dtt = 0; dtt < 2; ++dtt) {
+                const b8 qb = q_tr_order(sQ, tl, 2 * dtt, g);
+                OI[ct] = mfma(tr_op(sSlo, ct, 2 * dtt, lane), qb, OI[ct]);
+                OI[ct] = mfma(tr_op(sS, ct, 2 * dtt, lane), qb, OI[ct]);
+            }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -433,8 +545,13 @@ int run_fused(const FwdArgs& a) {
     float* wsG = (float*)((char*)a.ws + L.off_G);
     hipStream_t st = (hipStream_t)a.stream;
     ktimer_begin(a.timer, "lin_seg", a.stream);
-    hipLaunchKernelGGL(lin_seg_mfma, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k, (const bf16*)a.v, a.z,
-                       wsS, wsG, a.T, nseg, sc);
+    const bf16* cprev = (const bf16*)a.conv_prev;
+    if (a.conv_w)
+        hipLaunchKernelGGL(lin_seg_mfma<true>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k,
+                           (const bf16*)a.v, a.z, wsS, wsG, a.T, nseg, sc, a.conv_w, a.conv_b, cprev, a.H);
+    else
+        hipLaunchKernelGGL(lin_seg_mfma<false>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k,
+                           (const bf16*)a.v, a.z, wsS, wsG, a.T, nseg, sc, nullptr, nullptr, nullptr, a.H);
     ktimer_end(a.timer, a.stream);
     const int etiles = (kD * kD + 255) / 256;
     ktimer_begin(a.timer, "lin_scan", a.stream);
@@ -442,13 +559,23 @@ int run_fused(const FwdArgs& a) {
                        a.state_in, a.state_out, nseg, etiles);
     ktimer_end(a.timer, a.stream);
     ktimer_begin(a.timer, "lin_main", a.stream);
-    hipLaunchKernelGGL(lin_main_mfma, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, a.z, (const float*)wsS, (bf16*)a.out, a.T, nseg, sc, a.scale);
+    if (a.conv_w)
+        hipLaunchKernelGGL(lin_main_mfma<true>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q,
+                           (const bf16*)a.k, (const bf16*)a.v, a.z, (const float*)wsS, (bf16*)a.out, a.T, nseg, sc,
+                           a.scale, a.conv_w, a.conv_b, cprev, a.H);
+    else
+        hipLaunchKernelGGL(lin_main_mfma<false>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q,
+                           (const bf16*)a.k, (const bf16*)a.v, a.z, (const float*)wsS, (bf16*)a.out, a.T, nseg, sc,
+                           a.scale, nullptr, nullptr, nullptr, a.H);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
 }  // namespace
+
+bool lin_conv_fused(const FwdArgs& a) {
+    return a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
+}
 
 size_t lin_workspace(const FwdArgs& a) {
     if ((size_t)a.B * a.H * a.T == 0) return 0;
