@@ -1,8 +1,8 @@
 """Benchmark of the 2Mamba operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--legs sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,lin,
-                            lin_step]
+                    [--legs sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,fwd_conv,
+                            lin,lin_step]
                     [--cpu-seconds S]
 
 A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
@@ -280,6 +280,51 @@ def leg_conv(steps, warmup):
                 bytes_per_call=byts,
                 roofline=dict(bound="hbm", kernel="conv2_kernel", achieved=bw / 1e9, peak=PEAK_HBM / 1e9,
                               unit="GB/s", frac=bw / PEAK_HBM, traffic=measured_traffic("conv2_kernel")))
+
+
+def leg_fwd_conv(steps, warmup):
+    """The forward with the size-2 input convolution in front (twomamba_fwd_conv)
+    on the forward's workload (bf16, with bias and a cached row), for each
+    variant beside the forward alone and the unfused sequence (twomamba_conv2,
+    then twomamba_fwd).  Timed interleaved, median of rounds.  The first order
+    convolves in its kernels, 2Mamba-E convolves its queries in its kernel and
+    k, v in one pass, 2Mamba runs the pass over q, k, v into its workspace."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    shp = SQ_SHAPE
+    B, H, T, d = shp["B"], shp["H"], shp["T"], shp["d"]
+    q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=shp["seed"], dtype="bf16"))
+    r = np.random.default_rng(shp["seed"] + 900)
+    w = torch.from_numpy(r.normal(0.0, 0.7, size=(3, H, d, 2)).astype(np.float32)).cuda()
+    b = torch.from_numpy(r.normal(0.0, 0.1, size=(3, H, d)).astype(np.float32)).cuda()
+    prev = torch.zeros(B, H, 3, d, dtype=torch.bfloat16, device="cuda")
+    cbuf = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    res = {}
+    for variant in ("sq", "exp", "lin"):
+        out = torch.empty_like(v)
+        desc = tmb.make_desc(B, H, T, d, d, variant=variant, dtype=torch.bfloat16)
+        ws = torch.empty(max(1, tmb.workspace_size(desc)), dtype=torch.uint8, device="cuda")
+        wsc = torch.empty(max(1, tmb.conv_workspace_size(desc)), dtype=torch.uint8, device="cuda")
+        fns = {
+            "fwd": lambda: tmb.fwd(q, k, v, z, variant=variant, out=out, workspace=ws),
+            "conv_then_fwd": lambda: (tmb.conv2(q, k, v, w, b, prev, outs=cbuf),
+                                      tmb.fwd(*cbuf, z, variant=variant, out=out, workspace=ws)),
+            "fwd_conv": lambda: tmb.fwd_conv(q, k, v, z, w, b, prev, variant=variant, out=out, workspace=wsc),
+        }
+        t = {n: [] for n in fns}
+        for _ in range(max(3, steps // 5)):
+            for n, fn in fns.items():
+                t[n].append(time_loop(fn, 5, 1))
+        med = {n: statistics.median(x) for n, x in t.items()}
+        res[variant] = dict(ms=med, fused_over_fwd=med["fwd_conv"] / med["fwd"],
+                            fused_over_unfused=med["fwd_conv"] / med["conv_then_fwd"])
+    return dict(workload=f"forward with the size-2 input convolution, B={B} H={H} T={T} d={d} bf16", variants=res)
 
 
 def leg_lin(steps, warmup):
@@ -596,8 +641,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,lin,"
-                                      "lin_step")
+    ap.add_argument("--legs", default="sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,fwd_conv,"
+                                      "lin,lin_step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the copy / GEMM ceiling measurements")
@@ -642,6 +687,9 @@ def main():
     if "conv" in legs:
         res["conv"] = leg_conv(args.steps, args.warmup)
         print(f"[bench] conv leg done: {res['conv']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
+    if "fwd_conv" in legs:
+        res["fwd_conv"] = leg_fwd_conv(args.steps, args.warmup)
+        print(f"[bench] fwd_conv leg done", file=sys.stderr, flush=True)
     if "lin" in legs:
         res["lin"] = leg_lin(args.steps, args.warmup)
         print(f"[bench] lin leg done: {res['lin']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
@@ -654,13 +702,15 @@ def main():
     peaks = achievable_peaks() if args.peaks else None
     if peaks:
         for leg in res.values():
-            rf = leg["roofline"]
+            rf = leg.get("roofline")
+            if rf is None:
+                continue
             if rf["unit"] == "GB/s":
                 rf["frac_of_measured_copy"] = rf["achieved"] / peaks["copy_GBps"]
             elif rf["bound"] == "mfma":
                 rf["frac_of_measured_mfma"] = rf["achieved"] / peaks["mfma_loop_TFLOPs"]
     cpu = cpu_baseline(args.cpu_seconds) if args.cpu_seconds > 0 else None
-    head = res.get("sq") or next(iter(res.values()))
+    head = res.get("sq") or next(leg for leg in res.values() if "roofline" in leg)
     line = {
         "metric": METRIC,
         "value": head.get("head_tokens_per_s"),

@@ -329,6 +329,42 @@ int twomamba_conv2(const twomamba_conv_desc* desc,
                    void* q_out, void* k_out, void* v_out, void* conv_state_out, void* stream);
 
 /*
+ * twomamba_fwd with the size-2 input convolution in front of the operator, in
+ * one call: out = twomamba_fwd(conv2(q, k, v)) with conv2 as twomamba_conv2
+ * defines it (same weights, bias and cached rows, same fp32 arithmetic, the
+ * convolved values rounded to the input dtype before the operator uses them)
+ * [2M2F §3: the kernel-2 convolution directly in front of the attention kernel;
+ * §4: kept in Mamba-2S; App. A: decoding caches the one previous raw q, k, v].
+ * Results are bit-identical to twomamba_conv2 followed by twomamba_fwd.
+ *
+ *   q, k, v         [B][H][T][d]   dtype   device   RAW inputs (d = dk = dv)
+ *   z, state_in, norm_in, out, state_out, norm_out   as for twomamba_fwd
+ *   conv_weight     [3][H][d][2]   fp32    device   as for twomamba_conv2; 16-byte aligned
+ *   conv_bias       [3][H][d]      fp32    device   or NULL; 16-byte aligned
+ *   conv_state_in   [B][H][3][d]   dtype   device   raw q, k, v rows of the token before t = 0,
+ *                                                   or NULL (zeros); 16-byte aligned
+ *   conv_state_out  [B][H][3][d]   dtype   device   the raw rows of token T-1 (conv_state_in, or
+ *                                                   zeros, when T = 0), or NULL; may not overlap
+ *                                                   any other argument or the workspace
+ *   workspace                              device   >= twomamba_fwd_conv_workspace_size bytes
+ * Where the path's kernels apply the convolution while loading their operands
+ * (the first order at bf16, d = 64; the queries of 2Mamba-E at bf16, d = 64)
+ * nothing convolved reaches HBM; otherwise the workspace holds the convolved
+ * tensors, written by one pass in front of the forward.  Misaligned weight,
+ * bias or cache returns TWOMAMBA_ERR_UNSUPPORTED; the other errors are those of
+ * twomamba_fwd and twomamba_conv2.
+ */
+int twomamba_fwd_conv_workspace_size(const twomamba_fwd_desc* desc, size_t* bytes);
+
+int twomamba_fwd_conv(const twomamba_fwd_desc* desc,
+                      const void* q, const void* k, const void* v, const float* z,
+                      const float* conv_weight, const float* conv_bias,
+                      const void* conv_state_in, void* conv_state_out,
+                      const float* state_in, const float* norm_in,
+                      void* out, float* state_out, float* norm_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * twomamba_step with the size-2 input convolution in front: q, k, v are this
  * token's raw rows; each is convolved with the cached raw row of the previous
  * token (conv_state, [B][H][3][d] in the input dtype, read and then replaced

@@ -20,7 +20,7 @@ import torch
 __all__ = ["load", "abi_version", "status_str", "workspace_size", "fwd", "fwd_noalloc", "step", "library_path",
            "exp_cache", "exp_cache_fill", "exp_step_workspace_size", "exp_step", "bwd_workspace_size", "bwd", "conv2", "step_conv",
            "TwoMambaError", "SQ", "EXP", "LIN", "FLAG_NO_NORM", "FLAG_REFERENCE_KERNELS", "FLAG_FIRST_ORDER",
-           "num_pairs", "twomamba", "ceiling_copy", "ceiling_mfma"]
+           "num_pairs", "twomamba", "ceiling_copy", "ceiling_mfma", "fwd_conv", "conv_workspace_size"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # TWOMAMBA_LIBRARY names another build of the same library (e.g. the host-sanitized one)
@@ -110,6 +110,11 @@ def load(path: str | None = None):
     lib.twomamba_bwd_timed.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
                                        ctypes.POINTER(ctypes.c_char_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.twomamba_fwd_conv_workspace_size.restype = ctypes.c_int
+    lib.twomamba_fwd_conv_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.twomamba_fwd_conv.restype = ctypes.c_int
+    lib.twomamba_fwd_conv.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, ctypes.c_size_t, vp]
     lib.twomamba_fwd_noalloc.restype = ctypes.c_int
     lib.twomamba_fwd_noalloc.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.twomamba_ceiling_copy.restype = ctypes.c_int
@@ -439,6 +444,60 @@ def conv2(q, k, v, weight, bias=None, state_in=None, *, outs=None, want_state=Fa
     if s != 0:
         raise TwoMambaError(s, "twomamba_conv2")
     return (*outs, state_out) if (want_state or state_out is not None) else tuple(outs)
+
+
+def conv_workspace_size(desc: FwdDesc) -> int:
+    n = ctypes.c_size_t(0)
+    s = load().twomamba_fwd_conv_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_fwd_conv_workspace_size")
+    return n.value
+
+
+def fwd_conv(q, k, v, z, weight, bias=None, conv_state_in=None, *, variant="sq", scale=1.0, chunk=0, no_norm=False,
+             reference_kernels=False, state_in=None, norm_in=None, want_state=False, out=None, state_out=None,
+             norm_out=None, want_conv_state=False, conv_state_out=None, workspace=None):
+    """The forward with the size-2 input convolution in front (twomamba_fwd_conv):
+    q, k, v are the raw inputs.  Returns out, then (state_out, norm_out) with
+    ``want_state``, then conv_state_out with ``want_conv_state``."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    flags = (FLAG_NO_NORM if no_norm else 0) | (FLAG_REFERENCE_KERNELS if reference_kernels else 0)
+    desc = make_desc(B, H, T, dk, dv, variant=variant, dtype=q.dtype, scale=scale, chunk=chunk, flags=flags)
+    _check(q, (B, H, T, dk), q.dtype, "q")
+    _check(k, (B, H, T, dk), q.dtype, "k")
+    _check(v, (B, H, T, dv), q.dtype, "v")
+    _check(z, (B, H, T), torch.float32, "z")
+    _check(weight, (3, H, dk, 2), torch.float32, "weight")
+    if bias is not None:
+        _check(bias, (3, H, dk), torch.float32, "bias")
+    if conv_state_in is not None:
+        _check(conv_state_in, (B, H, 3, dk), q.dtype, "conv_state_in")
+    lin = desc.variant == LIN
+    D = dk if lin else num_pairs(dk)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
+        if not lin:
+            norm_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    if want_conv_state and conv_state_out is None:
+        conv_state_out = torch.empty((B, H, 3, dk), dtype=q.dtype, device=q.device)
+    nbytes = conv_workspace_size(desc)
+    if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    s = load().twomamba_fwd_conv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(weight), _ptr(bias),
+                                 _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_in), _ptr(norm_in), _ptr(out),
+                                 _ptr(state_out), _ptr(norm_out), _ptr(workspace) if nbytes else None,
+                                 ctypes.c_size_t(nbytes), _stream())
+    if s != 0:
+        raise TwoMambaError(s, "twomamba_fwd_conv")
+    res = (out,)
+    if want_state or state_out is not None:
+        res += (state_out, norm_out)
+    if want_conv_state or conv_state_out is not None:
+        res += (conv_state_out,)
+    return res if len(res) > 1 else out
 
 
 def step_conv(q, k, v, z, weight, bias, conv_state, state, norm, *, scale=1.0, no_norm=False, first_order=False,

@@ -110,6 +110,35 @@ size_t workspace_for(const FwdArgs& a, Path path) {
     return path == MFMA ? twm::mfma_sq_workspace(a) : twm::ref_sq_workspace(a);
 }
 
+// Input convolution of twomamba_fwd_conv: which tensors go through the
+// standalone pass into the workspace (after the path's own workspace) and which
+// the path's kernels convolve while loading them.
+struct ConvPlan {
+    int first, count;   // tensors (of q, k, v) convolved by the pass
+    bool fused_all;     // the first-order MFMA kernels convolve q, k and v themselves
+    bool fused_q;       // the 2Mamba-E MFMA kernel convolves q itself
+    size_t tensor_bytes, off, total;   // one convolved tensor; where the pass's outputs start; all bytes
+};
+
+ConvPlan conv_plan(const FwdArgs& a, Path path, size_t path_ws) {
+    ConvPlan c{0, 3, false, false, 0, 0, path_ws};
+    const size_t es = a.dtype == TWOMAMBA_BF16 ? 2 : 4;
+    c.tensor_bytes = twm::align256((size_t)a.B * a.H * a.T * a.dk * es);
+    if (path == LINP && twm::lin_conv_fused(a)) {
+        c.count = 0;
+        c.fused_all = true;
+    } else if (path == MFMA && a.variant == TWOMAMBA_EXP) {
+        c.first = 1;   // k and v: every query tile re-reads them, so they are convolved once up front
+        c.count = 2;
+        c.fused_q = true;
+    }
+    if ((size_t)a.B * a.H * a.T == 0) c.count = 0;
+    c.off = twm::align256(path_ws);
+    c.total = c.count ? c.off + (size_t)c.count * c.tensor_bytes : path_ws;
+    return c;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -148,13 +177,22 @@ int twomamba_fwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
 
 // With `noalloc`, the workspace arguments are ignored and the call runs on the
 // library's static scratch (twomamba_fwd_noalloc).
+// The size-2 input convolution of twomamba_fwd_conv (NULL for the other forwards).
+struct ConvIn {
+    const float* w;
+    const float* b;
+    const void* prev;
+    void* prev_out;
+};
+
 static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
                     const float* state_in, const float* norm_in, void* out, float* state_out, float* norm_out,
                     float* row_stat, void* workspace, size_t workspace_bytes, void* stream, twm::KTimer* timer,
-                    bool noalloc = false) {
+                    bool noalloc = false, const ConvIn* conv = nullptr) {
     size_t qkb, vb, zb, sb, nb;
     int s = check_desc(d, &qkb, &vb, &zb, &sb, &nb);
     if (s != TWOMAMBA_OK) return s;
+    if (conv && d->dk != d->dv) return TWOMAMBA_ERR_UNSUPPORTED;
     const bool any = qkb != 0;   // B*H*T > 0
     const bool sq = d->variant == TWOMAMBA_SQ, lin = d->variant == TWOMAMBA_LIN;
     if (!sq && !lin && (state_in || norm_in || state_out || norm_out)) return TWOMAMBA_ERR_UNSUPPORTED;
@@ -179,13 +217,35 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     const Range rst = rng(row_stat, zb);   // [B][H][T] fp32, the size of z
     for (const Range& x : {rq, rk, rv, rz, rsi, rni, ro, rso, rno})
         if (overlaps(rst, x)) return TWOMAMBA_ERR_ALIAS;
+    Range rcw{0, 0}, rcb{0, 0}, rcp{0, 0}, rcpo{0, 0};
+    if (conv) {
+        size_t wb, bb, cb;
+        const size_t es = d->dtype == TWOMAMBA_BF16 ? 2 : 4;
+        if (!prod(&wb, {3, (size_t)d->H, (size_t)d->dk, 2, 4}) || !prod(&bb, {3, (size_t)d->H, (size_t)d->dk, 4}) ||
+            !prod(&cb, {(size_t)d->B, (size_t)d->H, 3, (size_t)d->dk, es}))
+            return TWOMAMBA_ERR_SHAPE;
+        if ((size_t)d->B * d->H > 0 && !conv->w) return TWOMAMBA_ERR_NULL;
+        if (((uintptr_t)conv->w & 15u) || ((uintptr_t)conv->b & 15u) || ((uintptr_t)conv->prev & 15u))
+            return TWOMAMBA_ERR_UNSUPPORTED;
+        rcw = rng(conv->w, wb);
+        rcb = rng(conv->b, bb);
+        rcp = rng(conv->prev, cb);
+        rcpo = rng(conv->prev_out, cb);
+        for (const Range& o : {ro, rso, rno, rst})
+            for (const Range& in : {rcw, rcb, rcp})
+                if (overlaps(o, in)) return TWOMAMBA_ERR_ALIAS;
+        for (const Range& x : {rq, rk, rv, rz, rsi, rni, ro, rso, rno, rst, rcw, rcb, rcp})
+            if (overlaps(rcpo, x)) return TWOMAMBA_ERR_ALIAS;
+    }
 
     FwdArgs a;
     plan(d, &a);
     Path path;
     s = choose(&a, &path);
     if (s != TWOMAMBA_OK) return s;
-    const size_t need = workspace_for(a, path);
+    const size_t path_need = workspace_for(a, path);
+    const ConvPlan cp = conv ? conv_plan(a, path, path_need) : ConvPlan{0, 0, false, false, 0, 0, path_need};
+    const size_t need = cp.total;
     if (noalloc) {
         // every check above has passed; the scratch lookup is the call's first HIP call
         if (need > (size_t)TWOMAMBA_NOALLOC_SCRATCH_BYTES) return TWOMAMBA_ERR_SCRATCH;
@@ -199,7 +259,7 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     } else if (need > 0) {
         if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
         const Range rw = rng(workspace, need);
-        for (const Range& o : {rq, rk, rv, rz, rsi, rni, ro, rso, rno, rst})
+        for (const Range& o : {rq, rk, rv, rz, rsi, rni, ro, rso, rno, rst, rcw, rcb, rcp, rcpo})
             if (overlaps(rw, o)) return TWOMAMBA_ERR_ALIAS;
     }
     a.q = q; a.k = k; a.v = v; a.z = z;
@@ -208,9 +268,44 @@ static int fwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream;
     a.timer = timer;
     a.row_stat = row_stat;
-    if (path == LINP) return twm::lin_fwd(a);
-    if (a.variant == TWOMAMBA_EXP) return path == MFMA ? twm::mfma_exp_fwd(a) : twm::ref_exp_fwd(a);
-    return path == MFMA ? twm::mfma_sq_fwd(a) : twm::ref_sq_fwd(a);
+    if (conv) {
+        twm::ConvArgs ca;
+        memset(&ca, 0, sizeof(ca));
+        ca.B = d->B; ca.H = d->H; ca.T = d->T; ca.d = d->dk; ca.dtype = d->dtype;
+        ca.q = q; ca.k = k; ca.v = v; ca.w = conv->w; ca.b = conv->b; ca.prev = conv->prev;
+        ca.prev_out = conv->prev_out; ca.stream = stream;
+        if (cp.count > 0) {
+            // the pass's outputs: tensors first .. first + count - 1, one slot each
+            void* conv_out[3] = {nullptr, nullptr, nullptr};
+            for (int i = cp.first; i < cp.first + cp.count; ++i)
+                conv_out[i] = (char*)workspace + cp.off + (size_t)(i - cp.first) * cp.tensor_bytes;
+            ca.qo = conv_out[0]; ca.ko = conv_out[1]; ca.vo = conv_out[2];
+            ca.first = cp.first;
+            ca.count = cp.count;
+            ca.prev_out = nullptr;   // written by the tail below, from the raw rows
+            const int cs = twm::conv2_launch(ca);
+            if (cs != TWOMAMBA_OK) return cs;
+            if (cp.first <= 0) a.q = conv_out[0];
+            a.k = conv_out[1];
+            a.v = conv_out[2];
+        }
+        if (cp.fused_all || cp.fused_q) {
+            a.conv_w = conv->w;
+            a.conv_b = conv->b;
+            a.conv_prev = conv->prev;
+            a.conv_q_only = cp.fused_q;
+        }
+    }
+    int rs;
+    if (path == LINP) rs = twm::lin_fwd(a);
+    else if (a.variant == TWOMAMBA_EXP) rs = path == MFMA ? twm::mfma_exp_fwd(a) : twm::ref_exp_fwd(a);
+    else rs = path == MFMA ? twm::mfma_sq_fwd(a) : twm::ref_sq_fwd(a);
+    if (rs != TWOMAMBA_OK || !conv || !conv->prev_out) return rs;
+    twm::ConvArgs ct;
+    memset(&ct, 0, sizeof(ct));
+    ct.B = d->B; ct.H = d->H; ct.T = d->T; ct.d = d->dk; ct.dtype = d->dtype;
+    ct.q = q; ct.k = k; ct.v = v; ct.prev = conv->prev; ct.prev_out = conv->prev_out; ct.stream = stream;
+    return twm::conv_tail_launch(ct);
 }
 
 int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
@@ -218,6 +313,31 @@ int twomamba_fwd(const twomamba_fwd_desc* d, const void* q, const void* k, const
                  void* workspace, size_t workspace_bytes, void* stream) {
     return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, nullptr, workspace, workspace_bytes,
                     stream, nullptr);
+}
+
+int twomamba_fwd_conv_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
+    if (!bytes) return TWOMAMBA_ERR_NULL;
+    *bytes = 0;
+    size_t a1, a2, a3, a4, a5;
+    int s = check_desc(d, &a1, &a2, &a3, &a4, &a5);
+    if (s != TWOMAMBA_OK) return s;
+    if (d->dk != d->dv) return TWOMAMBA_ERR_UNSUPPORTED;
+    FwdArgs a;
+    plan(d, &a);
+    Path path;
+    s = choose(&a, &path);
+    if (s != TWOMAMBA_OK) return s;
+    *bytes = conv_plan(a, path, workspace_for(a, path)).total;
+    return TWOMAMBA_OK;
+}
+
+int twomamba_fwd_conv(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
+                      const float* conv_weight, const float* conv_bias, const void* conv_state_in,
+                      void* conv_state_out, const float* state_in, const float* norm_in, void* out, float* state_out,
+                      float* norm_out, void* workspace, size_t workspace_bytes, void* stream) {
+    const ConvIn c{conv_weight, conv_bias, conv_state_in, conv_state_out};
+    return fwd_impl(d, q, k, v, z, state_in, norm_in, out, state_out, norm_out, nullptr, workspace, workspace_bytes,
+                    stream, nullptr, false, &c);
 }
 
 int twomamba_fwd_noalloc(const twomamba_fwd_desc* d, const void* q, const void* k, const void* v, const float* z,
@@ -347,6 +467,8 @@ int twomamba_conv2(const twomamba_conv_desc* d, const void* q, const void* k, co
     a.B = d->B; a.H = d->H; a.T = d->T; a.d = d->d; a.dtype = d->dtype;
     a.q = q; a.k = k; a.v = v; a.w = weight; a.b = bias; a.prev = conv_state_in;
     a.qo = q_out; a.ko = k_out; a.vo = v_out; a.prev_out = conv_state_out; a.stream = stream;
+    a.first = 0;
+    a.count = 3;
     return twm::conv2_launch(a);
 }
 

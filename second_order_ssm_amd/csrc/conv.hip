@@ -8,6 +8,7 @@
 // bytes (bf16) of input (the earlier row mostly from L2) and stores 16 bytes;
 // the weights of its 8 channels come through the caches.  Index arithmetic is
 // 32-bit within a head.
+#include "conv_common.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -52,18 +53,18 @@ template <> struct Vec8<float> {
     }
 };
 
-// grid: x = (head, tile of 256 threads), y = tensor.  Thread (token group of
-// kTok, 8 channels): its weights and bias are loaded once, each input row once
-// (the row before the group as well), kTok rows are written.
+// grid: x = (head, tile of 256 threads), y = tensor (first + blockIdx.y).  Thread
+// (token group of kTok, 8 channels): its weights and bias are loaded once, each
+// input row once (the row before the group as well), kTok rows are written.
 constexpr int kTok = 4;
 template <int D, typename In>
 __global__ void __launch_bounds__(256)
 conv2_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
              const float* __restrict__ w, const float* __restrict__ b, const In* __restrict__ prev,
              In* __restrict__ qo, In* __restrict__ ko, In* __restrict__ vo, In* __restrict__ prev_out, int H, int T,
-             int tiles) {
+             int tiles, int first) {
     constexpr int CG = D / 8;
-    const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles, which = blockIdx.y;
+    const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles, which = first + (int)blockIdx.y;
     const int idx = tile * 256 + threadIdx.x;
     const int ngroups = (T + kTok - 1) / kTok;
     if (idx >= ngroups * CG) return;
@@ -73,23 +74,8 @@ conv2_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __res
     const In* x = which == 0 ? q : which == 1 ? k : v;
     In* y = which == 0 ? qo : which == 1 ? ko : vo;
     const size_t wo = (size_t)(which * H + h) * D + 8 * cg;
-    float w0[8], w1[8], bb[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float4 wv = *reinterpret_cast<const float4*>(w + 2 * wo + 4 * i);   // taps of channels 2i, 2i+1
-        w0[2 * i] = wv.x;
-        w1[2 * i] = wv.y;
-        w0[2 * i + 1] = wv.z;
-        w1[2 * i + 1] = wv.w;
-    }
-    if (b) {
-        const float4 b0 = *reinterpret_cast<const float4*>(b + wo), b1 = *reinterpret_cast<const float4*>(b + wo + 4);
-        bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
-        bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bb[i] = 0.f;
-    }
+    Conv8 cw;
+    conv8_load(cw, w, b, wo);
     const size_t row0 = ((size_t)bh * T + t0) * D + 8 * cg;
     float bef[8];
     if (t0 > 0) {
@@ -109,8 +95,7 @@ conv2_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __res
     for (int j = 0; j < kTok; ++j) {
         if (j >= nt) break;
         float o[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = fmaf(w1[i], cur[j][i], fmaf(w0[i], j == 0 ? bef[i] : cur[j - 1][i], bb[i]));
+        conv8_f32(cw, cur[j], j == 0 ? bef : cur[j - 1], o);
         Vec8<In>::st(y + row0 + (size_t)j * D, o);
     }
     if (prev_out && t0 + nt == T)
@@ -126,6 +111,26 @@ conv2_pass_kernel(const In* __restrict__ prev, In* __restrict__ prev_out, size_t
     IO<In>::st(prev_out, id, prev ? IO<In>::ld(prev, id) : 0.f);
 }
 
+// The raw rows of token T-1 of q, k and v into the cache [B][H][3][D] (the cached
+// rows, or zeros, when T = 0): one thread per element.
+template <int D, typename In>
+__global__ void __launch_bounds__(256)
+conv_tail_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+                 const In* __restrict__ prev, In* __restrict__ prev_out, int T, size_t n) {
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= n) return;
+    const int c = (int)(id % D), which = (int)((id / D) % 3);
+    const size_t bh = id / (3 * D);
+    float x;
+    if (T > 0) {
+        const In* src = which == 0 ? q : which == 1 ? k : v;
+        x = IO<In>::ld(src, (bh * T + (size_t)(T - 1)) * D + c);
+    } else {
+        x = prev ? IO<In>::ld(prev, id) : 0.f;
+    }
+    IO<In>::st(prev_out, id, x);
+}
+
 template <int D, typename In>
 int launch(const ConvArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
@@ -136,20 +141,37 @@ int launch(const ConvArgs& a) {
                            (const In*)a.prev, (In*)a.prev_out, n);
     } else {
         const int tiles = ((a.T + kTok - 1) / kTok * (D / 8) + 255) / 256;
-        hipLaunchKernelGGL((conv2_kernel<D, In>), dim3((unsigned)(a.B * a.H * tiles), 3), dim3(256), 0, st,
-                           (const In*)a.q, (const In*)a.k, (const In*)a.v, a.w, a.b, (const In*)a.prev, (In*)a.qo,
-                           (In*)a.ko, (In*)a.vo, (In*)a.prev_out, a.H, a.T, tiles);
+        hipLaunchKernelGGL((conv2_kernel<D, In>), dim3((unsigned)(a.B * a.H * tiles), (unsigned)a.count), dim3(256),
+                           0, st, (const In*)a.q, (const In*)a.k, (const In*)a.v, a.w, a.b, (const In*)a.prev,
+                           (In*)a.qo, (In*)a.ko, (In*)a.vo, (In*)a.prev_out, a.H, a.T, tiles, a.first);
     }
+    return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+}
+
+template <int D, typename In>
+int tail(const ConvArgs& a) {
+    const size_t n = (size_t)a.B * a.H * 3 * D;
+    hipLaunchKernelGGL((conv_tail_kernel<D, In>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)a.stream, (const In*)a.q, (const In*)a.k, (const In*)a.v, (const In*)a.prev,
+                       (In*)a.prev_out, a.T, n);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
 }  // namespace
 
 int conv2_launch(const ConvArgs& a) {
-    if ((size_t)a.B * a.H == 0) return TWOMAMBA_OK;
+    if ((size_t)a.B * a.H == 0 || a.count <= 0) return TWOMAMBA_OK;
     const bool bf = a.dtype == TWOMAMBA_BF16;
     if (a.d == 64) return bf ? launch<64, bf16>(a) : launch<64, float>(a);
     if (a.d == 16) return bf ? launch<16, bf16>(a) : launch<16, float>(a);
+    return TWOMAMBA_ERR_UNSUPPORTED;
+}
+
+int conv_tail_launch(const ConvArgs& a) {
+    if ((size_t)a.B * a.H == 0 || !a.prev_out) return TWOMAMBA_OK;
+    const bool bf = a.dtype == TWOMAMBA_BF16;
+    if (a.d == 64) return bf ? tail<64, bf16>(a) : tail<64, float>(a);
+    if (a.d == 16) return bf ? tail<16, bf16>(a) : tail<16, float>(a);
     return TWOMAMBA_ERR_UNSUPPORTED;
 }
 

@@ -25,6 +25,7 @@
 //  * Query tiles are dispatched longest first for load balance.
 #include <algorithm>
 
+#include "conv_common.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -379,7 +380,8 @@ __device__ __forceinline__ void tile_step(Slot* __restrict__ curp, Slot* __restr
 __global__ void __launch_bounds__(kThreads, 2)
 exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                 const float* __restrict__ z, uint16_t* __restrict__ out, int T, int nqt, int nbh, float scale,
-                float* __restrict__ row_stat) {
+                float* __restrict__ row_stat, const float* __restrict__ cw, const float* __restrict__ cb,
+                const uint16_t* __restrict__ cprev, int H) {
     __shared__ Slot slot0, slot1, slot2;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lo = lane & 31, g = lane >> 5;
     const int qt = nqt - 1 - (int)(blockIdx.x / nbh);   // longest query tiles first
@@ -407,6 +409,24 @@ exp_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             Qop[qb][ks] = as_b8(ld16(rq, (uint32_t)(t * kD + 16 * ks + 8 * g) * 2));
+        }
+    }
+    if (cw != nullptr) {
+        // input convolution of the queries (twomamba_fwd_conv): each row with the raw row
+        // before it (the cached one, or zeros, before token 0); rows past T stay zero
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            Conv8 c8;
+            conv8_load(c8, cw, cb, (size_t)(bh % H) * kD + 16 * ks + 8 * g);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int t = tw + 32 * qb + lo;
+                uint4 xp = make_uint4(0u, 0u, 0u, 0u);
+                if (t > 0) xp = ld16(rq, (uint32_t)((t - 1) * kD + 16 * ks + 8 * g) * 2);
+                else if (cprev) xp = *reinterpret_cast<const uint4*>(cprev + (size_t)bh * 3 * kD + 16 * ks + 8 * g);
+                const uint4 x = __builtin_bit_cast(uint4, Qop[qb][ks]);
+                Qop[qb][ks] = as_b8(t < T ? conv8_bf16(c8, x, xp) : make_uint4(0u, 0u, 0u, 0u));
+            }
         }
     }
 
@@ -485,7 +505,7 @@ int mfma_exp_fwd(const FwdArgs& a) {
     ktimer_begin(a.timer, "exp_mfma", a.stream);
     hipLaunchKernelGGL(exp_mfma_kernel, dim3((unsigned)nbh * nqt), dim3(kThreads), 0, (hipStream_t)a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.z, (uint16_t*)a.out, a.T,
-                       nqt, nbh, a.scale, a.row_stat);
+                       nqt, nbh, a.scale, a.row_stat, a.conv_w, a.conv_b, (const uint16_t*)a.conv_prev, a.H);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

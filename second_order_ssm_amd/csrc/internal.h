@@ -42,6 +42,14 @@ struct FwdArgs {
     void* stream;
     KTimer* timer;     // NULL unless called through twomamba_fwd_timed
     float* row_stat;   // NULL, or [B][H][T]: weight sum (2Mamba) / log-sum-exp (2Mamba-E) per query
+    // size-2 input convolution applied by the kernels themselves while they load q, k, v
+    // (twomamba_fwd_conv on the paths that fuse it): weights [3][H][d][2], bias [3][H][d]
+    // or NULL, raw rows of the token before t = 0 [B][H][3][d] or NULL; conv_w NULL = none.
+    // conv_q_only: only q is convolved in-kernel (k, v arrive convolved).
+    const float* conv_w;
+    const float* conv_b;
+    const void* conv_prev;
+    bool conv_q_only;
 };
 
 struct StepArgs {
@@ -75,8 +83,11 @@ struct ConvArgs {
     void *qo, *ko, *vo;
     void* prev_out;
     void* stream;
+    int first, count;   // the tensors convolved: first .. first + count - 1 of (q, k, v)
 };
 int conv2_launch(const ConvArgs& a);
+// conv_state_out only: the raw rows of token T-1 (prev, or zeros, when T = 0)
+int conv_tail_launch(const ConvArgs& a);
 
 inline size_t num_pairs(int d) { return (size_t)d * (size_t)(d + 1) / 2; }
 
@@ -97,6 +108,7 @@ int mfma_exp_fwd(const FwdArgs& a);
 // ---- first-order variant (lin.hip) -----------------------------------------
 size_t lin_workspace(const FwdArgs& a);
 int lin_fwd(const FwdArgs& a);
+bool lin_conv_fused(const FwdArgs& a);   // the path that applies conv_w in-kernel
 
 // ---- library-owned workspace of twomamba_fwd_noalloc (noalloc.hip) ----------
 // Device address of the current device's static scratch array (looked up once per

@@ -414,3 +414,29 @@ def test_ceiling_kernels_validate_before_any_hip_call(lib):
     assert lib.twomamba_ceiling_copy(fake(0), fake(1), ctypes.c_size_t(0), None) == OK           # nothing to do
     assert lib.twomamba_ceiling_mfma(0, 10, fake(0), None, None) == ESHAPE
     assert lib.twomamba_ceiling_mfma(4, 10, None, None, None) == ENULL
+
+
+def call_fwd_conv(lib, dsc, w=20, b=None, ci=None, co=None, ws=9, wsb=1 << 40, q=1, out=5):
+    p = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else fake(x))
+    return lib.twomamba_fwd_conv(ctypes.byref(dsc), p(q), p(2), p(3), p(4), p(w), p(b), p(ci), p(co), None, None,
+                                 p(out), None, None, p(ws), ctypes.c_size_t(wsb), None)
+
+
+def test_fwd_conv_validation_and_workspace(lib):
+    # the forward's checks plus those of the convolution, all before any HIP call
+    d = desc(T=100)
+    assert call_fwd_conv(lib, d, w=None) == ENULL
+    assert call_fwd_conv(lib, d, w=ctypes.c_void_p(BASE + 20 * GAP + 8)) == EUNSUP      # misaligned weight
+    assert call_fwd_conv(lib, d, co=1) == EALIAS                                      # cache out == q
+    assert call_fwd_conv(lib, d, co=20) == EALIAS                                     # cache out == weight
+    assert call_fwd_conv(lib, d, out=20) == EALIAS                                    # out == weight
+    assert call_fwd_conv(lib, d, ws=None) == EWS
+    n = ctypes.c_size_t(0)
+    # first order at bf16, d = 64 convolves in its kernels: no more workspace than the plain forward
+    for variant, extra in ((2, 0), (1, 2), (0, 3)):
+        dd = desc(B=2, H=3, T=1000, variant=variant)
+        assert lib.twomamba_fwd_conv_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == OK
+        s, plain = ws_size(lib, dd)
+        tensor = (2 * 3 * 1000 * 64 * 2 + 255) // 256 * 256
+        base = (plain + 255) // 256 * 256 if extra else plain
+        assert n.value == base + extra * tensor, (variant, n.value, plain)
