@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--legs sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,fwd_conv,
-                            lin,lin_step]
+                            lin,lin_step,lin_bwd]
                     [--cpu-seconds S]
 
 A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
@@ -253,6 +253,55 @@ def leg_bwd(steps, warmup, variant="sq"):
                       # counter traffic of the two MFMA kernels (the decay scan and dz kernels are small)
                       traffic=traffic_sum(*[("" if variant == "sq" else "exp_") + n for n in ("bwd_q", "bwd_kv")])),
     )
+
+
+def lin_bwd_bytes_per_head_token(d=64, dv=64, esize=2):
+    """Algorithmic bytes of the first-order backward per head-token: read q, k, v
+    and dout, write dq, dk and dv (input dtype), read z and write dz (fp32)."""
+    return (4 * d + 3 * dv) * esize + 8 if d == dv else (2 * d + 2 * dv + 2 * d + dv) * esize + 8
+
+
+def leg_lin_bwd(steps, warmup):
+    """First-order backward in O(T) (three segmented chunk passes, two in reverse
+    time, and a finishing pass) at the forward's workload and at the long-context
+    one (B=1 H=16 T=32768).  Its arithmetic is small (about 12 d dv FLOP per
+    head-token in the state contractions), so the roofline is HBM, over the
+    algorithmic bytes of the backward (inputs read and gradients written once)."""
+    import numpy as np
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    res = {}
+    for B, H, T in ((SQ_SHAPE["B"], SQ_SHAPE["H"], SQ_SHAPE["T"]), (1, 16, 32768)):
+        d = SQ_SHAPE["d"]
+        q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=SQ_SHAPE["seed"], dtype="bf16"))
+        dout = torch.from_numpy(np.random.default_rng(SQ_SHAPE["seed"] + 500).standard_normal((B, H, T, d))).to(
+            torch.bfloat16).cuda()
+        out = tmb.fwd(q, k, v, z, variant="lin")
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z))
+        desc = tmb.make_desc(B, H, T, d, d, variant="lin", dtype=torch.bfloat16)
+        ws = torch.empty(tmb.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+        fn = lambda: tmb.bwd(q, k, v, z, out, dout, variant="lin", grads=grads, workspace=ws)
+        ms = time_loop(fn, steps, warmup)
+        byts = B * H * T * lin_bwd_bytes_per_head_token(d, d)
+        bw = byts / (ms * 1e-3)
+        kt = []
+        tmb.bwd(q, k, v, z, out, dout, variant="lin", grads=grads, workspace=ws, kernel_times=kt)
+        per = {}
+        for n, x in kt:
+            per[n] = per.get(n, 0.0) + x
+        res[f"{B}x{H}x{T}"] = dict(ms=ms, head_tokens_per_s=B * H * T / (ms * 1e-3), bytes_per_call=byts,
+                                   kernels_ms=per, GBps=bw / 1e9, frac_hbm=bw / PEAK_HBM)
+        del q, k, v, z, dout, out, grads, ws
+        torch.cuda.empty_cache()
+    head = res[f"{SQ_SHAPE['B']}x{SQ_SHAPE['H']}x{SQ_SHAPE['T']}"]
+    return dict(workload="first-order (Mamba-2S) bwd in O(T), bf16 d=64: B=2 H=16 T=8192 and B=1 H=16 T=32768",
+                ms=head["ms"], shapes=res,
+                roofline=dict(bound="hbm", kernel="lin_seg+lin_scan+lin_main (x3)+lin_bwd_finish+bwd_dz",
+                              achieved=head["GBps"], peak=PEAK_HBM / 1e9, unit="GB/s", frac=head["frac_hbm"],
+                              traffic=None))
 
 
 def leg_conv(steps, warmup):
@@ -642,7 +691,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,fwd_conv,"
-                                      "lin,lin_step")
+                                      "lin,lin_step,lin_bwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the copy / GEMM ceiling measurements")
@@ -687,6 +736,9 @@ def main():
     if "conv" in legs:
         res["conv"] = leg_conv(args.steps, args.warmup)
         print(f"[bench] conv leg done: {res['conv']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
+    if "lin_bwd" in legs:
+        res["lin_bwd"] = leg_lin_bwd(args.steps, args.warmup)
+        print(f"[bench] lin_bwd leg done: {res['lin_bwd']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
     if "fwd_conv" in legs:
         res["fwd_conv"] = leg_fwd_conv(args.steps, args.warmup)
         print(f"[bench] fwd_conv leg done", file=sys.stderr, flush=True)

@@ -236,7 +236,7 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
     elif kernel_times is None:
         s = load().twomamba_fwd(*args)
     else:
-        cap = 8
+        cap = 16
         ms = (ctypes.c_float * cap)()
         names = (ctypes.c_char_p * cap)()
         cnt = ctypes.c_int(0)
@@ -410,7 +410,7 @@ def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, refere
     if kernel_times is None:
         s = load().twomamba_bwd(*args)
     else:
-        cap = 8
+        cap = 16
         ms = (ctypes.c_float * cap)()
         names = (ctypes.c_char_p * cap)()
         cnt = ctypes.c_int(0)

@@ -583,7 +583,8 @@ int twomamba_bwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
     size_t qkb, vb, zb;
     int s = check_bwd(d, &qkb, &vb, &zb);
     if (s != TWOMAMBA_OK) return s;
-    *bytes = twm::bwd_workspace(bwd_args(d));
+    const twm::BwdArgs ba = bwd_args(d);
+    *bytes = twm::lin_bwd_chunked_supported(ba) ? twm::lin_bwd_chunked_workspace(ba) : twm::bwd_workspace(ba);
     return TWOMAMBA_OK;
 }
 
@@ -596,7 +597,8 @@ static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     if (qkb == 0) return TWOMAMBA_OK;
     if (!q || !k || !v || !z || !out || !dout || !dq || !dk || !dv || !dz) return TWOMAMBA_ERR_NULL;
     twm::BwdArgs a = bwd_args(d);
-    const size_t need = twm::bwd_workspace(a);
+    const bool chunked = twm::lin_bwd_chunked_supported(a);
+    const size_t need = chunked ? twm::lin_bwd_chunked_workspace(a) : twm::bwd_workspace(a);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
     const Range ins[] = {rng(q, qkb), rng(k, qkb), rng(v, vb), rng(z, zb), rng(out, vb), rng(dout, vb),
                          rng(row_stat, zb)};
@@ -611,6 +613,7 @@ static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     a.row_stat = d->variant == TWOMAMBA_LIN ? nullptr : row_stat;   // the first order has none
     a.gq = dq; a.gk = dk; a.gv = dv; a.gz = dz;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream; a.timer = timer;
+    if (chunked) return twm::lin_bwd_chunked(a);
     return twm::mfma_bwd_supported(a) ? twm::mfma_bwd(a) : twm::ref_bwd(a);
 }
 

@@ -308,28 +308,27 @@ bwd_ref_kv_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* 
 }  // namespace
 
 // dz from the row and column sums: exclusive fp64 prefix of colsum - rowsum
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 bwd_dz_kernel(const float* __restrict__ z, const float* __restrict__ rowsum, const float* __restrict__ colsum,
               float* __restrict__ dz, int T) {
-    __shared__ double s_tot[256];
+    // one workgroup per head: each thread sums a run of tokens in fp64, a parallel
+    // exclusive scan over the runs in LDS, then each thread writes its run
+    __shared__ double s_tot[1024];
     const int bh = blockIdx.x, tid = threadIdx.x;
     const size_t base = (size_t)bh * T;
-    const int run = (T + 255) / 256;
+    const int run = (T + 1023) / 1024;
     const int t0 = min(T, tid * run), t1 = min(T, t0 + run);
     double acc = 0.0;
     for (int t = t0; t < t1; ++t) acc += (double)colsum[base + t] - (double)rowsum[base + t];
     s_tot[tid] = acc;
     __syncthreads();
-    if (tid == 0) {
-        double r = 0.0;
-        for (int i = 0; i < 256; ++i) {
-            const double x = s_tot[i];
-            s_tot[i] = r;
-            r += x;
-        }
+    for (int off = 1; off < 1024; off <<= 1) {
+        const double x = tid >= off ? s_tot[tid - off] : 0.0;
+        __syncthreads();
+        s_tot[tid] += x;
+        __syncthreads();
     }
-    __syncthreads();
-    double c = s_tot[tid];
+    double c = s_tot[tid] - acc;   // sum over the earlier runs
     for (int t = t0; t < t1; ++t) {
         dz[base + t] = -sigmoid_f(z[base + t]) * (float)c;
         c += (double)colsum[base + t] - (double)rowsum[base + t];
@@ -377,7 +376,7 @@ int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s, bool with_d) {
 
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s) {
     ktimer_begin(a.timer, "bwd_dz", a.stream);
-    hipLaunchKernelGGL(bwd_dz_kernel, dim3(a.B * a.H), dim3(256), 0, (hipStream_t)a.stream, a.z, s.rowsum,
+    hipLaunchKernelGGL(bwd_dz_kernel, dim3(a.B * a.H), dim3(1024), 0, (hipStream_t)a.stream, a.z, s.rowsum,
                        s.colsum, a.gz, a.T);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;

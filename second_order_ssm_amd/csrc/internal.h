@@ -12,7 +12,7 @@ namespace twm {
 // Optional per-launch timing: when a KTimer is attached to a call, every
 // kernel launch is bracketed by a pair of HIP events (see twomamba_fwd_timed).
 struct KTimer {
-    static constexpr int kMax = 8;
+    static constexpr int kMax = 16;
     void* ev[2 * kMax];
     const char* names[kMax];
     int n;
@@ -168,5 +168,9 @@ int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s);
 int ref_bwd(const BwdArgs& a);
 bool mfma_bwd_supported(const BwdArgs& a);
 int mfma_bwd(const BwdArgs& a);
+// first-order backward in O(T) through the segmented chunk kernels (lin.hip)
+bool lin_bwd_chunked_supported(const BwdArgs& a);
+size_t lin_bwd_chunked_workspace(const BwdArgs& a);
+int lin_bwd_chunked(const BwdArgs& a);
 
 }  // namespace twm

@@ -19,6 +19,8 @@
 // serves fp32 and d = 16; bf16 at d = 64 runs a segmented single pass on
 // 16x16x32 MFMAs instead (see below), which reads k and v twice and q once and
 // keeps the states of whole segments, not of chunks.
+#include <string.h>
+
 #include <algorithm>
 
 #include "conv_common.h"
@@ -227,7 +229,39 @@ __device__ __forceinline__ b8 q_tr_order(const Tile& t, int row, int dtt, int g)
     return as_b8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// Reverse-time mode (the first-order backward): the kernels walk the sequence
+// back to front.  Logical position tau is the stored row T-1-tau, and the decay
+// between logical positions takes the logit of the token one step later in
+// stored order, so that a logical prefix sum over (s, t] equals the stored sum
+// over [T-1-t, T-1-s): logical tau takes z_{T-tau}, and tau = 0 no decay at all.
+__device__ __forceinline__ int stored_row(int tau, int T, bool rev) { return rev ? T - 1 - tau : tau; }
+
+__device__ __forceinline__ float logical_decay_log(const float* zhead, int tau, int T, bool rev) {
+    if (!rev) return decay_log(zhead[tau]);
+    return tau == 0 ? 0.f : decay_log(zhead[T - tau]);
+}
+
+// rows t0 .. t0 + rows - 1 (logical) of a head's tensor in the Stage layout
+__device__ __forceinline__ void fetch_rows(Stage& s, const bf16* head, int t0, int rows, int T, bool rev, int tid) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int e = tid + n * kThreads, r = e >> 3, c = e & 7;
+        s.c[n] = r < rows ? *reinterpret_cast<const uint4*>(head + (size_t)stored_row(t0 + r, T, rev) * kD + 8 * c)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 // chunk-local inclusive prefix of g (log2 units) over the 64 lanes of one wave
+__device__ __forceinline__ float chunk_prefix_dir(const float* zhead, int t0, int T, bool rev, int lane, int Lc) {
+    float incl = lane < Lc ? logical_decay_log(zhead, t0 + lane, T, rev) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    return incl * kLog2e;
+}
+
 __device__ __forceinline__ float chunk_prefix(const float* z, int lane, int Lc) {
     float incl = lane < Lc ? decay_log(z[lane]) : 0.f;
 #pragma unroll
@@ -311,7 +345,7 @@ __device__ __forceinline__ void store_scaled(const Stage& st, Tile& t, const flo
 }
 
 // segment end states S_g^T[c][d] (transposed), weights relative to the segment end
-template <bool kConv>
+template <bool kConv, bool kRev>
 __global__ void __launch_bounds__(kThreads)
 lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
              float* __restrict__ wsS, float* __restrict__ wsG, int T, int nseg, int seg_chunks,
@@ -335,8 +369,8 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
     Stage sk, sv, bk, bv;
     {
         const int t0 = (c1 - 1) * kTile;
-        fetch(sk, k + (base + t0) * kD, min(kTile, T - t0), tid);
-        fetch(sv, v + (base + t0) * kD, min(kTile, T - t0), tid);
+        fetch_rows(sk, k + base * kD, t0, min(kTile, T - t0), T, kRev, tid);
+        fetch_rows(sv, v + base * kD, t0, min(kTile, T - t0), T, kRev, tid);
         if (conv) {
             fetch_before(bk, k + base * kD, kprev, t0, min(kTile, T - t0), tid);
             fetch_before(bv, v + base * kD, vprev, t0, min(kTile, T - t0), tid);
@@ -345,7 +379,7 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
     for (int c = c1 - 1; c >= c0; --c) {   // from the segment end backwards
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
         if (w == 0) {
-            const float incl = chunk_prefix(z + base + t0, lane, Lc);
+            const float incl = chunk_prefix_dir(z + base, t0, T, kRev, lane, Lc);
             const float total = __shfl(incl, 63);
             s_w[lane] = total - incl + later;      // log2 w_t relative to the segment end
             later += total;   // kept by wave 0, which also writes the segment's decay
@@ -360,8 +394,8 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
         __syncthreads();
         if (c > c0) {
             const int tn = t0 - kTile;
-            fetch(sk, k + (base + tn) * kD, kTile, tid);
-            fetch(sv, v + (base + tn) * kD, kTile, tid);
+            fetch_rows(sk, k + base * kD, tn, kTile, T, kRev, tid);
+            fetch_rows(sv, v + base * kD, tn, kTile, T, kRev, tid);
             if (conv) {
                 fetch_before(bk, k + base * kD, kprev, tn, kTile, tid);
                 fetch_before(bv, v + base * kD, vprev, tn, kTile, tid);
@@ -384,13 +418,14 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
 }
 
 // one segment of one head: carried state in accumulators (wave w: value rows
-// 16w..16w+15 of S^T), per chunk intra-chunk scores + readout + update
-template <bool kConv>
+// 16w..16w+15 of S^T), per chunk intra-chunk scores + readout + update.  kStrict:
+// every token sees only strictly earlier ones (the diagonal term is left out).
+template <bool kConv, bool kRev, bool kStrict>
 __global__ void __launch_bounds__(kThreads)
 lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const float* __restrict__ z, const float* __restrict__ carry, bf16* __restrict__ out, int T, int nseg,
               int seg_chunks, float scale, const float* __restrict__ cw, const float* __restrict__ cb,
-              const bf16* __restrict__ cprev, int H) {
+              const bf16* __restrict__ cprev, int H, const bf16* __restrict__ xdot, float* __restrict__ dot_out) {
     __shared__ __attribute__((aligned(16))) Tile sQ, sK, sV, sW, sS, sSlo;
     __shared__ float s_gl[kTile], s_w[kTile];
     __shared__ ConvLds s_conv;
@@ -419,9 +454,9 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     Stage sq, sk, sv, bq, bk, bv;
     {
         const int t0 = c0 * kTile, Lc = min(kTile, T - t0);
-        fetch(sq, q + (base + t0) * kD, Lc, tid);
-        fetch(sk, k + (base + t0) * kD, Lc, tid);
-        fetch(sv, v + (base + t0) * kD, Lc, tid);
+        fetch_rows(sq, q + base * kD, t0, Lc, T, kRev, tid);
+        fetch_rows(sk, k + base * kD, t0, Lc, T, kRev, tid);
+        fetch_rows(sv, v + base * kD, t0, Lc, T, kRev, tid);
         if (conv) {
             fetch_before(bq, q + base * kD, qprev, t0, Lc, tid);
             fetch_before(bk, k + base * kD, kprev, t0, Lc, tid);
@@ -431,7 +466,7 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     for (int c = c0; c < c1; ++c) {
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
         if (w == 0) {
-            const float incl = chunk_prefix(z + base + t0, lane, Lc);
+            const float incl = chunk_prefix_dir(z + base, t0, T, kRev, lane, Lc);
             const float total = __shfl(incl, 63);
             s_gl[lane] = incl;
             s_w[lane] = total - incl;              // log2 of w_t = exp(Gam - Gl_t)
@@ -463,9 +498,9 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         __syncthreads();
         if (c + 1 < c1) {
             const int tn = t0 + kTile, Ln = min(kTile, T - tn);
-            fetch(sq, q + (base + tn) * kD, Ln, tid);
-            fetch(sk, k + (base + tn) * kD, Ln, tid);
-            fetch(sv, v + (base + tn) * kD, Ln, tid);
+            fetch_rows(sq, q + base * kD, tn, Ln, T, kRev, tid);
+            fetch_rows(sk, k + base * kD, tn, Ln, T, kRev, tid);
+            fetch_rows(sv, v + base * kD, tn, Ln, T, kRev, tid);
             if (conv) {
                 fetch_before(bq, q + base * kD, qprev, tn, Ln, tid);
                 fetch_before(bk, k + base * kD, kprev, tn, Ln, tid);
@@ -501,21 +536,43 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int sl = 16 * st + 4 * g + i;
-                    p[4 * u + i] = sl <= tl ? scale * fexp2(glt - gs[i]) * X[i] : 0.f;
+                    p[4 * u + i] = (kStrict ? sl < tl : sl <= tl) ? scale * fexp2(glt - gs[i]) * X[i] : 0.f;
                 }
             }
             const b8 B = to_b(p);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) O[ct] = mfma(tr_op(sV, ct, 2 * h, lane), B, O[ct]);
         }
-        if (tl < Lc) {
+        {
+            // optional fp32 epilogue: dot_out_t = xdot_t . o_t over the 64 columns, before the
+            // output is rounded (the backward's strict row and column sums of dL/dlambda)
             const float dec = scale * fexp2(glt);
+            const size_t prow = base + stored_row(t0 + tl, T, kRev);
+            float dot = 0.f;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                uint2 o;
-                o.x = pack2(fmaf(dec, OI[ct][0], O[ct][0]), fmaf(dec, OI[ct][1], O[ct][1]));
-                o.y = pack2(fmaf(dec, OI[ct][2], O[ct][2]), fmaf(dec, OI[ct][3], O[ct][3]));
-                *reinterpret_cast<uint2*>(out + (base + t0 + tl) * kD + 16 * ct + 4 * g) = o;
+                float y[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = fmaf(dec, OI[ct][i], O[ct][i]);
+                if (tl < Lc) {
+                    uint2 o;
+                    o.x = pack2(y[0], y[1]);
+                    o.y = pack2(y[2], y[3]);
+                    *reinterpret_cast<uint2*>(out + prow * kD + 16 * ct + 4 * g) = o;
+                    if (kStrict && xdot != nullptr) {
+                        const uint2 xv = *reinterpret_cast<const uint2*>(xdot + prow * kD + 16 * ct + 4 * g);
+                        dot = fmaf(__uint_as_float(xv.x << 16), y[0], dot);
+                        dot = fmaf(__uint_as_float(xv.x & 0xffff0000u), y[1], dot);
+                        dot = fmaf(__uint_as_float(xv.y << 16), y[2], dot);
+                        dot = fmaf(__uint_as_float(xv.y & 0xffff0000u), y[3], dot);
+                    }
+                }
+            }
+            if (kStrict && xdot != nullptr) {
+                // the four lanes of a token (lane groups g = 0..3, 16 apart) hold its 64 columns
+                dot += __shfl_xor(dot, 16);
+                dot += __shfl_xor(dot, 32);
+                if (tl < Lc && g == 0) dot_out[prow] = dot;
             }
         }
         // update: S^T = exp(Gam) S^T + (w V)^T K
@@ -532,7 +589,8 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     }
 }
 
-int run_fused(const FwdArgs& a) {
+template <bool kRev, bool kStrict = kRev>
+int run_fused(const FwdArgs& a, const bf16* xdot = nullptr, float* dot_out = nullptr) {
     const int nc = (a.T + kTile - 1) / kTile;
     const int nbh = a.B * a.H;
     // segments: about two workgroups per CU, at least two chunks each
@@ -546,11 +604,11 @@ int run_fused(const FwdArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     ktimer_begin(a.timer, "lin_seg", a.stream);
     const bf16* cprev = (const bf16*)a.conv_prev;
-    if (a.conv_w)
-        hipLaunchKernelGGL(lin_seg_mfma<true>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k,
+    if (!kRev && a.conv_w)
+        hipLaunchKernelGGL((lin_seg_mfma<true, false>), dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k,
                            (const bf16*)a.v, a.z, wsS, wsG, a.T, nseg, sc, a.conv_w, a.conv_b, cprev, a.H);
     else
-        hipLaunchKernelGGL(lin_seg_mfma<false>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k,
+        hipLaunchKernelGGL((lin_seg_mfma<false, kRev>), dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.k,
                            (const bf16*)a.v, a.z, wsS, wsG, a.T, nseg, sc, nullptr, nullptr, nullptr, a.H);
     ktimer_end(a.timer, a.stream);
     const int etiles = (kD * kD + 255) / 256;
@@ -559,19 +617,131 @@ int run_fused(const FwdArgs& a) {
                        a.state_in, a.state_out, nseg, etiles);
     ktimer_end(a.timer, a.stream);
     ktimer_begin(a.timer, "lin_main", a.stream);
-    if (a.conv_w)
-        hipLaunchKernelGGL(lin_main_mfma<true>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q,
+    if (!kRev && a.conv_w)
+        hipLaunchKernelGGL((lin_main_mfma<true, false, false>), dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, a.z, (const float*)wsS, (bf16*)a.out, a.T, nseg, sc,
-                           a.scale, a.conv_w, a.conv_b, cprev, a.H);
+                           a.scale, a.conv_w, a.conv_b, cprev, a.H, nullptr, nullptr);
     else
-        hipLaunchKernelGGL(lin_main_mfma<false>, dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q,
+        hipLaunchKernelGGL((lin_main_mfma<false, kRev, kStrict>), dim3(nbh * nseg), dim3(kThreads), 0, st, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, a.z, (const float*)wsS, (bf16*)a.out, a.T, nseg, sc,
-                           a.scale, nullptr, nullptr, nullptr, a.H);
+                           a.scale, nullptr, nullptr, nullptr, a.H, xdot, dot_out);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
+// The gradients from the strictly causal passes (dq^S, dk^S, dv^S in the output
+// buffers) finished in place with their diagonal terms:
+//     dq_t = dq^S_t + a_t k_t,  dk_t = dk^S_t + a_t q_t,  dv_t = dv^S_t + c_t dout_t,
+//     a_t = scale dout_t.v_t,   c_t = scale q_t.k_t.
+// The strict row and column sums of dL/dlambda that dz needs (2Mamba2Furious,
+// App. C.1), rowsum_t = q_t . dq^S_t = sum_{s<t} dL/dlambda_ts and colsum_t =
+// k_t . dk^S_t = sum_{t'>t} dL/dlambda_t't, come from the passes in fp32: formed
+// from outputs that never held the diagonal, and before their rounding, since dz
+// is their running difference over the whole sequence.  One thread per token.
+__global__ void __launch_bounds__(256)
+lin_bwd_finish_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                      const bf16* __restrict__ dout, bf16* __restrict__ gq, bf16* __restrict__ gk,
+                      bf16* __restrict__ gv, float scale, size_t n) {
+    // eight consecutive lanes per token, each with 8 of its 64 channels (16-byte accesses)
+    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t t = e >> 3;
+    const bool live = t < n;
+    const size_t o = t * kD + 8 * (e & 7);
+    float xq[8], xk[8], xv[8], xd[8];
+    float a = 0.f, c = 0.f;
+    if (live) {
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(q + o), xq);
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(k + o), xk);
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(v + o), xv);
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(dout + o), xd);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a = fmaf(xd[i], xv[i], a);
+            c = fmaf(xq[i], xk[i], c);
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {   // sums over the token's eight lanes
+        a += __shfl_xor(a, m);
+        c += __shfl_xor(c, m);
+    }
+    if (!live) return;
+    a *= scale;
+    c *= scale;
+    float s8[8], y[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(gq + o), s8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fmaf(a, xk[i], s8[i]);
+    *reinterpret_cast<uint4*>(gq + o) = f32x8_to_bf16(y);
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(gk + o), s8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fmaf(a, xq[i], s8[i]);
+    *reinterpret_cast<uint4*>(gk + o) = f32x8_to_bf16(y);
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(gv + o), s8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fmaf(c, xd[i], s8[i]);
+    *reinterpret_cast<uint4*>(gv + o) = f32x8_to_bf16(y);
+}
+
+FwdArgs lin_bwd_fwd_args(const BwdArgs& a) {
+    FwdArgs f;
+    memset(&f, 0, sizeof(f));
+    f.B = a.B; f.H = a.H; f.T = a.T; f.dk = a.dk; f.dv = a.dv; f.chunk = kLinChunk;
+    f.scale = a.scale; f.variant = TWOMAMBA_LIN; f.dtype = a.dtype;
+    f.z = a.z; f.ws = a.ws; f.ws_bytes = a.ws_bytes; f.stream = a.stream; f.timer = a.timer;
+    return f;
+}
+
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// First-order backward in O(T) (bf16, d = 64).  With w_ts = L_ts scale q_t.k_s and
+// no normaliser, the gradients are three first-order forwards of the same decay:
+//     dq_t = sum_{s<=t} L_ts scale (dout_t.v_s) k_s      queries dout, keys v, values k
+//     dk_s = sum_{t>=s} L_ts scale (v_s.dout_t) q_t      the same in reverse time: queries v,
+//     dv_s = sum_{t>=s} L_ts scale (k_s.q_t) dout_t      keys dout, values q / queries k, keys q,
+//                                                       values dout
+// run by the segmented chunk kernels of the forward (the last two back to front)
+// with a strictly causal mask, then finished with the diagonal terms; dL/dg comes
+// from the strict row and column sums of dL/dlambda (2Mamba2Furious, App. C, C.1).
+bool lin_bwd_chunked_supported(const BwdArgs& a) {
+    return a.variant == TWOMAMBA_LIN && a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 &&
+           !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
+}
+
+size_t lin_bwd_chunked_workspace(const BwdArgs& a) {
+    const size_t n = (size_t)a.B * a.H * a.T;
+    if (n == 0) return 0;
+    return align256(lin_layout(lin_bwd_fwd_args(a)).total) + 2 * align256(n * sizeof(float));
+}
+
+int lin_bwd_chunked(const BwdArgs& a) {
+    const size_t n = (size_t)a.B * a.H * a.T;
+    if (n == 0) return TWOMAMBA_OK;
+    FwdArgs f = lin_bwd_fwd_args(a);
+    int r;
+    // strictly causal passes: the diagonal terms are added by the finishing kernel
+    BwdScratch sc;
+    memset(&sc, 0, sizeof(sc));
+    char* p = (char*)a.ws + align256(lin_layout(f).total);
+    sc.rowsum = (float*)p;
+    sc.colsum = (float*)(p + align256(n * sizeof(float)));
+    // rowsum_t = q_t . dq^S_t and colsum_s = k_s . dk^S_s are taken in fp32 by the passes
+    f.q = a.dout; f.k = a.v; f.v = a.k; f.out = a.gq;
+    if ((r = run_fused<false, true>(f, (const bf16*)a.q, sc.rowsum)) != TWOMAMBA_OK) return r;
+    f.q = a.v; f.k = a.dout; f.v = a.q; f.out = a.gk;
+    if ((r = run_fused<true, true>(f, (const bf16*)a.k, sc.colsum)) != TWOMAMBA_OK) return r;
+    f.q = a.k; f.k = a.q; f.v = a.dout; f.out = a.gv;
+    if ((r = run_fused<true, true>(f)) != TWOMAMBA_OK) return r;
+    ktimer_begin(a.timer, "lin_bwd_finish", a.stream);
+    hipLaunchKernelGGL(lin_bwd_finish_kernel, dim3((unsigned)((8 * n + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)a.stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, (bf16*)a.gq,
+                       (bf16*)a.gk, (bf16*)a.gv, a.scale, n);
+    ktimer_end(a.timer, a.stream);
+    if (hipGetLastError() != hipSuccess) return TWOMAMBA_ERR_DEVICE;
+    return bwd_dz_launch(a, sc);
+}
 
 bool lin_conv_fused(const FwdArgs& a) {
     return a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
@@ -594,7 +764,7 @@ int lin_fwd(const FwdArgs& a) {
         return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
     }
     const bool bf = a.dtype == TWOMAMBA_BF16;
-    if (bf && a.dk == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS)) return run_fused(a);
+    if (bf && a.dk == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS)) return run_fused<false, false>(a);
     if (a.dk == 64) return bf ? run<64, 64, bf16>(a) : run<64, 64, float>(a);
     if (a.dk == 16) return bf ? run<16, 16, bf16>(a) : run<16, 16, float>(a);
     return TWOMAMBA_ERR_UNSUPPORTED;

@@ -139,3 +139,40 @@ def test_bwd_full_size_two_heads(variant):
         sl = lambda t: SI.to_f64(t[b:b + 1, h:h + 1])
         ref = O.bwd_blocked(sl(q), sl(k), sl(v), sl(z), sl(do), variant=variant)
         check([x[b:b + 1, h:h + 1] for x in got], ref, TOL["bf16"], f"{variant} head ({b},{h})")
+
+
+@pytest.mark.parametrize("B,H,T,heads", [(2, 16, 8192, [(0, 3), (1, 12)]), (1, 16, 32768, [(0, 7)])])
+def test_lin_bwd_linear_in_T_full_size(B, H, T, heads):
+    # the first order's O(T) backward (three segmented forwards, two of them in reverse
+    # time) at the workload sizes, with slow decay (z_mean -8) so that the carried
+    # states of the reverse passes reach across chunks and segments
+    d = 64
+    announce(f"first-order chunked bwd {B}x{H}x{T} z_mean -8")
+    q, k, v, z = SI.draw(B, H, T, d, seed=3, dtype="bf16", z_mean=-8.0)
+    do = _dout(B, H, T, d, "bf16", 3)
+    qd, kd, vd, zd, dod = dev(q, k, v, z, do)
+    out = tmb.fwd(qd, kd, vd, zd, variant="lin")
+    g = tmb.bwd(qd, kd, vd, zd, out, dod, variant="lin")
+    torch.cuda.synchronize()
+    got = [host64(x) for x in g]
+    for b, h in heads:
+        sl = lambda t: SI.to_f64(t[b:b + 1, h:h + 1])
+        ref = O.bwd_blocked(sl(q), sl(k), sl(v), sl(z), sl(do), variant="lin")
+        check([x[b:b + 1, h:h + 1] for x in got], ref, TOL["bf16"], f"lin head ({b},{h})")
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 700])
+def test_lin_bwd_linear_form_matches_attention_form(T):
+    # the same gradients from the O(T) path and from the quadratic reference kernels
+    announce(f"first-order bwd: chunked vs reference kernels T={T}")
+    q, k, v, z = SI.draw(2, 3, T, 64, seed=60 + T, dtype="bf16", z_mean=-6.0)
+    do = _dout(2, 3, T, 64, "bf16", 61)
+    qd, kd, vd, zd, dod = dev(q, k, v, z, do)
+    out = tmb.fwd(qd, kd, vd, zd, variant="lin")
+    a = tmb.bwd(qd, kd, vd, zd, out, dod, variant="lin")
+    b = tmb.bwd(qd, kd, vd, zd, out, dod, variant="lin", reference_kernels=True)
+    torch.cuda.synchronize()
+    for nm, x, y in zip(("dq", "dk", "dv", "dz"), a, b):
+        e = relerr(host64(x), host64(y))
+        print(f"  {nm} {e:.2e}")
+        assert e < TOL["bf16"], nm
