@@ -175,11 +175,93 @@ step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __rest
     }
 }
 
+// First-order step at d = 64: the state is only 64 x 64 fp32 (16 KB) per head, so
+// one wave takes a head and four heads share a workgroup.  Lane (rq, cg) owns the
+// 16 rows 4i + rq (i = 0..15) of column group cg (4 columns): all 16 row loads are
+// in flight at once, every load and store instruction of the wave covers four whole
+// consecutive rows (1 KB), and the readout's sum over rows is finished across the
+// four lanes of a column group by shuffles in a fixed order (no LDS round trip).
+template <typename In>
+__global__ void __launch_bounds__(256)
+step_first_order64_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+                          const float* __restrict__ z, float* __restrict__ state, In* __restrict__ out,
+                          float scale, const float* __restrict__ cw, const float* __restrict__ cb,
+                          In* __restrict__ cst, int H, int nbh) {
+    constexpr int D = 64;
+    __shared__ float s_in[4][3][D];   // per wave: scale q, k, v (convolved when a cache is attached)
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * 4 + w;
+    const bool live = bh < nbh;   // uniform over the wave
+    const int cg = lane & 15, rq = lane >> 4;
+    float4* S = reinterpret_cast<float4*>(state + (size_t)bh * D * D);
+    // the state's loads go out first: nothing they fetch depends on the inputs
+    float4 x[16];
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = ld_nt(&S[(4 * i + rq) * 16 + cg]);
+    }
+    if (live) {
+#pragma unroll
+        for (int which = 0; which < 3; ++which) {
+            const In* src = which == 0 ? q : which == 1 ? k : v;
+            float x = IO<In>::ld(src, (size_t)bh * D + lane);
+            if (cw) {
+                const size_t wi = (size_t)(which * H + bh % H) * D + lane;
+                In* cs = cst + ((size_t)bh * 3 + which) * D;
+                const float before = IO<In>::ld(cs, lane);
+                IO<In>::st(cs, lane, x);
+                x = fmaf(cw[2 * wi + 1], x, cw[2 * wi] * before) + (cb ? cb[wi] : 0.f);
+            }
+            s_in[w][which][lane] = which == 0 ? x * scale : x;
+        }
+    }
+    __syncthreads();
+    if (!live) return;
+    const float a = expf(decay_log(z[bh]));
+    const float4 v4 = make_float4(s_in[w][2][4 * cg], s_in[w][2][4 * cg + 1], s_in[w][2][4 * cg + 2],
+                                  s_in[w][2][4 * cg + 3]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 4 * i + rq;
+        const float fk = s_in[w][1][r], fq = s_in[w][0][r];
+        float4 y;
+        y.x = fmaf(a, x[i].x, fk * v4.x);
+        y.y = fmaf(a, x[i].y, fk * v4.y);
+        y.z = fmaf(a, x[i].z, fk * v4.z);
+        y.w = fmaf(a, x[i].w, fk * v4.w);
+        st_nt(&S[r * 16 + cg], y);
+        acc.x = fmaf(fq, y.x, acc.x);
+        acc.y = fmaf(fq, y.y, acc.y);
+        acc.z = fmaf(fq, y.z, acc.z);
+        acc.w = fmaf(fq, y.w, acc.w);
+    }
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m);
+        acc.y += __shfl_xor(acc.y, m);
+        acc.z += __shfl_xor(acc.z, m);
+        acc.w += __shfl_xor(acc.w, m);
+    }
+    if (rq == 0) {
+        IO<In>::st(out, (size_t)bh * D + 4 * cg, acc.x);
+        IO<In>::st(out, (size_t)bh * D + 4 * cg + 1, acc.y);
+        IO<In>::st(out, (size_t)bh * D + 4 * cg + 2, acc.z);
+        IO<In>::st(out, (size_t)bh * D + 4 * cg + 3, acc.w);
+    }
+}
+
 template <int DK, int DV, typename In>
 int launch(const StepArgs& a) {
     const int nbh = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
     const bool first = (a.flags & TWOMAMBA_FLAG_FIRST_ORDER) != 0;
+    if (first && DK == 64 && DV == 64) {
+        hipLaunchKernelGGL(step_first_order64_kernel<In>, dim3((unsigned)((nbh + 3) / 4)), dim3(256), 0, st,
+                           (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, a.state, (In*)a.out, a.scale,
+                           a.conv_w, a.conv_b, (In*)a.conv_state, a.H, nbh);
+        return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
+    }
     auto kern = first ? step_kernel<DK, DV, In, 1> : step_kernel<DK, DV, In, 2>;
     hipLaunchKernelGGL(kern, dim3(nbh), dim3(kStepThreads), 0, st,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, a.z, a.state, a.norm, (In*)a.out,
