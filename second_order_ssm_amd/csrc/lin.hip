@@ -95,8 +95,8 @@ lin_scan(float* __restrict__ wsS, const float* __restrict__ wsG, const float* st
     float run = state_in ? state_in[(size_t)bh * DK * DV + ea] : 0.f;
     float* base = wsS + (size_t)bh * nc * DK * DV + e;
     const float* gb = wsG + (size_t)bh * nc;
-    // the chain is serial in c: load eight chunks' deltas and decays ahead of it
-    constexpr int U = 8;
+    // the chain is serial in c: load sixteen chunks' (segments') deltas and decays ahead of it
+    constexpr int U = 16;
     int c = 0;
     for (; c + U <= nc; c += U) {
         float x[U], a[U];
@@ -236,38 +236,71 @@ __device__ __forceinline__ b8 q_tr_order(const Tile& t, int row, int dtt, int g)
 // over [T-1-t, T-1-s): logical tau takes z_{T-tau}, and tau = 0 no decay at all.
 __device__ __forceinline__ int stored_row(int tau, int T, bool rev) { return rev ? T - 1 - tau : tau; }
 
-__device__ __forceinline__ float logical_decay_log(const float* zhead, int tau, int T, bool rev) {
-    if (!rev) return decay_log(zhead[tau]);
-    return tau == 0 ? 0.f : decay_log(zhead[T - tau]);
+
+// Per-head buffer resources: an access past `bytes` (or at a negative offset, which
+// wraps past it) loads zeros or stores nothing, so that ragged chunks need no branch
+// around a memory instruction.  Without such branches the compiler knows how many
+// loads and stores are in flight at every wait and waits for exactly the ones it
+// needs, instead of for all of them (the previous chunk's output stores included).
+// A head's rows are addressable this way while T * 128 bytes < 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 x) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, x), r,
+                                          off, 0, 0);
+}
+__device__ __forceinline__ void buf_st4f(__amdgpu_buffer_rsrc_t r, uint32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, 0);
+}
+// an offset past every resource (they hold < 2^31 bytes), also after the few hundred
+// bytes a caller may add to it
+constexpr uint32_t kNoAccess = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rows(const bf16* head, int T) {
+    return buf_rsrc(head, (uint32_t)T * kD * 2);
 }
 
-// rows t0 .. t0 + rows - 1 (logical) of a head's tensor in the Stage layout
-__device__ __forceinline__ void fetch_rows(Stage& s, const bf16* head, int t0, int rows, int T, bool rev, int tid) {
+// rows t0 .. t0 + 63 (logical) of a head's tensor in the Stage layout (zeros past T)
+__device__ __forceinline__ void fetch_rows(Stage& s, __amdgpu_buffer_rsrc_t head, int t0, int T, bool rev, int tid) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int e = tid + n * kThreads, r = e >> 3, c = e & 7;
-        s.c[n] = r < rows ? *reinterpret_cast<const uint4*>(head + (size_t)stored_row(t0 + r, T, rev) * kD + 8 * c)
-                          : make_uint4(0u, 0u, 0u, 0u);
+        s.c[n] = buf_ld16(head, (uint32_t)(stored_row(t0 + r, T, rev) * kD + 8 * c) * 2);
     }
 }
 
-// chunk-local inclusive prefix of g (log2 units) over the 64 lanes of one wave
-__device__ __forceinline__ float chunk_prefix_dir(const float* zhead, int t0, int T, bool rev, int lane, int Lc) {
-    float incl = lane < Lc ? logical_decay_log(zhead, t0 + lane, T, rev) : 0.f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    return incl * kLog2e;
+// The logit z behind g of logical token t0 + lane, loaded a chunk ahead (0 where the
+// token has no decay: past the chunk's last token, and logical 0 in reverse mode);
+// softplus is applied only when the chunk is processed, so that the load stays in
+// flight meanwhile.
+__device__ __forceinline__ bool lane_has_decay(int t0, int rev, int lane, int Lc) {
+    return lane < Lc && !(rev && t0 + lane == 0);
+}
+__device__ __forceinline__ float lane_z(__amdgpu_buffer_rsrc_t zhead, int t0, int T, bool rev, int lane, int Lc) {
+    const int i = rev ? T - (t0 + lane) : t0 + lane;
+    return buf_ld4f(zhead, lane_has_decay(t0, rev, lane, Lc) ? (uint32_t)i * 4 : kNoAccess);
+}
+__device__ __forceinline__ float lane_decay(float zraw, int t0, bool rev, int lane, int Lc) {
+    return lane_has_decay(t0, rev, lane, Lc) ? decay_log(zraw) : 0.f;
 }
 
-__device__ __forceinline__ float chunk_prefix(const float* z, int lane, int Lc) {
-    float incl = lane < Lc ? decay_log(z[lane]) : 0.f;
+// chunk-local inclusive prefix of g (log2 units) over the 64 lanes of one wave,
+// from each lane's own g
+__device__ __forceinline__ float chunk_prefix_of(float incl) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+        if ((int)(threadIdx.x & 63) >= o) incl += y;
     }
     return incl * kLog2e;
 }
@@ -302,19 +335,17 @@ __device__ __forceinline__ Conv8 conv_lds_get(const ConvLds& c, int tensor, int 
     return r;
 }
 
-// rows t0 - 1 .. t0 + rows - 2 of a head's tensor in the Stage layout (the row before
-// each staged row); `prev` is the cached raw row of token -1 (NULL = zeros)
-__device__ __forceinline__ void fetch_before(Stage& s, const bf16* head, const bf16* prev, int t0, int rows,
-                                             int tid) {
+// rows t0 - 1 .. t0 + 62 of a head's tensor in the Stage layout (the row before each
+// staged row); `prev` covers the cached raw row of token -1 (an empty resource =
+// zeros).  Both loads are issued for every row, one of them past its resource.
+__device__ __forceinline__ void fetch_before(Stage& s, __amdgpu_buffer_rsrc_t head, __amdgpu_buffer_rsrc_t prev,
+                                             int t0, int tid) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int e = tid + n * kThreads, r = e >> 3, c = e & 7, t = t0 + r - 1;
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (r < rows) {
-            if (t >= 0) x = *reinterpret_cast<const uint4*>(head + (size_t)t * kD + 8 * c);
-            else if (prev) x = *reinterpret_cast<const uint4*>(prev + 8 * c);
-        }
-        s.c[n] = x;
+        const uint4 a = buf_ld16(head, (uint32_t)(t * kD + 8 * c) * 2);
+        const uint4 b = buf_ld16(prev, t < 0 ? (uint32_t)(8 * c) * 2 : kNoAccess);
+        s.c[n] = make_uint4(a.x | b.x, a.y | b.y, a.z | b.z, a.w | b.w);
     }
 }
 
@@ -354,53 +385,54 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
     __shared__ float s_w[kTile];
     __shared__ ConvLds s_conv;
     const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, col = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nc = (T + kTile - 1) / kTile;
     const int c0 = seg * seg_chunks, c1 = min(nc, c0 + seg_chunks);
     const size_t base = (size_t)bh * T;
     constexpr bool conv = kConv;
-    const bf16* kprev = cprev ? cprev + ((size_t)bh * 3 + 1) * kD : nullptr;
-    const bf16* vprev = cprev ? cprev + ((size_t)bh * 3 + 2) * kD : nullptr;
+    const __amdgpu_buffer_rsrc_t rk = head_rows(k + base * kD, T), rv = head_rows(v + base * kD, T),
+                                 rz = buf_rsrc(z + base, (uint32_t)T * 4);
+    const __amdgpu_buffer_rsrc_t rkp = buf_rsrc(cprev ? cprev + ((size_t)bh * 3 + 1) * kD : nullptr, cprev ? kD * 2 : 0),
+                                 rvp = buf_rsrc(cprev ? cprev + ((size_t)bh * 3 + 2) * kD : nullptr, cprev ? kD * 2 : 0);
     if (conv) conv_lds_fill(s_conv, cw, cb, bh % H, H, tid);
     f4 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
     float later = 0.f;   // log2 decay from the end of the current chunk to the segment end
-    Stage sk, sv, bk, bv;
-    {
-        const int t0 = (c1 - 1) * kTile;
-        fetch_rows(sk, k + base * kD, t0, min(kTile, T - t0), T, kRev, tid);
-        fetch_rows(sv, v + base * kD, t0, min(kTile, T - t0), T, kRev, tid);
+    // the next chunk's rows in flight to registers while this one is computed
+    struct Ahead {
+        Stage k, v, bk, bv;
+        float gz;   // wave 0: this lane's z
+    };
+    auto fetch_chunk = [&](Ahead& f, int c) {
+        const int t0 = c * kTile, Lc = min(kTile, T - t0);
+        if (w == 0) f.gz = lane_z(rz, t0, T, kRev, lane, Lc);
+        fetch_rows(f.k, rk, t0, T, kRev, tid);
+        fetch_rows(f.v, rv, t0, T, kRev, tid);
         if (conv) {
-            fetch_before(bk, k + base * kD, kprev, t0, min(kTile, T - t0), tid);
-            fetch_before(bv, v + base * kD, vprev, t0, min(kTile, T - t0), tid);
+            fetch_before(f.bk, rk, rkp, t0, tid);
+            fetch_before(f.bv, rv, rvp, t0, tid);
         }
-    }
-    for (int c = c1 - 1; c >= c0; --c) {   // from the segment end backwards
+    };
+    // one chunk from buffer f, which is refilled with chunk c - 1 once staged
+    auto chunk = [&](int c, Ahead& f) {
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
         if (w == 0) {
-            const float incl = chunk_prefix_dir(z + base, t0, T, kRev, lane, Lc);
+            const float incl = chunk_prefix_of(lane_decay(f.gz, t0, kRev, lane, Lc));
             const float total = __shfl(incl, 63);
             s_w[lane] = total - incl + later;      // log2 w_t relative to the segment end
             later += total;   // kept by wave 0, which also writes the segment's decay
         }
         __syncthreads();
         if (conv) {
-            conv_stage(sk, bk, s_conv, 1, Lc, tid);
-            conv_stage(sv, bv, s_conv, 2, Lc, tid);
+            conv_stage(f.k, f.bk, s_conv, 1, Lc, tid);
+            conv_stage(f.v, f.bv, s_conv, 2, Lc, tid);
         }
-        store(sk, sK, tid);
-        store_scaled(sv, sV, s_w, tid);
+        store(f.k, sK, tid);
+        store_scaled(f.v, sV, s_w, tid);
         __syncthreads();
-        if (c > c0) {
-            const int tn = t0 - kTile;
-            fetch_rows(sk, k + base * kD, tn, kTile, T, kRev, tid);
-            fetch_rows(sv, v + base * kD, tn, kTile, T, kRev, tid);
-            if (conv) {
-                fetch_before(bk, k + base * kD, kprev, tn, kTile, tid);
-                fetch_before(bv, v + base * kD, vprev, tn, kTile, tid);
-            }
-        }
+        if (c > c0) fetch_chunk(f, c - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const b8 A = tr_op(sV, w, 2 * h, lane);
@@ -408,7 +440,11 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
             for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(A, tr_op(sK, dt, 2 * h, lane), acc[dt]);
         }
         __syncthreads();
-    }
+    };
+    Ahead f;
+    fetch_chunk(f, c1 - 1);   // from the segment end backwards
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing issued before the loop left in flight at its top
+    for (int c = c1 - 1; c >= c0; --c) chunk(c, f);
     float* dst = wsS + ((size_t)bh * nseg + seg) * kD * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -430,14 +466,19 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     __shared__ float s_gl[kTile], s_w[kTile];
     __shared__ ConvLds s_conv;
     const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, col = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nc = (T + kTile - 1) / kTile;
     const int c0 = seg * seg_chunks, c1 = min(nc, c0 + seg_chunks);
     const size_t base = (size_t)bh * T;
     constexpr bool conv = kConv;
-    const bf16* qprev = cprev ? cprev + ((size_t)bh * 3 + 0) * kD : nullptr;
-    const bf16* kprev = cprev ? cprev + ((size_t)bh * 3 + 1) * kD : nullptr;
-    const bf16* vprev = cprev ? cprev + ((size_t)bh * 3 + 2) * kD : nullptr;
+    const __amdgpu_buffer_rsrc_t rq = head_rows(q + base * kD, T), rk = head_rows(k + base * kD, T),
+                                 rv = head_rows(v + base * kD, T), rz = buf_rsrc(z + base, (uint32_t)T * 4),
+                                 ro = head_rows(out + base * kD, T);
+    auto prev_rows = [&](int which) {
+        return buf_rsrc(cprev ? cprev + ((size_t)bh * 3 + which) * kD : nullptr, cprev ? kD * 2 : 0);
+    };
+    const __amdgpu_buffer_rsrc_t rqp = prev_rows(0), rkp = prev_rows(1), rvp = prev_rows(2);
     if (conv) {
         conv_lds_fill(s_conv, cw, cb, bh % H, H, tid);
         __syncthreads();
@@ -451,22 +492,46 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[dt][i] = src[(16 * w + 4 * g + i) * kD + 16 * dt + col];
     }
-    Stage sq, sk, sv, bq, bk, bv;
-    {
-        const int t0 = c0 * kTile, Lc = min(kTile, T - t0);
-        fetch_rows(sq, q + base * kD, t0, Lc, T, kRev, tid);
-        fetch_rows(sk, k + base * kD, t0, Lc, T, kRev, tid);
-        fetch_rows(sv, v + base * kD, t0, Lc, T, kRev, tid);
+    // the next chunk's rows in flight to registers while this one is computed
+    const bool dots = kStrict && xdot != nullptr;
+    const __amdgpu_buffer_rsrc_t rx = head_rows(dots ? xdot + base * kD : out, T);
+    const int tl = 16 * w + col;   // this lane's query in the chunk (with its lane group g)
+    struct Ahead {
+        Stage q, k, v, bq, bk, bv;
+        uint2 x[4];   // the backward's dot operand at this lane's output positions
+        float gz;     // wave 0: this lane's z
+    };
+    auto fetch_chunk = [&](Ahead& f, int c) {
+        const int t0 = c * kTile, Lc = min(kTile, T - t0);
+        if (w == 0) f.gz = lane_z(rz, t0, T, kRev, lane, Lc);
+        fetch_rows(f.q, rq, t0, T, kRev, tid);
+        fetch_rows(f.k, rk, t0, T, kRev, tid);
+        fetch_rows(f.v, rv, t0, T, kRev, tid);
         if (conv) {
-            fetch_before(bq, q + base * kD, qprev, t0, Lc, tid);
-            fetch_before(bk, k + base * kD, kprev, t0, Lc, tid);
-            fetch_before(bv, v + base * kD, vprev, t0, Lc, tid);
+            fetch_before(f.bq, rq, rqp, t0, tid);
+            fetch_before(f.bk, rk, rkp, t0, tid);
+            fetch_before(f.bv, rv, rvp, t0, tid);
         }
-    }
-    for (int c = c0; c < c1; ++c) {
+        if (dots) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                f.x[ct] = buf_ld8(rx, (uint32_t)(stored_row(t0 + tl, T, kRev) * kD + 16 * ct + 4 * g) * 2);
+        }
+    };
+    // This chunk's output is stored one chunk later, right after the next prefetch is
+    // issued: stores issued at the end of a chunk would still be in flight at the next
+    // chunk's first wait for its rows.  An offset past the buffer = nothing pending.
+    uint2 po[4];
+    uint32_t poff = kNoAccess;
+    auto store_out = [&]() {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) buf_st8(ro, poff + 32 * ct, po[ct]);
+    };
+    // one chunk from buffer f, which is refilled with chunk c + 1 once staged
+    auto chunk = [&](int c, Ahead& f) {
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
         if (w == 0) {
-            const float incl = chunk_prefix_dir(z + base, t0, T, kRev, lane, Lc);
+            const float incl = chunk_prefix_of(lane_decay(f.gz, t0, kRev, lane, Lc));
             const float total = __shfl(incl, 63);
             s_gl[lane] = incl;
             s_w[lane] = total - incl;              // log2 of w_t = exp(Gam - Gl_t)
@@ -486,29 +551,22 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             *reinterpret_cast<uint2*>(&sSlo.X[16 * dt + col][16 * w + 4 * g]) = r;
         }
         if (conv) {
-            conv_stage(sq, bq, s_conv, 0, Lc, tid);
-            conv_stage(sk, bk, s_conv, 1, Lc, tid);
-            conv_stage(sv, bv, s_conv, 2, Lc, tid);
+            conv_stage(f.q, f.bq, s_conv, 0, Lc, tid);
+            conv_stage(f.k, f.bk, s_conv, 1, Lc, tid);
+            conv_stage(f.v, f.bv, s_conv, 2, Lc, tid);
         }
-        store(sq, sQ, tid);
-        store(sk, sK, tid);
+        uint2 xc[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) xc[ct] = f.x[ct];
+        store(f.q, sQ, tid);
+        store(f.k, sK, tid);
         __syncthreads();
-        store_scaled(sv, sW, s_w, tid);
-        store(sv, sV, tid);
+        store_scaled(f.v, sW, s_w, tid);
+        store(f.v, sV, tid);
         __syncthreads();
-        if (c + 1 < c1) {
-            const int tn = t0 + kTile, Ln = min(kTile, T - tn);
-            fetch_rows(sq, q + base * kD, tn, Ln, T, kRev, tid);
-            fetch_rows(sk, k + base * kD, tn, Ln, T, kRev, tid);
-            fetch_rows(sv, v + base * kD, tn, Ln, T, kRev, tid);
-            if (conv) {
-                fetch_before(bq, q + base * kD, qprev, tn, Ln, tid);
-                fetch_before(bk, k + base * kD, kprev, tn, Ln, tid);
-                fetch_before(bv, v + base * kD, vprev, tn, Ln, tid);
-            }
-        }
+        if (c + 1 < c1) fetch_chunk(f, c + 1);
+        store_out();   // the previous chunk's
         // this wave's queries 16w .. 16w + 15, one per lane column
-        const int tl = 16 * w + col;
         const float glt = s_gl[tl];
         const b8 Qb[2] = {row_op(sQ, tl, g, 0), row_op(sQ, tl, g, 1)};
         f4 O[4], OI[4];
@@ -547,32 +605,30 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             // optional fp32 epilogue: dot_out_t = xdot_t . o_t over the 64 columns, before the
             // output is rounded (the backward's strict row and column sums of dL/dlambda)
             const float dec = scale * fexp2(glt);
-            const size_t prow = base + stored_row(t0 + tl, T, kRev);
+            // the token's row in the head; rows past the chunk's last token fall outside the
+            // buffers (negative ones wrap past them), so their stores are dropped
+            const int hrow = stored_row(t0 + tl, T, kRev);
+            poff = (uint32_t)(hrow * kD + 4 * g) * 2;
             float dot = 0.f;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 float y[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = fmaf(dec, OI[ct][i], O[ct][i]);
-                if (tl < Lc) {
-                    uint2 o;
-                    o.x = pack2(y[0], y[1]);
-                    o.y = pack2(y[2], y[3]);
-                    *reinterpret_cast<uint2*>(out + prow * kD + 16 * ct + 4 * g) = o;
-                    if (kStrict && xdot != nullptr) {
-                        const uint2 xv = *reinterpret_cast<const uint2*>(xdot + prow * kD + 16 * ct + 4 * g);
-                        dot = fmaf(__uint_as_float(xv.x << 16), y[0], dot);
-                        dot = fmaf(__uint_as_float(xv.x & 0xffff0000u), y[1], dot);
-                        dot = fmaf(__uint_as_float(xv.y << 16), y[2], dot);
-                        dot = fmaf(__uint_as_float(xv.y & 0xffff0000u), y[3], dot);
-                    }
+                po[ct] = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
+                if (dots) {
+                    const uint2 xv = xc[ct];
+                    dot = fmaf(__uint_as_float(xv.x << 16), y[0], dot);
+                    dot = fmaf(__uint_as_float(xv.x & 0xffff0000u), y[1], dot);
+                    dot = fmaf(__uint_as_float(xv.y << 16), y[2], dot);
+                    dot = fmaf(__uint_as_float(xv.y & 0xffff0000u), y[3], dot);
                 }
             }
-            if (kStrict && xdot != nullptr) {
+            if (dots) {
                 // the four lanes of a token (lane groups g = 0..3, 16 apart) hold its 64 columns
                 dot += __shfl_xor(dot, 16);
                 dot += __shfl_xor(dot, 32);
-                if (tl < Lc && g == 0) dot_out[prow] = dot;
+                buf_st4f(buf_rsrc(dot_out + base, (uint32_t)T * 4), g == 0 ? (uint32_t)hrow * 4 : kNoAccess, dot);
             }
         }
         // update: S^T = exp(Gam) S^T + (w V)^T K
@@ -586,8 +642,19 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             for (int dt = 0; dt < 4; ++dt) S[dt] = mfma(A, tr_op(sK, dt, 2 * h, lane), S[dt]);
         }
         __syncthreads();
-    }
+    };
+    Ahead f;
+    fetch_chunk(f, c0);
+    // Retire the loads above (the carry and the first chunk) before the loop: the waits
+    // inside it are sized for the loop's own order of loads and stores, which only holds
+    // when nothing issued before the loop is still in flight at its top.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (int c = c0; c < c1; ++c) chunk(c, f);
+    store_out();   // the last chunk's
 }
+
+// the segmented kernels address a head's rows through 32-bit buffer offsets
+static bool lin_rows_addressable(int T) { return (size_t)T * kD * 2 < ((size_t)1 << 31); }
 
 template <bool kRev, bool kStrict = kRev>
 int run_fused(const FwdArgs& a, const bf16* xdot = nullptr, float* dot_out = nullptr) {
@@ -706,7 +773,7 @@ FwdArgs lin_bwd_fwd_args(const BwdArgs& a) {
 // from the strict row and column sums of dL/dlambda (2Mamba2Furious, App. C, C.1).
 bool lin_bwd_chunked_supported(const BwdArgs& a) {
     return a.variant == TWOMAMBA_LIN && a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 &&
-           !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
+           lin_rows_addressable(a.T) && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
 }
 
 size_t lin_bwd_chunked_workspace(const BwdArgs& a) {
@@ -744,7 +811,8 @@ int lin_bwd_chunked(const BwdArgs& a) {
 }
 
 bool lin_conv_fused(const FwdArgs& a) {
-    return a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
+    return a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 && lin_rows_addressable(a.T) &&
+           !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
 }
 
 size_t lin_workspace(const FwdArgs& a) {
@@ -764,7 +832,8 @@ int lin_fwd(const FwdArgs& a) {
         return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
     }
     const bool bf = a.dtype == TWOMAMBA_BF16;
-    if (bf && a.dk == 64 && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS)) return run_fused<false, false>(a);
+    if (bf && a.dk == 64 && lin_rows_addressable(a.T) && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS))
+        return run_fused<false, false>(a);
     if (a.dk == 64) return bf ? run<64, 64, bf16>(a) : run<64, 64, float>(a);
     if (a.dk == 16) return bf ? run<16, 16, bf16>(a) : run<16, 16, float>(a);
     return TWOMAMBA_ERR_UNSUPPORTED;

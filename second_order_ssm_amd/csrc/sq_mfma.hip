@@ -215,11 +215,14 @@ __device__ __forceinline__ void fetch(Raw& r, const bf16* q, const bf16* k, cons
     r.q = r.k = r.v = z4;
     r.z = 0.f;
     if (t0 + lane < T) {
+        // the logit first: the wait for the rows (before the maxima are published) then
+        // retires it as well, and the next chunk's first use of it waits for nothing,
+        // in particular not for the output stores issued after these loads
+        r.z = z[tok_base + t0 + lane];
         const size_t row = (tok_base + t0 + lane) * kD;
         if (kWithQ) r.q = *reinterpret_cast<const uint4*>(q + row + 8 * w);
         r.k = *reinterpret_cast<const uint4*>(k + row + 8 * w);
         if (w < 4) r.v = *reinterpret_cast<const uint4*>(v + row + col0 + 8 * w);
-        r.z = z[tok_base + t0 + lane];
     }
 }
 
@@ -403,6 +406,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     const int nc_total = (T + kC - 1) / kC;
     const int c_begin = seg * seg_chunks;
     const int c_end = min(nc_total, c_begin + seg_chunks);
+    const int seg_T = min(T, c_end * kC);   // tokens past the segment's last read as zeros
     const size_t tok_base = (size_t)bh * T;
     const int col0 = half * kDV;
 
@@ -838,7 +842,11 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         }
 
         // ------------------------------------------------ P4: update (and next chunk's fetch)
-        if (c + 1 < c_end) fetch<true>(raw, q, k, v, z, tok_base, T, t0 + kC, lane, wl, col0);
+        // Fetched and published in every chunk, the last one included (where nothing past
+        // the segment is loaded and zeros are published that nothing reads): under a
+        // branch of their own, the loads would count as possibly outstanding at the top
+        // of the loop, and the waits there would also wait for this chunk's output stores.
+        fetch<true>(raw, q, k, v, z, tok_base, seg_T, t0 + kC, lane, wl, col0);
         {
             const _Float16 cslot = (_Float16)(bq4 < gq ? 0.f : (bq4 == gq ? 1.f : 2.f));
             if (fs.mul) {
@@ -857,7 +865,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             }
             update_norm(N, sm, wl, l16, kg);
         }
-        if (c + 1 < c_end) publish_max(c + 1, lane, wl);   // rows fetched above
+        publish_max(c + 1, lane, wl);   // rows fetched above
         __syncthreads();   // D
 
         // ------------------------------------------------ P5: combine and write out
