@@ -23,7 +23,8 @@
 //    statistic, a second one for dq and rowsum.
 //  * bwd_ref_kv_kernel: two threads per key (half of the dims each); a pass
 //    over the queries t >= s for dk, dv and colsum.
-//  * bwd_dz_kernel: the scan of colsum - rowsum and dz (one workgroup per head).
+//  * bwd_dz_kernel: the scan of colsum - rowsum and dz (one workgroup per 2048
+//    tokens of a head).
 #include <type_traits>
 
 #include "device_common.h"
@@ -307,31 +308,52 @@ bwd_ref_kv_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* 
 
 }  // namespace
 
-// dz from the row and column sums: exclusive fp64 prefix of colsum - rowsum
-__global__ void __launch_bounds__(1024)
+// dz from the row and column sums: exclusive fp64 prefix of colsum - rowsum.
+// A workgroup takes 2048 consecutive tokens of a head (8 per thread): it sums every
+// earlier token of the head itself (coalesced reads, which the workgroups of a head
+// share through L2), scans its own block, and writes dz.  No workgroup waits on
+// another, and every sum is taken in a fixed order, so the result is deterministic.
+constexpr int kDzThreads = 256, kDzPer = 8, kDzBlock = kDzThreads * kDzPer;
+
+__global__ void __launch_bounds__(kDzThreads)
 bwd_dz_kernel(const float* __restrict__ z, const float* __restrict__ rowsum, const float* __restrict__ colsum,
-              float* __restrict__ dz, int T) {
-    // one workgroup per head: each thread sums a run of tokens in fp64, a parallel
-    // exclusive scan over the runs in LDS, then each thread writes its run
-    __shared__ double s_tot[1024];
-    const int bh = blockIdx.x, tid = threadIdx.x;
+              float* __restrict__ dz, int T, int nblk) {
+    __shared__ double s_pre[kDzThreads], s_run[kDzThreads];
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk, tid = threadIdx.x;
     const size_t base = (size_t)bh * T;
-    const int run = (T + 1023) / 1024;
-    const int t0 = min(T, tid * run), t1 = min(T, t0 + run);
-    double acc = 0.0;
-    for (int t = t0; t < t1; ++t) acc += (double)colsum[base + t] - (double)rowsum[base + t];
-    s_tot[tid] = acc;
+    const int b0 = blk * kDzBlock;
+    double pre = 0.0;   // this thread's share of the tokens before the block
+#pragma unroll 4
+    for (int t = tid; t < b0; t += kDzThreads) pre += (double)colsum[base + t] - (double)rowsum[base + t];
+    const int t0 = b0 + kDzPer * tid;
+    double x[kDzPer], run = 0.0;
+#pragma unroll
+    for (int i = 0; i < kDzPer; ++i) {
+        const int t = t0 + i;
+        x[i] = t < T ? (double)colsum[base + t] - (double)rowsum[base + t] : 0.0;
+        run += x[i];
+    }
+    s_pre[tid] = pre;
+    s_run[tid] = run;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const double x = tid >= off ? s_tot[tid - off] : 0.0;
-        __syncthreads();
-        s_tot[tid] += x;
+    // total of the earlier tokens (tree, fixed order) and the inclusive scan of the
+    // threads' runs (Hillis-Steele)
+    for (int off = kDzThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) s_pre[tid] += s_pre[tid + off];
         __syncthreads();
     }
-    double c = s_tot[tid] - acc;   // sum over the earlier runs
-    for (int t = t0; t < t1; ++t) {
-        dz[base + t] = -sigmoid_f(z[base + t]) * (float)c;
-        c += (double)colsum[base + t] - (double)rowsum[base + t];
+    for (int off = 1; off < kDzThreads; off <<= 1) {
+        const double y = tid >= off ? s_run[tid - off] : 0.0;
+        __syncthreads();
+        s_run[tid] += y;
+        __syncthreads();
+    }
+    double c = s_pre[0] + (s_run[tid] - run);   // sum over every token before t0
+#pragma unroll
+    for (int i = 0; i < kDzPer; ++i) {
+        const int t = t0 + i;
+        if (t < T) dz[base + t] = -sigmoid_f(z[base + t]) * (float)c;
+        c += x[i];
     }
 }
 
@@ -376,8 +398,13 @@ int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s, bool with_d) {
 
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s) {
     ktimer_begin(a.timer, "bwd_dz", a.stream);
-    hipLaunchKernelGGL(bwd_dz_kernel, dim3(a.B * a.H), dim3(1024), 0, (hipStream_t)a.stream, a.z, s.rowsum,
-                       s.colsum, a.gz, a.T);
+    const int nblk = (a.T + kDzBlock - 1) / kDzBlock;
+    if ((size_t)a.B * a.H * nblk == 0) {
+        ktimer_end(a.timer, a.stream);
+        return TWOMAMBA_OK;
+    }
+    hipLaunchKernelGGL(bwd_dz_kernel, dim3((unsigned)(a.B * a.H * nblk)), dim3(kDzThreads), 0, (hipStream_t)a.stream,
+                       a.z, s.rowsum, s.colsum, a.gz, a.T, nblk);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

@@ -55,7 +55,7 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float* o) {
 __device__ __forceinline__ uint4 f32x8_to_bf16(const float* x) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = bf16x2_rne(x[2 * i], x[2 * i + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 

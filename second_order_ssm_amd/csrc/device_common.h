@@ -21,14 +21,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// two fp32 -> two bf16 in one v_cvt_pk_bf16_f32: round to nearest even, the same
+// bits as f32_to_bf16 for every non-NaN input
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+    const f2v f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2v));
+}
+
 template <typename T> struct IO;
 template <> struct IO<float> {
     static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
     static __device__ __forceinline__ void st(float* p, size_t i, float x) { p[i] = x; }
+    static __device__ __forceinline__ float rnd(float x) { return x; }   // x in this dtype's precision
 };
 template <> struct IO<bf16> {
     static __device__ __forceinline__ float ld(const bf16* p, size_t i) { return bf16_to_f32(p[i].bits); }
     static __device__ __forceinline__ void st(bf16* p, size_t i, float x) { p[i].bits = f32_to_bf16(x); }
+    static __device__ __forceinline__ float rnd(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 };
 
 // log decay g = -softplus(z) with softplus(x) = max(x,0) + log1p(exp(-|x|));

@@ -335,17 +335,22 @@ __device__ __forceinline__ Conv8 conv_lds_get(const ConvLds& c, int tensor, int 
     return r;
 }
 
-// rows t0 - 1 .. t0 + 62 of a head's tensor in the Stage layout (the row before each
-// staged row); `prev` covers the cached raw row of token -1 (an empty resource =
-// zeros).  Both loads are issued for every row, one of them past its resource.
+// The raw row before each staged row (rows t0 - 1 .. t0 + 62), for the convolution.
+// Lane l of a wave stages row 8w' + (l >> 3) (w' = the wave's row group), so the row
+// before it sits in lane l - 8 of the same wave for all but the first 8 lanes: only
+// those load one here, from the head (row t0 + r - 1), or, for the first rows of the
+// sequence, from `prev`, the cached raw row of token -1 (an empty resource = zeros);
+// conv_stage takes the others from their neighbours.
 __device__ __forceinline__ void fetch_before(Stage& s, __amdgpu_buffer_rsrc_t head, __amdgpu_buffer_rsrc_t prev,
                                              int t0, int tid) {
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool edge = ((tid & 63) >> 3) == 0;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        const int e = tid + n * kThreads, r = e >> 3, c = e & 7, t = t0 + r - 1;
-        const uint4 a = buf_ld16(head, (uint32_t)(t * kD + 8 * c) * 2);
-        const uint4 b = buf_ld16(prev, t < 0 ? (uint32_t)(8 * c) * 2 : kNoAccess);
-        s.c[n] = make_uint4(a.x | b.x, a.y | b.y, a.z | b.z, a.w | b.w);
+        const int e = tid + n * kThreads, r = e >> 3, c = e & 7;
+        const bool from_prev = t0 == 0 && n == 0 && w == 0;   // row -1 (uniform per wave)
+        const uint32_t off = !edge ? kNoAccess : from_prev ? (uint32_t)(8 * c) * 2 : (uint32_t)((t0 + r - 1) * kD + 8 * c) * 2;
+        s.c[n] = buf_ld16(from_prev ? prev : head, off);
     }
 }
 
@@ -353,10 +358,17 @@ __device__ __forceinline__ void fetch_before(Stage& s, __amdgpu_buffer_rsrc_t he
 __device__ __forceinline__ void conv_stage(Stage& s, const Stage& before, const ConvLds& c, int tensor, int rows,
                                            int tid) {
     const Conv8 w = conv_lds_get(c, tensor, 8 * (tid & 7));   // a thread's channel group is the same for n = 0, 1
+    const int lane = tid & 63, src = (lane - 8) & 63;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int r = (tid + n * kThreads) >> 3;
-        s.c[n] = r < rows ? conv8_bf16(w, s.c[n], before.c[n]) : make_uint4(0u, 0u, 0u, 0u);
+        uint4 b;   // the raw row r - 1: the neighbour's staged row, or the one fetched for the first 8 lanes
+        b.x = __shfl(s.c[n].x, src);
+        b.y = __shfl(s.c[n].y, src);
+        b.z = __shfl(s.c[n].z, src);
+        b.w = __shfl(s.c[n].w, src);
+        if (lane < 8) b = before.c[n];
+        s.c[n] = r < rows ? conv8_bf16(w, s.c[n], b) : make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
@@ -454,8 +466,10 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
 }
 
 // one segment of one head: carried state in accumulators (wave w: value rows
-// 16w..16w+15 of S^T), per chunk intra-chunk scores + readout + update.  kStrict:
-// every token sees only strictly earlier ones (the diagonal term is left out).
+// 16w..16w+15 of S^T), per chunk intra-chunk scores + readout + update.  kStrict
+// (the backward's passes): the sums run over strictly earlier tokens, the optional
+// dot with xdot is taken over that strict output, and the diagonal term
+// scale (q_t.k_t) v_t is added to the stored output only afterwards.
 template <bool kConv, bool kRev, bool kStrict>
 __global__ void __launch_bounds__(kThreads)
 lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -609,13 +623,36 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             // buffers (negative ones wrap past them), so their stores are dropped
             const int hrow = stored_row(t0 + tl, T, kRev);
             poff = (uint32_t)(hrow * kD + 4 * g) * 2;
+            // strict passes: the diagonal term scale (q_t.k_t) v_t joins the output after the
+            // dot has been taken (q.k over the token's 64 dims: 16 per lane group)
+            float diag = 0.f;
+            if (kStrict) {
+                float fq[16], fk[16];
+                bf16x8_to_f32(*reinterpret_cast<const uint4*>(&sQ.X[tl][16 * g]), fq);
+                bf16x8_to_f32(*reinterpret_cast<const uint4*>(&sQ.X[tl][16 * g + 8]), fq + 8);
+                bf16x8_to_f32(*reinterpret_cast<const uint4*>(&sK.X[tl][16 * g]), fk);
+                bf16x8_to_f32(*reinterpret_cast<const uint4*>(&sK.X[tl][16 * g + 8]), fk + 8);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) diag = fmaf(fq[i], fk[i], diag);
+                diag += __shfl_xor(diag, 16);
+                diag += __shfl_xor(diag, 32);
+                diag *= scale;
+            }
             float dot = 0.f;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 float y[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = fmaf(dec, OI[ct][i], O[ct][i]);
-                po[ct] = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
+                if (kStrict) {
+                    const uint2 vv = *reinterpret_cast<const uint2*>(&sV.X[tl][16 * ct + 4 * g]);
+                    const float fv[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+                    po[ct] = make_uint2(pack2(fmaf(diag, fv[0], y[0]), fmaf(diag, fv[1], y[1])),
+                                        pack2(fmaf(diag, fv[2], y[2]), fmaf(diag, fv[3], y[3])));
+                } else {
+                    po[ct] = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
+                }
                 if (dots) {
                     const uint2 xv = xc[ct];
                     dot = fmaf(__uint_as_float(xv.x << 16), y[0], dot);
@@ -696,60 +733,6 @@ int run_fused(const FwdArgs& a, const bf16* xdot = nullptr, float* dot_out = nul
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }
 
-// The gradients from the strictly causal passes (dq^S, dk^S, dv^S in the output
-// buffers) finished in place with their diagonal terms:
-//     dq_t = dq^S_t + a_t k_t,  dk_t = dk^S_t + a_t q_t,  dv_t = dv^S_t + c_t dout_t,
-//     a_t = scale dout_t.v_t,   c_t = scale q_t.k_t.
-// The strict row and column sums of dL/dlambda that dz needs (2Mamba2Furious,
-// App. C.1), rowsum_t = q_t . dq^S_t = sum_{s<t} dL/dlambda_ts and colsum_t =
-// k_t . dk^S_t = sum_{t'>t} dL/dlambda_t't, come from the passes in fp32: formed
-// from outputs that never held the diagonal, and before their rounding, since dz
-// is their running difference over the whole sequence.  One thread per token.
-__global__ void __launch_bounds__(256)
-lin_bwd_finish_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-                      const bf16* __restrict__ dout, bf16* __restrict__ gq, bf16* __restrict__ gk,
-                      bf16* __restrict__ gv, float scale, size_t n) {
-    // eight consecutive lanes per token, each with 8 of its 64 channels (16-byte accesses)
-    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t t = e >> 3;
-    const bool live = t < n;
-    const size_t o = t * kD + 8 * (e & 7);
-    float xq[8], xk[8], xv[8], xd[8];
-    float a = 0.f, c = 0.f;
-    if (live) {
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(q + o), xq);
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(k + o), xk);
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(v + o), xv);
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(dout + o), xd);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            a = fmaf(xd[i], xv[i], a);
-            c = fmaf(xq[i], xk[i], c);
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {   // sums over the token's eight lanes
-        a += __shfl_xor(a, m);
-        c += __shfl_xor(c, m);
-    }
-    if (!live) return;
-    a *= scale;
-    c *= scale;
-    float s8[8], y[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(gq + o), s8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = fmaf(a, xk[i], s8[i]);
-    *reinterpret_cast<uint4*>(gq + o) = f32x8_to_bf16(y);
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(gk + o), s8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = fmaf(a, xq[i], s8[i]);
-    *reinterpret_cast<uint4*>(gk + o) = f32x8_to_bf16(y);
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(gv + o), s8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = fmaf(c, xd[i], s8[i]);
-    *reinterpret_cast<uint4*>(gv + o) = f32x8_to_bf16(y);
-}
-
 FwdArgs lin_bwd_fwd_args(const BwdArgs& a) {
     FwdArgs f;
     memset(&f, 0, sizeof(f));
@@ -768,9 +751,15 @@ FwdArgs lin_bwd_fwd_args(const BwdArgs& a) {
 //     dk_s = sum_{t>=s} L_ts scale (v_s.dout_t) q_t      the same in reverse time: queries v,
 //     dv_s = sum_{t>=s} L_ts scale (k_s.q_t) dout_t      keys dout, values q / queries k, keys q,
 //                                                       values dout
-// run by the segmented chunk kernels of the forward (the last two back to front)
-// with a strictly causal mask, then finished with the diagonal terms; dL/dg comes
-// from the strict row and column sums of dL/dlambda (2Mamba2Furious, App. C, C.1).
+// run by the segmented chunk kernels of the forward (the last two back to front).
+// dL/dg comes from the strict row and column sums of dL/dlambda (2Mamba2Furious,
+// App. C, C.1): rowsum_t = q_t . dq^S_t = sum_{s<t} dL/dlambda_ts and colsum_s =
+// k_s . dk^S_s = sum_{t>s} dL/dlambda_ts, with dq^S, dk^S the strictly causal parts.
+// The passes therefore run with the strict mask, take these dots in fp32 before
+// anything is rounded (dz is their running difference over the whole sequence),
+// and only then add the diagonal term, scale (q.k) v of their own operands:
+// a_t k_t to dq, a_t q_t to dk, c_t dout_t to dv (a_t = scale dout_t.v_t,
+// c_t = scale q_t.k_t).
 bool lin_bwd_chunked_supported(const BwdArgs& a) {
     return a.variant == TWOMAMBA_LIN && a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 &&
            lin_rows_addressable(a.T) && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
@@ -787,7 +776,6 @@ int lin_bwd_chunked(const BwdArgs& a) {
     if (n == 0) return TWOMAMBA_OK;
     FwdArgs f = lin_bwd_fwd_args(a);
     int r;
-    // strictly causal passes: the diagonal terms are added by the finishing kernel
     BwdScratch sc;
     memset(&sc, 0, sizeof(sc));
     char* p = (char*)a.ws + align256(lin_layout(f).total);
@@ -800,13 +788,6 @@ int lin_bwd_chunked(const BwdArgs& a) {
     if ((r = run_fused<true, true>(f, (const bf16*)a.k, sc.colsum)) != TWOMAMBA_OK) return r;
     f.q = a.k; f.k = a.q; f.v = a.dout; f.out = a.gv;
     if ((r = run_fused<true, true>(f)) != TWOMAMBA_OK) return r;
-    ktimer_begin(a.timer, "lin_bwd_finish", a.stream);
-    hipLaunchKernelGGL(lin_bwd_finish_kernel, dim3((unsigned)((8 * n + 255) / 256)), dim3(256), 0,
-                       (hipStream_t)a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, (bf16*)a.gq,
-                       (bf16*)a.gk, (bf16*)a.gv, a.scale, n);
-    ktimer_end(a.timer, a.stream);
-    if (hipGetLastError() != hipSuccess) return TWOMAMBA_ERR_DEVICE;
     return bwd_dz_launch(a, sc);
 }
 

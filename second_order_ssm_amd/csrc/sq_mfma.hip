@@ -189,9 +189,7 @@ __device__ __forceinline__ void unpack8(const uint4 u, float* o) {
     }
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return bf16x2_rne(a, b); }
 
 // log2(2^a + 2^b) for a or b possibly -inf
 __device__ __forceinline__ float log2_add(float a, float b) {

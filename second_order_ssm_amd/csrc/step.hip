@@ -74,7 +74,8 @@ step_kernel(const In* __restrict__ q, const In* __restrict__ k, const In* __rest
             In* cs = cst + (hoff * 3 + which) * DK;
             const float before = IO<In>::ld(cs, c);
             IO<In>::st(cs, c, x);
-            x = fmaf(cw[2 * wi + 1], x, cw[2 * wi] * before) + (cb ? cb[wi] : 0.f);
+            // as the forward's convolution, which also hands its output over in the input dtype
+            x = IO<In>::rnd(fmaf(cw[2 * wi + 1], x, fmaf(cw[2 * wi], before, cb ? cb[wi] : 0.f)));
         }
         if (which == 0) s_q[c] = x * scale;
         else if (which == 1) s_k[c] = x;
@@ -210,7 +211,8 @@ step_first_order64_kernel(const In* __restrict__ q, const In* __restrict__ k, co
                 In* cs = cst + ((size_t)bh * 3 + which) * D;
                 const float before = IO<In>::ld(cs, lane);
                 IO<In>::st(cs, lane, x);
-                x = fmaf(cw[2 * wi + 1], x, cw[2 * wi] * before) + (cb ? cb[wi] : 0.f);
+                // as the forward's convolution, which also hands its output over in the input dtype
+                x = IO<In>::rnd(fmaf(cw[2 * wi + 1], x, fmaf(cw[2 * wi], before, cb ? cb[wi] : 0.f)));
             }
             s_in[w][which][lane] = which == 0 ? x * scale : x;
         }
