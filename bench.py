@@ -109,7 +109,8 @@ KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "st
                   "exp_decode_partial": "exp_step.hip", "exp_decode_combine": "exp_step.hip",
                   "bwd_q": "bwd_mfma.hip", "bwd_kv": "bwd_mfma.hip", "exp_bwd_q": "bwd_mfma.hip",
                   "exp_bwd_kv": "bwd_mfma.hip", "conv2_kernel": "conv.hip", "lin_seg": "lin.hip",
-                  "lin_scan": "lin.hip", "lin_main": "lin.hip", "step_first_order64_kernel": "step.hip"}
+                  "lin_scan": "lin.hip", "lin_main": "lin.hip", "step_first_order64_kernel": "step.hip",
+                  "sq_segstate": "sq_mfma.hip", "bwd_prep": "bwd_ref.hip", "bwd_dz": "bwd_ref.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
