@@ -440,3 +440,21 @@ def test_fwd_conv_validation_and_workspace(lib):
         tensor = (2 * 3 * 1000 * 64 * 2 + 255) // 256 * 256
         base = (plain + 255) // 256 * 256 if extra else plain
         assert n.value == base + extra * tensor, (variant, n.value, plain)
+
+
+@pytest.mark.parametrize("variant,fused", [(1, 2), (2, 0)])   # 2Mamba-E convolves k, v up front; first order none
+def test_mfma_paths_stop_at_32bit_head_offsets(lib, variant, fused):
+    # The 2Mamba-E and first-order MFMA kernels address a head's rows through 32-bit
+    # buffer offsets; from 2^24 tokens per head (2^31 bytes at d = 64, bf16) the
+    # forward takes the reference kernels instead of wrapping.  The convolution's
+    # workspace shows which path a shape gets: the reference path convolves all
+    # three tensors up front, the MFMA paths fewer.
+    n = ctypes.c_size_t(0)
+    for T, expect in (((1 << 24) - 1, fused), (1 << 24, 3)):
+        dd = desc(B=1, H=1, T=T, variant=variant)
+        assert lib.twomamba_fwd_conv_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == OK
+        s, plain = ws_size(lib, dd)
+        assert s == OK
+        tensor = (T * 64 * 2 + 255) // 256 * 256
+        base = (plain + 255) // 256 * 256 if expect else plain
+        assert n.value == base + expect * tensor, (variant, T, n.value, plain)

@@ -126,6 +126,20 @@ def test_decode_writes_stay_in_bounds(dtype):
                       z[:, :, t].contiguous(), wc, None, cs.t, S.t, n.t, out=o2.t)
         torch.cuda.synchronize()
         assert o.intact() and o2.intact() and S.intact() and n.intact() and cs.intact()
+    # first-order decode (B*H = 6: the second workgroup of four heads has two without a head)
+    S1 = Guarded((B, H, d, d), torch.float32)
+    S1.t.zero_()
+    cs1 = Guarded((B, H, 3, d), td)
+    cs1.t.zero_()
+    for t in range(T0, T0 + 3):
+        o = Guarded((B, H, d), td)
+        tmb.step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(), z[:, :, t].contiguous(),
+                 S1.t, None, first_order=True, out=o.t)
+        o2 = Guarded((B, H, d), td)
+        tmb.step_conv(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                      z[:, :, t].contiguous(), wc, None, cs1.t, S1.t, None, first_order=True, out=o2.t)
+        torch.cuda.synchronize()
+        assert o.intact() and o2.intact() and S1.intact() and cs1.intact()
     # 2Mamba-E decode: cache rows past the newest position keep their pattern
     L = T0 + 8
     kc, vc, gc = Guarded((B, H, L, d), td), Guarded((B, H, L, d), td), Guarded((B, H, L), torch.float64)

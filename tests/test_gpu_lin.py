@@ -66,11 +66,13 @@ def test_lin_full_size_every_row():
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
-@pytest.mark.parametrize("dtype,conv", [("f32", False), ("bf16", False), ("f32", True)])
-def test_lin_prompt_then_steps(dtype, conv):
-    B, H, d, T0, N = 2, 2, 64, 130, 20
+# B*H not a multiple of 4 leaves dead waves in the last workgroup of the d = 64 step
+@pytest.mark.parametrize("dtype,conv,B,H", [("f32", False, 2, 2), ("bf16", False, 1, 3), ("f32", True, 2, 2),
+                                            ("f32", True, 1, 5), ("bf16", True, 2, 3)])
+def test_lin_prompt_then_steps(dtype, conv, B, H):
+    d, T0, N = 64, 130, 20
     T = T0 + N
-    announce(f"lin prompt T0={T0} + {N} first-order steps {dtype} conv={conv}")
+    announce(f"lin prompt T0={T0} + {N} first-order steps {dtype} conv={conv} B={B} H={H}")
     q, k, v, z = SI.draw(B, H, T, d, seed=43, dtype=dtype, z_mean=-3.0)
     qd, kd, vd, zd = dev(q, k, v, z)
     qq, kk, vv, zz = (SI.to_f64(t) for t in (q, k, v, z))
