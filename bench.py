@@ -264,8 +264,8 @@ def lin_bwd_bytes_per_head_token(d=64, dv=64, esize=2):
 
 def leg_lin_bwd(steps, warmup):
     """First-order backward in O(T) (three segmented chunk passes, two in reverse
-    time, and a finishing pass) at the forward's workload and at the long-context
-    one (B=1 H=16 T=32768).  Its arithmetic is small (about 12 d dv FLOP per
+    time, and the dz scan) at the forward's workload and at the long-context one
+    (B=1 H=16 T=32768), beside the attention (quadratic) form of the same backward.  Its arithmetic is small (about 12 d dv FLOP per
     head-token in the state contractions), so the roofline is HBM, over the
     algorithmic bytes of the backward (inputs read and gradients written once)."""
     import numpy as np
@@ -286,6 +286,12 @@ def leg_lin_bwd(steps, warmup):
         ws = torch.empty(tmb.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
         fn = lambda: tmb.bwd(q, k, v, z, out, dout, variant="lin", grads=grads, workspace=ws)
         ms = time_loop(fn, steps, warmup)
+        # the attention (quadratic) form of the same backward, for comparison
+        desc_a = tmb.make_desc(B, H, T, d, d, variant="lin", dtype=torch.bfloat16, flags=tmb.FLAG_ATTENTION_FORM)
+        ws_a = torch.empty(tmb.bwd_workspace_size(desc_a), dtype=torch.uint8, device="cuda")
+        fn_a = lambda: tmb.bwd(q, k, v, z, out, dout, variant="lin", attention_form=True, grads=grads, workspace=ws_a)
+        ms_att = time_loop(fn_a, max(3, steps // 5), 1)
+        del ws_a
         byts = B * H * T * lin_bwd_bytes_per_head_token(d, d)
         bw = byts / (ms * 1e-3)
         kt = []
@@ -294,7 +300,8 @@ def leg_lin_bwd(steps, warmup):
         for n, x in kt:
             per[n] = per.get(n, 0.0) + x
         res[f"{B}x{H}x{T}"] = dict(ms=ms, head_tokens_per_s=B * H * T / (ms * 1e-3), bytes_per_call=byts,
-                                   kernels_ms=per, GBps=bw / 1e9, frac_hbm=bw / PEAK_HBM)
+                                   kernels_ms=per, GBps=bw / 1e9, frac_hbm=bw / PEAK_HBM,
+                                   attention_form_ms=ms_att, speedup_over_attention_form=ms_att / ms)
         del q, k, v, z, dout, out, grads, ws
         torch.cuda.empty_cache()
     head = res[f"{SQ_SHAPE['B']}x{SQ_SHAPE['H']}x{SQ_SHAPE['T']}"]

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define TWOMAMBA_ABI_VERSION 3
+#define TWOMAMBA_ABI_VERSION 4
 
 typedef enum {
     TWOMAMBA_OK = 0,
@@ -92,7 +92,13 @@ enum {
     /* twomamba_step / twomamba_step_conv: the first-order (TWOMAMBA_LIN) step,
        S <- e^g S + k v^T, o = scale q.S, on a [B][H][dk][dv] state; norm must
        be NULL. */
-    TWOMAMBA_FLAG_FIRST_ORDER = 4u
+    TWOMAMBA_FLAG_FIRST_ORDER = 4u,
+    /* twomamba_bwd / twomamba_bwd_workspace_size with TWOMAMBA_LIN: the
+       attention (quadratic in T) form of the backward instead of the linear-in-T
+       chunked form, for comparison; the same gradients within bf16 rounding.
+       Ignored by the forward and by the other variants, whose backward is
+       always the attention form. */
+    TWOMAMBA_FLAG_ATTENTION_FORM = 8u
 };
 
 typedef struct {

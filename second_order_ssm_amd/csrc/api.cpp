@@ -47,7 +47,8 @@ int check_desc(const twomamba_fwd_desc* d, size_t* qk_bytes, size_t* v_bytes, si
     if (d->variant != TWOMAMBA_SQ && d->variant != TWOMAMBA_EXP && d->variant != TWOMAMBA_LIN)
         return TWOMAMBA_ERR_DTYPE;
     if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
-    if (d->flags & ~(unsigned)(TWOMAMBA_FLAG_NO_NORM | TWOMAMBA_FLAG_REFERENCE_KERNELS)) return TWOMAMBA_ERR_UNSUPPORTED;
+    if (d->flags & ~(unsigned)(TWOMAMBA_FLAG_NO_NORM | TWOMAMBA_FLAG_REFERENCE_KERNELS | TWOMAMBA_FLAG_ATTENTION_FORM))
+        return TWOMAMBA_ERR_UNSUPPORTED;
     if (d->variant == TWOMAMBA_EXP && (d->flags & TWOMAMBA_FLAG_NO_NORM)) return TWOMAMBA_ERR_UNSUPPORTED;
     if (!supported_dims(d->dk, d->dv)) return TWOMAMBA_ERR_UNSUPPORTED;
     if (!(d->scale == d->scale) || d->scale == __builtin_inff() || d->scale == -__builtin_inff())

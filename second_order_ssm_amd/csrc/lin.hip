@@ -762,7 +762,8 @@ FwdArgs lin_bwd_fwd_args(const BwdArgs& a) {
 // c_t = scale q_t.k_t).
 bool lin_bwd_chunked_supported(const BwdArgs& a) {
     return a.variant == TWOMAMBA_LIN && a.dtype == TWOMAMBA_BF16 && a.dk == 64 && a.dv == 64 &&
-           lin_rows_addressable(a.T) && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
+           lin_rows_addressable(a.T) &&
+           !(a.flags & (TWOMAMBA_FLAG_REFERENCE_KERNELS | TWOMAMBA_FLAG_ATTENTION_FORM));
 }
 
 size_t lin_bwd_chunked_workspace(const BwdArgs& a) {

@@ -43,7 +43,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.twomamba_abi_version() == 3
+    assert lib.twomamba_abi_version() == 4
     seen = set()
     for s in range(9):
         txt = lib.twomamba_status_str(s).decode()
@@ -246,6 +246,19 @@ def test_bwd_workspace_size(lib):
     n = 2 * 3 * 100
     assert bwd_ws(lib, desc(B=2, H=3, T=100)) == (OK, a256(8 * n) + 4 * a256(4 * n))
     assert bwd_ws(lib, desc(B=0)) == (OK, 0)
+
+
+def test_attention_form_flag_selects_the_quadratic_first_order_backward(lib):
+    # TWOMAMBA_FLAG_ATTENTION_FORM (8): the first order's backward takes the attention
+    # form, whose workspace is the per-token rows above; without it the O(T) form
+    # (segment slots plus two fp32 rows).  Other variants ignore it; unknown bits fail.
+    a256 = lambda x: (x + 255) // 256 * 256
+    n = 2 * 3 * 1000
+    s, chunked = bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2))
+    assert s == OK and chunked != a256(8 * n) + 4 * a256(4 * n)
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2, flags=8)) == (OK, a256(8 * n) + 4 * a256(4 * n))
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=0, flags=8)) == bwd_ws(lib, desc(B=2, H=3, T=1000, variant=0))
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2, flags=16))[0] == EUNSUP
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -163,7 +163,7 @@ def test_lin_bwd_linear_in_T_full_size(B, H, T, heads):
 
 @pytest.mark.parametrize("T", [1, 64, 65, 700])
 def test_lin_bwd_linear_form_matches_attention_form(T):
-    # the same gradients from the O(T) path and from the quadratic reference kernels
+    # the same gradients from the O(T) path, the quadratic reference kernels and the quadratic MFMA kernels
     announce(f"first-order bwd: chunked vs reference kernels T={T}")
     q, k, v, z = SI.draw(2, 3, T, 64, seed=60 + T, dtype="bf16", z_mean=-6.0)
     do = _dout(2, 3, T, 64, "bf16", 61)
@@ -171,8 +171,9 @@ def test_lin_bwd_linear_form_matches_attention_form(T):
     out = tmb.fwd(qd, kd, vd, zd, variant="lin")
     a = tmb.bwd(qd, kd, vd, zd, out, dod, variant="lin")
     b = tmb.bwd(qd, kd, vd, zd, out, dod, variant="lin", reference_kernels=True)
+    c = tmb.bwd(qd, kd, vd, zd, out, dod, variant="lin", attention_form=True)   # the MFMA attention form
     torch.cuda.synchronize()
-    for nm, x, y in zip(("dq", "dk", "dv", "dz"), a, b):
-        e = relerr(host64(x), host64(y))
-        print(f"  {nm} {e:.2e}")
-        assert e < TOL["bf16"], nm
+    for nm, x, y, w in zip(("dq", "dk", "dv", "dz"), a, b, c):
+        e, e2 = relerr(host64(x), host64(y)), relerr(host64(w), host64(y))
+        print(f"  {nm} {e:.2e} (attention form {e2:.2e})")
+        assert e < TOL["bf16"] and e2 < TOL["bf16"], nm
