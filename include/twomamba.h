@@ -190,7 +190,7 @@ int twomamba_fwd_timed(const twomamba_fwd_desc* desc,
  * overlap on one GPU (other streams, other host threads) race on it and must
  * be serialised by the caller.
  */
-#define TWOMAMBA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define TWOMAMBA_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 int twomamba_fwd_noalloc(const twomamba_fwd_desc* desc,
                          const void* q, const void* k, const void* v, const float* z,

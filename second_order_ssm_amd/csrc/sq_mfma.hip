@@ -198,6 +198,21 @@ __device__ __forceinline__ float log2_add(float a, float b) {
     return m + flog2(fexp2(a - m) + fexp2(b - m));
 }
 
+// Number of end-state boundaries in (0, x]: the segment boundaries k seg_chunks
+// (1 <= k <= nseg - 1, the last one ending the segment pass) and the piece
+// boundaries p piece_chunks (1 <= p < pieces) that are not segment boundaries.
+// For the chunk x where a virtual segment starts this is its index among the
+// head's end states; for the start of segment s, the number of end states
+// before it.
+__host__ __device__ inline int vseg_index(int x, int seg_chunks, int nseg, int piece_chunks, int pieces) {
+    if (x <= 0) return 0;
+    int n = x / seg_chunks;
+    n = n < nseg - 1 ? n : nseg - 1;
+    for (int p = 1; p < pieces && p * piece_chunks <= x; ++p)
+        if ((p * piece_chunks) % seg_chunks != 0) ++n;
+    return n;
+}
+
 // Raw inputs of one chunk, one token per lane: lane t of wave w holds dims
 // 8w..8w+7 of q and k of token t, waves 0..3 also value columns 8w..8w+7 of
 // this workgroup's half, every wave the decay logit.  Tokens past T read as 0.
@@ -376,7 +391,8 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                float* __restrict__ state_out, float* __restrict__ norm_out,
                const uint2* __restrict__ ws_state, const float* __restrict__ ws_norm,
                const float* __restrict__ ws_gam, int T, int nseg, int seg_chunks, float scale, int no_norm,
-               float* __restrict__ row_stat, int scanned, const int* __restrict__ ws_exp) {
+               float* __restrict__ row_stat, int scanned, const int* __restrict__ ws_exp, int pieces,
+               int piece_chunks, int nvs) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
     const int tid = threadIdx.x;
@@ -452,13 +468,14 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     }
                 }
             } else {
-                // carry into segment seg: sum over earlier segments h of
-                // exp(Gam_{h+1} + ... + Gam_{seg-1}) * dS_h
-                const int ns1 = nseg - 1;
+                // carry into segment seg: sum over the virtual segments h before it of
+                // exp(Gam_{h+1} + ... + Gam_{nv-1}) * dS_h (nv of them end at or before its start)
+                const int ns1 = nvs;
+                const int nv = vseg_index(seg * seg_chunks, seg_chunks, nseg, piece_chunks, pieces);
                 float lw = 0.f;   // log2 weight of slot h, built from the newest one down
-                // (scanned: slot seg-1 already holds the whole carry, see sq_carry_scan)
-                const int h_end = scanned ? seg - 1 : 0;
-                for (int h = seg - 1; h >= h_end; --h) {
+                // (scanned: slot nv-1 already holds the whole carry, see sq_carry_scan)
+                const int h_end = scanned ? nv - 1 : 0;
+                for (int h = nv - 1; h >= h_end; --h) {
                     const size_t slot = (size_t)(bh * ns1 + h) * 2 + half;
                     // fp16 slot with its own power-of-two scale, in two batches of loads,
                     // each all in flight before any is used
@@ -939,11 +956,13 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 // caller state for g = 0), accumulated from the segment end backwards so that
 // every weight is relative to the segment end and no accumulator is ever
 // rescaled except when a chunk's contribution would overflow the frame.
+template <bool kPieces>   // false: one piece per segment, no boundary inside a workgroup's range
 __global__ void __launch_bounds__(kThreads, 1)
 sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ z,
                    const float* __restrict__ state_in, const float* __restrict__ norm_in,
                    uint2* __restrict__ ws_state, float* __restrict__ ws_norm, float* __restrict__ ws_gam,
-                   int* __restrict__ ws_exp, int T, int nseg, int seg_chunks) {
+                   int* __restrict__ ws_exp, int T, int nseg, int seg_chunks, int pieces, int piece_chunks,
+                   int nvs) {
     __shared__ __attribute__((aligned(16))) SmemSeg sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -962,11 +981,15 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
             half = b & 1;
         }
     }
-    const int ns1 = nseg - 1;
-    const int seg = rest % ns1;
-    const int bh = rest / ns1;
-    const int c_begin = seg * seg_chunks;
-    const int c_end = c_begin + seg_chunks;   // segments before the last are full
+    const int piece = rest % pieces;
+    const int bh = rest / pieces;
+    const int span = (nseg - 1) * seg_chunks;   // segments before the last are full
+    const int c_begin = piece * piece_chunks;
+    const int c_end = min(span, c_begin + piece_chunks);
+    // a segment boundary inside the piece (at most one, since piece_chunks <= seg_chunks)
+    // ends the later virtual segment there: -1 if there is none
+    const int c_next = (c_begin / seg_chunks + 1) * seg_chunks;
+    const int split = kPieces && c_next < c_end ? c_next : -1;
     const size_t tok_base = (size_t)bh * T;
     const int col0 = half * kDV;
 
@@ -983,6 +1006,79 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
     fetch<false>(raw, k, k, v, z, tok_base, T, (c_end - 1) * kC, tid & 63, w, col0);
     __syncthreads();
 
+    auto flush = [&](int x0, bool may_start) {
+        // true end state (diagonal tiles weighted by c) of the virtual segment that starts at
+        // chunk x0, plus the decayed caller state for the one at chunk 0 (may_start: x0 can
+        // be 0; false where it cannot, so that the compiler drops that path there)
+        const int lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+        const float f = exp2f(lf), fnn = exp2f(lfn), fin = exp2f(lP);
+        const bool add_in = may_start && x0 == 0 && state_in != nullptr;
+        float cacc[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cacc[b] = b < kg ? 0.f : (b == kg ? 1.f : 2.f);
+        const size_t wsi = (size_t)bh * nvs + vseg_index(x0, seg_chunks, nseg, piece_chunks, pieces);
+        const float* Sg = state_in ? state_in + (size_t)bh * kPairs * kD : nullptr;
+        float mx = 0.f;
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) {
+            int ib, jb;
+            tile_block(w, u, ib, jb);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f4 x = S[u][ct] * f;
+                if (add_in) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int i = 4 * ib + kg, j = 4 * jb + b;
+                        float s0 = (i <= j) ? Sg[(size_t)pidx(i, j) * kD + col0 + 16 * ct + l16] : 0.f;
+                        if (u == 0 || u == 16) s0 *= cacc[b];
+                        x[b] = fmaf(fin, s0, x[b]);
+                    }
+                }
+                S[u][ct] = x;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(x[b]));
+            }
+        }
+        // fp16 slot: values scaled by 2^e so that the largest stays below 2^14 (the
+        // precision the readout's fp16 state operand has anyway); half the bytes for
+        // the main kernel to read back
+        mx = wave_max(mx);
+        if (lane == 0) sm.red[0][w][0] = mx;
+        __syncthreads();
+        float M = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) M = fmaxf(M, sm.red[0][i][0]);
+        // an all-zero slot takes the largest exponent, so that it adds next to nothing
+        // to the bound the carry scan keeps
+        const int e = uni(M > 0.f ? max(-120, min(120, unit_exp(M) + 14)) : 120);
+        const float sc = ldexpf(1.f, e);
+        uint2* Wh = ws_state + (wsi * 2 + half) * (kStateHalf / 4) + (size_t)w * 64 * kTiles * 2;
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const f4 x = S[u][ct] * sc;
+                const h4 hv = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+                Wh[(u * 2 + ct) * 64 + lane] = __builtin_bit_cast(uint2, hv);
+            }
+        if (tid == 0) ws_exp[wsi * 2 + half] = e;
+        if (half == 0) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
+                    float val = N[x][b] * fnn;
+                    if (add_in) val = fmaf(fin, norm_in[(size_t)bh * kPairs + pidx(min(i, j), max(i, j))], val);
+                    ws_norm[wsi * kNormWG + i * kD + j] = val;
+                }
+            }
+            if (tid == 0) ws_gam[wsi] = lP / kLog2e;
+        }
+        __syncthreads();   // the reductions above reuse LDS the next chunk writes
+    };
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int t0 = c * kC;
         const int par = c & 1;
@@ -1067,76 +1163,15 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
         Mb = fs.mb_new;
         Mn = fn.mb_new;
         lP += Gam * kLog2e;
-    }
-
-    // true end state (diagonal tiles weighted by c), plus the decayed caller state
-    const int lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
-    const float f = exp2f(lf), fnn = exp2f(lfn), fin = exp2f(lP);
-    const bool add_in = seg == 0 && state_in != nullptr;
-    float cacc[4];
+        if (kPieces && c == split) {   // [split, c_end) is complete: write it, start [c_begin, split) from zero
+            flush(split, false);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) cacc[b] = b < kg ? 0.f : (b == kg ? 1.f : 2.f);
-    const size_t wsi = (size_t)(bh * ns1 + seg);
-    const float* Sg = state_in ? state_in + (size_t)bh * kPairs * kD : nullptr;
-    float mx = 0.f;
-#pragma unroll
-    for (int u = 0; u < kTiles; ++u) {
-        int ib, jb;
-        tile_block(w, u, ib, jb);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            f4 x = S[u][ct] * f;
-            if (add_in) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int i = 4 * ib + kg, j = 4 * jb + b;
-                    float s0 = (i <= j) ? Sg[(size_t)pidx(i, j) * kD + col0 + 16 * ct + l16] : 0.f;
-                    if (u == 0 || u == 16) s0 *= cacc[b];
-                    x[b] = fmaf(fin, s0, x[b]);
-                }
-            }
-            S[u][ct] = x;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(x[b]));
+            for (int u = 0; u < kTiles; ++u) S[u][0] = S[u][1] = f4{0.f, 0.f, 0.f, 0.f};
+            N[0] = N[1] = f4{0.f, 0.f, 0.f, 0.f};
+            lf = lfn = Mb = Mn = lP = 0.f;
         }
     }
-    // fp16 slot: values scaled by 2^e so that the largest stays below 2^14 (the
-    // precision the readout's fp16 state operand has anyway); half the bytes for
-    // the main kernel to read back
-    mx = wave_max(mx);
-    if (lane == 0) sm.red[0][w][0] = mx;
-    __syncthreads();
-    float M = 0.f;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, sm.red[0][i][0]);
-    // an all-zero slot takes the largest exponent, so that it adds next to nothing
-    // to the bound the carry scan keeps
-    const int e = uni(M > 0.f ? max(-120, min(120, unit_exp(M) + 14)) : 120);
-    const float sc = ldexpf(1.f, e);
-    uint2* Wh = ws_state + (wsi * 2 + half) * (kStateHalf / 4) + (size_t)w * 64 * kTiles * 2;
-#pragma unroll
-    for (int u = 0; u < kTiles; ++u)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const f4 x = S[u][ct] * sc;
-            const h4 hv = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-            Wh[(u * 2 + ct) * 64 + lane] = __builtin_bit_cast(uint2, hv);
-        }
-    if (tid == 0) ws_exp[wsi * 2 + half] = e;
-    if (half == 0) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int nt = 2 * w + x, nib = nt >> 2, njb = nt & 3;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int i = 16 * nib + 4 * kg + b, j = 16 * njb + l16;
-                float val = N[x][b] * fnn;
-                if (add_in) val = fmaf(fin, norm_in[(size_t)bh * kPairs + pidx(min(i, j), max(i, j))], val);
-                ws_norm[wsi * kNormWG + i * kD + j] = val;
-            }
-        }
-        if (tid == 0) ws_gam[wsi] = lP / kLog2e;
-    }
+    flush(c_begin, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -1238,8 +1273,17 @@ sq_carry_scan(uint2* __restrict__ ws_state, float* __restrict__ ws_norm, const f
 // takes the main kernel from 0.44 to 0.09 ms.
 constexpr int kScanFrom = 9;
 
+// The segment pass cuts the chunks before the last segment ((nseg - 1) seg_chunks
+// of them) into `pieces` pieces of piece_chunks, one workgroup per (head, piece,
+// value half): as many as fill the CUs, which the one-piece-per-segment split
+// leaves partly idle (at 2x16x8192, 192 workgroups on 256 CUs).  A piece that
+// crosses a segment boundary ends one end state there and starts the next, so
+// the end states ("virtual segments") are the spans between consecutive
+// boundaries of either kind; `nvs` of them per head, the carry into a segment is
+// the decayed sum of those before its start.
 struct Plan {
     int nseg, seg_chunks;
+    int pieces, piece_chunks, nvs;
 };
 
 Plan plan_for(const FwdArgs& a) {
@@ -1252,6 +1296,20 @@ Plan plan_for(const FwdArgs& a) {
     Plan p;
     p.seg_chunks = sc;
     p.nseg = (nc + sc - 1) / sc;
+    const int ns1 = p.nseg - 1, span = ns1 * sc;
+    p.pieces = ns1;
+    p.piece_chunks = sc;
+    if (ns1 > 0) {
+        // pieces to fill the CUs (at most one boundary inside a piece: piece_chunks <= seg_chunks),
+        // used when one piece per segment would leave at least a fifth of the CUs idle
+        const int fill = (int)(256 / (2 * nbh));
+        const int pc = fill > 0 ? (span + fill - 1) / fill : sc;
+        if (fill * 4 >= ns1 * 5 && pc >= 4) {   // at least 4 chunks per piece, as per segment
+            p.piece_chunks = pc;
+            p.pieces = (span + pc - 1) / pc;
+        }
+    }
+    p.nvs = ns1 > 0 ? vseg_index(span, sc, p.nseg, p.piece_chunks, p.pieces) : 0;
     return p;
 }
 
@@ -1268,7 +1326,7 @@ struct WsLayout {
 
 WsLayout ws_layout(const FwdArgs& a, const Plan& p) {
     const size_t nbh = (size_t)a.B * a.H;
-    const size_t ns1 = p.nseg > 1 ? (size_t)(p.nseg - 1) : 0;
+    const size_t ns1 = p.nseg > 1 ? (size_t)p.nvs : 0;   // end-state slots per head
     WsLayout L;
     L.off_state = 0;
     L.off_norm = align256(nbh * ns1 * 2 * kStateHalf * sizeof(_Float16));
@@ -1293,7 +1351,7 @@ int run(const FwdArgs& a) {
     int* wsE = slots ? (int*)(ws + L.off_exp) : nullptr;
     int* wsEs = slots ? (int*)(ws + L.off_exps) : nullptr;
     // carries: scanned in place for many segments, else summed by each main workgroup
-    const int scanned = p.nseg >= kScanFrom;
+    const int scanned = p.nvs + 1 >= kScanFrom;
     const int nbh = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
     const int no_norm = (a.flags & TWOMAMBA_FLAG_NO_NORM) != 0;
@@ -1319,22 +1377,28 @@ int run(const FwdArgs& a) {
     }
     if (p.nseg > 1) {
         ktimer_begin(a.timer, "sq_segstate", a.stream);
-        hipLaunchKernelGGL(sq_segstate_kernel, dim3(nbh * (p.nseg - 1) * 2), dim3(kThreads), 0, st, k, v, a.z,
-                           state_in, norm_in, wsS, wsN, wsG, wsE, a.T, p.nseg, p.seg_chunks);
+        if (p.nvs > p.nseg - 1)
+            hipLaunchKernelGGL(sq_segstate_kernel<true>, dim3(nbh * p.pieces * 2), dim3(kThreads), 0, st, k, v, a.z,
+                               state_in, norm_in, wsS, wsN, wsG, wsE, a.T, p.nseg, p.seg_chunks, p.pieces,
+                               p.piece_chunks, p.nvs);
+        else
+            hipLaunchKernelGGL(sq_segstate_kernel<false>, dim3(nbh * p.pieces * 2), dim3(kThreads), 0, st, k, v, a.z,
+                               state_in, norm_in, wsS, wsN, wsG, wsE, a.T, p.nseg, p.seg_chunks, p.pieces,
+                               p.piece_chunks, p.nvs);
         ktimer_end(a.timer, a.stream);
     }
     if (scanned) {
         const int etiles = (kScanElems + 255) / 256;
         ktimer_begin(a.timer, "sq_carry_scan", a.stream);
         hipLaunchKernelGGL(sq_carry_scan, dim3(nbh * etiles), dim3(256), 0, st, wsS, wsN, (const float*)wsG,
-                           (const int*)wsE, wsEs, p.nseg - 1, etiles);
+                           (const int*)wsE, wsEs, p.nvs, etiles);
         ktimer_end(a.timer, a.stream);
     }
     ktimer_begin(a.timer, "sq_mfma_main", a.stream);
     hipLaunchKernelGGL(sq_main_kernel, dim3(nbh * p.nseg * 2), dim3(kThreads), 0, st, q, k, v, a.z, (bf16*)a.out,
                        state_in, norm_in, a.state_out, a.norm_out, (const uint2*)wsS, (const float*)wsN,
                        (const float*)wsG, a.T, p.nseg, p.seg_chunks, a.scale, no_norm, a.row_stat, scanned,
-                       (const int*)(scanned ? wsEs : wsE));
+                       (const int*)(scanned ? wsEs : wsE), p.pieces, p.piece_chunks, p.nvs);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
 }

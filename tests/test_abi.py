@@ -404,16 +404,16 @@ def call_fwd_noalloc(lib, dsc, q=1, k=2, v=3, z=4, si=None, ni=None, out=5, so=N
 
 
 def test_fwd_noalloc_validation_before_any_hip_call(lib):
-    # the checks of twomamba_fwd, then the static scratch's limit (64 MiB), all
+    # the checks of twomamba_fwd, then the static scratch's limit (128 MiB), all
     # before the scratch lookup (the call's first HIP call): nothing here is launched
     assert call_fwd_noalloc(lib, None) == ENULL
     assert call_fwd_noalloc(lib, desc(T=100), q=None) == ENULL
     assert call_fwd_noalloc(lib, desc(T=100), out=1) == EALIAS
     assert call_fwd_noalloc(lib, desc(T=100, d=48)) == EUNSUP
-    # fp32 reference kernels keep one state per chunk: 2 heads x 64 chunks x 532 KB > 64 MiB
-    big = desc(B=1, H=2, T=4096, d=64, dtype=0)
+    # fp32 reference kernels keep one state per chunk: 2 heads x 256 chunks x 532 KB > 128 MiB
+    big = desc(B=1, H=2, T=16384, d=64, dtype=0)
     s, need = ws_size(lib, big)
-    assert s == OK and need > (64 << 20)
+    assert s == OK and need > (128 << 20)
     assert call_fwd_noalloc(lib, big) == ESCRATCH
     assert lib.twomamba_status_str(ESCRATCH).decode() == "workspace larger than the library's static scratch"
 
