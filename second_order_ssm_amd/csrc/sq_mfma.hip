@@ -51,6 +51,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bh8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bh4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -240,7 +241,6 @@ __device__ __forceinline__ void fetch(Raw& r, const bf16* q, const bf16* k, cons
 }
 
 struct Smem {
-    _Float16 Q2[kC][kLS];       // 2 q~ [t][d] (must directly precede Q)
     _Float16 Q[kC][kLS];        // q~ [t][d]
     _Float16 K[kC][kLS];        // k~ [t][d]
     _Float16 KT[kD][kLS];       // k~^T [d][t]
@@ -271,10 +271,11 @@ struct SmemSeg {
 };
 
 // ---------------------------------------------------------------------------
-// update of the 17 x 2 state tiles and the 2 normaliser tiles of this wave from
-// the chunk's K^T / (w v)^T / (w k)^T in LDS.  kZero: start from zero.
+// Update of the 17 x 2 state tiles of this wave from the chunk's K^T and (w v)^T in
+// LDS, tile by tile (kZero: start from zero).  The segment pre-pass uses this order:
+// the token-half order of update_tiles below needs more registers than it has left.
 template <bool kZero, typename SM>
-__device__ __forceinline__ void update_tiles(f4 (&S)[kTiles][2], const SM& sm, int wl, int kg, int gq, int bq4,
+__device__ __forceinline__ void update_tiles_seg(f4 (&S)[kTiles][2], const SM& sm, int wl, int kg, int gq, int bq4,
                                              _Float16 cslot, int l16) {
     const char* smb = reinterpret_cast<const char*>(&sm);
     h8 BV[2][2];
@@ -317,6 +318,62 @@ __device__ __forceinline__ void update_tiles(f4 (&S)[kTiles][2], const SM& sm, i
                 S[u][0] = mfma(A, BV[kk][0], S[u][0]);
                 S[u][1] = mfma(A, BV[kk][1], S[u][1]);
             }
+        }
+    }
+}
+
+// The same update, token half (K = 32 tokens) outer: one half's (w v) operands and
+// the row factors of the wave's two block rows are read once per half, and the two
+// products into one accumulator are 17 tiles apart.  Used by the main kernel.
+template <bool kZero, typename SM>
+__device__ __forceinline__ void update_tiles(f4 (&S)[kTiles][2], const SM& sm, int wl, int kg, int gq, int bq4,
+                                             _Float16 cslot, int l16) {
+    const char* smb = reinterpret_cast<const char*>(&sm);
+    // K^T byte addresses: per-lane bases for the two block rows, block column as immediate
+    const int kt0 = (int)offsetof(SM, KT) + 16 * kg;
+    const int aiA = kt0 + (4 * wl + gq) * kRow, ajA = kt0 + (4 * wl + bq4) * kRow;
+    const int aiB = kt0 + (60 - 4 * wl + gq) * kRow, ajB = kt0 + bq4 * kRow;
+    const int ajD = kt0 + (60 - 4 * wl + bq4) * kRow;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const h8 BV0 = *reinterpret_cast<const h8*>(&sm.WVT[l16][32 * kk + 8 * kg]);
+        const h8 BV1 = *reinterpret_cast<const h8*>(&sm.WVT[16 + l16][32 * kk + 8 * kg]);
+        // row factors of block rows wl and 15 - wl; tiles 0..8 lie in row wl for every wave
+        const h8 kiA = *reinterpret_cast<const h8*>(smb + aiA + 64 * kk);
+        const h8 kiB = *reinterpret_cast<const h8*>(smb + aiB + 64 * kk);
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) {
+            h8 ki;
+            int aj;
+            if (u == 0) {
+                ki = kiA;
+                aj = ajA;
+            } else if (u == 16) {
+                ki = kiB;
+                aj = ajD;
+            } else if (u <= 8) {
+                ki = kiA;
+                aj = ajA + u * 4 * kRow;
+            } else if (u <= 15 - wl) {
+                ki = *reinterpret_cast<const h8*>(smb + aiA + 64 * kk);
+                aj = ajA + u * 4 * kRow;
+            } else {
+                ki = *reinterpret_cast<const h8*>(smb + aiB + 64 * kk);
+                aj = ajB + u * 4 * kRow;
+            }
+            const h8 kj = *reinterpret_cast<const h8*>(smb + aj + 64 * kk);
+            h8 A = ki * kj;
+            if (u == 0 || u == 16) A *= cslot;   // c * phi(k); zero on dead slots
+            if (kZero && kk == 0) {
+                S[u][0] = mfma(A, BV0, f4{0.f, 0.f, 0.f, 0.f});
+                S[u][1] = mfma(A, BV1, f4{0.f, 0.f, 0.f, 0.f});
+            } else {
+                S[u][0] = mfma(A, BV0, S[u][0]);
+                S[u][1] = mfma(A, BV1, S[u][1]);
+            }
+            // in pairs of tiles: left free, the scheduler hoists every tile's loads
+            // and runs out of registers
+            if (u & 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -651,7 +708,7 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
             const float swk = wt * fexp2(-fn.lf_new - (float)et);             // (w k) operand, dN_acc = 2^-lfn dN
             const float swv = wt * fexp2(-fs.lf_new - 2.f * (float)et);       // (w v) operand, dS_acc = 2^-lf dS
             const float svi = ldexpf(1.f, evi);
-            h8 q8, q28, k8;
+            h8 q8, k8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float qq = qv[i] * sq, kt = kv[i] * sk;
@@ -661,8 +718,6 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                 sm.WKT[8 * wl + i][lane] = (_Float16)(kv[i] * swk);
             }
             *reinterpret_cast<h8*>(&sm.Q[lane][8 * wl]) = q8;
-            q28 = q8 + q8;   // exact doubling in fp16 (|q8| < 1)
-            *reinterpret_cast<h8*>(&sm.Q2[lane][8 * wl]) = q28;
             *reinterpret_cast<h8*>(&sm.K[lane][8 * wl]) = k8;
             if (wl < 4) {
 #pragma unroll
@@ -694,39 +749,48 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) O[tb][0] = O[tb][1] = f4{0.f, 0.f, 0.f, 0.f};
             const char* smq = reinterpret_cast<const char*>(&sm);
-            constexpr int kQ2Q = (int)(offsetof(Smem, Q) - offsetof(Smem, Q2));
+            // The query factor q_i of a tile's rows depends only on the block row: read the
+            // lane's two (dims 4 wl + kg and 4 (15 - wl) + kg, tokens 16 tb + l16) once per
+            // chunk.  Off-diagonal tiles take 2 q_i (exact in fp16).
             const int rowq = kRow * l16;
-            const int qaA = (int)offsetof(Smem, Q2) + rowq + 8 * wl + 2 * kg;
-            const int qaB = (int)offsetof(Smem, Q2) + rowq + 8 * (15 - wl) + 2 * kg;
+            const int qrA = (int)offsetof(Smem, Q) + rowq + 8 * wl + 2 * kg;
+            const int qrB = (int)offsetof(Smem, Q) + rowq + 8 * (15 - wl) + 2 * kg;
+            h2 fA[2], fB[2];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int ro = 16 * kRow * tb;
+                fA[tb >> 1][tb & 1] = *reinterpret_cast<const _Float16*>(smq + qrA + ro);
+                fB[tb >> 1][tb & 1] = *reinterpret_cast<const _Float16*>(smq + qrB + ro);
+            }
+            const h2 fA2[2] = {fA[0] + fA[0], fA[1] + fA[1]};
+            const h2 fB2[2] = {fB[0] + fB[0], fB[1] + fB[1]};
             const int qjA = (int)offsetof(Smem, Q) + rowq + 8 * wl;
             const int qjB = (int)offsetof(Smem, Q) + rowq;
             const int qjD = (int)offsetof(Smem, Q) + rowq + 8 * (15 - wl);
+            // tile u: its row factors (packed by token block pairs) and the LDS address of
+            // the four column factors q_j; tiles 1..8 lie in row wl for every wave
+            auto tile_q = [&](int u, h2 (&f)[2], int& aj) {
+                if (u == 0) {
+                    f[0] = fA[0]; f[1] = fA[1];
+                    aj = qjA;
+                } else if (u == 16) {
+                    f[0] = fB[0]; f[1] = fB[1];
+                    aj = qjD;
+                } else if (u <= 8 || u <= 15 - wl) {
+                    f[0] = fA2[0]; f[1] = fA2[1];
+                    aj = qjA + 8 * u;
+                } else {
+                    f[0] = fB2[0]; f[1] = fB2[1];
+                    aj = qjB + 8 * u;
+                }
+            };
 #pragma unroll
             for (int kp = 0; kp < 9; ++kp) {
                 const int ua = 2 * kp, ub = 2 * kp + 1;
-                int aqa, aja, aqb = 0, ajb = 0;
-                if (ua == 0) {
-                    aqa = qaA + kQ2Q;
-                    aja = qjA;
-                } else if (ua == 16) {
-                    aqa = qaB + kQ2Q;
-                    aja = qjD;
-                } else if (ua <= 15 - wl) {
-                    aqa = qaA;
-                    aja = qjA + 8 * ua;
-                } else {
-                    aqa = qaB;
-                    aja = qjB + 8 * ua;
-                }
-                if (ub < kTiles) {
-                    if (ub <= 15 - wl) {
-                        aqb = qaA;
-                        ajb = qjA + 8 * ub;
-                    } else {
-                        aqb = qaB;
-                        ajb = qjB + 8 * ub;
-                    }
-                }
+                h2 fa[2], fb[2] = {h2{0, 0}, h2{0, 0}};
+                int aja, ajb = 0;
+                tile_q(ua, fa, aja);
+                if (ub < kTiles) tile_q(ub, fb, ajb);
                 h8 B0, B1;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -736,26 +800,23 @@ sq_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
                     B1[4 + b] = (ub < kTiles) ? (_Float16)S[ub][1][b] : (_Float16)0.f;
                 }
                 // all LDS reads of this tile pair first, so one wait covers them
-                _Float16 qa[4], qb[4];
                 h4 qja[4], qjb[4];
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     const int ro = 16 * kRow * tb;
-                    qa[tb] = *reinterpret_cast<const _Float16*>(smq + aqa + ro);
                     qja[tb] = *reinterpret_cast<const h4*>(smq + aja + ro);
-                    if (ub < kTiles) {
-                        qb[tb] = *reinterpret_cast<const _Float16*>(smq + aqb + ro);
-                        qjb[tb] = *reinterpret_cast<const h4*>(smq + ajb + ro);
-                    }
+                    if (ub < kTiles) qjb[tb] = *reinterpret_cast<const h4*>(smq + ajb + ro);
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
+                    const _Float16 qa = fa[tb >> 1][tb & 1];
                     h8 A;
-                    A[0] = qa[tb] * qja[tb][0]; A[1] = qa[tb] * qja[tb][1];
-                    A[2] = qa[tb] * qja[tb][2]; A[3] = qa[tb] * qja[tb][3];
+                    A[0] = qa * qja[tb][0]; A[1] = qa * qja[tb][1];
+                    A[2] = qa * qja[tb][2]; A[3] = qa * qja[tb][3];
                     if (ub < kTiles) {
-                        A[4] = qb[tb] * qjb[tb][0]; A[5] = qb[tb] * qjb[tb][1];
-                        A[6] = qb[tb] * qjb[tb][2]; A[7] = qb[tb] * qjb[tb][3];
+                        const _Float16 qb = fb[tb >> 1][tb & 1];
+                        A[4] = qb * qjb[tb][0]; A[5] = qb * qjb[tb][1];
+                        A[6] = qb * qjb[tb][2]; A[7] = qb * qjb[tb][3];
                     } else {
                         A[4] = A[5] = A[6] = A[7] = (_Float16)0.f;
                     }
@@ -1149,8 +1210,8 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
                     S[u][1] *= fs.ratio;
                 }
             }
-            if (fs.zero) update_tiles<true>(S, sm, wl, kg, gq, bq4, cslot, l16);
-            else update_tiles<false>(S, sm, wl, kg, gq, bq4, cslot, l16);
+            if (fs.zero) update_tiles_seg<true>(S, sm, wl, kg, gq, bq4, cslot, l16);
+            else update_tiles_seg<false>(S, sm, wl, kg, gq, bq4, cslot, l16);
             if (fn.zero) N[0] = N[1] = f4{0.f, 0.f, 0.f, 0.f};
             else if (fn.mul) {
                 N[0] *= fn.ratio;
