@@ -192,13 +192,6 @@ __device__ __forceinline__ void unpack8(const uint4 u, float* o) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return bf16x2_rne(a, b); }
 
-// log2(2^a + 2^b) for a or b possibly -inf
-__device__ __forceinline__ float log2_add(float a, float b) {
-    const float m = fmaxf(a, b);
-    if (m == -INFINITY) return -INFINITY;
-    return m + flog2(fexp2(a - m) + fexp2(b - m));
-}
-
 // Number of end-state boundaries in (0, x]: the segment boundaries k seg_chunks
 // (1 <= k <= nseg - 1, the last one ending the segment pass) and the piece
 // boundaries p piece_chunks (1 <= p < pieces) that are not segment boundaries.
@@ -407,7 +400,8 @@ __device__ __forceinline__ Frame choose_frame(float lf, float Mb, float lg, floa
     // stays within [2^10, 2^14]: large enough that the scaled operands keep fp16
     // precision, small enough that the readout's fp16 conversion cannot overflow.
     const float lf_d = lf + lg;
-    const float grow = (lc == -INFINITY) ? 0.f : fexp2(fminf(lc - lf_d, 64.f));
+    const float e = lc - lf_d;   // log2 bound of the chunk's part in the decayed frame
+    const float grow = (lc == -INFINITY) ? 0.f : fexp2(fminf(e, 64.f));
     const float mb_d = Mb + grow;
     if (mb_d <= 16384.f && mb_d >= 1024.f) {
         f.lf_new = lf_d;
@@ -417,8 +411,9 @@ __device__ __forceinline__ Frame choose_frame(float lf, float Mb, float lg, floa
         f.mb_new = mb_d;
         return f;
     }
-    const float lold = (Mb > 0.f) ? flog2(Mb) + lf + lg : -INFINITY;
-    const float lt = log2_add(lold, lc);
+    // log2 of the whole bound in true units, log2(Mb 2^lf_d + 2^lc) = log2(mb_d) + lf_d
+    // (the old part is negligible where grow was clamped)
+    const float lt = (e > 64.f) ? lc : flog2(mb_d) + lf_d;
     float ln = (lt == -INFINITY) ? lf : ceilf(lt - kTarget);
     ln = fmaxf(ln, lf + lg - 100.f);
     f.lf_new = ln;
@@ -427,15 +422,6 @@ __device__ __forceinline__ Frame choose_frame(float lf, float Mb, float lg, floa
     f.mul = !f.zero;
     const float add = (lc == -INFINITY) ? 0.f : fexp2(lc - ln);
     f.mb_new = (f.zero ? 0.f : Mb * f.ratio) + add;
-    return f;
-}
-
-__device__ __forceinline__ Frame uni_frame(Frame f) {
-    f.lf_new = uni(f.lf_new);
-    f.ratio = uni(f.ratio);
-    f.mb_new = uni(f.mb_new);
-    f.mul = uni((int)f.mul) != 0;
-    f.zero = uni((int)f.zero) != 0;
     return f;
 }
 
