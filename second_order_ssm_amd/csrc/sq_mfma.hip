@@ -33,13 +33,16 @@
 //    The chunk decay is absorbed into the frame whenever the bound allows;
 //    otherwise the accumulators are rescaled, or restarted from zero when the
 //    decayed carry is below 2^-40 of the bound (it cannot change an fp32 sum).
-//  * Long sequences are split into segments.  A first kernel computes every
-//    segment's own end state as one backward pass (a plain accumulation with
-//    weights relative to the segment end) and stores it as fp16 with one
-//    power-of-two scale per slot (2^-11 relative rounding, below that of the
-//    bf16 inputs); the main kernel starts segment g from the decayed sum of the
-//    earlier segments' end states, or, for heads with many segments, from one
-//    slot that a scan kernel has turned into the whole carry.
+//  * Long sequences are split into segments.  A first kernel computes the end
+//    states of the stretches before the last segment as backward passes (a
+//    plain accumulation with weights relative to the stretch's end), cutting
+//    them into as many pieces as fill the CUs; a piece that crosses a segment
+//    boundary ends one end state there and starts the next.  Each end state is
+//    stored as fp16 with one power-of-two scale per slot and value half (2^-11
+//    relative rounding, below that of the bf16 inputs).  The main kernel starts
+//    segment g from the decayed sum of the end states before it, or, for heads
+//    with many of them, from one slot that a scan kernel has turned into the
+//    whole carry.
 #include <algorithm>
 #include <type_traits>
 
