@@ -46,6 +46,7 @@ namespace twm {
 namespace {
 
 using namespace tiles;
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kBlk = 64;               // queries or keys per workgroup
 constexpr int kMinBlocks = 3;          // workgroups per CU the register budget is sized for
@@ -53,8 +54,10 @@ enum { kSq = 0, kExpV = 1, kLin = 2 };   // second order, exponentiated, first o
 
 // ---------------------------------------------------------------------------
 // query-major: D_t, row statistic, dq, row sums
+// The key and value tiles are double-buffered in separate shared arrays (see the
+// kernel), so that the compiler can tell a tile's reads from the transfers in flight
+// into the other buffer.
 struct QSmem {
-    Tile K[2], V[2];
     float A[2][kTile];      // log2(e) (G_s - G_ref) per key of the tile
 };
 
@@ -77,11 +80,13 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
              float* __restrict__ rowsum, bf16* __restrict__ dq, int T, int nqb, float scale, int norm, int use_d,
              int by_xcd) {
     __shared__ __attribute__((aligned(16))) QSmem sm;
+    __shared__ __attribute__((aligned(16))) Tile sK0, sK1, sV0, sV1;
     int bh, blk;
     xcd_map(blockIdx.x, nqb, by_xcd, bh, blk);
     const int qb = nqb - 1 - blk;                  // longest rows first
     const int q0 = qb * kBlk;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index as a scalar (tile transfers)
     const size_t base = (size_t)bh * T;
     const int t = q0 + 16 * w + col;               // this lane's query
     const bool tv = t < T;
@@ -112,13 +117,21 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     constexpr bool kSplit = kVar != kExpV;
     const float eb = kSplit ? fexp2(-b2) : 0.f;
 
-    auto stage_a = [&](int buf, int s0, bool split) {
+    // The key terms of a tile: raw G loaded first (before the tile's transfers, so that
+    // waiting for it does not wait for them), the terms written to LDS after the compute.
+    const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(const_cast<double*>(G + base), (short)0,
+                                                                        T * 8, 0x00020000);
+    auto load_a = [&](int s0) {
+        return __builtin_amdgcn_raw_buffer_load_b64(rG, (uint32_t)(s0 + (tid & (kTile - 1))) * 8, 0, 0);
+    };
+    auto write_a = [&](int buf, int s0, bool split, v2u raw) {
         if (tid < kTile) {
             const int s = s0 + tid;
-            const float a = s < T ? (float)(G[base + s] - gref) * kLog2e : -INFINITY;
+            const float a = s < T ? (float)(__builtin_bit_cast(double, raw) - gref) * kLog2e : -INFINITY;
             sm.A[buf][tid] = (kSplit && split) ? fexp2(a) : a;   // 2^a, or a
         }
     };
+    auto stage_a = [&](int buf, int s0, bool split) { write_a(buf, s0, split, load_a(s0)); };
     // S^T[s][t] for the key tiles st = 2h, 2h+1 of 16
     auto scores = [&](const Tile& K, int h, f4 (&S)[2]) {
 #pragma unroll
@@ -131,19 +144,19 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
     };
 
-    Stage sk, sv;
+    const __amdgpu_buffer_rsrc_t rk = head_tile_rsrc(k + base * kD, T), rv = head_tile_rsrc(v + base * kD, T);
     // ---------------------------------------------------------- sweep 1: statistic
     // (none for the first order; not needed without normalisation or when the
     // forward handed it over)
     const bool need_sweep1 = kVar != kLin && !fstat && !(kVar == kSq && !norm);
     float den = 0.f, m = -INFINITY, l = 0.f;
-    auto sweep1 = [&](int kt, auto diag_tag) {
+    auto sweep1 = [&](int kt, const Tile& K, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = kt & 1, s0 = kt * kTile;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f4 S[2];
-            scores(sm.K[cur], h, S);
+            scores(K, h, S);
             float y[8];
             float mx = -INFINITY;
 #pragma unroll
@@ -178,19 +191,26 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
     };
     if (need_sweep1) {
-        fetch(sk, k + base * kD, min(kTile, T), tid);
-        store(sk, sm.K[0], tid);
+        dma_tile(sK0, rk, 0, wu, lane);
         stage_a(0, 0, 0 < qb);
+        wait_vm();
         __syncthreads();
-        for (int kt = 0; kt < qb; ++kt) {   // key tiles wholly before the queries
+        // key tiles wholly before the queries, from Kc while the next goes into Kn
+        auto round1 = [&](int kt, const Tile& Kc, Tile& Kn) {
             const int cur = kt & 1, s0 = kt * kTile;
-            fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
-            sweep1(kt, std::false_type{});
-            store(sk, sm.K[cur ^ 1], tid);
-            stage_a(cur ^ 1, s0 + kTile, kt + 1 < qb);
+            const v2u an = load_a(s0 + kTile);
+            dma_tile(Kn, rk, s0 + kTile, wu, lane);
+            sweep1(kt, Kc, std::false_type{});
+            write_a(cur ^ 1, s0 + kTile, kt + 1 < qb, an);
+            wait_vm();
             __syncthreads();
+        };
+        for (int kt = 0; kt < qb; kt += 2) {
+            round1(kt, sK0, sK1);
+            if (kt + 1 < qb) round1(kt + 1, sK1, sK0);
         }
-        sweep1(qb, std::true_type{});
+        if (qb & 1) sweep1(qb, sK1, std::true_type{});
+        else sweep1(qb, sK0, std::true_type{});
         __syncthreads();
     }
     float st_v, cq;   // row statistic; cq: b2 + lse2 (2Mamba-E) or -D / den (2Mamba)
@@ -220,17 +240,14 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) dQ[dt] = f4{0.f, 0.f, 0.f, 0.f};
     float rs = 0.f;
-    fetch(sk, k + base * kD, min(kTile, T), tid);
-    fetch(sv, v + base * kD, min(kTile, T), tid);
-    store(sk, sm.K[0], tid);
-    store(sv, sm.V[0], tid);
+    dma_tile(sK0, rk, 0, wu, lane);
+    dma_tile(sV0, rv, 0, wu, lane);
     stage_a(0, 0, 0 < qb);
+    wait_vm();
     __syncthreads();
-    auto sweep2 = [&](int kt, auto diag_tag) {
+    auto sweep2 = [&](int kt, const Tile& K, const Tile& V, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = kt & 1, s0 = kt * kTile;
-        const Tile& K = sm.K[cur];
-        const Tile& V = sm.V[cur];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f4 S[2], P[2];
@@ -282,17 +299,23 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             for (int dt = 0; dt < 4; ++dt) dQ[dt] = mfma(tr_op(K, dt, 2 * h, lane), B, dQ[dt]);
         }
     };
-    for (int kt = 0; kt < qb; ++kt) {
+    // from (Kc, Vc) while the next tile goes into (Kn, Vn), read last round
+    auto round2 = [&](int kt, const Tile& Kc, const Tile& Vc, Tile& Kn, Tile& Vn) {
         const int cur = kt & 1, s0 = kt * kTile;
-        fetch(sk, k + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
-        fetch(sv, v + (base + s0 + kTile) * kD, min(kTile, T - s0 - kTile), tid);
-        sweep2(kt, std::false_type{});
-        store(sk, sm.K[cur ^ 1], tid);
-        store(sv, sm.V[cur ^ 1], tid);
-        stage_a(cur ^ 1, s0 + kTile, kt + 1 < qb);
+        const v2u an = load_a(s0 + kTile);
+        dma_tile(Kn, rk, s0 + kTile, wu, lane);
+        dma_tile(Vn, rv, s0 + kTile, wu, lane);
+        sweep2(kt, Kc, Vc, std::false_type{});
+        write_a(cur ^ 1, s0 + kTile, kt + 1 < qb, an);
+        wait_vm();
         __syncthreads();
+    };
+    for (int kt = 0; kt < qb; kt += 2) {
+        round2(kt, sK0, sV0, sK1, sV1);
+        if (kt + 1 < qb) round2(kt + 1, sK1, sV1, sK0, sV0);
     }
-    sweep2(qb, std::true_type{});
+    if (qb & 1) sweep2(qb, sK1, sV1, std::true_type{});
+    else sweep2(qb, sK0, sV0, std::true_type{});
     rs = xor_sum(rs);
     if (tv) {
         const float f = kVar == kSq ? 2.f * scale * scale : scale;
@@ -313,8 +336,10 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 
 // ---------------------------------------------------------------------------
 // key-major: dk, dv, column sums
+// The query and dout tiles are double-buffered in separate shared arrays (see the
+// kernel), so that the compiler can tell a tile's reads from the transfers in flight
+// into the other buffer; the per-row terms live here.
 struct KVSmem {
-    Tile Q[2], O[2];
     float B[2][kTile];      // log2(e) (G_t - G_ref) per query of the tile (+ lse2 for 2Mamba-E)
     float R[2][kTile];      // 2Mamba: 1/den_t; 2Mamba-E: unused
     float C[2][kTile];      // 2Mamba: -D_t/den_t; 2Mamba-E: D_t
@@ -327,10 +352,12 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
               const float* __restrict__ stat, float* __restrict__ colsum, bf16* __restrict__ dk,
               bf16* __restrict__ dv, int T, int nkb, float scale, int by_xcd) {
     __shared__ __attribute__((aligned(16))) KVSmem sm;
+    __shared__ __attribute__((aligned(16))) Tile sQ0, sQ1, sO0, sO1;
     int bh, kb;
     xcd_map(blockIdx.x, nkb, by_xcd, bh, kb);     // earliest keys (longest columns) first
     const int k0 = kb * kBlk;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index as a scalar (tile transfers)
     const size_t base = (size_t)bh * T;
     const int s = k0 + 16 * w + col;               // this lane's key
     const bool sv_ok = s < T;
@@ -347,14 +374,36 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     const b8 Vb[2] = {own_op(v + (base + sc) * kD, g, 0), own_op(v + (base + sc) * kD, g, 1)};
     const float sl2 = scale * kLog2e;
 
-    auto stage_rows = [&](int buf, int t0, bool split) {
+    // The query terms of a tile: raw G, statistic and D_t loaded first (before the tile's
+    // transfers, so that waiting for them does not wait for those), the terms written to
+    // LDS after the compute.  Rows past T read as zero and are marked by b.
+    const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(const_cast<double*>(G + base), (short)0,
+                                                                        T * 8, 0x00020000),
+                                 rS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(stat + base), (short)0,
+                                                                        T * 4, 0x00020000),
+                                 rD = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Dt + base), (short)0,
+                                                                        T * 4, 0x00020000);
+    struct RowRaw {
+        v2u g;
+        float st, d;
+    };
+    auto load_rows = [&](int t0) {
+        const uint32_t t = (uint32_t)(t0 + (tid & (kTile - 1)));
+        RowRaw r;
+        r.g = __builtin_amdgcn_raw_buffer_load_b64(rG, t * 8, 0, 0);
+        r.st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, t * 4, 0, 0));
+        r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, t * 4, 0, 0));
+        return r;
+    };
+    auto write_rows = [&](int buf, int t0, bool split, const RowRaw& raw) {
         if (tid < kTile) {
             const int t = t0 + tid;
             const bool lin = kSplit && split;   // B holds 2^-b (query factor) instead of b
             float b = lin ? 0.f : INFINITY, r = 0.f, c = 0.f;
             if (t < T) {
-                b = lin ? fexp2(-(float)(G[base + t] - gend) * kLog2e) : (float)(G[base + t] - gref) * kLog2e;
-                const float st = stat[base + t], d = Dt[base + t];
+                const double gt = __builtin_bit_cast(double, raw.g);
+                b = lin ? fexp2(-(float)(gt - gend) * kLog2e) : (float)(gt - gref) * kLog2e;
+                const float st = raw.st, d = raw.d;
                 if (kVar == kLin) {
                 } else if (kVar == kExpV) {
                     b += st;
@@ -369,24 +418,22 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             sm.C[buf][tid] = c;
         }
     };
+    auto stage_rows = [&](int buf, int t0, bool split) { write_rows(buf, t0, split, load_rows(t0)); };
 
     f4 dK[4], dV[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) dK[dt] = dV[dt] = f4{0.f, 0.f, 0.f, 0.f};
     float cs = 0.f;
     const int nqt = (T - k0 + kTile - 1) / kTile;
-    Stage sq, so;
-    fetch(sq, q + (base + k0) * kD, min(kTile, T - k0), tid);
-    fetch(so, dout + (base + k0) * kD, min(kTile, T - k0), tid);
-    store(sq, sm.Q[0], tid);
-    store(so, sm.O[0], tid);
+    const __amdgpu_buffer_rsrc_t rq = head_tile_rsrc(q + base * kD, T), ro = head_tile_rsrc(dout + base * kD, T);
+    dma_tile(sQ0, rq, k0, wu, lane);
+    dma_tile(sO0, ro, k0, wu, lane);
     stage_rows(0, k0, false);   // the diagonal tile
+    wait_vm();
     __syncthreads();
-    auto tile = [&](int it, auto diag_tag) {
+    auto tile = [&](int it, const Tile& Q, const Tile& O, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = it & 1, t0 = k0 + it * kTile;
-        const Tile& Q = sm.Q[cur];
-        const Tile& O = sm.O[cur];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f4 S[2], DP[2];
@@ -452,23 +499,25 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             }
         }
     };
-    auto step = [&](int it, auto diag_tag) {
+    // one query tile from (Qc, Oc) while the next goes into (Qn, On), read last round
+    auto step = [&](int it, const Tile& Qc, const Tile& Oc, Tile& Qn, Tile& On, auto diag_tag) {
         const int cur = it & 1, t0 = k0 + it * kTile;
         const bool more = it + 1 < nqt;
+        const RowRaw rn = load_rows(t0 + kTile);   // past T when !more: reads as zero, unused
         if (more) {
-            fetch(sq, q + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
-            fetch(so, dout + (base + t0 + kTile) * kD, min(kTile, T - t0 - kTile), tid);
+            dma_tile(Qn, rq, t0 + kTile, wu, lane);
+            dma_tile(On, ro, t0 + kTile, wu, lane);
         }
-        tile(it, diag_tag);
-        if (more) {
-            store(sq, sm.Q[cur ^ 1], tid);
-            store(so, sm.O[cur ^ 1], tid);
-            stage_rows(cur ^ 1, t0 + kTile, true);
-        }
+        tile(it, Qc, Oc, diag_tag);
+        if (more) write_rows(cur ^ 1, t0 + kTile, true, rn);
+        wait_vm();
         __syncthreads();
     };
-    step(0, std::true_type{});   // the diagonal tile
-    for (int it = 1; it < nqt; ++it) step(it, std::false_type{});
+    step(0, sQ0, sO0, sQ1, sO1, std::true_type{});   // the diagonal tile
+    for (int it = 1; it < nqt; it += 2) {
+        step(it, sQ1, sO1, sQ0, sO0, std::false_type{});
+        if (it + 1 < nqt) step(it + 1, sQ0, sO0, sQ1, sO1, std::false_type{});
+    }
     cs = xor_sum(cs);
     if (sv_ok) {
         const float fk = kVar == kSq ? 2.f * scale * scale : scale;
@@ -510,7 +559,9 @@ int launch(const BwdArgs& a, const BwdScratch& s) {
 }  // namespace
 
 bool mfma_bwd_supported(const BwdArgs& a) {
-    return a.dtype == TWOMAMBA_BF16 && a.dk == kD && a.dv == kD && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS);
+    // tiles reach LDS through buffer transfers with 32-bit byte offsets into a head's rows
+    return a.dtype == TWOMAMBA_BF16 && a.dk == kD && a.dv == kD && !(a.flags & TWOMAMBA_FLAG_REFERENCE_KERNELS) &&
+           (size_t)a.T * kD * 2 < ((size_t)1 << 31);
 }
 
 int mfma_bwd(const BwdArgs& a) {

@@ -107,6 +107,28 @@ __device__ __forceinline__ void store(const Stage& s, Tile& t, int tid) {
     }
 }
 
+// Buffer -> LDS for one 64-row tile of a head, rows row0 .. row0 + 63 (128 bytes each
+// in global memory, 144 in the tile): nine 1 KB transfers; lane l of transfer i lands at
+// byte 16 (64 i + l) of the tile, which is chunk (64 i + l) mod 9 of row (64 i + l) / 9,
+// so it fetches that chunk; the ninth chunk of a row is its padding and takes a copy of
+// the row's first.  Wave w issues transfers w, w + 4, w + 8.  Rows past the buffer's end
+// read as zero.  The transfers count in vmcnt: wait for them before the barrier that
+// hands the tile to the other waves.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int row0, int w, int lane) {
+    for (int i = w; i < 9; i += kW) {
+        const int c = 64 * i + lane, row = c / 9, col = c - 9 * row;
+        char* dst = reinterpret_cast<char*>(&t.X[0][0]) + 1024 * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16,
+                                                 (uint32_t)((row0 + row) * kD + 8 * (col < 8 ? col : 0)) * 2, 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// a head's rows as a buffer resource: byte offsets are 32-bit, rows past T read as zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_tile_rsrc(const bf16* p, int T) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p), (short)0, T * kD * 2, 0x00020000);
+}
+
 // a lane's own row (query or key) as a B operand: dims 8g + 32 kk .. + 7
 __device__ __forceinline__ b8 own_op(const bf16* row, int g, int kk) {
     return as_b8(*reinterpret_cast<const uint4*>(row + 8 * g + 32 * kk));
