@@ -345,8 +345,10 @@ struct KVSmem {
     float C[2][kTile];      // 2Mamba: -D_t/den_t; 2Mamba-E: D_t
 };
 
+// 2Mamba's key-major kernel is held to four workgroups per CU (128 registers, a few
+// spilled), which measured faster than three; the other two variants keep three
 template <int kVar>
-__global__ void __launch_bounds__(kThreads, kMinBlocks)
+__global__ void __launch_bounds__(kThreads, kVar == kSq ? 4 : kMinBlocks)
 bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const bf16* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
               const float* __restrict__ stat, float* __restrict__ colsum, bf16* __restrict__ dk,
