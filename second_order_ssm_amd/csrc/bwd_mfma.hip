@@ -111,9 +111,10 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     // Off the diagonal tile every key precedes every query of the block, so the
     // decay 2^(a_s - b_t) splits into a key factor 2^a_s and a query factor
     // 2^-b_t, each in (0, 1] (G rises along the sequence and the reference is the
-    // block's first query): one multiply per pair instead of an exp2.  The
-    // diagonal tile keeps the exact exponent.  2Mamba-E folds the decay into its
-    // softmax exponent and always takes the log form.
+    // block's first query): one multiply per pair instead of an exp2, and the
+    // query factor, common to all of a lane's pairs, is applied to their sums
+    // once.  The diagonal tile keeps the exact exponent.  2Mamba-E folds the
+    // decay into its softmax exponent and always takes the log form.
     constexpr bool kSplit = kVar != kExpV;
     const float eb = kSplit ? fexp2(-b2) : 0.f;
 
@@ -276,12 +277,13 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                         d = p * (P[u][i] - Dq);
                         Mv = d;
                     } else if (kVar == kSq) {
-                        const float uu = (kDiag ? fexp2(av[i] - b2) : av[i] * eb) * x;
+                        // off the diagonal the query factor eb is applied to the sums, once
+                        const float uu = (kDiag ? fexp2(av[i] - b2) : av[i]) * x;
                         const float dw = fmaf(P[u][i], st_v, cq);
                         d = uu * dw;
                         Mv = x * d;
                     } else {
-                        d = (kDiag ? fexp2(av[i] - b2) : av[i] * eb) * P[u][i];
+                        d = (kDiag ? fexp2(av[i] - b2) : av[i]) * P[u][i];
                         Mv = x * d;
                     }
                     if (kDiag) {
@@ -314,6 +316,13 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         round2(kt, sK0, sV0, sK1, sV1);
         if (kt + 1 < qb) round2(kt + 1, sK1, sV1, sK0, sV0);
     }
+    if (kSplit) {
+        // the key tiles before the diagonal left out the query factor eb (in (0, 1]) of
+        // every pair: it scales their sums before the diagonal tile adds its own terms
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dQ[dt] *= eb;
+        rs *= eb;
+    }
     if (qb & 1) sweep2(qb, sK1, sV1, std::true_type{});
     else sweep2(qb, sK0, sV0, std::true_type{});
     rs = xor_sum(rs);
@@ -340,9 +349,9 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 // kernel), so that the compiler can tell a tile's reads from the transfers in flight
 // into the other buffer; the per-row terms live here.
 struct KVSmem {
-    float B[2][kTile];      // log2(e) (G_t - G_ref) per query of the tile (+ lse2 for 2Mamba-E)
-    float R[2][kTile];      // 2Mamba: 1/den_t; 2Mamba-E: unused
-    float C[2][kTile];      // 2Mamba: -D_t/den_t; 2Mamba-E: D_t
+    float B[2][kTile];      // per query of the tile: the decay term (see write_rows)
+    float R[2][kTile];      // 2Mamba, diagonal tile: 1/den_t
+    float C[2][kTile];      // 2Mamba: -D_t/den_t (times the query factor off the diagonal); 2Mamba-E: D_t
 };
 
 // 2Mamba's key-major kernel is held to four workgroups per CU (128 registers, a few
@@ -410,6 +419,9 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
                 } else if (kVar == kExpV) {
                     b += st;
                     c = d;
+                } else if (lin) {   // 2Mamba off the diagonal: B = q_f/den_t, C = -q_f D_t/den_t
+                    c = -d * st * b;
+                    b *= st;
                 } else {
                     r = st;
                     c = -d * st;
@@ -457,7 +469,7 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
                 const float4 b4 = *reinterpret_cast<const float4*>(&sm.B[cur][16 * tt + 4 * g]);
                 const float4 c4 = *reinterpret_cast<const float4*>(&sm.C[cur][16 * tt + 4 * g]);
                 float4 r4 = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (kVar == kSq) r4 = *reinterpret_cast<const float4*>(&sm.R[cur][16 * tt + 4 * g]);
+                if (kVar == kSq && kDiag) r4 = *reinterpret_cast<const float4*>(&sm.R[cur][16 * tt + 4 * g]);
                 const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
                 const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
@@ -470,10 +482,15 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
                         d = pp * (DP[u][i] - cv[i]);
                         Mv = d;
                     } else if (kVar == kSq) {
-                        const float uu = (kDiag ? fexp2(a2 - bv[i]) : ea * bv[i]) * x;
-                        pp = uu * x * rv[i];
-                        const float dw = fmaf(DP[u][i], rv[i], cv[i]);
-                        d = uu * dw;
+                        if (kDiag) {
+                            const float uu = fexp2(a2 - bv[i]) * x;
+                            pp = uu * x * rv[i];
+                            d = uu * fmaf(DP[u][i], rv[i], cv[i]);
+                        } else {   // the rows hold q_f/den_t and -q_f D_t/den_t
+                            const float e = ea * x;
+                            pp = e * x * bv[i];
+                            d = e * fmaf(DP[u][i], bv[i], cv[i]);
+                        }
                         Mv = x * d;
                     } else {
                         const float L = kDiag ? fexp2(a2 - bv[i]) : ea * bv[i];
