@@ -87,6 +87,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     const int q0 = qb * kBlk;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
     const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index as a scalar (tile transfers)
+    const DmaOffsets dmo = dma_offsets(wu, lane);
     const size_t base = (size_t)bh * T;
     const int t = q0 + 16 * w + col;               // this lane's query
     const bool tv = t < T;
@@ -192,7 +193,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
     };
     if (need_sweep1) {
-        dma_tile(sK0, rk, 0, wu, lane);
+        dma_tile(sK0, rk, 0, wu, dmo);
         stage_a(0, 0, 0 < qb);
         wait_vm();
         __syncthreads();
@@ -200,7 +201,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         auto round1 = [&](int kt, const Tile& Kc, Tile& Kn) {
             const int cur = kt & 1, s0 = kt * kTile;
             const v2u an = load_a(s0 + kTile);
-            dma_tile(Kn, rk, s0 + kTile, wu, lane);
+            dma_tile(Kn, rk, s0 + kTile, wu, dmo);
             sweep1(kt, Kc, std::false_type{});
             write_a(cur ^ 1, s0 + kTile, kt + 1 < qb, an);
             wait_vm();
@@ -241,8 +242,8 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) dQ[dt] = f4{0.f, 0.f, 0.f, 0.f};
     float rs = 0.f;
-    dma_tile(sK0, rk, 0, wu, lane);
-    dma_tile(sV0, rv, 0, wu, lane);
+    dma_tile(sK0, rk, 0, wu, dmo);
+    dma_tile(sV0, rv, 0, wu, dmo);
     stage_a(0, 0, 0 < qb);
     wait_vm();
     __syncthreads();
@@ -305,8 +306,8 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     auto round2 = [&](int kt, const Tile& Kc, const Tile& Vc, Tile& Kn, Tile& Vn) {
         const int cur = kt & 1, s0 = kt * kTile;
         const v2u an = load_a(s0 + kTile);
-        dma_tile(Kn, rk, s0 + kTile, wu, lane);
-        dma_tile(Vn, rv, s0 + kTile, wu, lane);
+        dma_tile(Kn, rk, s0 + kTile, wu, dmo);
+        dma_tile(Vn, rv, s0 + kTile, wu, dmo);
         sweep2(kt, Kc, Vc, std::false_type{});
         write_a(cur ^ 1, s0 + kTile, kt + 1 < qb, an);
         wait_vm();
@@ -354,10 +355,10 @@ struct KVSmem {
     float C[2][kTile];      // 2Mamba: -D_t/den_t (times the query factor off the diagonal); 2Mamba-E: D_t
 };
 
-// 2Mamba's key-major kernel is held to four workgroups per CU (128 registers, a few
-// spilled), which measured faster than three; the other two variants keep three
+// The key-major kernel is held to four workgroups per CU (128 registers; 2Mamba's
+// spills a few), which measured faster than three for 2Mamba; 2Mamba-E keeps three
 template <int kVar>
-__global__ void __launch_bounds__(kThreads, kVar == kSq ? 4 : kMinBlocks)
+__global__ void __launch_bounds__(kThreads, kVar == kExpV ? kMinBlocks : 4)
 bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const bf16* __restrict__ dout, const double* __restrict__ G, const float* __restrict__ Dt,
               const float* __restrict__ stat, float* __restrict__ colsum, bf16* __restrict__ dk,
@@ -369,6 +370,7 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     const int k0 = kb * kBlk;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
     const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index as a scalar (tile transfers)
+    const DmaOffsets dmo = dma_offsets(wu, lane);
     const size_t base = (size_t)bh * T;
     const int s = k0 + 16 * w + col;               // this lane's key
     const bool sv_ok = s < T;
@@ -440,8 +442,8 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     float cs = 0.f;
     const int nqt = (T - k0 + kTile - 1) / kTile;
     const __amdgpu_buffer_rsrc_t rq = head_tile_rsrc(q + base * kD, T), ro = head_tile_rsrc(dout + base * kD, T);
-    dma_tile(sQ0, rq, k0, wu, lane);
-    dma_tile(sO0, ro, k0, wu, lane);
+    dma_tile(sQ0, rq, k0, wu, dmo);
+    dma_tile(sO0, ro, k0, wu, dmo);
     stage_rows(0, k0, false);   // the diagonal tile
     wait_vm();
     __syncthreads();
@@ -524,8 +526,8 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         const bool more = it + 1 < nqt;
         const RowRaw rn = load_rows(t0 + kTile);   // past T when !more: reads as zero, unused
         if (more) {
-            dma_tile(Qn, rq, t0 + kTile, wu, lane);
-            dma_tile(On, ro, t0 + kTile, wu, lane);
+            dma_tile(Qn, rq, t0 + kTile, wu, dmo);
+            dma_tile(On, ro, t0 + kTile, wu, dmo);
         }
         tile(it, Qc, Oc, diag_tag);
         if (more) write_rows(cur ^ 1, t0 + kTile, true, rn);

@@ -115,12 +115,30 @@ __device__ __forceinline__ void store(const Stage& s, Tile& t, int tid) {
 // read as zero.  The transfers count in vmcnt: wait for them before the barrier that
 // hands the tile to the other waves.
 typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void dma_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int row0, int w, int lane) {
-    for (int i = w; i < 9; i += kW) {
-        const int c = 64 * i + lane, row = c / 9, col = c - 9 * row;
-        char* dst = reinterpret_cast<char*>(&t.X[0][0]) + 1024 * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16,
-                                                 (uint32_t)((row0 + row) * kD + 8 * (col < 8 ? col : 0)) * 2, 0, 0, 0);
+// A lane's byte offsets inside a tile's rows for its wave's transfers (w, w + 4, w + 8),
+// the same for every tile: taken once per kernel.
+struct DmaOffsets {
+    uint32_t v[3];
+};
+__device__ __forceinline__ DmaOffsets dma_offsets(int w, int lane) {
+    DmaOffsets o;
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int c = 64 * (w + kW * n) + lane, row = c / 9, col = c - 9 * row;
+        o.v[n] = (uint32_t)(row * kD + 8 * (col < 8 ? col : 0)) * 2;
+    }
+    return o;
+}
+// the tile's first row goes in as the scalar offset
+__device__ __forceinline__ void dma_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int row0, int w, const DmaOffsets& o) {
+    const int so = row0 * kD * 2;
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int i = w + kW * n;
+        if (i < 9) {
+            char* dst = reinterpret_cast<char*>(&t.X[0][0]) + 1024 * i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, o.v[n], so, 0, 0);
+        }
     }
 }
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
