@@ -1132,12 +1132,14 @@ sq_segstate_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int t0 = c * kC;
         const int par = c & 1;
-        const int tidc = tid + sm.zero;
+        // re-derived from an LDS zero every chunk (kept out of registers across the loop),
+        // masked to their ranges so that the address products stay 24-bit
+        const int tidc = (tid + sm.zero) & (kThreads - 1);
         const int lane = tidc & 63;
         const int l16 = lane & 15;
         const int kg = lane >> 4;
         const int gq = l16 >> 2, bq4 = l16 & 3;
-        const int wl = __builtin_amdgcn_readfirstlane(tidc >> 6);
+        const int wl = __builtin_amdgcn_readfirstlane(tidc >> 6) & (kWaves - 1);
 
         float kv[8], vv[8];
         unpack8(raw.k, kv);
