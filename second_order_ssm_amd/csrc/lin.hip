@@ -270,12 +270,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rows(const bf16* head, in
     return buf_rsrc(head, (uint32_t)T * kD * 2);
 }
 
-// rows t0 .. t0 + 63 (logical) of a head's tensor in the Stage layout (zeros past T)
-__device__ __forceinline__ void fetch_rows(Stage& s, __amdgpu_buffer_rsrc_t head, int t0, int T, bool rev, int tid) {
+// rows t0 .. t0 + 63 (logical) of a head's tensor in the Stage layout (zeros past T).
+// Not `live`: the same loads at an offset past the buffer (zeros, no memory access), so
+// that every path through a chunk loop issues the same loads and the compiler can size
+// its waits for the one buffer a chunk consumes.
+__device__ __forceinline__ void fetch_rows(Stage& s, __amdgpu_buffer_rsrc_t head, int t0, int T, bool rev, int tid,
+                                           bool live) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int e = tid + n * kThreads, r = e >> 3, c = e & 7;
-        s.c[n] = buf_ld16(head, (uint32_t)(stored_row(t0 + r, T, rev) * kD + 8 * c) * 2);
+        s.c[n] = buf_ld16(head, live ? (uint32_t)(stored_row(t0 + r, T, rev) * kD + 8 * c) * 2 : kNoAccess);
     }
 }
 
@@ -342,14 +346,16 @@ __device__ __forceinline__ Conv8 conv_lds_get(const ConvLds& c, int tensor, int 
 // sequence, from `prev`, the cached raw row of token -1 (an empty resource = zeros);
 // conv_stage takes the others from their neighbours.
 __device__ __forceinline__ void fetch_before(Stage& s, __amdgpu_buffer_rsrc_t head, __amdgpu_buffer_rsrc_t prev,
-                                             int t0, int tid) {
+                                             int t0, int tid, bool live) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool edge = ((tid & 63) >> 3) == 0;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int e = tid + n * kThreads, r = e >> 3, c = e & 7;
         const bool from_prev = t0 == 0 && n == 0 && w == 0;   // row -1 (uniform per wave)
-        const uint32_t off = !edge ? kNoAccess : from_prev ? (uint32_t)(8 * c) * 2 : (uint32_t)((t0 + r - 1) * kD + 8 * c) * 2;
+        const uint32_t off = (!edge || !live) ? kNoAccess
+                             : from_prev        ? (uint32_t)(8 * c) * 2
+                                                : (uint32_t)((t0 + r - 1) * kD + 8 * c) * 2;
         s.c[n] = buf_ld16(from_prev ? prev : head, off);
     }
 }
@@ -412,22 +418,24 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
     float later = 0.f;   // log2 decay from the end of the current chunk to the segment end
-    // the next chunk's rows in flight to registers while this one is computed
+    // the next kDepth chunks' rows in flight to registers while this one is computed, one
+    // buffer per chunk (the chunk loop is unrolled so that each is named statically)
+    constexpr int kDepth = 2;
     struct Ahead {
         Stage k, v, bk, bv;
         float gz;   // wave 0: this lane's z
     };
-    auto fetch_chunk = [&](Ahead& f, int c) {
+    auto fetch_chunk = [&](Ahead& f, int c, bool live) {
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
-        if (w == 0) f.gz = lane_z(rz, t0, T, kRev, lane, Lc);
-        fetch_rows(f.k, rk, t0, T, kRev, tid);
-        fetch_rows(f.v, rv, t0, T, kRev, tid);
+        f.gz = lane_z(rz, t0, T, kRev, lane, (live && w == 0) ? Lc : 0);
+        fetch_rows(f.k, rk, t0, T, kRev, tid, live);
+        fetch_rows(f.v, rv, t0, T, kRev, tid, live);
         if (conv) {
-            fetch_before(f.bk, rk, rkp, t0, tid);
-            fetch_before(f.bv, rv, rvp, t0, tid);
+            fetch_before(f.bk, rk, rkp, t0, tid, live);
+            fetch_before(f.bv, rv, rvp, t0, tid, live);
         }
     };
-    // one chunk from buffer f, which is refilled with chunk c - 1 once staged
+    // one chunk from buffer f, which is refilled with chunk c - kDepth once staged
     auto chunk = [&](int c, Ahead& f) {
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
         if (w == 0) {
@@ -444,7 +452,7 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
         store(f.k, sK, tid);
         store_scaled(f.v, sV, s_w, tid);
         __syncthreads();
-        if (c > c0) fetch_chunk(f, c - 1);
+        fetch_chunk(f, c - kDepth, c - kDepth >= c0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const b8 A = tr_op(sV, w, 2 * h, lane);
@@ -453,10 +461,18 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
         }
         __syncthreads();
     };
-    Ahead f;
-    fetch_chunk(f, c1 - 1);   // from the segment end backwards
+    Ahead f[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) fetch_chunk(f[i], c1 - 1 - i, c1 - 1 - i >= c0);   // from the segment end backwards
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing issued before the loop left in flight at its top
-    for (int c = c1 - 1; c >= c0; --c) chunk(c, f);
+    int c = c1 - 1;
+    for (; c - (kDepth - 1) >= c0; c -= kDepth) {
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) chunk(c - i, f[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i)
+        if (c - i >= c0) chunk(c - i, f[i]);
     float* dst = wsS + ((size_t)bh * nseg + seg) * kD * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -470,8 +486,11 @@ lin_seg_mfma(const bf16* __restrict__ k, const bf16* __restrict__ v, const float
 // (the backward's passes): the sums run over strictly earlier tokens, the optional
 // dot with xdot is taken over that strict output, and the diagonal term
 // scale (q_t.k_t) v_t is added to the stored output only afterwards.
+// Bounded to two workgroups per CU (256 registers): the grid never holds more than
+// about two per CU, but under that register target the compiler schedules the chunk
+// loop into 170-180 registers and it runs 3-6 % faster than the 200+ it takes otherwise.
 template <bool kConv, bool kRev, bool kStrict>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)
 lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const float* __restrict__ z, const float* __restrict__ carry, bf16* __restrict__ out, int T, int nseg,
               int seg_chunks, float scale, const float* __restrict__ cw, const float* __restrict__ cb,
@@ -506,7 +525,8 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[dt][i] = src[(16 * w + 4 * g + i) * kD + 16 * dt + col];
     }
-    // the next chunk's rows in flight to registers while this one is computed
+    // the next chunk's rows in flight to registers while this one is computed (a second
+    // buffer, two chunks ahead, measured no faster here and costs 64 registers)
     const bool dots = kStrict && xdot != nullptr;
     const __amdgpu_buffer_rsrc_t rx = head_rows(dots ? xdot + base * kD : out, T);
     const int tl = 16 * w + col;   // this lane's query in the chunk (with its lane group g)
@@ -515,21 +535,22 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         uint2 x[4];   // the backward's dot operand at this lane's output positions
         float gz;     // wave 0: this lane's z
     };
-    auto fetch_chunk = [&](Ahead& f, int c) {
+    auto fetch_chunk = [&](Ahead& f, int c, bool live) {
         const int t0 = c * kTile, Lc = min(kTile, T - t0);
-        if (w == 0) f.gz = lane_z(rz, t0, T, kRev, lane, Lc);
-        fetch_rows(f.q, rq, t0, T, kRev, tid);
-        fetch_rows(f.k, rk, t0, T, kRev, tid);
-        fetch_rows(f.v, rv, t0, T, kRev, tid);
+        f.gz = lane_z(rz, t0, T, kRev, lane, (live && w == 0) ? Lc : 0);
+        fetch_rows(f.q, rq, t0, T, kRev, tid, live);
+        fetch_rows(f.k, rk, t0, T, kRev, tid, live);
+        fetch_rows(f.v, rv, t0, T, kRev, tid, live);
         if (conv) {
-            fetch_before(f.bq, rq, rqp, t0, tid);
-            fetch_before(f.bk, rk, rkp, t0, tid);
-            fetch_before(f.bv, rv, rvp, t0, tid);
+            fetch_before(f.bq, rq, rqp, t0, tid, live);
+            fetch_before(f.bk, rk, rkp, t0, tid, live);
+            fetch_before(f.bv, rv, rvp, t0, tid, live);
         }
         if (dots) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
-                f.x[ct] = buf_ld8(rx, (uint32_t)(stored_row(t0 + tl, T, kRev) * kD + 16 * ct + 4 * g) * 2);
+                f.x[ct] = buf_ld8(rx, live ? (uint32_t)(stored_row(t0 + tl, T, kRev) * kD + 16 * ct + 4 * g) * 2
+                                           : kNoAccess);
         }
     };
     // This chunk's output is stored one chunk later, right after the next prefetch is
@@ -578,7 +599,7 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         store_scaled(f.v, sW, s_w, tid);
         store(f.v, sV, tid);
         __syncthreads();
-        if (c + 1 < c1) fetch_chunk(f, c + 1);
+        fetch_chunk(f, c + 1, c + 1 < c1);
         store_out();   // the previous chunk's
         // this wave's queries 16w .. 16w + 15, one per lane column
         const float glt = s_gl[tl];
@@ -681,7 +702,7 @@ lin_main_mfma(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         __syncthreads();
     };
     Ahead f;
-    fetch_chunk(f, c0);
+    fetch_chunk(f, c0, true);
     // Retire the loads above (the carry and the first chunk) before the loop: the waits
     // inside it are sized for the loop's own order of loads and stores, which only holds
     // when nothing issued before the loop is still in flight at its top.
