@@ -369,9 +369,14 @@ __device__ __forceinline__ void tile_step(Slot* __restrict__ curp, Slot* __restr
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // The tile's bias row before the next transfers are issued: where the compiler has
+    // lost track of which slot a transfer in flight targets (at the top of the loop), the
+    // first LDS access after it waits for every transfer, and this way those are at least
+    // a tile old.
+    const bool act = wact && j <= jdiag;
+    if (act) tile_bias(cur, w, lane, j * kKT, Ew, ws.M, inv_scale);
     if (j >= 2) issue_tile(nxt, rk, rv, rz, (j - 2) * kKT, w, lane);
-    if (wact && j <= jdiag) {
-        tile_bias(cur, w, lane, j * kKT, Ew, ws.M, inv_scale);
+    if (act) {
         if (j < jdiag) tile_full(cur, w, lane, Qop, ws.O, ws.m, ws.l, scl, lazy);
         else tile_diag(cur, w, lane, Qop, ws.O, ws.m, ws.l, scl, lazy);
     }
