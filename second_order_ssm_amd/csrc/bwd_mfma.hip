@@ -33,9 +33,13 @@
 // operand layout of the next product: two vertically adjacent 16x16 tiles give
 // a lane the eight K-slots {4g..4g+3, 16+4g..16+4g+3}; the transposed A
 // operands (K^T, Q^T, dout^T) are read in that order with gfx950's
-// transposing LDS read.  Tiles are staged through LDS row-major (144-byte
-// rows), double-buffered, with the next tile's global loads in flight during
-// the current tile's MFMAs.
+// transposing LDS read.  Tiles reach LDS by buffer-to-LDS transfers as
+// SwTiles (128-byte rows whose 16-byte chunks are permuted per row, so that the
+// row reads and the transposing reads are free of bank conflicts),
+// double-buffered, with the next tile's transfers in flight during the current
+// tile's MFMAs.  The key-major kernel takes each lane's in-tile offsets once per
+// kernel (it is held to 128 registers); the query-major one forms them where
+// they are used, which it schedules better within its larger budget.
 #include <type_traits>
 
 #include "device_common.h"
@@ -80,7 +84,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
              float* __restrict__ rowsum, bf16* __restrict__ dq, int T, int nqb, float scale, int norm, int use_d,
              int by_xcd) {
     __shared__ __attribute__((aligned(16))) QSmem sm;
-    __shared__ __attribute__((aligned(16))) Tile sK0, sK1, sV0, sV1;
+    __shared__ __attribute__((aligned(16))) SwTile sK0, sK1, sV0, sV1;
     int bh, blk;
     xcd_map(blockIdx.x, nqb, by_xcd, bh, blk);
     const int qb = nqb - 1 - blk;                  // longest rows first
@@ -135,13 +139,12 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     };
     auto stage_a = [&](int buf, int s0, bool split) { write_a(buf, s0, split, load_a(s0)); };
     // S^T[s][t] for the key tiles st = 2h, 2h+1 of 16
-    auto scores = [&](const Tile& K, int h, f4 (&S)[2]) {
+    auto scores = [&](const SwTile& K, int h, f4 (&S)[2]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int r = 16 * (2 * h + u) + col;
             f4 c = {0.f, 0.f, 0.f, 0.f};
-            c = mfma(row_op(K, r, g, 0), Qb[0], c);
-            c = mfma(row_op(K, r, g, 1), Qb[1], c);
+            c = mfma(row_op(K, 16 * (2 * h + u) + col, g, 0), Qb[0], c);
+            c = mfma(row_op(K, 16 * (2 * h + u) + col, g, 1), Qb[1], c);
             S[u] = c;
         }
     };
@@ -152,7 +155,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     // forward handed it over)
     const bool need_sweep1 = kVar != kLin && !fstat && !(kVar == kSq && !norm);
     float den = 0.f, m = -INFINITY, l = 0.f;
-    auto sweep1 = [&](int kt, const Tile& K, auto diag_tag) {
+    auto sweep1 = [&](int kt, const SwTile& K, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = kt & 1, s0 = kt * kTile;
 #pragma unroll
@@ -198,7 +201,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         wait_vm();
         __syncthreads();
         // key tiles wholly before the queries, from Kc while the next goes into Kn
-        auto round1 = [&](int kt, const Tile& Kc, Tile& Kn) {
+        auto round1 = [&](int kt, const SwTile& Kc, SwTile& Kn) {
             const int cur = kt & 1, s0 = kt * kTile;
             const v2u an = load_a(s0 + kTile);
             dma_tile(Kn, rk, s0 + kTile, wu, dmo);
@@ -247,7 +250,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     stage_a(0, 0, 0 < qb);
     wait_vm();
     __syncthreads();
-    auto sweep2 = [&](int kt, const Tile& K, const Tile& V, auto diag_tag) {
+    auto sweep2 = [&](int kt, const SwTile& K, const SwTile& V, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = kt & 1, s0 = kt * kTile;
 #pragma unroll
@@ -256,10 +259,9 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             scores(K, h, S);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int r = 16 * (2 * h + u) + col;
                 f4 c = {0.f, 0.f, 0.f, 0.f};
-                c = mfma(row_op(V, r, g, 0), Ob[0], c);
-                c = mfma(row_op(V, r, g, 1), Ob[1], c);
+                c = mfma(row_op(V, 16 * (2 * h + u) + col, g, 0), Ob[0], c);
+                c = mfma(row_op(V, 16 * (2 * h + u) + col, g, 1), Ob[1], c);
                 P[u] = c;   // dP^T
             }
             float ds[8];
@@ -303,7 +305,7 @@ bwd_q_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
     };
     // from (Kc, Vc) while the next tile goes into (Kn, Vn), read last round
-    auto round2 = [&](int kt, const Tile& Kc, const Tile& Vc, Tile& Kn, Tile& Vn) {
+    auto round2 = [&](int kt, const SwTile& Kc, const SwTile& Vc, SwTile& Kn, SwTile& Vn) {
         const int cur = kt & 1, s0 = kt * kTile;
         const v2u an = load_a(s0 + kTile);
         dma_tile(Kn, rk, s0 + kTile, wu, dmo);
@@ -364,13 +366,14 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
               const float* __restrict__ stat, float* __restrict__ colsum, bf16* __restrict__ dk,
               bf16* __restrict__ dv, int T, int nkb, float scale, int by_xcd) {
     __shared__ __attribute__((aligned(16))) KVSmem sm;
-    __shared__ __attribute__((aligned(16))) Tile sQ0, sQ1, sO0, sO1;
+    __shared__ __attribute__((aligned(16))) SwTile sQ0, sQ1, sO0, sO1;
     int bh, kb;
     xcd_map(blockIdx.x, nkb, by_xcd, bh, kb);     // earliest keys (longest columns) first
     const int k0 = kb * kBlk;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
     const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index as a scalar (tile transfers)
     const DmaOffsets dmo = dma_offsets(wu, lane);
+    const SwOffsets swo = sw_offsets(lane);
     const size_t base = (size_t)bh * T;
     const int s = k0 + 16 * w + col;               // this lane's key
     const bool sv_ok = s < T;
@@ -447,7 +450,7 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
     stage_rows(0, k0, false);   // the diagonal tile
     wait_vm();
     __syncthreads();
-    auto tile = [&](int it, const Tile& Q, const Tile& O, auto diag_tag) {
+    auto tile = [&](int it, const SwTile& Q, const SwTile& O, auto diag_tag) {
         constexpr bool kDiag = decltype(diag_tag)::value;
         const int cur = it & 1, t0 = k0 + it * kTile;
 #pragma unroll
@@ -455,12 +458,11 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             f4 S[2], DP[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int r = 16 * (2 * h + u) + col;
                 f4 c = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
-                c = mfma(row_op(Q, r, g, 0), Kb[0], c);
-                c = mfma(row_op(Q, r, g, 1), Kb[1], c);
-                e = mfma(row_op(O, r, g, 0), Vb[0], e);
-                e = mfma(row_op(O, r, g, 1), Vb[1], e);
+                c = mfma(row_op(Q, swo, 2 * h + u, 0), Kb[0], c);
+                c = mfma(row_op(Q, swo, 2 * h + u, 1), Kb[1], c);
+                e = mfma(row_op(O, swo, 2 * h + u, 0), Vb[0], e);
+                e = mfma(row_op(O, swo, 2 * h + u, 1), Vb[1], e);
                 S[u] = c;
                 DP[u] = e;
             }
@@ -515,13 +517,13 @@ bwd_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
             const b8 BP = to_b(p), BD = to_b(ds);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                dV[dt] = mfma(tr_op(O, dt, 2 * h, lane), BP, dV[dt]);
-                dK[dt] = mfma(tr_op(Q, dt, 2 * h, lane), BD, dK[dt]);
+                dV[dt] = mfma(tr_op(O, swo, dt, 2 * h), BP, dV[dt]);
+                dK[dt] = mfma(tr_op(Q, swo, dt, 2 * h), BD, dK[dt]);
             }
         }
     };
     // one query tile from (Qc, Oc) while the next goes into (Qn, On), read last round
-    auto step = [&](int it, const Tile& Qc, const Tile& Oc, Tile& Qn, Tile& On, auto diag_tag) {
+    auto step = [&](int it, const SwTile& Qc, const SwTile& Oc, SwTile& Qn, SwTile& On, auto diag_tag) {
         const int cur = it & 1, t0 = k0 + it * kTile;
         const bool more = it + 1 < nqt;
         const RowRaw rn = load_rows(t0 + kTile);   // past T when !more: reads as zero, unused

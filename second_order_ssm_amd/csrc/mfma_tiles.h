@@ -107,38 +107,100 @@ __device__ __forceinline__ void store(const Stage& s, Tile& t, int tid) {
     }
 }
 
-// Buffer -> LDS for one 64-row tile of a head, rows row0 .. row0 + 63 (128 bytes each
-// in global memory, 144 in the tile): nine 1 KB transfers; lane l of transfer i lands at
-// byte 16 (64 i + l) of the tile, which is chunk (64 i + l) mod 9 of row (64 i + l) / 9,
-// so it fetches that chunk; the ninth chunk of a row is its padding and takes a copy of
-// the row's first.  Wave w issues transfers w, w + 4, w + 8.  Rows past the buffer's end
-// read as zero.  The transfers count in vmcnt: wait for them before the barrier that
-// hands the tile to the other waves.
+// A 64-row tile without padding (128-byte rows) whose 16-byte chunks are permuted
+// within each row: chunk c of row R sits at position c ^ sw_chunk(R), a function of
+// R mod 16.  Both read patterns of the MFMA operands then hit distinct banks, with
+// 32 banks of 4 bytes or with 64: the row reads (16 consecutive rows, one chunk each;
+// 8 rows per cycle at 32 banks) need sw_chunk to be one-to-one on the even and on the
+// odd rows of 16 and on each run of 8; the transposing reads (per 16-lane group 4
+// consecutive rows, two adjacent chunks 2dt, 2dt + 1 each) need sw_chunk / 2 to be
+// one-to-one on every 4 consecutive rows and on the rows 0, 2, 4, 6 (1, 3, 5, 7) of
+// each 8.  (The padded 144-byte rows of Tile serve the row reads but put two of the
+// eight rows of a transposing read on the same banks.)
+struct SwTile {
+    uint16_t X[kTile][kD];
+};
+__device__ __forceinline__ int sw_chunk(int row) {
+    const int R = row & 15;
+    return 2 * ((R & 3) ^ ((R >> 2) & 1)) + (((R >> 3) ^ (R >> 2)) & 1);
+}
+// The operands of row_op and tr_op above, read from a SwTile, with the lane's
+// addresses formed where they are used (the compiler keeps them in registers).
+__device__ __forceinline__ const char* sw_at(const SwTile& t, int row, int chunk) {
+    return reinterpret_cast<const char*>(&t.X[0][0]) + row * 128 + 16 * (chunk ^ sw_chunk(row));
+}
+__device__ __forceinline__ b8 row_op(const SwTile& t, int r, int g, int kk) {
+    return as_b8(*reinterpret_cast<const uint4*>(sw_at(t, r, g + 4 * kk)));
+}
+__device__ __forceinline__ b8 tr_op(const SwTile& t, int dt, int tt, int lane) {
+    const int g = lane >> 4, m = lane & 15, j = m >> 2, r = m & 3;
+    const int row = 16 * tt + 4 * g + j, chunk = 2 * dt + (r >> 1), half = 8 * (r & 1);
+    const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(sw_at(t, row, chunk) + half));
+    const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(sw_at(t, row + 16, chunk) + half));
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return as_b8(make_uint4(ua.x, ua.y, ub.x, ub.y));
+}
+// A lane's byte offsets inside a SwTile for its operand reads (below), the same for
+// every tile and every 16-row block: taken once per kernel, so that each read is one of
+// these registers plus an immediate (the tile's address and the block's 2048 bytes).
+struct SwOffsets {
+    uint32_t row[2];   // row_op: row (lane mod 16), chunk g + 4 kk
+    uint32_t tr[4];    // tr_op: row 4g + j, columns 16 dt + 4r .. + 3
+};
+__device__ __forceinline__ SwOffsets sw_offsets(int lane) {
+    const int g = lane >> 4, m = lane & 15, j = m >> 2, r = m & 3, R = 4 * g + j;
+    SwOffsets o;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) o.row[kk] = (uint32_t)(m * 128 + 16 * ((g + 4 * kk) ^ sw_chunk(m)));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+        o.tr[dt] = (uint32_t)(R * 128 + 16 * ((2 * dt + (r >> 1)) ^ sw_chunk(R)) + 8 * (r & 1));
+    return o;
+}
+// The same two operands through the offsets of sw_offsets: row 16 st + (lane mod 16),
+// dims 8g + 32 kk .. + 7; and the transposed tile's K-slots {16 tt + 4g + 0..3,
+// 16 tt + 16 + 4g + 0..3} for the columns 16 dt .. 16 dt + 15.
+__device__ __forceinline__ b8 row_op(const SwTile& t, const SwOffsets& o, int st, int kk) {
+    const char* p = reinterpret_cast<const char*>(&t.X[0][0]) + 2048 * st + o.row[kk];
+    return as_b8(*reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ b8 tr_op(const SwTile& t, const SwOffsets& o, int dt, int tt) {
+    const char* p = reinterpret_cast<const char*>(&t.X[0][0]) + 2048 * tt + o.tr[dt];
+    const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p);
+    const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p + 2048));
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return as_b8(make_uint4(ua.x, ua.y, ub.x, ub.y));
+}
+
+// Buffer -> LDS for one 64-row SwTile of a head, rows row0 .. row0 + 63: eight 1 KB
+// transfers; lane l of transfer i lands at byte 16 (64 i + l) of the tile, which is
+// position (64 i + l) mod 8 of row (64 i + l) / 8, so it fetches the chunk the
+// permutation places there (position ^ sw_chunk(row): the map is its own inverse).
+// Wave w issues transfers w and w + 4.  Rows past the buffer's end read as zero.  The
+// transfers count in vmcnt: wait for them before the barrier that hands the tile to the
+// other waves.
 typedef __attribute__((address_space(3))) void lds_void;
-// A lane's byte offsets inside a tile's rows for its wave's transfers (w, w + 4, w + 8),
-// the same for every tile: taken once per kernel.
+// A lane's byte offsets inside a tile's rows for its wave's transfers (w, w + 4), the
+// same for every tile: taken once per kernel.
 struct DmaOffsets {
-    uint32_t v[3];
+    uint32_t v[2];
 };
 __device__ __forceinline__ DmaOffsets dma_offsets(int w, int lane) {
     DmaOffsets o;
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int c = 64 * (w + kW * n) + lane, row = c / 9, col = c - 9 * row;
-        o.v[n] = (uint32_t)(row * kD + 8 * (col < 8 ? col : 0)) * 2;
+    for (int n = 0; n < 2; ++n) {
+        const int c = 64 * (w + kW * n) + lane, row = c >> 3, pos = c & 7;
+        o.v[n] = (uint32_t)(row * kD + 8 * (pos ^ sw_chunk(row))) * 2;
     }
     return o;
 }
 // the tile's first row goes in as the scalar offset
-__device__ __forceinline__ void dma_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int row0, int w, const DmaOffsets& o) {
+__device__ __forceinline__ void dma_tile(SwTile& t, __amdgpu_buffer_rsrc_t r, int row0, int w, const DmaOffsets& o) {
     const int so = row0 * kD * 2;
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int i = w + kW * n;
-        if (i < 9) {
-            char* dst = reinterpret_cast<char*>(&t.X[0][0]) + 1024 * i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, o.v[n], so, 0, 0);
-        }
+    for (int n = 0; n < 2; ++n) {
+        char* dst = reinterpret_cast<char*>(&t.X[0][0]) + 1024 * (w + kW * n);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, o.v[n], so, 0, 0);
     }
 }
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
