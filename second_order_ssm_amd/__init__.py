@@ -32,6 +32,7 @@ FLAG_NO_NORM = 1
 FLAG_REFERENCE_KERNELS = 2
 FLAG_FIRST_ORDER = 4
 FLAG_ATTENTION_FORM = 8
+FLAG_CHUNKED_FORM = 16
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _VARIANT = {"sq": SQ, "exp": EXP, "lin": LIN}
 
@@ -237,7 +238,7 @@ def fwd(q, k, v, z, *, variant="sq", scale=1.0, chunk=0, no_norm=False, referenc
     elif kernel_times is None:
         s = load().twomamba_fwd(*args)
     else:
-        cap = 16
+        cap = 24
         ms = (ctypes.c_float * cap)()
         names = (ctypes.c_char_p * cap)()
         cnt = ctypes.c_int(0)
@@ -376,19 +377,20 @@ def exp_step(q, k, v, z, k_cache, v_cache, g_cache, pos, *, scale=1.0, out=None,
 
 
 def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, reference_kernels=False,
-        attention_form=False, grads=None, workspace=None, kernel_times=None, row_stat=None):
+        attention_form=False, chunked_form=False, grads=None, workspace=None, kernel_times=None, row_stat=None):
     """Backward of fwd (no initial state): returns (dq, dk, dv, dz).
 
     ``out`` is the forward output for the same inputs; ``row_stat`` the
     forward's row statistics (fwd(..., want_stats=True)), or None to have the
     backward recompute them; ``grads`` may supply the four output tensors.  With ``kernel_times`` (a list) the call goes through
     twomamba_bwd_timed and appends (kernel name, milliseconds) per launch.  ``attention_form``: the first
-    order's quadratic form instead of its linear-in-T one.
+    order's quadratic form instead of its linear-in-T one; ``chunked_form``: 2Mamba's linear-in-T form
+    instead of its quadratic one (dz less precise, see TWOMAMBA_FLAG_CHUNKED_FORM).
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     flags = ((FLAG_NO_NORM if no_norm else 0) | (FLAG_REFERENCE_KERNELS if reference_kernels else 0)
-             | (FLAG_ATTENTION_FORM if attention_form else 0))
+             | (FLAG_ATTENTION_FORM if attention_form else 0) | (FLAG_CHUNKED_FORM if chunked_form else 0))
     desc = make_desc(B, H, T, dk, dv, variant=variant, dtype=q.dtype, scale=scale, flags=flags)
     _check(q, (B, H, T, dk), q.dtype, "q")
     _check(k, (B, H, T, dk), q.dtype, "k")
@@ -413,7 +415,7 @@ def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, refere
     if kernel_times is None:
         s = load().twomamba_bwd(*args)
     else:
-        cap = 16
+        cap = 24
         ms = (ctypes.c_float * cap)()
         names = (ctypes.c_char_p * cap)()
         cnt = ctypes.c_int(0)

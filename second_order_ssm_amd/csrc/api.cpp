@@ -47,7 +47,8 @@ int check_desc(const twomamba_fwd_desc* d, size_t* qk_bytes, size_t* v_bytes, si
     if (d->variant != TWOMAMBA_SQ && d->variant != TWOMAMBA_EXP && d->variant != TWOMAMBA_LIN)
         return TWOMAMBA_ERR_DTYPE;
     if (d->dtype != TWOMAMBA_F32 && d->dtype != TWOMAMBA_BF16) return TWOMAMBA_ERR_DTYPE;
-    if (d->flags & ~(unsigned)(TWOMAMBA_FLAG_NO_NORM | TWOMAMBA_FLAG_REFERENCE_KERNELS | TWOMAMBA_FLAG_ATTENTION_FORM))
+    if (d->flags & ~(unsigned)(TWOMAMBA_FLAG_NO_NORM | TWOMAMBA_FLAG_REFERENCE_KERNELS | TWOMAMBA_FLAG_ATTENTION_FORM |
+                               TWOMAMBA_FLAG_CHUNKED_FORM))
         return TWOMAMBA_ERR_UNSUPPORTED;
     if (d->variant == TWOMAMBA_EXP && (d->flags & TWOMAMBA_FLAG_NO_NORM)) return TWOMAMBA_ERR_UNSUPPORTED;
     if (!supported_dims(d->dk, d->dv)) return TWOMAMBA_ERR_UNSUPPORTED;
@@ -585,7 +586,9 @@ int twomamba_bwd_workspace_size(const twomamba_fwd_desc* d, size_t* bytes) {
     int s = check_bwd(d, &qkb, &vb, &zb);
     if (s != TWOMAMBA_OK) return s;
     const twm::BwdArgs ba = bwd_args(d);
-    *bytes = twm::lin_bwd_chunked_supported(ba) ? twm::lin_bwd_chunked_workspace(ba) : twm::bwd_workspace(ba);
+    *bytes = twm::lin_bwd_chunked_supported(ba)  ? twm::lin_bwd_chunked_workspace(ba)
+             : twm::sq_bwd_chunked_supported(ba) ? twm::sq_bwd_chunked_workspace(ba)
+                                                 : twm::bwd_workspace(ba);
     return TWOMAMBA_OK;
 }
 
@@ -599,7 +602,10 @@ static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     if (!q || !k || !v || !z || !out || !dout || !dq || !dk || !dv || !dz) return TWOMAMBA_ERR_NULL;
     twm::BwdArgs a = bwd_args(d);
     const bool chunked = twm::lin_bwd_chunked_supported(a);
-    const size_t need = chunked ? twm::lin_bwd_chunked_workspace(a) : twm::bwd_workspace(a);
+    const bool sq_chunked = !chunked && twm::sq_bwd_chunked_supported(a);
+    const size_t need = chunked      ? twm::lin_bwd_chunked_workspace(a)
+                        : sq_chunked ? twm::sq_bwd_chunked_workspace(a)
+                                     : twm::bwd_workspace(a);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return TWOMAMBA_ERR_WORKSPACE;
     const Range ins[] = {rng(q, qkb), rng(k, qkb), rng(v, vb), rng(z, zb), rng(out, vb), rng(dout, vb),
                          rng(row_stat, zb)};
@@ -615,6 +621,7 @@ static int bwd_impl(const twomamba_fwd_desc* d, const void* q, const void* k, co
     a.gq = dq; a.gk = dk; a.gv = dv; a.gz = dz;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.stream = stream; a.timer = timer;
     if (chunked) return twm::lin_bwd_chunked(a);
+    if (sq_chunked) return twm::sq_bwd_chunked(a);
     return twm::mfma_bwd_supported(a) ? twm::mfma_bwd(a) : twm::ref_bwd(a);
 }
 

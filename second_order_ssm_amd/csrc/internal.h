@@ -12,7 +12,7 @@ namespace twm {
 // Optional per-launch timing: when a KTimer is attached to a call, every
 // kernel launch is bracketed by a pair of HIP events (see twomamba_fwd_timed).
 struct KTimer {
-    static constexpr int kMax = 16;
+    static constexpr int kMax = 24;
     void* ev[2 * kMax];
     const char* names[kMax];
     int n;
@@ -166,6 +166,10 @@ BwdScratch bwd_scratch(const BwdArgs& a);
 int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s, bool with_d);
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s);
 int ref_bwd(const BwdArgs& a);
+// 2Mamba backward in O(T) (sq_bwd_chunk.hip): chosen by TWOMAMBA_FLAG_CHUNKED_FORM
+bool sq_bwd_chunked_supported(const BwdArgs& a);
+size_t sq_bwd_chunked_workspace(const BwdArgs& a);
+int sq_bwd_chunked(const BwdArgs& a);
 bool mfma_bwd_supported(const BwdArgs& a);
 int mfma_bwd(const BwdArgs& a);
 // first-order backward in O(T) through the segmented chunk kernels (lin.hip)

@@ -43,7 +43,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.twomamba_abi_version() == 4
+    assert lib.twomamba_abi_version() == 5
     seen = set()
     for s in range(9):
         txt = lib.twomamba_status_str(s).decode()
@@ -258,7 +258,27 @@ def test_attention_form_flag_selects_the_quadratic_first_order_backward(lib):
     assert s == OK and chunked != a256(8 * n) + 4 * a256(4 * n)
     assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2, flags=8)) == (OK, a256(8 * n) + 4 * a256(4 * n))
     assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=0, flags=8)) == bwd_ws(lib, desc(B=2, H=3, T=1000, variant=0))
-    assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2, flags=16))[0] == EUNSUP
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2, flags=32))[0] == EUNSUP
+
+
+def test_chunked_form_flag_selects_the_linear_2mamba_backward(lib):
+    # TWOMAMBA_FLAG_CHUNKED_FORM (16): 2Mamba's backward in its linear-in-T form (a
+    # workspace other than the attention form's per-token rows); without it the attention
+    # form at every T.  The first order and 2Mamba-E ignore the flag; fp32 and the
+    # reference kernels keep the attention form.
+    a256 = lambda x: (x + 255) // 256 * 256
+    att = lambda n: a256(8 * n) + 4 * a256(4 * n)
+    n = 2 * 3 * 1000
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000)) == (OK, att(n))
+    s, ch = bwd_ws(lib, desc(B=2, H=3, T=1000, flags=16))
+    assert s == OK and ch > att(n)
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, flags=16 | 2)) == (OK, att(n))
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, flags=16, dtype=0)) == (OK, att(n))
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=1, flags=16)) == (OK, att(n))
+    assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2, flags=16)) == bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2))
+    n = 1 * 2 * 32768
+    assert bwd_ws(lib, desc(B=1, H=2, T=32768)) == (OK, att(n))
+    assert bwd_ws(lib, desc(B=1, H=2, T=32768, flags=8 | 16)) == (OK, att(n))
 
 
 @pytest.mark.parametrize("kw,status", [
