@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--legs sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,fwd_conv,
-                            lin,lin_step,lin_bwd]
+                            lin,lin_step,lin_bwd,sq_bwd_chunked]
                     [--cpu-seconds S]
 
 A timed step is one 2Mamba chunked forward (decay prep, features, intra-chunk,
@@ -16,8 +16,10 @@ loop, the 2Mamba forward at B=4 H=16 T=2048 and at B=1 H=16 T=32768, the
 a T=2048 prefill) and the 2Mamba-E decode over a bf16 key/value cache (batch
 64, 32 heads, 256 sequential steps after a 2048-token prompt), and the
 backward pass of both variants, the size-2 input convolution and the
-first-order (Mamba-2S) forward on the forward's workload, and the first-order
-decode step; they are reported under ``legs``.
+first-order (Mamba-2S) forward on the forward's workload, the first-order
+decode step and backward, and the 2Mamba backward in its O(T) chunked form at
+B=2 H=16 T=8192 and B=1 H=16 T=32768 beside its attention form; they are
+reported under ``legs``.
 
 The roofline entry is for the dominant kernel of the timed step: algorithmic
 work attributed to that kernel per launch divided by its average duration,
@@ -110,7 +112,8 @@ KERNEL_SOURCES = {"sq_mfma_main": "sq_mfma.hip", "exp_mfma": "exp_mfma.hip", "st
                   "bwd_q": "bwd_mfma.hip", "bwd_kv": "bwd_mfma.hip", "exp_bwd_q": "bwd_mfma.hip",
                   "exp_bwd_kv": "bwd_mfma.hip", "conv2_kernel": "conv.hip", "lin_seg": "lin.hip",
                   "lin_scan": "lin.hip", "lin_main": "lin.hip", "step_first_order64_kernel": "step.hip",
-                  "sq_segstate": "sq_mfma.hip", "bwd_prep": "bwd_ref.hip", "bwd_dz": "bwd_ref.hip"}
+                  "sq_segstate": "sq_mfma.hip", "bwd_prep": "bwd_ref.hip", "bwd_dz": "bwd_ref.hip",
+                  "sqc_walk_q": "sq_bwd_chunk.hip", "sqc_walk_k": "sq_bwd_chunk.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -254,6 +257,73 @@ def leg_bwd(steps, warmup, variant="sq"):
                       # counter traffic of the two MFMA kernels (the decay scan and dz kernels are small)
                       traffic=traffic_sum(*[("" if variant == "sq" else "exp_") + n for n in ("bwd_q", "bwd_kv")])),
     )
+
+
+def sqc_walk_flops_per_head_token(d=64, dv=64):
+    """Work of one chunk walk of the 2Mamba O(T) backward per head-token: the
+    update S[i, c, j] += (lambda b_i e_c) b_j and the readout A_j += (a_i c_c) S[i, c, j]
+    over the unpacked state, d x (dv + 1) x d each (the 65th column included)."""
+    return 4 * d * d * (dv + 1)
+
+
+def sq_bwd_chunked_flops_per_head_token(d=64, dv=64):
+    """The O(T) backward's work per head-token: two walks (dq forward in time, dk
+    reversed) and the reversed-time forward that gives dv."""
+    return 2 * sqc_walk_flops_per_head_token(d, dv) + sq_flops_per_head_token(d, dv)
+
+
+def leg_sq_bwd_chunked(steps, warmup):
+    """2Mamba backward in O(T) (TWOMAMBA_FLAG_CHUNKED_FORM) at the forward's workload
+    and at the long-context one (B=1 H=16 T=32768), beside the attention form of the
+    same backward on the same inputs.  Roofline: the chunk-walk kernel, over the
+    walk's contractions (sqc_walk_flops_per_head_token) per launch."""
+    import numpy as np
+    import torch
+
+    import second_order_ssm_amd as tmb
+    import synth_inputs as SI
+
+    res = {}
+    for B, H, T in ((SQ_SHAPE["B"], SQ_SHAPE["H"], SQ_SHAPE["T"]), (1, 16, 32768)):
+        d = SQ_SHAPE["d"]
+        q, k, v, z = (t.cuda() for t in SI.draw(B, H, T, d, seed=SQ_SHAPE["seed"], dtype="bf16"))
+        dout = torch.from_numpy(np.random.default_rng(SQ_SHAPE["seed"] + 500).standard_normal((B, H, T, d))).to(
+            torch.bfloat16).cuda()
+        out, stat = tmb.fwd(q, k, v, z, want_stats=True)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z))
+        desc = tmb.make_desc(B, H, T, d, d, dtype=torch.bfloat16, flags=tmb.FLAG_CHUNKED_FORM)
+        ws = torch.empty(tmb.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+        fn = lambda: tmb.bwd(q, k, v, z, out, dout, chunked_form=True, grads=grads, workspace=ws, row_stat=stat)
+        ms = time_loop(fn, steps, warmup)
+        per = {}
+        calls = max(3, min(steps, 10))
+        for _ in range(calls):
+            kt = []
+            tmb.bwd(q, k, v, z, out, dout, chunked_form=True, grads=grads, workspace=ws, row_stat=stat,
+                    kernel_times=kt)
+            for n, x in kt:
+                per[n] = per.get(n, 0.0) + x / calls
+        del ws
+        desc_a = tmb.make_desc(B, H, T, d, d, dtype=torch.bfloat16)
+        ws_a = torch.empty(tmb.bwd_workspace_size(desc_a), dtype=torch.uint8, device="cuda")
+        fn_a = lambda: tmb.bwd(q, k, v, z, out, dout, grads=grads, workspace=ws_a, row_stat=stat)
+        ms_att = time_loop(fn_a, max(3, steps // 5), 1)
+        del ws_a
+        walk_ms = (per.get("sqc_walk_q", 0.0) + per.get("sqc_walk_k", 0.0)) / 2
+        walk_work = B * H * T * sqc_walk_flops_per_head_token(d, d)
+        work = B * H * T * sq_bwd_chunked_flops_per_head_token(d, d)
+        res[f"{B}x{H}x{T}"] = dict(ms=ms, head_tokens_per_s=B * H * T / (ms * 1e-3), flops_per_call=work,
+                                   tflops=work / (ms * 1e-3) / 1e12, kernels_ms=per,
+                                   walk_kernel_ms=walk_ms, walk_kernel_tflops=walk_work / (walk_ms * 1e-3) / 1e12,
+                                   attention_form_ms=ms_att, speedup_over_attention_form=ms_att / ms)
+        del q, k, v, z, dout, out, stat, grads
+        torch.cuda.empty_cache()
+    head = res["1x16x32768"]
+    wt = head["walk_kernel_tflops"] * 1e12
+    return dict(workload="2Mamba bwd in O(T) (chunked form), bf16 d=64: B=2 H=16 T=8192 and B=1 H=16 T=32768",
+                ms=res[f"{SQ_SHAPE['B']}x{SQ_SHAPE['H']}x{SQ_SHAPE['T']}"]["ms"], shapes=res,
+                roofline=dict(bound="mfma", kernel="sqc_walk_kernel (main walk, 1x16x32768)", achieved=wt / 1e12,
+                              peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s", frac=wt / PEAK_BF16_FLOPS, traffic=None))
 
 
 def lin_bwd_bytes_per_head_token(d=64, dv=64, esize=2):
@@ -702,7 +772,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="sq,sq_4x16x2048,sq_1x16x32768,exp,step,exp_step,bwd,exp_bwd,conv,fwd_conv,"
-                                      "lin,lin_step,lin_bwd")
+                                      "lin,lin_step,lin_bwd,sq_bwd_chunked")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the copy / GEMM ceiling measurements")
@@ -747,6 +817,10 @@ def main():
     if "conv" in legs:
         res["conv"] = leg_conv(args.steps, args.warmup)
         print(f"[bench] conv leg done: {res['conv']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
+    if "sq_bwd_chunked" in legs:
+        res["sq_bwd_chunked"] = leg_sq_bwd_chunked(args.steps, args.warmup)
+        print(f"[bench] sq_bwd_chunked leg done: {res['sq_bwd_chunked']['ms']:.3f} ms/call", file=sys.stderr,
+              flush=True)
     if "lin_bwd" in legs:
         res["lin_bwd"] = leg_lin_bwd(args.steps, args.warmup)
         print(f"[bench] lin_bwd leg done: {res['lin_bwd']['ms']:.4f} ms/call", file=sys.stderr, flush=True)
