@@ -66,6 +66,7 @@ constexpr int kWv = 8;            // waves per workgroup
 constexpr int kTh = 64 * kWv;
 constexpr int kR4 = 34;           // carried float4 per lane: S (32) and N (2)
 constexpr int kMaxSeg = 8;
+constexpr int kMaxPieces = 4;     // pre-pass pieces per segment
 
 typedef short s4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f4 mfma16(uint2 a, uint2 b, f4 c) {
@@ -248,13 +249,14 @@ __device__ __forceinline__ void state_update(f4 (&S)[8][4], f4 (&N)[2], const Ld
     }
 }
 
-// One launch: kPre = update only over segments 0 .. nseg-2 (end states out);
-// otherwise every segment, from the carried end states, with A out.
+// One launch: kPre = update only over the pieces of segments 0 .. nseg-2 (m per
+// segment, pc chunks each; end states out); otherwise every segment, from the
+// decayed sum of the end states of the pieces before it, with A out.
 template <bool kPre>
 __global__ void __launch_bounds__(kTh)
 sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const bf16* __restrict__ gc,
                 const bf16* __restrict__ ge, const float* __restrict__ gz, const float* __restrict__ gx65,
-                int x65_on_key, const float* __restrict__ gks, int T, int nbh, int nseg, int sc,
+                int x65_on_key, const float* __restrict__ gks, int T, int nbh, int nseg, int sc, int m, int pc,
                 float* __restrict__ E, float* __restrict__ Lam,
                 float* __restrict__ Aout) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -264,7 +266,7 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
     // another wave's case runs under an empty exec mask (MFMAs ignore exec)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // the four quarters of one (head, segment) on one XCD: block i runs on XCD i mod 8
-    const int segs = kPre ? nseg - 1 : nseg;
+    const int segs = kPre ? (nseg - 1) * m : nseg;   // pieces (pre-pass) or segments
     const int x = blockIdx.x % kXcd, jx = blockIdx.x / kXcd;
     const int q = jx & 3, unit = (jx >> 2) * kXcd + x;
     if (unit >= nbh * segs) return;
@@ -284,7 +286,16 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
         src.ks = has_ks ? rsrc(gks + hoff, (size_t)T * 4) : rsrc(gz, 0);
     }
     const int nc = (T + kCk - 1) / kCk;
-    const int ch0 = seg * sc, ch1 = min(nc, ch0 + sc);
+    const int npieces = (nseg - 1) * m;
+    int ch0, ch1;
+    if (kPre) {   // piece seg = segment seg / m, part seg mod m
+        const int sg = seg / m, r = seg - sg * m;
+        ch0 = min(nc, sg * sc + r * pc);
+        ch1 = min(min(nc, (sg + 1) * sc), ch0 + pc);
+    } else {
+        ch0 = seg * sc;
+        ch1 = min(nc, ch0 + sc);
+    }
 
     f4 S[8][4];    // S[i = 8w + il][c = 4g + r][j = 16 jt + m16]
     f4 N[2];       // N[i = 16 (2 (w >> 2) + n) + 4g + r][j = 16 (w & 3) + m16]
@@ -297,11 +308,11 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
     for (int n = 0; n < 2; ++n) N[n] = zero4;
     const size_t slot = (size_t)kWv * kR4 * 64 * 4;   // floats of one (segment, quarter) end state
     if (!kPre && seg > 0) {
-        // carry: sum_{g' < seg} exp(Lam_{g'+1} + ... + Lam_{seg-1}) E_{g'}
+        // carry: the pieces before the segment, sum_{p < seg m} exp(Lam_{p+1} + ...) E_p
         float lsum = 0.f;
-        for (int gp = seg - 1; gp >= 0; --gp) {
+        for (int gp = seg * m - 1; gp >= 0; --gp) {
             const float f = fexp(lsum);
-            const float4* src = reinterpret_cast<const float4*>(E + ((size_t)(bh * kMaxSeg + gp) * 4 + q) * slot) +
+            const float4* src = reinterpret_cast<const float4*>(E + ((size_t)(bh * npieces + gp) * 4 + q) * slot) +
                                 (size_t)w * kR4 * 64 + lane;
 #pragma unroll
             for (int il = 0; il < 8; ++il)
@@ -318,7 +329,7 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
                     N[n][0] += f * v.x; N[n][1] += f * v.y; N[n][2] += f * v.z; N[n][3] += f * v.w;
                 }
             }
-            lsum += Lam[bh * kMaxSeg + gp];
+            lsum += Lam[bh * npieces + gp];
         }
     }
 
@@ -418,7 +429,7 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
     }
 
     if (kPre) {
-        float4* dst = reinterpret_cast<float4*>(E + ((size_t)(bh * kMaxSeg + seg) * 4 + q) * slot) +
+        float4* dst = reinterpret_cast<float4*>(E + ((size_t)(bh * npieces + seg) * 4 + q) * slot) +
                       (size_t)w * kR4 * 64 + lane;
 #pragma unroll
         for (int il = 0; il < 8; ++il)
@@ -429,7 +440,7 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             dst[(32 + n) * 64] = make_float4(fr * N[n][0], fr * N[n][1], fr * N[n][2], fr * N[n][3]);
-        if (q == 0 && tid == 0) Lam[bh * kMaxSeg + seg] = lam_tot;
+        if (q == 0 && tid == 0) Lam[bh * npieces + seg] = lam_tot;
     }
 }
 
@@ -639,7 +650,8 @@ sqc_combine_kernel(const float* __restrict__ A, const float* __restrict__ rsum, 
 }
 
 struct Plan {
-    int nseg, sc;
+    int nseg, sc;   // segments of the main walk, chunks per segment
+    int m, pc;      // pre-pass pieces per segment, chunks per piece
 };
 Plan plan_for(const BwdArgs& a) {
     const int nc = (a.T + kCk - 1) / kCk;
@@ -649,6 +661,23 @@ Plan plan_for(const BwdArgs& a) {
     Plan p;
     p.sc = (nc + want - 1) / want;
     p.nseg = (nc + p.sc - 1) / p.sc;
+    // pre-pass pieces: the fewest per segment that minimise rounds x chunks per piece
+    // over the CUs (256, one workgroup each)
+    p.m = 1;
+    p.pc = p.sc;
+    if (p.nseg > 1) {
+        long best = -1;
+        for (int m = 1; m <= kMaxPieces; ++m) {
+            const int pc = (p.sc + m - 1) / m;
+            const long wgs = (long)nbh * 4 * (p.nseg - 1) * m;
+            const long cost = (wgs + 255) / 256 * pc;
+            if (best < 0 || cost < best) {
+                best = cost;
+                p.m = m;
+                p.pc = pc;
+            }
+        }
+    }
     return p;
 }
 
@@ -691,8 +720,10 @@ Layout layout_for(const BwdArgs& a) {
     L.cols = o; o += toks;
     L.rsum = o; o += toks;
     L.A = o; o += align256(5 * n * kD * 4);
-    L.E = o; o += align256(nbh * kMaxSeg * 4 * (size_t)kWv * kR4 * 64 * 16);
-    L.Lam = o; o += align256(nbh * kMaxSeg * 4);
+    const Plan pl = plan_for(a);
+    const size_t npieces = (size_t)std::max(1, (pl.nseg - 1) * pl.m);
+    L.E = o; o += align256(nbh * npieces * 4 * (size_t)kWv * kR4 * 64 * 16);
+    L.Lam = o; o += align256(nbh * npieces * 4);
     L.total = o;
     return L;
 }
@@ -709,11 +740,11 @@ int walk(const BwdArgs& a, const Layout& Ly, const Plan& p, const void* A_, cons
     float* Lam = (float*)(ws + Ly.Lam);
     float* Aout = (float*)(ws + Ly.A);
     if (p.nseg > 1) {
-        const int units = nbh * (p.nseg - 1);
+        const int units = nbh * (p.nseg - 1) * p.m;
         const int grid = ((units + kXcd - 1) / kXcd) * kXcd * 4;
         ktimer_begin(a.timer, pre_name, a.stream);
         hipLaunchKernelGGL(sqc_walk_kernel<true>, dim3(grid), dim3(kTh), lds, st, (const bf16*)A_, (const bf16*)B_,
-                           (const bf16*)C_, (const bf16*)E_, z, x65, (int)x65_on_key, ks, a.T, nbh, p.nseg, p.sc, E, Lam,
+                           (const bf16*)C_, (const bf16*)E_, z, x65, (int)x65_on_key, ks, a.T, nbh, p.nseg, p.sc, p.m, p.pc, E, Lam,
                            Aout);
         ktimer_end(a.timer, a.stream);
     }
@@ -721,7 +752,7 @@ int walk(const BwdArgs& a, const Layout& Ly, const Plan& p, const void* A_, cons
     const int grid = ((units + kXcd - 1) / kXcd) * kXcd * 4;
     ktimer_begin(a.timer, main_name, a.stream);
     hipLaunchKernelGGL(sqc_walk_kernel<false>, dim3(grid), dim3(kTh), lds, st, (const bf16*)A_, (const bf16*)B_,
-                       (const bf16*)C_, (const bf16*)E_, z, x65, (int)x65_on_key, ks, a.T, nbh, p.nseg, p.sc, E, Lam, Aout);
+                       (const bf16*)C_, (const bf16*)E_, z, x65, (int)x65_on_key, ks, a.T, nbh, p.nseg, p.sc, p.m, p.pc, E, Lam, Aout);
     ktimer_end(a.timer, a.stream);
     const int nc = (a.T + kCk - 1) / kCk;
     ktimer_begin(a.timer, "sqc_intra", a.stream);
