@@ -259,8 +259,7 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
                 int x65_on_key, const float* __restrict__ gks, int T, int nbh, int nseg, int sc, int m, int pc,
                 float* __restrict__ E, float* __restrict__ Lam,
                 float* __restrict__ Aout) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    Lds& L = *reinterpret_cast<Lds*>(smem);
+    __shared__ __attribute__((aligned(16))) Lds L;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m16 = lane & 15;
     // the wave index as a wave-uniform value: branches on it are then scalar, so no MFMA of
     // another wave's case runs under an empty exec mask (MFMAs ignore exec)
@@ -735,7 +734,6 @@ int walk(const BwdArgs& a, const Layout& Ly, const Plan& p, const void* A_, cons
     char* ws = (char*)a.ws;
     const int nbh = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
-    const size_t lds = sizeof(Lds);
     float* E = (float*)(ws + Ly.E);
     float* Lam = (float*)(ws + Ly.Lam);
     float* Aout = (float*)(ws + Ly.A);
@@ -743,7 +741,7 @@ int walk(const BwdArgs& a, const Layout& Ly, const Plan& p, const void* A_, cons
         const int units = nbh * (p.nseg - 1) * p.m;
         const int grid = ((units + kXcd - 1) / kXcd) * kXcd * 4;
         ktimer_begin(a.timer, pre_name, a.stream);
-        hipLaunchKernelGGL(sqc_walk_kernel<true>, dim3(grid), dim3(kTh), lds, st, (const bf16*)A_, (const bf16*)B_,
+        hipLaunchKernelGGL(sqc_walk_kernel<true>, dim3(grid), dim3(kTh), 0, st, (const bf16*)A_, (const bf16*)B_,
                            (const bf16*)C_, (const bf16*)E_, z, x65, (int)x65_on_key, ks, a.T, nbh, p.nseg, p.sc, p.m, p.pc, E, Lam,
                            Aout);
         ktimer_end(a.timer, a.stream);
@@ -751,7 +749,7 @@ int walk(const BwdArgs& a, const Layout& Ly, const Plan& p, const void* A_, cons
     const int units = nbh * p.nseg;
     const int grid = ((units + kXcd - 1) / kXcd) * kXcd * 4;
     ktimer_begin(a.timer, main_name, a.stream);
-    hipLaunchKernelGGL(sqc_walk_kernel<false>, dim3(grid), dim3(kTh), lds, st, (const bf16*)A_, (const bf16*)B_,
+    hipLaunchKernelGGL(sqc_walk_kernel<false>, dim3(grid), dim3(kTh), 0, st, (const bf16*)A_, (const bf16*)B_,
                        (const bf16*)C_, (const bf16*)E_, z, x65, (int)x65_on_key, ks, a.T, nbh, p.nseg, p.sc, p.m, p.pc, E, Lam, Aout);
     ktimer_end(a.timer, a.stream);
     const int nc = (a.T + kCk - 1) / kCk;
@@ -761,18 +759,6 @@ int walk(const BwdArgs& a, const Layout& Ly, const Plan& p, const void* A_, cons
                        Aout + (size_t)4 * nbh * a.T * kD, rsum);
     ktimer_end(a.timer, a.stream);
     return hipGetLastError() == hipSuccess ? TWOMAMBA_OK : TWOMAMBA_ERR_DEVICE;
-}
-
-bool lds_ready() {
-    static int ok = -1;
-    if (ok < 0) {
-        const size_t lds = sizeof(Lds);
-        ok = hipFuncSetAttribute((const void*)sqc_walk_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds) == hipSuccess &&
-             hipFuncSetAttribute((const void*)sqc_walk_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds) == hipSuccess;
-    }
-    return ok == 1;
 }
 
 }  // namespace
@@ -794,7 +780,6 @@ size_t sq_bwd_chunked_workspace(const BwdArgs& a) {
 int sq_bwd_chunked(const BwdArgs& a) {
     const size_t n = (size_t)a.B * a.H * a.T;
     if (n == 0) return TWOMAMBA_OK;
-    if (!lds_ready()) return TWOMAMBA_ERR_DEVICE;
     const Layout Ly = layout_for(a);
     const Plan p = plan_for(a);
     char* ws = (char*)a.ws;

@@ -279,6 +279,10 @@ def test_chunked_form_flag_selects_the_linear_2mamba_backward(lib):
     n = 1 * 2 * 32768
     assert bwd_ws(lib, desc(B=1, H=2, T=32768)) == (OK, att(n))
     assert bwd_ws(lib, desc(B=1, H=2, T=32768, flags=8 | 16)) == (OK, att(n))
+    # heads of 2^24 tokens or more: rows past 32-bit buffer offsets, the attention form
+    assert bwd_ws(lib, desc(B=1, H=1, T=1 << 24, flags=16)) == (OK, att(1 << 24))
+    s, ch = bwd_ws(lib, desc(B=1, H=1, T=(1 << 24) - 1, flags=16))
+    assert s == OK and ch > att((1 << 24) - 1)
 
 
 @pytest.mark.parametrize("kw,status", [
