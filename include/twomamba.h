@@ -96,20 +96,16 @@ enum {
     /* twomamba_bwd / twomamba_bwd_workspace_size with TWOMAMBA_LIN: the
        attention (quadratic in T) form of the backward instead of the linear-in-T
        chunked form, for comparison; the same gradients within bf16 rounding.
-       Ignored by the forward and by 2Mamba-E, whose backward is always the
-       attention form. */
+       With TWOMAMBA_SQ it keeps the attention form at every T.  Ignored by the
+       forward and by 2Mamba-E, whose backward is always the attention form. */
     TWOMAMBA_FLAG_ATTENTION_FORM = 8u,
     /* twomamba_bwd / twomamba_bwd_workspace_size with TWOMAMBA_SQ (bf16,
        dk = dv = 64, T < 2^24): the linear-in-T chunked form of the backward
-       [2M2F App. C] instead of the attention form, which is quadratic in T.
-       dq, dk and dv agree with the attention form within bf16 rounding.  dz
-       is less precise: its row and column sums of dL/dlambda take the earlier
-       chunks' share from bf16 state readouts, and a running sum over the
-       sequence accumulates that rounding (measured up to 6e-2 relative
-       against an fp64 reference on slowly decaying inputs of 700 tokens, and
-       more on long sequences), so a caller that trains the decay logits should
-       keep the default attention form.  Ignored by the forward and by the
-       other variants. */
+       [2M2F App. C] at any T.  Without this flag that form is taken from
+       20480 tokens per head on, where it overtakes the attention form (whose
+       cost per token grows with T), and TWOMAMBA_FLAG_ATTENTION_FORM keeps
+       the attention form.  The same gradients within bf16 rounding.  Ignored
+       by the forward and by the other variants. */
     TWOMAMBA_FLAG_CHUNKED_FORM = 16u
 };
 

@@ -383,9 +383,9 @@ def bwd(q, k, v, z, out, dout, *, variant="sq", scale=1.0, no_norm=False, refere
     ``out`` is the forward output for the same inputs; ``row_stat`` the
     forward's row statistics (fwd(..., want_stats=True)), or None to have the
     backward recompute them; ``grads`` may supply the four output tensors.  With ``kernel_times`` (a list) the call goes through
-    twomamba_bwd_timed and appends (kernel name, milliseconds) per launch.  ``attention_form``: the first
-    order's quadratic form instead of its linear-in-T one; ``chunked_form``: 2Mamba's linear-in-T form
-    instead of its quadratic one (dz less precise, see TWOMAMBA_FLAG_CHUNKED_FORM).
+    twomamba_bwd_timed and appends (kernel name, milliseconds) per launch.  ``attention_form``: the
+    quadratic form instead of the linear-in-T one (first order at any T, 2Mamba from 20480 tokens on);
+    ``chunked_form``: 2Mamba's linear-in-T form at any T.
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]

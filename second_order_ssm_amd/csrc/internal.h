@@ -166,7 +166,10 @@ BwdScratch bwd_scratch(const BwdArgs& a);
 int bwd_prep_launch(const BwdArgs& a, const BwdScratch& s, bool with_d);
 int bwd_dz_launch(const BwdArgs& a, const BwdScratch& s);
 int ref_bwd(const BwdArgs& a);
-// 2Mamba backward in O(T) (sq_bwd_chunk.hip): chosen by TWOMAMBA_FLAG_CHUNKED_FORM
+// 2Mamba backward in O(T) (sq_bwd_chunk.hip): chosen by TWOMAMBA_FLAG_CHUNKED_FORM,
+// and by default from kSqChunkedMinT tokens per head on (where it overtakes the
+// attention form, whose cost per token grows with T)
+constexpr int kSqChunkedMinT = 20480;
 bool sq_bwd_chunked_supported(const BwdArgs& a);
 size_t sq_bwd_chunked_workspace(const BwdArgs& a);
 int sq_bwd_chunked(const BwdArgs& a);

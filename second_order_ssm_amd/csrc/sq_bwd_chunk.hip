@@ -23,12 +23,13 @@
 // the forward's state with both pair orders kept), read out by
 // A_t[j] = sum_{i,c} a_t[i] c_t[c] S[i, c, j]: a contraction with K = (i, c).
 // The strict row and column sums of dL/dlambda (C.1) need no pass of their own:
-// P_ts is homogeneous of degree 2 in q_t and in k_s, so the keys of earlier chunks
-// give q_t.dq^inter_t / 2 (and the queries of later chunks k_s.dk^inter_s / 2),
-// while the pairs inside a chunk are summed in fp32 by the kernel that forms their
-// weights.  The inter-chunk shares come from bf16 state readouts, and dz is a
-// running sum of column minus row sums over the whole sequence, which accumulates
-// that rounding: dz is less precise than in the attention form.
+// P_ts is homogeneous of degree 2 in q_t and in k_s, so the keys two or more chunks
+// back give q_t.dq^far_t / 2 (and the queries two or more chunks ahead
+// k_s.dk^far_s / 2), while the pairs within a query's own chunk and the chunk before
+// it are summed in fp32 by the kernel that forms their weights.  dz is a running sum
+// of column minus row sums over the whole sequence; leaving the nearest chunk out of
+// the bf16 state readout keeps the large near terms exact (with the previous chunk in
+// the readout, that rounding accumulated to 5e-2 of dz at 2x16x8192).
 //
 // sqc_walk_kernel: one workgroup of 8 waves per (head, segment, quarter of the
 // value columns c), the quarter's S (64 i x 16 c x 64 j, fp32) held in MFMA
@@ -37,7 +38,8 @@
 // N[i, j] = sum lambda e65_s b_s[i] b_s[j].  Per chunk of 64 tokens:
 //   intra:   W^T[s, t] = exp(Gl_t - Gl_s) (b_s.a_t) (e_s.c_t + e65_s c65_t) for
 //            s <= t in the chunk, then A += W b (16x16x32 and 16x16x16 MFMAs);
-//   readout: A_t += sum_{i,c} (exp(Gl_t) a_t[i] c_t[c]) S[i, c, j], with K = 32
+//   readout: A_t += sum_{i,c} (exp(G_t - G_anchor) a_t[i] c_t[c]) S[i, c, j] from the
+//            state of the keys before the previous chunk (anchored at its start), with K = 32
 //            slots = two i by four c per lane group, the state tiles of i and
 //            i + 1 stacked as the B operand (the rows 4g..4g+3 a lane holds are
 //            its K-slots);
@@ -78,13 +80,20 @@ __device__ __forceinline__ uint32_t pk(float a, float b) { return pack2(a, b); }
 __device__ __forceinline__ float lo16(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-struct Lds {
+// One chunk's keys as the update reads them.  The main pass adds a chunk's keys one
+// chunk after staging them (its readout of chunk c leaves out the keys of chunk c - 1,
+// which the chunk-local kernel takes), so it holds two.
+struct KeySide {
     float b32t[kD][68];      // b_s[i] as [i][s]: products of the update operand
-    float el[kQc][68];       // exp(Gamma - Gl_s) e_s[c] as [c][s]
-    float ag[kCk][68];       // exp(Gl_t) a_t[i] as [t][i]: readout products
-    float cq[kCk][20];       // c_t[c] as [t][c]
+    float el[kQc][68];       // exp(Gamma - Gl_s) e_s[c] / frame as [c][s]
     uint16_t bt16[kD][72];   // b_s[j] as [j][s], bf16 (update B operand)
-    float c65[kCk], el65[kCk];
+    float el65[kCk];         // the 65th column's weights
+};
+struct Lds {
+    KeySide kb[2];
+    float ag[kCk][68];       // (frame) exp(G_t - G_anchor) a_t[i] as [t][i]: readout products
+    float cq[kCk][20];       // c_t[c] as [t][c]
+    float c65[kCk];
     float red[kWv][2 * 16 * 64];   // the waves' partial A over two query tiles
 };
 
@@ -136,48 +145,55 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
     return x;
 }
 
-// Stages one chunk into LDS.  Gl (of the lane's token) and Gamma are per wave.
-__device__ __forceinline__ void stage(Lds& L, const Fetch& f, float Gl, float Gam, float fr, float rfn, int tid,
-                                      bool main, bool has65, bool x65_on_key, bool has_ks) {
+// Stages one chunk's keys (b, e, the 65th column) into K, with the update weights
+// exp(Gamma - Gl_s) f_s / frame.  Gl (of the lane's token) and Gamma are per wave.
+__device__ __forceinline__ void stage_keys(KeySide& K, const Fetch& f, float Gl, float Gam, float rfn, int tid,
+                                           bool has65, bool x65_on_key, bool has_ks) {
     const int lane = tid & 63;
-    {   // a and b: token tid / 8, dims 8 (tid mod 8) .. + 7
+    {   // b: token tid / 8, dims 8 (tid mod 8) .. + 7
         const int t = tid >> 3, d = 8 * (tid & 7);
         const uint32_t bw[4] = {f.b.x, f.b.y, f.b.z, f.b.w};
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const uint32_t u = bw[m >> 1];
-            L.b32t[d + m][t] = (m & 1) ? hi16(u) : lo16(u);
-            L.bt16[d + m][t] = (uint16_t)(u >> (16 * (m & 1)));
-        }
-        if (main) {
-            const float eg = fr * fexp(__shfl(Gl, t));
-            const uint4 u = f.a;
-            *reinterpret_cast<float4*>(&L.ag[t][d]) =
-                make_float4(eg * lo16(u.x), eg * hi16(u.x), eg * lo16(u.y), eg * hi16(u.y));
-            *reinterpret_cast<float4*>(&L.ag[t][d + 4]) =
-                make_float4(eg * lo16(u.z), eg * hi16(u.z), eg * lo16(u.w), eg * hi16(u.w));
+            K.b32t[d + m][t] = (m & 1) ? hi16(u) : lo16(u);
+            K.bt16[d + m][t] = (uint16_t)(u >> (16 * (m & 1)));
         }
     }
-    {   // c (threads < 256) or e (the others): token u / 4, columns 4 (u mod 4) .. + 3
+    if (tid >= 256) {   // e: token u / 4, columns 4 (u mod 4) .. + 3
         const int u = tid & 255, t = u >> 2, col = 4 * (u & 3);
         const uint2 x = f.ce;
-        if (tid < 256) {
-            if (main) {
-                *reinterpret_cast<float4*>(&L.cq[t][col]) = make_float4(lo16(x.x), hi16(x.x), lo16(x.y), hi16(x.y));
-            }
-        } else {
-            const float l = rfn * fexp(Gam - __shfl(Gl, t)) * (has_ks ? __shfl(f.ks, t) : 1.f);
-            L.el[col + 0][t] = l * lo16(x.x);
-            L.el[col + 1][t] = l * hi16(x.x);
-            L.el[col + 2][t] = l * lo16(x.y);
-            L.el[col + 3][t] = l * hi16(x.y);
-        }
+        const float l = rfn * fexp(Gam - __shfl(Gl, t)) * (has_ks ? __shfl(f.ks, t) : 1.f);
+        K.el[col + 0][t] = l * lo16(x.x);
+        K.el[col + 1][t] = l * hi16(x.x);
+        K.el[col + 2][t] = l * lo16(x.y);
+        K.el[col + 3][t] = l * hi16(x.y);
     }
-    if (has65 && tid < 64) {   // the 65th column: c65_t e65_s = -x_t (query side) or -x_s (key side)
-        const float cv = x65_on_key ? -1.f : -f.x65, ev = x65_on_key ? f.x65 : 1.f;
-        L.c65[lane] = cv;
-        L.el65[lane] = rfn * fexp(Gam - Gl) * (has_ks ? f.ks : 1.f) * ev;
+    if (has65 && tid < 64) {   // e65_s: x_s (key side) or 1
+        const float ev = x65_on_key ? f.x65 : 1.f;
+        K.el65[lane] = rfn * fexp(Gam - Gl) * (has_ks ? f.ks : 1.f) * ev;
     }
+}
+
+// Stages one chunk's queries (a with the factor frq exp(Gl_t), c, the 65th column).
+__device__ __forceinline__ void stage_queries(Lds& L, const Fetch& f, float Gl, float frq, int tid, bool has65,
+                                              bool x65_on_key) {
+    const int lane = tid & 63;
+    {   // a: token tid / 8, dims 8 (tid mod 8) .. + 7
+        const int t = tid >> 3, d = 8 * (tid & 7);
+        const float eg = frq * fexp(__shfl(Gl, t));
+        const uint4 u = f.a;
+        *reinterpret_cast<float4*>(&L.ag[t][d]) =
+            make_float4(eg * lo16(u.x), eg * hi16(u.x), eg * lo16(u.y), eg * hi16(u.y));
+        *reinterpret_cast<float4*>(&L.ag[t][d + 4]) =
+            make_float4(eg * lo16(u.z), eg * hi16(u.z), eg * lo16(u.w), eg * hi16(u.w));
+    }
+    if (tid < 256) {   // c: token u / 4, columns 4 (u mod 4) .. + 3
+        const int u = tid, t = u >> 2, col = 4 * (u & 3);
+        const uint2 x = f.ce;
+        *reinterpret_cast<float4*>(&L.cq[t][col]) = make_float4(lo16(x.x), hi16(x.x), lo16(x.y), hi16(x.y));
+    }
+    if (has65 && tid < 64) L.c65[lane] = x65_on_key ? -1.f : -f.x65;   // c65_t: -1 or -x_t (query side)
 }
 
 // The 65th column's readout into the accumulators of key tile JT, for the query tiles
@@ -204,7 +220,7 @@ __device__ __forceinline__ void n_readout(f4 (&O)[2][4], const f4 (&N)[2], const
 // S <- e^Gamma S + sum_s (exp(Gamma - Gl_s) e_s[c] b_s[i]) b_s[j] in the frame (el
 // carries the new frame's reciprocal); resc: the stored state first takes the
 // factor fn0 (the frame was reset to 1).  K = the chunk's tokens, 32 per MFMA.
-__device__ __forceinline__ void state_update(f4 (&S)[8][4], f4 (&N)[2], const Lds& L, bool resc, float fn0,
+__device__ __forceinline__ void state_update(f4 (&S)[8][4], f4 (&N)[2], const KeySide& L, bool resc, float fn0,
                                              bool n_here, int w, int g, int m16) {
     if (resc) {
 #pragma unroll
@@ -287,10 +303,12 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
     const int nc = (T + kCk - 1) / kCk;
     const int npieces = (nseg - 1) * m;
     int ch0, ch1;
-    if (kPre) {   // piece seg = segment seg / m, part seg mod m
+    if (kPre) {   // piece seg = segment seg / m, part seg mod m, over the keys the main pass does
+                  // not add itself: segment sg's keys are chunks sg sc - 1 .. (sg + 1) sc - 2
         const int sg = seg / m, r = seg - sg * m;
-        ch0 = min(nc, sg * sc + r * pc);
-        ch1 = min(min(nc, (sg + 1) * sc), ch0 + pc);
+        const int k0 = max(0, sg * sc - 1), k1 = min(nc, (sg + 1) * sc - 1);
+        ch0 = min(k1, k0 + r * pc);
+        ch1 = min(k1, ch0 + pc);
     } else {
         ch0 = seg * sc;
         ch1 = min(nc, ch0 + sc);
@@ -334,10 +352,28 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
 
     // The state is kept in a frame: true S = fr * stored S, so that the chunk decay
     // multiplies one scalar instead of every accumulator; the stored state is rescaled
-    // only when fr would drop below 2^-64 (or underflow).
+    // only when the frame would drop below 2^-64 (or underflow).  Every wave forms the
+    // same frame and decay totals, so branches on them are uniform.
     float fr = 1.f;
     float lam_tot = 0.f;
+    // The main pass reads chunk c's queries out of the state of the keys before chunk
+    // c - 1 (the chunk-local kernel takes chunk c - 1's keys), then adds chunk c - 1's
+    // keys: "pend" is that chunk, staged one iteration earlier, with its decay total and
+    // the frame its weights were staged in.
+    bool pend = false, pend_resc = false;
+    float pend_gam = 0.f, pend_fn0 = 1.f, pend_fnew = 1.f;
     Fetch f;
+    if (!kPre && seg > 0) {   // the previous segment's last chunk: staged now, added after the first readout
+        fetch<true>(f, src, (ch0 - 1) * kCk, q, tid);
+        const float glp = wave_incl_scan(decay_log(f.z), lane);
+        const float gp = __shfl(glp, 63);
+        pend_fn0 = fr * fexp(gp);
+        pend_resc = pend_fn0 < 0x1p-64f;
+        pend_fnew = pend_resc ? 1.f : pend_fn0;
+        pend_gam = gp;
+        pend = true;
+        stage_keys(L.kb[(ch0 - 1) & 1], f, glp, gp, 1.f / pend_fnew, tid, has65, x65_on_key != 0, has_ks);
+    }
     fetch<kPre>(f, src, ch0 * kCk, q, tid);
     for (int ch = ch0; ch < ch1; ++ch) {
         const int c0 = ch * kCk;
@@ -345,86 +381,93 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
         const float gl = wave_incl_scan(c0 + lane < T ? decay_log(f.z) : 0.f, lane);
         const float Gam = __shfl(gl, 63);
         lam_tot += Gam;
-        // the readout sees the old frame, the update's weights the new one; when the new
-        // frame would fall below 2^-64 the stored state takes it before the update
-        // (wave-uniform: every wave forms the same fr and Gam)
-        const float fn0 = fr * fexp(Gam);
+        // the frame of this chunk's keys: after the pending update, times e^Gamma
+        const float fr_after = pend ? pend_fnew : fr;
+        const float fn0 = fr_after * fexp(Gam);
         const bool resc = fn0 < 0x1p-64f;
         const float fnew = resc ? 1.f : fn0;
-        stage(L, f, gl, Gam, fr, 1.f / fnew, tid, !kPre, has65, x65_on_key != 0, has_ks);
+        KeySide& K = L.kb[kPre ? 0 : (ch & 1)];
+        stage_keys(K, f, gl, Gam, 1.f / fnew, tid, has65, x65_on_key != 0, has_ks);
+        // the queries see the stored state (frame fr) anchored before the pending chunk
+        if (!kPre) stage_queries(L, f, gl, fr * (pend ? fexp(pend_gam) : 1.f), tid, has65, x65_on_key != 0);
         __syncthreads();
         fetch<kPre>(f, src, c0 + kCk, q, tid);   // past the segment: loads nothing used
 
-        if (!kPre) {
-            // ---- readout from the state at the chunk's start, in two passes of two query tiles
-            float* dst = Aout + ((size_t)q * nbh * T + hoff) * kD;
-#pragma unroll 1
-            for (int pass = 0; pass < 2; ++pass) {
-                f4 O[2][4];   // partial A[t = 16 (2 pass + tl) + 4g + r][j = 16 jt + m16] of this wave
-#pragma unroll
-                for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) O[tl][jt] = zero4;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    b8 B[4];
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) {
-                        const float xs[8] = {S[2 * p][jt][0],     S[2 * p][jt][1],     S[2 * p][jt][2],
-                                             S[2 * p][jt][3],     S[2 * p + 1][jt][0], S[2 * p + 1][jt][1],
-                                             S[2 * p + 1][jt][2], S[2 * p + 1][jt][3]};
-                        B[jt] = to_b(xs);
-                    }
-                    const int i0 = 8 * w + 2 * p;
-#pragma unroll
-                    for (int tl = 0; tl < 2; ++tl) {
-                        const int t = 16 * (2 * pass + tl) + m16;
-                        const float2 av = *reinterpret_cast<const float2*>(&L.ag[t][i0]);
-                        const float4 cv = *reinterpret_cast<const float4*>(&L.cq[t][4 * g]);
-                        const b8 X = as_b8(make_uint4(pk(av.x * cv.x, av.x * cv.y), pk(av.x * cv.z, av.x * cv.w),
-                                                      pk(av.y * cv.x, av.y * cv.y), pk(av.y * cv.z, av.y * cv.w)));
-#pragma unroll
-                        for (int jt = 0; jt < 4; ++jt) O[tl][jt] = mfma(X, B[jt], O[tl][jt]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (n_here) {   // the 65th column: K = i over the two row tiles this wave holds
-                    switch (w & 3) {
-                        case 0: n_readout<0>(O, N, L, w, g, m16, pass); break;
-                        case 1: n_readout<1>(O, N, L, w, g, m16, pass); break;
-                        case 2: n_readout<2>(O, N, L, w, g, m16, pass); break;
-                        default: n_readout<3>(O, N, L, w, g, m16, pass); break;
-                    }
-                }
-#pragma unroll
-                for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) L.red[w][((tl * 4 + jt) * 4 + r) * 64 + lane] = O[tl][jt][r];
-                if (pass == 1) {
-                    state_update(S, N, L, resc, fn0, n_here, w, g, m16);
-                    fr = fnew;
-                }
-                __syncthreads();   // every wave's partial in LDS (and, after the second pass, the update's reads done)
-                // the eight partials summed and stored: fp32, this quarter's share
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const int ei = tid + kTh * n, rho = ei >> 6, l = ei & 63;
-                    const int tl = rho >> 4, jt = (rho >> 2) & 3, r = rho & 3;
-                    const int t = c0 + 16 * (2 * pass + tl) + 4 * (l >> 4) + r, j = 16 * jt + (l & 15);
-                    float v = 0.f;
-#pragma unroll
-                    for (int ww = 0; ww < kWv; ++ww) v += L.red[ww][ei];
-                    if (t < T) dst[(size_t)t * kD + j] = v;
-                }
-                if (pass == 0) __syncthreads();   // the sums read before the second pass writes
-            }
-        } else {
-            state_update(S, N, L, resc, fn0, n_here, w, g, m16);
+        if (kPre) {
+            state_update(S, N, K, resc, fn0, n_here, w, g, m16);
             fr = fnew;
             __syncthreads();   // the update's reads done before the next chunk is staged
+            continue;
         }
+        // ---- readout from the stored state, in two passes of two query tiles
+        float* dst = Aout + ((size_t)q * nbh * T + hoff) * kD;
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            f4 O[2][4];   // partial A[t = 16 (2 pass + tl) + 4g + r][j = 16 jt + m16] of this wave
+#pragma unroll
+            for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) O[tl][jt] = zero4;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                b8 B[4];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    const float xs[8] = {S[2 * p][jt][0],     S[2 * p][jt][1],     S[2 * p][jt][2],
+                                         S[2 * p][jt][3],     S[2 * p + 1][jt][0], S[2 * p + 1][jt][1],
+                                         S[2 * p + 1][jt][2], S[2 * p + 1][jt][3]};
+                    B[jt] = to_b(xs);
+                }
+                const int i0 = 8 * w + 2 * p;
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl) {
+                    const int t = 16 * (2 * pass + tl) + m16;
+                    const float2 av = *reinterpret_cast<const float2*>(&L.ag[t][i0]);
+                    const float4 cv = *reinterpret_cast<const float4*>(&L.cq[t][4 * g]);
+                    const b8 X = as_b8(make_uint4(pk(av.x * cv.x, av.x * cv.y), pk(av.x * cv.z, av.x * cv.w),
+                                                  pk(av.y * cv.x, av.y * cv.y), pk(av.y * cv.z, av.y * cv.w)));
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt) O[tl][jt] = mfma(X, B[jt], O[tl][jt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (n_here) {   // the 65th column: K = i over the two row tiles this wave holds
+                switch (w & 3) {
+                    case 0: n_readout<0>(O, N, L, w, g, m16, pass); break;
+                    case 1: n_readout<1>(O, N, L, w, g, m16, pass); break;
+                    case 2: n_readout<2>(O, N, L, w, g, m16, pass); break;
+                    default: n_readout<3>(O, N, L, w, g, m16, pass); break;
+                }
+            }
+#pragma unroll
+            for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) L.red[w][((tl * 4 + jt) * 4 + r) * 64 + lane] = O[tl][jt][r];
+            if (pass == 1 && pend) {   // the pending chunk's keys, after this chunk's readout
+                state_update(S, N, L.kb[(ch - 1) & 1], pend_resc, pend_fn0, n_here, w, g, m16);
+                fr = pend_fnew;
+            }
+            __syncthreads();   // every wave's partial in LDS (and, after the second pass, the update's reads done)
+            // the eight partials summed and stored: fp32, this quarter's share
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int ei = tid + kTh * n, rho = ei >> 6, l = ei & 63;
+                const int tl = rho >> 4, jt = (rho >> 2) & 3, r = rho & 3;
+                const int t = c0 + 16 * (2 * pass + tl) + 4 * (l >> 4) + r, j = 16 * jt + (l & 15);
+                float v = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWv; ++ww) v += L.red[ww][ei];
+                if (t < T) dst[(size_t)t * kD + j] = v;
+            }
+            if (pass == 0) __syncthreads();   // the sums read before the second pass writes
+        }
+        pend = true;
+        pend_gam = Gam;
+        pend_fn0 = fn0;
+        pend_resc = resc;
+        pend_fnew = fnew;
     }
 
     if (kPre) {
@@ -443,87 +486,108 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
     }
 }
 
-// The keys of the query's own chunk: A_t += sum_{s in chunk, s <= t} exp(Gl_t - Gl_s)
-// (b_s.a_t) (e_s.c_t + e65_s c65_t) f_s b_s over all 64 value columns (the dot
-// products in fp32 from the bf16 rows, before any rounding), into the fifth
-// slot of A; and rsum_t = sum over the same keys with s < t of that weight times
-// b_s.a_t, which is the chunk's share of the strict row sum of dL/dlambda (up to
-// scale^2 and the row's 1/den_t).  One workgroup of four waves per (head, chunk); wave w takes query
-// tile w.  Scores transposed (S^T = B A^T and U^T = E C^T on 16x16x32 MFMAs, so a
-// lane column is one query), then A = W B with W^T's accumulators as the A
-// operand and B read through the transposing LDS read.
+// The keys of the query's own chunk and of the chunk before it (which the main pass
+// leaves out of its readout): A_t += sum_{s in [c0 - 64, t]} exp(G_t - G_s) (b_s.a_t)
+// (e_s.c_t + e65_s c65_t) f_s b_s over all 64 value columns (the dot products in fp32
+// from the bf16 rows, before any rounding), into the fifth slot of A; and rsum_t =
+// the same keys' sum with s < t of that weight times b_s.a_t, which is their share of
+// the strict row sum of dL/dlambda (up to scale^2 and the row's 1/den_t), summed in
+// fp32.  One workgroup of four waves per (head, chunk); wave w takes query tile w.
+// Scores transposed (S^T = B A^T and U^T = E C^T on 16x16x32 MFMAs, so a lane column is
+// one query), then A = W B with W^T's accumulators as the A operand and B read through
+// the transposing LDS read.
 __global__ void __launch_bounds__(256)
 sqc_intra_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const bf16* __restrict__ gc,
                  const bf16* __restrict__ ge, const float* __restrict__ gz, const float* __restrict__ gx65,
                  int x65_on_key, const float* __restrict__ gks, int T, int nc, float* __restrict__ Aout,
                  float* __restrict__ rsum) {
-    __shared__ Tile tA, tB, tC, tE;
-    __shared__ float sGl[kCk], sC65[kCk], sE65[kCk], sKs[kCk];
+    __shared__ Tile tA, tC, tB[2], tE[2];   // queries of the chunk; keys of the chunk before it [0] and of it [1]
+    __shared__ float sGl[2 * kCk], sE65[2 * kCk], sKs[2 * kCk], sC65[kCk];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m16 = lane & 15;
-    // the wave index as a wave-uniform value: branches on it are then scalar, so no MFMA of
-    // another wave's case runs under an empty exec mask (MFMAs ignore exec)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.x / nc, ch = blockIdx.x % nc, c0 = ch * kCk;
+    const bool has_prev = ch > 0;
     const size_t hoff = (size_t)bh * T;
     const bool has65 = gx65 != nullptr, has_ks = gks != nullptr;
     {
         const size_t rb = (size_t)T * kD * 2;
         const __amdgpu_buffer_rsrc_t ra = rsrc(ga + hoff * kD, rb), rbb = rsrc(gb + hoff * kD, rb),
                                      rc = rsrc(gc + hoff * kD, rb), re = rsrc(ge + hoff * kD, rb);
-        const int so = c0 * kD * 2;
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int e = tid + 256 * n, r = e >> 3, d = 8 * (e & 7);
             const int off = r * kD * 2 + 2 * d;
-            *reinterpret_cast<uint4*>(&tA.X[r][d]) = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, so, 0));
-            *reinterpret_cast<uint4*>(&tB.X[r][d]) = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbb, off, so, 0));
-            *reinterpret_cast<uint4*>(&tC.X[r][d]) = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, so, 0));
-            *reinterpret_cast<uint4*>(&tE.X[r][d]) = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(re, off, so, 0));
+            *reinterpret_cast<uint4*>(&tA.X[r][d]) = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, c0 * kD * 2, 0));
+            *reinterpret_cast<uint4*>(&tC.X[r][d]) = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, c0 * kD * 2, 0));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = h == 1 || has_prev;
+                const int so = (c0 + (h - 1) * kCk) * kD * 2;
+                *reinterpret_cast<uint4*>(&tB[h].X[r][d]) =
+                    ok ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbb, off, ok ? so : 0, 0)) : z4;
+                *reinterpret_cast<uint4*>(&tE[h].X[r][d]) =
+                    ok ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(re, off, ok ? so : 0, 0)) : z4;
+            }
         }
-        if (w == 0) {
-            const int t = c0 + lane;
-            const float zz = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(gz + hoff, (size_t)T * 4), lane * 4, c0 * 4, 0));
-            sGl[lane] = wave_incl_scan(t < T ? decay_log(zz) : 0.f, lane);
+        if (w < 2) {   // wave 0: the chunk before (zeros for the first chunk), wave 1: the chunk
+            const int h = w, t = c0 + (h - 1) * kCk + lane;
+            const bool ok = h == 1 || has_prev;
+            const int so = ok ? (c0 + (h - 1) * kCk) * 4 : 0;
+            const float zz = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(gz + hoff, (size_t)T * 4), lane * 4, so, 0));
+            const float gv = (ok && t < T) ? decay_log(zz) : 0.f;
+            sGl[h * kCk + lane] = wave_incl_scan(gv, lane);
             const float m = has65 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                        rsrc(gx65 + hoff, (size_t)T * 4), lane * 4, c0 * 4, 0))
+                                        rsrc(gx65 + hoff, (size_t)T * 4), lane * 4, so, 0))
                                   : 0.f;
-            sC65[lane] = has65 ? (x65_on_key ? -1.f : -m) : 0.f;
-            sE65[lane] = has65 ? (x65_on_key ? m : 1.f) : 0.f;
-            sKs[lane] = has_ks ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                     rsrc(gks + hoff, (size_t)T * 4), lane * 4, c0 * 4, 0))
-                               : 1.f;
+            const float ksv = has_ks ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rsrc(gks + hoff, (size_t)T * 4), lane * 4, so, 0))
+                                     : 1.f;
+            sE65[h * kCk + lane] = (has65 && ok) ? (x65_on_key ? m : 1.f) : 0.f;
+            sKs[h * kCk + lane] = ksv;
+            if (h == 1) sC65[lane] = has65 ? (x65_on_key ? -1.f : -m) : 0.f;
         }
     }
     __syncthreads();
+    // the window's running log decay: the chunk's own offset by the chunk before's total
+    if (tid < kCk) sGl[kCk + tid] += sGl[kCk - 1];
+    __syncthreads();
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const int tt = w, t = 16 * tt + m16;
-    const float glt = sGl[t], c65t = sC65[t];
+    const float glt = sGl[kCk + t], c65t = sC65[t];
     f4 Oi[4] = {zero4, zero4, zero4, zero4};
-    float rs = 0.f;   // sum over the chunk's earlier keys of W_ts (b_s.a_t), in fp32
-    for (int sp = 0; 2 * sp <= tt; ++sp) {
+    float rs = 0.f;   // sum over the window's earlier keys of W_ts (b_s.a_t), in fp32
+    // key pairs of tiles: the chunk before (two pairs, every key earlier), then the chunk's
+    // own tiles up to the query tile
+    for (int kp = 0; kp < 2 + (tt >> 1) + 1; ++kp) {
+        const int h = kp < 2 ? 0 : 1, sp = kp < 2 ? kp : kp - 2;
+        const Tile& KB = tB[h];
+        const Tile& KE = tE[h];
         float wv[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int st = 2 * sp + h;
+        for (int hh = 0; hh < 2; ++hh) {
+            const int st = 2 * sp + hh;
+            const bool live = h == 0 || st <= tt;
             f4 sab = zero4, uce = zero4;
-            if (st <= tt) {
+            if (live) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    sab = mfma(row_op(tB, 16 * st + m16, g, kk), row_op(tA, t, g, kk), sab);
-                    uce = mfma(row_op(tE, 16 * st + m16, g, kk), row_op(tC, t, g, kk), uce);
+                    sab = mfma(row_op(KB, 16 * st + m16, g, kk), row_op(tA, t, g, kk), sab);
+                    uce = mfma(row_op(KE, 16 * st + m16, g, kk), row_op(tC, t, g, kk), uce);
                 }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int s = 16 * st + 4 * g + r;
-                const float v = fexp(glt - sGl[s & 63]) * sab[r] * (uce[r] + sE65[s & 63] * c65t) * sKs[s & 63];
-                wv[4 * h + r] = (st <= tt && s <= t) ? v : 0.f;
-                rs += (st <= tt && s < t) ? v * sab[r] : 0.f;
+                const int s = 16 * st + 4 * g + r, sw = h * kCk + s;
+                const bool before = h == 0 || s < t;
+                const float v = fexp(glt - sGl[sw]) * sab[r] * (uce[r] + sE65[sw] * c65t) * sKs[sw];
+                wv[4 * hh + r] = (live && (before || s == t)) ? v : 0.f;
+                rs += (live && before) ? v * sab[r] : 0.f;
             }
         }
         const b8 wa = to_b(wv);
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) Oi[jt] = mfma(wa, tr_op(tB, jt, 2 * sp, lane), Oi[jt]);
+        for (int jt = 0; jt < 4; ++jt) Oi[jt] = mfma(wa, tr_op(KB, jt, 2 * sp, lane), Oi[jt]);
     }
     // the strict row sum: the lane groups' shares of the keys, then one lane per query
     rs += __shfl_xor(rs, 16);
@@ -764,12 +828,13 @@ int walk(const BwdArgs& a, const Layout& Ly, const Plan& p, const void* A_, cons
 }  // namespace
 
 // The chunked form takes 2Mamba at bf16, d = 64, heads under 2^24 tokens, when
-// TWOMAMBA_FLAG_CHUNKED_FORM asks for it.
+// TWOMAMBA_FLAG_CHUNKED_FORM asks for it, and by default from kSqChunkedMinT tokens
+// per head on (TWOMAMBA_FLAG_ATTENTION_FORM keeps the attention form).
 bool sq_bwd_chunked_supported(const BwdArgs& a) {
     if (a.variant != TWOMAMBA_SQ || a.dtype != TWOMAMBA_BF16 || a.dk != 64 || a.dv != 64 || a.T <= 0) return false;
     if (a.T >= (1 << 24)) return false;   // rows through 32-bit buffer offsets
     if (a.flags & (TWOMAMBA_FLAG_REFERENCE_KERNELS | TWOMAMBA_FLAG_ATTENTION_FORM)) return false;
-    return (a.flags & TWOMAMBA_FLAG_CHUNKED_FORM) != 0;
+    return (a.flags & TWOMAMBA_FLAG_CHUNKED_FORM) != 0 || a.T >= kSqChunkedMinT;
 }
 
 size_t sq_bwd_chunked_workspace(const BwdArgs& a) {

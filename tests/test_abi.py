@@ -263,9 +263,10 @@ def test_attention_form_flag_selects_the_quadratic_first_order_backward(lib):
 
 def test_chunked_form_flag_selects_the_linear_2mamba_backward(lib):
     # TWOMAMBA_FLAG_CHUNKED_FORM (16): 2Mamba's backward in its linear-in-T form (a
-    # workspace other than the attention form's per-token rows); without it the attention
-    # form at every T.  The first order and 2Mamba-E ignore the flag; fp32 and the
-    # reference kernels keep the attention form.
+    # workspace other than the attention form's per-token rows); by default that form from
+    # 20480 tokens on, where TWOMAMBA_FLAG_ATTENTION_FORM (8) keeps the quadratic one.  The
+    # first order and 2Mamba-E ignore the flag; fp32 and the reference kernels keep the
+    # attention form.
     a256 = lambda x: (x + 255) // 256 * 256
     att = lambda n: a256(8 * n) + 4 * a256(4 * n)
     n = 2 * 3 * 1000
@@ -276,9 +277,12 @@ def test_chunked_form_flag_selects_the_linear_2mamba_backward(lib):
     assert bwd_ws(lib, desc(B=2, H=3, T=1000, flags=16, dtype=0)) == (OK, att(n))
     assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=1, flags=16)) == (OK, att(n))
     assert bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2, flags=16)) == bwd_ws(lib, desc(B=2, H=3, T=1000, variant=2))
-    n = 1 * 2 * 32768
-    assert bwd_ws(lib, desc(B=1, H=2, T=32768)) == (OK, att(n))
-    assert bwd_ws(lib, desc(B=1, H=2, T=32768, flags=8 | 16)) == (OK, att(n))
+    n = 1 * 2 * 20480
+    s, ch = bwd_ws(lib, desc(B=1, H=2, T=20480))
+    assert s == OK and ch > att(n)
+    assert bwd_ws(lib, desc(B=1, H=2, T=20480, flags=8)) == (OK, att(n))
+    assert bwd_ws(lib, desc(B=1, H=2, T=20480, flags=8 | 16)) == (OK, att(n))
+    assert bwd_ws(lib, desc(B=1, H=2, T=20479)) == (OK, att(1 * 2 * 20479))
     # heads of 2^24 tokens or more: rows past 32-bit buffer offsets, the attention form
     assert bwd_ws(lib, desc(B=1, H=1, T=1 << 24, flags=16)) == (OK, att(1 << 24))
     s, ch = bwd_ws(lib, desc(B=1, H=1, T=(1 << 24) - 1, flags=16))

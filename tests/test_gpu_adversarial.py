@@ -131,7 +131,8 @@ def test_first_order_forward(mode):
 # The backward takes the resets on top of ordinary decay: with no decay between
 # them, every dz is zero or the sigmoid of 50 times a vanishing dL/dg, so the
 # reference dz is ~1e-22 and only the rounding of the running sums is compared.
-@pytest.mark.parametrize("variant", ["sq", "exp"])
+# "sq_chunked" is 2Mamba's linear-in-T backward (TWOMAMBA_FLAG_CHUNKED_FORM).
+@pytest.mark.parametrize("variant", ["sq", "exp", "sq_chunked"])
 @pytest.mark.parametrize("mode", ["small_q", "small_k", "small_k_aligned", "huge_v", "tiny_k", "resets_decay"])
 def test_backward(variant, mode):
     announce(f"adversarial backward {variant} {mode}")
@@ -139,8 +140,10 @@ def test_backward(variant, mode):
     q, k, v, z = adversarial(B, H, T, d, mode, seed=304)
     do = torch.from_numpy(np.random.default_rng(305).standard_normal((B, H, T, d))).to(torch.bfloat16)
     qd, kd, vd, zd, dod = dev(q, k, v, z, do)
+    chunked = variant == "sq_chunked"
+    variant = "sq" if chunked else variant
     out = tmb.fwd(qd, kd, vd, zd, variant=variant)
-    g = tmb.bwd(qd, kd, vd, zd, out, dod, variant=variant)
+    g = tmb.bwd(qd, kd, vd, zd, out, dod, variant=variant, chunked_form=chunked)
     torch.cuda.synchronize()
     qq, kk, vv, dd = f64(q, k, v, do)
     zz = SI.to_f64(z)

@@ -1,4 +1,5 @@
-"""GPU parity of 2Mamba's linear-in-T backward (twomamba_bwd with TWOMAMBA_FLAG_CHUNKED_FORM).
+"""GPU parity of 2Mamba's linear-in-T backward (twomamba_bwd with TWOMAMBA_FLAG_CHUNKED_FORM,
+and by default from 20480 tokens per head on).
 
 The chunked form (dq and dk from a chunk walk over the state S[i, c, j], dv from the
 unnormalised forward in reversed time, dz from the strict row and column sums of
@@ -7,12 +8,9 @@ sizes, bwd_blocked on whole heads at the workload sizes) and with the attention-
 MFMA kernels on every head.  The forward output and row statistics handed to the
 backward are the library's own.
 
-Tolerance: per-head inf-norm relative error <= 2e-2 (bf16) for dq, dk and dv against
-the oracle, and <= 4e-2 between the two GPU forms (each within 2e-2 of the oracle).
-dz is less precise in this form (its row and column sums take the earlier chunks'
-share from bf16 state readouts, and dz is their running sum over the sequence): it
-is held to DZ_TOL against the oracle on the short sequences, and at the workload
-sizes its error is printed, not asserted.
+Tolerance: per-head inf-norm relative error <= 2e-2 (bf16) for each of the four
+gradients against the oracle, and <= 4e-2 between the two GPU forms (each within 2e-2
+of the oracle).
 """
 
 import numpy as np
@@ -26,7 +24,6 @@ from gpu_util import TOL, announce, dev, host64, relerr
 
 pytestmark = pytest.mark.gpu
 
-DZ_TOL = 1e-1   # measured up to 6.1e-2 on these cases (slow decay, 700 tokens)
 
 
 def _dout(B, H, T, d, seed):
@@ -52,15 +49,12 @@ def _run(B, H, T, zm, scale, no_norm, stats, seed, z_neg_inf=False, forms=("chun
     return res, (q, k, v, z, do)
 
 
-def _check(got, ref, label, tol=TOL["bf16"], dz_tol=DZ_TOL):
+def _check(got, ref, label, tol=TOL["bf16"]):
     names = ("dq", "dk", "dv", "dz")
     errs = {n: relerr(g, r) for n, g, r in zip(names, got, ref)}
     print(f"  {label}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
-        bound = tol if n != "dz" else dz_tol
-        if bound is not None:
-            assert e < bound, f"{label} {n} error {e:.3e}"
-    assert np.isfinite(got[3]).all()
+        assert e < tol, f"{label} {n} error {e:.3e}"
 
 
 CASES = [
@@ -105,7 +99,7 @@ def test_sq_chunked_matches_attention_form(B, H, T, zm):
     # every head, against the quadratic MFMA kernels on the same forward output
     announce(f"sq bwd chunked vs attention form {B}x{H}x{T} z_mean={zm}")
     res, _ = _run(B, H, T, zm, 1.0, False, True, seed=90, forms=("chunked", "attention"))
-    _check(res["chunked"], res["attention"], "chunked vs attention", tol=2 * TOL["bf16"], dz_tol=None)
+    _check(res["chunked"], res["attention"], "chunked vs attention", tol=2 * TOL["bf16"])
 
 
 def test_sq_chunked_bwd_deterministic():
@@ -122,22 +116,23 @@ def test_sq_chunked_bwd_deterministic():
     (1, 16, 32768, -8.0, [(0, 2)]),
 ])
 def test_sq_chunked_bwd_full_size(B, H, T, zm, heads):
-    # the workload sizes, in the launch configuration the benchmark times: every head
-    # against the attention form, whole heads against the oracle's whole-matrix gradients
+    # the workload sizes, in the launch configuration the benchmark times (at 32768 tokens
+    # the default dispatch takes the chunked form): every head against the attention form,
+    # whole heads against the oracle's whole-matrix gradients
     announce(f"sq chunked bwd full size {B}x{H}x{T} z_mean={zm}")
     q, k, v, z = SI.draw(B, H, T, 64, seed=3, dtype="bf16", z_mean=zm)
     do = _dout(B, H, T, 64, 3)
     qd, kd, vd, zd, dod = dev(q, k, v, z, do)
     out, rs = tmb.fwd(qd, kd, vd, zd, want_stats=True)
-    ch = tmb.bwd(qd, kd, vd, zd, out, dod, row_stat=rs, chunked_form=True)
+    ch = tmb.bwd(qd, kd, vd, zd, out, dod, row_stat=rs, chunked_form=(T < 20480))
     torch.cuda.synchronize()
     got = [host64(x) for x in ch]
     del ch
     at = tmb.bwd(qd, kd, vd, zd, out, dod, row_stat=rs, attention_form=True)
     torch.cuda.synchronize()
-    _check(got, [host64(x) for x in at], "chunked vs attention", tol=2 * TOL["bf16"], dz_tol=None)
+    _check(got, [host64(x) for x in at], "chunked vs attention", tol=2 * TOL["bf16"])
     del at
     for b, h in heads:
         sl = lambda t: SI.to_f64(t[b:b + 1, h:h + 1])
         ref = O.bwd_blocked(sl(q), sl(k), sl(v), sl(z), sl(do), variant="sq")
-        _check([x[b:b + 1, h:h + 1] for x in got], ref, f"head ({b},{h}) vs oracle", dz_tol=None)
+        _check([x[b:b + 1, h:h + 1] for x in got], ref, f"head ({b},{h}) vs oracle")
