@@ -273,9 +273,9 @@ def sq_bwd_chunked_flops_per_head_token(d=64, dv=64):
 
 
 def leg_sq_bwd_chunked(steps, warmup):
-    """2Mamba backward in O(T) (TWOMAMBA_FLAG_CHUNKED_FORM) at the forward's workload
-    and at the long-context one (B=1 H=16 T=32768), beside the attention form of the
-    same backward on the same inputs.  Roofline: the chunk-walk kernel, over the
+    """2Mamba backward in O(T) (TWOMAMBA_FLAG_CHUNKED_FORM; the default from 20480 tokens
+    per head) at the forward's workload and at the long-context one (B=1 H=16 T=32768),
+    beside the attention form of the same backward on the same inputs.  Roofline: the chunk-walk kernel, over the
     walk's contractions (sqc_walk_flops_per_head_token) per launch."""
     import numpy as np
     import torch
@@ -304,9 +304,10 @@ def leg_sq_bwd_chunked(steps, warmup):
             for n, x in kt:
                 per[n] = per.get(n, 0.0) + x / calls
         del ws
-        desc_a = tmb.make_desc(B, H, T, d, d, dtype=torch.bfloat16)
+        desc_a = tmb.make_desc(B, H, T, d, d, dtype=torch.bfloat16, flags=tmb.FLAG_ATTENTION_FORM)
         ws_a = torch.empty(tmb.bwd_workspace_size(desc_a), dtype=torch.uint8, device="cuda")
-        fn_a = lambda: tmb.bwd(q, k, v, z, out, dout, grads=grads, workspace=ws_a, row_stat=stat)
+        fn_a = lambda: tmb.bwd(q, k, v, z, out, dout, attention_form=True, grads=grads, workspace=ws_a,
+                               row_stat=stat)
         ms_att = time_loop(fn_a, max(3, steps // 5), 1)
         del ws_a
         walk_ms = (per.get("sqc_walk_q", 0.0) + per.get("sqc_walk_k", 0.0)) / 2
