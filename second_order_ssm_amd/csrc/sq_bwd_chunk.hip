@@ -366,7 +366,7 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
     if (!kPre && seg > 0) {   // the previous segment's last chunk: staged now, added after the first readout
         fetch<true>(f, src, (ch0 - 1) * kCk, q, tid);
         const float glp = wave_incl_scan(decay_log(f.z), lane);
-        const float gp = __shfl(glp, 63);
+        const float gp = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __shfl(glp, 63))));
         pend_fn0 = fr * fexp(gp);
         pend_resc = pend_fn0 < 0x1p-64f;
         pend_fnew = pend_resc ? 1.f : pend_fn0;
@@ -379,7 +379,8 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
         const int c0 = ch * kCk;
         // chunk-local cumulative log decay of the lane's token, and the chunk total
         const float gl = wave_incl_scan(c0 + lane < T ? decay_log(f.z) : 0.f, lane);
-        const float Gam = __shfl(gl, 63);
+        // the chunk total as a wave-uniform value: the frame bookkeeping below stays scalar
+        const float Gam = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __shfl(gl, 63))));
         lam_tot += Gam;
         // the frame of this chunk's keys: after the pending update, times e^Gamma
         const float fr_after = pend ? pend_fnew : fr;
