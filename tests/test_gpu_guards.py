@@ -156,17 +156,20 @@ def test_decode_writes_stay_in_bounds(dtype):
             assert bool((tail == c.ref[G:G + 1][0]).all()), f"cache rows past {pos} written"
 
 
+# "sq_chunked": 2Mamba's linear-in-T backward (TWOMAMBA_FLAG_CHUNKED_FORM)
 @pytest.mark.parametrize("variant,dtype,d", [("sq", "bf16", 64), ("exp", "bf16", 64), ("lin", "bf16", 64),
-                                             ("sq", "f32", 16)])
+                                             ("sq", "f32", 16), ("sq_chunked", "bf16", 64)])
 def test_backward_writes_stay_in_bounds(variant, dtype, d):
     announce(f"canaries backward {variant} {dtype} d={d}")
     td = SI.torch_dtype(dtype)
     B, H, T = 1, 2, 130
+    chunked = variant == "sq_chunked"
+    variant = "sq" if chunked else variant
     q, k, v, z = _inputs(B, H, T, d, dtype, seed=430)
     out = tmb.fwd(q, k, v, z, variant=variant)
     do = torch.randn_like(out)
     gs = [Guarded((B, H, T, d), td) for _ in range(3)] + [Guarded((B, H, T), torch.float32)]
-    tmb.bwd(q, k, v, z, out, do, variant=variant, grads=[g.t for g in gs])
+    tmb.bwd(q, k, v, z, out, do, variant=variant, chunked_form=chunked, grads=[g.t for g in gs])
     torch.cuda.synchronize()
     assert all(g.intact() for g in gs)
 
@@ -184,6 +187,7 @@ def test_bitwise_determinism_ten_runs_interleaved():
         "lin": lambda: tmb.fwd(q, k, v, z, variant="lin", want_state=True),
         "bwd": lambda: tmb.bwd(q, k, v, z, q, v, variant="sq"),
         "exp_bwd": lambda: tmb.bwd(q, k, v, z, q, v, variant="exp"),
+        "sq_bwd_chunked": lambda: tmb.bwd(q, k, v, z, q, v, variant="sq", chunked_form=True),
         "step": lambda: (lambda S, n: (tmb.step(q[:, :, 7].contiguous().float(), k[:, :, 7].contiguous().float(),
                                                 v[:, :, 7].contiguous().float(), z[:, :, 7].contiguous(), S, n),
                                        S, n))(S0.clone(), n0.clone()),
