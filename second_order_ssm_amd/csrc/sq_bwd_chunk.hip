@@ -405,6 +405,7 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
 #pragma unroll 1
         for (int pass = 0; pass < 2; ++pass) {
             f4 O[2][4];   // partial A[t = 16 (2 pass + tl) + 4g + r][j = 16 jt + m16] of this wave
+            const int ag0 = (32 * pass + m16) * 68, cq0 = (32 * pass + m16) * 20 + 4 * g;   // 32-bit LDS offsets
 #pragma unroll
             for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
@@ -422,9 +423,9 @@ sqc_walk_kernel(const bf16* __restrict__ ga, const bf16* __restrict__ gb, const 
                 const int i0 = 8 * w + 2 * p;
 #pragma unroll
                 for (int tl = 0; tl < 2; ++tl) {
-                    const int t = 16 * (2 * pass + tl) + m16;
-                    const float2 av = *reinterpret_cast<const float2*>(&L.ag[t][i0]);
-                    const float4 cv = *reinterpret_cast<const float4*>(&L.cq[t][4 * g]);
+                    // row 32 pass + 16 tl + m16 of ag and cq, from the pass's base offsets
+                    const float2 av = *reinterpret_cast<const float2*>(&L.ag[0][0] + ag0 + tl * 16 * 68 + i0);
+                    const float4 cv = *reinterpret_cast<const float4*>(&L.cq[0][0] + cq0 + tl * 16 * 20);
                     const b8 X = as_b8(make_uint4(pk(av.x * cv.x, av.x * cv.y), pk(av.x * cv.z, av.x * cv.w),
                                                   pk(av.y * cv.x, av.y * cv.y), pk(av.y * cv.z, av.y * cv.w)));
 #pragma unroll
